@@ -1,0 +1,169 @@
+/*
+ * efla_oracle.c -- plain, slow, fp64 CPU oracle for Error-Free Linear Attention (EFLA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this file:
+ * it exists so that tests, the smoke check and the CPU-baseline leg of the benchmark can
+ * compare the HIP kernels against an obviously correct token-by-token recurrence.  It shares
+ * no code, header, table or constant with the HIP library.
+ *
+ * What it computes (all in double precision, one token at a time, no chunking, no blocking):
+ *
+ *   per token t, with key k_t, value v_t, query q_t and step beta_t
+ *     lambda_t = ||k_t||^2
+ *     alpha_t  = (1 - e^{-beta_t lambda_t}) / lambda_t            (and alpha_t = beta_t if lambda_t = 0)
+ *     S_t      = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T
+ *     o_t      = S_t^T q_t                                          (read after the update)
+ *
+ *   Sources: "Exact Flow Linear Attention: Exact Solution from Continuous-Time Dynamics"
+ *   (gist.science), section Metodologia, item 2 (closed-form exponential) and item 3 (update rule
+ *   and coefficient); "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 1
+ *   (alpha from lambda = ||k||^2), Step 2 (exact memory update), Step 3 (readout o_t = S_t^T q_t)
+ *   and "Putting it all together (pipeline)" (update first, then emit o = S^T q).
+ *
+ * Readings taken where the pages are silent:
+ *   - 1 - e^{-x} is evaluated as -expm1(-x): the same quantity, without cancellation for small x.
+ *   - lambda = 0 (k = 0): the 0/0 in the coefficient is replaced by its limit beta; the state update
+ *     is a no-op in that case because k = 0.
+ *   - S is d_k x d_v (k v^T is d_k x d_v and o = S^T q has d_v entries); an absent initial state is 0.
+ *
+ * The product (alpha k k^T) S_{t-1} is evaluated as alpha k (k^T S_{t-1}), which is the same matrix by
+ * associativity; both the erase term and the write term of the update are kept as written.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, k [B,H,L,d_k]; v [B,H,L,d_v]; beta [B,H,L]; o [B,H,L,d_v]; state [B,H,d_k,d_v].
+ * Parallelism: OpenMP over independent (b, h) pairs only.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* alpha_t = (1 - e^{-beta lambda}) / lambda, lambda = ||k||^2; the lambda = 0 limit is beta. */
+static double oracle_alpha_one(const double *k, double beta, int d_k)
+{
+    double lambda = 0.0;
+    for (int i = 0; i < d_k; ++i)
+        lambda += k[i] * k[i];
+    if (lambda == 0.0 || beta * lambda == 0.0)
+        return beta;
+    return -expm1(-beta * lambda) / lambda;
+}
+
+/* One exact EFLA token update applied to S (d_k x d_v), followed by the readout o = S^T q.
+ * kS is caller-provided scratch of d_v doubles. */
+static void oracle_token(double *S, const double *q, const double *k, const double *v, double beta,
+                         double *o, double *kS, int d_k, int d_v)
+{
+    const double alpha = oracle_alpha_one(k, beta, d_k);
+    /* kS = k^T S_{t-1} (a row vector of length d_v) */
+    for (int j = 0; j < d_v; ++j)
+        kS[j] = 0.0;
+    for (int i = 0; i < d_k; ++i)
+        for (int j = 0; j < d_v; ++j)
+            kS[j] += k[i] * S[(size_t)i * d_v + j];
+    /* S_t = S_{t-1} - alpha k (k^T S_{t-1}) + alpha k v^T */
+    for (int i = 0; i < d_k; ++i)
+        for (int j = 0; j < d_v; ++j)
+            S[(size_t)i * d_v + j] = S[(size_t)i * d_v + j] - alpha * k[i] * kS[j] + alpha * k[i] * v[j];
+    /* o_t = S_t^T q_t */
+    if (o) {
+        for (int j = 0; j < d_v; ++j)
+            o[j] = 0.0;
+        for (int i = 0; i < d_k; ++i)
+            for (int j = 0; j < d_v; ++j)
+                o[j] += S[(size_t)i * d_v + j] * q[i];
+    }
+}
+
+static int oracle_threads(int requested)
+{
+#ifdef _OPENMP
+    if (requested > 0)
+        return requested;
+    return omp_get_max_threads();
+#else
+    (void)requested;
+    return 1;
+#endif
+}
+
+/* alpha for n_tokens keys of length d_k. */
+void efla_oracle_alpha(const double *k, const double *beta, double *alpha, int64_t n_tokens, int d_k)
+{
+    for (int64_t t = 0; t < n_tokens; ++t)
+        alpha[t] = oracle_alpha_one(k + t * d_k, beta[t], d_k);
+}
+
+/* Full-sequence recurrence for every (b, h).  initial_state may be NULL (zeros); final_state may
+ * be NULL (not written); o may be NULL (not written).  Returns the number of threads used. */
+int efla_oracle_fwd(const double *q, const double *k, const double *v, const double *beta,
+                    const double *initial_state, double *o, double *final_state,
+                    int B, int H, int L, int d_k, int d_v, int n_threads)
+{
+    const int64_t BH = (int64_t)B * H;
+    const int nt = oracle_threads(n_threads);
+    int used = 1;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double *S = (double *)malloc(sizeof(double) * (size_t)d_k * d_v);
+        double *kS = (double *)malloc(sizeof(double) * (size_t)d_v);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t bh = 0; bh < BH; ++bh) {
+            const size_t ssz = (size_t)d_k * d_v;
+            if (initial_state)
+                memcpy(S, initial_state + bh * ssz, sizeof(double) * ssz);
+            else
+                memset(S, 0, sizeof(double) * ssz);
+            for (int t = 0; t < L; ++t) {
+                const int64_t tok = bh * L + t;
+                oracle_token(S, q + tok * d_k, k + tok * d_k, v + tok * d_v, beta[tok],
+                             o ? o + tok * d_v : NULL, kS, d_k, d_v);
+            }
+            if (final_state)
+                memcpy(final_state + bh * ssz, S, sizeof(double) * ssz);
+        }
+        free(S);
+        free(kS);
+    }
+    (void)nt;
+    return used;
+}
+
+/* One decode step for NH independent (sequence, head) states, updated in place.
+ * q, k [NH,d_k]; v [NH,d_v]; beta [NH]; state [NH,d_k,d_v]; o [NH,d_v]. Returns threads used. */
+int efla_oracle_step(const double *q, const double *k, const double *v, const double *beta,
+                     double *state, double *o, int64_t NH, int d_k, int d_v, int n_threads)
+{
+    const int nt = oracle_threads(n_threads);
+    int used = 1;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double *kS = (double *)malloc(sizeof(double) * (size_t)d_v);
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t n = 0; n < NH; ++n)
+            oracle_token(state + n * (int64_t)d_k * d_v, q + n * d_k, k + n * d_k, v + n * d_v, beta[n],
+                         o ? o + n * d_v : NULL, kS, d_k, d_v);
+        free(kS);
+    }
+    (void)nt;
+    return used;
+}

@@ -1,0 +1,406 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix (CPU only).
+
+Each ``check_*`` takes an oracle object (``alpha``, ``fwd``, ``step``) so that the same pins
+can be run against deliberately broken copies of the oracle source (see ``test_pins_catch_mutants``).
+
+Sources of the pins:
+  * the worked example printed in "Error-Free Linear Attention is a Free Lunch" (howistudyai.com),
+    Steps 1-3 (tests/golden/page4_worked_example.json);
+  * the closed-form matrix exponential of the rank-1 dynamics, "Exact Flow Linear Attention"
+    (gist.science), Metodologia item 2 -- checked against scipy's Pade/scaling-and-squaring expm;
+  * the zero-order-hold ODE dS/dt = -k k^T S + k v^T of Metodologia item 1 -- checked by the
+    augmented-matrix exponential (Van Loan) and by brute-force fine-step RK4 integration;
+  * the directional decay e^{-beta lambda} along k and the untouched orthogonal complement
+    (Contributi Chiave, "Stabilita Teorica"; howistudyai.com Step 5);
+  * the Euler / delta-rule limit for small beta*lambda (howistudyai.com Step 5, "Delta Rule");
+  * the chunkwise WY/UT rewriting (Metodologia item 3; howistudyai.com Step 4), checked with an
+    independent fp64 numpy model of the chunked form;
+  * state passing between chunks (howistudyai.com Step 4) and prefill followed by decode.
+"""
+import json
+import os
+import re
+import shutil
+import tempfile
+
+import mpmath
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from exact_flow_delta_amd import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+with open(os.path.join(HERE, "golden", "page4_worked_example.json")) as f:
+    GOLD = json.load(f)
+
+
+def _one_token(orc, k, v, beta, S0, q=None):
+    d_k, d_v = len(k), len(v)
+    q = np.zeros(d_k) if q is None else np.asarray(q, float)
+    o, S, _ = orc.fwd(q.reshape(1, 1, 1, d_k), np.asarray(k, float).reshape(1, 1, 1, d_k),
+                      np.asarray(v, float).reshape(1, 1, 1, d_v), np.array([[[beta]]]),
+                      np.asarray(S0, float).reshape(1, 1, d_k, d_v))
+    return o[0, 0, 0], S[0, 0]
+
+
+def _mixed_keys(rng, L, d_k, lo=1e-2, hi=3.0):
+    g = rng.standard_normal((L, d_k))
+    u = g / np.linalg.norm(g, axis=-1, keepdims=True)
+    s = np.exp(rng.uniform(np.log(lo), np.log(hi), (L, 1)))
+    return u * s
+
+
+# ----------------------------------------------------------------------------------------------
+# pins
+# ----------------------------------------------------------------------------------------------
+
+def check_worked_example(orc):
+    """Printed numbers of the worked example (d = 2)."""
+    p = GOLD["printed"]
+    tol = 0.5 * 10.0 ** -p["printed_decimals"]
+    k = np.array(GOLD["k"])
+    v = np.array(GOLD["v"])
+    q = np.array(GOLD["q"])
+    beta = GOLD["beta"]
+    a = orc.alpha(k[None], np.array([beta]))[0]
+    assert abs(a - p["alpha"]) <= tol, a
+    # 1 - alpha*lambda is the decay factor e^{-beta lambda} printed as 0.3679, and 1 - e^{-1} as 0.6321
+    assert abs((1.0 - a * p["lambda"]) - p["exp_minus_beta_lambda"]) <= tol
+    assert abs(a * p["lambda"] - p["one_minus_exp"]) <= tol
+    # from an empty memory the update writes alpha * k v^T; the page prints k v^T
+    o, S = _one_token(orc, k, v, beta, np.zeros((2, 2)), q)
+    np.testing.assert_allclose(S / a, np.array(p["k_vT"]), rtol=0, atol=1e-12)
+    # readout o = S^T q with the printed q, from the printed alpha and k v^T
+    want = p["alpha"] * (np.array(p["k_vT"]).T @ q)
+    assert np.max(np.abs(o - want)) <= 2 * tol, (o, want)
+
+
+def check_expm_erase(orc):
+    """v = 0: one token maps S0 to expm(-beta k k^T) S0 (closed form of the rank-1 exponential)."""
+    rng = np.random.default_rng(11)
+    cases = [(2, 3, 1.0, 0.2), (3, 2, 3.0, 0.7), (4, 4, 0.01, 0.5), (4, 1, 10.0, 0.9), (3, 3, 1e-5, 0.3),
+             (2, 2, 30.0, 0.05)]
+    for d_k, d_v, scale, beta in cases:
+        k = rng.standard_normal(d_k) * scale
+        S0 = rng.standard_normal((d_k, d_v))
+        E = scipy.linalg.expm(-beta * np.outer(k, k))
+        _, S1 = _one_token(orc, k, np.zeros(d_v), beta, S0)
+        np.testing.assert_allclose(S1, E @ S0, rtol=0, atol=1e-12 * max(1.0, np.abs(S0).max()))
+
+
+def check_van_loan(orc):
+    """Full ZOH step: expm(beta [[-A, k v^T], [0, 0]]) gives e^{-beta A} and the input integral."""
+    rng = np.random.default_rng(12)
+    cases = [(2, 2, 1.0, 0.2), (3, 4, 2.0, 0.8), (4, 3, 0.05, 0.6), (3, 3, 6.0, 0.9), (4, 2, 1e-4, 0.4)]
+    for d_k, d_v, scale, beta in cases:
+        k = rng.standard_normal(d_k) * scale
+        v = rng.standard_normal(d_v)
+        S0 = rng.standard_normal((d_k, d_v))
+        M = np.zeros((d_k + d_v, d_k + d_v))
+        M[:d_k, :d_k] = -np.outer(k, k)
+        M[:d_k, d_k:] = np.outer(k, v)
+        E = scipy.linalg.expm(beta * M)
+        want = E[:d_k, :d_k] @ S0 + E[:d_k, d_k:]
+        _, S1 = _one_token(orc, k, v, beta, S0)
+        np.testing.assert_allclose(S1, want, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
+        # the decode step is the same token update
+        q = rng.standard_normal(d_k)
+        o, S2, _ = orc.step(q[None], k[None], v[None], np.array([beta]), S0[None])
+        np.testing.assert_allclose(S2[0], want, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
+        np.testing.assert_allclose(o[0], want.T @ q, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
+
+
+def _rk4_token(S, k, v, beta, nsub):
+    A = np.outer(k, k)
+    Bm = np.outer(k, v)
+    h = beta / nsub
+
+    def f(X):
+        return -A @ X + Bm
+
+    for _ in range(nsub):
+        k1 = f(S)
+        k2 = f(S + 0.5 * h * k1)
+        k3 = f(S + 0.5 * h * k2)
+        k4 = f(S + h * k3)
+        S = S + (h / 6.0) * (k1 + 2 * k2 + 2 * k3 + k4)
+    return S
+
+
+def check_rk4_sequence(orc):
+    """A sequence of tokens: integrate the ODE over each hold interval [0, beta_t] with fine RK4,
+    read o_t = S_t^T q_t after each interval, and compare with the closed-form recurrence."""
+    rng = np.random.default_rng(13)
+    L, d_k, d_v = 10, 3, 2
+    k = _mixed_keys(rng, L, d_k, 0.1, 2.0)
+    v = rng.standard_normal((L, d_v))
+    q = rng.standard_normal((L, d_k))
+    beta = rng.uniform(0.05, 1.0, L)
+    S = rng.standard_normal((d_k, d_v)) * 0.3
+    S0 = S.copy()
+    o_ref = np.zeros((L, d_v))
+    for t in range(L):
+        S = _rk4_token(S, k[t], v[t], beta[t], 2000)
+        o_ref[t] = S.T @ q[t]
+    o, Sf, _ = orc.fwd(q[None, None], k[None, None], v[None, None], beta[None, None], S0[None, None])
+    np.testing.assert_allclose(o[0, 0], o_ref, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(Sf[0, 0], S, rtol=0, atol=1e-10)
+
+
+def check_alpha_extremes(orc):
+    """alpha against a 50-digit evaluation of (1 - e^{-beta lambda}) / lambda, and lambda = 0 -> beta."""
+    mpmath.mp.dps = 50
+    for kk in [1e-150, 1e-8, 1e-4, 0.03, 1.0, 2.2360679, 31.6, 1e3, 1e5]:
+        for beta in [1e-7, 0.2, 0.5, 0.97]:
+            a = orc.alpha(np.array([[kk]]), np.array([beta]))[0]
+            lam = mpmath.mpf(kk) ** 2
+            x = mpmath.mpf(beta) * lam
+            ref = beta if lam == 0 else -mpmath.expm1(-x) / lam
+            assert abs(a - float(ref)) <= 4e-16 * abs(float(ref)), (kk, beta, a, ref)
+    for beta in [0.0, 0.3, 1.0]:
+        assert orc.alpha(np.zeros((1, 4)), np.array([beta]))[0] == beta
+    assert orc.alpha(np.ones((1, 4)), np.array([0.0]))[0] == 0.0
+
+
+def check_euler_limit(orc):
+    """beta*lambda -> 0: alpha -> beta (one explicit Euler step = delta rule) with |alpha - beta| <= beta^2 lambda / 2."""
+    rng = np.random.default_rng(14)
+    for _ in range(40):
+        d_k = 4
+        k = rng.standard_normal(d_k) * 10.0 ** rng.uniform(-4, 0)
+        beta = rng.uniform(0.01, 1.0)
+        lam = float(k @ k)
+        a = orc.alpha(k[None], np.array([beta]))[0]
+        slack = 8e-16 * beta  # rounding of the difference beta - alpha
+        assert -slack <= beta - a <= 0.5 * beta * beta * lam + slack
+        # and from the other side: the second-order term is not dropped
+        assert beta - a >= 0.5 * beta * beta * lam * (1 - beta * lam / 3.0) - slack
+
+
+def check_directional_decay(orc):
+    """Memory along k relaxes by e^{-beta lambda} towards v; the part orthogonal to k is untouched."""
+    rng = np.random.default_rng(15)
+    for scale in [0.01, 0.5, 1.0, 4.0, 20.0]:
+        d_k, d_v = 5, 3
+        k = rng.standard_normal(d_k) * scale
+        v = rng.standard_normal(d_v)
+        beta = rng.uniform(0.1, 1.0)
+        S0 = rng.standard_normal((d_k, d_v))
+        _, S1 = _one_token(orc, k, v, beta, S0)
+        lam = float(k @ k)
+        decay = np.exp(-beta * lam)
+        np.testing.assert_allclose(k @ S1, decay * (k @ S0) + (1 - decay) * v,
+                                   rtol=0, atol=1e-12 * max(1.0, lam) * max(1.0, np.abs(S0).max()))
+        u = rng.standard_normal(d_k)
+        u -= (u @ k) / lam * k
+        np.testing.assert_allclose(u @ S1, u @ S0, rtol=0, atol=1e-12 * max(1.0, scale))
+
+
+def check_stiff_overwrite(orc):
+    """beta*lambda >> 1: the memory along k is overwritten, k^T S_t = v_t^T."""
+    rng = np.random.default_rng(16)
+    for scale in [8.0, 30.0, 300.0]:
+        d_k, d_v = 4, 3
+        k = rng.standard_normal(d_k) * scale
+        v = rng.standard_normal(d_v)
+        _, S1 = _one_token(orc, k, v, 0.9, rng.standard_normal((d_k, d_v)))
+        np.testing.assert_allclose(k @ S1, v, rtol=0, atol=1e-9)
+
+
+def check_contractive(orc):
+    """v = 0: ||S_t||_F never grows (eigenvalues of e^{-beta k k^T} are e^{-beta lambda} and 1)."""
+    rng = np.random.default_rng(17)
+    L, d_k, d_v = 40, 4, 3
+    k = _mixed_keys(rng, L, d_k, 0.01, 10.0)
+    beta = rng.uniform(0.0, 1.0, L)
+    S = rng.standard_normal((d_k, d_v))
+    prev = np.linalg.norm(S)
+    for t in range(L):
+        _, S = _one_token(orc, k[t], np.zeros(d_v), beta[t], S)
+        cur = np.linalg.norm(S)
+        assert cur <= prev * (1 + 1e-14)
+        prev = cur
+
+
+def check_linearity(orc):
+    """For fixed q, k, beta the outputs and state are jointly linear in (S0, V)."""
+    rng = np.random.default_rng(18)
+    B, H, L, d_k, d_v = 1, 2, 17, 4, 3
+    q = rng.standard_normal((B, H, L, d_k))
+    k = rng.standard_normal((B, H, L, d_k))
+    beta = rng.uniform(0, 1, (B, H, L))
+    va, vb = rng.standard_normal((2, B, H, L, d_v))
+    sa, sb = rng.standard_normal((2, B, H, d_k, d_v))
+    c = -1.7
+    oa, Sa, _ = orc.fwd(q, k, va, beta, sa)
+    ob, Sb, _ = orc.fwd(q, k, vb, beta, sb)
+    oc, Sc, _ = orc.fwd(q, k, va + c * vb, beta, sa + c * sb)
+    np.testing.assert_allclose(oc, oa + c * ob, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(Sc, Sa + c * Sb, rtol=0, atol=1e-11)
+
+
+def _chunked_model(q, k, v, beta, S0, C):
+    """Independent fp64 model of the chunkwise WY/UT form (one head):
+    A = strict_tril(diag(alpha) K K^T), T = (I + A)^{-1}, W = T diag(alpha) K, U = T diag(alpha) V,
+    Delta = U - W S, O = Q S + tril(Q K^T) Delta, S <- S + K^T Delta."""
+    L = k.shape[0]
+    lam = np.sum(k * k, axis=-1)
+    x = beta * lam
+    alpha = np.where(x == 0, beta, -np.expm1(-x) / np.where(lam == 0, 1.0, lam))
+    S = S0.copy()
+    o = np.zeros((L, v.shape[1]))
+    for t0 in range(0, L, C):
+        sl = slice(t0, min(L, t0 + C))
+        K, Q, V, a = k[sl], q[sl], v[sl], alpha[sl]
+        n = K.shape[0]
+        A = np.tril(a[:, None] * (K @ K.T), -1)
+        T = np.linalg.inv(np.eye(n) + A)
+        Wm = T @ (a[:, None] * K)
+        U = T @ (a[:, None] * V)
+        D = U - Wm @ S
+        o[sl] = Q @ S + np.tril(Q @ K.T) @ D
+        S = S + K.T @ D
+    return o, S
+
+
+def check_chunk_identity(orc):
+    """The chunkwise-parallel form reaches the recurrence's result for every chunk size."""
+    rng = np.random.default_rng(19)
+    L, d_k, d_v = 100, 8, 6
+    k = _mixed_keys(rng, L, d_k, 1e-3, 6.0)
+    q = rng.standard_normal((L, d_k))
+    v = rng.standard_normal((L, d_v))
+    beta = rng.uniform(0, 1, L)
+    S0 = rng.standard_normal((d_k, d_v)) * 0.1
+    o, Sf, _ = orc.fwd(q[None, None], k[None, None], v[None, None], beta[None, None], S0[None, None])
+    for C in [1, 2, 4, 16, 64, L]:
+        oc, Sc = _chunked_model(q, k, v, beta, S0, C)
+        np.testing.assert_allclose(o[0, 0], oc, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(Sf[0, 0], Sc, rtol=0, atol=1e-11)
+
+
+def check_state_chaining(orc):
+    """fwd over [0, L) equals fwd over [0, L1) then [L1, L) from its final state; prefill then decode steps."""
+    rng = np.random.default_rng(20)
+    B, H, L, d_k, d_v = 2, 2, 33, 5, 4
+    q = rng.standard_normal((B, H, L, d_k))
+    k = rng.standard_normal((B, H, L, d_k))
+    v = rng.standard_normal((B, H, L, d_v))
+    beta = rng.uniform(0, 1, (B, H, L))
+    S0 = rng.standard_normal((B, H, d_k, d_v))
+    o, Sf, _ = orc.fwd(q, k, v, beta, S0)
+    L1 = 20
+    o1, S1, _ = orc.fwd(q[:, :, :L1], k[:, :, :L1], v[:, :, :L1], beta[:, :, :L1], S0)
+    o2, S2, _ = orc.fwd(q[:, :, L1:], k[:, :, L1:], v[:, :, L1:], beta[:, :, L1:], S1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S2, Sf, rtol=0, atol=1e-12)
+    S = S1.reshape(B * H, d_k, d_v)
+    for t in range(L1, L):
+        ot, S, _ = orc.step(q[:, :, t].reshape(B * H, d_k), k[:, :, t].reshape(B * H, d_k),
+                            v[:, :, t].reshape(B * H, d_v), beta[:, :, t].reshape(B * H), S)
+        np.testing.assert_allclose(ot.reshape(B, H, d_v), o[:, :, t], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S.reshape(B, H, d_k, d_v), Sf, rtol=0, atol=1e-12)
+
+
+def check_zero_initial_state(orc):
+    """An absent initial state is the zero matrix."""
+    rng = np.random.default_rng(21)
+    q, k = rng.standard_normal((2, 1, 2, 9, 4))
+    v = rng.standard_normal((1, 2, 9, 3))
+    beta = rng.uniform(0, 1, (1, 2, 9))
+    o1, S1, _ = orc.fwd(q, k, v, beta, None)
+    o2, S2, _ = orc.fwd(q, k, v, beta, np.zeros((1, 2, 4, 3)))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+PINS = [check_worked_example, check_expm_erase, check_van_loan, check_rk4_sequence, check_alpha_extremes,
+        check_euler_limit, check_directional_decay, check_stiff_overwrite, check_contractive,
+        check_linearity, check_chunk_identity, check_state_chaining, check_zero_initial_state]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(oracle.default())
+
+
+def test_oracle_mpmath_recurrence():
+    """Rounding of the fp64 recurrence: a 40-digit mpmath run of the same tokens agrees to ~1e-14."""
+    mpmath.mp.dps = 40
+    rng = np.random.default_rng(22)
+    L, d_k, d_v = 24, 4, 3
+    k = _mixed_keys(rng, L, d_k, 1e-3, 8.0)
+    q = rng.standard_normal((L, d_k))
+    v = rng.standard_normal((L, d_v))
+    beta = rng.uniform(0, 1, L)
+    o, Sf, _ = oracle.fwd(q[None, None], k[None, None], v[None, None], beta[None, None])
+    S = mpmath.zeros(d_k, d_v)
+    for t in range(L):
+        kt = mpmath.matrix([mpmath.mpf(x) for x in k[t]])
+        lam = sum(x * x for x in kt)
+        a = (1 - mpmath.exp(-mpmath.mpf(beta[t]) * lam)) / lam
+        vt = mpmath.matrix([mpmath.mpf(x) for x in v[t]])
+        kS = kt.T * S
+        S = S - a * kt * kS + a * kt * vt.T
+        ot = S.T * mpmath.matrix([mpmath.mpf(x) for x in q[t]])
+        for j in range(d_v):
+            assert abs(o[0, 0, t, j] - float(ot[j])) <= 1e-13
+    for i in range(d_k):
+        for j in range(d_v):
+            assert abs(Sf[0, 0, i, j] - float(S[i, j])) <= 1e-13
+
+
+def test_oracle_threads_do_not_change_results():
+    w = W.workload(2, B=2, H=2, L=96)
+    x = W.make_fwd_inputs(w)
+    o1, s1, n1 = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["initial_state"], n_threads=1)
+    o4, s4, n4 = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["initial_state"], n_threads=4)
+    assert n1 == 1
+    np.testing.assert_array_equal(o1, o4)
+    np.testing.assert_array_equal(s1, s4)
+
+
+# ----------------------------------------------------------------------------------------------
+# the pins must be able to fail: plausible mistakes planted in a copy of the oracle's C source
+# ----------------------------------------------------------------------------------------------
+
+MUTANTS = {
+    "erase_sign": ("S[(size_t)i * d_v + j] - alpha * k[i] * kS[j]", "S[(size_t)i * d_v + j] + alpha * k[i] * kS[j]"),
+    "write_dropped": ("- alpha * k[i] * kS[j] + alpha * k[i] * v[j];", "- alpha * k[i] * kS[j];"),
+    "euler_alpha": ("return -expm1(-beta * lambda) / lambda;", "return beta;"),
+    "no_divide": ("return -expm1(-beta * lambda) / lambda;", "return -expm1(-beta * lambda);"),
+    "lambda_off_by_one": ("for (int i = 0; i < d_k; ++i)\n        lambda", "for (int i = 1; i < d_k; ++i)\n        lambda"),
+    "readout_with_key": ("o[j] += S[(size_t)i * d_v + j] * q[i];", "o[j] += S[(size_t)i * d_v + j] * k[i];"),
+    "readout_before_update": ("o[j] += S[(size_t)i * d_v + j] * q[i];",
+                              "o[j] += (S[(size_t)i * d_v + j] + alpha * k[i] * kS[j] - alpha * k[i] * v[j]) * q[i];"),
+    "exp_sign": ("return -expm1(-beta * lambda) / lambda;", "return expm1(beta * lambda) / lambda;"),
+    "initial_state_ignored": ("memcpy(S, initial_state + bh * ssz, sizeof(double) * ssz);",
+                              "memset(S, 0, sizeof(double) * ssz);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutants(name):
+    src_path = os.path.join(os.path.dirname(oracle.__file__), "efla_oracle.c")
+    src = open(src_path).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, "mutation anchor not found: " + name
+    tmp = tempfile.mkdtemp(prefix="efla_mutant_")
+    try:
+        mpath = os.path.join(tmp, "mutant.c")
+        with open(mpath, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.build(force=True, src=mpath, out=os.path.join(tmp, "libmutant.so"))
+        orc = oracle.Oracle(lib)
+        failed = []
+        for pin in PINS:
+            try:
+                with np.errstate(all="ignore"):
+                    pin(orc)
+            except AssertionError:
+                failed.append(pin.__name__)
+        assert failed, "no pin detects mutant " + name
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
