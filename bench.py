@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the EFLA hot path on one MI355X.
+
+One step = one chunked forward of the LM-layer workload (B8 H16 L4096 d_k = d_v = 128, bf16 q/k/v/o,
+fp32 beta and state, chunk 64, zero initial state, final state returned): the exact gate, the
+intra-chunk UT transform and the inter-chunk state pass all run inside the fused kernel.
+The batched decode workload (256 sequences x 32 heads, d 128, 512 MiB fp32 state, 64 dependent
+one-token steps, one launch per step) is timed in the same run and reported under "decode".
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+
+Prints one JSON line.  Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EFLA chunked-fwd tokens/s at B8 H16 L4096 d128; % MFMA peak; decode HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+
+
+def fwd_algorithmic(B, H, L, dk, dv, C, esize=2):
+    """Bytes and flops one chunked forward must move / do, counted from the algorithm.
+
+    Bytes: q, k (d_k each), v, o (d_v each) in the storage type and beta (fp32) once per token-head,
+    plus the fp32 final state once per head.
+    Flops per chunk (dense products counted 2 per multiply-add, triangular ones by their lower half):
+    K S and Q S 2*(2 C dk dv), K^T Delta 2 C dk dv, lower(K K^T) and lower(Q K^T) 2*(C^2 dk),
+    T diag(alpha) R and lower(Q K^T) Delta 2*(C^2 dv), T by substitution C^3/3.
+    """
+    tok = B * H * L
+    nbytes = tok * ((2 * dk + 2 * dv) * esize + 4) + B * H * dk * dv * 4
+    per_chunk = 6 * C * dk * dv + 2 * C * C * dk + 2 * C * C * dv + C ** 3 / 3.0
+    flops = per_chunk * (tok / C)
+    return nbytes, flops
+
+
+def decode_algorithmic(NH, dk, dv, esize=2):
+    """Bytes per decode step: the fp32 state read and written once, q, k, v, o in the storage type, beta."""
+    return NH * (2 * dk * dv * 4 + (2 * dk + 2 * dv) * esize + 4)
+
+
+def run_forward(efla, W, torch, steps, warmup):
+    w = W.workload(3)
+    x = W.make_fwd_inputs(w)
+
+    def dev(a):
+        return torch.from_numpy(W.bf16_bits(a)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    beta = torch.from_numpy(x["beta"]).cuda()
+    o = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    del x
+    for _ in range(warmup):
+        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    assert torch.isfinite(S).all().item(), "non-finite final state"
+    wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
+    return w, ms, dict(workgroups=wg, slab_width=slab, lds_bytes=lds)
+
+
+def run_decode(efla, W, torch, warmup=3):
+    w = W.workload(5)
+    S = torch.from_numpy(W.make_decode_state(w)).cuda()
+    toks = []
+    for s in range(w.steps):
+        t = W.make_decode_token(w, s)
+        toks.append(tuple(torch.from_numpy(W.bf16_bits(t[n])).view(torch.bfloat16).cuda() for n in ("q", "k", "v"))
+                    + (torch.from_numpy(t["beta"]).cuda(),))
+    o = torch.empty((w.NH, w.d_v), dtype=torch.bfloat16, device="cuda")
+    scratch = S.clone()
+    for i in range(warmup):
+        efla.recurrent_step(*toks[i], scratch, out=o)
+    del scratch
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.steps + 1)]
+    ev[0].record()
+    for s in range(w.steps):
+        efla.recurrent_step(*toks[s], S, out=o)
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(w.steps)]
+    assert torch.isfinite(S).all().item(), "non-finite decode state"
+    return w, step_ms
+
+
+def cpu_baseline(W, max_threads):
+    """The fp64 oracle on the full LM-layer forward (all heads, full length) on the host cores."""
+    import oracle
+
+    w = W.workload(3)
+    x = W.make_fwd_inputs(w)
+    t0 = time.perf_counter()
+    _, _, used = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], None, n_threads=max_threads, want_o=True,
+                            want_state=True)
+    dt = time.perf_counter() - t0
+    return dict(value=w.B * w.L / dt, unit="tokens/s", cores=int(used), kind="oracle",
+                sample="full LM-layer forward B8 H16 L4096 d128 (all 128 heads), fp64 token-by-token, %.1f s" % dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the forward and decode workloads shard across GPUs by independent "
+              "heads with no communication, so a multi-GPU figure would be N independent copies; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_flow_delta_amd as efla
+    from exact_flow_delta_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    efla.load_library()
+
+    w, ms, plan = run_forward(efla, W, torch, args.steps, args.warmup)
+    tokens_per_s = w.B * w.L / (ms * 1e-3)
+    nbytes, flops = fwd_algorithmic(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
+    achieved_gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "lm_layer_fwd", "B": w.B, "H": w.H, "L": w.L, "d_k": w.d_k, "d_v": w.d_v,
+                   "chunk": w.chunk, "io": "bf16", "state": "fp32", "launch": plan},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "chunk_fwd_kernel<bf16,128,64,64>", "bytes_per_launch": nbytes},
+        "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops},
+    }
+    if not args.no_decode:
+        dw, step_ms = run_decode(efla, W, torch)
+        med = statistics.median(step_ms)
+        dbytes = decode_algorithmic(dw.NH, dw.d_k, dw.d_v)
+        gbs = dbytes / (med * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": "decode 256 seq x 32 heads d128, fp32 state, 64 steps",
+            "median_step_ms": round(med, 5), "total_ms": round(sum(step_ms), 4),
+            "tokens_per_s": round(dw.B / (med * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "recurrent_step_kernel<bf16,128,128>", "bytes_per_launch": dbytes},
+        }
+    if not args.no_cpu:
+        threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
+        result["cpu_baseline"] = cpu_baseline(W, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

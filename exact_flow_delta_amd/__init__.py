@@ -1,0 +1,207 @@
+"""Error-Free Linear Attention (EFLA) on AMD Instinct MI355X -- Python binding of libefla.so.
+
+Argument marshalling only: every step of the operator runs in the HIP kernels of ``libefla.so``
+(built in-tree by ``python -m exact_flow_delta_amd.build``).  PyTorch supplies device memory and
+the current stream; nothing here computes on the CPU, and there is no fallback path: if the
+library is missing, every call raises.
+
+    o, S = chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_size=64)
+    o    = recurrent_step(q, k, v, beta, state)          # state updated in place
+    a    = alpha(k, beta)
+
+The operator ("Exact Flow Linear Attention" (gist.science), Metodologia items 1-3; "Error-Free
+Linear Attention is a Free Lunch" (howistudyai.com), Steps 1-4):
+    alpha_t = (1 - exp(-beta_t ||k_t||^2)) / ||k_t||^2
+    S_t     = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T
+    o_t     = S_t^T q_t
+Layouts: q, k [B,H,L,d_k]; v, o [B,H,L,d_v]; beta [B,H,L] fp32; state [B,H,d_k,d_v] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["EflaError", "alpha", "chunk_fwd", "recurrent_step", "chunk_plan", "library_path", "load_library"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libefla.so")
+_lib = None
+
+EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_NO_DEVICE, EFLA_ERR_HIP = range(5)
+EFLA_F32, EFLA_BF16 = 0, 1
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+
+
+class EflaError(RuntimeError):
+    """A non-OK status from libefla.so."""
+
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        msg = "%s failed: %s" % (where, _status_string(status))
+        if detail:
+            msg += " -- " + detail
+        super().__init__(msg)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libefla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libefla.so is not built (%s); run `python -m exact_flow_delta_amd.build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.efla_alpha.argtypes = [_vp, _i32, _vp, _vp, _i64, _i32, _vp]
+    lib.efla_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    lib.efla_chunk_fwd_slab.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    lib.efla_recurrent_step.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp]
+    lib.efla_chunk_fwd_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+    for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan"):
+        getattr(lib, fn).restype = _i32
+    lib.efla_status_string.argtypes = [_i32]
+    lib.efla_status_string.restype = ctypes.c_char_p
+    lib.efla_last_error.argtypes = []
+    lib.efla_last_error.restype = ctypes.c_char_p
+    lib.efla_version.argtypes = []
+    lib.efla_version.restype = _i32
+    _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load_library().efla_status_string(status).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "status %d" % status
+
+
+def _check(status: int, where: str):
+    if status != EFLA_OK:
+        detail = load_library().efla_last_error().decode() if status == EFLA_ERR_HIP else ""
+        raise EflaError(status, where, detail)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return EFLA_BF16
+    if t.dtype == torch.float32:
+        return EFLA_F32
+    raise TypeError("q, k, v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s); libefla has no CPU path" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device: torch.device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def alpha(k: torch.Tensor, beta: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Exact gate alpha for keys k [..., d_k] (fp32/bf16) and steps beta [...] (fp32); returns fp32 [...]."""
+    lib = load_library()
+    _dev_tensor(k, "k")
+    _dev_tensor(beta, "beta")
+    if beta.dtype != torch.float32 or tuple(beta.shape) != tuple(k.shape[:-1]):
+        raise ValueError("beta must be float32 with shape k.shape[:-1]")
+    if out is None:
+        out = torch.empty(beta.shape, dtype=torch.float32, device=k.device)
+    _dev_tensor(out, "out")
+    _check(lib.efla_alpha(_ptr(k), _dtype_code(k), _ptr(beta), _ptr(out), beta.numel(), k.shape[-1],
+                          _stream(k.device)), "efla_alpha")
+    return out
+
+
+def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_size=64, dv_slab=0,
+              out=None, final_state=None):
+    """Chunkwise-parallel EFLA forward over [B,H,L,*] inputs.
+
+    Returns (o [B,H,L,d_v] in the input dtype, final state [B,H,d_k,d_v] fp32 or None).
+    ``final_state`` may be passed (and may be ``initial_state`` itself) to receive the state in place.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _dev_tensor(t, name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    B, H, L, d_k = k.shape
+    d_v = v.shape[-1]
+    if tuple(q.shape) != (B, H, L, d_k) or tuple(v.shape[:3]) != (B, H, L):
+        raise ValueError("q, k, v shapes disagree: %s %s %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, L):
+        raise ValueError("beta must be float32 [B,H,L]")
+    if initial_state is not None:
+        _dev_tensor(initial_state, "initial_state")
+        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (B, H, d_k, d_v):
+            raise ValueError("initial_state must be float32 [B,H,d_k,d_v]")
+    if out is None:
+        out = torch.empty((B, H, L, d_v), dtype=v.dtype, device=v.device)
+    _dev_tensor(out, "out")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=v.device)
+    if final_state is not None:
+        _dev_tensor(final_state, "final_state")
+        if final_state.dtype != torch.float32 or tuple(final_state.shape) != (B, H, d_k, d_v):
+            raise ValueError("final_state must be float32 [B,H,d_k,d_v]")
+    _check(lib.efla_chunk_fwd_slab(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                   _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
+                                   int(dv_slab), _stream(v.device)), "efla_chunk_fwd")
+    return out, final_state
+
+
+def recurrent_step(q, k, v, beta, state, out=None):
+    """One decode token for [NH,*] inputs (or [N,H,*]); ``state`` [..., d_k, d_v] fp32 is updated in place.
+
+    Returns o [..., d_v] in the input dtype.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("state", state)):
+        _dev_tensor(t, name)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    d_k = k.shape[-1]
+    d_v = v.shape[-1]
+    lead = tuple(k.shape[:-1])
+    NH = k.numel() // d_k
+    if tuple(q.shape) != tuple(k.shape) or tuple(v.shape[:-1]) != lead or tuple(beta.shape) != lead:
+        raise ValueError("q, k, v, beta leading shapes disagree")
+    if state.dtype != torch.float32 or tuple(state.shape) != lead + (d_k, d_v):
+        raise ValueError("state must be float32 %s" % (lead + (d_k, d_v),))
+    if beta.dtype != torch.float32:
+        raise ValueError("beta must be float32")
+    if out is None:
+        out = torch.empty(lead + (d_v,), dtype=v.dtype, device=v.device)
+    _dev_tensor(out, "out")
+    _check(lib.efla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(state), _ptr(out),
+                                   NH, d_k, d_v, _stream(v.device)), "efla_recurrent_step")
+    return out
+
+
+def chunk_plan(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, dv_slab=0):
+    """(workgroups, slab width, LDS bytes) that chunk_fwd would launch; host only."""
+    lib = load_library()
+    wg, sw, lds = _i32(), _i32(), _i32()
+    code = EFLA_BF16 if dtype == torch.bfloat16 else EFLA_F32
+    _check(lib.efla_chunk_fwd_plan(B, H, L, d_k, d_v, chunk, code, dv_slab, ctypes.byref(wg), ctypes.byref(sw),
+                                   ctypes.byref(lds)), "efla_chunk_fwd_plan")
+    return wg.value, sw.value, lds.value

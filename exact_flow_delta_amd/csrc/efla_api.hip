@@ -1,0 +1,196 @@
+// efla_api.hip -- the exported C ABI of libefla.so: argument checks, launch planning, error mapping.
+// Every check runs before anything is enqueued; on error no output is touched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "efla.h"
+#include "efla_chunk_fwd.hpp"
+#include "efla_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+efla_status fail_hip(hipError_t e, const char* where) {
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%s)", where, hipGetErrorName(e), hipGetErrorString(e));
+    return EFLA_ERR_HIP;
+}
+
+bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+bool valid_dtype(efla_dtype dt) { return dt == EFLA_F32 || dt == EFLA_BF16; }
+size_t esize(efla_dtype dt) { return dt == EFLA_BF16 ? 2 : 4; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// do [a, a+na) and [b, b+nb) share a byte?  (null or empty ranges never overlap)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+efla_status device_present() {
+    int n = 0;
+    const hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        snprintf(g_last_error, sizeof(g_last_error), "no HIP device visible (%s)",
+                 e != hipSuccess ? hipGetErrorName(e) : "0 devices");
+        return EFLA_ERR_NO_DEVICE;
+    }
+    return EFLA_OK;
+}
+
+int lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) {
+    const int b = dt == EFLA_BF16 ? efla::chunk_layout_bytes<2>(d_k, chunk, dvs)
+                                  : efla::chunk_layout_bytes<4>(d_k, chunk, dvs);
+    return b <= efla::kMaxLdsBytes ? b : -1;
+}
+
+// Slab width: the widest (fewest waves re-reading the chunk data) that still gives the GPU enough
+// workgroups; narrower when B*H is small so that more compute units carry a slab.
+int auto_slab(int64_t BH, int d_k, int d_v, int chunk, efla_dtype dt) {
+    int dvs = d_v < 64 ? d_v : 64;
+    while (dvs > 16 && BH * (d_v / dvs) < 256) dvs /= 2;
+    while (dvs > 16 && lds_bytes(dt, d_k, chunk, dvs) < 0) dvs /= 2;
+    return dvs;
+}
+
+efla_status check_chunk_sizes(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, int dv_slab,
+                              int* dvs_out) {
+    if (!valid_dtype(dt)) return EFLA_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || L < 0) return EFLA_ERR_INVALID_ARG;
+    if ((int64_t)B * H > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
+    if (dv_slab != 0 && dv_slab != 16 && dv_slab != 32 && dv_slab != 64) return EFLA_ERR_UNSUPPORTED;
+    if (dv_slab != 0 && (dv_slab > d_v || d_v % dv_slab != 0)) return EFLA_ERR_UNSUPPORTED;
+    const int dvs = dv_slab ? dv_slab : auto_slab((int64_t)B * H, d_k, d_v, chunk, dt);
+    if (lds_bytes(dt, d_k, chunk, dvs) < 0) return EFLA_ERR_UNSUPPORTED;
+    if (efla::chunk_grid((int)((int64_t)B * H), d_v, dvs) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    *dvs_out = dvs;
+    return EFLA_OK;
+}
+
+}  // namespace
+
+namespace efla {
+int chunk_lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) { return lds_bytes(dt, d_k, chunk, dvs); }
+int64_t chunk_grid(int BH, int d_v, int dvs) { return (int64_t)((BH + 7) / 8) * 8 * (d_v / dvs); }
+}  // namespace efla
+
+extern "C" {
+
+int efla_version(void) { return 10000; }
+
+const char* efla_status_string(efla_status s) {
+    switch (s) {
+        case EFLA_OK: return "EFLA_OK";
+        case EFLA_ERR_INVALID_ARG: return "EFLA_ERR_INVALID_ARG: invalid argument";
+        case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED: size or type combination not built";
+        case EFLA_ERR_NO_DEVICE: return "EFLA_ERR_NO_DEVICE: no HIP device";
+        case EFLA_ERR_HIP: return "EFLA_ERR_HIP: HIP runtime error";
+    }
+    return "EFLA: unknown status";
+}
+
+const char* efla_last_error(void) { return g_last_error; }
+
+efla_status efla_alpha(const void* k, efla_dtype k_dtype, const float* beta, float* alpha, int64_t n_tokens, int d_k,
+                       void* stream) {
+    if (!valid_dtype(k_dtype) || n_tokens < 0) return EFLA_ERR_INVALID_ARG;
+    if (!valid_dim(d_k)) return EFLA_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return EFLA_OK;
+    if (!k || !beta || !alpha) return EFLA_ERR_INVALID_ARG;
+    if (!aligned(k, 16) || !aligned(beta, 4) || !aligned(alpha, 4)) return EFLA_ERR_INVALID_ARG;
+    const size_t nk = (size_t)n_tokens * d_k * esize(k_dtype), nb = (size_t)n_tokens * 4;
+    if (overlap(alpha, nb, k, nk) || overlap(alpha, nb, beta, nb)) return EFLA_ERR_INVALID_ARG;
+    // keys per workgroup is at least 8 (fp32, d_k = 128)
+    if (n_tokens / 8 + 1 > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    efla_status st = device_present();
+    if (st != EFLA_OK) return st;
+    const hipError_t e = efla::launch_alpha(k, k_dtype, beta, alpha, n_tokens, d_k, (hipStream_t)stream);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_alpha launch");
+}
+
+efla_status efla_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int dv_slab,
+                                int* workgroups, int* slab_width, int* lds) {
+    int dvs = 0;
+    const efla_status st = check_chunk_sizes(B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
+    if (st != EFLA_OK) return st;
+    if (workgroups) *workgroups = (int)efla::chunk_grid(B * H, d_v, dvs);
+    if (slab_width) *slab_width = dvs;
+    if (lds) *lds = lds_bytes(dtype, d_k, chunk, dvs);
+    return EFLA_OK;
+}
+
+efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
+                                int d_v, int chunk, int dv_slab, void* stream) {
+    int dvs = 0;
+    efla_status st = check_chunk_sizes(B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
+    if (st != EFLA_OK) return st;
+    const int64_t BH = (int64_t)B * H;
+    const size_t es = esize(dtype);
+    const size_t nq = (size_t)BH * L * d_k * es, nv = (size_t)BH * L * d_v * es, nb = (size_t)BH * L * 4;
+    const size_t ns = (size_t)BH * d_k * d_v * 4;
+    if (L > 0 && BH > 0) {
+        if (!q || !k || !v || !beta || !o) return EFLA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(beta, 4))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+        return EFLA_ERR_INVALID_ARG;
+    // o overlaps nothing; the final state overlaps no input; initial and final state are identical or disjoint
+    if (overlap(o, nv, q, nq) || overlap(o, nv, k, nq) || overlap(o, nv, v, nv) || overlap(o, nv, beta, nb) ||
+        overlap(o, nv, initial_state, ns) || overlap(o, nv, final_state, ns))
+        return EFLA_ERR_INVALID_ARG;
+    if (overlap(final_state, ns, q, nq) || overlap(final_state, ns, k, nq) || overlap(final_state, ns, v, nv) ||
+        overlap(final_state, ns, beta, nb))
+        return EFLA_ERR_INVALID_ARG;
+    if ((const void*)initial_state != (const void*)final_state && overlap(initial_state, ns, final_state, ns))
+        return EFLA_ERR_INVALID_ARG;
+    if (BH == 0) return EFLA_OK;
+    if (L == 0 && !final_state) return EFLA_OK;
+    st = device_present();
+    if (st != EFLA_OK) return st;
+    efla::ChunkArgs a{q, k, v, beta, o, initial_state, final_state, (int)BH, L, d_k, d_v, chunk, dvs};
+    const hipError_t e = dtype == EFLA_BF16 ? efla::launch_chunk_fwd_bf16(a, (hipStream_t)stream)
+                                            : efla::launch_chunk_fwd_f32(a, (hipStream_t)stream);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd launch");
+}
+
+efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype, void* o,
+                           const float* initial_state, float* final_state, int B, int H, int L, int d_k, int d_v,
+                           int chunk, void* stream) {
+    return efla_chunk_fwd_slab(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, 0,
+                               stream);
+}
+
+efla_status efla_recurrent_step(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                float* state, void* o, int64_t NH, int d_k, int d_v, void* stream) {
+    if (!valid_dtype(dtype) || NH < 0) return EFLA_ERR_INVALID_ARG;
+    if (!valid_dim(d_k) || !valid_dim(d_v)) return EFLA_ERR_UNSUPPORTED;
+    if (NH == 0) return EFLA_OK;
+    if (NH > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !beta || !state || !o) return EFLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16) ||
+        !aligned(beta, 4))
+        return EFLA_ERR_INVALID_ARG;
+    const size_t es = esize(dtype);
+    const size_t nq = (size_t)NH * d_k * es, nv = (size_t)NH * d_v * es, nb = (size_t)NH * 4;
+    const size_t ns = (size_t)NH * d_k * d_v * 4;
+    if (overlap(o, nv, q, nq) || overlap(o, nv, k, nq) || overlap(o, nv, v, nv) || overlap(o, nv, beta, nb) ||
+        overlap(o, nv, state, ns))
+        return EFLA_ERR_INVALID_ARG;
+    if (overlap(state, ns, q, nq) || overlap(state, ns, k, nq) || overlap(state, ns, v, nv) ||
+        overlap(state, ns, beta, nb))
+        return EFLA_ERR_INVALID_ARG;
+    const efla_status st = device_present();
+    if (st != EFLA_OK) return st;
+    const hipError_t e = efla::launch_recurrent_step(q, k, v, beta, dtype, state, o, NH, d_k, d_v, (hipStream_t)stream);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_recurrent_step launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// efla_common.hpp -- shared device helpers of the EFLA HIP kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used by every kernel here (16x16 output tiles, 64-wide wavefront):
+//   lane = 16*g + r with r = lane & 15, g = lane >> 4.
+//   An A operand fragment of a 16x16 block (rows m, reduction index k) is a "quad": lane (r, g)
+//   holds A[r][4g .. 4g+3].  A B operand fragment (rows k, columns n) is a quad too: lane (r, g)
+//   holds B[4g .. 4g+3][r].  The 16x16 fp32 accumulator D has lane (r, g) holding D[4g+i][r],
+//   i = 0..3 -- i.e. an accumulator tile is already a B-operand quad of the same matrix.
+// The matrix instructions reduce over whatever k each (lane group, slot) carries, as long as the
+// A and B fragments agree, so two quads (two 16-wide k blocks) feed one 16x16x32 bf16 instruction,
+// a single quad goes through 16x16x32 with a zero second half, and one fp32 quad feeds four 16x16x4
+// fp32 instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace efla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+
+// ------------------------------------------------------------------------------------------------
+// The exact gate.  alpha = (1 - e^{-beta lambda}) / lambda, evaluated as -expm1(-x)/lambda with
+// x = beta*lambda so that small x does not cancel; x == 0 (lambda == 0 or beta == 0) gives the
+// limit beta.  Large x: expm1 -> -1 and alpha -> 1/lambda.
+// ("Exact Flow Linear Attention", Metodologia item 3; "Error-Free Linear Attention is a Free
+// Lunch", Step 1.)
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float exact_alpha(float beta, float lambda) {
+    const float x = beta * lambda;
+    if (x == 0.0f) return beta;
+    return -expm1f(-x) / lambda;
+}
+
+// ------------------------------------------------------------------------------------------------
+// element conversion
+// ------------------------------------------------------------------------------------------------
+template <typename E> __device__ __forceinline__ float to_f32(E x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+template <typename E> __device__ __forceinline__ E from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// 16-byte vector of storage elements (8 bf16 or 4 fp32)
+template <typename E> struct Vec16;
+template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
+
+// ------------------------------------------------------------------------------------------------
+// matrix-core policy per operand type
+// ------------------------------------------------------------------------------------------------
+template <typename E> struct Mma;
+
+template <> struct Mma<bf16> {
+    typedef bf16x4 quad;
+    static __device__ __forceinline__ quad cvt(f32x4 v) {
+        quad q;
+        q[0] = (bf16)v[0]; q[1] = (bf16)v[1]; q[2] = (bf16)v[2]; q[3] = (bf16)v[3];
+        return q;
+    }
+    static __device__ __forceinline__ quad cvt_neg(f32x4 v) { return cvt(-v); }
+    static __device__ __forceinline__ quad zero() { return cvt(f32x4{0.f, 0.f, 0.f, 0.f}); }
+    // acc += [A0 A1](16 x 32) * [B0; B1](32 x 16)
+    static __device__ __forceinline__ void mma2(f32x4& acc, quad a0, quad a1, quad b0, quad b1) {
+        bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    // acc += A(16 x 16) * B(16 x 16), issued as 16x16x32 with a zero upper k half.  Every accumulator
+    // chain stays on the one instruction shape: a 16x16x16 bf16 instruction reading, as its C operand,
+    // the result of a 16x16x32 bf16 instruction a few cycles earlier gave wrong sums with this
+    // toolchain (the generated code left too few wait states between the two shapes).
+    static __device__ __forceinline__ void mma1(f32x4& acc, quad a, quad b) { mma2(acc, a, zero(), b, zero()); }
+    static __device__ __forceinline__ quad lds_quad(const bf16* p) {  // 8-byte aligned
+        return *reinterpret_cast<const quad*>(p);
+    }
+    static __device__ __forceinline__ void lds_store_quad(bf16* p, quad q) { *reinterpret_cast<quad*>(p) = q; }
+    // Column quad of a row-major 16x16 LDS block X (leading dimension ld): lane (r, g) receives
+    // X[4g .. 4g+3][r].  One transposing LDS read: within each 16-lane group, lane i gets element i%4
+    // of the 8-byte runs addressed by lanes 4e + i/4 (e = 0..3), so lane 16g + 4e + c points at
+    // X[4g + e][4c .. 4c+3].  The per-lane offset (4g + e) * ld + 4c comes from tr_offset().
+    static __device__ __forceinline__ int tr_offset(int lane, int ld) {
+        const int j = lane & 15;
+        return (4 * (lane >> 4) + (j >> 2)) * ld + 4 * (j & 3);
+    }
+    static __device__ __forceinline__ quad lds_quad_t(const bf16* X, int ld, int tr_off) {
+        (void)ld;
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + tr_off));
+        return __builtin_bit_cast(quad, v);
+    }
+};
+
+template <> struct Mma<float> {
+    typedef f32x4 quad;
+    static __device__ __forceinline__ quad cvt(f32x4 v) { return v; }
+    static __device__ __forceinline__ quad cvt_neg(f32x4 v) { return -v; }
+    static __device__ __forceinline__ quad zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+    static __device__ __forceinline__ void mma1(f32x4& acc, quad a, quad b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void mma2(f32x4& acc, quad a0, quad a1, quad b0, quad b1) {
+        mma1(acc, a0, b0);
+        mma1(acc, a1, b1);
+    }
+    static __device__ __forceinline__ quad lds_quad(const float* p) {  // 16-byte aligned
+        return *reinterpret_cast<const quad*>(p);
+    }
+    static __device__ __forceinline__ void lds_store_quad(float* p, quad q) { *reinterpret_cast<quad*>(p) = q; }
+    // Column quad of a row-major 16x16 LDS block X: lane (r, g) receives X[4g .. 4g+3][r] (four reads).
+    static __device__ __forceinline__ int tr_offset(int lane, int ld) { return 4 * (lane >> 4) * ld + (lane & 15); }
+    static __device__ __forceinline__ quad lds_quad_t(const float* X, int ld, int tr_off) {
+        const float* p = X + tr_off;
+        return quad{p[0], p[ld], p[2 * ld], p[3 * ld]};
+    }
+};
+
+// wave-level sum over groups of `width` consecutive lanes (width a power of two <= 64)
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < WIDTH; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace efla

@@ -1,0 +1,137 @@
+/*
+ * efla.h -- C ABI of libefla.so: Error-Free Linear Attention (EFLA) on AMD Instinct MI355X (gfx950).
+ *
+ * The operator (per batch b, head h, token t; S is d_k x d_v, k v^T is d_k x d_v):
+ *   lambda_t = ||k_t||^2
+ *   alpha_t  = (1 - e^{-beta_t lambda_t}) / lambda_t           (alpha_t = beta_t when lambda_t = 0)
+ *   S_t      = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T
+ *   o_t      = S_t^T q_t                                       (read after the update)
+ * Sources: "Exact Flow Linear Attention: Exact Solution from Continuous-Time Dynamics" (gist.science),
+ * Metodologia items 1-3 (ZOH ODE, closed-form rank-1 exponential, update rule and coefficient);
+ * "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Steps 1-4 and the pipeline summary
+ * (alpha from ||k||^2, exact update, readout o = S^T q, chunkwise parallel form with state passing).
+ * Keys are used as given: nothing here normalises k (its norm is the gate).
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers (memory from hipMalloc / a PyTorch CUDA tensor) unless stated.
+ *     The library never allocates, frees or keeps device memory, and keeps no state between calls
+ *     apart from a thread-local copy of the last HIP error text.
+ *   - Layouts are contiguous row-major.  q, k: [B,H,L,d_k]; v, o: [B,H,L,d_v]; beta: [B,H,L];
+ *     state: [B,H,d_k,d_v] (S as the update writes it: row i is key dimension i).
+ *   - q, k, v, o use the storage type `dtype` (fp32 or bf16).  beta, alpha and the state are fp32.
+ *     Arithmetic is fp32 (bf16 operands are multiplied on bf16 matrix cores with fp32 accumulation).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work and returns;
+ *     results are valid once the stream has been synchronised.
+ *   - All arguments are checked BEFORE anything is enqueued.  On any error nothing is launched and
+ *     no output is touched.  A failed launch returns EFLA_ERR_HIP (text: efla_last_error()).
+ *     Faults of running kernels surface at the caller's next synchronisation.
+ *   - Supported sizes: d_k, d_v in {16, 32, 64, 128}; chunk in {16, 32, 64}; any L >= 0 (a short
+ *     last chunk is handled).  Tensor pointers must be 16-byte aligned, beta/alpha 4-byte aligned.
+ *   - Preconditions not checked on the device: beta >= 0 and finite inputs (NaN propagates).
+ */
+#ifndef EFLA_H
+#define EFLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EFLA_OK = 0,
+    EFLA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, overlapping buffers, bad enum */
+    EFLA_ERR_UNSUPPORTED = 2,   /* d_k, d_v, chunk or dtype combination this build does not provide    */
+    EFLA_ERR_NO_DEVICE = 3,     /* no HIP device is visible to the process                             */
+    EFLA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed                          */
+} efla_status;
+
+typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
+
+/*
+ * efla_alpha -- the exact gate alpha_t for n_tokens keys.
+ * "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 1; "Exact Flow Linear
+ * Attention" (gist.science), Metodologia item 3 (the effective coefficient).
+ *   k     [n_tokens, d_k] in k_dtype (device), read only
+ *   beta  [n_tokens] fp32 (device), read only
+ *   alpha [n_tokens] fp32 (device), written; must not overlap k or beta
+ * Evaluated as -expm1(-beta*lambda)/lambda in fp32 with lambda summed in fp32; beta when
+ * beta*lambda == 0.  n_tokens == 0 is a no-op.  d_k may be any of 16, 32, 64, 128.
+ */
+efla_status efla_alpha(const void* k, efla_dtype k_dtype, const float* beta, float* alpha,
+                       int64_t n_tokens, int d_k, void* stream);
+
+/*
+ * efla_chunk_fwd -- the whole sequence forward: every o_t and (optionally) the final state.
+ * Chunkwise-parallel form ("Exact Flow Linear Attention", Metodologia item 3: the update keeps the
+ * rank-1 delta-rule structure, so the WY/UT chunk scheme applies; "Error-Free Linear Attention is a
+ * Free Lunch", Step 4: within-chunk transforms in parallel, chunks joined by passing the state).
+ * Per chunk of C tokens with state S entering it:
+ *   A = strict_lower(diag(alpha) K K^T),  T = (I + A)^{-1},  R = V - K S,  Delta = T diag(alpha) R,
+ *   O = Q S + lower_incl(Q K^T) Delta,    S <- S + K^T Delta
+ * which is the token recurrence above, regrouped; the result does not depend on `chunk` beyond
+ * rounding.
+ *   q, k          [B,H,L,d_k] dtype, read only
+ *   v             [B,H,L,d_v] dtype, read only
+ *   beta          [B,H,L] fp32, read only
+ *   o             [B,H,L,d_v] dtype, written; must not overlap any other argument
+ *   initial_state [B,H,d_k,d_v] fp32 or NULL (= zeros), read only
+ *   final_state   [B,H,d_k,d_v] fp32 or NULL (= not written).  May be the same pointer as
+ *                 initial_state (in-place state passing); any other overlap is rejected.
+ *   chunk         16, 32 or 64 tokens per chunk
+ * The state is carried in fp32 for the whole sequence.  L == 0 copies initial_state (or zeros) to
+ * final_state.  q, k, v, beta and o may be NULL only when L == 0.
+ */
+efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
+                           efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                           int B, int H, int L, int d_k, int d_v, int chunk, void* stream);
+
+/*
+ * efla_chunk_fwd_slab -- efla_chunk_fwd with an explicit split of the d_v columns of the state
+ * across workgroups: each workgroup owns `dv_slab` columns (16, 32 or 64, dividing d_v; 0 = the
+ * library's choice).  Columns of S evolve independently, so every valid split gives the same
+ * result up to rounding; this exists to test and tune that split.  Same arguments and errors as
+ * efla_chunk_fwd otherwise.
+ */
+efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, const float* beta,
+                                efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab, void* stream);
+
+/*
+ * efla_recurrent_step -- one decode token for NH independent (sequence, head) states, in place.
+ * "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), pipeline summary ("for each
+ * token": alpha, update S, emit o = S^T q); "Exact Flow Linear Attention", Metodologia item 3.
+ * Per state (a = S^T k and b = S^T q taken before the update):
+ *   S <- S + alpha k (v - a)^T,   o = b + alpha (k^T q) (v - a)      (= S_new^T q)
+ *   q, k  [NH, d_k] dtype, read only
+ *   v     [NH, d_v] dtype, read only
+ *   beta  [NH] fp32, read only
+ *   state [NH, d_k, d_v] fp32, read and overwritten in place
+ *   o     [NH, d_v] dtype, written; must not overlap state or the inputs
+ * NH == 0 is a no-op.
+ */
+efla_status efla_recurrent_step(const void* q, const void* k, const void* v, const float* beta,
+                                efla_dtype dtype, float* state, void* o,
+                                int64_t NH, int d_k, int d_v, void* stream);
+
+/* Workgroups and d_v slab width efla_chunk_fwd would launch for these sizes (host only, no device
+ * needed).  Returns EFLA_OK and fills the outputs, or the error efla_chunk_fwd would return for
+ * the sizes alone. */
+efla_status efla_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                int dv_slab, int* workgroups, int* slab_width, int* lds_bytes);
+
+/* Static description of a status code (never NULL). */
+const char* efla_status_string(efla_status s);
+
+/* Text of the last HIP error seen by a call on this thread ("" if none). */
+const char* efla_last_error(void);
+
+/* ABI version of this library (major * 10000 + minor * 100 + patch). */
+int efla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EFLA_H */

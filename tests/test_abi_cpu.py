@@ -1,0 +1,147 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and rejects bad arguments
+before touching any device (no GPU needed).  Nothing here launches a kernel: calls either fail
+argument checks, or -- only on a machine with no GPU -- reach the device check and report
+EFLA_ERR_NO_DEVICE."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import exact_flow_delta_amd as efla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "efla.h")
+
+OK, INVALID, UNSUPPORTED, NO_DEVICE, HIP = range(5)
+F32, BF16 = 0, 1
+
+pytestmark = pytest.mark.skipif(not os.path.exists(efla.library_path()), reason="libefla.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:efla_status|const char\*|int)\s+(efla_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return efla.load_library()
+
+
+def _no_gpu():
+    return torch.cuda.device_count() == 0
+
+
+# fake, 16-byte-aligned, non-overlapping device addresses (never dereferenced by these tests)
+def P(i):
+    return ctypes.c_void_p(0x7F0000000000 + i * (1 << 32))
+
+
+def test_exports_match_header(lib):
+    names = _declared()
+    assert {"efla_alpha", "efla_chunk_fwd", "efla_recurrent_step"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+
+
+def test_status_strings_and_version(lib):
+    for s in range(5):
+        assert lib.efla_status_string(s).decode().startswith("EFLA")
+    assert lib.efla_status_string(99).decode().startswith("EFLA")
+    assert lib.efla_version() >= 10000
+    assert isinstance(lib.efla_last_error(), bytes)
+
+
+def test_plan_default_slabs(lib):
+    # headline forward: 128 heads x 2 slabs of 64 columns, 4 waves each
+    wg, sw, lds = efla.chunk_plan(8, 16, 4096, 128, 128, 64, torch.bfloat16)
+    assert (wg, sw) == (256, 64) and 0 < lds <= 160 * 1024
+    # few heads: narrower slabs give more workgroups
+    wg, sw, _ = efla.chunk_plan(1, 16, 65536, 128, 128, 64, torch.bfloat16)
+    assert sw == 16 and wg == 128
+    # explicit slab, grid padded to whole groups of 8 heads
+    wg, sw, _ = efla.chunk_plan(1, 1, 256, 16, 16, 16, torch.float32, 16)
+    assert (wg, sw) == (8, 16)
+
+
+def test_plan_rejects_unsupported(lib):
+    wg = ctypes.c_int()
+    for args in [(1, 1, 8, 48, 64, 64, BF16, 0), (1, 1, 8, 64, 256, 64, BF16, 0), (1, 1, 8, 64, 64, 128, BF16, 0),
+                 (1, 1, 8, 64, 64, 64, BF16, 48), (1, 1, 8, 64, 32, 64, BF16, 64)]:
+        assert lib.efla_chunk_fwd_plan(*args, ctypes.byref(wg), None, None) == UNSUPPORTED, args
+    assert lib.efla_chunk_fwd_plan(-1, 1, 8, 64, 64, 64, BF16, 0, None, None, None) == INVALID
+    assert lib.efla_chunk_fwd_plan(1, 1, 8, 64, 64, 64, 7, 0, None, None, None) == INVALID
+    assert lib.efla_chunk_fwd_plan(1, 1, 8, 128, 128, 64, F32, 0, None, None, None) == OK
+    for sizes in [(16, 16, 16), (128, 128, 64), (64, 64, 64)]:
+        for dt in (F32, BF16):
+            assert lib.efla_chunk_fwd_plan(1, 1, 8, sizes[0], sizes[1], sizes[2], dt, 0, None, None, None) == OK
+
+
+def _chunk(lib, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=BF16, o=P(5), s0=None, sf=P(6), B=2, H=3, L=100, dk=64, dv=64,
+             C=64, slab=0)
+    a.update(kw)
+    return lib.efla_chunk_fwd_slab(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["o"], a["s0"], a["sf"], a["B"],
+                                   a["H"], a["L"], a["dk"], a["dv"], a["C"], a["slab"], None)
+
+
+def test_chunk_fwd_argument_errors(lib):
+    assert _chunk(lib, q=None) == INVALID
+    assert _chunk(lib, o=None) == INVALID
+    assert _chunk(lib, beta=None) == INVALID
+    assert _chunk(lib, k=ctypes.c_void_p(0x7F0000000008)) == INVALID      # misaligned
+    assert _chunk(lib, sf=ctypes.c_void_p(0x7F0600000004)) == INVALID     # misaligned state
+    assert _chunk(lib, L=-1) == INVALID
+    assert _chunk(lib, dt=5) == INVALID
+    assert _chunk(lib, dk=96) == UNSUPPORTED
+    assert _chunk(lib, C=8) == UNSUPPORTED
+    assert _chunk(lib, slab=32, dv=16) == UNSUPPORTED
+    # o overlapping an input, the final state overlapping an input, partially overlapping states
+    assert _chunk(lib, o=ctypes.c_void_p(0x7F0100000000 + 256)) == INVALID
+    assert _chunk(lib, sf=P(3)) == INVALID
+    assert _chunk(lib, s0=P(6), sf=ctypes.c_void_p(0x7F0600000000 + 1024)) == INVALID
+    # empty problems are no-ops that need no device
+    assert _chunk(lib, B=0) == OK
+    assert _chunk(lib, L=0, sf=None, q=None, k=None, v=None, beta=None, o=None) == OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_no_device_reported_after_valid_arguments(lib):
+    assert _chunk(lib) == NO_DEVICE
+    assert _chunk(lib, s0=P(6)) == NO_DEVICE           # in-place state passing is allowed
+    assert lib.efla_recurrent_step(P(1), P(2), P(3), P(4), BF16, P(5), P(6), 8192, 128, 128, None) == NO_DEVICE
+    assert lib.efla_alpha(P(1), BF16, P(2), P(3), 1000, 128, None) == NO_DEVICE
+    assert b"no HIP device" in lib.efla_last_error()
+
+
+def test_recurrent_step_argument_errors(lib):
+    f = lib.efla_recurrent_step
+    assert f(P(1), P(2), P(3), P(4), BF16, P(5), P(6), 0, 128, 128, None) == OK    # empty
+    assert f(P(1), P(2), P(3), P(4), BF16, P(5), P(6), -1, 128, 128, None) == INVALID
+    assert f(P(1), P(2), P(3), P(4), BF16, None, P(6), 8, 128, 128, None) == INVALID
+    assert f(P(1), P(2), P(3), P(4), BF16, P(5), P(5), 8, 128, 128, None) == INVALID  # o aliases state
+    assert f(P(1), P(2), P(3), P(4), BF16, P(5), P(6), 8, 100, 128, None) == UNSUPPORTED
+    assert f(P(1), P(2), P(3), P(4), 3, P(5), P(6), 8, 128, 128, None) == INVALID
+    assert f(P(1), P(2), P(3), P(4), BF16, ctypes.c_void_p(0x7F0500000008), P(6), 8, 128, 128, None) == INVALID
+
+
+def test_alpha_argument_errors(lib):
+    f = lib.efla_alpha
+    assert f(P(1), BF16, P(2), P(3), 0, 128, None) == OK
+    assert f(P(1), BF16, P(2), P(3), -5, 128, None) == INVALID
+    assert f(None, BF16, P(2), P(3), 5, 128, None) == INVALID
+    assert f(P(1), BF16, P(2), P(1), 5, 128, None) == INVALID     # alpha overlaps k
+    assert f(P(1), BF16, P(2), P(3), 5, 20, None) == UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(1, 1, 16, 16)
+    b = torch.zeros(1, 1, 16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        efla.chunk_fwd(x, x, x, b)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        efla.recurrent_step(x[0, 0], x[0, 0], x[0, 0], b[0, 0], torch.zeros(16, 16, 16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        efla.alpha(x, b)

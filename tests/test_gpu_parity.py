@@ -1,0 +1,266 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle, element by element on the
+same seeded inputs.  Gate: relative max error max|x - ref| / max|ref| per tensor, 1e-5 for fp32
+inputs and 2e-2 for bf16 inputs, on the outputs and on the final state separately."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_flow_delta_amd as efla
+import oracle
+from exact_flow_delta_amd import workloads as W
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from gpu_helpers import TOL, dev, errs, fwd_inputs_dev, host  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_fwd(x, dtype, chunk, dv_slab=0, poison=True):
+    d = fwd_inputs_dev(x, dtype)
+    B, H, L, _ = d["k"].shape
+    d_v = d["v"].shape[-1]
+    out = torch.empty((B, H, L, d_v), dtype=d["v"].dtype, device="cuda")
+    if poison:
+        out.fill_(float("nan"))
+    o, S = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=d["initial_state"], chunk_size=chunk,
+                          dv_slab=dv_slab, out=out)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _oracle_fwd(x):
+    ro, rS, _ = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["initial_state"])
+    return ro, rS
+
+
+# ------------------------------------------------------------------------------------------------
+# alpha
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d_k", [16, 32, 64, 128])
+def test_alpha(dtype, d_k):
+    rng = np.random.default_rng(100 + d_k)
+    n = 3001
+    g = rng.standard_normal((n, d_k))
+    scale = np.exp(rng.uniform(np.log(1e-4), np.log(40.0), (n, 1)))
+    k = (g / np.linalg.norm(g, axis=-1, keepdims=True) * scale).astype(np.float32)
+    k[:7] = 0.0                                  # lambda = 0 -> alpha = beta
+    if dtype == "bf16":
+        k = W.round_bf16(k)
+    beta = rng.uniform(0, 1, n).astype(np.float32)
+    beta[3] = 0.0
+    a = host(efla.alpha(dev(k, dtype), torch.from_numpy(beta).cuda()))
+    ref = oracle.alpha(k, beta)
+    np.testing.assert_array_equal(a[:7], beta[:7].astype(np.float64))
+    rel = np.abs(a - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert rel.max() < 2e-6, rel.max()
+
+
+# ------------------------------------------------------------------------------------------------
+# decode step
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d_k,d_v", [(16, 16), (64, 32), (32, 128), (128, 128), (128, 16)])
+def test_recurrent_step_multi(dtype, d_k, d_v):
+    w = W.workload(5, B=7, H=3, d_k=d_k, d_v=d_v, dtype=dtype)
+    S0 = W.make_decode_state(w)
+    S = torch.from_numpy(S0.copy()).cuda()
+    rS = S0.astype(np.float64)
+    for step in range(6):
+        t = W.make_decode_token(w, step, salt=d_k * 1000 + d_v)
+        out = torch.full((w.NH, d_v), float("nan"), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                         device="cuda")
+        o = efla.recurrent_step(dev(t["q"], dtype), dev(t["k"], dtype), dev(t["v"], dtype),
+                                torch.from_numpy(t["beta"]).cuda(), S, out=out)
+        ro, rS, _ = oracle.step(t["q"], t["k"], t["v"], t["beta"], rS)
+        torch.cuda.synchronize()
+        eo = W.rel_max_err(host(o), ro)
+        assert eo < TOL[dtype], (step, eo)
+        eS = W.rel_max_err(host(S), rS)      # the state is fp32 in both paths
+        assert eS < 1e-5, (step, eS)
+
+
+def test_recurrent_step_headline_sampled():
+    """256 sequences x 32 heads, d 128, 64 steps (the decode workload), sampled states vs the oracle."""
+    w = W.workload(5)
+    S0 = W.make_decode_state(w)
+    S = torch.from_numpy(S0).cuda()
+    idx = np.array([0, 1, 31, 32, 1000, 4095, 4096, 8000, 8191])
+    rS = S0[idx].astype(np.float64)
+    for step in range(w.steps):
+        t = W.make_decode_token(w, step)
+        o = efla.recurrent_step(dev(t["q"], "bf16"), dev(t["k"], "bf16"), dev(t["v"], "bf16"),
+                                torch.from_numpy(t["beta"]).cuda(), S)
+        ro, rS, _ = oracle.step(t["q"][idx], t["k"][idx], t["v"][idx], t["beta"][idx], rS)
+        eo = W.rel_max_err(host(o[idx]), ro)
+        assert eo < TOL["bf16"], (step, eo)
+    torch.cuda.synchronize()
+    eS = W.rel_max_err(host(S[idx]), rS)
+    assert eS < TOL["bf16"], eS
+    assert torch.isfinite(S).all()
+
+
+# ------------------------------------------------------------------------------------------------
+# chunked forward: the small workloads at full size
+# ------------------------------------------------------------------------------------------------
+def test_chunk_fwd_tiny_workload():
+    w = W.workload(1)
+    x = W.make_fwd_inputs(w)
+    o, S = _run_fwd(x, w.dtype, w.chunk)
+    eo, eS = errs(o, S, *_oracle_fwd(x))
+    assert eo < TOL["f32"] and eS < TOL["f32"], (eo, eS)
+
+
+def test_chunk_fwd_stiff_workload():
+    w = W.workload(2)
+    x = W.make_fwd_inputs(w)
+    o, S = _run_fwd(x, w.dtype, w.chunk)
+    eo, eS = errs(o, S, *_oracle_fwd(x))
+    assert eo < TOL["f32"] and eS < TOL["f32"], (eo, eS)
+
+
+# ------------------------------------------------------------------------------------------------
+# chunked forward: every (d_k, d_v, chunk, dtype) at sizes spanning several chunks and a ragged tail
+# ------------------------------------------------------------------------------------------------
+SWEEP = [(dk, dv, c, dt) for dt in ("f32", "bf16") for dk in (16, 32, 64, 128) for dv in (16, 64, 128)
+         for c in (16, 32, 64)]
+
+
+@pytest.mark.parametrize("d_k,d_v,chunk,dtype", SWEEP)
+def test_chunk_fwd_sweep(d_k, d_v, chunk, dtype):
+    cfg = 2 if dtype == "f32" else 3
+    w = W.workload(cfg, B=2, H=3, L=3 * chunk + 5, d_k=d_k, d_v=d_v, dtype=dtype)
+    x = W.make_fwd_inputs(w, salt=d_k + 7 * d_v + 31 * chunk)
+    if x["initial_state"] is None:
+        x["initial_state"] = (0.1 * np.random.default_rng(d_k + d_v).standard_normal((2, 3, d_k, d_v))).astype(
+            np.float32)
+    else:
+        x["initial_state"] = x["initial_state"][:, :, :d_k, :d_v].copy()
+    o, S = _run_fwd(x, dtype, chunk)
+    eo, eS = errs(o, S, *_oracle_fwd(x))
+    assert eo < TOL[dtype] and eS < TOL[dtype], (eo, eS)
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 63, 64, 65, 784])
+def test_chunk_fwd_ragged_lengths(L):
+    """Short and ragged sequences, including the 784-token d=64 shape of the pixel-sequence workload."""
+    w = W.workload(2, B=1, H=9, L=L)
+    x = W.make_fwd_inputs(w, salt=L)
+    o, S = _run_fwd(x, "f32", 64)
+    eo, eS = errs(o, S, *_oracle_fwd(x))
+    assert eo < TOL["f32"] and eS < TOL["f32"], (eo, eS)
+
+
+def test_chunk_fwd_empty_sequence_copies_state():
+    rng = np.random.default_rng(5)
+    s0 = torch.from_numpy(rng.standard_normal((2, 3, 64, 32)).astype(np.float32)).cuda()
+    e = torch.empty((2, 3, 0, 64), device="cuda")
+    ev = torch.empty((2, 3, 0, 32), device="cuda")
+    b = torch.empty((2, 3, 0), device="cuda")
+    o, S = efla.chunk_fwd(e, e, ev, b, initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 32)
+    assert torch.equal(S, s0)
+    o, S = efla.chunk_fwd(e, e, ev, b)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0
+
+
+# ------------------------------------------------------------------------------------------------
+# metamorphic properties
+# ------------------------------------------------------------------------------------------------
+def test_slab_split_is_bitwise_identical():
+    """State columns are independent: every d_v split gives bit-identical results."""
+    w = W.workload(3, B=1, H=5, L=300)
+    x = W.make_fwd_inputs(w)
+    res = [_run_fwd(x, "bf16", 64, dv_slab=s) for s in (16, 32, 64)]
+    for o, S in res[1:]:
+        assert torch.equal(o, res[0][0]) and torch.equal(S, res[0][1])
+
+
+def test_deterministic():
+    w = W.workload(3, B=2, H=4, L=500)
+    x = W.make_fwd_inputs(w)
+    o1, S1 = _run_fwd(x, "bf16", 64)
+    o2, S2 = _run_fwd(x, "bf16", 64)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_size_independence(dtype):
+    w = W.workload(2 if dtype == "f32" else 3, B=1, H=4, L=200, d_k=64, d_v=64, dtype=dtype)
+    x = W.make_fwd_inputs(w)
+    ro, rS = _oracle_fwd(x)
+    for c in (16, 32, 64):
+        o, S = _run_fwd(x, dtype, c)
+        eo, eS = errs(o, S, ro, rS)
+        assert eo < TOL[dtype] and eS < TOL[dtype], (c, eo, eS)
+
+
+def test_state_chaining_bitwise_at_chunk_boundary():
+    """fwd over [0, L) == fwd over [0, L1) then [L1, L) from its final state, when L1 is a chunk multiple."""
+    w = W.workload(3, B=2, H=3, L=320)
+    x = W.make_fwd_inputs(w)
+    d = fwd_inputs_dev(x, "bf16")
+    o, S = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"])
+    L1 = 192
+    o1, S1 = efla.chunk_fwd(d["q"][:, :, :L1].contiguous(), d["k"][:, :, :L1].contiguous(),
+                            d["v"][:, :, :L1].contiguous(), d["beta"][:, :, :L1].contiguous())
+    o2, S2 = efla.chunk_fwd(d["q"][:, :, L1:].contiguous(), d["k"][:, :, L1:].contiguous(),
+                            d["v"][:, :, L1:].contiguous(), d["beta"][:, :, L1:].contiguous(),
+                            initial_state=S1, final_state=S1)      # in place
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=2), o)
+    assert torch.equal(S2, S)
+
+
+def test_prefill_then_decode_matches_oracle():
+    w = W.workload(3, B=2, H=4, L=150)
+    x = W.make_fwd_inputs(w)
+    d = fwd_inputs_dev(x, "bf16")
+    Lp = 130
+    o, S = efla.chunk_fwd(d["q"][:, :, :Lp].contiguous(), d["k"][:, :, :Lp].contiguous(),
+                          d["v"][:, :, :Lp].contiguous(), d["beta"][:, :, :Lp].contiguous())
+    outs = [o]
+    for t in range(Lp, w.L):
+        ot = efla.recurrent_step(d["q"][:, :, t].contiguous(), d["k"][:, :, t].contiguous(),
+                                 d["v"][:, :, t].contiguous(), d["beta"][:, :, t].contiguous(), S)
+        outs.append(ot.unsqueeze(2))
+    torch.cuda.synchronize()
+    ro, rS = _oracle_fwd(x)
+    eo, eS = errs(torch.cat(outs, dim=2), S, ro, rS)
+    assert eo < TOL["bf16"] and eS < TOL["bf16"], (eo, eS)
+
+
+# ------------------------------------------------------------------------------------------------
+# the headline workloads at full size, in the launch configuration the benchmark times
+# ------------------------------------------------------------------------------------------------
+def _sampled_heads(w, x, o, S, heads):
+    B, H = w.B, w.H
+    for (b, h) in heads:
+        sl = lambda a: a[b:b + 1, h:h + 1]  # noqa: E731
+        xs = dict(q=sl(x["q"]), k=sl(x["k"]), v=sl(x["v"]), beta=sl(x["beta"]),
+                  initial_state=None if x["initial_state"] is None else sl(x["initial_state"]))
+        ro, rS = _oracle_fwd(xs)
+        eo = W.rel_max_err(host(o[b, h]), ro[0, 0])
+        eS = W.rel_max_err(host(S[b, h]), rS[0, 0])
+        assert eo < TOL[w.dtype] and eS < TOL[w.dtype], ((b, h), eo, eS)
+
+
+def test_lm_layer_workload_full_size_sampled():
+    w = W.workload(3)
+    x = W.make_fwd_inputs(w)
+    o, S = _run_fwd(x, "bf16", w.chunk)
+    assert not torch.isnan(o).any()
+    _sampled_heads(w, x, o, S, [(0, 0), (0, 15), (3, 7), (7, 15)])
+
+
+def test_long_context_workload_full_size_sampled():
+    w = W.workload(4)
+    x = W.make_fwd_inputs(w)
+    o, S = _run_fwd(x, "bf16", w.chunk)
+    assert not torch.isnan(o).any()
+    _sampled_heads(w, x, o, S, [(0, 0), (0, 11)])
