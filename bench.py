@@ -7,7 +7,10 @@ intra-chunk UT transform and the inter-chunk state pass all run inside the fused
 The batched decode workload (256 sequences x 32 heads, d 128, 512 MiB fp32 state, 64 dependent
 one-token steps, one launch per step) is timed in the same run and reported under "decode".
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--only fwd|decode|copy]
+
+--only runs one leg for profiling: the forward alone, the decode alone, or a plain 512 MiB
+device-to-device copy (the reference for scaling the HBM byte counters).
 
 Prints one JSON line.  Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 """
@@ -47,6 +50,24 @@ def fwd_algorithmic(B, H, L, dk, dv, C, esize=2):
 def decode_algorithmic(NH, dk, dv, esize=2):
     """Bytes per decode step: the fp32 state read and written once, q, k, v, o in the storage type, beta."""
     return NH * (2 * dk * dv * 4 + (2 * dk + 2 * dv) * esize + 4)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary (profiles/hbm_traffic.json),
+    or None when the kernel's sources no longer hash to what was measured."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f)[kernel]
+        h = hashlib.sha256()
+        for src in entry["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        return entry["traffic_bytes"] if h.hexdigest()[:16] == entry["sources_sha256_16"] else None
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def run_forward(efla, W, torch, steps, warmup):
@@ -123,6 +144,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
+                    help="run one leg only (for profiling); prints a short JSON line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -141,7 +164,25 @@ def main():
         sys.exit(1)
     efla.load_library()
 
+    if args.only == "copy":
+        n = 512 * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"leg": "copy", "bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return
+    if args.only == "decode":
+        dw, step_ms = run_decode(efla, W, torch)
+        print(json.dumps({"leg": "decode", "median_step_ms": statistics.median(step_ms)}), flush=True)
+        return
+
     w, ms, plan = run_forward(efla, W, torch, args.steps, args.warmup)
+    if args.only == "fwd":
+        print(json.dumps({"leg": "fwd", "ms_per_step": ms, "launch": plan}), flush=True)
+        return
     tokens_per_s = w.B * w.L / (ms * 1e-3)
     nbytes, flops = fwd_algorithmic(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
     achieved_gbs = nbytes / (ms * 1e-3) / 1e9
@@ -162,7 +203,8 @@ def main():
         "config": {"workload": "lm_layer_fwd", "B": w.B, "H": w.H, "L": w.L, "d_k": w.d_k, "d_v": w.d_v,
                    "chunk": w.chunk, "io": "bf16", "state": "fp32", "launch": plan},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("chunk_fwd_kernel<bf16,128,64,64>"),
                      "kernel": "chunk_fwd_kernel<bf16,128,64,64>", "bytes_per_launch": nbytes},
         "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops},
@@ -177,7 +219,8 @@ def main():
             "median_step_ms": round(med, 5), "total_ms": round(sum(step_ms), 4),
             "tokens_per_s": round(dw.B / (med * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("recurrent_step_kernel<bf16,128,128>"),
                          "kernel": "recurrent_step_kernel<bf16,128,128>", "bytes_per_launch": dbytes},
         }
     if not args.no_cpu:

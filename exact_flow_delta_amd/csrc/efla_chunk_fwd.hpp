@@ -18,11 +18,12 @@
 //   1. the chunk's Q, K, V slab (prefetched into registers during the previous chunk) go to LDS, with
 //      lambda = ||k||^2 reduced across the lanes holding a key row and alpha from it; the next chunk's
 //      global loads are issued right after;
-//   2. Gram tiles alpha_i k_i.k_j (upper tiles, stored transposed = lower) and the lower tiles of Q K^T
-//      on the matrix cores, a fixed set of tiles per wave;
-//   3. T: the 16x16 diagonal blocks by right-looking forward substitution in fp32 (one 16-lane group per
-//      block), then the off-diagonal blocks level by level, T_ij = -T_ii sum_m A_im T_mj, on the matrix
-//      cores; T diag(alpha) is written as a matrix-core operand;
+//   2. per wave, a Gram block row alpha_i k_i.k_j (upper tiles, stored transposed = lower) and a block
+//      row of Q K^T on the matrix cores; the wave then solves its 16x16 diagonal block of T by
+//      right-looking forward substitution in fp32 (lane r carries column r);
+//   3. the off-diagonal blocks of T, one block column per wave, walked down the column with the blocks
+//      found so far kept in registers: T_IJ = -T_II sum_m A_Im T_mJ on the matrix cores; T diag(alpha)
+//      is written as a matrix-core operand;
 //   4. per wave: X = [Q; K] S, R = V - K S, Delta = T diag(alpha) R, O = Q S + P Delta (stored),
 //      S += K^T Delta -- all on the matrix cores with the state as an in-register operand.
 // Operands that must be read "down a column" (K^T, V, T as a right-hand factor) are fetched with the
@@ -59,14 +60,13 @@ struct ChunkLayout {
     static constexpr int PAD = ESIZE == 2 ? 20 : 4;
     static constexpr int LD_DK = DK + PAD;   // sQ, sK   [C][LD_DK]   storage type, row-major
     static constexpr int LD_V = DVS + PAD;   // sV       [C][LD_V]    storage type
-    static constexpr int LD_CE = C + PAD;    // sT, sTa, sP [C][LD_CE] storage type
-    static constexpr int LD_CF = C + 4;      // sA       [C][LD_CF]   fp32 (alpha_i k_i.k_j, strict lower)
+    static constexpr int LD_CE = C + PAD;    // sA, sT, sTa, sP [C][LD_CE] storage type
     static constexpr int LD_AT = 16 + 4;     // sAt      [C][LD_AT]   fp32, diagonal blocks of A transposed
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_K = OFF_Q + C * LD_DK * ESIZE;
     static constexpr int OFF_V = OFF_K + C * LD_DK * ESIZE;
-    static constexpr int OFF_A = OFF_V + C * LD_V * ESIZE;
-    static constexpr int OFF_AT = OFF_A + C * LD_CF * 4;
+    static constexpr int OFF_A = OFF_V + C * LD_V * ESIZE;    // alpha_i k_i.k_j, off-diagonal blocks
+    static constexpr int OFF_AT = OFF_A + C * LD_CE * ESIZE;
     static constexpr int OFF_T = OFF_AT + C * LD_AT * 4;
     static constexpr int OFF_TA = OFF_T + C * LD_CE * ESIZE;
     static constexpr int OFF_P = OFF_TA + C * LD_CE * ESIZE;
@@ -80,8 +80,7 @@ constexpr int kMaxLdsBytes = 160 * 1024;
 template <int ESIZE>
 constexpr int chunk_layout_bytes(int dk, int c, int dvs) {
     const int pad = ESIZE == 2 ? 20 : 4;
-    return c * (dk + pad) * ESIZE * 2 + c * (dvs + pad) * ESIZE + c * (c + 4) * 4 + c * 20 * 4 +
-           c * (c + pad) * ESIZE * 3 + c * 4;
+    return c * (dk + pad) * ESIZE * 2 + c * (dvs + pad) * ESIZE + c * 20 * 4 + c * (c + pad) * ESIZE * 4 + c * 4;
 }
 
 // global -> register staging of one chunk; prefetched when it fits in a few registers per thread
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     constexpr int NT = NW * 64;
     constexpr int NB = C / 16;
     constexpr int NKD = DK / 16;
-    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE, LD_CF = LY::LD_CF, LD_AT = LY::LD_AT;
+    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE, LD_AT = LY::LD_AT;
     typedef ChunkStage<E, DK, C, DVS, NT> Stage;
     // prefetching keeps one chunk in registers: only when that is a few registers per thread
     constexpr bool kPrefetch = (2 * Stage::NQK + Stage::NV) <= 12;
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     E* sQ = reinterpret_cast<E*>(smem + LY::OFF_Q);
     E* sK = reinterpret_cast<E*>(smem + LY::OFF_K);
     E* sV = reinterpret_cast<E*>(smem + LY::OFF_V);
-    float* sA = reinterpret_cast<float*>(smem + LY::OFF_A);
+    E* sA = reinterpret_cast<E*>(smem + LY::OFF_A);
     float* sAt = reinterpret_cast<float*>(smem + LY::OFF_AT);
     E* sT = reinterpret_cast<E*>(smem + LY::OFF_T);
     E* sTa = reinterpret_cast<E*>(smem + LY::OFF_TA);
@@ -236,114 +235,112 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
         }
         __syncthreads();
 
-        // ---- 2. Gram (-> A, and the diagonal blocks transposed -> At) and Q K^T (-> P) tiles ----------
-        {
-            constexpr int NTRI = NB * (NB + 1) / 2;
-            constexpr int NTILE = 2 * NTRI;
-            static_for<(NTILE + NW - 1) / NW>([&](auto jc) {
+        // ---- 2. per wave: Gram block row hi (-> A; its diagonal block is solved right here for T_hh) and
+        //         Q K^T block row NB-1-hi (-> P): NB+1 tiles per block row pair, the same for every wave
+        for (int hi = w; hi < NB; hi += NW) {
+            const int hp = NB - 1 - hi;
+            static_for<NB + 1>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
-                const int tile = w + j * NW;
-                if (NTILE % NW == 0 || tile < NTILE) {
-                    const bool isG = tile < NTRI;
-                    const int tt = isG ? tile : tile - NTRI;
-                    int hi = 0;
+                const bool isG = j <= hi;
+                const int lo = isG ? j : j - hi - 1;
+                const int rowb = isG ? hi : hp;
+                const E* pa = sK + (16 * lo + r) * LD_DK + 4 * g;
+                const E* pb = (isG ? sK : sQ) + (16 * rowb + r) * LD_DK + 4 * g;
+                quad qa[NKD], qb[NKD];
 #pragma unroll
-                    for (int h = 1; h < NB; ++h) hi += (tt >= h * (h + 1) / 2) ? 1 : 0;
-                    const int lo = tt - hi * (hi + 1) / 2;   // lo <= hi
-                    const E* pa = sK + (16 * lo + r) * LD_DK + 4 * g;
-                    const E* pb = (isG ? sK : sQ) + (16 * hi + r) * LD_DK + 4 * g;
-                    quad qa[NKD], qb[NKD];
+                for (int kd = 0; kd < NKD; ++kd) {
+                    qa[kd] = M::lds_quad(pa + 16 * kd);
+                    qb[kd] = M::lds_quad(pb + 16 * kd);
+                }
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kd = 0; kd < NKD; ++kd) {
-                        qa[kd] = M::lds_quad(pa + 16 * kd);
-                        qb[kd] = M::lds_quad(pb + 16 * kd);
-                    }
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, qa[kd], qa[kd + 1], qb[kd], qb[kd + 1]);
+                if constexpr (NKD & 1) M::mma1(acc, qa[NKD - 1], qb[NKD - 1]);
+                // acc lane (r, g), element i: X[16 lo + 4g + i][16 rowb + r] with X = K K^T or K Q^T,
+                // i.e. entry (row, col + i) of K K^T or Q K^T with row = 16 rowb + r, col = 16 lo + 4g
+                const int row = 16 * rowb + r;
+                const int col = 16 * lo + 4 * g;
+                if (isG) {
+                    const float ar = sAlpha[row];
+                    f32x4 out;
 #pragma unroll
-                    for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, qa[kd], qa[kd + 1], qb[kd], qb[kd + 1]);
-                    if constexpr (NKD & 1) M::mma1(acc, qa[NKD - 1], qb[NKD - 1]);
-                    // acc lane (r, g), element i: X[16 lo + 4g + i][16 hi + r] with X = K K^T or K Q^T
-                    const int row = 16 * hi + r;
-                    const int col = 16 * lo + 4 * g;
-                    if (isG) {
-                        const float ar = sAlpha[row];
-                        f32x4 out;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) out[i] = (col + i < row) ? ar * acc[i] : 0.0f;
-                        *reinterpret_cast<f32x4*>(sA + row * LD_CF + col) = out;
-                        // diagonal block: At[m][i] = A[16b + i][16b + m], i.e. column m of the block as a row
-                        if (lo == hi) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) sAt[(col + i) * LD_AT + r] = out[i];
-                        }
+                    for (int i = 0; i < 4; ++i) out[i] = (col + i < row) ? ar * acc[i] : 0.0f;
+                    if (lo < hi) {
+                        M::lds_store_quad(sA + row * LD_CE + col, M::cvt(out));
                     } else {
-                        f32x4 out;
+                        // diagonal block: At[m][i] = A[16 hi + i][16 hi + m] (column m as a row), fp32
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) out[i] = (col + i <= row) ? acc[i] : 0.0f;
-                        M::lds_store_quad(sP + row * LD_CE + col, M::cvt(out));
+                        for (int i = 0; i < 4; ++i) sAt[(col + i) * LD_AT + r] = out[i];
                     }
+                } else {
+                    f32x4 out;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) out[i] = (col + i <= row) ? acc[i] : 0.0f;
+                    M::lds_store_quad(sP + row * LD_CE + col, M::cvt(out));
                 }
             });
+            // T_hh = (I + A_hh)^{-1}: right-looking substitution, lane r of the first group holds column r.
+            // The block was written to LDS by this wave just above (LDS operations of a wave stay in order).
+            __asm__ volatile("" ::: "memory");
+            if (g == 0) {
+                const int b0 = 16 * hi;
+                float sv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+#pragma unroll
+                for (int m = 0; m < 15; ++m) {
+                    const float* colm = sAt + (b0 + m) * LD_AT;   // A[b0 + i][b0 + m], i = 0..15
+                    float c[16];
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(colm + 4 * i4);
+                        c[4 * i4] = x[0];
+                        c[4 * i4 + 1] = x[1];
+                        c[4 * i4 + 2] = x[2];
+                        c[4 * i4 + 3] = x[3];
+                    }
+#pragma unroll
+                    for (int i = m + 1; i < 16; ++i) sv[i] -= c[i] * sv[m];
+                }
+                const float ar = sAlpha[b0 + r];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    sT[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i]);
+                    sTa[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i] * ar);
+                }
+            }
         }
         __syncthreads();
 
-        // ---- 3a. diagonal 16x16 blocks of T: right-looking substitution, lane r holds column r ---------
-        if (w == 0 && g < NB) {
-            const int b0 = 16 * g;
-            float s[16];
+        // ---- 3. off-diagonal blocks of T, one block column J per wave, walked down the column with the
+        //         blocks already found kept in registers: T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ
+        static_for<NB - 1>([&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            if (J % NW == w) {
+                quad Tq[NB];
+                Tq[J] = M::lds_quad_t(sT + 16 * J * LD_CE + 16 * J, LD_CE, tr_ce);
+                const float aj = sAlpha[16 * J + r];
+                static_for<NB>([&](auto ic) {
+                    constexpr int I = decltype(ic)::value;
+                    if constexpr (I > J) {
+                        const E* pa = sA + (16 * I + r) * LD_CE + 4 * g;
+                        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                        static_for<(I - J) / 2>([&](auto pc) {
+                            constexpr int m = J + 2 * decltype(pc)::value;
+                            M::mma2(y, M::lds_quad(pa + 16 * m), M::lds_quad(pa + 16 * m + 16), Tq[m], Tq[m + 1]);
+                        });
+                        if constexpr ((I - J) & 1) M::mma1(y, M::lds_quad(pa + 16 * (I - 1)), Tq[I - 1]);
+                        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                        M::mma1(z, M::lds_quad(sT + (16 * I + r) * LD_CE + 16 * I + 4 * g), M::cvt_neg(y));
+                        // z lane (r, g), element e: T[16 I + 4g + e][16 J + r]
+                        Tq[I] = M::cvt(z);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = (i == r) ? 1.0f : 0.0f;
-#pragma unroll
-            for (int m = 0; m < 15; ++m) {
-                // column m of the block: A[b0 + i][b0 + m], i > m
-                const float* col = sAt + (b0 + m) * LD_AT;
-                float c[16];
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(col + 4 * i4);
-                    c[4 * i4] = x[0];
-                    c[4 * i4 + 1] = x[1];
-                    c[4 * i4 + 2] = x[2];
-                    c[4 * i4 + 3] = x[3];
-                }
-#pragma unroll
-                for (int i = m + 1; i < 16; ++i) s[i] -= c[i] * s[m];
-            }
-            const float ar = sAlpha[b0 + r];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                sT[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(s[i]);
-                sTa[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(s[i] * ar);
-            }
-        }
-        __syncthreads();
-
-        // ---- 3b. off-diagonal blocks, one level (i - j = d) at a time ----------------------------------
-        static_for<NB>([&](auto dc) {
-            constexpr int d = decltype(dc)::value;
-            if constexpr (d >= 1) {
-                for (int i = d + w; i < NB; i += NW) {
-                    const int j = i - d;
-                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int mm = 0; mm < d; ++mm) {
-                        const int m = j + mm;
-                        const f32x4 am = *reinterpret_cast<const f32x4*>(sA + (16 * i + r) * LD_CF + 16 * m + 4 * g);
-                        M::mma1(y, M::cvt(am), M::lds_quad_t(sT + 16 * m * LD_CE + 16 * j, LD_CE, tr_ce));
+                        for (int e = 0; e < 4; ++e) sTa[(16 * I + 4 * g + e) * LD_CE + 16 * J + r] = from_f32<E>(z[e] * aj);
                     }
-                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    M::mma1(z, M::lds_quad(sT + (16 * i + r) * LD_CE + 16 * i + 4 * g), M::cvt_neg(y));
-                    // z lane (r, g), element e: T[16 i + 4g + e][16 j + r]
-                    const float aj = sAlpha[16 * j + r];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sT[(16 * i + 4 * g + e) * LD_CE + 16 * j + r] = from_f32<E>(z[e]);
-                        sTa[(16 * i + 4 * g + e) * LD_CE + 16 * j + r] = from_f32<E>(z[e] * aj);
-                    }
-                }
-                __syncthreads();
+                });
             }
         });
+        __syncthreads();
 
         // ---- 4. the state-dependent part, per wave on its 16 columns ---------------------------------
         {

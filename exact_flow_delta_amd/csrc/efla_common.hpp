@@ -124,11 +124,24 @@ template <> struct Mma<float> {
     }
 };
 
-// wave-level sum over groups of `width` consecutive lanes (width a power of two <= 64)
+// x from another lane of the same 16-lane row, through a DPP lane move (no LDS traffic)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of WIDTH consecutive lanes (WIDTH a power of two <= 64); every lane of a
+// group receives the group's sum.  Within a 16-lane row the partners come from DPP moves: swap
+// neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror each half row, mirror the
+// row; wider groups add cross-row swizzles.
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < WIDTH; off <<= 1) x += __shfl_xor(x, off, 64);
+    if constexpr (WIDTH >= 2) x += dpp_mov<0xB1>(x);
+    if constexpr (WIDTH >= 4) x += dpp_mov<0x4E>(x);
+    if constexpr (WIDTH >= 8) x += dpp_mov<0x141>(x);
+    if constexpr (WIDTH >= 16) x += dpp_mov<0x140>(x);
+    if constexpr (WIDTH >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (WIDTH >= 64) x += __shfl_xor(x, 32, 64);
     return x;
 }
 
