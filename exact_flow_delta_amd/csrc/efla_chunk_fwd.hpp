@@ -16,16 +16,18 @@
 // independently, so slabs never talk to each other.  Each wave owns 16 columns of the slab and keeps
 // its d_k x 16 piece of S in fp32 accumulator registers for the whole sequence.  Per chunk:
 //   1. the chunk's Q, K, V slab (prefetched into registers during the previous chunk) go to LDS, with
-//      lambda = ||k||^2 reduced across the lanes holding a key row and alpha from it; the next chunk's
-//      global loads are issued right after;
-//   2. per wave, a Gram block row alpha_i k_i.k_j (upper tiles, stored transposed = lower) and a block
-//      row of Q K^T on the matrix cores; the wave then solves its 16x16 diagonal block of T by
-//      right-looking forward substitution in fp32 (lane r carries column r);
+//      lambda = ||k||^2 reduced across the lanes holding a key row; the next chunk's global loads are
+//      issued right after;
+//   2. per wave: alpha for 16 tokens, a Gram block row alpha_i k_i.k_j (upper tiles, stored transposed =
+//      lower) and a block row of Q K^T on the matrix cores; the wave then solves its 16x16 diagonal block
+//      of T by right-looking forward substitution in fp32 (lane r carries column r, the block's entries
+//      come straight from the Gram tile's registers through lane reads);
 //   3. the off-diagonal blocks of T, one block column per wave, walked down the column with the blocks
 //      found so far kept in registers: T_IJ = -T_II sum_m A_Im T_mJ on the matrix cores; T diag(alpha)
 //      is written as a matrix-core operand;
-//   4. per wave: X = [Q; K] S, R = V - K S, Delta = T diag(alpha) R, O = Q S + P Delta (stored),
-//      S += K^T Delta -- all on the matrix cores with the state as an in-register operand.
+//   4. per wave: K S and (Q S)^T, R = V - K S, Delta = T diag(alpha) R, O^T = (Q S)^T + Delta^T P^T
+//      (stored, four consecutive outputs per lane), S += K^T Delta -- all on the matrix cores with the
+//      state as an in-register operand.
 // Operands that must be read "down a column" (K^T, V, T as a right-hand factor) are fetched with the
 // transposing LDS read, so K, V and T live in LDS once, row-major.
 // bf16 inputs use the 16x16x32 bf16 instruction with fp32 accumulation (S, R, Delta and T diag(alpha)
@@ -61,16 +63,15 @@ struct ChunkLayout {
     static constexpr int LD_DK = DK + PAD;   // sQ, sK   [C][LD_DK]   storage type, row-major
     static constexpr int LD_V = DVS + PAD;   // sV       [C][LD_V]    storage type
     static constexpr int LD_CE = C + PAD;    // sA, sT, sTa, sP [C][LD_CE] storage type
-    static constexpr int LD_AT = 16 + 4;     // sAt      [C][LD_AT]   fp32, diagonal blocks of A transposed
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_K = OFF_Q + C * LD_DK * ESIZE;
     static constexpr int OFF_V = OFF_K + C * LD_DK * ESIZE;
     static constexpr int OFF_A = OFF_V + C * LD_V * ESIZE;    // alpha_i k_i.k_j, off-diagonal blocks
-    static constexpr int OFF_AT = OFF_A + C * LD_CE * ESIZE;
-    static constexpr int OFF_T = OFF_AT + C * LD_AT * 4;
+    static constexpr int OFF_T = OFF_A + C * LD_CE * ESIZE;
     static constexpr int OFF_TA = OFF_T + C * LD_CE * ESIZE;
     static constexpr int OFF_P = OFF_TA + C * LD_CE * ESIZE;
-    static constexpr int OFF_ALPHA = OFF_P + C * LD_CE * ESIZE;
+    static constexpr int OFF_LB = OFF_P + C * LD_CE * ESIZE;   // lambda[C], beta[C] (fp32)
+    static constexpr int OFF_ALPHA = OFF_LB + 2 * C * 4;
     static constexpr int BYTES = OFF_ALPHA + C * 4;
 };
 
@@ -80,7 +81,7 @@ constexpr int kMaxLdsBytes = 160 * 1024;
 template <int ESIZE>
 constexpr int chunk_layout_bytes(int dk, int c, int dvs) {
     const int pad = ESIZE == 2 ? 20 : 4;
-    return c * (dk + pad) * ESIZE * 2 + c * (dvs + pad) * ESIZE + c * 20 * 4 + c * (c + pad) * ESIZE * 4 + c * 4;
+    return c * (dk + pad) * ESIZE * 2 + c * (dvs + pad) * ESIZE + c * (c + pad) * ESIZE * 4 + c * 4 * 3;
 }
 
 // global -> register staging of one chunk; prefetched when it fits in a few registers per thread
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     constexpr int NT = NW * 64;
     constexpr int NB = C / 16;
     constexpr int NKD = DK / 16;
-    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE, LD_AT = LY::LD_AT;
+    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE;
     typedef ChunkStage<E, DK, C, DVS, NT> Stage;
     // prefetching keeps one chunk in registers: only when that is a few registers per thread
     constexpr bool kPrefetch = (2 * Stage::NQK + Stage::NV) <= 12;
@@ -145,7 +146,8 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     E* sK = reinterpret_cast<E*>(smem + LY::OFF_K);
     E* sV = reinterpret_cast<E*>(smem + LY::OFF_V);
     E* sA = reinterpret_cast<E*>(smem + LY::OFF_A);
-    float* sAt = reinterpret_cast<float*>(smem + LY::OFF_AT);
+    float* sLam = reinterpret_cast<float*>(smem + LY::OFF_LB);
+    float* sBeta = sLam + C;
     E* sT = reinterpret_cast<E*>(smem + LY::OFF_T);
     E* sTa = reinterpret_cast<E*>(smem + LY::OFF_TA);
     E* sP = reinterpret_cast<E*>(smem + LY::OFF_P);
@@ -212,7 +214,10 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
                         M::lds_store_quad(dk + 4 * h, quad{st.k[it][4 * h], st.k[it][4 * h + 1], st.k[it][4 * h + 2],
                                                            st.k[it][4 * h + 3]});
                     }
-                    if (cv == 0) sAlpha[t] = exact_alpha(st.beta[it], ss);
+                    if (cv == 0) {
+                        sLam[t] = ss;
+                        sBeta[t] = st.beta[it];
+                    }
                 }
             }
 #pragma unroll
@@ -236,79 +241,81 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
         __syncthreads();
 
         // ---- 2. per wave: Gram block row hi (-> A; its diagonal block is solved right here for T_hh) and
-        //         Q K^T block row NB-1-hi (-> P): NB+1 tiles per block row pair, the same for every wave
+        //         Q K^T block row NB-1-hi (-> P).  Both rows share the A-side K blocks; each row keeps its
+        //         B-side block (K_hi, Q_hp) in registers across its tiles.
         for (int hi = w; hi < NB; hi += NW) {
             const int hp = NB - 1 - hi;
-            static_for<NB + 1>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                const bool isG = j <= hi;
-                const int lo = isG ? j : j - hi - 1;
-                const int rowb = isG ? hi : hp;
-                const E* pa = sK + (16 * lo + r) * LD_DK + 4 * g;
-                const E* pb = (isG ? sK : sQ) + (16 * rowb + r) * LD_DK + 4 * g;
-                quad qa[NKD], qb[NKD];
+            // alpha of this block row's tokens (lane r: token 16 hi + r)
+            const float ar = exact_alpha(sBeta[16 * hi + r], sLam[16 * hi + r]);
+            if (g == 0) sAlpha[16 * hi + r] = ar;
+            quad bk[NKD], bq[NKD];
 #pragma unroll
-                for (int kd = 0; kd < NKD; ++kd) {
-                    qa[kd] = M::lds_quad(pa + 16 * kd);
-                    qb[kd] = M::lds_quad(pb + 16 * kd);
-                }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kd = 0; kd < NKD; ++kd) {
+                bk[kd] = M::lds_quad(sK + (16 * hi + r) * LD_DK + 4 * g + 16 * kd);
+                bq[kd] = M::lds_quad(sQ + (16 * hp + r) * LD_DK + 4 * g + 16 * kd);
+            }
+            static_for<NB>([&](auto lc) {
+                constexpr int lo = decltype(lc)::value;
+                if (lo <= hi || lo <= hp) {
+                    quad ak[NKD];
 #pragma unroll
-                for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, qa[kd], qa[kd + 1], qb[kd], qb[kd + 1]);
-                if constexpr (NKD & 1) M::mma1(acc, qa[NKD - 1], qb[NKD - 1]);
-                // acc lane (r, g), element i: X[16 lo + 4g + i][16 rowb + r] with X = K K^T or K Q^T,
-                // i.e. entry (row, col + i) of K K^T or Q K^T with row = 16 rowb + r, col = 16 lo + 4g
-                const int row = 16 * rowb + r;
-                const int col = 16 * lo + 4 * g;
-                if (isG) {
-                    const float ar = sAlpha[row];
-                    f32x4 out;
+                    for (int kd = 0; kd < NKD; ++kd) ak[kd] = M::lds_quad(sK + (16 * lo + r) * LD_DK + 4 * g + 16 * kd);
+                    const int col = 16 * lo + 4 * g;
+                    if (lo <= hi) {
+                        // acc lane (r, g), element i: (K K^T)[16 hi + r][16 lo + 4g + i]
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) out[i] = (col + i < row) ? ar * acc[i] : 0.0f;
-                    if (lo < hi) {
-                        M::lds_store_quad(sA + row * LD_CE + col, M::cvt(out));
-                    } else {
-                        // diagonal block: At[m][i] = A[16 hi + i][16 hi + m] (column m as a row), fp32
+                        for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, ak[kd], ak[kd + 1], bk[kd], bk[kd + 1]);
+                        if constexpr (NKD & 1) M::mma1(acc, ak[NKD - 1], bk[NKD - 1]);
+                        const int row = 16 * hi + r;
+                        f32x4 out;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sAt[(col + i) * LD_AT + r] = out[i];
+                        for (int i = 0; i < 4; ++i) out[i] = (col + i < row) ? ar * acc[i] : 0.0f;
+                        if (lo < hi) {
+                            M::lds_store_quad(sA + row * LD_CE + col, M::cvt(out));
+                        } else {
+                            // T_hh = (I + A_hh)^{-1} by right-looking substitution; lane r carries column r.
+                            // A_hh[i][m] sits in lane i + 16 (m / 4), element m % 4 of `out`: read it with a
+                            // lane read (a wave-uniform scalar), so the sweep never touches LDS.
+                            float sv[16];
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+#pragma unroll
+                            for (int m = 0; m < 15; ++m) {
+                                // (the element is copied to a scalar first: a bit cast applied directly to a
+                                // vector element expression picked element 0 with this toolchain)
+                                const float om = out[m & 3];
+#pragma unroll
+                                for (int i = m + 1; i < 16; ++i) {
+                                    const float aim = __builtin_bit_cast(
+                                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, om), i + 16 * (m >> 2)));
+                                    sv[i] -= aim * sv[m];
+                                }
+                            }
+                            if (g == 0) {
+                                const int b0 = 16 * hi;
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) {
+                                    sT[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i]);
+                                    sTa[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i] * ar);
+                                }
+                            }
+                        }
                     }
-                } else {
-                    f32x4 out;
+                    if (lo <= hp) {
+                        // acc lane (r, g), element i: (Q K^T)[16 hp + r][16 lo + 4g + i]
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) out[i] = (col + i <= row) ? acc[i] : 0.0f;
-                    M::lds_store_quad(sP + row * LD_CE + col, M::cvt(out));
+                        for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, ak[kd], ak[kd + 1], bq[kd], bq[kd + 1]);
+                        if constexpr (NKD & 1) M::mma1(acc, ak[NKD - 1], bq[NKD - 1]);
+                        const int row = 16 * hp + r;
+                        f32x4 out;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) out[i] = (col + i <= row) ? acc[i] : 0.0f;
+                        M::lds_store_quad(sP + row * LD_CE + col, M::cvt(out));
+                    }
                 }
             });
-            // T_hh = (I + A_hh)^{-1}: right-looking substitution, lane r of the first group holds column r.
-            // The block was written to LDS by this wave just above (LDS operations of a wave stay in order).
-            __asm__ volatile("" ::: "memory");
-            if (g == 0) {
-                const int b0 = 16 * hi;
-                float sv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
-#pragma unroll
-                for (int m = 0; m < 15; ++m) {
-                    const float* colm = sAt + (b0 + m) * LD_AT;   // A[b0 + i][b0 + m], i = 0..15
-                    float c[16];
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                        const f32x4 x = *reinterpret_cast<const f32x4*>(colm + 4 * i4);
-                        c[4 * i4] = x[0];
-                        c[4 * i4 + 1] = x[1];
-                        c[4 * i4 + 2] = x[2];
-                        c[4 * i4 + 3] = x[3];
-                    }
-#pragma unroll
-                    for (int i = m + 1; i < 16; ++i) sv[i] -= c[i] * sv[m];
-                }
-                const float ar = sAlpha[b0 + r];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    sT[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i]);
-                    sTa[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i] * ar);
-                }
-            }
         }
         __syncthreads();
 
@@ -347,21 +354,24 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
             quad Sq[NKD];
 #pragma unroll
             for (int rt = 0; rt < NKD; ++rt) Sq[rt] = M::cvt(S[rt]);
-            f32x4 XQ[NB];
+            // Ot = (Q S)^T accumulates O transposed: lane (r, g), element e = O[16 rb + r][colw + 4g + e], so each
+            // lane later stores four consecutive outputs of one token.  (Q S)^T = S^T Q^T takes the state quads
+            // as the A operand and the same row quads of Q as the B operand.
+            f32x4 Ot[NB];
             quad Rq[NB];
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
                 f32x4 xk = {0.f, 0.f, 0.f, 0.f};
-                XQ[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Ot[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 const E* pq = sQ + (16 * rb + r) * LD_DK + 4 * g;
                 const E* pk = sK + (16 * rb + r) * LD_DK + 4 * g;
 #pragma unroll
                 for (int kd = 0; kd + 1 < NKD; kd += 2) {
-                    M::mma2(XQ[rb], M::lds_quad(pq + 16 * kd), M::lds_quad(pq + 16 * kd + 16), Sq[kd], Sq[kd + 1]);
+                    M::mma2(Ot[rb], Sq[kd], Sq[kd + 1], M::lds_quad(pq + 16 * kd), M::lds_quad(pq + 16 * kd + 16));
                     M::mma2(xk, M::lds_quad(pk + 16 * kd), M::lds_quad(pk + 16 * kd + 16), Sq[kd], Sq[kd + 1]);
                 }
                 if constexpr (NKD & 1) {
-                    M::mma1(XQ[rb], M::lds_quad(pq + 16 * (NKD - 1)), Sq[NKD - 1]);
+                    M::mma1(Ot[rb], Sq[NKD - 1], M::lds_quad(pq + 16 * (NKD - 1)));
                     M::mma1(xk, M::lds_quad(pk + 16 * (NKD - 1)), Sq[NKD - 1]);
                 }
                 // R = V - K S: lane (r, g), element e: row 16 rb + 4g + e, column 16 w + r of the slab
@@ -384,20 +394,18 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
                 if constexpr ((rb + 1) & 1) M::mma1(acc, M::lds_quad(pt + 16 * rb), Rq[rb]);
                 Dq[rb] = M::cvt(acc);
             });
-            // O = Q S + lower_incl(Q K^T) Delta, written straight from the accumulators
+            // O^T = (Q S)^T + Delta^T lower_incl(Q K^T)^T: Delta quads as the A operand, row quads of P as B;
+            // each lane stores four consecutive outputs of token 16 rb + r with one vector store
             static_for<NB>([&](auto rbc) {
                 constexpr int rb = decltype(rbc)::value;
                 const E* pp = sP + (16 * rb + r) * LD_CE + 4 * g;
                 static_for<(rb + 1) / 2>([&](auto hc) {
                     constexpr int kb = 2 * decltype(hc)::value;
-                    M::mma2(XQ[rb], M::lds_quad(pp + 16 * kb), M::lds_quad(pp + 16 * kb + 16), Dq[kb], Dq[kb + 1]);
+                    M::mma2(Ot[rb], Dq[kb], Dq[kb + 1], M::lds_quad(pp + 16 * kb), M::lds_quad(pp + 16 * kb + 16));
                 });
-                if constexpr ((rb + 1) & 1) M::mma1(XQ[rb], M::lds_quad(pp + 16 * rb), Dq[rb]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * rb + 4 * g + e;
-                    if (t < n) o[(tok0 + t0 + t) * DV + colw + r] = from_f32<E>(XQ[rb][e]);
-                }
+                if constexpr ((rb + 1) & 1) M::mma1(Ot[rb], Dq[rb], M::lds_quad(pp + 16 * rb));
+                const int t = 16 * rb + r;
+                if (t < n) *reinterpret_cast<quad*>(o + (tok0 + t0 + t) * DV + colw + 4 * g) = M::cvt(Ot[rb]);
             });
             // S += K^T Delta (K^T blocks fetched down the columns of K)
 #pragma unroll
