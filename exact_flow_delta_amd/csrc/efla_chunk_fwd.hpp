@@ -20,16 +20,17 @@
 //      issued right after;
 //   2. per wave: alpha for 16 tokens, a Gram block row alpha_i k_i.k_j (upper tiles, stored transposed =
 //      lower) and a block row of Q K^T on the matrix cores; the wave then solves its 16x16 diagonal block
-//      of T by right-looking forward substitution in fp32 (lane r carries column r, the block's entries
-//      come straight from the Gram tile's registers through lane reads);
+//      of T by right-looking forward substitution in fp32 (lane r carries column r; step m reads column m
+//      of the block as one broadcast LDS row);
 //   3. the off-diagonal blocks of T, one block column per wave, walked down the column with the blocks
 //      found so far kept in registers: T_IJ = -T_II sum_m A_Im T_mJ on the matrix cores; T diag(alpha)
 //      is written as a matrix-core operand;
 //   4. per wave: K S and (Q S)^T, R = V - K S, Delta = T diag(alpha) R, O^T = (Q S)^T + Delta^T P^T
 //      (stored, four consecutive outputs per lane), S += K^T Delta -- all on the matrix cores with the
 //      state as an in-register operand.
-// Operands that must be read "down a column" (K^T, V, T as a right-hand factor) are fetched with the
-// transposing LDS read, so K, V and T live in LDS once, row-major.
+// Operands that must be read "down a column" (K^T, V) are fetched with the transposing LDS read, so K and
+// V live in LDS once, row-major.  T and T diag(alpha) are stored transposed (every writer then emits
+// contiguous runs) and read back with plain or transposing quad reads as the product needs.
 // bf16 inputs use the 16x16x32 bf16 instruction with fp32 accumulation (S, R, Delta and T diag(alpha)
 // are rounded to bf16 only as instruction operands; the carried state stays fp32); fp32 inputs use the
 // 16x16x4 fp32 instruction throughout.
@@ -62,14 +63,16 @@ struct ChunkLayout {
     static constexpr int PAD = ESIZE == 2 ? 20 : 4;
     static constexpr int LD_DK = DK + PAD;   // sQ, sK   [C][LD_DK]   storage type, row-major
     static constexpr int LD_V = DVS + PAD;   // sV       [C][LD_V]    storage type
-    static constexpr int LD_CE = C + PAD;    // sA, sT, sTa, sP [C][LD_CE] storage type
+    static constexpr int LD_CE = C + PAD;    // sA, sTt, sTat, sP [C][LD_CE] storage type
+    static constexpr int LD_AT = 16 + 4;     // sAt [C][LD_AT] fp32: diagonal blocks of A, transposed
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_K = OFF_Q + C * LD_DK * ESIZE;
     static constexpr int OFF_V = OFF_K + C * LD_DK * ESIZE;
     static constexpr int OFF_A = OFF_V + C * LD_V * ESIZE;    // alpha_i k_i.k_j, off-diagonal blocks
-    static constexpr int OFF_T = OFF_A + C * LD_CE * ESIZE;
-    static constexpr int OFF_TA = OFF_T + C * LD_CE * ESIZE;
-    static constexpr int OFF_P = OFF_TA + C * LD_CE * ESIZE;
+    static constexpr int OFF_AT = OFF_A + C * LD_CE * ESIZE;
+    static constexpr int OFF_TT = OFF_AT + C * LD_AT * 4;       // T^T (diagonal blocks used)
+    static constexpr int OFF_TAT = OFF_TT + C * LD_CE * ESIZE;  // (T diag(alpha))^T
+    static constexpr int OFF_P = OFF_TAT + C * LD_CE * ESIZE;
     static constexpr int OFF_LB = OFF_P + C * LD_CE * ESIZE;   // lambda[C], beta[C] (fp32)
     static constexpr int OFF_ALPHA = OFF_LB + 2 * C * 4;
     static constexpr int BYTES = OFF_ALPHA + C * 4;
@@ -81,7 +84,7 @@ constexpr int kMaxLdsBytes = 160 * 1024;
 template <int ESIZE>
 constexpr int chunk_layout_bytes(int dk, int c, int dvs) {
     const int pad = ESIZE == 2 ? 20 : 4;
-    return c * (dk + pad) * ESIZE * 2 + c * (dvs + pad) * ESIZE + c * (c + pad) * ESIZE * 4 + c * 4 * 3;
+    return c * (dk + pad) * ESIZE * 2 + c * (dvs + pad) * ESIZE + c * (c + pad) * ESIZE * 4 + c * 20 * 4 + c * 4 * 3;
 }
 
 // global -> register staging of one chunk; prefetched when it fits in a few registers per thread
@@ -99,6 +102,11 @@ struct ChunkStage {
     __device__ __forceinline__ void load(const E* __restrict__ gq, const E* __restrict__ gk, const E* __restrict__ gv,
                                          const float* __restrict__ gbeta, int64_t tok, int n, int DV, int slab_col,
                                          int tid) {
+        // chunk base pointers are uniform; lanes add 32-bit offsets
+        const E* q0 = gq + tok * DK;
+        const E* k0 = gk + tok * DK;
+        const E* v0 = gv + tok * DV + slab_col;
+        const float* b0 = gbeta + tok;
 #pragma unroll
         for (int it = 0; it < NQK; ++it) {
             const int idx = it * NT + tid;
@@ -108,9 +116,9 @@ struct ChunkStage {
             k[it] = V16{};
             beta[it] = 0.0f;
             if (idx < C * VPR && t < n) {
-                q[it] = *reinterpret_cast<const V16*>(gq + (tok + t) * DK + cv * VEC);
-                k[it] = *reinterpret_cast<const V16*>(gk + (tok + t) * DK + cv * VEC);
-                if (cv == 0) beta[it] = gbeta[tok + t];
+                q[it] = *reinterpret_cast<const V16*>(q0 + (t * DK + cv * VEC));
+                k[it] = *reinterpret_cast<const V16*>(k0 + (t * DK + cv * VEC));
+                if (cv == 0) beta[it] = b0[t];
             }
         }
 #pragma unroll
@@ -119,7 +127,7 @@ struct ChunkStage {
             const int t = idx / VPRV;
             const int cv = idx % VPRV;
             v[it] = V16{};
-            if (idx < C * VPRV && t < n) v[it] = *reinterpret_cast<const V16*>(gv + (tok + t) * DV + slab_col + cv * VEC);
+            if (idx < C * VPRV && t < n) v[it] = *reinterpret_cast<const V16*>(v0 + (t * DV + cv * VEC));
         }
     }
 };
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     constexpr int NT = NW * 64;
     constexpr int NB = C / 16;
     constexpr int NKD = DK / 16;
-    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE;
+    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE, LD_AT = LY::LD_AT;
     typedef ChunkStage<E, DK, C, DVS, NT> Stage;
     // prefetching keeps one chunk in registers: only when that is a few registers per thread
     constexpr bool kPrefetch = (2 * Stage::NQK + Stage::NV) <= 12;
@@ -148,8 +156,9 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     E* sA = reinterpret_cast<E*>(smem + LY::OFF_A);
     float* sLam = reinterpret_cast<float*>(smem + LY::OFF_LB);
     float* sBeta = sLam + C;
-    E* sT = reinterpret_cast<E*>(smem + LY::OFF_T);
-    E* sTa = reinterpret_cast<E*>(smem + LY::OFF_TA);
+    float* sAt = reinterpret_cast<float*>(smem + LY::OFF_AT);
+    E* sTt = reinterpret_cast<E*>(smem + LY::OFF_TT);
+    E* sTat = reinterpret_cast<E*>(smem + LY::OFF_TAT);
     E* sP = reinterpret_cast<E*>(smem + LY::OFF_P);
     float* sAlpha = reinterpret_cast<float*>(smem + LY::OFF_ALPHA);
 
@@ -197,23 +206,10 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
                 const int idx = it * NT + tid;
                 const int t = idx / Stage::VPR;
                 const int cv = idx % Stage::VPR;
-                float ss = 0.0f;
-#pragma unroll
-                for (int e = 0; e < Stage::VEC; ++e) {
-                    const float f = to_f32<E>(st.k[it][e]);
-                    ss += f * f;
-                }
-                ss = group_sum<Stage::VPR>(ss);
+                const float ss = group_sum<Stage::VPR>(sum_sq(st.k[it]));
                 if (idx < C * Stage::VPR) {
-                    E* dq = sQ + t * LD_DK + cv * Stage::VEC;
-                    E* dk = sK + t * LD_DK + cv * Stage::VEC;
-#pragma unroll
-                    for (int h = 0; h < Stage::VEC / 4; ++h) {
-                        M::lds_store_quad(dq + 4 * h, quad{st.q[it][4 * h], st.q[it][4 * h + 1], st.q[it][4 * h + 2],
-                                                           st.q[it][4 * h + 3]});
-                        M::lds_store_quad(dk + 4 * h, quad{st.k[it][4 * h], st.k[it][4 * h + 1], st.k[it][4 * h + 2],
-                                                           st.k[it][4 * h + 3]});
-                    }
+                    lds_store_vec16(sQ + t * LD_DK + cv * Stage::VEC, st.q[it]);
+                    lds_store_vec16(sK + t * LD_DK + cv * Stage::VEC, st.k[it]);
                     if (cv == 0) {
                         sLam[t] = ss;
                         sBeta[t] = st.beta[it];
@@ -226,11 +222,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
                 if (idx < C * Stage::VPRV) {
                     const int t = idx / Stage::VPRV;
                     const int cv = idx % Stage::VPRV;
-                    E* dv = sV + t * LD_V + cv * Stage::VEC;
-#pragma unroll
-                    for (int h = 0; h < Stage::VEC / 4; ++h)
-                        M::lds_store_quad(dv + 4 * h, quad{st.v[it][4 * h], st.v[it][4 * h + 1], st.v[it][4 * h + 2],
-                                                           st.v[it][4 * h + 3]});
+                    lds_store_vec16(sV + t * LD_V + cv * Stage::VEC, st.v[it]);
                 }
             }
             if constexpr (kPrefetch) {
@@ -243,8 +235,10 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
         // ---- 2. per wave: Gram block row hi (-> A; its diagonal block is solved right here for T_hh) and
         //         Q K^T block row NB-1-hi (-> P).  Both rows share the A-side K blocks; each row keeps its
         //         B-side block (K_hi, Q_hp) in registers across its tiles.
-        for (int hi = w; hi < NB; hi += NW) {
-            const int hp = NB - 1 - hi;
+        static_for<NB>([&](auto hc) {
+          constexpr int hi = decltype(hc)::value;
+          constexpr int hp = NB - 1 - hi;
+          if (hi % NW == w) {
             // alpha of this block row's tokens (lane r: token 16 hi + r)
             const float ar = exact_alpha(sBeta[16 * hi + r], sLam[16 * hi + r]);
             if (g == 0) sAlpha[16 * hi + r] = ar;
@@ -256,12 +250,12 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
             }
             static_for<NB>([&](auto lc) {
                 constexpr int lo = decltype(lc)::value;
-                if (lo <= hi || lo <= hp) {
+                if constexpr (lo <= hi || lo <= hp) {
                     quad ak[NKD];
 #pragma unroll
                     for (int kd = 0; kd < NKD; ++kd) ak[kd] = M::lds_quad(sK + (16 * lo + r) * LD_DK + 4 * g + 16 * kd);
                     const int col = 16 * lo + 4 * g;
-                    if (lo <= hi) {
+                    if constexpr (lo <= hi) {
                         // acc lane (r, g), element i: (K K^T)[16 hi + r][16 lo + 4g + i]
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -271,38 +265,15 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
                         f32x4 out;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) out[i] = (col + i < row) ? ar * acc[i] : 0.0f;
-                        if (lo < hi) {
+                        if constexpr (lo < hi) {
                             M::lds_store_quad(sA + row * LD_CE + col, M::cvt(out));
                         } else {
-                            // T_hh = (I + A_hh)^{-1} by right-looking substitution; lane r carries column r.
-                            // A_hh[i][m] sits in lane i + 16 (m / 4), element m % 4 of `out`: read it with a
-                            // lane read (a wave-uniform scalar), so the sweep never touches LDS.
-                            float sv[16];
+                            // diagonal block, transposed: At[16 hi + m][i] = A[16 hi + i][16 hi + m]
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
-#pragma unroll
-                            for (int m = 0; m < 15; ++m) {
-                                // (the element is copied to a scalar first: a bit cast applied directly to a
-                                // vector element expression picked element 0 with this toolchain)
-                                const float om = out[m & 3];
-#pragma unroll
-                                for (int i = m + 1; i < 16; ++i) {
-                                    const float aim = __builtin_bit_cast(
-                                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, om), i + 16 * (m >> 2)));
-                                    sv[i] -= aim * sv[m];
-                                }
-                            }
-                            if (g == 0) {
-                                const int b0 = 16 * hi;
-#pragma unroll
-                                for (int i = 0; i < 16; ++i) {
-                                    sT[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i]);
-                                    sTa[(b0 + i) * LD_CE + b0 + r] = from_f32<E>(sv[i] * ar);
-                                }
-                            }
+                            for (int i = 0; i < 4; ++i) sAt[(col + i) * LD_AT + r] = out[i];
                         }
                     }
-                    if (lo <= hp) {
+                    if constexpr (lo <= hp) {
                         // acc lane (r, g), element i: (Q K^T)[16 hp + r][16 lo + 4g + i]
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -316,7 +287,42 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
                     }
                 }
             });
-        }
+            // T_hh = (I + A_hh)^{-1} by right-looking substitution; lane r carries column r and step m reads
+            // column m of the block as a broadcast row of At (written by this wave in the loop above; LDS
+            // operations of a wave complete in order).  Rows are read three steps ahead of their use.
+            __asm__ volatile("" ::: "memory");
+            {
+                const float* at = sAt + 16 * hi * LD_AT;
+                float sv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+                f32x4 ring[4][4];
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) ring[m][i4] = *reinterpret_cast<const f32x4*>(at + m * LD_AT + 4 * i4);
+                }
+#pragma unroll
+                for (int m = 0; m < 15; ++m) {
+                    if (m + 3 < 15) {
+#pragma unroll
+                        for (int i4 = (m + 3) / 4; i4 < 4; ++i4)
+                            ring[(m + 3) & 3][i4] = *reinterpret_cast<const f32x4*>(at + (m + 3) * LD_AT + 4 * i4);
+                    }
+#pragma unroll
+                    for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
+                }
+                // lane (r, g) writes T[16 hi + 4g + e][16 hi + r], e = 0..3: four consecutive entries of row
+                // 16 hi + r of T^T, and the same scaled by alpha_{16 hi + r}
+                f32x4 mine;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mine[e] = g == 0 ? sv[e] : g == 1 ? sv[4 + e] : g == 2 ? sv[8 + e] : sv[12 + e];
+                const int b0 = 16 * hi;
+                M::lds_store_quad(sTt + (b0 + r) * LD_CE + b0 + 4 * g, M::cvt(mine));
+                M::lds_store_quad(sTat + (b0 + r) * LD_CE + b0 + 4 * g, M::cvt(mine * ar));
+            }
+          }
+        });
         __syncthreads();
 
         // ---- 3. off-diagonal blocks of T, one block column J per wave, walked down the column with the
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
             constexpr int J = decltype(jc)::value;
             if (J % NW == w) {
                 quad Tq[NB];
-                Tq[J] = M::lds_quad_t(sT + 16 * J * LD_CE + 16 * J, LD_CE, tr_ce);
+                Tq[J] = M::lds_quad(sTt + (16 * J + r) * LD_CE + 16 * J + 4 * g);   // T_JJ as B: row quad of T^T
                 const float aj = sAlpha[16 * J + r];
                 static_for<NB>([&](auto ic) {
                     constexpr int I = decltype(ic)::value;
@@ -338,11 +344,11 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
                         });
                         if constexpr ((I - J) & 1) M::mma1(y, M::lds_quad(pa + 16 * (I - 1)), Tq[I - 1]);
                         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                        M::mma1(z, M::lds_quad(sT + (16 * I + r) * LD_CE + 16 * I + 4 * g), M::cvt_neg(y));
-                        // z lane (r, g), element e: T[16 I + 4g + e][16 J + r]
+                        // T_II as A: column quad of T^T
+                        M::mma1(z, M::lds_quad_t(sTt + 16 * I * LD_CE + 16 * I, LD_CE, tr_ce), M::cvt_neg(y));
+                        // z lane (r, g), element e: T[16 I + 4g + e][16 J + r] = T^T[16 J + r][16 I + 4g + e]
                         Tq[I] = M::cvt(z);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sTa[(16 * I + 4 * g + e) * LD_CE + 16 * J + r] = from_f32<E>(z[e] * aj);
+                        M::lds_store_quad(sTat + (16 * J + r) * LD_CE + 16 * I + 4 * g, M::cvt(z * aj));
                     }
                 });
             }
@@ -386,12 +392,14 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
             static_for<NB>([&](auto rbc) {
                 constexpr int rb = decltype(rbc)::value;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const E* pt = sTa + (16 * rb + r) * LD_CE + 4 * g;
+                // A quads of T diag(alpha) = column quads of its stored transpose
+                const E* pt = sTat + 16 * rb;
                 static_for<(rb + 1) / 2>([&](auto hc) {
                     constexpr int kb = 2 * decltype(hc)::value;
-                    M::mma2(acc, M::lds_quad(pt + 16 * kb), M::lds_quad(pt + 16 * kb + 16), Rq[kb], Rq[kb + 1]);
+                    M::mma2(acc, M::lds_quad_t(pt + 16 * kb * LD_CE, LD_CE, tr_ce),
+                            M::lds_quad_t(pt + 16 * (kb + 1) * LD_CE, LD_CE, tr_ce), Rq[kb], Rq[kb + 1]);
                 });
-                if constexpr ((rb + 1) & 1) M::mma1(acc, M::lds_quad(pt + 16 * rb), Rq[rb]);
+                if constexpr ((rb + 1) & 1) M::mma1(acc, M::lds_quad_t(pt + 16 * rb * LD_CE, LD_CE, tr_ce), Rq[rb]);
                 Dq[rb] = M::cvt(acc);
             });
             // O^T = (Q S)^T + Delta^T lower_incl(Q K^T)^T: Delta quads as the A operand, row quads of P as B;

@@ -53,6 +53,26 @@ template <typename E> struct Vec16;
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum of squares of a 16-byte vector, accumulated in fp32 (bf16 products are exact in fp32)
+__device__ __forceinline__ float sum_sq(f32x4 x) { return x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]; }
+__device__ __forceinline__ float sum_sq(bf16x8 x) {
+    float s = 0.0f;
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), __builtin_shufflevector(x, x, 0, 1), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), __builtin_shufflevector(x, x, 2, 3), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), __builtin_shufflevector(x, x, 4, 5), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), __builtin_shufflevector(x, x, 6, 7), s, false);
+    return s;
+}
+
+// store a 16-byte vector to an LDS address that is only 8-byte aligned (two 8-byte halves)
+__device__ __forceinline__ void lds_store_vec16(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ __forceinline__ void lds_store_vec16(bf16* p, bf16x8 x) {
+    *reinterpret_cast<bf16x4*>(p) = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4*>(p + 4) = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+}
+
 // ------------------------------------------------------------------------------------------------
 // matrix-core policy per operand type
 // ------------------------------------------------------------------------------------------------
