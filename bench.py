@@ -2,8 +2,11 @@
 """Benchmark of the EFLA hot path on one MI355X.
 
 One step = one chunked forward of the LM-layer workload (B8 H16 L4096 d_k = d_v = 128, bf16 q/k/v/o,
-fp32 beta and state, chunk 64, zero initial state, final state returned): the exact gate, the
-intra-chunk UT transform and the inter-chunk state pass all run inside the fused kernel.
+fp32 beta and state, chunk 64, zero initial state, final state returned), as the library's default
+two-launch form: the UT transform of all 8192 (head, chunk) pairs (exact gate included) into a workspace,
+then the inter-chunk state pass.  The two launches are also timed one by one (HIP events on the stream
+they run on, through the stand-alone UT and state-pass entry points, which launch the same kernels), and
+the roofline line is the state-pass kernel's, the dominant one.
 The batched decode workload (256 sequences x 32 heads, d 128, 512 MiB fp32 state, 64 dependent
 one-token steps, one launch per step) is timed in the same run and reported under "decode".
 
@@ -29,6 +32,16 @@ sys.path.insert(0, ROOT)
 METRIC = "EFLA chunked-fwd tokens/s at B8 H16 L4096 d128; % MFMA peak; decode HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+
+
+def chain_algorithmic(B, H, L, dk, dv, esize=2):
+    """Bytes the state pass must move: q, k, v read and o written once per token-head, the fp32 final state."""
+    return B * H * L * (2 * dk + 2 * dv) * esize + B * H * dk * dv * 4
+
+
+def ut_algorithmic(B, H, L, dk, esize=2):
+    """Bytes the UT transform must read: k and beta once per token-head."""
+    return B * H * L * (dk * esize + 4)
 
 
 def fwd_algorithmic(B, H, L, dk, dv, C, esize=2):
@@ -82,20 +95,42 @@ def run_forward(efla, W, torch, steps, warmup):
     o = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.bfloat16, device="cuda")
     S = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
     del x
+    nbytes = efla.chunk_workspace_size(w.B, w.H, w.L, w.chunk, torch.bfloat16)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    nc, nb = (w.L + w.chunk - 1) // w.chunk, (w.chunk // 16) * (w.chunk // 16 + 1) // 2
+    t = ws.view(torch.bfloat16).view(w.B, w.H, nc, nb, 64, 4)
+
+    def step():
+        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws)
+
     for _ in range(warmup):
-        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S)
+        step()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
-        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S)
+        step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     assert torch.isfinite(S).all().item(), "non-finite final state"
+
+    # the same two kernels, one entry point each, with events between them (all on torch's current stream,
+    # which is the stream the library launches on)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    for i in range(steps):
+        ev[3 * i].record()
+        efla.ut_transform(k, beta, chunk_size=w.chunk, out=t)
+        ev[3 * i + 1].record()
+        efla.state_pass(q, k, v, t, chunk_size=w.chunk, out=o, final_state=S)
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    ut_ms = statistics.mean(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps))
+    chain_ms = statistics.mean(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))
     wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
-    return w, ms, dict(workgroups=wg, slab_width=slab, lds_bytes=lds)
+    return w, ms, dict(ut_ms=ut_ms, chain_ms=chain_ms, workspace_bytes=nbytes,
+                       launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds, ut_workgroups=w.B * w.H * nc))
 
 
 def run_decode(efla, W, torch, warmup=3):
@@ -179,14 +214,18 @@ def main():
         print(json.dumps({"leg": "decode", "median_step_ms": statistics.median(step_ms)}), flush=True)
         return
 
-    w, ms, plan = run_forward(efla, W, torch, args.steps, args.warmup)
+    w, ms, info = run_forward(efla, W, torch, args.steps, args.warmup)
     if args.only == "fwd":
-        print(json.dumps({"leg": "fwd", "ms_per_step": ms, "launch": plan}), flush=True)
+        print(json.dumps({"leg": "fwd", "ms_per_step": ms, **info}), flush=True)
         return
     tokens_per_s = w.B * w.L / (ms * 1e-3)
     nbytes, flops = fwd_algorithmic(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
-    achieved_gbs = nbytes / (ms * 1e-3) / 1e9
+    chain_bytes = chain_algorithmic(w.B, w.H, w.L, w.d_k, w.d_v)
+    ut_bytes = ut_algorithmic(w.B, w.H, w.L, w.d_k)
+    chain_gbs = chain_bytes / (info["chain_ms"] * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
+    chain_kernel = "chain_kernel<bf16,128,64,64>"
+    ut_kernel = "ut_kernel<bf16,128,64>"
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -201,11 +240,16 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "lm_layer_fwd", "B": w.B, "H": w.H, "L": w.L, "d_k": w.d_k, "d_v": w.d_v,
-                   "chunk": w.chunk, "io": "bf16", "state": "fp32", "launch": plan},
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("chunk_fwd_kernel<bf16,128,64,64>"),
-                     "kernel": "chunk_fwd_kernel<bf16,128,64,64>", "bytes_per_launch": nbytes},
+                   "chunk": w.chunk, "io": "bf16", "state": "fp32", "method": "split", **info["launch"]},
+        "roofline": {"bound": "hbm", "achieved": round(chain_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(chain_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(chain_kernel),
+                     "kernel": chain_kernel, "bytes_per_launch": chain_bytes,
+                     "avg_launch_ms": round(info["chain_ms"], 5)},
+        "ut": {"kernel": ut_kernel, "avg_launch_ms": round(info["ut_ms"], 5), "bytes_per_launch": ut_bytes,
+               "achieved_gbs": round(ut_bytes / (info["ut_ms"] * 1e-3) / 1e9, 1),
+               "workspace_bytes": info["workspace_bytes"], "traffic": measured_traffic(ut_kernel)},
+        "step": {"algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                 "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops},
     }

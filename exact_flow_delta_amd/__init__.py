@@ -8,6 +8,10 @@ library is missing, every call raises.
     o, S = chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_size=64)
     o    = recurrent_step(q, k, v, beta, state)          # state updated in place
     a    = alpha(k, beta)
+    t    = ut_transform(k, beta, chunk_size=64)          # T diag(alpha) per chunk (operand layout)
+
+chunk_fwd runs the two-launch form by default (UT transform of all chunks into a workspace, then the
+state pass); method="fused" runs the single-kernel form, which needs no workspace.
 
 The operator ("Exact Flow Linear Attention" (gist.science), Metodologia items 1-3; "Error-Free
 Linear Attention is a Free Lunch" (howistudyai.com), Steps 1-4):
@@ -23,18 +27,20 @@ import os
 
 import torch
 
-__all__ = ["EflaError", "alpha", "chunk_fwd", "recurrent_step", "chunk_plan", "library_path", "load_library"]
+__all__ = ["EflaError", "alpha", "chunk_fwd", "recurrent_step", "chunk_plan", "chunk_workspace_size", "ut_transform",
+           "state_pass", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libefla.so")
 _lib = None
 
-EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_NO_DEVICE, EFLA_ERR_HIP = range(5)
+EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_NO_DEVICE, EFLA_ERR_HIP, EFLA_ERR_WORKSPACE = range(6)
 EFLA_F32, EFLA_BF16 = 0, 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int
 _i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
 
 
 class EflaError(RuntimeError):
@@ -67,7 +73,16 @@ def load_library():
     lib.efla_recurrent_step.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp]
     lib.efla_chunk_fwd_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                         ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
-    for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan"):
+    lib.efla_chunk_fwd_split_plan.argtypes = lib.efla_chunk_fwd_plan.argtypes
+    lib.efla_chunk_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+    lib.efla_ut_transform.argtypes = [_vp, _vp, _i32, _vp, _sz, _i32, _i32, _i32, _i32, _i32, _vp]
+    lib.efla_chunk_fwd_split.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+    lib.efla_chunk_state_pass.argtypes = [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _vp, _vp,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
+               "efla_chunk_fwd_split_plan", "efla_chunk_workspace_size", "efla_ut_transform", "efla_chunk_fwd_split",
+               "efla_chunk_state_pass"):
         getattr(lib, fn).restype = _i32
     lib.efla_status_string.argtypes = [_i32]
     lib.efla_status_string.restype = ctypes.c_char_p
@@ -132,12 +147,50 @@ def alpha(k: torch.Tensor, beta: torch.Tensor, out: torch.Tensor | None = None) 
     return out
 
 
+def _dtype_of(dtype) -> int:
+    return EFLA_BF16 if dtype == torch.bfloat16 else EFLA_F32
+
+
+def chunk_workspace_size(B, H, L, chunk=64, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace the two-launch chunked forward needs (= size of the UT transform output)."""
+    lib = load_library()
+    n = _sz()
+    _check(lib.efla_chunk_workspace_size(B, H, L, chunk, _dtype_of(dtype), ctypes.byref(n)),
+           "efla_chunk_workspace_size")
+    return n.value
+
+
+def ut_transform(k, beta, chunk_size=64, out=None):
+    """T diag(alpha) of every chunk, T = (I + strict_lower(diag(alpha) K K^T))^{-1}, in the library's
+    operand layout: a tensor [B, H, ceil(L/chunk), nblocks, 64, 4] of k's dtype, where block
+    rb (rb+1)/2 + kb (kb <= rb < chunk/16) holds at [lane = 16 g + r][j] the entry
+    (T diag(alpha))[16 rb + r][16 kb + 4 g + j] of that chunk.
+    """
+    lib = load_library()
+    _dev_tensor(k, "k")
+    _dev_tensor(beta, "beta")
+    B, H, L, d_k = k.shape
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, L):
+        raise ValueError("beta must be float32 [B,H,L]")
+    nb = (chunk_size // 16) * (chunk_size // 16 + 1) // 2
+    nc = (L + chunk_size - 1) // chunk_size
+    if out is None:
+        out = torch.empty((B, H, nc, nb, 64, 4), dtype=k.dtype, device=k.device)
+    _dev_tensor(out, "out")
+    _check(lib.efla_ut_transform(_ptr(k), _ptr(beta), _dtype_code(k), _ptr(out), out.numel() * out.element_size(),
+                                 B, H, L, d_k, int(chunk_size), _stream(k.device)), "efla_ut_transform")
+    return out
+
+
 def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_size=64, dv_slab=0,
-              out=None, final_state=None):
+              out=None, final_state=None, method="split", workspace=None):
     """Chunkwise-parallel EFLA forward over [B,H,L,*] inputs.
 
     Returns (o [B,H,L,d_v] in the input dtype, final state [B,H,d_k,d_v] fp32 or None).
     ``final_state`` may be passed (and may be ``initial_state`` itself) to receive the state in place.
+    ``method`` is "split" (UT transform launch + state-pass launch, through ``workspace``: a device
+    tensor of at least chunk_workspace_size(...) bytes, allocated here when not given) or "fused" (one
+    kernel, no workspace).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
@@ -163,9 +216,50 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
         _dev_tensor(final_state, "final_state")
         if final_state.dtype != torch.float32 or tuple(final_state.shape) != (B, H, d_k, d_v):
             raise ValueError("final_state must be float32 [B,H,d_k,d_v]")
-    _check(lib.efla_chunk_fwd_slab(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
-                                   _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
-                                   int(dv_slab), _stream(v.device)), "efla_chunk_fwd")
+    if method == "fused":
+        _check(lib.efla_chunk_fwd_slab(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                       _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
+                                       int(dv_slab), _stream(v.device)), "efla_chunk_fwd")
+    elif method == "split":
+        need = chunk_workspace_size(B, H, L, int(chunk_size), v.dtype)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+        _dev_tensor(workspace, "workspace")
+        _check(lib.efla_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                        _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
+                                        int(dv_slab), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(v.device)), "efla_chunk_fwd_split")
+    else:
+        raise ValueError("method must be 'split' or 'fused'")
+    return out, final_state
+
+
+def state_pass(q, k, v, t, initial_state=None, output_final_state=True, chunk_size=64, dv_slab=0, out=None,
+               final_state=None):
+    """Inter-chunk state pass alone, from ``t`` = ut_transform(k, beta, chunk_size).
+
+    Returns (o, final state or None) exactly as chunk_fwd(method="split") would.
+    """
+    lib = load_library()
+    for name, x in (("q", q), ("k", k), ("v", v), ("t", t)):
+        _dev_tensor(x, name)
+    B, H, L, d_k = k.shape
+    d_v = v.shape[-1]
+    if tuple(q.shape) != (B, H, L, d_k) or tuple(v.shape[:3]) != (B, H, L):
+        raise ValueError("q, k, v shapes disagree")
+    if out is None:
+        out = torch.empty((B, H, L, d_v), dtype=v.dtype, device=v.device)
+    _dev_tensor(out, "out")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=v.device)
+    for name, x in (("initial_state", initial_state), ("final_state", final_state)):
+        if x is not None:
+            _dev_tensor(x, name)
+            if x.dtype != torch.float32 or tuple(x.shape) != (B, H, d_k, d_v):
+                raise ValueError("%s must be float32 [B,H,d_k,d_v]" % name)
+    _check(lib.efla_chunk_state_pass(_ptr(q), _ptr(k), _ptr(v), _ptr(t), t.numel() * t.element_size(),
+                                     _dtype_code(v), _ptr(out), _ptr(initial_state), _ptr(final_state), B, H, L, d_k,
+                                     d_v, int(chunk_size), int(dv_slab), _stream(v.device)), "efla_chunk_state_pass")
     return out, final_state
 
 
@@ -197,11 +291,11 @@ def recurrent_step(q, k, v, beta, state, out=None):
     return out
 
 
-def chunk_plan(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, dv_slab=0):
-    """(workgroups, slab width, LDS bytes) that chunk_fwd would launch; host only."""
+def chunk_plan(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, dv_slab=0, method="split"):
+    """(workgroups, slab width, LDS bytes) of the state-carrying launch chunk_fwd would make; host only."""
     lib = load_library()
     wg, sw, lds = _i32(), _i32(), _i32()
-    code = EFLA_BF16 if dtype == torch.bfloat16 else EFLA_F32
-    _check(lib.efla_chunk_fwd_plan(B, H, L, d_k, d_v, chunk, code, dv_slab, ctypes.byref(wg), ctypes.byref(sw),
-                                   ctypes.byref(lds)), "efla_chunk_fwd_plan")
+    fn = lib.efla_chunk_fwd_split_plan if method == "split" else lib.efla_chunk_fwd_plan
+    _check(fn(B, H, L, d_k, d_v, chunk, _dtype_of(dtype), dv_slab, ctypes.byref(wg), ctypes.byref(sw),
+              ctypes.byref(lds)), "chunk_plan")
     return wg.value, sw.value, lds.value

@@ -7,6 +7,7 @@
 
 #include "efla.h"
 #include "efla_chunk_fwd.hpp"
+#include "efla_chunk_split.hpp"
 #include "efla_launch.hpp"
 
 namespace {
@@ -43,6 +44,13 @@ efla_status device_present() {
     return EFLA_OK;
 }
 
+int split_lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) {
+    const int b = dt == EFLA_BF16 ? efla::chain_layout_bytes<2>(d_k, chunk, dvs)
+                                  : efla::chain_layout_bytes<4>(d_k, chunk, dvs);
+    const int u = dt == EFLA_BF16 ? efla::ut_layout_bytes<2>(d_k, chunk) : efla::ut_layout_bytes<4>(d_k, chunk);
+    return (b <= efla::kMaxLdsBytes && u <= efla::kMaxLdsBytes) ? b : -1;
+}
+
 int lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) {
     const int b = dt == EFLA_BF16 ? efla::chunk_layout_bytes<2>(d_k, chunk, dvs)
                                   : efla::chunk_layout_bytes<4>(d_k, chunk, dvs);
@@ -51,29 +59,73 @@ int lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) {
 
 // Slab width: the widest (fewest waves re-reading the chunk data) that still gives the GPU enough
 // workgroups; narrower when B*H is small so that more compute units carry a slab.
-int auto_slab(int64_t BH, int d_k, int d_v, int chunk, efla_dtype dt) {
+int kernel_lds(bool split, efla_dtype dt, int d_k, int chunk, int dvs) {
+    return split ? split_lds_bytes(dt, d_k, chunk, dvs) : lds_bytes(dt, d_k, chunk, dvs);
+}
+
+int auto_slab(bool split, int64_t BH, int d_k, int d_v, int chunk, efla_dtype dt) {
     int dvs = d_v < 64 ? d_v : 64;
     while (dvs > 16 && BH * (d_v / dvs) < 256) dvs /= 2;
-    while (dvs > 16 && lds_bytes(dt, d_k, chunk, dvs) < 0) dvs /= 2;
+    while (dvs > 16 && kernel_lds(split, dt, d_k, chunk, dvs) < 0) dvs /= 2;
     return dvs;
 }
 
-efla_status check_chunk_sizes(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, int dv_slab,
-                              int* dvs_out) {
+efla_status check_chunk_sizes(bool split, int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt,
+                              int dv_slab, int* dvs_out) {
     if (!valid_dtype(dt)) return EFLA_ERR_INVALID_ARG;
     if (B < 0 || H < 0 || L < 0) return EFLA_ERR_INVALID_ARG;
     if ((int64_t)B * H > INT32_MAX) return EFLA_ERR_INVALID_ARG;
     if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
     if (dv_slab != 0 && dv_slab != 16 && dv_slab != 32 && dv_slab != 64) return EFLA_ERR_UNSUPPORTED;
     if (dv_slab != 0 && (dv_slab > d_v || d_v % dv_slab != 0)) return EFLA_ERR_UNSUPPORTED;
-    const int dvs = dv_slab ? dv_slab : auto_slab((int64_t)B * H, d_k, d_v, chunk, dt);
-    if (lds_bytes(dt, d_k, chunk, dvs) < 0) return EFLA_ERR_UNSUPPORTED;
+    const int dvs = dv_slab ? dv_slab : auto_slab(split, (int64_t)B * H, d_k, d_v, chunk, dt);
+    if (kernel_lds(split, dt, d_k, chunk, dvs) < 0) return EFLA_ERR_UNSUPPORTED;
     if (efla::chunk_grid((int)((int64_t)B * H), d_v, dvs) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    // the UT launch has one workgroup per (batch*head, chunk)
+    if (split && (int64_t)B * H * ((L + chunk - 1) / chunk) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
     *dvs_out = dvs;
     return EFLA_OK;
 }
 
+// pointer checks shared by the chunked-forward entry points (sizes already validated); beta is
+// required unless need_beta is false (the state pass alone does not read it)
+efla_status check_fwd_buffers(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                              const void* o, const float* initial_state, const float* final_state, int64_t BH, int L,
+                              int d_k, int d_v, bool need_beta = true) {
+    const size_t es = esize(dtype);
+    const size_t nq = (size_t)BH * L * d_k * es, nv = (size_t)BH * L * d_v * es, nb = (size_t)BH * L * 4;
+    const size_t ns = (size_t)BH * d_k * d_v * 4;
+    if (L > 0 && BH > 0) {
+        if (!q || !k || !v || (need_beta && !beta) || !o) return EFLA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(beta, 4))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+        return EFLA_ERR_INVALID_ARG;
+    // o overlaps nothing; the final state overlaps no input; initial and final state are identical or disjoint
+    if (overlap(o, nv, q, nq) || overlap(o, nv, k, nq) || overlap(o, nv, v, nv) || overlap(o, nv, beta, nb) ||
+        overlap(o, nv, initial_state, ns) || overlap(o, nv, final_state, ns))
+        return EFLA_ERR_INVALID_ARG;
+    if (overlap(final_state, ns, q, nq) || overlap(final_state, ns, k, nq) || overlap(final_state, ns, v, nv) ||
+        overlap(final_state, ns, beta, nb))
+        return EFLA_ERR_INVALID_ARG;
+    if ((const void*)initial_state != (const void*)final_state && overlap(initial_state, ns, final_state, ns))
+        return EFLA_ERR_INVALID_ARG;
+    return EFLA_OK;
+}
+
+size_t ut_bytes(int64_t BH, int L, int chunk, efla_dtype dt) {
+    return (size_t)BH * (size_t)((L + chunk - 1) / chunk) * (size_t)efla::ut_block_elems(chunk) * esize(dt);
+}
+
 }  // namespace
+
+namespace efla {
+int chain_lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) { return split_lds_bytes(dt, d_k, chunk, dvs); }
+int ut_lds_bytes(efla_dtype dt, int d_k, int chunk) {
+    return dt == EFLA_BF16 ? ut_layout_bytes<2>(d_k, chunk) : ut_layout_bytes<4>(d_k, chunk);
+}
+}  // namespace efla
 
 namespace efla {
 int chunk_lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) { return lds_bytes(dt, d_k, chunk, dvs); }
@@ -82,7 +134,7 @@ int64_t chunk_grid(int BH, int d_v, int dvs) { return (int64_t)((BH + 7) / 8) * 
 
 extern "C" {
 
-int efla_version(void) { return 10000; }
+int efla_version(void) { return 10100; }
 
 const char* efla_status_string(efla_status s) {
     switch (s) {
@@ -91,6 +143,7 @@ const char* efla_status_string(efla_status s) {
         case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED: size or type combination not built";
         case EFLA_ERR_NO_DEVICE: return "EFLA_ERR_NO_DEVICE: no HIP device";
         case EFLA_ERR_HIP: return "EFLA_ERR_HIP: HIP runtime error";
+        case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     }
     return "EFLA: unknown status";
 }
@@ -117,7 +170,7 @@ efla_status efla_alpha(const void* k, efla_dtype k_dtype, const float* beta, flo
 efla_status efla_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int dv_slab,
                                 int* workgroups, int* slab_width, int* lds) {
     int dvs = 0;
-    const efla_status st = check_chunk_sizes(B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
+    const efla_status st = check_chunk_sizes(false, B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
     if (st != EFLA_OK) return st;
     if (workgroups) *workgroups = (int)efla::chunk_grid(B * H, d_v, dvs);
     if (slab_width) *slab_width = dvs;
@@ -129,28 +182,11 @@ efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, con
                                 void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
                                 int d_v, int chunk, int dv_slab, void* stream) {
     int dvs = 0;
-    efla_status st = check_chunk_sizes(B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
+    efla_status st = check_chunk_sizes(false, B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
     if (st != EFLA_OK) return st;
     const int64_t BH = (int64_t)B * H;
-    const size_t es = esize(dtype);
-    const size_t nq = (size_t)BH * L * d_k * es, nv = (size_t)BH * L * d_v * es, nb = (size_t)BH * L * 4;
-    const size_t ns = (size_t)BH * d_k * d_v * 4;
-    if (L > 0 && BH > 0) {
-        if (!q || !k || !v || !beta || !o) return EFLA_ERR_INVALID_ARG;
-        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(beta, 4))
-            return EFLA_ERR_INVALID_ARG;
-    }
-    if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
-        return EFLA_ERR_INVALID_ARG;
-    // o overlaps nothing; the final state overlaps no input; initial and final state are identical or disjoint
-    if (overlap(o, nv, q, nq) || overlap(o, nv, k, nq) || overlap(o, nv, v, nv) || overlap(o, nv, beta, nb) ||
-        overlap(o, nv, initial_state, ns) || overlap(o, nv, final_state, ns))
-        return EFLA_ERR_INVALID_ARG;
-    if (overlap(final_state, ns, q, nq) || overlap(final_state, ns, k, nq) || overlap(final_state, ns, v, nv) ||
-        overlap(final_state, ns, beta, nb))
-        return EFLA_ERR_INVALID_ARG;
-    if ((const void*)initial_state != (const void*)final_state && overlap(initial_state, ns, final_state, ns))
-        return EFLA_ERR_INVALID_ARG;
+    st = check_fwd_buffers(q, k, v, beta, dtype, o, initial_state, final_state, BH, L, d_k, d_v);
+    if (st != EFLA_OK) return st;
     if (BH == 0) return EFLA_OK;
     if (L == 0 && !final_state) return EFLA_OK;
     st = device_present();
@@ -159,6 +195,91 @@ efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, con
     const hipError_t e = dtype == EFLA_BF16 ? efla::launch_chunk_fwd_bf16(a, (hipStream_t)stream)
                                             : efla::launch_chunk_fwd_f32(a, (hipStream_t)stream);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd launch");
+}
+
+
+efla_status efla_chunk_workspace_size(int B, int H, int L, int chunk, efla_dtype dtype, size_t* bytes) {
+    if (!valid_dtype(dtype) || B < 0 || H < 0 || L < 0 || !bytes) return EFLA_ERR_INVALID_ARG;
+    if (!valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
+    *bytes = ut_bytes((int64_t)B * H, L, chunk, dtype);
+    return EFLA_OK;
+}
+
+efla_status efla_ut_transform(const void* k, const float* beta, efla_dtype dtype, void* t_out, size_t t_out_bytes,
+                              int B, int H, int L, int d_k, int chunk, void* stream) {
+    if (!valid_dtype(dtype) || B < 0 || H < 0 || L < 0) return EFLA_ERR_INVALID_ARG;
+    if (!valid_dim(d_k) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    if (BH > INT32_MAX || BH * ((L + chunk - 1) / chunk) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    if (BH == 0 || L == 0) return EFLA_OK;
+    if (!k || !beta || !aligned(k, 16) || !aligned(beta, 4)) return EFLA_ERR_INVALID_ARG;
+    const size_t need = ut_bytes(BH, L, chunk, dtype);
+    if (!t_out || !aligned(t_out, 16) || t_out_bytes < need) return EFLA_ERR_WORKSPACE;
+    const size_t nk = (size_t)BH * L * d_k * esize(dtype), nb = (size_t)BH * L * 4;
+    if (overlap(t_out, need, k, nk) || overlap(t_out, need, beta, nb)) return EFLA_ERR_INVALID_ARG;
+    const efla_status st = device_present();
+    if (st != EFLA_OK) return st;
+    const hipError_t e = dtype == EFLA_BF16 ? efla::launch_ut_bf16(k, beta, t_out, (int)BH, L, d_k, chunk, (hipStream_t)stream)
+                                            : efla::launch_ut_f32(k, beta, t_out, (int)BH, L, d_k, chunk, (hipStream_t)stream);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_ut_transform launch");
+}
+
+efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int dv_slab,
+                                      int* workgroups, int* slab_width, int* lds) {
+    int dvs = 0;
+    const efla_status st = check_chunk_sizes(true, B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
+    if (st != EFLA_OK) return st;
+    if (workgroups) *workgroups = (int)efla::chunk_grid(B * H, d_v, dvs);
+    if (slab_width) *slab_width = dvs;
+    if (lds) *lds = split_lds_bytes(dtype, d_k, chunk, dvs);
+    return EFLA_OK;
+}
+
+namespace {
+efla_status split_entry(bool with_ut, const void* q, const void* k, const void* v, const float* beta,
+                        efla_dtype dtype, void* o, const float* initial_state, float* final_state, int B, int H, int L,
+                        int d_k, int d_v, int chunk, int dv_slab, void* tw, size_t tw_bytes, void* stream) {
+    int dvs = 0;
+    efla_status st = check_chunk_sizes(true, B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
+    if (st != EFLA_OK) return st;
+    const int64_t BH = (int64_t)B * H;
+    st = check_fwd_buffers(q, k, v, beta, dtype, o, initial_state, final_state, BH, L, d_k, d_v, with_ut);
+    if (st != EFLA_OK) return st;
+    const size_t need = ut_bytes(BH, L, chunk, dtype);
+    if (need > 0) {
+        if (!tw || !aligned(tw, 16) || tw_bytes < need) return EFLA_ERR_WORKSPACE;
+        const size_t es = esize(dtype);
+        const size_t nq = (size_t)BH * L * d_k * es, nv = (size_t)BH * L * d_v * es, nb = (size_t)BH * L * 4;
+        const size_t ns = (size_t)BH * d_k * d_v * 4;
+        if (overlap(tw, need, q, nq) || overlap(tw, need, k, nq) || overlap(tw, need, v, nv) ||
+            overlap(tw, need, beta, nb) || overlap(tw, need, o, nv) || overlap(tw, need, initial_state, ns) ||
+            overlap(tw, need, final_state, ns))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if (BH == 0) return EFLA_OK;
+    if (L == 0 && !final_state) return EFLA_OK;
+    st = device_present();
+    if (st != EFLA_OK) return st;
+    efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, tw, (int)BH, L, d_k, d_v, chunk, dvs};
+    const hipError_t e = dtype == EFLA_BF16 ? efla::launch_split_fwd_bf16(a, with_ut, (hipStream_t)stream)
+                                            : efla::launch_split_fwd_f32(a, with_ut, (hipStream_t)stream);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, with_ut ? "efla_chunk_fwd_split launch" : "efla_chunk_state_pass launch");
+}
+}  // namespace
+
+efla_status efla_chunk_fwd_split(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                 void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
+                                 int d_v, int chunk, int dv_slab, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return split_entry(true, q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, dv_slab,
+                       workspace, workspace_bytes, stream);
+}
+
+efla_status efla_chunk_state_pass(const void* q, const void* k, const void* v, const void* t_in, size_t t_in_bytes,
+                                  efla_dtype dtype, void* o, const float* initial_state, float* final_state, int B,
+                                  int H, int L, int d_k, int d_v, int chunk, int dv_slab, void* stream) {
+    return split_entry(false, q, k, v, nullptr, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, dv_slab,
+                       const_cast<void*>(t_in), t_in_bytes, stream);
 }
 
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype, void* o,

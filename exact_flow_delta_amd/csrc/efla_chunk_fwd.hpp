@@ -36,24 +36,11 @@
 // 16x16x4 fp32 instruction throughout.
 #pragma once
 
-#include <type_traits>
-
 #include "efla_common.hpp"
 #include "efla_launch.hpp"
+#include "efla_ut.hpp"
 
 namespace efla {
-
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for_impl(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for_impl<I + 1, N>(f);
-    }
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl<0, N>(f);
-}
 
 // LDS carve-up of one workgroup.  Row strides of the storage-type matrices are padded by 20 elements
 // for bf16 (40 bytes: quad reads of 16 consecutive rows hit distinct banks and the transposing reads
@@ -64,21 +51,18 @@ struct ChunkLayout {
     static constexpr int LD_DK = DK + PAD;   // sQ, sK   [C][LD_DK]   storage type, row-major
     static constexpr int LD_V = DVS + PAD;   // sV       [C][LD_V]    storage type
     static constexpr int LD_CE = C + PAD;    // sA, sTt, sTat, sP [C][LD_CE] storage type
-    static constexpr int LD_AT = 16 + 4;     // sAt [C][LD_AT] fp32: diagonal blocks of A, transposed
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_K = OFF_Q + C * LD_DK * ESIZE;
     static constexpr int OFF_V = OFF_K + C * LD_DK * ESIZE;
     static constexpr int OFF_A = OFF_V + C * LD_V * ESIZE;    // alpha_i k_i.k_j, off-diagonal blocks
     static constexpr int OFF_AT = OFF_A + C * LD_CE * ESIZE;
-    static constexpr int OFF_TT = OFF_AT + C * LD_AT * 4;       // T^T (diagonal blocks used)
+    static constexpr int OFF_TT = OFF_AT + C * kLdAt * 4;       // T^T (diagonal blocks used)
     static constexpr int OFF_TAT = OFF_TT + C * LD_CE * ESIZE;  // (T diag(alpha))^T
     static constexpr int OFF_P = OFF_TAT + C * LD_CE * ESIZE;
     static constexpr int OFF_LB = OFF_P + C * LD_CE * ESIZE;   // lambda[C], beta[C] (fp32)
     static constexpr int OFF_ALPHA = OFF_LB + 2 * C * 4;
     static constexpr int BYTES = OFF_ALPHA + C * 4;
 };
-
-constexpr int kMaxLdsBytes = 160 * 1024;
 
 // host-side mirror of ChunkLayout::BYTES
 template <int ESIZE>
@@ -143,7 +127,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     constexpr int NT = NW * 64;
     constexpr int NB = C / 16;
     constexpr int NKD = DK / 16;
-    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE, LD_AT = LY::LD_AT;
+    constexpr int LD_DK = LY::LD_DK, LD_V = LY::LD_V, LD_CE = LY::LD_CE;
     typedef ChunkStage<E, DK, C, DVS, NT> Stage;
     // prefetching keeps one chunk in registers: only when that is a few registers per thread
     constexpr bool kPrefetch = (2 * Stage::NQK + Stage::NV) <= 12;
@@ -235,124 +219,12 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
         // ---- 2. per wave: Gram block row hi (-> A; its diagonal block is solved right here for T_hh) and
         //         Q K^T block row NB-1-hi (-> P).  Both rows share the A-side K blocks; each row keeps its
         //         B-side block (K_hi, Q_hp) in registers across its tiles.
-        static_for<NB>([&](auto hc) {
-          constexpr int hi = decltype(hc)::value;
-          constexpr int hp = NB - 1 - hi;
-          if (hi % NW == w) {
-            // alpha of this block row's tokens (lane r: token 16 hi + r)
-            const float ar = exact_alpha(sBeta[16 * hi + r], sLam[16 * hi + r]);
-            if (g == 0) sAlpha[16 * hi + r] = ar;
-            quad bk[NKD], bq[NKD];
-#pragma unroll
-            for (int kd = 0; kd < NKD; ++kd) {
-                bk[kd] = M::lds_quad(sK + (16 * hi + r) * LD_DK + 4 * g + 16 * kd);
-                bq[kd] = M::lds_quad(sQ + (16 * hp + r) * LD_DK + 4 * g + 16 * kd);
-            }
-            static_for<NB>([&](auto lc) {
-                constexpr int lo = decltype(lc)::value;
-                if constexpr (lo <= hi || lo <= hp) {
-                    quad ak[NKD];
-#pragma unroll
-                    for (int kd = 0; kd < NKD; ++kd) ak[kd] = M::lds_quad(sK + (16 * lo + r) * LD_DK + 4 * g + 16 * kd);
-                    const int col = 16 * lo + 4 * g;
-                    if constexpr (lo <= hi) {
-                        // acc lane (r, g), element i: (K K^T)[16 hi + r][16 lo + 4g + i]
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, ak[kd], ak[kd + 1], bk[kd], bk[kd + 1]);
-                        if constexpr (NKD & 1) M::mma1(acc, ak[NKD - 1], bk[NKD - 1]);
-                        const int row = 16 * hi + r;
-                        f32x4 out;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) out[i] = (col + i < row) ? ar * acc[i] : 0.0f;
-                        if constexpr (lo < hi) {
-                            M::lds_store_quad(sA + row * LD_CE + col, M::cvt(out));
-                        } else {
-                            // diagonal block, transposed: At[16 hi + m][i] = A[16 hi + i][16 hi + m]
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) sAt[(col + i) * LD_AT + r] = out[i];
-                        }
-                    }
-                    if constexpr (lo <= hp) {
-                        // acc lane (r, g), element i: (Q K^T)[16 hp + r][16 lo + 4g + i]
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, ak[kd], ak[kd + 1], bq[kd], bq[kd + 1]);
-                        if constexpr (NKD & 1) M::mma1(acc, ak[NKD - 1], bq[NKD - 1]);
-                        const int row = 16 * hp + r;
-                        f32x4 out;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) out[i] = (col + i <= row) ? acc[i] : 0.0f;
-                        M::lds_store_quad(sP + row * LD_CE + col, M::cvt(out));
-                    }
-                }
-            });
-            // T_hh = (I + A_hh)^{-1} by right-looking substitution; lane r carries column r and step m reads
-            // column m of the block as a broadcast row of At (written by this wave in the loop above; LDS
-            // operations of a wave complete in order).  Rows are read three steps ahead of their use.
-            __asm__ volatile("" ::: "memory");
-            {
-                const float* at = sAt + 16 * hi * LD_AT;
-                float sv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
-                f32x4 ring[4][4];
-#pragma unroll
-                for (int m = 0; m < 3; ++m) {
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) ring[m][i4] = *reinterpret_cast<const f32x4*>(at + m * LD_AT + 4 * i4);
-                }
-#pragma unroll
-                for (int m = 0; m < 15; ++m) {
-                    if (m + 3 < 15) {
-#pragma unroll
-                        for (int i4 = (m + 3) / 4; i4 < 4; ++i4)
-                            ring[(m + 3) & 3][i4] = *reinterpret_cast<const f32x4*>(at + (m + 3) * LD_AT + 4 * i4);
-                    }
-#pragma unroll
-                    for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
-                }
-                // lane (r, g) writes T[16 hi + 4g + e][16 hi + r], e = 0..3: four consecutive entries of row
-                // 16 hi + r of T^T, and the same scaled by alpha_{16 hi + r}
-                f32x4 mine;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mine[e] = g == 0 ? sv[e] : g == 1 ? sv[4 + e] : g == 2 ? sv[8 + e] : sv[12 + e];
-                const int b0 = 16 * hi;
-                M::lds_store_quad(sTt + (b0 + r) * LD_CE + b0 + 4 * g, M::cvt(mine));
-                M::lds_store_quad(sTat + (b0 + r) * LD_CE + b0 + 4 * g, M::cvt(mine * ar));
-            }
-          }
-        });
+        ut_rows<E, DK, C, NW, LD_DK, LD_CE, true>(sQ, sK, sLam, sBeta, sA, sAt, sTt, sTat, sP, sAlpha, w, r, g);
         __syncthreads();
 
         // ---- 3. off-diagonal blocks of T, one block column J per wave, walked down the column with the
         //         blocks already found kept in registers: T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ
-        static_for<NB - 1>([&](auto jc) {
-            constexpr int J = decltype(jc)::value;
-            if (J % NW == w) {
-                quad Tq[NB];
-                Tq[J] = M::lds_quad(sTt + (16 * J + r) * LD_CE + 16 * J + 4 * g);   // T_JJ as B: row quad of T^T
-                const float aj = sAlpha[16 * J + r];
-                static_for<NB>([&](auto ic) {
-                    constexpr int I = decltype(ic)::value;
-                    if constexpr (I > J) {
-                        const E* pa = sA + (16 * I + r) * LD_CE + 4 * g;
-                        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                        static_for<(I - J) / 2>([&](auto pc) {
-                            constexpr int m = J + 2 * decltype(pc)::value;
-                            M::mma2(y, M::lds_quad(pa + 16 * m), M::lds_quad(pa + 16 * m + 16), Tq[m], Tq[m + 1]);
-                        });
-                        if constexpr ((I - J) & 1) M::mma1(y, M::lds_quad(pa + 16 * (I - 1)), Tq[I - 1]);
-                        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                        // T_II as A: column quad of T^T
-                        M::mma1(z, M::lds_quad_t(sTt + 16 * I * LD_CE + 16 * I, LD_CE, tr_ce), M::cvt_neg(y));
-                        // z lane (r, g), element e: T[16 I + 4g + e][16 J + r] = T^T[16 J + r][16 I + 4g + e]
-                        Tq[I] = M::cvt(z);
-                        M::lds_store_quad(sTat + (16 * J + r) * LD_CE + 16 * I + 4 * g, M::cvt(z * aj));
-                    }
-                });
-            }
-        });
+        ut_offdiag<E, C, NW, LD_CE>(sA, sTt, sTat, sAlpha, w, r, g, tr_ce);
         __syncthreads();
 
         // ---- 4. the state-dependent part, per wave on its 16 columns ---------------------------------

@@ -24,6 +24,39 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 
+constexpr int kMaxLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
+
+// ------------------------------------------------------------------------------------------------
+// Buffer resources (CDNA raw buffers: stride 0, byte-granular range check).  A load whose offset
+// falls outside [0, bytes) returns zeros and such a store is dropped by the address unit, so a
+// ragged tail needs neither a branch nor an exec mask, and the compiler can count outstanding
+// memory operations exactly.  Third descriptor word as for every gfx9-family part.
+// ------------------------------------------------------------------------------------------------
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ V buffer_load(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    static_assert(sizeof(V) == 16 || sizeof(V) == 8, "8- or 16-byte vectors");
+    if constexpr (sizeof(V) == 16) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+    } else {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, 0, 0));
+    }
+}
+template <typename V>
+__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t rs, int byte_off, V x) {
+    static_assert(sizeof(V) == 16 || sizeof(V) == 8, "8- or 16-byte vectors");
+    if constexpr (sizeof(V) == 16) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, byte_off, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), rs, byte_off, 0, 0);
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // The exact gate.  alpha = (1 - e^{-beta lambda}) / lambda, evaluated as -expm1(-x)/lambda with
 // x = beta*lambda so that small x does not cancel; x == 0 (lambda == 0 or beta == 0) gives the

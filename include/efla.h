@@ -15,7 +15,8 @@
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers (memory from hipMalloc / a PyTorch CUDA tensor) unless stated.
  *     The library never allocates, frees or keeps device memory, and keeps no state between calls
- *     apart from a thread-local copy of the last HIP error text.
+ *     apart from a thread-local copy of the last HIP error text.  Calls that need scratch memory
+ *     take a caller-owned workspace and say how large it must be.
  *   - Layouts are contiguous row-major.  q, k: [B,H,L,d_k]; v, o: [B,H,L,d_v]; beta: [B,H,L];
  *     state: [B,H,d_k,d_v] (S as the update writes it: row i is key dimension i).
  *   - q, k, v, o use the storage type `dtype` (fp32 or bf16).  beta, alpha and the state are fp32.
@@ -44,7 +45,8 @@ typedef enum {
     EFLA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, overlapping buffers, bad enum */
     EFLA_ERR_UNSUPPORTED = 2,   /* d_k, d_v, chunk or dtype combination this build does not provide    */
     EFLA_ERR_NO_DEVICE = 3,     /* no HIP device is visible to the process                             */
-    EFLA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed                          */
+    EFLA_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed                          */
+    EFLA_ERR_WORKSPACE = 5      /* workspace / output buffer missing, misaligned or smaller than needed */
 } efla_status;
 
 typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
@@ -114,6 +116,67 @@ efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, con
 efla_status efla_recurrent_step(const void* q, const void* k, const void* v, const float* beta,
                                 efla_dtype dtype, float* state, void* o,
                                 int64_t NH, int d_k, int d_v, void* stream);
+
+/*
+ * efla_chunk_workspace_size -- bytes of the workspace efla_chunk_fwd_split needs, which is also the
+ * size of the efla_ut_transform output: ceil(L / chunk) * (chunk/16)(chunk/16 + 1)/2 * 256 elements of
+ * the storage type per (batch, head).  Host only.  Fills *bytes and returns EFLA_OK, or INVALID_ARG
+ * (negative size, bad dtype, NULL bytes) / UNSUPPORTED (chunk).
+ */
+efla_status efla_chunk_workspace_size(int B, int H, int L, int chunk, efla_dtype dtype, size_t* bytes);
+
+/*
+ * efla_ut_transform -- the intra-chunk UT transform alone: for every chunk of C = chunk tokens of every
+ * (batch, head), with alpha the exact gate of its tokens,
+ *   A = strict_lower(diag(alpha) K K^T),  T = (I + A)^{-1},  output T diag(alpha)  (C x C, lower).
+ * "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 4 (precompute the within-chunk
+ * transforms in parallel); "Exact Flow Linear Attention" (gist.science), Metodologia item 3 (the update
+ * keeps the delta-rule rank-1 form, so the WY/UT representation applies).  A short last chunk is padded
+ * with zero keys and zero beta, so its missing rows and columns of T diag(alpha) are zero.
+ *   k      [B,H,L,d_k] dtype, read only;  beta [B,H,L] fp32, read only
+ *   t_out  written, t_out_bytes >= efla_chunk_workspace_size(...) (else EFLA_ERR_WORKSPACE), 16-byte
+ *          aligned, no overlap with k or beta.  Layout, in the storage type, per (bh, chunk c): the
+ *          (C/16)(C/16+1)/2 lower 16x16 blocks (rb, kb), kb <= rb, in the order rb (rb+1)/2 + kb, each as
+ *          256 elements [lane][j] with lane = 16 g + r holding (T diag(alpha))[16 rb + r][16 kb + 4 g + j]
+ *          (the matrix-core operand layout in which efla_chunk_fwd_split consumes it).
+ * The substitution runs in fp32; the bf16 build rounds the result to bf16.  L == 0 is a no-op.
+ */
+efla_status efla_ut_transform(const void* k, const float* beta, efla_dtype dtype, void* t_out, size_t t_out_bytes,
+                              int B, int H, int L, int d_k, int chunk, void* stream);
+
+/*
+ * efla_chunk_fwd_split -- efla_chunk_fwd as two launches on `stream`: efla_ut_transform of every chunk into
+ * `workspace`, then the inter-chunk state pass, which reads T diag(alpha) from it.  Same operator, arguments,
+ * aliasing rules and errors as efla_chunk_fwd_slab, plus:
+ *   workspace        device memory of at least efla_chunk_workspace_size(B, H, L, chunk, dtype) bytes,
+ *                    16-byte aligned, overlapping no other argument (else EFLA_ERR_WORKSPACE /
+ *                    EFLA_ERR_INVALID_ARG); its contents on return are the UT output described above.
+ * The UT launch spreads over all (batch*head, chunk) pairs, so the serial state pass carries only the
+ * state-dependent products.  Calls that share a workspace must be ordered on one stream.
+ */
+efla_status efla_chunk_fwd_split(const void* q, const void* k, const void* v, const float* beta,
+                                 efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                 int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * efla_chunk_state_pass -- the inter-chunk state pass alone, from a UT output made beforehand by
+ * efla_ut_transform (same k, beta, B, H, L, d_k, chunk, dtype).  For each (batch, head), S starts at
+ * initial_state (or 0) and, chunk after chunk, with Ta = T diag(alpha) read from t_in:
+ *   Delta = Ta (V - K S),  O = Q S + lower_incl(Q K^T) Delta,  S <- S + K^T Delta
+ * ("Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 4: chunks joined by passing the
+ * state; Step 3: o_t = S_t^T q_t after each token's update).  efla_chunk_fwd_split is efla_ut_transform
+ * followed by this call, and gives bit-identical results.
+ *   t_in  read only, t_in_bytes >= efla_chunk_workspace_size(...) (else EFLA_ERR_WORKSPACE), 16-byte
+ *         aligned, overlapping no output.  Other arguments as efla_chunk_fwd_slab (there is no beta).
+ */
+efla_status efla_chunk_state_pass(const void* q, const void* k, const void* v, const void* t_in, size_t t_in_bytes,
+                                  efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                  int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab, void* stream);
+
+/* Like efla_chunk_fwd_plan, for the state-pass launch of efla_chunk_fwd_split / efla_chunk_state_pass. */
+efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                      int dv_slab, int* workgroups, int* slab_width, int* lds_bytes);
 
 /* Workgroups and d_v slab width efla_chunk_fwd would launch for these sizes (host only, no device
  * needed).  Returns EFLA_OK and fills the outputs, or the error efla_chunk_fwd would return for

@@ -53,6 +53,9 @@ class Oracle:
         lib.efla_oracle_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp,
                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.efla_oracle_step.restype = ctypes.c_int
+        lib.efla_oracle_ut.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int]
+        lib.efla_oracle_ut.restype = ctypes.c_int
         self.lib = lib
 
     def alpha(self, k, beta):
@@ -83,6 +86,19 @@ class Oracle:
         used = self.lib.efla_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
                                         B, H, L, d_k, d_v, int(n_threads))
         return o, sf, used
+
+    def ut(self, k, beta, chunk, n_threads=0):
+        """Intra-chunk transform T diag(alpha), T = (I + strict_lower(diag(alpha) K K^T))^{-1}, per chunk.
+
+        Returns float64 [B,H,ceil(L/chunk),chunk,chunk] (rows/columns past a short last chunk are zero).
+        """
+        k, beta = _f64(k), _f64(beta)
+        B, H, L, d_k = k.shape
+        assert beta.shape == (B, H, L)
+        nc = (L + chunk - 1) // chunk
+        out = np.empty((B, H, nc, chunk, chunk), dtype=np.float64)
+        self.lib.efla_oracle_ut(_ptr(k), _ptr(beta), _ptr(out), B, H, L, d_k, int(chunk), int(n_threads))
+        return out
 
     def step(self, q, k, v, beta, state, n_threads=0):
         """One decode step for [NH,*] inputs; ``state`` [NH,d_k,d_v] is copied, updated and returned.
@@ -123,6 +139,10 @@ def fwd(q, k, v, beta, initial_state=None, n_threads=0, want_o=True, want_state=
 
 def step(q, k, v, beta, state, n_threads=0):
     return default().step(q, k, v, beta, state, n_threads)
+
+
+def ut(k, beta, chunk, n_threads=0):
+    return default().ut(k, beta, chunk, n_threads)
 
 
 def _f64(x):

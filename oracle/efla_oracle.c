@@ -29,6 +29,9 @@
  * The product (alpha k k^T) S_{t-1} is evaluated as alpha k (k^T S_{t-1}), which is the same matrix by
  * associativity; both the erase term and the write term of the update are kept as written.
  *
+ * A second function, efla_oracle_ut, gives the intra-chunk transform of the chunked form by its
+ * definition (used to check the GPU's UT output; see its own comment).
+ *
  * Layouts (all contiguous, row-major):
  *   q, k [B,H,L,d_k]; v [B,H,L,d_v]; beta [B,H,L]; o [B,H,L,d_v]; state [B,H,d_k,d_v].
  * Parallelism: OpenMP over independent (b, h) pairs only.
@@ -163,6 +166,74 @@ int efla_oracle_step(const double *q, const double *k, const double *v, const do
             oracle_token(state + n * (int64_t)d_k * d_v, q + n * d_k, k + n * d_k, v + n * d_v, beta[n],
                          o ? o + n * d_v : NULL, kS, d_k, d_v);
         free(kS);
+    }
+    (void)nt;
+    return used;
+}
+
+/* The intra-chunk UT transform of the chunked form, by its definition.  For every (b, h) and every
+ * chunk of C consecutive tokens (the last chunk may hold n < C tokens), with alpha_i the gate of token i
+ * of the chunk and k_i its key:
+ *   A[i][j] = alpha_i k_i . k_j  for j < i, else 0        (strict lower part of diag(alpha) K K^T)
+ *   T       = (I + A)^{-1}                                 (unit lower triangular)
+ *   out     = T diag(alpha)                                (column j of T scaled by alpha_j)
+ * Sources: "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 4 (chunkwise-parallel
+ * form: the within-chunk transforms are computed in parallel and the chunks are joined by passing the
+ * state); "Exact Flow Linear Attention" (gist.science), Metodologia item 3 (the update keeps the
+ * delta-rule rank-1 form, which is what makes the WY/UT representation apply).  Column j of T solves
+ * (I + A) x = e_j, taken by forward substitution: x_i = [i == j] - sum_{m < i} A[i][m] x_m.
+ * Output: tout[bh][c][i][j], a C x C row-major block per chunk; rows and columns n .. C-1 of a short
+ * last chunk are zero.  Returns the number of threads used. */
+int efla_oracle_ut(const double *k, const double *beta, double *tout, int B, int H, int L, int d_k, int C,
+                   int n_threads)
+{
+    const int64_t BH = (int64_t)B * H;
+    const int64_t NC = (L + C - 1) / C;
+    const int nt = oracle_threads(n_threads);
+    int used = 1;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double *A = (double *)malloc(sizeof(double) * (size_t)C * C);
+        double *alpha = (double *)malloc(sizeof(double) * (size_t)C);
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t u = 0; u < BH * NC; ++u) {
+            const int64_t bh = u / NC;
+            const int t0 = (int)(u % NC) * C;
+            const int n = L - t0 < C ? L - t0 : C;
+            const double *kc = k + (bh * L + t0) * d_k;
+            double *T = tout + u * (int64_t)C * C;
+            memset(T, 0, sizeof(double) * (size_t)C * C);
+            memset(A, 0, sizeof(double) * (size_t)C * C);
+            for (int i = 0; i < n; ++i)
+                alpha[i] = oracle_alpha_one(kc + (size_t)i * d_k, beta[bh * L + t0 + i], d_k);
+            for (int i = 0; i < n; ++i)
+                for (int j = 0; j < i; ++j) {
+                    double dot = 0.0;
+                    for (int e = 0; e < d_k; ++e)
+                        dot += kc[(size_t)i * d_k + e] * kc[(size_t)j * d_k + e];
+                    A[(size_t)i * C + j] = alpha[i] * dot;
+                }
+            for (int j = 0; j < n; ++j)
+                for (int i = 0; i < n; ++i) {
+                    double x = (i == j) ? 1.0 : 0.0;
+                    for (int m = 0; m < i; ++m)
+                        x -= A[(size_t)i * C + m] * T[(size_t)m * C + j];
+                    T[(size_t)i * C + j] = x;
+                }
+            for (int i = 0; i < n; ++i)
+                for (int j = 0; j < n; ++j)
+                    T[(size_t)i * C + j] *= alpha[j];
+        }
+        free(A);
+        free(alpha);
     }
     (void)nt;
     return used;

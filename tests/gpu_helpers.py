@@ -26,3 +26,20 @@ def fwd_inputs_dev(x: dict, dtype: str) -> dict:
 
 def errs(o, S, ro, rS):
     return W.rel_max_err(host(o), ro), W.rel_max_err(host(S), rS)
+
+
+def ut_dense(t: torch.Tensor, chunk: int) -> np.ndarray:
+    """UT-transform output in the library's operand layout [B,H,NC,nblocks,64,4] -> dense float64
+    [B,H,NC,chunk,chunk]: block rb (rb+1)/2 + kb holds at [16 g + r][j] the entry [16 rb + r][16 kb + 4 g + j]."""
+    a = host(t)
+    B, H, NC = a.shape[:3]
+    out = np.zeros((B, H, NC, chunk, chunk))
+    lane = np.arange(64)
+    r, g = lane % 16, lane // 16
+    qi = 0
+    for rb in range(chunk // 16):
+        for kb in range(rb + 1):
+            for j in range(4):
+                out[:, :, :, 16 * rb + r, 16 * kb + 4 * g + j] = a[:, :, :, qi, :, j]
+            qi += 1
+    return out

@@ -14,7 +14,7 @@ import exact_flow_delta_amd as efla
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "efla.h")
 
-OK, INVALID, UNSUPPORTED, NO_DEVICE, HIP = range(5)
+OK, INVALID, UNSUPPORTED, NO_DEVICE, HIP, WORKSPACE = range(6)
 F32, BF16 = 0, 1
 
 pytestmark = pytest.mark.skipif(not os.path.exists(efla.library_path()), reason="libefla.so not built")
@@ -47,8 +47,9 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(5):
+    for s in range(6):
         assert lib.efla_status_string(s).decode().startswith("EFLA")
+    assert b"WORKSPACE" in lib.efla_status_string(WORKSPACE)
     assert lib.efla_status_string(99).decode().startswith("EFLA")
     assert lib.efla_version() >= 10000
     assert isinstance(lib.efla_last_error(), bytes)
@@ -64,6 +65,13 @@ def test_plan_default_slabs(lib):
     # explicit slab, grid padded to whole groups of 8 heads
     wg, sw, _ = efla.chunk_plan(1, 1, 256, 16, 16, 16, torch.float32, 16)
     assert (wg, sw) == (8, 16)
+    # the fused kernel plans the same grid
+    assert efla.chunk_plan(8, 16, 4096, 128, 128, 64, torch.bfloat16, method="fused")[:2] == (256, 64)
+    # state pass: Q, K, V-slab rows padded by 4 fp32 elements, two buffers when they fit in 160 KiB
+    wg, sw, lds = efla.chunk_plan(1, 2, 256, 128, 128, 64, torch.float32)
+    assert sw == 16 and lds == 2 * 64 * (2 * 132 + 20) * 4
+    wg, sw, lds = efla.chunk_plan(1, 2, 256, 128, 128, 64, torch.float32, dv_slab=64)
+    assert sw == 64 and lds == 64 * (2 * 132 + 68) * 4
 
 
 def test_plan_rejects_unsupported(lib):
@@ -145,3 +153,75 @@ def test_binding_refuses_cpu_tensors():
         efla.recurrent_step(x[0, 0], x[0, 0], x[0, 0], b[0, 0], torch.zeros(16, 16, 16))
     with pytest.raises(ValueError, match="GPU tensor"):
         efla.alpha(x, b)
+
+
+def test_workspace_size(lib):
+    # per (batch, head) and chunk: (C/16)(C/16+1)/2 blocks of 256 elements
+    assert efla.chunk_workspace_size(2, 3, 100, 64, torch.bfloat16) == 6 * 2 * 10 * 256 * 2
+    assert efla.chunk_workspace_size(2, 3, 100, 16, torch.float32) == 6 * 7 * 1 * 256 * 4
+    assert efla.chunk_workspace_size(8, 16, 4096, 64, torch.bfloat16) == 128 * 64 * 10 * 512
+    assert efla.chunk_workspace_size(1, 1, 0, 32, torch.bfloat16) == 0
+    n = ctypes.c_size_t()
+    assert lib.efla_chunk_workspace_size(1, 1, 8, 48, BF16, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.efla_chunk_workspace_size(1, -1, 8, 64, BF16, ctypes.byref(n)) == INVALID
+    assert lib.efla_chunk_workspace_size(1, 1, 8, 64, BF16, None) == INVALID
+
+
+def _split(lib, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=BF16, o=P(5), s0=None, sf=P(6), B=2, H=3, L=100, dk=64, dv=64,
+             C=64, slab=0, ws=P(7), wsb=6 * 2 * 10 * 256 * 2)
+    a.update(kw)
+    return lib.efla_chunk_fwd_split(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["o"], a["s0"], a["sf"], a["B"],
+                                    a["H"], a["L"], a["dk"], a["dv"], a["C"], a["slab"], a["ws"], a["wsb"], None)
+
+
+def test_split_argument_errors(lib):
+    assert _split(lib, ws=None) == WORKSPACE
+    assert _split(lib, wsb=6 * 2 * 10 * 256 * 2 - 1) == WORKSPACE
+    assert _split(lib, ws=ctypes.c_void_p(0x7F0700000008)) == WORKSPACE           # misaligned
+    assert _split(lib, ws=ctypes.c_void_p(0x7F0500000000 + 4096)) == INVALID     # inside o
+    assert _split(lib, ws=P(6)) == INVALID                                        # is the final state
+    assert _split(lib, q=None) == INVALID
+    assert _split(lib, dk=96) == UNSUPPORTED
+    assert _split(lib, slab=32, dv=16) == UNSUPPORTED
+    assert _split(lib, B=0, ws=None, wsb=0) == OK
+    assert _split(lib, L=0, sf=None, q=None, k=None, v=None, beta=None, o=None, ws=None, wsb=0) == OK
+
+
+def test_ut_transform_argument_errors(lib):
+    f = lib.efla_ut_transform
+    need = 6 * 2 * 10 * 256 * 2
+    assert f(P(1), P(2), BF16, P(3), need, 2, 3, 0, 64, 64, None) == OK          # empty
+    assert f(P(1), P(2), BF16, P(3), need - 2, 2, 3, 100, 64, 64, None) == WORKSPACE
+    assert f(P(1), P(2), BF16, None, need, 2, 3, 100, 64, 64, None) == WORKSPACE
+    assert f(None, P(2), BF16, P(3), need, 2, 3, 100, 64, 64, None) == INVALID
+    assert f(P(1), P(2), BF16, P(1), need, 2, 3, 100, 64, 64, None) == INVALID    # output overlaps k
+    assert f(P(1), P(2), BF16, P(3), need, 2, 3, 100, 64, 48, None) == UNSUPPORTED
+    assert f(P(1), P(2), BF16, P(3), need, 2, 3, 100, 20, 64, None) == UNSUPPORTED
+    assert f(P(1), P(2), 9, P(3), need, 2, 3, 100, 64, 64, None) == INVALID
+
+
+def test_state_pass_argument_errors(lib):
+    f = lib.efla_chunk_state_pass
+    need = 6 * 2 * 10 * 256 * 2
+
+    def call(**kw):
+        a = dict(q=P(1), k=P(2), v=P(3), t=P(7), tb=need, dt=BF16, o=P(5), s0=None, sf=P(6), L=100)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["t"], a["tb"], a["dt"], a["o"], a["s0"], a["sf"], 2, 3, a["L"], 64, 64, 64,
+                 0, None)
+
+    assert call(t=None) == WORKSPACE
+    assert call(tb=need - 1) == WORKSPACE
+    assert call(t=P(5)) == INVALID                 # t overlaps o
+    assert call(v=None) == INVALID
+    assert call(dt=4) == INVALID
+    assert call(L=0, q=None, k=None, v=None, o=None, t=None, tb=0, sf=None) == OK
+    if _no_gpu():
+        assert call() == NO_DEVICE
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_split_no_device_after_valid_arguments(lib):
+    assert _split(lib) == NO_DEVICE
+    assert lib.efla_ut_transform(P(1), P(2), BF16, P(3), 6 * 2 * 10 * 256 * 2, 2, 3, 100, 64, 64, None) == NO_DEVICE

@@ -18,15 +18,23 @@ from gpu_helpers import TOL, dev, errs, fwd_inputs_dev, host  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-def _run_fwd(x, dtype, chunk, dv_slab=0, poison=True):
+METHODS = ["split", "fused"]
+
+
+def _run_fwd(x, dtype, chunk, dv_slab=0, poison=True, method="split"):
     d = fwd_inputs_dev(x, dtype)
     B, H, L, _ = d["k"].shape
     d_v = d["v"].shape[-1]
     out = torch.empty((B, H, L, d_v), dtype=d["v"].dtype, device="cuda")
     if poison:
         out.fill_(float("nan"))
+    ws = None
+    if method == "split":
+        # a NaN-filled workspace: every block the state pass reads must have been written by the UT launch
+        ws = torch.full((max(1, efla.chunk_workspace_size(B, H, L, chunk, d["v"].dtype)),), 0xFF, dtype=torch.uint8,
+                        device="cuda")
     o, S = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=d["initial_state"], chunk_size=chunk,
-                          dv_slab=dv_slab, out=out)
+                          dv_slab=dv_slab, out=out, method=method, workspace=ws)
     torch.cuda.synchronize()
     return o, S
 
@@ -106,18 +114,20 @@ def test_recurrent_step_headline_sampled():
 # ------------------------------------------------------------------------------------------------
 # chunked forward: the small workloads at full size
 # ------------------------------------------------------------------------------------------------
-def test_chunk_fwd_tiny_workload():
+@pytest.mark.parametrize("method", METHODS)
+def test_chunk_fwd_tiny_workload(method):
     w = W.workload(1)
     x = W.make_fwd_inputs(w)
-    o, S = _run_fwd(x, w.dtype, w.chunk)
+    o, S = _run_fwd(x, w.dtype, w.chunk, method=method)
     eo, eS = errs(o, S, *_oracle_fwd(x))
     assert eo < TOL["f32"] and eS < TOL["f32"], (eo, eS)
 
 
-def test_chunk_fwd_stiff_workload():
+@pytest.mark.parametrize("method", METHODS)
+def test_chunk_fwd_stiff_workload(method):
     w = W.workload(2)
     x = W.make_fwd_inputs(w)
-    o, S = _run_fwd(x, w.dtype, w.chunk)
+    o, S = _run_fwd(x, w.dtype, w.chunk, method=method)
     eo, eS = errs(o, S, *_oracle_fwd(x))
     assert eo < TOL["f32"] and eS < TOL["f32"], (eo, eS)
 
@@ -129,8 +139,9 @@ SWEEP = [(dk, dv, c, dt) for dt in ("f32", "bf16") for dk in (16, 32, 64, 128) f
          for c in (16, 32, 64)]
 
 
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("d_k,d_v,chunk,dtype", SWEEP)
-def test_chunk_fwd_sweep(d_k, d_v, chunk, dtype):
+def test_chunk_fwd_sweep(d_k, d_v, chunk, dtype, method):
     cfg = 2 if dtype == "f32" else 3
     w = W.workload(cfg, B=2, H=3, L=3 * chunk + 5, d_k=d_k, d_v=d_v, dtype=dtype)
     x = W.make_fwd_inputs(w, salt=d_k + 7 * d_v + 31 * chunk)
@@ -139,32 +150,34 @@ def test_chunk_fwd_sweep(d_k, d_v, chunk, dtype):
             np.float32)
     else:
         x["initial_state"] = x["initial_state"][:, :, :d_k, :d_v].copy()
-    o, S = _run_fwd(x, dtype, chunk)
+    o, S = _run_fwd(x, dtype, chunk, method=method)
     eo, eS = errs(o, S, *_oracle_fwd(x))
     assert eo < TOL[dtype] and eS < TOL[dtype], (eo, eS)
 
 
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("L", [1, 15, 16, 17, 63, 64, 65, 784])
-def test_chunk_fwd_ragged_lengths(L):
+def test_chunk_fwd_ragged_lengths(L, method):
     """Short and ragged sequences, including the 784-token d=64 shape of the pixel-sequence workload."""
     w = W.workload(2, B=1, H=9, L=L)
     x = W.make_fwd_inputs(w, salt=L)
-    o, S = _run_fwd(x, "f32", 64)
+    o, S = _run_fwd(x, "f32", 64, method=method)
     eo, eS = errs(o, S, *_oracle_fwd(x))
     assert eo < TOL["f32"] and eS < TOL["f32"], (eo, eS)
 
 
-def test_chunk_fwd_empty_sequence_copies_state():
+@pytest.mark.parametrize("method", METHODS)
+def test_chunk_fwd_empty_sequence_copies_state(method):
     rng = np.random.default_rng(5)
     s0 = torch.from_numpy(rng.standard_normal((2, 3, 64, 32)).astype(np.float32)).cuda()
     e = torch.empty((2, 3, 0, 64), device="cuda")
     ev = torch.empty((2, 3, 0, 32), device="cuda")
     b = torch.empty((2, 3, 0), device="cuda")
-    o, S = efla.chunk_fwd(e, e, ev, b, initial_state=s0)
+    o, S = efla.chunk_fwd(e, e, ev, b, initial_state=s0, method=method)
     torch.cuda.synchronize()
     assert o.shape == (2, 3, 0, 32)
     assert torch.equal(S, s0)
-    o, S = efla.chunk_fwd(e, e, ev, b)
+    o, S = efla.chunk_fwd(e, e, ev, b, method=method)
     torch.cuda.synchronize()
     assert torch.count_nonzero(S) == 0
 
@@ -172,46 +185,50 @@ def test_chunk_fwd_empty_sequence_copies_state():
 # ------------------------------------------------------------------------------------------------
 # metamorphic properties
 # ------------------------------------------------------------------------------------------------
-def test_slab_split_is_bitwise_identical():
+@pytest.mark.parametrize("method", METHODS)
+def test_slab_split_is_bitwise_identical(method):
     """State columns are independent: every d_v split gives bit-identical results."""
     w = W.workload(3, B=1, H=5, L=300)
     x = W.make_fwd_inputs(w)
-    res = [_run_fwd(x, "bf16", 64, dv_slab=s) for s in (16, 32, 64)]
+    res = [_run_fwd(x, "bf16", 64, dv_slab=s, method=method) for s in (16, 32, 64)]
     for o, S in res[1:]:
         assert torch.equal(o, res[0][0]) and torch.equal(S, res[0][1])
 
 
-def test_deterministic():
+@pytest.mark.parametrize("method", METHODS)
+def test_deterministic(method):
     w = W.workload(3, B=2, H=4, L=500)
     x = W.make_fwd_inputs(w)
-    o1, S1 = _run_fwd(x, "bf16", 64)
-    o2, S2 = _run_fwd(x, "bf16", 64)
+    o1, S1 = _run_fwd(x, "bf16", 64, method=method)
+    o2, S2 = _run_fwd(x, "bf16", 64, method=method)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_chunk_size_independence(dtype):
+def test_chunk_size_independence(dtype, method):
     w = W.workload(2 if dtype == "f32" else 3, B=1, H=4, L=200, d_k=64, d_v=64, dtype=dtype)
     x = W.make_fwd_inputs(w)
     ro, rS = _oracle_fwd(x)
     for c in (16, 32, 64):
-        o, S = _run_fwd(x, dtype, c)
+        o, S = _run_fwd(x, dtype, c, method=method)
         eo, eS = errs(o, S, ro, rS)
         assert eo < TOL[dtype] and eS < TOL[dtype], (c, eo, eS)
 
 
-def test_state_chaining_bitwise_at_chunk_boundary():
+@pytest.mark.parametrize("method", METHODS)
+def test_state_chaining_bitwise_at_chunk_boundary(method):
     """fwd over [0, L) == fwd over [0, L1) then [L1, L) from its final state, when L1 is a chunk multiple."""
     w = W.workload(3, B=2, H=3, L=320)
     x = W.make_fwd_inputs(w)
     d = fwd_inputs_dev(x, "bf16")
-    o, S = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"])
+    o, S = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], method=method)
     L1 = 192
     o1, S1 = efla.chunk_fwd(d["q"][:, :, :L1].contiguous(), d["k"][:, :, :L1].contiguous(),
-                            d["v"][:, :, :L1].contiguous(), d["beta"][:, :, :L1].contiguous())
+                            d["v"][:, :, :L1].contiguous(), d["beta"][:, :, :L1].contiguous(), method=method)
     o2, S2 = efla.chunk_fwd(d["q"][:, :, L1:].contiguous(), d["k"][:, :, L1:].contiguous(),
                             d["v"][:, :, L1:].contiguous(), d["beta"][:, :, L1:].contiguous(),
-                            initial_state=S1, final_state=S1)      # in place
+                            initial_state=S1, final_state=S1, method=method)      # in place
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([o1, o2], dim=2), o)
     assert torch.equal(S2, S)
@@ -250,17 +267,19 @@ def _sampled_heads(w, x, o, S, heads):
         assert eo < TOL[w.dtype] and eS < TOL[w.dtype], ((b, h), eo, eS)
 
 
-def test_lm_layer_workload_full_size_sampled():
+@pytest.mark.parametrize("method", METHODS)
+def test_lm_layer_workload_full_size_sampled(method):
     w = W.workload(3)
     x = W.make_fwd_inputs(w)
-    o, S = _run_fwd(x, "bf16", w.chunk)
+    o, S = _run_fwd(x, "bf16", w.chunk, method=method)
     assert not torch.isnan(o).any()
     _sampled_heads(w, x, o, S, [(0, 0), (0, 15), (3, 7), (7, 15)])
 
 
-def test_long_context_workload_full_size_sampled():
+@pytest.mark.parametrize("method", METHODS)
+def test_long_context_workload_full_size_sampled(method):
     w = W.workload(4)
     x = W.make_fwd_inputs(w)
-    o, S = _run_fwd(x, "bf16", w.chunk)
+    o, S = _run_fwd(x, "bf16", w.chunk, method=method)
     assert not torch.isnan(o).any()
     _sampled_heads(w, x, o, S, [(0, 0), (0, 11)])

@@ -316,9 +316,64 @@ def check_zero_initial_state(orc):
     np.testing.assert_array_equal(S1, S2)
 
 
+def check_ut_chunk_identity(orc):
+    """The oracle's UT output, used in the chunked form, reproduces the token recurrence.
+
+    With T diag(alpha) from ``orc.ut`` for each chunk and S the recurrence's own state entering it,
+    Delta = T diag(alpha) (V - K S) must give the recurrence's state after the chunk as S + K^T Delta and
+    its outputs as Q S + lower_incl(Q K^T) Delta ("Error-Free Linear Attention is a Free Lunch", Step 4;
+    "Exact Flow Linear Attention", Metodologia item 3).  Ragged last chunk; padding must be zero.
+    """
+    rng = np.random.default_rng(31)
+    B, H, C, d_k, d_v = 1, 2, 8, 6, 5
+    L = 2 * C + 5
+    k = np.stack([_mixed_keys(rng, L, d_k, 0.05, 2.5) for _ in range(B * H)]).reshape(B, H, L, d_k)
+    q = rng.standard_normal((B, H, L, d_k))
+    v = rng.standard_normal((B, H, L, d_v))
+    beta = rng.uniform(0.05, 1.0, (B, H, L))
+    S0 = 0.3 * rng.standard_normal((B, H, d_k, d_v))
+    T = orc.ut(k, beta, C)
+    nc = (L + C - 1) // C
+    assert T.shape == (B, H, nc, C, C)
+    o_ref, _, _ = orc.fwd(q, k, v, beta, S0)
+    for c in range(nc):
+        t0, t1 = c * C, min(L, (c + 1) * C)
+        n = t1 - t0
+        assert np.all(T[:, :, c, n:, :] == 0) and np.all(T[:, :, c, :, n:] == 0)
+        if c == 0:
+            S_in = S0
+        else:
+            _, S_in, _ = orc.fwd(q[:, :, :t0], k[:, :, :t0], v[:, :, :t0], beta[:, :, :t0], S0)
+        _, S_out, _ = orc.fwd(q[:, :, :t1], k[:, :, :t1], v[:, :, :t1], beta[:, :, :t1], S0)
+        for b in range(B):
+            for h in range(H):
+                Kc, Qc, Vc = k[b, h, t0:t1], q[b, h, t0:t1], v[b, h, t0:t1]
+                Tc = T[b, h, c, :n, :n]
+                assert np.all(np.triu(Tc, 1) == 0)
+                D = Tc @ (Vc - Kc @ S_in[b, h])
+                S_new = S_in[b, h] + Kc.T @ D
+                O = Qc @ S_in[b, h] + np.tril(Qc @ Kc.T) @ D
+                assert np.max(np.abs(S_new - S_out[b, h])) <= 1e-12 * max(1.0, np.max(np.abs(S_out[b, h])))
+                assert np.max(np.abs(O - o_ref[b, h, t0:t1])) <= 1e-12 * max(1.0, np.max(np.abs(o_ref[b, h, t0:t1])))
+
+
+def check_ut_orthogonal_keys(orc):
+    """Mutually orthogonal keys make A = 0, so T diag(alpha) = diag(alpha) with alpha the exact gate."""
+    rng = np.random.default_rng(32)
+    C, d_k = 16, 16
+    Qm, _ = np.linalg.qr(rng.standard_normal((d_k, d_k)))
+    k = (Qm.T * np.exp(rng.uniform(-2, 2, (C, 1))))[None, None]
+    beta = rng.uniform(0.1, 2.0, (1, 1, C))
+    T = orc.ut(k, beta, C)[0, 0, 0]
+    lam = np.sum(k[0, 0] ** 2, axis=-1)
+    a = -np.expm1(-beta[0, 0] * lam) / lam
+    assert np.max(np.abs(T - np.diag(a))) <= 1e-13
+
+
 PINS = [check_worked_example, check_expm_erase, check_van_loan, check_rk4_sequence, check_alpha_extremes,
         check_euler_limit, check_directional_decay, check_stiff_overwrite, check_contractive,
-        check_linearity, check_chunk_identity, check_state_chaining, check_zero_initial_state]
+        check_linearity, check_chunk_identity, check_state_chaining, check_zero_initial_state,
+        check_ut_chunk_identity, check_ut_orthogonal_keys]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -378,6 +433,15 @@ MUTANTS = {
     "exp_sign": ("return -expm1(-beta * lambda) / lambda;", "return expm1(beta * lambda) / lambda;"),
     "initial_state_ignored": ("memcpy(S, initial_state + bh * ssz, sizeof(double) * ssz);",
                               "memset(S, 0, sizeof(double) * ssz);"),
+    "ut_substitution_sign": ("x -= A[(size_t)i * C + m] * T[(size_t)m * C + j];",
+                             "x += A[(size_t)i * C + m] * T[(size_t)m * C + j];"),
+    "ut_alpha_on_rows": ("T[(size_t)i * C + j] *= alpha[j];", "T[(size_t)i * C + j] *= alpha[i];"),
+    "ut_gram_without_alpha": ("A[(size_t)i * C + j] = alpha[i] * dot;", "A[(size_t)i * C + j] = dot;"),
+    "ut_gram_alpha_of_column": ("A[(size_t)i * C + j] = alpha[i] * dot;", "A[(size_t)i * C + j] = alpha[j] * dot;"),
+    "ut_gram_wrong_key": ("dot += kc[(size_t)i * d_k + e] * kc[(size_t)j * d_k + e];",
+                          "dot += kc[(size_t)i * d_k + e] * kc[(size_t)i * d_k + e];"),
+    "ut_substitution_range": ("for (int m = 0; m < i; ++m)\n                        x -=",
+                              "for (int m = 0; m + 1 < i; ++m)\n                        x -="),
 }
 
 
