@@ -1,0 +1,351 @@
+// efla_chain_bf16.hpp -- the inter-chunk state pass for bf16 inputs with d_k in {32, 64, 128}.
+//
+// Same arithmetic as the generic state-pass kernel (per chunk, with S the state entering it and
+// Ta = T diag(alpha) read from the UT transform's output:
+//   R = V - K S,  Delta = Ta R,  O = Q S + lower_incl(Q K^T) Delta,  S <- S + K^T Delta;
+// "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 4; "Exact Flow Linear
+// Attention" (gist.science), Metodologia item 3), organised around three gfx950 features:
+//
+//  * Direct global -> LDS loads.  The next chunk's Q, K, V slab and Ta blocks are fetched with buffer
+//    loads that write LDS themselves (16 bytes per lane, one contiguous KiB per wave instruction), so
+//    staging takes no registers and no LDS store instructions, and the only vector-memory traffic of a
+//    chunk is that prefetch and the output stores.  Lanes whose rows lie past the end of the sequence
+//    are outside the buffer range and write zeros.
+//  * 16-byte LDS fragment reads.  Every 32-wide slice of d_k is split among the four lane groups as
+//    eight consecutive elements each, which makes each Q or K matrix-core fragment one ds_read_b128.
+//    The reduction index must run in the same order in the state operand, so the state tile rows are
+//    permuted to match: accumulator tile rt = 2 kp + h, lane (r, g), element i holds
+//    S[32 kp + 8 g + 4 h + i][column r].  The K^T operand of the state update is read with the
+//    transposing LDS read, addressed with the same permutation.
+//  * XOR-swizzled, unpadded tiles.  Row t of a tile keeps its 16-byte chunk c at position c ^ sw(t),
+//    with sw chosen per row width so that the 16 rows of a fragment read and the 4x4 row/column
+//    pattern of a transposing read land on distinct banks.
+//
+// One workgroup per (batch*head, slab of DVS state columns), 16 columns per wave, one barrier per chunk.
+// The chunk loop is unrolled by two so that the two LDS buffers alternate as distinct arrays (which also
+// lets the compiler see that loads into one never alias reads of the other).  The outputs of a chunk are
+// stored at the start of the next one, so the wait that precedes each barrier never waits on a store.
+#pragma once
+
+#include "efla_chunk_split.hpp"
+
+namespace efla {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef bf16x8 __attribute__((address_space(3))) lds_bf16x8;
+
+template <int DK, int C, int DVS>
+struct ChainBf16Shape {
+    static constexpr int RBQ = DK * 2;                       // bytes per Q / K row
+    static constexpr int RBV = DVS * 2;                      // bytes per V-slab row
+    static constexpr int QBYTES = C * RBQ;
+    static constexpr int VBYTES = C * RBV;
+    static constexpr int NLQ = (QBYTES + 1023) / 1024;       // wave loads (1 KiB each) per Q or K tile
+    static constexpr int NLV = (VBYTES + 1023) / 1024;
+    static constexpr int TBYTES = TaShape<C>::NQ * TaShape<C>::QE * 2;   // T diag(alpha) blocks of one chunk
+    static constexpr int NLT = (TBYTES + 1023) / 1024;
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_K = NLQ * 1024;
+    static constexpr int OFF_V = 2 * NLQ * 1024;
+    static constexpr int OFF_T = (2 * NLQ + NLV) * 1024;
+    static constexpr int BUF = (2 * NLQ + NLV + NLT) * 1024;   // one buffer (each tile rounded up to 1 KiB)
+    static constexpr int BYTES = 2 * BUF;
+};
+
+// shape of one tile for the load routine: row bytes, wave loads, whether it is a V tile
+template <int RB_, int NL_, int ISV_>
+struct TileTag {
+    static constexpr int RB = RB_;
+    static constexpr int NL = NL_;
+    static constexpr int ISV = ISV_;
+};
+
+// chunk swizzles (16-byte chunks within a row)
+template <int DK>
+__device__ __forceinline__ int sw_qk(int t) {
+    if constexpr (DK == 128) return 4 * (t & 3) + ((t >> 2) & 3);
+    else if constexpr (DK == 64) return 4 * ((t >> 1) & 1) + ((t >> 2) & 3);
+    else return (t >> 2) & 3;
+}
+template <int DVS>
+__device__ __forceinline__ int sw_v(int t) {
+    if constexpr (DVS == 64) return 2 * ((t >> 1) & 1);
+    else return 0;
+}
+
+template <int DK, int C, int DVS>
+__global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
+    bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab) {
+    typedef ChainBf16Shape<DK, C, DVS> SH;
+    typedef Mma<bf16> M;
+    typedef M::quad quad;
+    constexpr int NW = DVS / 16;
+    constexpr int NB = C / 16;
+    constexpr int NKD = DK / 16;   // state tiles (16 d_k rows each)
+    constexpr int NKP = DK / 32;   // 32-wide d_k slices
+    constexpr int NQ = TaShape<C>::NQ;
+    constexpr int QE = TaShape<C>::QE;
+    constexpr int NCV = DVS / 8;   // 16-byte chunks per V row
+    static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
+    static_assert(SH::BYTES <= kMaxLdsBytes, "state pass LDS too large");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char buf0_[SH::BUF];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf1_[SH::BUF];
+    // LDS is addressed only through LDS-space pointers (no generic pointer ever points into it)
+    lds_u8* const buf0 = (lds_u8*)buf0_;
+    lds_u8* const buf1 = (lds_u8*)buf1_;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+
+    const int bid = blockIdx.x;
+    const int slab = (bid >> 3) % nslab;
+    const int bh = ((bid >> 3) / nslab) * 8 + (bid & 7);
+    if (bh >= BH) return;
+    const int slab_col = slab * DVS;
+    const int colw = slab_col + 16 * w;
+    const int64_t tok0 = (int64_t)bh * L;
+    const int NC = (L + C - 1) / C;
+    const bf16* twh = tw + (int64_t)bh * NC * (NQ * QE);
+
+    // ---- per-lane LDS byte offsets, fixed for the whole sequence ---------------------------------
+    // fragment reads: row 16 rb + r, logical chunk 4 kp + g  ->  + 16 * ((4 kp + g) ^ sw(row))
+    // (sw of rows 16 rb + r depends on r only, since 16 rb leaves the low four bits alone)
+    const int swr = sw_qk<DK>(r);
+    // transposing K^T reads: lane (g, e, c) = (lane >> 4, (lane >> 2) & 3, lane & 3): row 16 kb + 4 g + e,
+    // logical chunk 4 kp + c, byte 8 h within it; sw of that row depends on (g, e) only
+    const int te = 4 * g + ((lane >> 2) & 3);
+    const int tc = lane & 3;
+    const int swt = sw_qk<DK>(te);
+    // transposing V reads: row 16 rb + 4 g + e, columns 16 w + 4 c .. +3: logical chunk 2 w + (c >> 1), byte 8 (c & 1)
+    const int v_off = te * SH::RBV + 16 * (((2 * w + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
+
+    // ---- loads: wave load j of a tile covers its bytes [1024 j, 1024 j + 1024); lane L writes 16 bytes at
+    //      1024 j + 16 L --------------------------------------------------------------------------------
+    // This wave's share of one chunk's loads, numbered k = 0 .. NLOAD-1 (its Q loads, K loads, V loads,
+    // Ta loads); issue_part(c, buf, part) issues those with k % NPART == part, so that the loads spread
+    // over the first NPART row blocks of the computation instead of queueing behind each other.
+    constexpr int PQ = (SH::NLQ + NW - 1) / NW, PV = (SH::NLV + NW - 1) / NW, PT = (SH::NLT + NW - 1) / NW;
+    constexpr int NLOAD = 2 * PQ + PV + PT;
+    constexpr int NPART = NB > 1 ? NB - 1 : 1;
+    auto issue_part = [&](int c, lds_u8* buf, auto part_c) __attribute__((always_inline)) {
+        constexpr int part = decltype(part_c)::value;
+        const int t = c * C;
+        const int n = (L - t < C) ? (L - t) : C;   // <= 0 past the end: an empty range, zeros
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (tok0 + t) * DK, n > 0 ? ((n - 1) * DK + DK) * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, n > 0 ? ((n - 1) * DK + DK) * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + (tok0 + t) * DV + slab_col, n > 0 ? ((n - 1) * DV + DVS) * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(twh + (int64_t)c * (NQ * QE), SH::TBYTES);
+        static_for<NLOAD>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            if constexpr (kk % NPART == part) {
+                // tile, pass i within it, and the tile's shape
+                constexpr int tile = kk < PQ ? 0 : kk < 2 * PQ ? 1 : kk < 2 * PQ + PV ? 2 : 3;
+                constexpr int i = tile == 0 ? kk : tile == 1 ? kk - PQ : tile == 2 ? kk - 2 * PQ : kk - 2 * PQ - PV;
+                constexpr int NL = tile < 2 ? SH::NLQ : tile == 2 ? SH::NLV : SH::NLT;
+                constexpr int RB = tile < 2 ? SH::RBQ : SH::RBV;
+                constexpr int OFF = tile == 0 ? SH::OFF_Q : tile == 1 ? SH::OFF_K : tile == 2 ? SH::OFF_V : SH::OFF_T;
+                const int j = w + NW * i;
+                if ((i + 1) * NW <= NL || j < NL) {
+                    lds_void* dst = (lds_void*)(buf + OFF + 1024 * j);
+                    const int p = 1024 * j + 16 * lane;
+                    if constexpr (tile == 3) {
+                        // Ta blocks: contiguous in the workspace, copied as they are
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
+                    } else {
+                        // physical chunk pc of row tr holds logical chunk pc ^ sw(tr); rows >= C (slack of a
+                        // last partial load) and rows >= n are out of range and land as zeros
+                        const int tr = p / RB;
+                        const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
+                        const int ld = tile == 2 ? DV : DK;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 0 ? rq : tile == 1 ? rk : rv, dst, 16,
+                                                                 (tr * ld + 8 * lc) * 2, 0, 0, 0);
+                    }
+                }
+            }
+        });
+    };
+    auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
+        static_for<NPART>([&](auto pc) { issue_part(c, buf, pc); });
+    };
+    // wait for this wave's loads and LDS reads, then the barrier: a buffer written by direct loads is
+    // complete in LDS once every wave has waited for its own loads
+    auto wait_all_and_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // ---- the state: S[32 kp + 8 g + 4 h + i][colw + r] in tile rt = 2 kp + h, element i ------------------
+    auto srow = [&](int rt, int i) __attribute__((always_inline)) { return 32 * (rt >> 1) + 8 * g + 4 * (rt & 1) + i; };
+    f32x4 S[NKD];
+#pragma unroll
+    for (int rt = 0; rt < NKD; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[((int64_t)bh * DK + srow(rt, i)) * DV + colw + r] : 0.0f;
+    }
+
+    f32x4 Ot[NB];
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) Ot[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int pend_t0 = 0, pend_n = 0;   // the computed chunk whose outputs are still to be stored (none: n = 0)
+    // row block rb of those outputs, through a buffer range ending at the chunk's last valid row (an
+    // empty range before the first chunk)
+    auto store_pending = [&](int rb) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t ors =
+            buffer_rsrc(o + (tok0 + pend_t0) * DV + colw, pend_n > 0 ? ((pend_n - 1) * DV + 16) * 2 : 0);
+        buffer_store<quad>(ors, ((16 * rb + r) * DV + 4 * g) * 2, M::cvt(Ot[rb]));
+    };
+
+    // one chunk: outputs of the previous one stored and the next chunk's loads issued, both spread over the
+    // row blocks of this one's computation
+    auto step = [&](int c, const lds_u8* cur, lds_u8* nxt) __attribute__((always_inline)) {
+        const bool more = c + 1 < NC;
+        const lds_u8* cQ = cur + SH::OFF_Q;
+        const lds_u8* cK = cur + SH::OFF_K;
+        const lds_u8* cV = cur + SH::OFF_V;
+        typedef bf16x8 bx8;
+        auto frag = [&](const lds_u8* tile, int rb, int kp) __attribute__((always_inline)) {   // row 16 rb + r, d_k 32 kp + 8 g .. +7
+            return bx8(*reinterpret_cast<const lds_bf16x8*>(tile + (16 * rb + r) * SH::RBQ + 16 * ((4 * kp + g) ^ swr)));
+        };
+        auto pair = [&](quad a, quad b) __attribute__((always_inline)) -> bx8 { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); };
+
+        bx8 Sq[NKP];   // state operand: lane (r, g) holds S[32 kp + 8 g .. +7][colw + r]
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) Sq[kp] = pair(M::cvt(S[2 * kp]), M::cvt(S[2 * kp + 1]));
+
+        quad Rq[NB];
+        bx8 kq[NB][NKP];
+        quad Pq[NB * (NB + 1) / 2];
+        static_for<NB>([&](auto rbc) {
+            constexpr int rb = decltype(rbc)::value;
+            store_pending(rb);
+            if constexpr (rb < NPART) {
+                if (more) issue_part(c + 1, nxt, std::integral_constant<int, rb>{});
+            }
+            bx8 qq[NKP];
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) {
+                qq[kp] = frag(cQ, rb, kp);
+                kq[rb][kp] = frag(cK, rb, kp);
+            }
+            f32x4 xk = {0.f, 0.f, 0.f, 0.f};
+            Ot[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) {
+                Ot[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Sq[kp], qq[kp], Ot[rb], 0, 0, 0);   // (Q S)^T
+                xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[rb][kp], Sq[kp], xk, 0, 0, 0);       // K S
+            }
+            // R = V - K S: lane (r, g), element e: row 16 rb + 4g + e, column 16 w + r of the slab
+            const s16x4 vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_u8*>(cV) + 16 * rb * SH::RBV + v_off));
+            const quad vq = __builtin_bit_cast(quad, vr);
+            f32x4 rr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[e] = (float)vq[e] - xk[e];
+            Rq[rb] = M::cvt(rr);
+            // block row rb of lower_incl(Q K^T): acc lane (r, g), element e = (Q K^T)[16 rb + r][16 lo + 4g + e];
+            // the blocks' accumulation chains are interleaved (reduction step outer) so that consecutive
+            // matrix instructions are independent
+            f32x4 pacc[rb + 1];
+#pragma unroll
+            for (int lo = 0; lo <= rb; ++lo) pacc[lo] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) {
+#pragma unroll
+                for (int lo = 0; lo <= rb; ++lo)
+                    pacc[lo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[lo][kp], qq[kp], pacc[lo], 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pacc[rb][e] = (4 * g + e <= r) ? pacc[rb][e] : 0.0f;
+#pragma unroll
+            for (int lo = 0; lo <= rb; ++lo) Pq[rb * (rb + 1) / 2 + lo] = M::cvt(pacc[lo]);
+        });
+        // Delta = Ta R (block lower triangular); Ta block qi as lane (r, g)'s quad at byte 512 qi + 8 lane
+        typedef quad __attribute__((address_space(3))) lds_quad;
+        quad ta[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) ta[i] = *reinterpret_cast<const lds_quad*>(cur + SH::OFF_T + 512 * i + 8 * lane);
+        quad Dq[NB];
+        static_for<NB>([&](auto rbc) {
+            constexpr int rb = decltype(rbc)::value;
+            constexpr int q0 = rb * (rb + 1) / 2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            static_for<(rb + 1) / 2>([&](auto hc) {
+                constexpr int kb = 2 * decltype(hc)::value;
+                M::mma2(acc, ta[q0 + kb], ta[q0 + kb + 1], Rq[kb], Rq[kb + 1]);
+            });
+            if constexpr ((rb + 1) & 1) M::mma1(acc, ta[q0 + rb], Rq[rb]);
+            Dq[rb] = M::cvt(acc);
+        });
+        // O^T += Delta^T lower_incl(Q K^T)^T (stored with the next chunk)
+        static_for<NB>([&](auto rbc) {
+            constexpr int rb = decltype(rbc)::value;
+            constexpr int p0 = rb * (rb + 1) / 2;
+            static_for<(rb + 1) / 2>([&](auto hc) {
+                constexpr int kb = 2 * decltype(hc)::value;
+                M::mma2(Ot[rb], Dq[kb], Dq[kb + 1], Pq[p0 + kb], Pq[p0 + kb + 1]);
+            });
+            if constexpr ((rb + 1) & 1) M::mma1(Ot[rb], Dq[rb], Pq[p0 + rb]);
+        });
+        pend_t0 = c * C;
+        pend_n = (L - pend_t0 < C) ? (L - pend_t0) : C;
+        // S += K^T Delta: tile rt = 2 kp + h takes, as A operand, the transposed K block whose lane (g, e, c)
+        // points at row 16 kb + 4 g + e, logical chunk 4 kp + c, byte 8 h; the tiles' chains are interleaved
+        auto kt = [&](int rt, int kb) __attribute__((always_inline)) {
+            const int off = te * SH::RBQ + 16 * ((4 * (rt >> 1) + tc) ^ swt) + 8 * (rt & 1);
+            return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (lds_s16x4*)(const_cast<lds_u8*>(cK) + 16 * kb * SH::RBQ + off)));
+        };
+#pragma unroll
+        for (int kb = 0; kb + 1 < NB; kb += 2) {
+            quad k0[NKD], k1[NKD];
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) {
+                k0[rt] = kt(rt, kb);
+                k1[rt] = kt(rt, kb + 1);
+            }
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) M::mma2(S[rt], k0[rt], k1[rt], Dq[kb], Dq[kb + 1]);
+        }
+        if constexpr (NB & 1) {
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) M::mma1(S[rt], kt(rt, NB - 1), Dq[NB - 1]);
+        }
+        wait_all_and_barrier();
+    };
+
+    if (NC > 0) {
+        issue_chunk(0, buf0);
+        wait_all_and_barrier();
+    }
+    for (int c = 0; c < NC; c += 2) {
+        step(c, buf0, buf1);
+        if (c + 1 < NC) step(c + 1, buf1, buf0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) store_pending(rb);
+
+    if (sf) {
+#pragma unroll
+        for (int rt = 0; rt < NKD; ++rt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sf[((int64_t)bh * DK + srow(rt, i)) * DV + colw + r] = S[rt][i];
+        }
+    }
+}
+
+template <int DK, int C, int DVS>
+hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
+    const int nslab = a.d_v / DVS;
+    const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
+    hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS>), dim3((unsigned)grid), dim3(DVS / 16 * 64), 0, stream,
+                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                       static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab);
+    return hipGetLastError();
+}
+
+}  // namespace efla

@@ -23,6 +23,8 @@
 // reads for Q S and K S anyway, so that product costs no LDS traffic and no exchange between waves.
 #pragma once
 
+#include <type_traits>
+
 #include "efla_common.hpp"
 #include "efla_launch.hpp"
 #include "efla_ut.hpp"
@@ -67,7 +69,9 @@ struct TaShape {
 };
 
 // ------------------------------------------------------------------------------------------------
-// UT kernel: workgroup u = bh * NC + c handles chunk c of sequence-head bh.  C/16 waves.
+// UT kernel.  C/16 waves per workgroup; a grid of a few workgroups per compute unit walks the
+// (batch*head, chunk) pairs u = blockIdx.x, blockIdx.x + gridDim.x, ..., prefetching the next pair's
+// keys and steps into registers while the current one is transformed.
 // ------------------------------------------------------------------------------------------------
 template <int ESIZE, int DK, int C>
 struct UtLayout {
@@ -79,7 +83,7 @@ struct UtLayout {
     static constexpr int OFF_AT = OFF_A + C * LD_CE * ESIZE;
     static constexpr int OFF_TT = OFF_AT + C * kLdAt * 4;
     static constexpr int OFF_TAT = OFF_TT + C * LD_CE * ESIZE;
-    static constexpr int OFF_LB = OFF_TAT + C * LD_CE * ESIZE;
+    static constexpr int OFF_LB = OFF_TAT + C * LD_CE * ESIZE;   // lambda[C], beta[C]
     static constexpr int OFF_ALPHA = OFF_LB + 2 * C * 4;
     static constexpr int BYTES = OFF_ALPHA + C * 4;
 };
@@ -91,9 +95,90 @@ constexpr int ut_layout_bytes(int dk, int c) {
     return c * (dk + pad) * ESIZE + 3 * c * (c + pad) * ESIZE + c * kLdAt * 4 + 3 * c * 4;
 }
 
+// Gram blocks and diagonal solves of one chunk, balanced over NW = C/16 waves: wave w forms the diagonal
+// block (w, w) of A and solves T_ww = (I + A_ww)^{-1} from it; the off-diagonal blocks (hi, lo), lo < hi,
+// numbered in row order, go round-robin to the waves.  Every wave evaluates the gate of all C tokens once
+// (lane 16 g + r: token 16 g + r) and takes the ones it needs from the owning lanes; wave 0 publishes them
+// for the off-diagonal phase.  The solve is right-looking forward substitution in fp32 (lane r carries
+// column r; step m reads column m of the block as one broadcast row of At), with every row of At read
+// before the first step so that the substitution runs at arithmetic speed.
+template <typename E, int DK, int C, int LD_DK, int LD_CE>
+__device__ __forceinline__ void ut_rows_balanced(const E* sK, const float* sLam, const float* sBeta, float* sAlpha,
+                                                 E* sA, float* sAt, E* sTt, E* sTat, int w, int r, int g) {
+    typedef Mma<E> M;
+    typedef typename M::quad quad;
+    constexpr int NB = C / 16;
+    constexpr int NW = NB;
+    constexpr int NKD = DK / 16;
+    const int lane = 16 * g + r;
+    const float a_mine = lane < C ? exact_alpha(sBeta[lane < C ? lane : 0], sLam[lane < C ? lane : 0]) : 0.0f;
+    if (w == 0 && lane < C) sAlpha[lane] = a_mine;
+    auto alpha_of_row = [&](int blk) { return __shfl(a_mine, 16 * blk + r, 64); };   // alpha of token 16 blk + r
+    auto gram = [&](int hi, int lo, f32x4& acc) {   // acc lane (r, g), element i: (K K^T)[16 hi + r][16 lo + 4g + i]
+        const E* pa = sK + (16 * lo + r) * LD_DK + 4 * g;
+        const E* pb = sK + (16 * hi + r) * LD_DK + 4 * g;
+        quad qa[NKD], qb[NKD];
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd) {
+            qa[kd] = M::lds_quad(pa + 16 * kd);
+            qb[kd] = M::lds_quad(pb + 16 * kd);
+        }
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kd = 0; kd + 1 < NKD; kd += 2) M::mma2(acc, qa[kd], qa[kd + 1], qb[kd], qb[kd + 1]);
+        if constexpr (NKD & 1) M::mma1(acc, qa[NKD - 1], qb[NKD - 1]);
+    };
+    // off-diagonal blocks of A: alpha_i k_i . k_j with i the row token
+    static_for<NB>([&](auto hc) {
+        constexpr int hi = decltype(hc)::value;
+        static_for<hi>([&](auto lc) {
+            constexpr int lo = decltype(lc)::value;
+            constexpr int idx = hi * (hi - 1) / 2 + lo;
+            if (idx % NW == w) {
+                f32x4 acc;
+                gram(hi, lo, acc);
+                const float ar = alpha_of_row(hi);
+                M::lds_store_quad(sA + (16 * hi + r) * LD_CE + 16 * lo + 4 * g, M::cvt(acc * ar));
+            }
+        });
+    });
+    // diagonal block w: strict lower part, stored transposed in fp32: At[16 w + m][i] = A[16 w + i][16 w + m]
+    const int b0 = 16 * w;
+    const float ar = alpha_of_row(w);
+    {
+        f32x4 acc;
+        gram(w, w, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sAt[(b0 + 4 * g + i) * kLdAt + r] = (4 * g + i < r) ? ar * acc[i] : 0.0f;
+    }
+    // sAt rows were written by this wave just above; LDS operations of one wave complete in order
+    __asm__ volatile("" ::: "memory");
+    const float* at = sAt + b0 * kLdAt;
+    f32x4 rows[15][4];
+#pragma unroll
+    for (int m = 0; m < 15; ++m) {
+#pragma unroll
+        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) rows[m][i4] = *reinterpret_cast<const f32x4*>(at + m * kLdAt + 4 * i4);
+    }
+    float sv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int m = 0; m < 15; ++m) {
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) sv[i] -= rows[m][i / 4][i % 4] * sv[m];
+    }
+    // lane (r, g) writes T[b0 + 4g + e][b0 + r], e = 0..3 (row b0 + r of T^T) and the same scaled by alpha_{b0 + r}
+    f32x4 mine;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mine[e] = g == 0 ? sv[e] : g == 1 ? sv[4 + e] : g == 2 ? sv[8 + e] : sv[12 + e];
+    M::lds_store_quad(sTt + (b0 + r) * LD_CE + b0 + 4 * g, M::cvt(mine));
+    M::lds_store_quad(sTat + (b0 + r) * LD_CE + b0 + 4 * g, M::cvt(mine * ar));
+}
+
 template <typename E, int DK, int C>
 __global__ __launch_bounds__(C / 16 * 64) void ut_kernel(const E* __restrict__ k, const float* __restrict__ beta,
-                                                         E* __restrict__ tw, int L, int NC) {
+                                                         E* __restrict__ tw, int L, int NC, int total) {
     typedef UtLayout<sizeof(E), DK, C> LY;
     typedef Mma<E> M;
     typedef typename M::quad quad;
@@ -120,47 +205,59 @@ __global__ __launch_bounds__(C / 16 * 64) void ut_kernel(const E* __restrict__ k
     const int g = lane >> 4;
     const int tr_ce = M::tr_offset(lane, LD_CE);
 
-    const int64_t u = blockIdx.x;
-    const int64_t bh = u / NC;
-    const int t0 = (int)(u - bh * NC) * C;
-    const int n = (L - t0 < C) ? (L - t0) : C;
-    const int64_t tok = bh * L + t0;
-
-    // keys -> LDS with lambda = ||k||^2 reduced across the lanes that hold one key row; beta
-    {
-        KT kt;
+    // keys (16-byte vectors over the threads) and, for the thread holding the first vector of a key row,
+    // that token's step; rows past the end of the sequence read as zero keys with zero step
+    KT kt;
+    float bt[KT::N];
+    auto load = [&](int u) {
+        const int bh = u / NC;
+        const int t0 = (u - bh * NC) * C;
+        const int n = (L - t0 < C) ? (L - t0) : C;
+        const int64_t tok = (int64_t)bh * L + t0;
         kt.load(k + tok * DK, DK, n, tid);
+        const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(beta + tok, n * 4);
+#pragma unroll
+        for (int it = 0; it < KT::N; ++it)
+            bt[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, ((it * NT + tid) / KT::VPR) * 4, 0, 0));
+    };
+    int u = blockIdx.x;
+    if (u < total) load(u);
+    for (; u < total; u += gridDim.x) {
+        // keys -> LDS; lambda = ||k||^2 reduced across the lanes holding one key row, and beta, per token
 #pragma unroll
         for (int it = 0; it < KT::N; ++it) {
             const int idx = it * NT + tid;
-            const float ss = group_sum<KT::VPR>(sum_sq(kt.x[it]));
+            const float lam = group_sum<KT::VPR>(sum_sq(kt.x[it]));
             if ((C * KT::VPR) % NT == 0 || it + 1 < KT::N || idx < C * KT::VPR) {
                 const int t = idx / KT::VPR;
                 const int cv = idx % KT::VPR;
                 lds_store_vec16(sK + t * LD_DK + cv * KT::VEC, kt.x[it]);
-                if (cv == 0) sLam[t] = ss;
+                if (cv == 0) {
+                    sLam[t] = lam;
+                    sBeta[t] = bt[it];
+                }
             }
         }
-        if (tid < C) sBeta[tid] = tid < n ? beta[tok + tid] : 0.0f;
-    }
-    __syncthreads();
-    ut_rows<E, DK, C, NW, LD_DK, LD_CE, false>(nullptr, sK, sLam, sBeta, sA, sAt, sTt, sTat, nullptr, sAlpha, w, r, g);
-    __syncthreads();
-    ut_offdiag<E, C, NW, LD_CE>(sA, sTt, sTat, sAlpha, w, r, g, tr_ce);
-    __syncthreads();
-    // export: the A-operand quads of Ta are the column quads of its stored transpose
-    E* dst = tw + u * (TaShape<C>::NQ * TaShape<C>::QE) + lane * 4;
-    static_for<NB>([&](auto rbc) {
-        constexpr int rb = decltype(rbc)::value;
-        static_for<rb + 1>([&](auto kbc) {
-            constexpr int kb = decltype(kbc)::value;
-            constexpr int qi = rb * (rb + 1) / 2 + kb;
-            if (qi % NW == w) {
-                const quad x = M::lds_quad_t(sTat + 16 * kb * LD_CE + 16 * rb, LD_CE, tr_ce);
-                *reinterpret_cast<quad*>(dst + qi * TaShape<C>::QE) = x;
-            }
+        if (u + (int)gridDim.x < total) load(u + gridDim.x);
+        __syncthreads();   // also: every wave is done with the previous pair's LDS
+        ut_rows_balanced<E, DK, C, LD_DK, LD_CE>(sK, sLam, sBeta, sAlpha, sA, sAt, sTt, sTat, w, r, g);
+        __syncthreads();
+        ut_offdiag<E, C, NW, LD_CE>(sA, sTt, sTat, sAlpha, w, r, g, tr_ce);
+        __syncthreads();
+        // export: the A-operand quads of Ta are the column quads of its stored transpose
+        E* dst = tw + (int64_t)u * (TaShape<C>::NQ * TaShape<C>::QE) + lane * 4;
+        static_for<NB>([&](auto rbc) {
+            constexpr int rb = decltype(rbc)::value;
+            static_for<rb + 1>([&](auto kbc) {
+                constexpr int kb = decltype(kbc)::value;
+                constexpr int qi = rb * (rb + 1) / 2 + kb;
+                if (qi % NW == w) {
+                    const quad x = M::lds_quad_t(sTat + 16 * kb * LD_CE + 16 * rb, LD_CE, tr_ce);
+                    *reinterpret_cast<quad*>(dst + qi * TaShape<C>::QE) = x;
+                }
+            });
         });
-    });
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -179,9 +276,21 @@ struct ChainLayout {
     static constexpr int BYTES = NBUF * BUF;
 };
 
-// host-side mirror of ChainLayout::BYTES
+// LDS of the bf16 state pass for d_k >= 32 (two buffers of Q, K, V-slab and Ta tiles, each rounded up to 1 KiB)
+constexpr int chain_bf16_bytes(int dk, int c, int dvs) {
+    return 2 * (2 * ((c * dk * 2 + 1023) / 1024) + (c * dvs * 2 + 1023) / 1024 +
+                ((c / 16) * (c / 16 + 1) / 2 * 512 + 1023) / 1024) * 1024;
+}
+
+// The bf16 state pass for d_k >= 32 (direct global -> LDS staging, swizzled tiles); defined in
+// efla_chain_bf16.hpp, which the bf16 translation unit includes.
+template <int DK, int C, int DVS>
+hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream);
+
+// host-side mirror of the state pass's LDS bytes
 template <int ESIZE>
 constexpr int chain_layout_bytes(int dk, int c, int dvs) {
+    if (ESIZE == 2 && dk >= 32) return chain_bf16_bytes(dk, c, dvs);
     const int pad = ESIZE == 2 ? 20 : 4;
     const int buf = c * (2 * (dk + pad) + (dvs + pad)) * ESIZE;
     return 2 * buf <= kMaxLdsBytes ? 2 * buf : buf;
@@ -260,6 +369,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
 
     quad ta[NQ];
     if (NC > 0) {
+        load_ta(ta, 0);
         load_stage(0);
         if constexpr (DB) {
             store_stage(0);
@@ -272,8 +382,6 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
         const int t0 = c * C;
         const int n = (L - t0 < C) ? (L - t0) : C;
         const int b = DB ? (c & 1) : 0;
-        // this chunk's T diag(alpha) operands; first used after K S below, which covers their latency
-        load_ta(ta, c);
         if constexpr (DB) {
             // Straight-line on purpose (no branch for the last chunks): past the end of the sequence the
             // buffer ranges are empty, so chunk c+1's stage and chunk c+2's loads are zeros that nobody reads.
@@ -354,6 +462,9 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
             if constexpr ((rb + 1) & 1) M::mma1(acc, ta[q0 + rb], Rq[rb]);
             Dq[rb] = M::cvt(acc);
         });
+        // the next chunk's T diag(alpha) operands go into the registers just consumed: a whole iteration
+        // covers their latency (the last chunk reloads its own, unused)
+        load_ta(ta, c + 1 < NC ? c + 1 : c);
         // O^T = (Q S)^T + Delta^T lower_incl(Q K^T)^T; four consecutive outputs of one token per lane, stored
         // through a buffer resource that ends at the chunk's last valid row
         const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(o + (tok0 + t0) * DV + colw, ((n - 1) * DV + 16) * (int)sizeof(E));
@@ -396,16 +507,28 @@ template <typename E, int DK, int C>
 hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L, hipStream_t stream) {
     static_assert(UtLayout<sizeof(E), DK, C>::BYTES <= kMaxLdsBytes, "UT kernel LDS too large");
     const int NC = (L + C - 1) / C;
-    const int64_t grid = (int64_t)BH * NC;
-    if (grid == 0) return hipSuccess;
+    const int64_t total = (int64_t)BH * NC;
+    if (total == 0) return hipSuccess;
+    // as many workgroups as the device holds at once, each walking several pairs
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ut_kernel<E, DK, C>),
+                                                          C / 16 * 64, 0);
+    if (e != hipSuccess) return e;
+    const int64_t resident = (int64_t)(cus < 1 ? 1 : cus) * (per_cu < 1 ? 1 : per_cu);
+    const int64_t grid = total < resident ? total : resident;
     hipLaunchKernelGGL((ut_kernel<E, DK, C>), dim3((unsigned)grid), dim3(C / 16 * 64), 0, stream,
-                       static_cast<const E*>(k), beta, static_cast<E*>(tw), L, NC);
+                       static_cast<const E*>(k), beta, static_cast<E*>(tw), L, NC, (int)total);
     return hipGetLastError();
 }
 
 template <typename E, int DK, int C, int DVS>
 hipError_t launch_chain_t(const SplitArgs& a, hipStream_t stream) {
-    if constexpr (ChainLayout<sizeof(E), DK, C, DVS>::BYTES > kMaxLdsBytes) {
+    if constexpr (std::is_same<E, bf16>::value && DK >= 32) {
+        return launch_chain_bf16<DK, C, DVS>(a, stream);
+    } else if constexpr (ChainLayout<sizeof(E), DK, C, DVS>::BYTES > kMaxLdsBytes) {
         return hipErrorInvalidConfiguration;
     } else {
         const int nslab = a.d_v / DVS;

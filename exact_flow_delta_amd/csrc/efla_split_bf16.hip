@@ -1,4 +1,5 @@
 // efla_split_bf16.hip -- bf16-input instantiations of the two-launch chunked forward.
+#include "efla_chain_bf16.hpp"
 #include "efla_chunk_split.hpp"
 
 namespace efla {
