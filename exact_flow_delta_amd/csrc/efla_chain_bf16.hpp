@@ -21,10 +21,13 @@
 //    with sw chosen per row width so that the 16 rows of a fragment read and the 4x4 row/column
 //    pattern of a transposing read land on distinct banks.
 //
-// One workgroup per (batch*head, slab of DVS state columns), 16 columns per wave, one barrier per chunk.
-// The chunk loop is unrolled by two so that the two LDS buffers alternate as distinct arrays (which also
-// lets the compiler see that loads into one never alias reads of the other).  The outputs of a chunk are
-// stored at the start of the next one, so the wait that precedes each barrier never waits on a store.
+// One workgroup per (batch*head, slab of DVS state columns): DVS/16 compute waves (16 state columns each)
+// and one producer wave that only issues the tile loads and waits for them, so the compute waves never
+// stall on the address unit.  All waves meet at one barrier per chunk.  Tiles are fetched two chunks
+// ahead into three LDS buffers when they fit (else one chunk ahead into two); the chunk loops are unrolled
+// so that the buffers rotate as distinct arrays, which also lets the compiler see that loads into one
+// never alias reads of another.  A chunk's outputs are stored a row block at a time while the following
+// chunk is computed.
 #pragma once
 
 #include "efla_chunk_split.hpp"
@@ -50,7 +53,8 @@ struct ChainBf16Shape {
     static constexpr int OFF_V = 2 * NLQ * 1024;
     static constexpr int OFF_T = (2 * NLQ + NLV) * 1024;
     static constexpr int BUF = (2 * NLQ + NLV + NLT) * 1024;   // one buffer (each tile rounded up to 1 KiB)
-    static constexpr int BYTES = 2 * BUF;
+    static constexpr int NBUF = 3 * BUF <= kMaxLdsBytes ? 3 : 2;   // prefetch distance NBUF - 1 chunks
+    static constexpr int BYTES = NBUF * BUF;
 };
 
 // shape of one tile for the load routine: row bytes, wave loads, whether it is a V tile
@@ -75,7 +79,7 @@ __device__ __forceinline__ int sw_v(int t) {
 }
 
 template <int DK, int C, int DVS>
-__global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
+__global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
     bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab) {
     typedef ChainBf16Shape<DK, C, DVS> SH;
@@ -91,11 +95,14 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
     static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
     static_assert(SH::BYTES <= kMaxLdsBytes, "state pass LDS too large");
 
+    constexpr int PD = SH::NBUF - 1;   // chunks fetched ahead
     __shared__ __attribute__((aligned(1024))) unsigned char buf0_[SH::BUF];
     __shared__ __attribute__((aligned(1024))) unsigned char buf1_[SH::BUF];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf2_[PD == 2 ? SH::BUF : 1024];
     // LDS is addressed only through LDS-space pointers (no generic pointer ever points into it)
     lds_u8* const buf0 = (lds_u8*)buf0_;
     lds_u8* const buf1 = (lds_u8*)buf1_;
+    lds_u8* const buf2 = (lds_u8*)buf2_;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -108,7 +115,8 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
     const int bh = ((bid >> 3) / nslab) * 8 + (bid & 7);
     if (bh >= BH) return;
     const int slab_col = slab * DVS;
-    const int colw = slab_col + 16 * w;
+    const bool producer = w == NW;                 // the extra wave: it only fetches
+    const int colw = slab_col + 16 * (producer ? 0 : w);
     const int64_t tok0 = (int64_t)bh * L;
     const int NC = (L + C - 1) / C;
     const bf16* twh = tw + (int64_t)bh * NC * (NQ * QE);
@@ -125,60 +133,86 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
     // transposing V reads: row 16 rb + 4 g + e, columns 16 w + 4 c .. +3: logical chunk 2 w + (c >> 1), byte 8 (c & 1)
     const int v_off = te * SH::RBV + 16 * (((2 * w + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
 
-    // ---- loads: wave load j of a tile covers its bytes [1024 j, 1024 j + 1024); lane L writes 16 bytes at
-    //      1024 j + 16 L --------------------------------------------------------------------------------
-    // This wave's share of one chunk's loads, numbered k = 0 .. NLOAD-1 (its Q loads, K loads, V loads,
-    // Ta loads); issue_part(c, buf, part) issues those with k % NPART == part, so that the loads spread
-    // over the first NPART row blocks of the computation instead of queueing behind each other.
-    constexpr int PQ = (SH::NLQ + NW - 1) / NW, PV = (SH::NLV + NW - 1) / NW, PT = (SH::NLT + NW - 1) / NW;
-    constexpr int NLOAD = 2 * PQ + PV + PT;
-    constexpr int NPART = NB > 1 ? NB - 1 : 1;
-    auto issue_part = [&](int c, lds_u8* buf, auto part_c) __attribute__((always_inline)) {
-        constexpr int part = decltype(part_c)::value;
+    // ---- loads (producer wave only): wave load j of a tile covers its bytes [1024 j, 1024 j + 1024); lane L
+    //      writes 16 bytes at 1024 j + 16 L, i.e. physical chunk p of row t, holding logical chunk p ^ sw(t)
+    constexpr int NLOAD = 2 * SH::NLQ + SH::NLV + SH::NLT;   // loads per chunk
+    auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
         const int t = c * C;
         const int n = (L - t < C) ? (L - t) : C;   // <= 0 past the end: an empty range, zeros
-        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (tok0 + t) * DK, n > 0 ? ((n - 1) * DK + DK) * 2 : 0);
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, n > 0 ? ((n - 1) * DK + DK) * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (tok0 + t) * DK, n > 0 ? n * DK * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, n > 0 ? n * DK * 2 : 0);
         const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + (tok0 + t) * DV + slab_col, n > 0 ? ((n - 1) * DV + DVS) * 2 : 0);
         const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(twh + (int64_t)c * (NQ * QE), SH::TBYTES);
         static_for<NLOAD>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            if constexpr (kk % NPART == part) {
-                // tile, pass i within it, and the tile's shape
-                constexpr int tile = kk < PQ ? 0 : kk < 2 * PQ ? 1 : kk < 2 * PQ + PV ? 2 : 3;
-                constexpr int i = tile == 0 ? kk : tile == 1 ? kk - PQ : tile == 2 ? kk - 2 * PQ : kk - 2 * PQ - PV;
-                constexpr int NL = tile < 2 ? SH::NLQ : tile == 2 ? SH::NLV : SH::NLT;
-                constexpr int RB = tile < 2 ? SH::RBQ : SH::RBV;
-                constexpr int OFF = tile == 0 ? SH::OFF_Q : tile == 1 ? SH::OFF_K : tile == 2 ? SH::OFF_V : SH::OFF_T;
-                const int j = w + NW * i;
-                if ((i + 1) * NW <= NL || j < NL) {
-                    lds_void* dst = (lds_void*)(buf + OFF + 1024 * j);
-                    const int p = 1024 * j + 16 * lane;
-                    if constexpr (tile == 3) {
-                        // Ta blocks: contiguous in the workspace, copied as they are
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
-                    } else {
-                        // physical chunk pc of row tr holds logical chunk pc ^ sw(tr); rows >= C (slack of a
-                        // last partial load) and rows >= n are out of range and land as zeros
-                        const int tr = p / RB;
-                        const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
-                        const int ld = tile == 2 ? DV : DK;
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 0 ? rq : tile == 1 ? rk : rv, dst, 16,
-                                                                 (tr * ld + 8 * lc) * 2, 0, 0, 0);
-                    }
-                }
+            constexpr int tile = kk < SH::NLQ ? 0 : kk < 2 * SH::NLQ ? 1 : kk < 2 * SH::NLQ + SH::NLV ? 2 : 3;
+            constexpr int j = tile == 0 ? kk : tile == 1 ? kk - SH::NLQ : tile == 2 ? kk - 2 * SH::NLQ
+                                                                                  : kk - 2 * SH::NLQ - SH::NLV;
+            constexpr int RB = tile < 2 ? SH::RBQ : SH::RBV;
+            constexpr int OFF = tile == 0 ? SH::OFF_Q : tile == 1 ? SH::OFF_K : tile == 2 ? SH::OFF_V : SH::OFF_T;
+            lds_void* dst = (lds_void*)(buf + OFF + 1024 * j);
+            const int p = 1024 * j + 16 * lane;
+            if constexpr (tile == 3) {
+                // Ta blocks: contiguous in the workspace, copied as they are
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
+            } else {
+                // rows >= C (slack of a last partial load) and rows >= n are out of range and land as zeros
+                const int tr = p / RB;
+                const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
+                const int ld = tile == 2 ? DV : DK;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 0 ? rq : tile == 1 ? rk : rv, dst, 16,
+                                                         (tr * ld + 8 * lc) * 2, 0, 0, 0);
             }
         });
     };
-    auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
-        static_for<NPART>([&](auto pc) { issue_part(c, buf, pc); });
+    // wait until at most N vector-memory operations of this wave are in flight and all its LDS operations
+    // are done (N is an immediate of the wait instruction; operations retire in issue order)
+    auto wait_vm = [&](auto n_c) __attribute__((always_inline)) {
+        constexpr int N = decltype(n_c)::value;
+        static_assert(N >= 0 && N < 64, "vector-memory count field");
+        __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
     };
-    // wait for this wave's loads and LDS reads, then the barrier: a buffer written by direct loads is
-    // complete in LDS once every wave has waited for its own loads
-    auto wait_all_and_barrier = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_s_barrier();
-    };
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, NLOAD> ILOAD;
+    typedef std::integral_constant<int, NB> INB;
+
+    if (producer) {
+        // Chunk c's tiles go out at the step of chunk c - PD (the prologue fetches the first PD).  At the end
+        // of the step of chunk c those of chunk c + 1 must have landed; with PD = 2 the ones issued during
+        // the step (chunk c + 2) may still be in flight.  One barrier per step, as the compute waves.
+        if (NC > 0) {
+            issue_chunk(0, buf0);
+            if (PD == 2 && NC > 1) {
+                issue_chunk(1, buf1);
+                wait_vm(ILOAD{});
+            } else {
+                wait_vm(I0{});
+            }
+            __builtin_amdgcn_s_barrier();
+        }
+        auto pstep = [&](int c, lds_u8* nxt) __attribute__((always_inline)) {
+            if (c + PD < NC) {
+                issue_chunk(c + PD, nxt);
+                if constexpr (PD == 2) wait_vm(ILOAD{}); else wait_vm(I0{});
+            } else {
+                wait_vm(I0{});
+            }
+            __builtin_amdgcn_s_barrier();
+        };
+        if constexpr (PD == 2) {
+            for (int c = 0; c < NC; c += 3) {
+                pstep(c, buf2);
+                if (c + 1 < NC) pstep(c + 1, buf0);
+                if (c + 2 < NC) pstep(c + 2, buf1);
+            }
+        } else {
+            for (int c = 0; c < NC; c += 2) {
+                pstep(c, buf1);
+                if (c + 1 < NC) pstep(c + 1, buf0);
+            }
+        }
+        return;
+    }
 
     // ---- the state: S[32 kp + 8 g + 4 h + i][colw + r] in tile rt = 2 kp + h, element i ------------------
     auto srow = [&](int rt, int i) __attribute__((always_inline)) { return 32 * (rt >> 1) + 8 * g + 4 * (rt & 1) + i; };
@@ -201,10 +235,9 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
         buffer_store<quad>(ors, ((16 * rb + r) * DV + 4 * g) * 2, M::cvt(Ot[rb]));
     };
 
-    // one chunk: outputs of the previous one stored and the next chunk's loads issued, both spread over the
-    // row blocks of this one's computation
-    auto step = [&](int c, const lds_u8* cur, lds_u8* nxt) __attribute__((always_inline)) {
-        const bool more = c + 1 < NC;
+    // one chunk of the compute waves: the previous chunk's outputs are stored a row block at a time while
+    // this one is computed
+    auto step = [&](int c, const lds_u8* cur) __attribute__((always_inline)) {
         const lds_u8* cQ = cur + SH::OFF_Q;
         const lds_u8* cK = cur + SH::OFF_K;
         const lds_u8* cV = cur + SH::OFF_V;
@@ -224,9 +257,6 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
         static_for<NB>([&](auto rbc) {
             constexpr int rb = decltype(rbc)::value;
             store_pending(rb);
-            if constexpr (rb < NPART) {
-                if (more) issue_part(c + 1, nxt, std::integral_constant<int, rb>{});
-            }
             bx8 qq[NKP];
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) {
@@ -315,16 +345,22 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_bf16_kernel(
 #pragma unroll
             for (int rt = 0; rt < NKD; ++rt) M::mma1(S[rt], kt(rt, NB - 1), Dq[NB - 1]);
         }
-        wait_all_and_barrier();
+        wait_vm(INB{});   // LDS reads done; only this chunk's stores may still be in flight
+        __builtin_amdgcn_s_barrier();
     };
 
-    if (NC > 0) {
-        issue_chunk(0, buf0);
-        wait_all_and_barrier();
-    }
-    for (int c = 0; c < NC; c += 2) {
-        step(c, buf0, buf1);
-        if (c + 1 < NC) step(c + 1, buf1, buf0);
+    if (NC > 0) __builtin_amdgcn_s_barrier();   // the producer's prologue
+    if constexpr (PD == 2) {
+        for (int c = 0; c < NC; c += 3) {
+            step(c, buf0);
+            if (c + 1 < NC) step(c + 1, buf1);
+            if (c + 2 < NC) step(c + 2, buf2);
+        }
+    } else {
+        for (int c = 0; c < NC; c += 2) {
+            step(c, buf0);
+            if (c + 1 < NC) step(c + 1, buf1);
+        }
     }
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) store_pending(rb);
@@ -342,7 +378,7 @@ template <int DK, int C, int DVS>
 hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
     const int nslab = a.d_v / DVS;
     const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
-    hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS>), dim3((unsigned)grid), dim3(DVS / 16 * 64), 0, stream,
+    hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS>), dim3((unsigned)grid), dim3(DVS / 16 * 64 + 64), 0, stream,
                        static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                        static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab);
     return hipGetLastError();

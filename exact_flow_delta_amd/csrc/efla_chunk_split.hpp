@@ -276,10 +276,12 @@ struct ChainLayout {
     static constexpr int BYTES = NBUF * BUF;
 };
 
-// LDS of the bf16 state pass for d_k >= 32 (two buffers of Q, K, V-slab and Ta tiles, each rounded up to 1 KiB)
+// LDS of the bf16 state pass for d_k >= 32 (three buffers of Q, K, V-slab and Ta tiles when they fit, else
+// two; each tile rounded up to 1 KiB)
 constexpr int chain_bf16_bytes(int dk, int c, int dvs) {
-    return 2 * (2 * ((c * dk * 2 + 1023) / 1024) + (c * dvs * 2 + 1023) / 1024 +
-                ((c / 16) * (c / 16 + 1) / 2 * 512 + 1023) / 1024) * 1024;
+    const int buf = (2 * ((c * dk * 2 + 1023) / 1024) + (c * dvs * 2 + 1023) / 1024 +
+                     ((c / 16) * (c / 16 + 1) / 2 * 512 + 1023) / 1024) * 1024;
+    return (3 * buf <= kMaxLdsBytes ? 3 : 2) * buf + (3 * buf <= kMaxLdsBytes ? 0 : 1024);
 }
 
 // The bf16 state pass for d_k >= 32 (direct global -> LDS staging, swizzled tiles); defined in
