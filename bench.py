@@ -11,9 +11,13 @@ The batched decode workload (256 sequences x 32 heads, d 128, 512 MiB fp32 state
 one-token steps, one launch per step) is timed in the same run and reported under "decode".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--only fwd|decode|copy]
+    python bench.py --record-traffic DIR
 
 --only runs one leg for profiling: the forward alone, the decode alone, or a plain 512 MiB
 device-to-device copy (the reference for scaling the HBM byte counters).
+--record-traffic (host only) reads the rocprofv3 counter CSVs of six runs under DIR -- fetch_fwd,
+write_fwd, fetch_dec, write_dec, fetch_copy, write_copy, one FETCH_SIZE or WRITE_SIZE run each (the
+commands are in profiles/hbm_counter_calibration_copy512MiB.md) -- and writes profiles/hbm_traffic.json.
 
 Prints one JSON line.  Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 """
@@ -65,20 +69,88 @@ def decode_algorithmic(NH, dk, dv, esize=2):
     return NH * (2 * dk * dv * 4 + (2 * dk + 2 * dv) * esize + 4)
 
 
+# kernels whose HBM traffic bench.py reports: the names the profiler may list them under (mangled or
+# demangled) and the sources they are built from (the recorded traffic is used only while these still
+# hash to what was measured)
+TRAFFIC_KERNELS = {
+    "chain_bf16_kernel<128,64,64>": {
+        "symbol": ["chain_bf16_kernelILi128ELi64ELi64E", "chain_bf16_kernel<128, 64, 64>"],
+        "sources": ["exact_flow_delta_amd/csrc/efla_chain_bf16.hpp", "exact_flow_delta_amd/csrc/efla_chunk_split.hpp",
+                    "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
+    "ut_kernel<bf16,128,64>": {
+        "symbol": ["ut_kernelIDF16bLi128ELi64E", "ut_kernel<__bf16, 128, 64>"],
+        "sources": ["exact_flow_delta_amd/csrc/efla_chunk_split.hpp", "exact_flow_delta_amd/csrc/efla_ut.hpp",
+                    "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
+    "recurrent_step_kernel<bf16,128,128>": {
+        "symbol": ["recurrent_step_kernelIDF16bLi128ELi128E", "recurrent_step_kernel<__bf16, 128, 128>"],
+        "sources": ["exact_flow_delta_amd/csrc/efla_recurrent.hip", "exact_flow_delta_amd/csrc/efla_common.hpp"]},
+}
+
+
+def _sources_hash(sources):
+    import hashlib
+
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def record_traffic(run_dir):
+    """profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs (host only)."""
+    import csv
+    import glob
+
+    def per_dispatch(sub, counter, match):
+        files = glob.glob(os.path.join(run_dir, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter CSV under %s" % os.path.join(run_dir, sub))
+        vals = {}
+        with open(files[0]) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter and match(row["Kernel_Name"]):
+                    vals[row["Dispatch_Id"]] = vals.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+        if not vals:
+            raise SystemExit("no %s dispatch in %s" % (counter, sub))
+        return statistics.mean(vals.values())
+
+    copy_bytes = 512 * 1024 * 1024
+    is_copy = lambda n: "copyBuffer" in n  # noqa: E731
+    fetch_copy = per_dispatch("fetch_copy", "FETCH_SIZE", is_copy)
+    write_copy = per_dispatch("write_copy", "WRITE_SIZE", is_copy)
+    out = {
+        "note": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (separate runs), each scaled "
+                "by the reading of the same counter for a plain 512 MiB device copy; valid only while the kernel "
+                "sources hash to 'sources_sha256_16'. Written by bench.py --record-traffic.",
+        "copy_calibration": {"bytes": copy_bytes, "FETCH_SIZE_KiB": fetch_copy, "WRITE_SIZE_KiB": write_copy,
+                             "read_factor": copy_bytes / (fetch_copy * 1024.0),
+                             "write_factor": copy_bytes / (write_copy * 1024.0)},
+    }
+    rf, wf = out["copy_calibration"]["read_factor"], out["copy_calibration"]["write_factor"]
+    for name, info in TRAFFIC_KERNELS.items():
+        leg = "dec" if name.startswith("recurrent") else "fwd"
+        match = lambda n, syms=info["symbol"]: any(x in n for x in syms)  # noqa: E731
+        fk = per_dispatch("fetch_" + leg, "FETCH_SIZE", match)
+        wk = per_dispatch("write_" + leg, "WRITE_SIZE", match)
+        out[name] = {"sources": info["sources"], "sources_sha256_16": _sources_hash(info["sources"]),
+                     "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "read_bytes": fk * 1024.0 * rf,
+                     "write_bytes": wk * 1024.0 * wf, "traffic_bytes": (fk * rf + wk * wf) * 1024.0}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: (v["traffic_bytes"] if isinstance(v, dict) and "traffic_bytes" in v else None)
+                      for k, v in out.items() if k not in ("note",)}))
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary (profiles/hbm_traffic.json),
     or None when the kernel's sources no longer hash to what was measured."""
-    import hashlib
-
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             entry = json.load(f)[kernel]
-        h = hashlib.sha256()
-        for src in entry["sources"]:
-            with open(os.path.join(ROOT, src), "rb") as f:
-                h.update(f.read())
-        return entry["traffic_bytes"] if h.hexdigest()[:16] == entry["sources_sha256_16"] else None
+        return entry["traffic_bytes"] if _sources_hash(entry["sources"]) == entry["sources_sha256_16"] else None
     except (OSError, KeyError, ValueError):
         return None
 
@@ -181,7 +253,12 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
                     help="run one leg only (for profiling); prints a short JSON line")
+    ap.add_argument("--record-traffic", metavar="DIR", default=None,
+                    help="write profiles/hbm_traffic.json from rocprofv3 counter CSVs under DIR (host only)")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the forward and decode workloads shard across GPUs by independent "
@@ -224,7 +301,7 @@ def main():
     ut_bytes = ut_algorithmic(w.B, w.H, w.L, w.d_k)
     chain_gbs = chain_bytes / (info["chain_ms"] * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
-    chain_kernel = "chain_kernel<bf16,128,64,64>"
+    chain_kernel = "chain_bf16_kernel<128,64,64>"
     ut_kernel = "ut_kernel<bf16,128,64>"
     result = {
         "metric": METRIC,
