@@ -77,9 +77,9 @@ TRAFFIC_KERNELS = {
         "symbol": ["chain_bf16_kernelILi128ELi64ELi64E", "chain_bf16_kernel<128, 64, 64>"],
         "sources": ["exact_flow_delta_amd/csrc/efla_chain_bf16.hpp", "exact_flow_delta_amd/csrc/efla_chunk_split.hpp",
                     "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
-    "ut_kernel<bf16,128,64>": {
-        "symbol": ["ut_kernelIDF16bLi128ELi64E", "ut_kernel<__bf16, 128, 64>"],
-        "sources": ["exact_flow_delta_amd/csrc/efla_chunk_split.hpp", "exact_flow_delta_amd/csrc/efla_ut.hpp",
+    "ut_wave_kernel<128,64>": {
+        "symbol": ["ut_wave_kernelILi128ELi64E", "ut_wave_kernel<128, 64>"],
+        "sources": ["exact_flow_delta_amd/csrc/efla_ut_wave.hpp", "exact_flow_delta_amd/csrc/efla_chunk_split.hpp",
                     "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
     "recurrent_step_kernel<bf16,128,128>": {
         "symbol": ["recurrent_step_kernelIDF16bLi128ELi128E", "recurrent_step_kernel<__bf16, 128, 128>"],
@@ -202,7 +202,7 @@ def run_forward(efla, W, torch, steps, warmup):
     chain_ms = statistics.mean(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))
     wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
     return w, ms, dict(ut_ms=ut_ms, chain_ms=chain_ms, workspace_bytes=nbytes,
-                       launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds, ut_workgroups=w.B * w.H * nc))
+                       launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds, ut_waves=w.B * w.H * nc))
 
 
 def run_decode(efla, W, torch, warmup=3):
@@ -302,7 +302,7 @@ def main():
     chain_gbs = chain_bytes / (info["chain_ms"] * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     chain_kernel = "chain_bf16_kernel<128,64,64>"
-    ut_kernel = "ut_kernel<bf16,128,64>"
+    ut_kernel = "ut_wave_kernel<128,64>"
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),

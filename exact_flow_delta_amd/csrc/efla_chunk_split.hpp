@@ -28,6 +28,7 @@
 #include "efla_common.hpp"
 #include "efla_launch.hpp"
 #include "efla_ut.hpp"
+#include "efla_ut_wave.hpp"
 
 namespace efla {
 
@@ -511,6 +512,13 @@ hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L
     const int NC = (L + C - 1) / C;
     const int64_t total = (int64_t)BH * NC;
     if (total == 0) return hipSuccess;
+    if constexpr (std::is_same<E, bf16>::value && DK >= 32) {
+        // one wave per (batch*head, chunk)
+        constexpr int WPB = UtWaveShape<DK, C>::WPB;
+        hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3((unsigned)((total + WPB - 1) / WPB)), dim3(WPB * 64), 0, stream,
+                           static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, (int)total);
+        return hipGetLastError();
+    }
     // as many workgroups as the device holds at once, each walking several pairs
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
