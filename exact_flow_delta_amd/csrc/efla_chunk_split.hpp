@@ -513,10 +513,19 @@ hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L
     const int64_t total = (int64_t)BH * NC;
     if (total == 0) return hipSuccess;
     if constexpr (std::is_same<E, bf16>::value && DK >= 32) {
-        // one wave per (batch*head, chunk)
+        // one wave per (batch*head, chunk) at a time; as many waves as the device holds at once
         constexpr int WPB = UtWaveShape<DK, C>::WPB;
-        hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3((unsigned)((total + WPB - 1) / WPB)), dim3(WPB * 64), 0, stream,
-                           static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, (int)total);
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ut_wave_kernel<DK, C>),
+                                                              WPB * 64, 0);
+        if (e != hipSuccess) return e;
+        const int64_t resident = (int64_t)(cus < 1 ? 1 : cus) * (per_cu < 1 ? 1 : per_cu);
+        const int64_t need = (total + WPB - 1) / WPB;
+        hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3((unsigned)(need < resident ? need : resident)), dim3(WPB * 64), 0,
+                           stream, static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, (int)total);
         return hipGetLastError();
     }
     // as many workgroups as the device holds at once, each walking several pairs

@@ -12,12 +12,15 @@
 // holds row 16 rb + r, d_k 32 kp + 8 g .. +7 of the key tile, which is at once the A and the B operand of
 // the Gram blocks K_lo K_hi^T, so the Gram needs no LDS at all.  ||k_t||^2 is summed from the same
 // registers.  The off-diagonal blocks of A stay in registers as the A operands of the block substitution.
-// Only the small pieces that change hands between lanes pass through a private 12 KiB slice of LDS:
+// Only the small pieces that change hands between lanes pass through a private 7 KiB slice of LDS:
 // the diagonal blocks of A (fp32, transposed) for the 16x16 solves, which run for all C/16 blocks at once
 // (lane (r, g): column r of block g, right-looking substitution in fp32), the solved diagonal blocks of
-// T (bf16, transposed, read back as either operand), and Ta^T for the export.
+// T (bf16, transposed, read back as either operand), and Ta^T for the export (in the space of the
+// A blocks, which are dead by then).
 //
-// Many waves per compute unit, each on its own chunk, hide one another's load and dependency latency.
+// The grid is persistent: each wave walks chunks u, u + W, u + 2W, ... (W waves in the grid) and loads
+// the next chunk's keys into the operand registers once the current chunk's Gram blocks and diagonal
+// solves are done, so that the load runs under the off-diagonal blocks and the export.  Several waves per SIMD hide the rest.
 #pragma once
 
 #include "efla_common.hpp"
@@ -32,14 +35,14 @@ struct UtWaveShape {
     static constexpr int LDAT = 20;                   // row stride (floats) of a transposed diagonal A block
     static constexpr int ATB = 16 * LDAT + 4;         // block stride (floats): blocks start on different banks
     static constexpr int OFF_AT = 0;                  // fp32 [NB][ATB]
-    static constexpr int OFF_TT = OFF_AT + NB * ATB * 4;   // bf16 [NB][16][16]: T_bb^T
-    static constexpr int OFF_TAT = OFF_TT + NB * 512;      // bf16 [NQ][16][16]: Ta_qi^T
-    static constexpr int BYTES = (OFF_TAT + NQ * 512 + 15) / 16 * 16;   // per wave
+    static constexpr int OFF_TAT = 0;                 // bf16 [NQ][16][16]: Ta_qi^T, over the dead A blocks
+    static constexpr int OFF_TT = (NB * ATB * 4 > NQ * 512 ? NB * ATB * 4 : NQ * 512);   // bf16 [NB][16][16]: T_bb^T
+    static constexpr int BYTES = (OFF_TT + NB * 512 + 15) / 16 * 16;   // per wave
     static constexpr int WPB = 4;                     // waves per workgroup (the launch bounds assume 4)
 };
 
 template <int DK, int C>
-__global__ __launch_bounds__(256) void ut_wave_kernel(
+__global__ __launch_bounds__(256, 3) void ut_wave_kernel(
     const bf16* __restrict__ k, const float* __restrict__ beta, bf16* __restrict__ tw, int L, int NC, int total) {
     typedef UtWaveShape<DK, C> SH;
     typedef Mma<bf16> M;
@@ -56,145 +59,159 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;
     const int g = lane >> 4;
-    const int u = blockIdx.x * SH::WPB + w;
+    const int stride = gridDim.x * SH::WPB;
+    int u = blockIdx.x * SH::WPB + w;
     if (u >= total) return;   // whole wave
     float* sAt = reinterpret_cast<float*>(smem + w * SH::BYTES + SH::OFF_AT);
     bf16* sTt = reinterpret_cast<bf16*>(smem + w * SH::BYTES + SH::OFF_TT);
     bf16* sTat = reinterpret_cast<bf16*>(smem + w * SH::BYTES + SH::OFF_TAT);
 
-    const int bh = u / NC;
-    const int t0 = (u - bh * NC) * C;
-    const int n = (L - t0 < C) ? (L - t0) : C;   // valid rows; the rest read as zero keys and zero steps
-    const int64_t tok = (int64_t)bh * L + t0;
-
-    // ---- keys into operand registers, and the step of token `lane` ----------------------------------
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + tok * DK, n * DK * 2);
-    bx8 kf[NB][NKP];
-#pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp)
-            kf[rb][kp] = __builtin_bit_cast(bx8, buffer_load<u32x4>(rk, ((16 * rb + r) * DK + 32 * kp + 8 * g) * 2));
-    }
-    const __amdgpu_buffer_rsrc_t rb_ = buffer_rsrc(beta + tok, n * 4);
-    const float beta_mine = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, lane * 4, 0, 0));
-
-    // ---- lambda of rows 16 rb + r (fp32 sum of exact bf16 squares; the four lanes of a row combined) ----
-    float lam[NB];
-#pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-        float s = 0.0f;
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp) s += sum_sq(kf[rb][kp]);
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
-        lam[rb] = s;
-    }
-    // gate of token 16 g + r on lane (r, g) (lanes past the chunk compute an unused value), then the gate
-    // of row 16 rb + r on every lane of row r
-    float lam_mine = lam[0];
-#pragma unroll
-    for (int rb = 1; rb < NB; ++rb) lam_mine = g == rb ? lam[rb] : lam_mine;
-    const float alpha_mine = exact_alpha(beta_mine, lam_mine);
-    float ar[NB];
-#pragma unroll
-    for (int rb = 0; rb < NB; ++rb) ar[rb] = __shfl(alpha_mine, 16 * rb + r, 64);
-
-    // ---- Gram blocks: acc lane (r, g), element i = (K K^T)[16 hi + r][16 lo + 4 g + i] --------------------
-    quad Aq[SH::NQ];   // off-diagonal blocks of A (row order, qi = hi (hi + 1) / 2 + lo), bf16 A operands
-    static_for<NB>([&](auto hc) {
-        constexpr int hi = decltype(hc)::value;
-        static_for<hi + 1>([&](auto lc) {
-            constexpr int lo = decltype(lc)::value;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[lo][kp], kf[hi][kp], acc, 0, 0, 0);
-            if constexpr (lo < hi) {
-                Aq[hi * (hi + 1) / 2 + lo] = M::cvt(acc * ar[hi]);
-            } else {
-                // strict lower part, transposed: At[m][i] = A[16 hi + i][16 hi + m]
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sAt[hi * SH::ATB + (4 * g + i) * SH::LDAT + r] = (4 * g + i < r) ? ar[hi] * acc[i] : 0.0f;
-            }
-        });
-    });
-    // sAt was written by this wave; its LDS operations complete in order
-    __asm__ volatile("" ::: "memory");
-
-    // ---- diagonal solves, all blocks at once: lane (r, g) carries column r of T_gg --------------------------
-    const int blk = g < NB ? g : 0;   // lanes of groups past the last block repeat block 0 and store nothing
-    const float* at = sAt + blk * SH::ATB;
-    float sv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
-    f32x4 ring[4][4];   // rows of At read three steps ahead of their use
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-#pragma unroll
-        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) ring[m][i4] = *reinterpret_cast<const f32x4*>(at + m * SH::LDAT + 4 * i4);
-    }
-#pragma unroll
-    for (int m = 0; m < 15; ++m) {
-        if (m + 3 < 15) {
-#pragma unroll
-            for (int i4 = (m + 4) / 4; i4 < 4; ++i4)
-                ring[(m + 3) & 3][i4] = *reinterpret_cast<const f32x4*>(at + (m + 3) * SH::LDAT + 4 * i4);
-        }
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
-    }
-    if (g < NB) {
-        // row r of T_gg^T and of Ta_gg^T (column r scaled by the gate of token 16 g + r)
-        bx8 t0v, t1v, a0v, a1v;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            t0v[i] = (bf16)sv[i];
-            t1v[i] = (bf16)sv[8 + i];
-            a0v[i] = (bf16)(sv[i] * alpha_mine);
-            a1v[i] = (bf16)(sv[8 + i] * alpha_mine);
-        }
-        bf16* tt = sTt + g * 256 + r * 16;
-        *reinterpret_cast<bx8*>(tt) = t0v;
-        *reinterpret_cast<bx8*>(tt + 8) = t1v;
-        // diagonal block qi = g (g + 3) / 2
-        bf16* ta = sTat + (g * (g + 3) / 2) * 256 + r * 16;
-        *reinterpret_cast<bx8*>(ta) = a0v;
-        *reinterpret_cast<bx8*>(ta + 8) = a1v;
-    }
-    __asm__ volatile("" ::: "memory");
-
-    // ---- off-diagonal blocks, down each block column J: T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ ------------
-    // B operands (column quads, lane (r, g): T_mJ[4 g + e][r]) of the blocks found so far stay in registers
     const int tr = M::tr_offset(lane, 16);
-    static_for<NB - 1>([&](auto jc) {
-        constexpr int J = decltype(jc)::value;
-        quad Tq[NB];
-        Tq[J] = M::lds_quad(sTt + J * 256 + r * 16 + 4 * g);   // T_JJ[4g + e][r] = T_JJ^T[r][4g + e]
-        static_for<NB>([&](auto ic) {
-            constexpr int I = decltype(ic)::value;
-            if constexpr (I > J) {
-                f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                static_for<(I - J) / 2>([&](auto pc) {
-                    constexpr int m = J + 2 * decltype(pc)::value;
-                    M::mma2(y, Aq[I * (I + 1) / 2 + m], Aq[I * (I + 1) / 2 + m + 1], Tq[m], Tq[m + 1]);
-                });
-                if constexpr ((I - J) & 1) M::mma1(y, Aq[I * (I + 1) / 2 + I - 1], Tq[I - 1]);
-                // T_II as the A operand: lane (r, g) <- T_II[r][4g + e] = T_II^T[4g + e][r]
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                M::mma1(z, M::lds_quad_t(sTt + I * 256, 16, tr), M::cvt_neg(y));
-                // z lane (r, g), element e = T_IJ[4g + e][r]: row r of Ta_IJ^T after the column gate of token 16 J + r
-                Tq[I] = M::cvt(z);
-                M::lds_store_quad(sTat + (I * (I + 1) / 2 + J) * 256 + r * 16 + 4 * g, M::cvt(z * ar[J]));
-            }
-        });
-    });
-    __asm__ volatile("" ::: "memory");
 
-    // ---- export: lane (r, g) of block qi takes Ta[16 rb + r][16 kb + 4 g + e] = Ta^T[4 g + e][r] -----------
-    bf16* dst = tw + (int64_t)u * (SH::NQ * 256) + lane * 4;
+    // ---- keys of chunk uu into operand registers, and the step of token `lane` ------------------------
+    // (uu >= total: an empty range, zeros, no memory access -- the registers are written either way, so the
+    // previous chunk's keys are not kept alive across a conditional load)
+    bx8 kf[NB][NKP];
+    float beta_mine;
+    auto load = [&](int uu) __attribute__((always_inline)) {
+        const bool any = uu < total;
+        if (!any) uu = 0;
+        const int bh = uu / NC;
+        const int t0 = (uu - bh * NC) * C;
+        const int n = !any ? 0 : (L - t0 < C) ? (L - t0) : C;   // valid rows; the rest read as zero keys and steps
+        const int64_t tok = (int64_t)bh * L + t0;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + tok * DK, n * DK * 2);
 #pragma unroll
-    for (int qi = 0; qi < SH::NQ; ++qi) *reinterpret_cast<quad*>(dst + qi * 256) = M::lds_quad_t(sTat + qi * 256, 16, tr);
+        for (int rb = 0; rb < NB; ++rb) {
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp)
+                kf[rb][kp] = __builtin_bit_cast(bx8, buffer_load<u32x4>(rk, ((16 * rb + r) * DK + 32 * kp + 8 * g) * 2));
+        }
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(beta + tok, n * 4);
+        beta_mine = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0));
+    };
+    load(u);
+    for (; u < total; u += stride) {
+
+        // ---- lambda of rows 16 rb + r (fp32 sum of exact bf16 squares; the four lanes of a row combined) ----
+        float lam[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+            float s = 0.0f;
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) s += sum_sq(kf[rb][kp]);
+            s += __shfl_xor(s, 16, 64);
+            s += __shfl_xor(s, 32, 64);
+            lam[rb] = s;
+        }
+        // gate of token 16 g + r on lane (r, g) (lanes past the chunk compute an unused value), then the gate
+        // of row 16 rb + r on every lane of row r
+        float lam_mine = lam[0];
+#pragma unroll
+        for (int rb = 1; rb < NB; ++rb) lam_mine = g == rb ? lam[rb] : lam_mine;
+        const float alpha_mine = exact_alpha(beta_mine, lam_mine);
+        float ar[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) ar[rb] = __shfl(alpha_mine, 16 * rb + r, 64);
+
+        // ---- Gram blocks: acc lane (r, g), element i = (K K^T)[16 hi + r][16 lo + 4 g + i] --------------------
+        quad Aq[SH::NQ];   // off-diagonal blocks of A (row order, qi = hi (hi + 1) / 2 + lo), bf16 A operands
+        static_for<NB>([&](auto hc) {
+            constexpr int hi = decltype(hc)::value;
+            static_for<hi + 1>([&](auto lc) {
+                constexpr int lo = decltype(lc)::value;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[lo][kp], kf[hi][kp], acc, 0, 0, 0);
+                if constexpr (lo < hi) {
+                    Aq[hi * (hi + 1) / 2 + lo] = M::cvt(acc * ar[hi]);
+                } else {
+                    // strict lower part, transposed: At[m][i] = A[16 hi + i][16 hi + m]
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sAt[hi * SH::ATB + (4 * g + i) * SH::LDAT + r] = (4 * g + i < r) ? ar[hi] * acc[i] : 0.0f;
+                }
+            });
+        });
+        // sAt was written by this wave; its LDS operations complete in order
+        __asm__ volatile("" ::: "memory");
+
+        // ---- diagonal solves, all blocks at once: lane (r, g) carries column r of T_gg --------------------------
+        const int blk = g < NB ? g : 0;   // lanes of groups past the last block repeat block 0 and store nothing
+        const float* at = sAt + blk * SH::ATB;
+        float sv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+        f32x4 ring[4][4];   // rows of At read three steps ahead of their use
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+#pragma unroll
+            for (int i4 = (m + 1) / 4; i4 < 4; ++i4) ring[m][i4] = *reinterpret_cast<const f32x4*>(at + m * SH::LDAT + 4 * i4);
+        }
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+            if (m + 3 < 15) {
+#pragma unroll
+                for (int i4 = (m + 4) / 4; i4 < 4; ++i4)
+                    ring[(m + 3) & 3][i4] = *reinterpret_cast<const f32x4*>(at + (m + 3) * SH::LDAT + 4 * i4);
+            }
+#pragma unroll
+            for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
+        }
+        // the keys are consumed: fetch the next chunk's (after the solves, which hold the most registers)
+        load(u + stride);
+        if (g < NB) {
+            // row r of T_gg^T and of Ta_gg^T (column r scaled by the gate of token 16 g + r)
+            bx8 t0v, t1v, a0v, a1v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                t0v[i] = (bf16)sv[i];
+                t1v[i] = (bf16)sv[8 + i];
+                a0v[i] = (bf16)(sv[i] * alpha_mine);
+                a1v[i] = (bf16)(sv[8 + i] * alpha_mine);
+            }
+            bf16* tt = sTt + g * 256 + r * 16;
+            *reinterpret_cast<bx8*>(tt) = t0v;
+            *reinterpret_cast<bx8*>(tt + 8) = t1v;
+            // diagonal block qi = g (g + 3) / 2
+            bf16* ta = sTat + (g * (g + 3) / 2) * 256 + r * 16;
+            *reinterpret_cast<bx8*>(ta) = a0v;
+            *reinterpret_cast<bx8*>(ta + 8) = a1v;
+        }
+        __asm__ volatile("" ::: "memory");
+
+        // ---- off-diagonal blocks, down each block column J: T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ ------------
+        // B operands (column quads, lane (r, g): T_mJ[4 g + e][r]) of the blocks found so far stay in registers
+        static_for<NB - 1>([&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            quad Tq[NB];
+            Tq[J] = M::lds_quad(sTt + J * 256 + r * 16 + 4 * g);   // T_JJ[4g + e][r] = T_JJ^T[r][4g + e]
+            static_for<NB>([&](auto ic) {
+                constexpr int I = decltype(ic)::value;
+                if constexpr (I > J) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    static_for<(I - J) / 2>([&](auto pc) {
+                        constexpr int m = J + 2 * decltype(pc)::value;
+                        M::mma2(y, Aq[I * (I + 1) / 2 + m], Aq[I * (I + 1) / 2 + m + 1], Tq[m], Tq[m + 1]);
+                    });
+                    if constexpr ((I - J) & 1) M::mma1(y, Aq[I * (I + 1) / 2 + I - 1], Tq[I - 1]);
+                    // T_II as the A operand: lane (r, g) <- T_II[r][4g + e] = T_II^T[4g + e][r]
+                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    M::mma1(z, M::lds_quad_t(sTt + I * 256, 16, tr), M::cvt_neg(y));
+                    // z lane (r, g), element e = T_IJ[4g + e][r]: row r of Ta_IJ^T after the column gate of token 16 J + r
+                    Tq[I] = M::cvt(z);
+                    M::lds_store_quad(sTat + (I * (I + 1) / 2 + J) * 256 + r * 16 + 4 * g, M::cvt(z * ar[J]));
+                }
+            });
+        });
+        __asm__ volatile("" ::: "memory");
+
+        // ---- export: lane (r, g) of block qi takes Ta[16 rb + r][16 kb + 4 g + e] = Ta^T[4 g + e][r] -----------
+        bf16* dst = tw + (int64_t)u * (SH::NQ * 256) + lane * 4;
+#pragma unroll
+        for (int qi = 0; qi < SH::NQ; ++qi) *reinterpret_cast<quad*>(dst + qi * 256) = M::lds_quad_t(sTat + qi * 256, 16, tr);
+        __asm__ volatile("" ::: "memory");   // the next chunk's A blocks overwrite Ta^T
+    }
 }
 
 }  // namespace efla
