@@ -172,36 +172,51 @@ def run_forward(efla, W, torch, steps, warmup):
     nc, nb = (w.L + w.chunk - 1) // w.chunk, (w.chunk // 16) * (w.chunk // 16 + 1) // 2
     t = ws.view(torch.bfloat16).view(w.B, w.H, nc, nb, 64, 4)
 
-    def step():
-        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws)
+    # One step = the two launches of the split forward (UT transform of every chunk into the workspace, then
+    # the state pass), made through their own entry points so that HIP events between them time each kernel
+    # inside the timed region itself; efla.chunk_fwd(method="split") makes the same two launches and gives
+    # bit-identical results.  The events sit on torch's current stream, the stream the library launches on.
+    def step(ev_a=None, ev_b=None, ev_c=None, gate=efla.GATE_EXACT):
+        if ev_a is not None:
+            ev_a.record()
+        efla.ut_transform(k, beta, chunk_size=w.chunk, out=t, gate=gate)
+        if ev_b is not None:
+            ev_b.record()
+        efla.state_pass(q, k, v, t, chunk_size=w.chunk, out=o, final_state=S)
+        if ev_c is not None:
+            ev_c.record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    assert torch.isfinite(S).all().item(), "non-finite final state"
-
-    # the same two kernels, one entry point each, with events between them (all on torch's current stream,
-    # which is the stream the library launches on)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     for i in range(steps):
-        ev[3 * i].record()
-        efla.ut_transform(k, beta, chunk_size=w.chunk, out=t)
-        ev[3 * i + 1].record()
-        efla.state_pass(q, k, v, t, chunk_size=w.chunk, out=o, final_state=S)
-        ev[3 * i + 2].record()
+        step(ev[3 * i], ev[3 * i + 1], ev[3 * i + 2])
     torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[3 * steps - 1]) / steps
     ut_ms = statistics.mean(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps))
     chain_ms = statistics.mean(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))
+    assert torch.isfinite(S).all().item(), "non-finite final state"
+
+    # the whole forward as one call, and with the delta rule's coefficient alpha = beta (gate 1) on the same
+    # kernels, each over the same number of steps
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    one_call_ms = timed(lambda: efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S,
+                                               workspace=ws))
+    deltanet_ms = timed(lambda: step(gate=efla.GATE_DELTANET))
     wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
-    return w, ms, dict(ut_ms=ut_ms, chain_ms=chain_ms, workspace_bytes=nbytes,
+    return w, ms, dict(ut_ms=ut_ms, chain_ms=chain_ms, workspace_bytes=nbytes, deltanet_ms=deltanet_ms,
+                       one_call_ms=one_call_ms,
                        launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds, ut_waves=w.B * w.H * nc))
 
 
@@ -327,6 +342,9 @@ def main():
                "workspace_bytes": info["workspace_bytes"], "traffic": measured_traffic(ut_kernel)},
         "step": {"algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                  "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "one_call": {"entry": "efla_chunk_fwd_split", "ms_per_step": round(info["one_call_ms"], 5)},
+        "deltanet_gate": {"ms_per_step": round(info["deltanet_ms"], 5),
+                          "exact_over_deltanet": round(ms / info["deltanet_ms"], 4)},
         "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops},
     }

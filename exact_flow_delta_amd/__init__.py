@@ -13,6 +13,10 @@ library is missing, every call raises.
 chunk_fwd runs the two-launch form by default (UT transform of all chunks into a workspace, then the
 state pass); method="fused" runs the single-kernel form, which needs no workspace.
 
+Every call that forms alpha takes ``gate``: GATE_EXACT (0, the default) for the exact coefficient, or
+p in 1 .. GATE_MAX_ORDER for the coefficient of a p-th order Runge-Kutta step of the same dynamics
+(GATE_DELTANET = 1 is the delta rule's alpha = beta); see efla.h, "Gates".
+
 The operator ("Exact Flow Linear Attention" (gist.science), Metodologia items 1-3; "Error-Free
 Linear Attention is a Free Lunch" (howistudyai.com), Steps 1-4):
     alpha_t = (1 - exp(-beta_t ||k_t||^2)) / ||k_t||^2
@@ -36,6 +40,7 @@ _lib = None
 
 EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_NO_DEVICE, EFLA_ERR_HIP, EFLA_ERR_WORKSPACE = range(6)
 EFLA_F32, EFLA_BF16 = 0, 1
+GATE_EXACT, GATE_DELTANET, GATE_MAX_ORDER = 0, 1, 16
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int
@@ -78,6 +83,13 @@ def load_library():
     lib.efla_ut_transform.argtypes = [_vp, _vp, _i32, _vp, _sz, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.efla_chunk_fwd_split.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+    lib.efla_alpha_gate.argtypes = [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp]
+    lib.efla_chunk_fwd_slab_gate.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    lib.efla_recurrent_step_gate.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _vp]
+    lib.efla_ut_transform_gate.argtypes = [_vp, _vp, _i32, _vp, _sz, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    lib.efla_chunk_fwd_split_gate.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _vp, _sz, _vp]
     lib.efla_chunk_state_pass.argtypes = [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
@@ -132,8 +144,8 @@ def _stream(device: torch.device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def alpha(k: torch.Tensor, beta: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Exact gate alpha for keys k [..., d_k] (fp32/bf16) and steps beta [...] (fp32); returns fp32 [...]."""
+def alpha(k: torch.Tensor, beta: torch.Tensor, out: torch.Tensor | None = None, gate: int = GATE_EXACT) -> torch.Tensor:
+    """Gate alpha for keys k [..., d_k] (fp32/bf16) and steps beta [...] (fp32); returns fp32 [...]."""
     lib = load_library()
     _dev_tensor(k, "k")
     _dev_tensor(beta, "beta")
@@ -142,8 +154,8 @@ def alpha(k: torch.Tensor, beta: torch.Tensor, out: torch.Tensor | None = None) 
     if out is None:
         out = torch.empty(beta.shape, dtype=torch.float32, device=k.device)
     _dev_tensor(out, "out")
-    _check(lib.efla_alpha(_ptr(k), _dtype_code(k), _ptr(beta), _ptr(out), beta.numel(), k.shape[-1],
-                          _stream(k.device)), "efla_alpha")
+    _check(lib.efla_alpha_gate(_ptr(k), _dtype_code(k), _ptr(beta), _ptr(out), beta.numel(), k.shape[-1], int(gate),
+                               _stream(k.device)), "efla_alpha")
     return out
 
 
@@ -160,7 +172,7 @@ def chunk_workspace_size(B, H, L, chunk=64, dtype=torch.bfloat16) -> int:
     return n.value
 
 
-def ut_transform(k, beta, chunk_size=64, out=None):
+def ut_transform(k, beta, chunk_size=64, out=None, gate=GATE_EXACT):
     """T diag(alpha) of every chunk, T = (I + strict_lower(diag(alpha) K K^T))^{-1}, in the library's
     operand layout: a tensor [B, H, ceil(L/chunk), nblocks, 64, 4] of k's dtype, where block
     rb (rb+1)/2 + kb (kb <= rb < chunk/16) holds at [lane = 16 g + r][j] the entry
@@ -177,13 +189,13 @@ def ut_transform(k, beta, chunk_size=64, out=None):
     if out is None:
         out = torch.empty((B, H, nc, nb, 64, 4), dtype=k.dtype, device=k.device)
     _dev_tensor(out, "out")
-    _check(lib.efla_ut_transform(_ptr(k), _ptr(beta), _dtype_code(k), _ptr(out), out.numel() * out.element_size(),
-                                 B, H, L, d_k, int(chunk_size), _stream(k.device)), "efla_ut_transform")
+    _check(lib.efla_ut_transform_gate(_ptr(k), _ptr(beta), _dtype_code(k), _ptr(out), out.numel() * out.element_size(),
+                                      B, H, L, d_k, int(chunk_size), int(gate), _stream(k.device)), "efla_ut_transform")
     return out
 
 
 def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_size=64, dv_slab=0,
-              out=None, final_state=None, method="split", workspace=None):
+              out=None, final_state=None, method="split", workspace=None, gate=GATE_EXACT):
     """Chunkwise-parallel EFLA forward over [B,H,L,*] inputs.
 
     Returns (o [B,H,L,d_v] in the input dtype, final state [B,H,d_k,d_v] fp32 or None).
@@ -217,18 +229,20 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
         if final_state.dtype != torch.float32 or tuple(final_state.shape) != (B, H, d_k, d_v):
             raise ValueError("final_state must be float32 [B,H,d_k,d_v]")
     if method == "fused":
-        _check(lib.efla_chunk_fwd_slab(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
-                                       _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
-                                       int(dv_slab), _stream(v.device)), "efla_chunk_fwd")
+        _check(lib.efla_chunk_fwd_slab_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                            _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v,
+                                            int(chunk_size), int(dv_slab), int(gate), _stream(v.device)),
+               "efla_chunk_fwd")
     elif method == "split":
         need = chunk_workspace_size(B, H, L, int(chunk_size), v.dtype)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
         _dev_tensor(workspace, "workspace")
-        _check(lib.efla_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
-                                        _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
-                                        int(dv_slab), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                        _stream(v.device)), "efla_chunk_fwd_split")
+        _check(lib.efla_chunk_fwd_split_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                             _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v,
+                                             int(chunk_size), int(dv_slab), int(gate), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(v.device)),
+               "efla_chunk_fwd_split")
     else:
         raise ValueError("method must be 'split' or 'fused'")
     return out, final_state
@@ -263,7 +277,7 @@ def state_pass(q, k, v, t, initial_state=None, output_final_state=True, chunk_si
     return out, final_state
 
 
-def recurrent_step(q, k, v, beta, state, out=None):
+def recurrent_step(q, k, v, beta, state, out=None, gate=GATE_EXACT):
     """One decode token for [NH,*] inputs (or [N,H,*]); ``state`` [..., d_k, d_v] fp32 is updated in place.
 
     Returns o [..., d_v] in the input dtype.
@@ -286,8 +300,8 @@ def recurrent_step(q, k, v, beta, state, out=None):
     if out is None:
         out = torch.empty(lead + (d_v,), dtype=v.dtype, device=v.device)
     _dev_tensor(out, "out")
-    _check(lib.efla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(state), _ptr(out),
-                                   NH, d_k, d_v, _stream(v.device)), "efla_recurrent_step")
+    _check(lib.efla_recurrent_step_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(state),
+                                        _ptr(out), NH, d_k, d_v, int(gate), _stream(v.device)), "efla_recurrent_step")
     return out
 
 

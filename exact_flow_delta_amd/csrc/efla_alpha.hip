@@ -9,7 +9,7 @@ namespace efla {
 
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void alpha_kernel(const E* __restrict__ k, const float* __restrict__ beta,
-                                                    float* __restrict__ alpha, int64_t n) {
+                                                    float* __restrict__ alpha, int64_t n, int gate) {
     typedef typename Vec16<E>::type V;
     constexpr int VEC = Vec16<E>::N;
     constexpr int LPT = DK / VEC;     // lanes per key
@@ -26,33 +26,34 @@ __global__ __launch_bounds__(256) void alpha_kernel(const E* __restrict__ k, con
         }
     }
     s = group_sum<LPT>(s);
-    if (tok < n && part == 0) alpha[tok] = exact_alpha(beta[tok], s);
+    if (tok < n && part == 0) alpha[tok] = gate_alpha(beta[tok], s, gate);
 }
 
 template <typename E, int DK>
-static hipError_t launch_alpha_t(const void* k, const float* beta, float* alpha, int64_t n, hipStream_t stream) {
+static hipError_t launch_alpha_t(const void* k, const float* beta, float* alpha, int64_t n, int gate,
+                                 hipStream_t stream) {
     constexpr int TPB = 256 / (DK / Vec16<E>::N);
     const int64_t blocks = (n + TPB - 1) / TPB;
     hipLaunchKernelGGL((alpha_kernel<E, DK>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const E*>(k), beta, alpha, n);
+                       static_cast<const E*>(k), beta, alpha, n, gate);
     return hipGetLastError();
 }
 
 hipError_t launch_alpha(const void* k, efla_dtype dt, const float* beta, float* alpha, int64_t n, int d_k,
-                        hipStream_t stream) {
+                        int gate, hipStream_t stream) {
     if (dt == EFLA_BF16) {
         switch (d_k) {
-            case 16: return launch_alpha_t<bf16, 16>(k, beta, alpha, n, stream);
-            case 32: return launch_alpha_t<bf16, 32>(k, beta, alpha, n, stream);
-            case 64: return launch_alpha_t<bf16, 64>(k, beta, alpha, n, stream);
-            case 128: return launch_alpha_t<bf16, 128>(k, beta, alpha, n, stream);
+            case 16: return launch_alpha_t<bf16, 16>(k, beta, alpha, n, gate, stream);
+            case 32: return launch_alpha_t<bf16, 32>(k, beta, alpha, n, gate, stream);
+            case 64: return launch_alpha_t<bf16, 64>(k, beta, alpha, n, gate, stream);
+            case 128: return launch_alpha_t<bf16, 128>(k, beta, alpha, n, gate, stream);
         }
     } else {
         switch (d_k) {
-            case 16: return launch_alpha_t<float, 16>(k, beta, alpha, n, stream);
-            case 32: return launch_alpha_t<float, 32>(k, beta, alpha, n, stream);
-            case 64: return launch_alpha_t<float, 64>(k, beta, alpha, n, stream);
-            case 128: return launch_alpha_t<float, 128>(k, beta, alpha, n, stream);
+            case 16: return launch_alpha_t<float, 16>(k, beta, alpha, n, gate, stream);
+            case 32: return launch_alpha_t<float, 32>(k, beta, alpha, n, gate, stream);
+            case 64: return launch_alpha_t<float, 64>(k, beta, alpha, n, gate, stream);
+            case 128: return launch_alpha_t<float, 128>(k, beta, alpha, n, gate, stream);
         }
     }
     return hipErrorInvalidValue;

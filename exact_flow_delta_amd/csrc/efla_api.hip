@@ -22,6 +22,7 @@ efla_status fail_hip(hipError_t e, const char* where) {
 bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 bool valid_dtype(efla_dtype dt) { return dt == EFLA_F32 || dt == EFLA_BF16; }
+bool valid_gate(int gate) { return gate >= EFLA_GATE_EXACT && gate <= EFLA_GATE_MAX_ORDER; }
 size_t esize(efla_dtype dt) { return dt == EFLA_BF16 ? 2 : 4; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -134,7 +135,7 @@ int64_t chunk_grid(int BH, int d_v, int dvs) { return (int64_t)((BH + 7) / 8) * 
 
 extern "C" {
 
-int efla_version(void) { return 10100; }
+int efla_version(void) { return 10200; }
 
 const char* efla_status_string(efla_status s) {
     switch (s) {
@@ -150,9 +151,9 @@ const char* efla_status_string(efla_status s) {
 
 const char* efla_last_error(void) { return g_last_error; }
 
-efla_status efla_alpha(const void* k, efla_dtype k_dtype, const float* beta, float* alpha, int64_t n_tokens, int d_k,
-                       void* stream) {
-    if (!valid_dtype(k_dtype) || n_tokens < 0) return EFLA_ERR_INVALID_ARG;
+efla_status efla_alpha_gate(const void* k, efla_dtype k_dtype, const float* beta, float* alpha, int64_t n_tokens,
+                            int d_k, int gate, void* stream) {
+    if (!valid_dtype(k_dtype) || n_tokens < 0 || !valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
     if (!valid_dim(d_k)) return EFLA_ERR_UNSUPPORTED;
     if (n_tokens == 0) return EFLA_OK;
     if (!k || !beta || !alpha) return EFLA_ERR_INVALID_ARG;
@@ -163,8 +164,13 @@ efla_status efla_alpha(const void* k, efla_dtype k_dtype, const float* beta, flo
     if (n_tokens / 8 + 1 > INT32_MAX) return EFLA_ERR_INVALID_ARG;
     efla_status st = device_present();
     if (st != EFLA_OK) return st;
-    const hipError_t e = efla::launch_alpha(k, k_dtype, beta, alpha, n_tokens, d_k, (hipStream_t)stream);
+    const hipError_t e = efla::launch_alpha(k, k_dtype, beta, alpha, n_tokens, d_k, gate, (hipStream_t)stream);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_alpha launch");
+}
+
+efla_status efla_alpha(const void* k, efla_dtype k_dtype, const float* beta, float* alpha, int64_t n_tokens, int d_k,
+                       void* stream) {
+    return efla_alpha_gate(k, k_dtype, beta, alpha, n_tokens, d_k, EFLA_GATE_EXACT, stream);
 }
 
 efla_status efla_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int dv_slab,
@@ -178,9 +184,10 @@ efla_status efla_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int chunk
     return EFLA_OK;
 }
 
-efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
-                                void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
-                                int d_v, int chunk, int dv_slab, void* stream) {
+efla_status efla_chunk_fwd_slab_gate(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                     void* o, const float* initial_state, float* final_state, int B, int H, int L,
+                                     int d_k, int d_v, int chunk, int dv_slab, int gate, void* stream) {
+    if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
     int dvs = 0;
     efla_status st = check_chunk_sizes(false, B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
     if (st != EFLA_OK) return st;
@@ -191,10 +198,17 @@ efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, con
     if (L == 0 && !final_state) return EFLA_OK;
     st = device_present();
     if (st != EFLA_OK) return st;
-    efla::ChunkArgs a{q, k, v, beta, o, initial_state, final_state, (int)BH, L, d_k, d_v, chunk, dvs};
+    efla::ChunkArgs a{q, k, v, beta, o, initial_state, final_state, (int)BH, L, d_k, d_v, chunk, dvs, gate};
     const hipError_t e = dtype == EFLA_BF16 ? efla::launch_chunk_fwd_bf16(a, (hipStream_t)stream)
                                             : efla::launch_chunk_fwd_f32(a, (hipStream_t)stream);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd launch");
+}
+
+efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
+                                int d_v, int chunk, int dv_slab, void* stream) {
+    return efla_chunk_fwd_slab_gate(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk,
+                                    dv_slab, EFLA_GATE_EXACT, stream);
 }
 
 
@@ -205,9 +219,9 @@ efla_status efla_chunk_workspace_size(int B, int H, int L, int chunk, efla_dtype
     return EFLA_OK;
 }
 
-efla_status efla_ut_transform(const void* k, const float* beta, efla_dtype dtype, void* t_out, size_t t_out_bytes,
-                              int B, int H, int L, int d_k, int chunk, void* stream) {
-    if (!valid_dtype(dtype) || B < 0 || H < 0 || L < 0) return EFLA_ERR_INVALID_ARG;
+efla_status efla_ut_transform_gate(const void* k, const float* beta, efla_dtype dtype, void* t_out,
+                                   size_t t_out_bytes, int B, int H, int L, int d_k, int chunk, int gate, void* stream) {
+    if (!valid_dtype(dtype) || B < 0 || H < 0 || L < 0 || !valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
     if (!valid_dim(d_k) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     if (BH > INT32_MAX || BH * ((L + chunk - 1) / chunk) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
@@ -219,9 +233,15 @@ efla_status efla_ut_transform(const void* k, const float* beta, efla_dtype dtype
     if (overlap(t_out, need, k, nk) || overlap(t_out, need, beta, nb)) return EFLA_ERR_INVALID_ARG;
     const efla_status st = device_present();
     if (st != EFLA_OK) return st;
-    const hipError_t e = dtype == EFLA_BF16 ? efla::launch_ut_bf16(k, beta, t_out, (int)BH, L, d_k, chunk, (hipStream_t)stream)
-                                            : efla::launch_ut_f32(k, beta, t_out, (int)BH, L, d_k, chunk, (hipStream_t)stream);
+    const hipError_t e = dtype == EFLA_BF16
+                             ? efla::launch_ut_bf16(k, beta, t_out, (int)BH, L, d_k, chunk, gate, (hipStream_t)stream)
+                             : efla::launch_ut_f32(k, beta, t_out, (int)BH, L, d_k, chunk, gate, (hipStream_t)stream);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_ut_transform launch");
+}
+
+efla_status efla_ut_transform(const void* k, const float* beta, efla_dtype dtype, void* t_out, size_t t_out_bytes,
+                              int B, int H, int L, int d_k, int chunk, void* stream) {
+    return efla_ut_transform_gate(k, beta, dtype, t_out, t_out_bytes, B, H, L, d_k, chunk, EFLA_GATE_EXACT, stream);
 }
 
 efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int dv_slab,
@@ -238,7 +258,8 @@ efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int
 namespace {
 efla_status split_entry(bool with_ut, const void* q, const void* k, const void* v, const float* beta,
                         efla_dtype dtype, void* o, const float* initial_state, float* final_state, int B, int H, int L,
-                        int d_k, int d_v, int chunk, int dv_slab, void* tw, size_t tw_bytes, void* stream) {
+                        int d_k, int d_v, int chunk, int dv_slab, int gate, void* tw, size_t tw_bytes, void* stream) {
+    if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
     int dvs = 0;
     efla_status st = check_chunk_sizes(true, B, H, L, d_k, d_v, chunk, dtype, dv_slab, &dvs);
     if (st != EFLA_OK) return st;
@@ -260,26 +281,34 @@ efla_status split_entry(bool with_ut, const void* q, const void* k, const void* 
     if (L == 0 && !final_state) return EFLA_OK;
     st = device_present();
     if (st != EFLA_OK) return st;
-    efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, tw, (int)BH, L, d_k, d_v, chunk, dvs};
+    efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, tw, (int)BH, L, d_k, d_v, chunk, dvs, gate};
     const hipError_t e = dtype == EFLA_BF16 ? efla::launch_split_fwd_bf16(a, with_ut, (hipStream_t)stream)
                                             : efla::launch_split_fwd_f32(a, with_ut, (hipStream_t)stream);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, with_ut ? "efla_chunk_fwd_split launch" : "efla_chunk_state_pass launch");
 }
 }  // namespace
 
+efla_status efla_chunk_fwd_split_gate(const void* q, const void* k, const void* v, const float* beta,
+                                      efla_dtype dtype, void* o, const float* initial_state, float* final_state, int B,
+                                      int H, int L, int d_k, int d_v, int chunk, int dv_slab, int gate,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    return split_entry(true, q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, dv_slab,
+                       gate, workspace, workspace_bytes, stream);
+}
+
 efla_status efla_chunk_fwd_split(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
                                  void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
                                  int d_v, int chunk, int dv_slab, void* workspace, size_t workspace_bytes,
                                  void* stream) {
     return split_entry(true, q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, dv_slab,
-                       workspace, workspace_bytes, stream);
+                       EFLA_GATE_EXACT, workspace, workspace_bytes, stream);
 }
 
 efla_status efla_chunk_state_pass(const void* q, const void* k, const void* v, const void* t_in, size_t t_in_bytes,
                                   efla_dtype dtype, void* o, const float* initial_state, float* final_state, int B,
                                   int H, int L, int d_k, int d_v, int chunk, int dv_slab, void* stream) {
     return split_entry(false, q, k, v, nullptr, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, dv_slab,
-                       const_cast<void*>(t_in), t_in_bytes, stream);
+                       EFLA_GATE_EXACT, const_cast<void*>(t_in), t_in_bytes, stream);
 }
 
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype, void* o,
@@ -289,9 +318,9 @@ efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const fl
                                stream);
 }
 
-efla_status efla_recurrent_step(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
-                                float* state, void* o, int64_t NH, int d_k, int d_v, void* stream) {
-    if (!valid_dtype(dtype) || NH < 0) return EFLA_ERR_INVALID_ARG;
+efla_status efla_recurrent_step_gate(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                     float* state, void* o, int64_t NH, int d_k, int d_v, int gate, void* stream) {
+    if (!valid_dtype(dtype) || NH < 0 || !valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
     if (!valid_dim(d_k) || !valid_dim(d_v)) return EFLA_ERR_UNSUPPORTED;
     if (NH == 0) return EFLA_OK;
     if (NH > INT32_MAX) return EFLA_ERR_INVALID_ARG;
@@ -310,8 +339,14 @@ efla_status efla_recurrent_step(const void* q, const void* k, const void* v, con
         return EFLA_ERR_INVALID_ARG;
     const efla_status st = device_present();
     if (st != EFLA_OK) return st;
-    const hipError_t e = efla::launch_recurrent_step(q, k, v, beta, dtype, state, o, NH, d_k, d_v, (hipStream_t)stream);
+    const hipError_t e =
+        efla::launch_recurrent_step(q, k, v, beta, dtype, state, o, NH, d_k, d_v, gate, (hipStream_t)stream);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_recurrent_step launch");
+}
+
+efla_status efla_recurrent_step(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                float* state, void* o, int64_t NH, int d_k, int d_v, void* stream) {
+    return efla_recurrent_step_gate(q, k, v, beta, dtype, state, o, NH, d_k, d_v, EFLA_GATE_EXACT, stream);
 }
 
 }  // extern "C"

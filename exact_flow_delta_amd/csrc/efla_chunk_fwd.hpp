@@ -119,7 +119,7 @@ struct ChunkStage {
 template <typename E, int DK, int C, int DVS>
 __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ beta,
-    E* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab) {
+    E* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, int gate) {
     typedef ChunkLayout<sizeof(E), DK, C, DVS> LY;
     typedef Mma<E> M;
     typedef typename M::quad quad;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
         // ---- 2. per wave: Gram block row hi (-> A; its diagonal block is solved right here for T_hh) and
         //         Q K^T block row NB-1-hi (-> P).  Both rows share the A-side K blocks; each row keeps its
         //         B-side block (K_hi, Q_hp) in registers across its tiles.
-        ut_rows<E, DK, C, NW, LD_DK, LD_CE, true>(sQ, sK, sLam, sBeta, sA, sAt, sTt, sTat, sP, sAlpha, w, r, g);
+        ut_rows<E, DK, C, NW, LD_DK, LD_CE, true>(sQ, sK, sLam, sBeta, sA, sAt, sTt, sTat, sP, sAlpha, w, r, g, gate);
         __syncthreads();
 
         // ---- 3. off-diagonal blocks of T, one block column J per wave, walked down the column with the
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chunk_fwd_kernel(
 
 template <typename E, int DK, int C, int DVS>
 hipError_t launch_chunk_t(const void* q, const void* k, const void* v, const float* beta, void* o, const float* s0,
-                          float* sf, int BH, int L, int DV, hipStream_t stream) {
+                          float* sf, int BH, int L, int DV, int gate, hipStream_t stream) {
     if constexpr (ChunkLayout<sizeof(E), DK, C, DVS>::BYTES > kMaxLdsBytes) {
         return hipErrorInvalidConfiguration;
     } else {
@@ -320,7 +320,7 @@ hipError_t launch_chunk_t(const void* q, const void* k, const void* v, const flo
         const int64_t grid = (int64_t)((BH + 7) / 8) * 8 * nslab;
         hipLaunchKernelGGL((chunk_fwd_kernel<E, DK, C, DVS>), dim3((unsigned)grid), dim3(DVS / 16 * 64), 0, stream,
                            static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), beta,
-                           static_cast<E*>(o), s0, sf, BH, L, DV, nslab);
+                           static_cast<E*>(o), s0, sf, BH, L, DV, nslab, gate);
         return hipGetLastError();
     }
 }
@@ -328,9 +328,9 @@ hipError_t launch_chunk_t(const void* q, const void* k, const void* v, const flo
 template <typename E, int DK, int C>
 hipError_t launch_chunk_dvs(const ChunkArgs& a, hipStream_t s) {
     switch (a.dvs) {
-        case 16: return launch_chunk_t<E, DK, C, 16>(a.q, a.k, a.v, a.beta, a.o, a.s0, a.sf, a.BH, a.L, a.d_v, s);
-        case 32: return launch_chunk_t<E, DK, C, 32>(a.q, a.k, a.v, a.beta, a.o, a.s0, a.sf, a.BH, a.L, a.d_v, s);
-        case 64: return launch_chunk_t<E, DK, C, 64>(a.q, a.k, a.v, a.beta, a.o, a.s0, a.sf, a.BH, a.L, a.d_v, s);
+        case 16: return launch_chunk_t<E, DK, C, 16>(a.q, a.k, a.v, a.beta, a.o, a.s0, a.sf, a.BH, a.L, a.d_v, a.gate, s);
+        case 32: return launch_chunk_t<E, DK, C, 32>(a.q, a.k, a.v, a.beta, a.o, a.s0, a.sf, a.BH, a.L, a.d_v, a.gate, s);
+        case 64: return launch_chunk_t<E, DK, C, 64>(a.q, a.k, a.v, a.beta, a.o, a.s0, a.sf, a.BH, a.L, a.d_v, a.gate, s);
     }
     return hipErrorInvalidValue;
 }

@@ -105,14 +105,14 @@ constexpr int ut_layout_bytes(int dk, int c) {
 // before the first step so that the substitution runs at arithmetic speed.
 template <typename E, int DK, int C, int LD_DK, int LD_CE>
 __device__ __forceinline__ void ut_rows_balanced(const E* sK, const float* sLam, const float* sBeta, float* sAlpha,
-                                                 E* sA, float* sAt, E* sTt, E* sTat, int w, int r, int g) {
+                                                 E* sA, float* sAt, E* sTt, E* sTat, int w, int r, int g, int gate) {
     typedef Mma<E> M;
     typedef typename M::quad quad;
     constexpr int NB = C / 16;
     constexpr int NW = NB;
     constexpr int NKD = DK / 16;
     const int lane = 16 * g + r;
-    const float a_mine = lane < C ? exact_alpha(sBeta[lane < C ? lane : 0], sLam[lane < C ? lane : 0]) : 0.0f;
+    const float a_mine = lane < C ? gate_alpha(sBeta[lane < C ? lane : 0], sLam[lane < C ? lane : 0], gate) : 0.0f;
     if (w == 0 && lane < C) sAlpha[lane] = a_mine;
     auto alpha_of_row = [&](int blk) { return __shfl(a_mine, 16 * blk + r, 64); };   // alpha of token 16 blk + r
     auto gram = [&](int hi, int lo, f32x4& acc) {   // acc lane (r, g), element i: (K K^T)[16 hi + r][16 lo + 4g + i]
@@ -179,7 +179,7 @@ __device__ __forceinline__ void ut_rows_balanced(const E* sK, const float* sLam,
 
 template <typename E, int DK, int C>
 __global__ __launch_bounds__(C / 16 * 64) void ut_kernel(const E* __restrict__ k, const float* __restrict__ beta,
-                                                         E* __restrict__ tw, int L, int NC, int total) {
+                                                         E* __restrict__ tw, int L, int NC, int total, int gate) {
     typedef UtLayout<sizeof(E), DK, C> LY;
     typedef Mma<E> M;
     typedef typename M::quad quad;
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(C / 16 * 64) void ut_kernel(const E* __restrict__ k
         }
         if (u + (int)gridDim.x < total) load(u + gridDim.x);
         __syncthreads();   // also: every wave is done with the previous pair's LDS
-        ut_rows_balanced<E, DK, C, LD_DK, LD_CE>(sK, sLam, sBeta, sAlpha, sA, sAt, sTt, sTat, w, r, g);
+        ut_rows_balanced<E, DK, C, LD_DK, LD_CE>(sK, sLam, sBeta, sAlpha, sA, sAt, sTt, sTat, w, r, g, gate);
         __syncthreads();
         ut_offdiag<E, C, NW, LD_CE>(sA, sTt, sTat, sAlpha, w, r, g, tr_ce);
         __syncthreads();
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
 // launchers
 // ------------------------------------------------------------------------------------------------
 template <typename E, int DK, int C>
-hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L, hipStream_t stream) {
+hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L, int gate, hipStream_t stream) {
     static_assert(UtLayout<sizeof(E), DK, C>::BYTES <= kMaxLdsBytes, "UT kernel LDS too large");
     const int NC = (L + C - 1) / C;
     const int64_t total = (int64_t)BH * NC;
@@ -525,7 +525,7 @@ hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L
         const int64_t resident = (int64_t)(cus < 1 ? 1 : cus) * (per_cu < 1 ? 1 : per_cu);
         const int64_t need = (total + WPB - 1) / WPB;
         hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3((unsigned)(need < resident ? need : resident)), dim3(WPB * 64), 0,
-                           stream, static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, (int)total);
+                           stream, static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, (int)total, gate);
         return hipGetLastError();
     }
     // as many workgroups as the device holds at once, each walking several pairs
@@ -539,7 +539,7 @@ hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L
     const int64_t resident = (int64_t)(cus < 1 ? 1 : cus) * (per_cu < 1 ? 1 : per_cu);
     const int64_t grid = total < resident ? total : resident;
     hipLaunchKernelGGL((ut_kernel<E, DK, C>), dim3((unsigned)grid), dim3(C / 16 * 64), 0, stream,
-                       static_cast<const E*>(k), beta, static_cast<E*>(tw), L, NC, (int)total);
+                       static_cast<const E*>(k), beta, static_cast<E*>(tw), L, NC, (int)total, gate);
     return hipGetLastError();
 }
 
@@ -562,7 +562,7 @@ hipError_t launch_chain_t(const SplitArgs& a, hipStream_t stream) {
 template <typename E, int DK, int C>
 hipError_t launch_split_c(const SplitArgs& a, bool with_ut, hipStream_t s) {
     if (with_ut && a.L > 0) {
-        const hipError_t e = launch_ut_t<E, DK, C>(a.k, a.beta, a.tw, a.BH, a.L, s);
+        const hipError_t e = launch_ut_t<E, DK, C>(a.k, a.beta, a.tw, a.BH, a.L, a.gate, s);
         if (e != hipSuccess) return e;
     }
     switch (a.dvs) {
@@ -596,22 +596,23 @@ hipError_t launch_split_e(const SplitArgs& a, bool with_ut, hipStream_t s) {
 }
 
 template <typename E, int DK>
-hipError_t launch_ut_dk(const void* k, const float* beta, void* tw, int BH, int L, int chunk, hipStream_t s) {
+hipError_t launch_ut_dk(const void* k, const float* beta, void* tw, int BH, int L, int chunk, int gate, hipStream_t s) {
     switch (chunk) {
-        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, s);
-        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, s);
-        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, s);
+        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, gate, s);
+        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, gate, s);
+        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, gate, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename E>
-hipError_t launch_ut_e(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, hipStream_t s) {
+hipError_t launch_ut_e(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
+                       hipStream_t s) {
     switch (d_k) {
-        case 16: return launch_ut_dk<E, 16>(k, beta, tw, BH, L, chunk, s);
-        case 32: return launch_ut_dk<E, 32>(k, beta, tw, BH, L, chunk, s);
-        case 64: return launch_ut_dk<E, 64>(k, beta, tw, BH, L, chunk, s);
-        case 128: return launch_ut_dk<E, 128>(k, beta, tw, BH, L, chunk, s);
+        case 16: return launch_ut_dk<E, 16>(k, beta, tw, BH, L, chunk, gate, s);
+        case 32: return launch_ut_dk<E, 32>(k, beta, tw, BH, L, chunk, gate, s);
+        case 64: return launch_ut_dk<E, 64>(k, beta, tw, BH, L, chunk, gate, s);
+        case 128: return launch_ut_dk<E, 128>(k, beta, tw, BH, L, chunk, gate, s);
     }
     return hipErrorInvalidValue;
 }

@@ -70,6 +70,24 @@ __device__ __forceinline__ float exact_alpha(float beta, float lambda) {
     return -expm1f(-x) / lambda;
 }
 
+// The coefficient of the update for one of the integrators of the same dynamics dS/dt = -k k^T S + k v^T
+// over a step beta ("Error-Free Linear Attention guida completa" (mauroscia.it), the section on RK-infinity:
+// Euler and Runge-Kutta steps of rising order approach the exact flow; "Error-Free Linear Attention is a
+// Free Lunch" (howistudyai.com), building blocks "Delta Rule" and "Runge-Kutta Methods").
+//   gate == 0: the exact flow, exact_alpha above.
+//   gate == p in 1 .. kMaxGate: a p-th order Runge-Kutta step, whose update keeps the same rank-1 form
+//     (the p-th degree Taylor polynomial of e^{-beta k k^T}, with (k k^T)^n = lambda^{n-1} k k^T) with
+//     alpha_p = beta sum_{n=0}^{p-1} (-beta lambda)^n / (n+1)!   -- p = 1 is the delta rule's alpha = beta.
+// Horner's scheme in fp32.
+constexpr int kMaxGate = 16;
+__device__ __forceinline__ float gate_alpha(float beta, float lambda, int gate) {
+    if (gate == 0) return exact_alpha(beta, lambda);
+    const float mx = -beta * lambda;
+    float s = 1.0f;
+    for (int n = gate - 1; n >= 1; --n) s = 1.0f + s * mx / (float)(n + 1);
+    return beta * s;
+}
+
 // ------------------------------------------------------------------------------------------------
 // element conversion
 // ------------------------------------------------------------------------------------------------

@@ -9,12 +9,13 @@
 namespace efla {
 
 // Exact gate for n tokens of d_k keys.
-hipError_t launch_alpha(const void* k, efla_dtype dt, const float* beta, float* alpha, int64_t n, int d_k,
+// gate: 0 for the exact coefficient, p in 1 .. 16 for the p-th order Runge-Kutta one (gate_alpha)
+hipError_t launch_alpha(const void* k, efla_dtype dt, const float* beta, float* alpha, int64_t n, int d_k, int gate,
                         hipStream_t stream);
 
 // One decode token for NH independent states (in place).
 hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, const float* beta, efla_dtype dt,
-                                 float* state, void* o, int64_t NH, int d_k, int d_v, hipStream_t stream);
+                                 float* state, void* o, int64_t NH, int d_k, int d_v, int gate, hipStream_t stream);
 
 // Chunked forward.  One workgroup per (batch*head, d_v slab of `dvs` columns); every workgroup
 // walks the chunks of its sequence in order, carrying its slab of the state.
@@ -27,6 +28,7 @@ struct ChunkArgs {
     const float* s0;   // may be null
     float* sf;         // may be null
     int BH, L, d_k, d_v, chunk, dvs;
+    int gate;          // 0: exact coefficient; p: p-th order Runge-Kutta (gate_alpha)
 };
 
 // LDS bytes of the chunk kernel for these sizes, or -1 when no kernel is built for them.
@@ -49,6 +51,7 @@ struct SplitArgs {
     float* sf;         // may be null
     void* tw;          // T diag(alpha) blocks, BH * ceil(L / chunk) * ut_block_elems(chunk) elements
     int BH, L, d_k, d_v, chunk, dvs;
+    int gate;          // 0: exact coefficient; p: p-th order Runge-Kutta (gate_alpha)
 };
 
 // elements of the UT output per chunk: (chunk/16)(chunk/16 + 1)/2 blocks of 256
@@ -61,9 +64,9 @@ int ut_lds_bytes(efla_dtype dt, int d_k, int chunk);
 // with_ut = false: a.tw already holds the UT output; only the state pass is launched
 hipError_t launch_split_fwd_f32(const SplitArgs& a, bool with_ut, hipStream_t stream);
 hipError_t launch_split_fwd_bf16(const SplitArgs& a, bool with_ut, hipStream_t stream);
-hipError_t launch_ut_f32(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk,
+hipError_t launch_ut_f32(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
                          hipStream_t stream);
-hipError_t launch_ut_bf16(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk,
+hipError_t launch_ut_bf16(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
                           hipStream_t stream);
 
 }  // namespace efla

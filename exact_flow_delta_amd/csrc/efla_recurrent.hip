@@ -30,7 +30,7 @@ struct StepShape {
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__((StepShape<DK, DV>::NT)) void recurrent_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ beta,
-    float* __restrict__ state, E* __restrict__ o) {
+    float* __restrict__ state, E* __restrict__ o, int gate) {
     typedef StepShape<DK, DV> SH;
     __shared__ float red_a[SH::NW][DV];
     __shared__ float red_b[SH::NW][DV];
@@ -109,7 +109,7 @@ __global__ __launch_bounds__((StepShape<DK, DV>::NT)) void recurrent_step_kernel
         kq += red_s[w][1];
     }
     // every row of the key was summed exactly once into lambda and k^T q
-    const float alpha = exact_alpha(bt, lam);
+    const float alpha = gate_alpha(bt, lam, gate);
     const f32x4 d = vv - a;
 #pragma unroll
     for (int i = 0; i < SH::RPT; ++i) {
@@ -126,41 +126,41 @@ __global__ __launch_bounds__((StepShape<DK, DV>::NT)) void recurrent_step_kernel
 
 template <typename E, int DK, int DV>
 static hipError_t launch_step_t(const void* q, const void* k, const void* v, const float* beta, float* state,
-                                void* o, int64_t NH, hipStream_t stream) {
+                                void* o, int64_t NH, int gate, hipStream_t stream) {
     hipLaunchKernelGGL((recurrent_step_kernel<E, DK, DV>), dim3((unsigned)NH), dim3(StepShape<DK, DV>::NT), 0,
                        stream, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), beta,
-                       state, static_cast<E*>(o));
+                       state, static_cast<E*>(o), gate);
     return hipGetLastError();
 }
 
 template <typename E, int DK>
 static hipError_t launch_step_dv(const void* q, const void* k, const void* v, const float* beta, float* state,
-                                 void* o, int64_t NH, int d_v, hipStream_t stream) {
+                                 void* o, int64_t NH, int d_v, int gate, hipStream_t stream) {
     switch (d_v) {
-        case 16: return launch_step_t<E, DK, 16>(q, k, v, beta, state, o, NH, stream);
-        case 32: return launch_step_t<E, DK, 32>(q, k, v, beta, state, o, NH, stream);
-        case 64: return launch_step_t<E, DK, 64>(q, k, v, beta, state, o, NH, stream);
-        case 128: return launch_step_t<E, DK, 128>(q, k, v, beta, state, o, NH, stream);
+        case 16: return launch_step_t<E, DK, 16>(q, k, v, beta, state, o, NH, gate, stream);
+        case 32: return launch_step_t<E, DK, 32>(q, k, v, beta, state, o, NH, gate, stream);
+        case 64: return launch_step_t<E, DK, 64>(q, k, v, beta, state, o, NH, gate, stream);
+        case 128: return launch_step_t<E, DK, 128>(q, k, v, beta, state, o, NH, gate, stream);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename E>
 static hipError_t launch_step_e(const void* q, const void* k, const void* v, const float* beta, float* state,
-                                void* o, int64_t NH, int d_k, int d_v, hipStream_t stream) {
+                                void* o, int64_t NH, int d_k, int d_v, int gate, hipStream_t stream) {
     switch (d_k) {
-        case 16: return launch_step_dv<E, 16>(q, k, v, beta, state, o, NH, d_v, stream);
-        case 32: return launch_step_dv<E, 32>(q, k, v, beta, state, o, NH, d_v, stream);
-        case 64: return launch_step_dv<E, 64>(q, k, v, beta, state, o, NH, d_v, stream);
-        case 128: return launch_step_dv<E, 128>(q, k, v, beta, state, o, NH, d_v, stream);
+        case 16: return launch_step_dv<E, 16>(q, k, v, beta, state, o, NH, d_v, gate, stream);
+        case 32: return launch_step_dv<E, 32>(q, k, v, beta, state, o, NH, d_v, gate, stream);
+        case 64: return launch_step_dv<E, 64>(q, k, v, beta, state, o, NH, d_v, gate, stream);
+        case 128: return launch_step_dv<E, 128>(q, k, v, beta, state, o, NH, d_v, gate, stream);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, const float* beta, efla_dtype dt,
-                                 float* state, void* o, int64_t NH, int d_k, int d_v, hipStream_t stream) {
-    if (dt == EFLA_BF16) return launch_step_e<bf16>(q, k, v, beta, state, o, NH, d_k, d_v, stream);
-    return launch_step_e<float>(q, k, v, beta, state, o, NH, d_k, d_v, stream);
+                                 float* state, void* o, int64_t NH, int d_k, int d_v, int gate, hipStream_t stream) {
+    if (dt == EFLA_BF16) return launch_step_e<bf16>(q, k, v, beta, state, o, NH, d_k, d_v, gate, stream);
+    return launch_step_e<float>(q, k, v, beta, state, o, NH, d_k, d_v, gate, stream);
 }
 
 }  // namespace efla

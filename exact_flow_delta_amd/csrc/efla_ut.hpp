@@ -45,7 +45,8 @@ constexpr int kLdAt = 16 + 4;   // row stride of sAt (fp32)
 // go to sTt / sTat.  Both block rows share the A-side K blocks; each keeps its B-side block in registers.
 template <typename E, int DK, int C, int NW, int LD_DK, int LD_CE, bool WITH_P>
 __device__ __forceinline__ void ut_rows(const E* sQ, const E* sK, const float* sLam, const float* sBeta, E* sA,
-                                        float* sAt, E* sTt, E* sTat, E* sP, float* sAlpha, int w, int r, int g) {
+                                        float* sAt, E* sTt, E* sTat, E* sP, float* sAlpha, int w, int r, int g,
+                                        int gate) {
     typedef Mma<E> M;
     typedef typename M::quad quad;
     constexpr int NB = C / 16;
@@ -55,7 +56,7 @@ __device__ __forceinline__ void ut_rows(const E* sQ, const E* sK, const float* s
         constexpr int hp = NB - 1 - hi;
         if (hi % NW == w) {
             // alpha of this block row's tokens (lane r: token 16 hi + r)
-            const float ar = exact_alpha(sBeta[16 * hi + r], sLam[16 * hi + r]);
+            const float ar = gate_alpha(sBeta[16 * hi + r], sLam[16 * hi + r], gate);
             if (g == 0) sAlpha[16 * hi + r] = ar;
             quad bk[NKD], bq[NKD];
 #pragma unroll

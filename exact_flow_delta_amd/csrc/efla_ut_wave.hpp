@@ -43,7 +43,8 @@ struct UtWaveShape {
 
 template <int DK, int C>
 __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
-    const bf16* __restrict__ k, const float* __restrict__ beta, bf16* __restrict__ tw, int L, int NC, int total) {
+    const bf16* __restrict__ k, const float* __restrict__ beta, bf16* __restrict__ tw, int L, int NC, int total,
+    int gate) {
     typedef UtWaveShape<DK, C> SH;
     typedef Mma<bf16> M;
     typedef M::quad quad;
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
         float lam_mine = lam[0];
 #pragma unroll
         for (int rb = 1; rb < NB; ++rb) lam_mine = g == rb ? lam[rb] : lam_mine;
-        const float alpha_mine = exact_alpha(beta_mine, lam_mine);
+        const float alpha_mine = gate_alpha(beta_mine, lam_mine, gate);
         float ar[NB];
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) ar[rb] = __shfl(alpha_mine, 16 * rb + r, 64);

@@ -18,6 +18,9 @@ The five workloads (sizes, distributions) follow the targets this library is mea
                     per (b, t) shared by all heads, v = N(0,1) + 0.5 N(0,1), beta = sigmoid(N(0,1)), chunk 64
   5 "decode"        256 sequences x 32 heads, d128, fp32 state S0 = 0.1 N(0,1); per step s: q,k,v bf16
                     N(0,1), beta = sigmoid(N(0,1)); 64 steps
+  6 "gates"         B2 H2 L300 d64 fp32 (or bf16), q,v ~ N(0,1), k = u*s with u uniform on the unit sphere
+                    and s uniform in [0.2, 1.3], beta = sigmoid(N(0,1)), S0 = 0.1 N(0,1), chunk 32: keys of
+                    moderate norm (beta ||k||^2 < 1.7), where the explicit Runge-Kutta gates are stable
 
 "N(0, s)" is read as a normal with standard deviation s.
 """
@@ -54,6 +57,7 @@ WORKLOADS = {
     3: Workload(3, "lm_layer", 8, 16, 4096, 128, 128, "bf16", 64),
     4: Workload(4, "long_context", 1, 16, 65536, 128, 128, "bf16", 64),
     5: Workload(5, "decode", 256, 32, 1, 128, 128, "bf16", 64, steps=64),
+    6: Workload(6, "gates", 2, 2, 300, 64, 64, "f32", 32),
 }
 
 
@@ -119,6 +123,13 @@ def make_fwd_inputs(w: Workload, salt: int = 0) -> dict:
         v = _rng(c, T_V, 0, salt).standard_normal((B, H, L, dv)) + \
             0.5 * _rng(c, T_NOISE, 0, salt).standard_normal((B, H, L, dv))
         beta = _sigmoid(beta_z)
+    elif c == 6:
+        g = _rng(c, T_K, 0, salt).standard_normal((B, H, L, dk))
+        u = g / np.linalg.norm(g, axis=-1, keepdims=True)
+        k = u * _rng(c, T_SCALE, 0, salt).uniform(0.2, 1.3, (B, H, L, 1))
+        v = _rng(c, T_V, 0, salt).standard_normal((B, H, L, dv))
+        beta = _sigmoid(beta_z)
+        s0 = 0.1 * _rng(c, T_S0, 0, salt).standard_normal((B, H, dk, dv))
     else:  # 1 and any plain workload
         k = _rng(c, T_K, 0, salt).standard_normal((B, H, L, dk))
         v = _rng(c, T_V, 0, salt).standard_normal((B, H, L, dv))

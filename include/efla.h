@@ -52,6 +52,27 @@ typedef enum {
 typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
 
 /*
+ * Gates.  The calls below use the exact coefficient alpha_t.  Their *_gate variants take an `int gate`
+ * that selects the coefficient of another integrator of the same per-token dynamics
+ * dS/dt = -k k^T S + k v^T over a step beta, with every kernel and layout unchanged:
+ *   EFLA_GATE_EXACT (0)     the exact flow, alpha = (1 - e^{-beta lambda}) / lambda
+ *   p in 1 .. EFLA_GATE_MAX_ORDER
+ *                           one p-th order Runge-Kutta step.  For this rank-1 dynamics it has the same
+ *                           update form, with alpha_p = sum_{n=1}^{p} (-1)^{n-1} beta^n lambda^{n-1} / n!
+ *                           (the degree-p Taylor polynomial of the exponential, reduced with
+ *                           (k k^T)^n = lambda^{n-1} k k^T).  p = 1 (EFLA_GATE_DELTANET) is the explicit
+ *                           Euler step, the delta rule's alpha = beta; alpha_p -> alpha as p grows.
+ * ("Error-Free Linear Attention guida completa" (mauroscia.it), the section on RK-infinity: Euler and
+ * Runge-Kutta steps of rising order approach the exact solution; "Error-Free Linear Attention is a Free
+ * Lunch" (howistudyai.com), building blocks "Delta Rule" and "Runge-Kutta Methods".)  A gate outside
+ * 0 .. EFLA_GATE_MAX_ORDER is EFLA_ERR_INVALID_ARG.  alpha_p is evaluated in fp32 by Horner's scheme;
+ * for large beta*lambda it grows like (beta lambda)^{p-1} (the explicit schemes are not stable there).
+ */
+#define EFLA_GATE_EXACT 0
+#define EFLA_GATE_DELTANET 1
+#define EFLA_GATE_MAX_ORDER 16
+
+/*
  * efla_alpha -- the exact gate alpha_t for n_tokens keys.
  * "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 1; "Exact Flow Linear
  * Attention" (gist.science), Metodologia item 3 (the effective coefficient).
@@ -63,6 +84,9 @@ typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
  */
 efla_status efla_alpha(const void* k, efla_dtype k_dtype, const float* beta, float* alpha,
                        int64_t n_tokens, int d_k, void* stream);
+/* efla_alpha with a gate (see "Gates" above); efla_alpha is gate EFLA_GATE_EXACT. */
+efla_status efla_alpha_gate(const void* k, efla_dtype k_dtype, const float* beta, float* alpha,
+                            int64_t n_tokens, int d_k, int gate, void* stream);
 
 /*
  * efla_chunk_fwd -- the whole sequence forward: every o_t and (optionally) the final state.
@@ -99,6 +123,11 @@ efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const fl
 efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, const float* beta,
                                 efla_dtype dtype, void* o, const float* initial_state, float* final_state,
                                 int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab, void* stream);
+/* efla_chunk_fwd_slab with a gate (see "Gates" above): alpha_t of every token is the gate's. */
+efla_status efla_chunk_fwd_slab_gate(const void* q, const void* k, const void* v, const float* beta,
+                                     efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                     int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab, int gate,
+                                     void* stream);
 
 /*
  * efla_recurrent_step -- one decode token for NH independent (sequence, head) states, in place.
@@ -116,6 +145,10 @@ efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, con
 efla_status efla_recurrent_step(const void* q, const void* k, const void* v, const float* beta,
                                 efla_dtype dtype, float* state, void* o,
                                 int64_t NH, int d_k, int d_v, void* stream);
+/* efla_recurrent_step with a gate (see "Gates" above). */
+efla_status efla_recurrent_step_gate(const void* q, const void* k, const void* v, const float* beta,
+                                     efla_dtype dtype, float* state, void* o,
+                                     int64_t NH, int d_k, int d_v, int gate, void* stream);
 
 /*
  * efla_chunk_workspace_size -- bytes of the workspace efla_chunk_fwd_split needs, which is also the
@@ -143,6 +176,10 @@ efla_status efla_chunk_workspace_size(int B, int H, int L, int chunk, efla_dtype
  */
 efla_status efla_ut_transform(const void* k, const float* beta, efla_dtype dtype, void* t_out, size_t t_out_bytes,
                               int B, int H, int L, int d_k, int chunk, void* stream);
+/* efla_ut_transform with a gate (see "Gates" above): alpha in A and in T diag(alpha) is the gate's. */
+efla_status efla_ut_transform_gate(const void* k, const float* beta, efla_dtype dtype, void* t_out,
+                                   size_t t_out_bytes, int B, int H, int L, int d_k, int chunk, int gate,
+                                   void* stream);
 
 /*
  * efla_chunk_fwd_split -- efla_chunk_fwd as two launches on `stream`: efla_ut_transform of every chunk into
@@ -158,6 +195,12 @@ efla_status efla_chunk_fwd_split(const void* q, const void* k, const void* v, co
                                  efla_dtype dtype, void* o, const float* initial_state, float* final_state,
                                  int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab,
                                  void* workspace, size_t workspace_bytes, void* stream);
+/* efla_chunk_fwd_split with a gate (see "Gates" above).  The state pass itself does not depend on the
+ * gate (it reads T diag(alpha) from the workspace), so efla_chunk_state_pass serves every gate. */
+efla_status efla_chunk_fwd_split_gate(const void* q, const void* k, const void* v, const float* beta,
+                                      efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                      int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab, int gate,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * efla_chunk_state_pass -- the inter-chunk state pass alone, from a UT output made beforehand by

@@ -44,31 +44,33 @@ class Oracle:
 
     def __init__(self, lib_path: str):
         lib = ctypes.CDLL(lib_path)
-        lib.efla_oracle_alpha.argtypes = [_dp, _dp, _dp, ctypes.c_int64, ctypes.c_int]
+        lib.efla_oracle_alpha.argtypes = [_dp, _dp, _dp, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
         lib.efla_oracle_alpha.restype = None
         lib.efla_oracle_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.efla_oracle_fwd.restype = ctypes.c_int
         lib.efla_oracle_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp,
-                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.efla_oracle_step.restype = ctypes.c_int
         lib.efla_oracle_ut.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_int, ctypes.c_int]
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.efla_oracle_ut.restype = ctypes.c_int
         self.lib = lib
 
-    def alpha(self, k, beta):
-        """alpha for keys k [..., d_k] and steps beta [...]; returns float64 [...]."""
+    def alpha(self, k, beta, gate=0):
+        """alpha for keys k [..., d_k] and steps beta [...]; returns float64 [...].
+
+        gate 0: the exact coefficient; gate p >= 1: the p-th order Runge-Kutta coefficient."""
         k = _f64(k)
         beta = _f64(beta)
         d_k = k.shape[-1]
         assert beta.shape == k.shape[:-1]
         out = np.empty(beta.shape, dtype=np.float64)
-        self.lib.efla_oracle_alpha(_ptr(k), _ptr(beta), _ptr(out), int(beta.size), int(d_k))
+        self.lib.efla_oracle_alpha(_ptr(k), _ptr(beta), _ptr(out), int(beta.size), int(d_k), int(gate))
         return out
 
-    def fwd(self, q, k, v, beta, initial_state=None, n_threads=0, want_o=True, want_state=True):
+    def fwd(self, q, k, v, beta, initial_state=None, n_threads=0, want_o=True, want_state=True, gate=0):
         """Token-by-token recurrence over [B,H,L,*] inputs.
 
         Returns (o [B,H,L,d_v] float64 or None, final_state [B,H,d_k,d_v] float64 or None, threads).
@@ -84,10 +86,10 @@ class Oracle:
         o = np.empty((B, H, L, d_v), dtype=np.float64) if want_o else None
         sf = np.empty((B, H, d_k, d_v), dtype=np.float64) if want_state else None
         used = self.lib.efla_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
-                                        B, H, L, d_k, d_v, int(n_threads))
+                                        B, H, L, d_k, d_v, int(gate), int(n_threads))
         return o, sf, used
 
-    def ut(self, k, beta, chunk, n_threads=0):
+    def ut(self, k, beta, chunk, n_threads=0, gate=0):
         """Intra-chunk transform T diag(alpha), T = (I + strict_lower(diag(alpha) K K^T))^{-1}, per chunk.
 
         Returns float64 [B,H,ceil(L/chunk),chunk,chunk] (rows/columns past a short last chunk are zero).
@@ -97,10 +99,10 @@ class Oracle:
         assert beta.shape == (B, H, L)
         nc = (L + chunk - 1) // chunk
         out = np.empty((B, H, nc, chunk, chunk), dtype=np.float64)
-        self.lib.efla_oracle_ut(_ptr(k), _ptr(beta), _ptr(out), B, H, L, d_k, int(chunk), int(n_threads))
+        self.lib.efla_oracle_ut(_ptr(k), _ptr(beta), _ptr(out), B, H, L, d_k, int(chunk), int(gate), int(n_threads))
         return out
 
-    def step(self, q, k, v, beta, state, n_threads=0):
+    def step(self, q, k, v, beta, state, n_threads=0, gate=0):
         """One decode step for [NH,*] inputs; ``state`` [NH,d_k,d_v] is copied, updated and returned.
 
         Returns (o [NH,d_v] float64, new_state float64, threads).
@@ -112,7 +114,7 @@ class Oracle:
         assert s.shape == (NH, d_k, d_v) and beta.shape == (NH,)
         o = np.empty((NH, d_v), dtype=np.float64)
         used = self.lib.efla_oracle_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s), _ptr(o),
-                                         int(NH), int(d_k), int(d_v), int(n_threads))
+                                         int(NH), int(d_k), int(d_v), int(gate), int(n_threads))
         return o, s, used
 
 
@@ -129,20 +131,20 @@ def default() -> Oracle:
     return _default
 
 
-def alpha(k, beta):
-    return default().alpha(k, beta)
+def alpha(k, beta, gate=0):
+    return default().alpha(k, beta, gate)
 
 
-def fwd(q, k, v, beta, initial_state=None, n_threads=0, want_o=True, want_state=True):
-    return default().fwd(q, k, v, beta, initial_state, n_threads, want_o, want_state)
+def fwd(q, k, v, beta, initial_state=None, n_threads=0, want_o=True, want_state=True, gate=0):
+    return default().fwd(q, k, v, beta, initial_state, n_threads, want_o, want_state, gate)
 
 
-def step(q, k, v, beta, state, n_threads=0):
-    return default().step(q, k, v, beta, state, n_threads)
+def step(q, k, v, beta, state, n_threads=0, gate=0):
+    return default().step(q, k, v, beta, state, n_threads, gate)
 
 
-def ut(k, beta, chunk, n_threads=0):
-    return default().ut(k, beta, chunk, n_threads)
+def ut(k, beta, chunk, n_threads=0, gate=0):
+    return default().ut(k, beta, chunk, n_threads, gate)
 
 
 def _f64(x):

@@ -32,6 +32,13 @@
  * A second function, efla_oracle_ut, gives the intra-chunk transform of the chunked form by its
  * definition (used to check the GPU's UT output; see its own comment).
  *
+ * Gates.  Every entry point takes `gate`: 0 is the exact coefficient above; p >= 1 replaces alpha_t by
+ * the coefficient of one p-th order Runge-Kutta step of the same per-token ODE over [0, beta_t]
+ * (see oracle_alpha_rk).  "Error-Free Linear Attention guida completa" (mauroscia.it), section on
+ * RK-infinity (Euler and Runge-Kutta schemes of rising order approach the exact solution, which is the
+ * infinite-order limit); "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), building blocks
+ * "Delta Rule" (S <- (I - beta k k^T) S + beta k v^T, the Euler step) and "Runge-Kutta Methods".
+ *
  * Layouts (all contiguous, row-major):
  *   q, k [B,H,L,d_k]; v [B,H,L,d_v]; beta [B,H,L]; o [B,H,L,d_v]; state [B,H,d_k,d_v].
  * Parallelism: OpenMP over independent (b, h) pairs only.
@@ -44,12 +51,33 @@
 #include <omp.h>
 #endif
 
-/* alpha_t = (1 - e^{-beta lambda}) / lambda, lambda = ||k||^2; the lambda = 0 limit is beta. */
-static double oracle_alpha_one(const double *k, double beta, int d_k)
+/* One step of a p-th order Runge-Kutta method for dS/dt = -A S + k v^T (A = k k^T) over [0, beta]
+ * multiplies S by the degree-p Taylor polynomial of e^{-beta A}, sum_{n=0}^{p} (-beta A)^n / n!, and adds
+ * the matching truncation of the input integral.  With A^n = lambda^{n-1} A (n >= 1) both collapse to the
+ * rank-1 form (I - alpha_p A) S + alpha_p k v^T with
+ *   alpha_p = sum_{n=1}^{p} (-1)^{n-1} beta^n lambda^{n-1} / n!
+ * (p = 1: alpha = beta, the delta rule).  Written out term by term. */
+static double oracle_alpha_rk(double beta, double lambda, int p)
+{
+    double alpha = 0.0;
+    double factorial = 1.0;
+    for (int n = 1; n <= p; ++n) {
+        factorial *= n;
+        const double sign = (n % 2 == 1) ? 1.0 : -1.0;   /* (-1)^{n-1} */
+        alpha += sign * pow(beta, n) * pow(lambda, n - 1) / factorial;
+    }
+    return alpha;
+}
+
+/* gate 0: alpha_t = (1 - e^{-beta lambda}) / lambda, lambda = ||k||^2, with the lambda = 0 limit beta;
+ * gate p >= 1: oracle_alpha_rk. */
+static double oracle_alpha_one(const double *k, double beta, int d_k, int gate)
 {
     double lambda = 0.0;
     for (int i = 0; i < d_k; ++i)
         lambda += k[i] * k[i];
+    if (gate > 0)
+        return oracle_alpha_rk(beta, lambda, gate);
     if (lambda == 0.0 || beta * lambda == 0.0)
         return beta;
     return -expm1(-beta * lambda) / lambda;
@@ -58,9 +86,9 @@ static double oracle_alpha_one(const double *k, double beta, int d_k)
 /* One exact EFLA token update applied to S (d_k x d_v), followed by the readout o = S^T q.
  * kS is caller-provided scratch of d_v doubles. */
 static void oracle_token(double *S, const double *q, const double *k, const double *v, double beta,
-                         double *o, double *kS, int d_k, int d_v)
+                         double *o, double *kS, int d_k, int d_v, int gate)
 {
-    const double alpha = oracle_alpha_one(k, beta, d_k);
+    const double alpha = oracle_alpha_one(k, beta, d_k, gate);
     /* kS = k^T S_{t-1} (a row vector of length d_v) */
     for (int j = 0; j < d_v; ++j)
         kS[j] = 0.0;
@@ -94,17 +122,17 @@ static int oracle_threads(int requested)
 }
 
 /* alpha for n_tokens keys of length d_k. */
-void efla_oracle_alpha(const double *k, const double *beta, double *alpha, int64_t n_tokens, int d_k)
+void efla_oracle_alpha(const double *k, const double *beta, double *alpha, int64_t n_tokens, int d_k, int gate)
 {
     for (int64_t t = 0; t < n_tokens; ++t)
-        alpha[t] = oracle_alpha_one(k + t * d_k, beta[t], d_k);
+        alpha[t] = oracle_alpha_one(k + t * d_k, beta[t], d_k, gate);
 }
 
 /* Full-sequence recurrence for every (b, h).  initial_state may be NULL (zeros); final_state may
  * be NULL (not written); o may be NULL (not written).  Returns the number of threads used. */
 int efla_oracle_fwd(const double *q, const double *k, const double *v, const double *beta,
                     const double *initial_state, double *o, double *final_state,
-                    int B, int H, int L, int d_k, int d_v, int n_threads)
+                    int B, int H, int L, int d_k, int d_v, int gate, int n_threads)
 {
     const int64_t BH = (int64_t)B * H;
     const int nt = oracle_threads(n_threads);
@@ -131,7 +159,7 @@ int efla_oracle_fwd(const double *q, const double *k, const double *v, const dou
             for (int t = 0; t < L; ++t) {
                 const int64_t tok = bh * L + t;
                 oracle_token(S, q + tok * d_k, k + tok * d_k, v + tok * d_v, beta[tok],
-                             o ? o + tok * d_v : NULL, kS, d_k, d_v);
+                             o ? o + tok * d_v : NULL, kS, d_k, d_v, gate);
             }
             if (final_state)
                 memcpy(final_state + bh * ssz, S, sizeof(double) * ssz);
@@ -146,7 +174,7 @@ int efla_oracle_fwd(const double *q, const double *k, const double *v, const dou
 /* One decode step for NH independent (sequence, head) states, updated in place.
  * q, k [NH,d_k]; v [NH,d_v]; beta [NH]; state [NH,d_k,d_v]; o [NH,d_v]. Returns threads used. */
 int efla_oracle_step(const double *q, const double *k, const double *v, const double *beta,
-                     double *state, double *o, int64_t NH, int d_k, int d_v, int n_threads)
+                     double *state, double *o, int64_t NH, int d_k, int d_v, int gate, int n_threads)
 {
     const int nt = oracle_threads(n_threads);
     int used = 1;
@@ -164,7 +192,7 @@ int efla_oracle_step(const double *q, const double *k, const double *v, const do
 #endif
         for (int64_t n = 0; n < NH; ++n)
             oracle_token(state + n * (int64_t)d_k * d_v, q + n * d_k, k + n * d_k, v + n * d_v, beta[n],
-                         o ? o + n * d_v : NULL, kS, d_k, d_v);
+                         o ? o + n * d_v : NULL, kS, d_k, d_v, gate);
         free(kS);
     }
     (void)nt;
@@ -185,7 +213,7 @@ int efla_oracle_step(const double *q, const double *k, const double *v, const do
  * Output: tout[bh][c][i][j], a C x C row-major block per chunk; rows and columns n .. C-1 of a short
  * last chunk are zero.  Returns the number of threads used. */
 int efla_oracle_ut(const double *k, const double *beta, double *tout, int B, int H, int L, int d_k, int C,
-                   int n_threads)
+                   int gate, int n_threads)
 {
     const int64_t BH = (int64_t)B * H;
     const int64_t NC = (L + C - 1) / C;
@@ -213,7 +241,7 @@ int efla_oracle_ut(const double *k, const double *beta, double *tout, int B, int
             memset(T, 0, sizeof(double) * (size_t)C * C);
             memset(A, 0, sizeof(double) * (size_t)C * C);
             for (int i = 0; i < n; ++i)
-                alpha[i] = oracle_alpha_one(kc + (size_t)i * d_k, beta[bh * L + t0 + i], d_k);
+                alpha[i] = oracle_alpha_one(kc + (size_t)i * d_k, beta[bh * L + t0 + i], d_k, gate);
             for (int i = 0; i < n; ++i)
                 for (int j = 0; j < i; ++j) {
                     double dot = 0.0;

@@ -225,3 +225,31 @@ def test_state_pass_argument_errors(lib):
 def test_split_no_device_after_valid_arguments(lib):
     assert _split(lib) == NO_DEVICE
     assert lib.efla_ut_transform(P(1), P(2), BF16, P(3), 6 * 2 * 10 * 256 * 2, 2, 3, 100, 64, 64, None) == NO_DEVICE
+
+
+def _gated_calls(lib, gate):
+    """Every *_gate entry point, with arguments that are valid apart from (possibly) the gate."""
+    need = 6 * 2 * 10 * 256 * 2
+    return {
+        "alpha": lib.efla_alpha_gate(P(1), BF16, P(2), P(3), 5, 128, gate, None),
+        "recurrent_step": lib.efla_recurrent_step_gate(P(1), P(2), P(3), P(4), BF16, P(5), P(6), 8, 128, 128, gate,
+                                                       None),
+        "ut_transform": lib.efla_ut_transform_gate(P(1), P(2), BF16, P(3), need, 2, 3, 100, 64, 64, gate, None),
+        "chunk_fwd_split": lib.efla_chunk_fwd_split_gate(P(1), P(2), P(3), P(4), BF16, P(5), None, P(6), 2, 3, 100,
+                                                         64, 64, 64, 0, gate, P(7), need, None),
+        "chunk_fwd_slab": lib.efla_chunk_fwd_slab_gate(P(1), P(2), P(3), P(4), BF16, P(5), None, P(6), 2, 3, 100,
+                                                       64, 64, 64, 0, gate, None),
+    }
+
+
+def test_gate_argument_errors(lib):
+    for gate in (-1, efla.GATE_MAX_ORDER + 1, 1000):
+        for name, st in _gated_calls(lib, gate).items():
+            assert st == INVALID, (name, gate)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_every_gate_passes_argument_checks(lib):
+    for gate in (efla.GATE_EXACT, efla.GATE_DELTANET, 2, 4, efla.GATE_MAX_ORDER):
+        for name, st in _gated_calls(lib, gate).items():
+            assert st == NO_DEVICE, (name, gate)

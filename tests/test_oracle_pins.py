@@ -15,7 +15,11 @@ Sources of the pins:
   * the Euler / delta-rule limit for small beta*lambda (howistudyai.com Step 5, "Delta Rule");
   * the chunkwise WY/UT rewriting (Metodologia item 3; howistudyai.com Step 4), checked with an
     independent fp64 numpy model of the chunked form;
-  * state passing between chunks (howistudyai.com Step 4) and prefill followed by decode.
+  * state passing between chunks (howistudyai.com Step 4) and prefill followed by decode;
+  * the integrator family the exact flow closes ("Error-Free Linear Attention guida completa"
+    (mauroscia.it), section on RK-infinity; howistudyai.com building blocks "Delta Rule" and
+    "Runge-Kutta Methods"): a gate of order p must be one step of a textbook p-th order Runge-Kutta
+    method applied to the ODE itself, order 1 the delta rule, and high orders the exact flow.
 """
 import json
 import os
@@ -42,6 +46,14 @@ def _one_token(orc, k, v, beta, S0, q=None):
     o, S, _ = orc.fwd(q.reshape(1, 1, 1, d_k), np.asarray(k, float).reshape(1, 1, 1, d_k),
                       np.asarray(v, float).reshape(1, 1, 1, d_v), np.array([[[beta]]]),
                       np.asarray(S0, float).reshape(1, 1, d_k, d_v))
+    return o[0, 0, 0], S[0, 0]
+
+
+def _one_token_gate(orc, k, v, beta, S0, q, gate):
+    d_k, d_v = len(k), len(v)
+    o, S, _ = orc.fwd(np.asarray(q, float).reshape(1, 1, 1, d_k), np.asarray(k, float).reshape(1, 1, 1, d_k),
+                      np.asarray(v, float).reshape(1, 1, 1, d_v), np.array([[[beta]]]),
+                      np.asarray(S0, float).reshape(1, 1, d_k, d_v), gate=gate)
     return o[0, 0, 0], S[0, 0]
 
 
@@ -241,14 +253,15 @@ def check_linearity(orc):
     np.testing.assert_allclose(Sc, Sa + c * Sb, rtol=0, atol=1e-11)
 
 
-def _chunked_model(q, k, v, beta, S0, C):
+def _chunked_model(q, k, v, beta, S0, C, alpha=None):
     """Independent fp64 model of the chunkwise WY/UT form (one head):
     A = strict_tril(diag(alpha) K K^T), T = (I + A)^{-1}, W = T diag(alpha) K, U = T diag(alpha) V,
-    Delta = U - W S, O = Q S + tril(Q K^T) Delta, S <- S + K^T Delta."""
+    Delta = U - W S, O = Q S + tril(Q K^T) Delta, S <- S + K^T Delta.  alpha: the exact gate unless given."""
     L = k.shape[0]
-    lam = np.sum(k * k, axis=-1)
-    x = beta * lam
-    alpha = np.where(x == 0, beta, -np.expm1(-x) / np.where(lam == 0, 1.0, lam))
+    if alpha is None:
+        lam = np.sum(k * k, axis=-1)
+        x = beta * lam
+        alpha = np.where(x == 0, beta, -np.expm1(-x) / np.where(lam == 0, 1.0, lam))
     S = S0.copy()
     o = np.zeros((L, v.shape[1]))
     for t0 in range(0, L, C):
@@ -370,10 +383,98 @@ def check_ut_orthogonal_keys(orc):
     assert np.max(np.abs(T - np.diag(a))) <= 1e-13
 
 
+# explicit Runge-Kutta methods of order p (Butcher tableaux: stage coefficients a, weights b)
+RK_TABLEAUS = {
+    1: ([[]], [1.0]),                                                          # explicit Euler
+    2: ([[], [1.0]], [0.5, 0.5]),                                              # Heun
+    3: ([[], [0.5], [-1.0, 2.0]], [1 / 6, 2 / 3, 1 / 6]),                      # Kutta's third-order method
+    4: ([[], [0.5], [0.0, 0.5], [0.0, 0.0, 1.0]], [1 / 6, 1 / 3, 1 / 3, 1 / 6]),  # classical RK4
+}
+
+
+def _rk_step(S, k, v, beta, tableau):
+    """One step of size beta of an explicit Runge-Kutta method for dS/dt = -k (k^T S) + k v^T."""
+    a, b = tableau
+    f = lambda X: -np.outer(k, k @ X) + np.outer(k, v)
+    stages = []
+    for i in range(len(b)):
+        X = S.copy()
+        for j, aij in enumerate(a[i]):
+            X = X + beta * aij * stages[j]
+        stages.append(f(X))
+    out = S.copy()
+    for bi, Ki in zip(b, stages):
+        out = out + beta * bi * Ki
+    return out
+
+
+def check_gate_rk_tableaus(orc):
+    """Gate p <= 4 is one step of a textbook p-th order Runge-Kutta method of the ODE itself (the stages
+    integrate the full matrix dynamics; nothing here uses the rank-1 closed form)."""
+    rng = np.random.default_rng(41)
+    d_k, d_v = 5, 4
+    for p, tab in RK_TABLEAUS.items():
+        for _ in range(4):
+            k = rng.standard_normal(d_k) * rng.uniform(0.3, 1.5)
+            v, q = rng.standard_normal(d_v), rng.standard_normal(d_k)
+            S0 = rng.standard_normal((d_k, d_v))
+            beta = rng.uniform(0.05, 0.9)
+            o, S = _one_token_gate(orc, k, v, beta, S0, q, p)
+            S_ref = _rk_step(S0, k, v, beta, tab)
+            scale = max(1.0, np.max(np.abs(S_ref)))
+            assert np.max(np.abs(S - S_ref)) <= 1e-12 * scale, p
+            assert np.max(np.abs(o - S_ref.T @ q)) <= 1e-12 * scale * max(1.0, np.abs(q).sum()), p
+            o1, S1, _ = orc.step(q[None], k[None], v[None], np.array([beta]), S0[None], gate=p)
+            assert np.max(np.abs(S1[0] - S_ref)) <= 1e-12 * scale, p
+
+
+def check_gate_limits(orc):
+    """Order 1 is the delta rule's alpha = beta for every key (zero keys included); high orders reach
+    the exact flow where the series converges fast."""
+    rng = np.random.default_rng(42)
+    k = rng.standard_normal((64, 7)) * np.exp(rng.uniform(-3, 1.5, (64, 1)))
+    k[5] = 0.0
+    beta = rng.uniform(0.0, 1.0, 64)
+    np.testing.assert_array_equal(orc.alpha(k, beta, gate=1), beta)
+    small = np.sum(k * k, axis=-1) * beta <= 1.0
+    a16 = orc.alpha(k[small], beta[small], gate=16)
+    a = orc.alpha(k[small], beta[small])
+    assert np.max(np.abs(a16 - a) / np.maximum(a, 1e-300)) <= 1e-13
+
+
+def check_gate_chunk_identity(orc):
+    """With a Runge-Kutta gate the recurrence, the decode step, the chunked form and the UT transform all use
+    the same coefficient: the chunk algebra reproduces the gated recurrence for any chunk size, and the UT
+    output satisfies the chunk identity of the gated recurrence."""
+    rng = np.random.default_rng(43)
+    L, d_k, d_v, gate, C = 40, 6, 5, 3, 8
+    k = _mixed_keys(rng, L, d_k, 0.05, 1.5)
+    q = rng.standard_normal((L, d_k))
+    v = rng.standard_normal((L, d_v))
+    beta = rng.uniform(0.05, 0.8, L)
+    S0 = 0.2 * rng.standard_normal((d_k, d_v))
+    o, Sf, _ = orc.fwd(q[None, None], k[None, None], v[None, None], beta[None, None], S0[None, None], gate=gate)
+    ap = orc.alpha(k, beta, gate=gate)
+    for c in [1, 4, 16, L]:
+        oc, Sc = _chunked_model(q, k, v, beta, S0, c, alpha=ap)
+        np.testing.assert_allclose(o[0, 0], oc, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(Sf[0, 0], Sc, rtol=0, atol=1e-11)
+    T = orc.ut(k[None, None], beta[None, None], C, gate=gate)[0, 0]
+    S = S0.copy()
+    for c in range(L // C):
+        sl = slice(c * C, (c + 1) * C)
+        D = T[c] @ (v[sl] - k[sl] @ S)
+        oc = q[sl] @ S + np.tril(q[sl] @ k[sl].T) @ D
+        S = S + k[sl].T @ D
+        np.testing.assert_allclose(oc, o[0, 0, sl], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(S, Sf[0, 0], rtol=0, atol=1e-11)
+
+
 PINS = [check_worked_example, check_expm_erase, check_van_loan, check_rk4_sequence, check_alpha_extremes,
         check_euler_limit, check_directional_decay, check_stiff_overwrite, check_contractive,
         check_linearity, check_chunk_identity, check_state_chaining, check_zero_initial_state,
-        check_ut_chunk_identity, check_ut_orthogonal_keys]
+        check_ut_chunk_identity, check_ut_orthogonal_keys, check_gate_rk_tableaus, check_gate_limits,
+        check_gate_chunk_identity]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -442,6 +543,12 @@ MUTANTS = {
                           "dot += kc[(size_t)i * d_k + e] * kc[(size_t)i * d_k + e];"),
     "ut_substitution_range": ("for (int m = 0; m < i; ++m)\n                        x -=",
                               "for (int m = 0; m + 1 < i; ++m)\n                        x -="),
+    "rk_sign": ("(n % 2 == 1) ? 1.0 : -1.0", "(n % 2 == 0) ? 1.0 : -1.0"),
+    "rk_order_short": ("for (int n = 1; n <= p; ++n)", "for (int n = 1; n < p; ++n)"),
+    "rk_order_long": ("for (int n = 1; n <= p; ++n)", "for (int n = 1; n <= p + 1; ++n)"),
+    "rk_factorial": ("factorial *= n;", "factorial *= (n > 1 ? n - 1 : 1);"),
+    "rk_lambda_power": ("pow(lambda, n - 1)", "pow(lambda, n)"),
+    "gate_ignored": ("    if (gate > 0)\n        return oracle_alpha_rk(beta, lambda, gate);\n", ""),
 }
 
 
