@@ -234,6 +234,46 @@ def run_forward(efla, W, torch, steps, warmup):
                        launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds, ut_waves=w.B * w.H * nc))
 
 
+def run_long_context(efla, W, torch, steps=8, warmup=2):
+    """The long-context forward (16 heads x 65,536 tokens): the split forward, whose state pass runs 1,024
+    chunks back to back per (head, slab), against the segment-parallel one."""
+    w = W.workload(4)
+    x = W.make_fwd_inputs(w)
+
+    def dev(a):
+        return torch.from_numpy(W.bf16_bits(a)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    beta = torch.from_numpy(x["beta"]).cuda()
+    del x
+    o = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    nseg, seg_chunks, _, need = efla.scan_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
+    ws = torch.empty((max(need, efla.chunk_workspace_size(w.B, w.H, w.L, w.chunk, torch.bfloat16)),),
+                     dtype=torch.uint8, device="cuda")
+    res = {}
+    for method in ("split", "scan"):
+        def fn():
+            efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, method=method)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        time.sleep(0.5)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[method] = a.elapsed_time(b) / steps
+    assert torch.isfinite(S).all().item(), "non-finite long-context state"
+    return {"workload": "long_context B1 H16 L65536 d128 bf16 chunk 64", "steps": steps,
+            "split_ms_per_step": round(res["split"], 4), "scan_ms_per_step": round(res["scan"], 4),
+            "segments": nseg, "chunks_per_segment": seg_chunks,
+            "tokens_per_s_scan": round(w.B * w.L / (res["scan"] * 1e-3), 1),
+            "scan_speedup": round(res["split"] / res["scan"], 3)}
+
+
 def run_decode(efla, W, torch, warmup=3):
     w = W.workload(5)
     S = torch.from_numpy(W.make_decode_state(w)).cuda()
@@ -281,6 +321,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context forward")
     ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
                     help="run one leg only (for profiling); prints a short JSON line")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
@@ -377,6 +418,8 @@ def main():
                          "traffic": measured_traffic("recurrent_step_kernel<bf16,128,128>"),
                          "kernel": "recurrent_step_kernel<bf16,128,128>", "bytes_per_launch": dbytes},
         }
+    if not args.no_long:
+        result["long_context"] = run_long_context(efla, W, torch)
     if not args.no_cpu:
         threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
         result["cpu_baseline"] = cpu_baseline(W, threads)

@@ -11,7 +11,8 @@ library is missing, every call raises.
     t    = ut_transform(k, beta, chunk_size=64)          # T diag(alpha) per chunk (operand layout)
 
 chunk_fwd runs the two-launch form by default (UT transform of all chunks into a workspace, then the
-state pass); method="fused" runs the single-kernel form, which needs no workspace.
+state pass); method="fused" runs the single-kernel form, which needs no workspace; method="scan" cuts long
+sequences into segments processed at the same time (for few heads), see efla_chunk_fwd_scan.
 
 Every call that forms alpha takes ``gate``: GATE_EXACT (0, the default) for the exact coefficient, or
 p in 1 .. GATE_MAX_ORDER for the coefficient of a p-th order Runge-Kutta step of the same dynamics
@@ -32,7 +33,7 @@ import os
 import torch
 
 __all__ = ["EflaError", "alpha", "chunk_fwd", "recurrent_step", "chunk_plan", "chunk_workspace_size", "ut_transform",
-           "state_pass", "library_path", "load_library"]
+           "state_pass", "scan_plan", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libefla.so")
@@ -90,6 +91,10 @@ def load_library():
     lib.efla_ut_transform_gate.argtypes = [_vp, _vp, _i32, _vp, _sz, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.efla_chunk_fwd_split_gate.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+    lib.efla_chunk_fwd_scan.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _vp, _sz, _vp]
+    lib.efla_chunk_scan_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32),
+                                         ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
     lib.efla_chunk_state_pass.argtypes = [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
@@ -195,14 +200,15 @@ def ut_transform(k, beta, chunk_size=64, out=None, gate=GATE_EXACT):
 
 
 def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_size=64, dv_slab=0,
-              out=None, final_state=None, method="split", workspace=None, gate=GATE_EXACT):
+              out=None, final_state=None, method="split", workspace=None, gate=GATE_EXACT, segments=0):
     """Chunkwise-parallel EFLA forward over [B,H,L,*] inputs.
 
     Returns (o [B,H,L,d_v] in the input dtype, final state [B,H,d_k,d_v] fp32 or None).
     ``final_state`` may be passed (and may be ``initial_state`` itself) to receive the state in place.
     ``method`` is "split" (UT transform launch + state-pass launch, through ``workspace``: a device
-    tensor of at least chunk_workspace_size(...) bytes, allocated here when not given) or "fused" (one
-    kernel, no workspace).
+    tensor of at least chunk_workspace_size(...) bytes, allocated here when not given), "fused" (one
+    kernel, no workspace) or "scan" (segment-parallel: ``segments`` segments per sequence, 0 = the library's
+    choice; workspace of scan_plan(...)[3] bytes).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
@@ -243,9 +249,28 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
                                              int(chunk_size), int(dv_slab), int(gate), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(v.device)),
                "efla_chunk_fwd_split")
+    elif method == "scan":
+        need = scan_plan(B, H, L, d_k, d_v, int(chunk_size), v.dtype, int(segments))[3]
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+        _dev_tensor(workspace, "workspace")
+        _check(lib.efla_chunk_fwd_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                       _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
+                                       int(segments), int(gate), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(v.device)),
+               "efla_chunk_fwd_scan")
     else:
-        raise ValueError("method must be 'split' or 'fused'")
+        raise ValueError("method must be 'split', 'fused' or 'scan'")
     return out, final_state
+
+
+def scan_plan(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, segments=0):
+    """(segments, chunks per segment, slab width, workspace bytes) of chunk_fwd(method="scan"); host only."""
+    lib = load_library()
+    ns, sc, sw, nb = _i32(), _i32(), _i32(), _sz()
+    _check(lib.efla_chunk_scan_plan(B, H, L, d_k, d_v, chunk, _dtype_of(dtype), segments, ctypes.byref(ns),
+                                    ctypes.byref(sc), ctypes.byref(sw), ctypes.byref(nb)), "efla_chunk_scan_plan")
+    return ns.value, sc.value, sw.value, nb.value
 
 
 def state_pass(q, k, v, t, initial_state=None, output_final_state=True, chunk_size=64, dv_slab=0, out=None,

@@ -119,6 +119,49 @@ size_t ut_bytes(int64_t BH, int L, int chunk, efla_dtype dt) {
     return (size_t)BH * (size_t)((L + chunk - 1) / chunk) * (size_t)efla::ut_block_elems(chunk) * esize(dt);
 }
 
+size_t round_up_256(size_t n) { return (n + 255) / 256 * 256; }
+
+// The segment-parallel forward's launch shape and workspace: a slab width dividing d_v and d_k, the number of
+// segments (0 asked = automatic: as many as keep the second pass within one workgroup per compute unit, with at
+// least 16 chunks per segment) and the chunks per segment; workspace = UT output, then the per-segment states
+// [S_g(0) | M_g] (fp32, d_k x (d_v + d_k)), then the segments' initial states (fp32, d_k x d_v).
+struct ScanPlan {
+    int dvs, nseg, seg_chunks;
+    size_t off_states, off_sin, total;
+};
+
+efla_status scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, int segments, ScanPlan* p) {
+    if (!valid_dtype(dt) || B < 0 || H < 0 || L < 0 || segments < 0) return EFLA_ERR_INVALID_ARG;
+    if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    const int64_t NC = (L + chunk - 1) / chunk;
+    if (BH > INT32_MAX || BH * NC > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    int dvs = 64;
+    while (dvs > 16 && (dvs > d_v || dvs > d_k || split_lds_bytes(dt, d_k, chunk, dvs) < 0)) dvs /= 2;
+    if (split_lds_bytes(dt, d_k, chunk, dvs) < 0) return EFLA_ERR_UNSUPPORTED;
+    if (efla::chunk_grid((int)BH, d_v + d_k, dvs) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    int64_t G = segments;
+    if (G == 0) {
+        const int64_t per_seg = BH * (d_v / dvs);   // second-pass workgroups of one segment
+        G = 1;
+        while (per_seg * 2 * G <= 256 && NC >= 32 * G) G *= 2;
+    }
+    if (G > NC) G = NC > 0 ? NC : 1;
+    if (G > 65535) return EFLA_ERR_INVALID_ARG;
+    const int64_t sc = NC > 0 ? (NC + G - 1) / G : 1;
+    G = NC > 0 ? (NC + sc - 1) / sc : 1;   // no empty segment
+    p->dvs = dvs;
+    p->nseg = (int)G;
+    p->seg_chunks = (int)sc;
+    const size_t ut = round_up_256(ut_bytes(BH, L, chunk, dt));
+    const size_t states = G > 1 ? round_up_256((size_t)BH * G * d_k * (d_v + d_k) * 4) : 0;
+    const size_t sin = G > 1 ? round_up_256((size_t)BH * G * d_k * d_v * 4) : 0;
+    p->off_states = ut;
+    p->off_sin = ut + states;
+    p->total = ut + states + sin;
+    return EFLA_OK;
+}
+
 }  // namespace
 
 namespace efla {
@@ -309,6 +352,80 @@ efla_status efla_chunk_state_pass(const void* q, const void* k, const void* v, c
                                   int H, int L, int d_k, int d_v, int chunk, int dv_slab, void* stream) {
     return split_entry(false, q, k, v, nullptr, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, dv_slab,
                        EFLA_GATE_EXACT, const_cast<void*>(t_in), t_in_bytes, stream);
+}
+
+efla_status efla_chunk_scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int segments,
+                                 int* nseg, int* seg_chunks, int* slab_width, size_t* workspace_bytes) {
+    ScanPlan p;
+    const efla_status st = scan_plan(B, H, L, d_k, d_v, chunk, dtype, segments, &p);
+    if (st != EFLA_OK) return st;
+    if (nseg) *nseg = p.nseg;
+    if (seg_chunks) *seg_chunks = p.seg_chunks;
+    if (slab_width) *slab_width = p.dvs;
+    if (workspace_bytes) *workspace_bytes = p.total;
+    return EFLA_OK;
+}
+
+efla_status efla_chunk_fwd_scan(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
+                                int d_v, int chunk, int segments, int gate, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
+    ScanPlan p;
+    efla_status st = scan_plan(B, H, L, d_k, d_v, chunk, dtype, segments, &p);
+    if (st != EFLA_OK) return st;
+    const int64_t BH = (int64_t)B * H;
+    st = check_fwd_buffers(q, k, v, beta, dtype, o, initial_state, final_state, BH, L, d_k, d_v);
+    if (st != EFLA_OK) return st;
+    if (p.total > 0 && BH > 0 && L > 0) {
+        if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total) return EFLA_ERR_WORKSPACE;
+        const size_t es = esize(dtype);
+        const size_t nq = (size_t)BH * L * d_k * es, nv = (size_t)BH * L * d_v * es, nb = (size_t)BH * L * 4;
+        const size_t ns = (size_t)BH * d_k * d_v * 4;
+        const size_t need = p.total;
+        if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nq) || overlap(workspace, need, v, nv) ||
+            overlap(workspace, need, beta, nb) || overlap(workspace, need, o, nv) ||
+            overlap(workspace, need, initial_state, ns) || overlap(workspace, need, final_state, ns))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if (BH == 0) return EFLA_OK;
+    if (L == 0 && !final_state) return EFLA_OK;
+    st = device_present();
+    if (st != EFLA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = static_cast<char*>(workspace);
+    const bool bf = dtype == EFLA_BF16;
+    auto chain = [&](const efla::SplitArgs& a, bool with_ut) {
+        return bf ? efla::launch_split_fwd_bf16(a, with_ut, s) : efla::launch_split_fwd_f32(a, with_ut, s);
+    };
+    efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, ws, (int)BH, L, d_k, d_v, chunk, p.dvs, gate};
+    if (p.nseg == 1) {
+        const hipError_t e = chain(a, true);
+        return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_scan launch");
+    }
+    float* states = reinterpret_cast<float*>(ws + p.off_states);
+    float* s_in = reinterpret_cast<float*>(ws + p.off_sin);
+    // UT transform of every chunk; pass 1: every segment from a zero state, with the transition columns
+    hipError_t e = bf ? efla::launch_ut_bf16(k, beta, ws, (int)BH, L, d_k, chunk, gate, s)
+                      : efla::launch_ut_f32(k, beta, ws, (int)BH, L, d_k, chunk, gate, s);
+    efla::SplitArgs a1 = a;
+    a1.o = nullptr;
+    a1.s0 = nullptr;
+    a1.sf = states;
+    a1.nseg = p.nseg;
+    a1.seg_chunks = p.seg_chunks;
+    a1.aug = 1;
+    a1.sf_all = 1;
+    if (e == hipSuccess) e = chain(a1, false);
+    // the segments' initial states
+    if (e == hipSuccess) e = efla::launch_seg_scan(states, initial_state, s_in, (int)BH, p.nseg, d_k, d_v, s);
+    // pass 2: every segment from its initial state, writing the outputs and the last segment's final state
+    efla::SplitArgs a2 = a;
+    a2.s0 = s_in;
+    a2.nseg = p.nseg;
+    a2.seg_chunks = p.seg_chunks;
+    if (e == hipSuccess) e = chain(a2, false);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_scan launch");
 }
 
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype, void* o,

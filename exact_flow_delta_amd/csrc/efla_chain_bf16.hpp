@@ -78,10 +78,12 @@ __device__ __forceinline__ int sw_v(int t) {
     else return 0;
 }
 
-template <int DK, int C, int DVS>
+// OUT = false: no outputs (the first pass of the segment-parallel forward needs only the final states), so no
+// Q tile, no Q S, no Q K^T and no O -- 38 matrix instructions per chunk and wave instead of 100.
+template <int DK, int C, int DVS, bool OUT>
 __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
-    bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab) {
+    bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg) {
     typedef ChainBf16Shape<DK, C, DVS> SH;
     typedef Mma<bf16> M;
     typedef M::quad quad;
@@ -114,11 +116,15 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     const int slab = (bid >> 3) % nslab;
     const int bh = ((bid >> 3) / nslab) * 8 + (bid & 7);
     if (bh >= BH) return;
-    const int slab_col = slab * DVS;
+    const int slab_col = slab * DVS;               // column of the state (value columns first, then transition)
+    const bool trans = slab >= sg.nslab_v;         // transition slab: zero values, identity start, no outputs
     const bool producer = w == NW;                 // the extra wave: it only fetches
     const int colw = slab_col + 16 * (producer ? 0 : w);
     const int64_t tok0 = (int64_t)bh * L;
     const int NC = (L + C - 1) / C;
+    const int seg = blockIdx.y, nseg = gridDim.y;
+    const int c0 = seg * sg.seg_chunks;            // this workgroup's chunks [c0, c1)
+    const int c1 = NC < c0 + sg.seg_chunks ? NC : c0 + sg.seg_chunks;
     const bf16* twh = tw + (int64_t)bh * NC * (NQ * QE);
 
     // ---- per-lane LDS byte offsets, fixed for the whole sequence ---------------------------------
@@ -135,13 +141,15 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
 
     // ---- loads (producer wave only): wave load j of a tile covers its bytes [1024 j, 1024 j + 1024); lane L
     //      writes 16 bytes at 1024 j + 16 L, i.e. physical chunk p of row t, holding logical chunk p ^ sw(t)
-    constexpr int NLOAD = 2 * SH::NLQ + SH::NLV + SH::NLT;   // loads per chunk
+    constexpr int NLOAD = 2 * SH::NLQ + SH::NLV + SH::NLT;   // loads of a chunk's tiles
+    constexpr int NISSUE = NLOAD - (OUT ? 0 : SH::NLQ);       // the ones issued (no Q tile without outputs)
     auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
         const int t = c * C;
         const int n = (L - t < C) ? (L - t) : C;   // <= 0 past the end: an empty range, zeros
         const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (tok0 + t) * DK, n > 0 ? n * DK * 2 : 0);
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, n > 0 ? n * DK * 2 : 0);
-        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + (tok0 + t) * DV + slab_col, n > 0 ? ((n - 1) * DV + DVS) * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rv =
+            buffer_rsrc(v + (tok0 + t) * DV + slab_col, n > 0 && !trans ? ((n - 1) * DV + DVS) * 2 : 0);
         const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(twh + (int64_t)c * (NQ * QE), SH::TBYTES);
         static_for<NLOAD>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
@@ -152,7 +160,9 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
             constexpr int OFF = tile == 0 ? SH::OFF_Q : tile == 1 ? SH::OFF_K : tile == 2 ? SH::OFF_V : SH::OFF_T;
             lds_void* dst = (lds_void*)(buf + OFF + 1024 * j);
             const int p = 1024 * j + 16 * lane;
-            if constexpr (tile == 3) {
+            if constexpr (tile == 0 && !OUT) {
+                return;
+            } else if constexpr (tile == 3) {
                 // Ta blocks: contiguous in the workspace, copied as they are
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
             } else {
@@ -173,17 +183,17 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
         __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
     };
     typedef std::integral_constant<int, 0> I0;
-    typedef std::integral_constant<int, NLOAD> ILOAD;
+    typedef std::integral_constant<int, NISSUE> ILOAD;
     typedef std::integral_constant<int, NB> INB;
 
     if (producer) {
         // Chunk c's tiles go out at the step of chunk c - PD (the prologue fetches the first PD).  At the end
         // of the step of chunk c those of chunk c + 1 must have landed; with PD = 2 the ones issued during
         // the step (chunk c + 2) may still be in flight.  One barrier per step, as the compute waves.
-        if (NC > 0) {
-            issue_chunk(0, buf0);
-            if (PD == 2 && NC > 1) {
-                issue_chunk(1, buf1);
+        if (c1 > c0) {
+            issue_chunk(c0, buf0);
+            if (PD == 2 && c0 + 1 < c1) {
+                issue_chunk(c0 + 1, buf1);
                 wait_vm(ILOAD{});
             } else {
                 wait_vm(I0{});
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
             __builtin_amdgcn_s_barrier();
         }
         auto pstep = [&](int c, lds_u8* nxt) __attribute__((always_inline)) {
-            if (c + PD < NC) {
+            if (c + PD < c1) {
                 issue_chunk(c + PD, nxt);
                 if constexpr (PD == 2) wait_vm(ILOAD{}); else wait_vm(I0{});
             } else {
@@ -200,15 +210,15 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
             __builtin_amdgcn_s_barrier();
         };
         if constexpr (PD == 2) {
-            for (int c = 0; c < NC; c += 3) {
+            for (int c = c0; c < c1; c += 3) {
                 pstep(c, buf2);
-                if (c + 1 < NC) pstep(c + 1, buf0);
-                if (c + 2 < NC) pstep(c + 2, buf1);
+                if (c + 1 < c1) pstep(c + 1, buf0);
+                if (c + 2 < c1) pstep(c + 2, buf1);
             }
         } else {
-            for (int c = 0; c < NC; c += 2) {
+            for (int c = c0; c < c1; c += 2) {
                 pstep(c, buf1);
-                if (c + 1 < NC) pstep(c + 1, buf0);
+                if (c + 1 < c1) pstep(c + 1, buf0);
             }
         }
         return;
@@ -220,8 +230,13 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
 #pragma unroll
     for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[((int64_t)bh * DK + srow(rt, i)) * DV + colw + r] : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            const int row = srow(rt, i);
+            S[rt][i] = trans ? (row == colw - DV + r ? 1.0f : 0.0f)
+                             : s0 ? s0[(((int64_t)bh * nseg + seg) * DK + row) * DV + colw + r] : 0.0f;
+        }
     }
+    const bool write_o = o != nullptr && !trans;
 
     f32x4 Ot[NB];
 #pragma unroll
@@ -256,18 +271,18 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
         quad Pq[NB * (NB + 1) / 2];
         static_for<NB>([&](auto rbc) {
             constexpr int rb = decltype(rbc)::value;
-            store_pending(rb);
+            if constexpr (OUT) store_pending(rb);
             bx8 qq[NKP];
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) {
-                qq[kp] = frag(cQ, rb, kp);
+                if constexpr (OUT) qq[kp] = frag(cQ, rb, kp);
                 kq[rb][kp] = frag(cK, rb, kp);
             }
             f32x4 xk = {0.f, 0.f, 0.f, 0.f};
             Ot[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) {
-                Ot[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Sq[kp], qq[kp], Ot[rb], 0, 0, 0);   // (Q S)^T
+                if constexpr (OUT) Ot[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Sq[kp], qq[kp], Ot[rb], 0, 0, 0);   // (Q S)^T
                 xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[rb][kp], Sq[kp], xk, 0, 0, 0);       // K S
             }
             // R = V - K S: lane (r, g), element e: row 16 rb + 4g + e, column 16 w + r of the slab
@@ -277,6 +292,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) rr[e] = (float)vq[e] - xk[e];
             Rq[rb] = M::cvt(rr);
+            if constexpr (!OUT) return;
             // block row rb of lower_incl(Q K^T): acc lane (r, g), element e = (Q K^T)[16 rb + r][16 lo + 4g + e];
             // the blocks' accumulation chains are interleaved (reduction step outer) so that consecutive
             // matrix instructions are independent
@@ -313,6 +329,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
         });
         // O^T += Delta^T lower_incl(Q K^T)^T (stored with the next chunk)
         static_for<NB>([&](auto rbc) {
+            if constexpr (!OUT) return;
             constexpr int rb = decltype(rbc)::value;
             constexpr int p0 = rb * (rb + 1) / 2;
             static_for<(rb + 1) / 2>([&](auto hc) {
@@ -322,7 +339,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
             if constexpr ((rb + 1) & 1) M::mma1(Ot[rb], Dq[rb], Pq[p0 + rb]);
         });
         pend_t0 = c * C;
-        pend_n = (L - pend_t0 < C) ? (L - pend_t0) : C;
+        pend_n = !write_o ? 0 : (L - pend_t0 < C) ? (L - pend_t0) : C;
         // S += K^T Delta: tile rt = 2 kp + h takes, as A operand, the transposed K block whose lane (g, e, c)
         // points at row 16 kb + 4 g + e, logical chunk 4 kp + c, byte 8 h; the tiles' chains are interleaved
         auto kt = [&](int rt, int kb) __attribute__((always_inline)) {
@@ -349,38 +366,51 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
         __builtin_amdgcn_s_barrier();
     };
 
-    if (NC > 0) __builtin_amdgcn_s_barrier();   // the producer's prologue
+    if (c1 > c0) __builtin_amdgcn_s_barrier();   // the producer's prologue
     if constexpr (PD == 2) {
-        for (int c = 0; c < NC; c += 3) {
+        for (int c = c0; c < c1; c += 3) {
             step(c, buf0);
-            if (c + 1 < NC) step(c + 1, buf1);
-            if (c + 2 < NC) step(c + 2, buf2);
+            if (c + 1 < c1) step(c + 1, buf1);
+            if (c + 2 < c1) step(c + 2, buf2);
         }
     } else {
-        for (int c = 0; c < NC; c += 2) {
+        for (int c = c0; c < c1; c += 2) {
             step(c, buf0);
-            if (c + 1 < NC) step(c + 1, buf1);
+            if (c + 1 < c1) step(c + 1, buf1);
         }
     }
+    if constexpr (OUT) {
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) store_pending(rb);
+        for (int rb = 0; rb < NB; ++rb) store_pending(rb);
+    }
 
-    if (sf) {
+    if (sf && (sg.sf_all || seg == nseg - 1)) {
+        const int64_t base = sg.sf_all ? (int64_t)bh * nseg + seg : bh;
+        const int ld = sg.sf_all ? sg.ld_sf : DV;
 #pragma unroll
         for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sf[((int64_t)bh * DK + srow(rt, i)) * DV + colw + r] = S[rt][i];
+            for (int i = 0; i < 4; ++i) sf[(base * DK + srow(rt, i)) * ld + colw + r] = S[rt][i];
         }
     }
 }
 
 template <int DK, int C, int DVS>
 hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
-    const int nslab = a.d_v / DVS;
+    const ChainSeg sg = chain_seg(a, DK, C, DVS);
+    const int nslab = (a.d_v + (a.aug ? DK : 0)) / DVS;
     const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
-    hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS>), dim3((unsigned)grid), dim3(DVS / 16 * 64 + 64), 0, stream,
-                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
-                       static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab);
+    const dim3 g3((unsigned)grid, (unsigned)(a.nseg > 0 ? a.nseg : 1));
+    if (a.o == nullptr)
+        hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, false>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
+                           static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                           static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
+                           sg);
+    else
+        hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, true>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
+                           static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                           static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
+                           sg);
     return hipGetLastError();
 }
 

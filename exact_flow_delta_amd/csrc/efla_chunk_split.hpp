@@ -302,7 +302,7 @@ constexpr int chain_layout_bytes(int dk, int c, int dvs) {
 template <typename E, int DK, int C, int DVS>
 __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ tw,
-    E* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab) {
+    E* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg) {
     typedef ChainLayout<sizeof(E), DK, C, DVS> LY;
     typedef Mma<E> M;
     typedef typename M::quad quad;
@@ -332,10 +332,15 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
     const int slab = (bid >> 3) % nslab;
     const int bh = ((bid >> 3) / nslab) * 8 + (bid & 7);
     if (bh >= BH) return;
-    const int slab_col = slab * DVS;
+    const int slab_col = slab * DVS;              // column of the state (value columns first, then transition)
+    const bool trans = slab >= sg.nslab_v;        // transition slab: zero values, identity start, no outputs
     const int colw = slab_col + 16 * w;
     const int64_t tok0 = (int64_t)bh * L;
     const int NC = (L + C - 1) / C;
+    const int seg = blockIdx.y, nseg = gridDim.y;
+    const int c0 = seg * sg.seg_chunks;           // this workgroup's chunks [c0, c1)
+    const int c1 = NC < c0 + sg.seg_chunks ? NC : c0 + sg.seg_chunks;
+    const bool write_o = o != nullptr && !trans;
     const E* twh = tw + (int64_t)bh * NC * (NQ * QE) + lane * 4;
 
     auto sQ = [&](int b) { return reinterpret_cast<E*>(smem + b * LY::BUF + LY::OFF_Q); };
@@ -349,7 +354,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
         const int n = (L - t < C) ? (L - t) : C;
         rq.load(q + (tok0 + t) * DK, DK, n, tid);
         rk.load(k + (tok0 + t) * DK, DK, n, tid);
-        rv.load(v + (tok0 + t) * DV + slab_col, DV, n, tid);
+        rv.load(v + (tok0 + t) * DV + slab_col, DV, trans ? 0 : n, tid);
     };
     auto store_stage = [&](int b) {
         rq.store(sQ(b), LD_DK, tid);
@@ -366,34 +371,37 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
 #pragma unroll
     for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[rt][i] = s0 ? s0[((int64_t)bh * DK + 16 * rt + 4 * g + i) * DV + colw + r] : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g + i;
+            S[rt][i] = trans ? (row == colw - DV + r ? 1.0f : 0.0f)
+                             : s0 ? s0[(((int64_t)bh * nseg + seg) * DK + row) * DV + colw + r] : 0.0f;
+        }
     }
 
     quad ta[NQ];
-    if (NC > 0) {
-        load_ta(ta, 0);
-        load_stage(0);
+    if (c1 > c0) {
+        load_ta(ta, c0);
+        load_stage(c0);
         if constexpr (DB) {
             store_stage(0);
-            load_stage(1);
+            load_stage(c0 + 1);
             __syncthreads();
         }
     }
 
-    for (int c = 0; c < NC; ++c) {
+    for (int c = c0; c < c1; ++c) {
         const int t0 = c * C;
         const int n = (L - t0 < C) ? (L - t0) : C;
-        const int b = DB ? (c & 1) : 0;
+        const int b = DB ? ((c - c0) & 1) : 0;
         if constexpr (DB) {
             // Straight-line on purpose (no branch for the last chunks): past the end of the sequence the
             // buffer ranges are empty, so chunk c+1's stage and chunk c+2's loads are zeros that nobody reads.
             store_stage(b ^ 1);
             load_stage(c + 2);
         } else {
-            if (c > 0) __syncthreads();   // the previous chunk is done with the buffer
+            if (c > c0) __syncthreads();   // the previous chunk is done with the buffer
             store_stage(0);
-            if (c + 1 < NC) load_stage(c + 1);
+            if (c + 1 < c1) load_stage(c + 1);
             __syncthreads();
         }
         const E* cQ = sQ(b);
@@ -467,10 +475,11 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
         });
         // the next chunk's T diag(alpha) operands go into the registers just consumed: a whole iteration
         // covers their latency (the last chunk reloads its own, unused)
-        load_ta(ta, c + 1 < NC ? c + 1 : c);
+        load_ta(ta, c + 1 < c1 ? c + 1 : c);
         // O^T = (Q S)^T + Delta^T lower_incl(Q K^T)^T; four consecutive outputs of one token per lane, stored
         // through a buffer resource that ends at the chunk's last valid row
-        const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(o + (tok0 + t0) * DV + colw, ((n - 1) * DV + 16) * (int)sizeof(E));
+        const __amdgpu_buffer_rsrc_t ors =
+            buffer_rsrc(o + (tok0 + t0) * DV + colw, write_o ? ((n - 1) * DV + 16) * (int)sizeof(E) : 0);
         static_for<NB>([&](auto rbc) {
             constexpr int rb = decltype(rbc)::value;
             constexpr int p0 = rb * (rb + 1) / 2;
@@ -494,11 +503,13 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
         if constexpr (DB) __syncthreads();   // buffer b is free and chunk c+1's stage is in LDS
     }
 
-    if (sf) {
+    if (sf && (sg.sf_all || seg == nseg - 1)) {
+        const int64_t base = sg.sf_all ? (int64_t)bh * nseg + seg : bh;
+        const int ld = sg.sf_all ? sg.ld_sf : DV;
 #pragma unroll
         for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sf[((int64_t)bh * DK + 16 * rt + 4 * g + i) * DV + colw + r] = S[rt][i];
+            for (int i = 0; i < 4; ++i) sf[(base * DK + 16 * rt + 4 * g + i) * ld + colw + r] = S[rt][i];
         }
     }
 }
@@ -550,11 +561,13 @@ hipError_t launch_chain_t(const SplitArgs& a, hipStream_t stream) {
     } else if constexpr (ChainLayout<sizeof(E), DK, C, DVS>::BYTES > kMaxLdsBytes) {
         return hipErrorInvalidConfiguration;
     } else {
-        const int nslab = a.d_v / DVS;
+        const ChainSeg sg = chain_seg(a, DK, C, DVS);
+        const int nslab = (a.d_v + (a.aug ? DK : 0)) / DVS;
         const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
-        hipLaunchKernelGGL((chain_kernel<E, DK, C, DVS>), dim3((unsigned)grid), dim3(DVS / 16 * 64), 0, stream,
-                           static_cast<const E*>(a.q), static_cast<const E*>(a.k), static_cast<const E*>(a.v),
-                           static_cast<const E*>(a.tw), static_cast<E*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab);
+        hipLaunchKernelGGL((chain_kernel<E, DK, C, DVS>), dim3((unsigned)grid, (unsigned)(a.nseg > 0 ? a.nseg : 1)),
+                           dim3(DVS / 16 * 64), 0, stream, static_cast<const E*>(a.q), static_cast<const E*>(a.k),
+                           static_cast<const E*>(a.v), static_cast<const E*>(a.tw), static_cast<E*>(a.o), a.s0, a.sf,
+                           a.BH, a.L, a.d_v, nslab, sg);
         return hipGetLastError();
     }
 }

@@ -217,6 +217,33 @@ efla_status efla_chunk_state_pass(const void* q, const void* k, const void* v, c
                                   efla_dtype dtype, void* o, const float* initial_state, float* final_state,
                                   int B, int H, int L, int d_k, int d_v, int chunk, int dv_slab, void* stream);
 
+/*
+ * efla_chunk_fwd_scan -- efla_chunk_fwd for few (batch, head) pairs and long sequences: the chunks of each
+ * sequence are cut into `segments` consecutive segments that are processed at the same time.  The state
+ * recurrence is affine in the state ("Exact Flow Linear Attention" (gist.science), Metodologia item 3: the
+ * update is linear in S; "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 4: chunks are
+ * joined by passing the state), so over a segment S_out = M S_in + S_out(0), with M the product of the chunk
+ * transitions I - K^T T diag(alpha) K.  Launches, all on `stream`: the UT transform of every chunk; a state pass
+ * over every segment from a zero state, on the state augmented with d_k columns that start as the identity
+ * and see zero values (they end as M); a scan S_in[g+1] = M_g S_in[g] + S_g(0) from initial_state; a state pass
+ * over every segment from its S_in that writes the outputs and the last segment's final state.  About three
+ * times the state-pass work of efla_chunk_fwd_split, spread over `segments` times as many workgroups.
+ * Same operator, arguments, aliasing rules and errors as efla_chunk_fwd_split_gate, plus:
+ *   segments   0 = the library's choice (efla_chunk_scan_plan), else the number of segments wanted (at most
+ *              one per chunk; the count actually used is ceil(chunks / ceil(chunks / segments)))
+ *   workspace  device memory of at least efla_chunk_scan_plan(...)'s workspace_bytes, 256-byte aligned,
+ *              overlapping no other argument; with one segment this is the efla_chunk_fwd_split workspace.
+ */
+efla_status efla_chunk_fwd_scan(const void* q, const void* k, const void* v, const float* beta,
+                                efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                int B, int H, int L, int d_k, int d_v, int chunk, int segments, int gate,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Launch shape and workspace of efla_chunk_fwd_scan for these sizes (host only): segments used, chunks per
+ * segment, state slab width and workspace bytes.  Errors as efla_chunk_fwd_scan would return for the sizes. */
+efla_status efla_chunk_scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int segments,
+                                 int* nseg, int* seg_chunks, int* slab_width, size_t* workspace_bytes);
+
 /* Like efla_chunk_fwd_plan, for the state-pass launch of efla_chunk_fwd_split / efla_chunk_state_pass. */
 efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
                                       int dv_slab, int* workgroups, int* slab_width, int* lds_bytes);

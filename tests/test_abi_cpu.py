@@ -253,3 +253,48 @@ def test_every_gate_passes_argument_checks(lib):
     for gate in (efla.GATE_EXACT, efla.GATE_DELTANET, 2, 4, efla.GATE_MAX_ORDER):
         for name, st in _gated_calls(lib, gate).items():
             assert st == NO_DEVICE, (name, gate)
+
+
+def test_scan_plan(lib):
+    # long-context shape: 16 heads x 2 slabs per segment, eight segments of 128 chunks fill 256 workgroups
+    assert efla.scan_plan(1, 16, 65536, 128, 128, 64, torch.bfloat16) == (8, 128, 64, 109051904)
+    # many heads: one segment, i.e. the split forward and its workspace
+    assert efla.scan_plan(8, 16, 4096, 128, 128, 64, torch.bfloat16) == (1, 64, 64, 41943040)
+    # explicit counts: no empty segment; at most one per chunk; d_k = 16 narrows the slab
+    assert efla.scan_plan(1, 1, 256, 16, 16, 16, torch.float32, 5)[:3] == (4, 4, 16)
+    assert efla.scan_plan(1, 1, 100, 64, 64, 64, torch.float32, 9)[:2] == (2, 1)
+    ns, sc, sw, nb = efla.scan_plan(2, 3, 1000, 64, 32, 32, torch.bfloat16, 4)
+    assert (ns, sc, sw) == (4, 8, 32)
+    ut = 6 * 32 * 3 * 256 * 2
+    assert nb == ut + 6 * 4 * 64 * (32 + 64) * 4 + 6 * 4 * 64 * 32 * 4
+    n = ctypes.c_int()
+    assert lib.efla_chunk_scan_plan(1, 1, 8, 64, 64, 48, BF16, 0, ctypes.byref(n), None, None, None) == UNSUPPORTED
+    assert lib.efla_chunk_scan_plan(1, 1, 8, 64, 64, 64, BF16, -1, ctypes.byref(n), None, None, None) == INVALID
+
+
+def _scan_call(lib, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=BF16, o=P(5), s0=None, sf=P(6), B=1, H=2, L=4096, dk=128, dv=128,
+             C=64, seg=4, gate=0, ws=P(7), wsb=1 << 30)
+    a.update(kw)
+    return lib.efla_chunk_fwd_scan(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["o"], a["s0"], a["sf"], a["B"], a["H"],
+                                   a["L"], a["dk"], a["dv"], a["C"], a["seg"], a["gate"], a["ws"], a["wsb"], None)
+
+
+def test_scan_argument_errors(lib):
+    need = efla.scan_plan(1, 2, 4096, 128, 128, 64, torch.bfloat16, 4)[3]
+    assert _scan_call(lib, ws=None) == WORKSPACE
+    assert _scan_call(lib, wsb=need - 1) == WORKSPACE
+    assert _scan_call(lib, ws=ctypes.c_void_p(0x7F0700000000 + 128)) == WORKSPACE   # not 256-byte aligned
+    assert _scan_call(lib, ws=ctypes.c_void_p(0x7F0500000000 + 4096)) == INVALID    # inside o
+    assert _scan_call(lib, seg=-2) == INVALID
+    assert _scan_call(lib, gate=17) == INVALID
+    assert _scan_call(lib, dk=96) == UNSUPPORTED
+    assert _scan_call(lib, q=None) == INVALID
+    assert _scan_call(lib, B=0, ws=None, wsb=0) == OK
+    assert _scan_call(lib, L=0, sf=None, q=None, k=None, v=None, beta=None, o=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_scan_reaches_the_device_check(lib):
+    assert _scan_call(lib) == NO_DEVICE
+    assert _scan_call(lib, seg=0, s0=P(6)) == NO_DEVICE      # in-place state passing

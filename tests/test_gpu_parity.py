@@ -33,6 +33,9 @@ def _run_fwd(x, dtype, chunk, dv_slab=0, poison=True, method="split"):
         # a NaN-filled workspace: every block the state pass reads must have been written by the UT launch
         ws = torch.full((max(1, efla.chunk_workspace_size(B, H, L, chunk, d["v"].dtype)),), 0xFF, dtype=torch.uint8,
                         device="cuda")
+    elif method == "scan":
+        need = efla.scan_plan(B, H, L, d["k"].shape[-1], d_v, chunk, d["v"].dtype)[3]
+        ws = torch.full((max(1, need),), 0xFF, dtype=torch.uint8, device="cuda")
     o, S = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=d["initial_state"], chunk_size=chunk,
                           dv_slab=dv_slab, out=out, method=method, workspace=ws)
     torch.cuda.synchronize()
@@ -276,7 +279,7 @@ def test_lm_layer_workload_full_size_sampled(method):
     _sampled_heads(w, x, o, S, [(0, 0), (0, 15), (3, 7), (7, 15)])
 
 
-@pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("method", METHODS + ["scan"])
 def test_long_context_workload_full_size_sampled(method):
     w = W.workload(4)
     x = W.make_fwd_inputs(w)
