@@ -180,7 +180,7 @@ def run_forward(efla, W, torch, steps, warmup):
         time.sleep(0.5)
 
     def one_call(gate=efla.GATE_EXACT):
-        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, gate=gate)
+        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, gate=gate, method="split")
 
     def timed(fn):
         settle()
@@ -322,7 +322,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context forward")
-    ap.add_argument("--only", choices=["fwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "copy", "long"], default=None,
                     help="run one leg only (for profiling); prints a short JSON line")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter CSVs under DIR (host only)")
@@ -356,6 +356,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"leg": "copy", "bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
                           "launches": args.warmup + args.steps}), flush=True)
+        return
+    if args.only == "long":
+        print(json.dumps({"leg": "long", **run_long_context(efla, W, torch)}), flush=True)
         return
     if args.only == "decode":
         dw, step_ms = run_decode(efla, W, torch)

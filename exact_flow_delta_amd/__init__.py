@@ -200,15 +200,17 @@ def ut_transform(k, beta, chunk_size=64, out=None, gate=GATE_EXACT):
 
 
 def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_size=64, dv_slab=0,
-              out=None, final_state=None, method="split", workspace=None, gate=GATE_EXACT, segments=0):
+              out=None, final_state=None, method="auto", workspace=None, gate=GATE_EXACT, segments=0):
     """Chunkwise-parallel EFLA forward over [B,H,L,*] inputs.
 
     Returns (o [B,H,L,d_v] in the input dtype, final state [B,H,d_k,d_v] fp32 or None).
     ``final_state`` may be passed (and may be ``initial_state`` itself) to receive the state in place.
     ``method`` is "split" (UT transform launch + state-pass launch, through ``workspace``: a device
     tensor of at least chunk_workspace_size(...) bytes, allocated here when not given), "fused" (one
-    kernel, no workspace) or "scan" (segment-parallel: ``segments`` segments per sequence, 0 = the library's
-    choice; workspace of scan_plan(...)[3] bytes).
+    kernel, no workspace), "scan" (segment-parallel: ``segments`` segments per sequence, 0 = the library's
+    choice; workspace of scan_plan(...)[3] bytes) or "auto" (the default: "scan" when the library would
+    cut the sequences into more than one segment -- few heads, long sequences -- else "split"; the scan
+    workspace is then the split one).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
@@ -234,6 +236,8 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
         _dev_tensor(final_state, "final_state")
         if final_state.dtype != torch.float32 or tuple(final_state.shape) != (B, H, d_k, d_v):
             raise ValueError("final_state must be float32 [B,H,d_k,d_v]")
+    if method == "auto":
+        method = "scan" if scan_plan(B, H, L, d_k, d_v, int(chunk_size), v.dtype)[0] > 1 else "split"
     if method == "fused":
         _check(lib.efla_chunk_fwd_slab_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
                                             _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v,
