@@ -94,6 +94,8 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     constexpr int NQ = TaShape<C>::NQ;
     constexpr int QE = TaShape<C>::QE;
     constexpr int NCV = DVS / 8;   // 16-byte chunks per V row
+    constexpr int NSUB = C > 32 ? C / 32 : 1;   // sub-chunks of at most 32 tokens per chunk
+    constexpr int NBS = NB / NSUB;              // row blocks per sub-chunk
     static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
     static_assert(SH::BYTES <= kMaxLdsBytes, "state pass LDS too large");
 
@@ -262,106 +264,116 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
         };
         auto pair = [&](quad a, quad b) __attribute__((always_inline)) -> bx8 { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); };
 
-        bx8 Sq[NKP];   // state operand: lane (r, g) holds S[32 kp + 8 g .. +7][colw + r]
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp) Sq[kp] = pair(M::cvt(S[2 * kp]), M::cvt(S[2 * kp + 1]));
-
-        quad Rq[NB];
-        bx8 kq[NB][NKP];
-        quad Pq[NB * (NB + 1) / 2];
-        static_for<NB>([&](auto rbc) {
-            constexpr int rb = decltype(rbc)::value;
-            if constexpr (OUT) store_pending(rb);
-            bx8 qq[NKP];
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) {
-                if constexpr (OUT) qq[kp] = frag(cQ, rb, kp);
-                kq[rb][kp] = frag(cK, rb, kp);
-            }
-            f32x4 xk = {0.f, 0.f, 0.f, 0.f};
-            Ot[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) {
-                if constexpr (OUT) Ot[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Sq[kp], qq[kp], Ot[rb], 0, 0, 0);   // (Q S)^T
-                xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[rb][kp], Sq[kp], xk, 0, 0, 0);       // K S
-            }
-            // R = V - K S: lane (r, g), element e: row 16 rb + 4g + e, column 16 w + r of the slab
-            const s16x4 vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_u8*>(cV) + 16 * rb * SH::RBV + v_off));
-            const quad vq = __builtin_bit_cast(quad, vr);
-            f32x4 rr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rr[e] = (float)vq[e] - xk[e];
-            Rq[rb] = M::cvt(rr);
-            if constexpr (!OUT) return;
-            // block row rb of lower_incl(Q K^T): acc lane (r, g), element e = (Q K^T)[16 rb + r][16 lo + 4g + e];
-            // the blocks' accumulation chains are interleaved (reduction step outer) so that consecutive
-            // matrix instructions are independent
-            f32x4 pacc[rb + 1];
-#pragma unroll
-            for (int lo = 0; lo <= rb; ++lo) pacc[lo] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) {
-#pragma unroll
-                for (int lo = 0; lo <= rb; ++lo)
-                    pacc[lo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[lo][kp], qq[kp], pacc[lo], 0, 0, 0);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pacc[rb][e] = (4 * g + e <= r) ? pacc[rb][e] : 0.0f;
-#pragma unroll
-            for (int lo = 0; lo <= rb; ++lo) Pq[rb * (rb + 1) / 2 + lo] = M::cvt(pacc[lo]);
-        });
-        // Delta = Ta R (block lower triangular); Ta block qi as lane (r, g)'s quad at byte 512 qi + 8 lane
-        typedef quad __attribute__((address_space(3))) lds_quad;
-        quad ta[NQ];
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) ta[i] = *reinterpret_cast<const lds_quad*>(cur + SH::OFF_T + 512 * i + 8 * lane);
-        quad Dq[NB];
-        static_for<NB>([&](auto rbc) {
-            constexpr int rb = decltype(rbc)::value;
-            constexpr int q0 = rb * (rb + 1) / 2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            static_for<(rb + 1) / 2>([&](auto hc) {
-                constexpr int kb = 2 * decltype(hc)::value;
-                M::mma2(acc, ta[q0 + kb], ta[q0 + kb + 1], Rq[kb], Rq[kb + 1]);
-            });
-            if constexpr ((rb + 1) & 1) M::mma1(acc, ta[q0 + rb], Rq[rb]);
-            Dq[rb] = M::cvt(acc);
-        });
-        // O^T += Delta^T lower_incl(Q K^T)^T (stored with the next chunk)
-        static_for<NB>([&](auto rbc) {
-            if constexpr (!OUT) return;
-            constexpr int rb = decltype(rbc)::value;
-            constexpr int p0 = rb * (rb + 1) / 2;
-            static_for<(rb + 1) / 2>([&](auto hc) {
-                constexpr int kb = 2 * decltype(hc)::value;
-                M::mma2(Ot[rb], Dq[kb], Dq[kb + 1], Pq[p0 + kb], Pq[p0 + kb + 1]);
-            });
-            if constexpr ((rb + 1) & 1) M::mma1(Ot[rb], Dq[rb], Pq[p0 + rb]);
-        });
-        pend_t0 = c * C;
-        pend_n = !write_o ? 0 : (L - pend_t0 < C) ? (L - pend_t0) : C;
         // S += K^T Delta: tile rt = 2 kp + h takes, as A operand, the transposed K block whose lane (g, e, c)
-        // points at row 16 kb + 4 g + e, logical chunk 4 kp + c, byte 8 h; the tiles' chains are interleaved
+        // points at row 16 kb + 4 g + e, logical chunk 4 kp + c, byte 8 h
         auto kt = [&](int rt, int kb) __attribute__((always_inline)) {
             const int off = te * SH::RBQ + 16 * ((4 * (rt >> 1) + tc) ^ swt) + 8 * (rt & 1);
             return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                 (lds_s16x4*)(const_cast<lds_u8*>(cK) + 16 * kb * SH::RBQ + off)));
         };
+        typedef quad __attribute__((address_space(3))) lds_quad;
+        // The chunk is stepped through in sub-chunks of NBS row blocks (32 tokens): the sub-chunks' T diag(alpha)
+        // are the diagonal 32 x 32 blocks of the chunk's (the diagonal blocks of the inverse of a block lower
+        // triangular matrix are the inverses of its diagonal blocks), so the same UT output serves, and the
+        // intra-chunk products shrink: Q K^T, Delta and O take 32 instead of 52 matrix instructions per 64 tokens.
+        static_for<NSUB>([&](auto hc) {
+            constexpr int b0 = decltype(hc)::value * NBS;   // first row block of the sub-chunk
+            bx8 Sq[NKP];   // state operand: lane (r, g) holds S[32 kp + 8 g .. +7][colw + r]
 #pragma unroll
-        for (int kb = 0; kb + 1 < NB; kb += 2) {
-            quad k0[NKD], k1[NKD];
+            for (int kp = 0; kp < NKP; ++kp) Sq[kp] = pair(M::cvt(S[2 * kp]), M::cvt(S[2 * kp + 1]));
+            quad Rq[NBS];
+            bx8 kq[NBS][NKP];
+            quad Pq[NBS * (NBS + 1) / 2];   // block (j, lo) of the sub-chunk at j (j + 1) / 2 + lo
+            static_for<NBS>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int rb = b0 + j;
+                if constexpr (OUT) store_pending(rb);
+                bx8 qq[NKP];
 #pragma unroll
-            for (int rt = 0; rt < NKD; ++rt) {
-                k0[rt] = kt(rt, kb);
-                k1[rt] = kt(rt, kb + 1);
+                for (int kp = 0; kp < NKP; ++kp) {
+                    if constexpr (OUT) qq[kp] = frag(cQ, rb, kp);
+                    kq[j][kp] = frag(cK, rb, kp);
+                }
+                f32x4 xk = {0.f, 0.f, 0.f, 0.f};
+                Ot[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) {
+                    if constexpr (OUT) Ot[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Sq[kp], qq[kp], Ot[rb], 0, 0, 0);   // (Q S)^T
+                    xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[j][kp], Sq[kp], xk, 0, 0, 0);       // K S
+                }
+                // R = V - K S: lane (r, g), element e: row 16 rb + 4g + e, column 16 w + r of the slab
+                const s16x4 vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_u8*>(cV) + 16 * rb * SH::RBV + v_off));
+                const quad vq = __builtin_bit_cast(quad, vr);
+                f32x4 rr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rr[e] = (float)vq[e] - xk[e];
+                Rq[j] = M::cvt(rr);
+                if constexpr (!OUT) return;
+                // block row rb of lower_incl(Q K^T) within the sub-chunk: acc lane (r, g), element e =
+                // (Q K^T)[16 rb + r][16 (b0 + lo) + 4g + e]; the blocks' chains are interleaved (reduction step
+                // outer) so that consecutive matrix instructions are independent
+                f32x4 pacc[j + 1];
+#pragma unroll
+                for (int lo = 0; lo <= j; ++lo) pacc[lo] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) {
+#pragma unroll
+                    for (int lo = 0; lo <= j; ++lo)
+                        pacc[lo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[lo][kp], qq[kp], pacc[lo], 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pacc[j][e] = (4 * g + e <= r) ? pacc[j][e] : 0.0f;
+#pragma unroll
+                for (int lo = 0; lo <= j; ++lo) Pq[j * (j + 1) / 2 + lo] = M::cvt(pacc[lo]);
+            });
+            // Delta = Ta R over the sub-chunk; Ta block (rb, kb) of the chunk is quad qi = rb (rb + 1) / 2 + kb,
+            // lane (r, g)'s at byte 512 qi + 8 lane
+            auto ta = [&](int rb, int kb) __attribute__((always_inline)) {
+                return *reinterpret_cast<const lds_quad*>(cur + SH::OFF_T + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+            };
+            quad Dq[NBS];
+            static_for<NBS>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int rb = b0 + j;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                static_for<(j + 1) / 2>([&](auto pc) {
+                    constexpr int i = 2 * decltype(pc)::value;
+                    M::mma2(acc, ta(rb, b0 + i), ta(rb, b0 + i + 1), Rq[i], Rq[i + 1]);
+                });
+                if constexpr ((j + 1) & 1) M::mma1(acc, ta(rb, rb), Rq[j]);
+                Dq[j] = M::cvt(acc);
+            });
+            // O^T += Delta^T lower_incl(Q K^T)^T within the sub-chunk (stored with the next chunk)
+            if constexpr (OUT) {
+                static_for<NBS>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    constexpr int p0 = j * (j + 1) / 2;
+                    static_for<(j + 1) / 2>([&](auto pc) {
+                        constexpr int i = 2 * decltype(pc)::value;
+                        M::mma2(Ot[b0 + j], Dq[i], Dq[i + 1], Pq[p0 + i], Pq[p0 + i + 1]);
+                    });
+                    if constexpr ((j + 1) & 1) M::mma1(Ot[b0 + j], Dq[j], Pq[p0 + j]);
+                });
             }
+            // S += K^T Delta over the sub-chunk; the tiles' chains are interleaved
 #pragma unroll
-            for (int rt = 0; rt < NKD; ++rt) M::mma2(S[rt], k0[rt], k1[rt], Dq[kb], Dq[kb + 1]);
-        }
-        if constexpr (NB & 1) {
+            for (int i = 0; i + 1 < NBS; i += 2) {
+                quad k0[NKD], k1[NKD];
 #pragma unroll
-            for (int rt = 0; rt < NKD; ++rt) M::mma1(S[rt], kt(rt, NB - 1), Dq[NB - 1]);
-        }
+                for (int rt = 0; rt < NKD; ++rt) {
+                    k0[rt] = kt(rt, b0 + i);
+                    k1[rt] = kt(rt, b0 + i + 1);
+                }
+#pragma unroll
+                for (int rt = 0; rt < NKD; ++rt) M::mma2(S[rt], k0[rt], k1[rt], Dq[i], Dq[i + 1]);
+            }
+            if constexpr (NBS & 1) {
+#pragma unroll
+                for (int rt = 0; rt < NKD; ++rt) M::mma1(S[rt], kt(rt, b0 + NBS - 1), Dq[NBS - 1]);
+            }
+        });
+        pend_t0 = c * C;
+        pend_n = !write_o ? 0 : (L - pend_t0 < C) ? (L - pend_t0) : C;
         wait_vm(INB{});   // LDS reads done; only this chunk's stores may still be in flight
         __builtin_amdgcn_s_barrier();
     };
