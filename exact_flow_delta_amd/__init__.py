@@ -10,6 +10,8 @@ library is missing, every call raises.
     a    = alpha(k, beta)
     t    = ut_transform(k, beta, chunk_size=64)          # T diag(alpha) per chunk (operand layout)
 
+    o, S = chunk_fwd_layout(q, k, v, beta, cu_seqlens=None)   # strided [B,H,L,d] views, packed sequences
+
 chunk_fwd runs the two-launch form by default (UT transform of all chunks into a workspace, then the
 state pass); method="fused" runs the single-kernel form, which needs no workspace; method="scan" cuts long
 sequences into segments processed at the same time (for few heads), see efla_chunk_fwd_scan.
@@ -32,8 +34,8 @@ import os
 
 import torch
 
-__all__ = ["EflaError", "alpha", "chunk_fwd", "recurrent_step", "chunk_plan", "chunk_workspace_size", "ut_transform",
-           "state_pass", "scan_plan", "library_path", "load_library"]
+__all__ = ["EflaError", "alpha", "chunk_fwd", "chunk_fwd_layout", "layout_plan", "recurrent_step", "chunk_plan",
+           "chunk_workspace_size", "ut_transform", "state_pass", "scan_plan", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libefla.so")
@@ -47,6 +49,12 @@ _vp = ctypes.c_void_p
 _i32 = ctypes.c_int
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
+
+
+class Layout(ctypes.Structure):
+    """efla_layout: element strides (batch, head, token) of q, k, v, o and beta, and packed-sequence offsets."""
+    _fields_ = [("q", _i64 * 3), ("k", _i64 * 3), ("v", _i64 * 3), ("o", _i64 * 3), ("beta", _i64 * 3),
+                ("cu_seqlens", _vp)]
 
 
 class EflaError(RuntimeError):
@@ -95,6 +103,10 @@ def load_library():
                                         _i32, _i32, _i32, _vp, _sz, _vp]
     lib.efla_chunk_scan_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                          ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
+    lib.efla_chunk_fwd_layout.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, ctypes.POINTER(Layout), _vp, _sz, _vp]
+    lib.efla_chunk_layout_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                           ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
     lib.efla_chunk_state_pass.argtypes = [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
@@ -265,6 +277,90 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
                "efla_chunk_fwd_scan")
     else:
         raise ValueError("method must be 'split', 'fused' or 'scan'")
+    return out, final_state
+
+
+def _dev_view(t: torch.Tensor, name: str, ndim: int):
+    """A GPU tensor of `ndim` dims whose last dimension is contiguous (other strides free)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s); libefla has no CPU path" % (name, t.device))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, ndim, tuple(t.shape)))
+    if ndim == 4 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("%s: the feature dimension must be contiguous" % name)
+
+
+def layout_plan(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, varlen=False, segments=0):
+    """(segments, workspace bytes) of chunk_fwd_layout; host only."""
+    lib = load_library()
+    ns, nb = _i32(), _sz()
+    _check(lib.efla_chunk_layout_plan(B, H, L, d_k, d_v, chunk, _dtype_of(dtype), int(bool(varlen)), segments,
+                                      ctypes.byref(ns), ctypes.byref(nb)), "efla_chunk_layout_plan")
+    return ns.value, nb.value
+
+
+def chunk_fwd_layout(q, k, v, beta, cu_seqlens=None, initial_state=None, output_final_state=True, chunk_size=64,
+                     segments=0, gate=GATE_EXACT, out=None, final_state=None, workspace=None):
+    """The chunked forward over strided views, or over packed sequences (efla_chunk_fwd_layout).
+
+    q, k [B,H,L,d_k], v [B,H,L,d_v], beta [B,H,L] are views with any strides (the feature dimension
+    contiguous): e.g. ``x.transpose(1, 2)`` of a [B,L,H,d] tensor, or slices of a fused projection.  With
+    ``cu_seqlens`` (int32 GPU tensor of N + 1 offsets) the views are [1,H,T,d] and [1,H,T] holding N packed
+    sequences, sequence n being tokens cu_seqlens[n] .. cu_seqlens[n+1]-1; states are then [N,H,d_k,d_v].
+    ``out`` (default: like ``v``, keeping its strides when it is dense) receives o.  ``segments`` as
+    chunk_fwd(method="scan"); with packed sequences one segment.  Returns (o, final state or None).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_view(t, name, 4)
+    _dev_view(beta, "beta", 3)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    B, H, L, d_k = k.shape
+    d_v = v.shape[-1]
+    if tuple(q.shape) != (B, H, L, d_k) or tuple(v.shape[:3]) != (B, H, L):
+        raise ValueError("q, k, v shapes disagree: %s %s %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, L):
+        raise ValueError("beta must be float32 [B,H,L]")
+    N = B
+    if cu_seqlens is not None:
+        _dev_tensor(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+        if B != 1:
+            raise ValueError("packed sequences are given as [1,H,T,d] views")
+        N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _dev_tensor(initial_state, "initial_state")
+        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (N, H, d_k, d_v):
+            raise ValueError("initial_state must be float32 [%d,H,d_k,d_v]" % N)
+    if out is None:
+        out = torch.empty_like(v)
+    _dev_view(out, "out", 4)
+    if tuple(out.shape) != (B, H, L, d_v) or out.dtype != v.dtype:
+        raise ValueError("out must be %s [B,H,L,d_v]" % v.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, d_k, d_v), dtype=torch.float32, device=v.device)
+    if final_state is not None:
+        _dev_tensor(final_state, "final_state")
+        if final_state.dtype != torch.float32 or tuple(final_state.shape) != (N, H, d_k, d_v):
+            raise ValueError("final_state must be float32 [%d,H,d_k,d_v]" % N)
+    lay = Layout()
+    for f, t in (("q", q), ("k", k), ("v", v), ("o", out)):
+        getattr(lay, f)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    lay.beta[:] = [beta.stride(0), beta.stride(1), beta.stride(2)]
+    lay.cu_seqlens = _ptr(cu_seqlens)
+    need = layout_plan(N, H, L, d_k, d_v, int(chunk_size), v.dtype, cu_seqlens is not None, int(segments))[1]
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+    _dev_tensor(workspace, "workspace")
+    _check(lib.efla_chunk_fwd_layout(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                     _ptr(initial_state), _ptr(final_state), N, H, L, d_k, d_v, int(chunk_size),
+                                     int(segments), int(gate), ctypes.byref(lay), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(v.device)),
+           "efla_chunk_fwd_layout")
     return out, final_state
 
 

@@ -162,6 +162,35 @@ efla_status scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dty
     return EFLA_OK;
 }
 
+// The split forward (one segment: UT transform, then the state pass) or the segment-parallel one: UT transform
+// of every chunk; pass 1 over every segment from a zero state with the transition columns; the scan of the
+// segments' initial states; pass 2 over every segment from its initial state, writing the outputs and the last
+// segment's final state.  a.tw is the workspace base (the UT output).
+hipError_t run_fwd(bool bf, const efla::SplitArgs& a, const ScanPlan& p, char* ws, hipStream_t s) {
+    auto chain = [&](const efla::SplitArgs& x, bool with_ut) {
+        return bf ? efla::launch_split_fwd_bf16(x, with_ut, s) : efla::launch_split_fwd_f32(x, with_ut, s);
+    };
+    if (p.nseg == 1) return chain(a, true);
+    float* states = reinterpret_cast<float*>(ws + p.off_states);
+    float* s_in = reinterpret_cast<float*>(ws + p.off_sin);
+    efla::SplitArgs a1 = a;
+    a1.o = nullptr;
+    a1.s0 = nullptr;
+    a1.sf = states;
+    a1.nseg = p.nseg;
+    a1.seg_chunks = p.seg_chunks;
+    a1.aug = 1;
+    a1.sf_all = 1;
+    hipError_t e = chain(a1, true);
+    if (e == hipSuccess) e = efla::launch_seg_scan(states, a.s0, s_in, a.BH, p.nseg, a.d_k, a.d_v, s);
+    efla::SplitArgs a2 = a;
+    a2.s0 = s_in;
+    a2.nseg = p.nseg;
+    a2.seg_chunks = p.seg_chunks;
+    if (e == hipSuccess) e = chain(a2, false);
+    return e;
+}
+
 }  // namespace
 
 namespace efla {
@@ -178,7 +207,7 @@ int64_t chunk_grid(int BH, int d_v, int dvs) { return (int64_t)((BH + 7) / 8) * 
 
 extern "C" {
 
-int efla_version(void) { return 10200; }
+int efla_version(void) { return 10300; }
 
 const char* efla_status_string(efla_status s) {
     switch (s) {
@@ -392,40 +421,181 @@ efla_status efla_chunk_fwd_scan(const void* q, const void* k, const void* v, con
     if (L == 0 && !final_state) return EFLA_OK;
     st = device_present();
     if (st != EFLA_OK) return st;
+    efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, workspace, (int)BH, L, d_k, d_v, chunk, p.dvs, gate};
+    const hipError_t e = run_fwd(dtype == EFLA_BF16, a, p, static_cast<char*>(workspace), (hipStream_t)stream);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_scan launch");
+}
+
+namespace {
+
+// Launch shape and workspace of efla_chunk_fwd_layout: the scan plan of the sizes (fixed-length sequences), or
+// one segment over packed sequences, whose workspace is the sanitised token offsets and the chunk offsets
+// (B + 1 int32 each) and the chunk -> sequence table (ceil(L / C) + B int32), then H * (ceil(L / C) + B) UT
+// chunks (the sanitised sequences are disjoint, so their sum_b ceil(len_b / C) is at most ceil(L / C) + B).
+// One segment takes the split forward's slab.
+struct LayoutPlan {
+    ScanPlan sp;
+    size_t off_ut;
+};
+
+efla_status layout_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, bool varlen, int segments,
+                        LayoutPlan* lp) {
+    if (segments < 0) return EFLA_ERR_INVALID_ARG;
+    if (varlen && segments > 1) return EFLA_ERR_UNSUPPORTED;
+    if (varlen) {
+        int dvs = 0;
+        const efla_status st = check_chunk_sizes(true, B, H, 0, d_k, d_v, chunk, dt, 0, &dvs);
+        if (st != EFLA_OK) return st;
+        if (L < 0) return EFLA_ERR_INVALID_ARG;
+        const int64_t n_ut = (int64_t)H * ((L + chunk - 1) / chunk + B);
+        if (n_ut > INT32_MAX || (int64_t)B + 1 > INT32_MAX / 8) return EFLA_ERR_INVALID_ARG;
+        lp->sp.dvs = dvs;
+        lp->sp.nseg = 1;
+        lp->sp.seg_chunks = 0;
+        lp->off_ut = round_up_256((size_t)(B + 1) * 8 + (size_t)((L + chunk - 1) / chunk + B) * 4);
+        lp->sp.off_states = lp->sp.off_sin = 0;
+        lp->sp.total = lp->off_ut + round_up_256((size_t)n_ut * efla::ut_block_elems(chunk) * esize(dt));
+        return EFLA_OK;
+    }
+    efla_status st = scan_plan(B, H, L, d_k, d_v, chunk, dt, segments, &lp->sp);
+    if (st != EFLA_OK) return st;
+    if (lp->sp.nseg == 1) {
+        int dvs = 0;
+        st = check_chunk_sizes(true, B, H, L, d_k, d_v, chunk, dt, 0, &dvs);
+        if (st != EFLA_OK) return st;
+        lp->sp.dvs = dvs;
+    }
+    lp->off_ut = 0;
+    return EFLA_OK;
+}
+
+// Elements spanned by a strided tensor of n0 x n1 x n2 rows of `inner` contiguous elements (0 when empty).
+int64_t span(const int64_t st[3], int64_t n0, int64_t n1, int64_t n2, int64_t inner) {
+    if (n0 <= 0 || n1 <= 0 || n2 <= 0) return 0;
+    return (n0 - 1) * st[0] + (n1 - 1) * st[1] + (n2 - 1) * st[2] + inner;
+}
+
+// No two rows share an element: the dimensions of more than one row, sorted by stride, each step over at
+// least the extent of the ones inside it.
+bool rows_disjoint(const int64_t st[3], const int64_t n[3], int64_t inner) {
+    int idx[3] = {0, 1, 2};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (st[idx[j]] < st[idx[i]]) { const int t = idx[i]; idx[i] = idx[j]; idx[j] = t; }
+    int64_t ext = inner;
+    for (int i = 0; i < 3; ++i) {
+        const int d = idx[i];
+        if (n[d] <= 1) continue;
+        if (st[d] < ext) return false;
+        ext += (n[d] - 1) * st[d];
+    }
+    return true;
+}
+
+}  // namespace
+
+efla_status efla_chunk_layout_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int varlen,
+                                   int segments, int* nseg, size_t* workspace_bytes) {
+    LayoutPlan lp;
+    const efla_status st = layout_plan(B, H, L, d_k, d_v, chunk, dtype, varlen != 0, segments, &lp);
+    if (st != EFLA_OK) return st;
+    if (nseg) *nseg = lp.sp.nseg;
+    if (workspace_bytes) *workspace_bytes = lp.sp.total;
+    return EFLA_OK;
+}
+
+efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                  void* o, const float* initial_state, float* final_state, int B, int H, int L,
+                                  int d_k, int d_v, int chunk, int segments, int gate, const efla_layout* layout,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
+    const bool varlen = layout && layout->cu_seqlens;
+    LayoutPlan lp;
+    efla_status st = layout_plan(B, H, L, d_k, d_v, chunk, dtype, varlen, segments, &lp);
+    if (st != EFLA_OK) return st;
+    const int64_t BH = (int64_t)B * H;
+    const int64_t es = (int64_t)esize(dtype);
+    efla::TokLayout ly = efla::contiguous_layout(H, L, d_k, d_v);
+    if (layout) {
+        const int64_t* src[5] = {layout->q, layout->k, layout->v, layout->o, layout->beta};
+        int64_t* dst[5] = {&ly.q_b, &ly.k_b, &ly.v_b, &ly.o_b, &ly.be_b};
+        for (int i = 0; i < 5; ++i) {
+            for (int j = 0; j < 3; ++j) {
+                const int64_t x = (varlen && j == 0) ? 0 : src[i][j];   // packed: no batch stride
+                if (x < 0) return EFLA_ERR_INVALID_ARG;
+                if (i < 4 && x % (16 / es) != 0) return EFLA_ERR_INVALID_ARG;   // 16-byte rows
+                dst[i][j] = x;
+            }
+        }
+        // rows of a chunk past the end of a sequence read as zeros only when no token's row overlaps the next
+        if (ly.q_t < d_k || ly.k_t < d_k || ly.v_t < d_v || ly.be_t < 1) return EFLA_ERR_INVALID_ARG;
+        // in-chunk offsets are 32-bit byte offsets
+        const int64_t lim = (int64_t)INT32_MAX / 64;
+        if (ly.q_t * es >= lim || ly.k_t * es >= lim || ly.v_t * es >= lim || ly.o_t * es >= lim || ly.be_t * 4 >= lim)
+            return EFLA_ERR_INVALID_ARG;
+        ly.cu_seqlens = layout->cu_seqlens;
+    }
+    ly.H = H;
+    ly.nseq = B;
+    const int64_t nb = varlen ? 1 : B;   // batch extent of the token tensors
+    const int64_t so[3] = {ly.o_b, ly.o_h, ly.o_t}, no[3] = {nb, H, L};
+    if (!rows_disjoint(so, no, d_v)) return EFLA_ERR_INVALID_ARG;
+    const int64_t sq[3] = {ly.q_b, ly.q_h, ly.q_t}, sk[3] = {ly.k_b, ly.k_h, ly.k_t}, sv[3] = {ly.v_b, ly.v_h, ly.v_t};
+    const int64_t sb[3] = {ly.be_b, ly.be_h, ly.be_t};
+    const size_t nq = (size_t)(span(sq, nb, H, L, d_k) * es), nk = (size_t)(span(sk, nb, H, L, d_k) * es);
+    const size_t nv = (size_t)(span(sv, nb, H, L, d_v) * es), nob = (size_t)(span(so, nb, H, L, d_v) * es);
+    const size_t nbe = (size_t)(span(sb, nb, H, L, 1) * 4);
+    const size_t ns = (size_t)BH * d_k * d_v * 4;
+    const size_t ncu = varlen ? (size_t)(B + 1) * 4 : 0;
+    if (L > 0 && BH > 0) {
+        if (!q || !k || !v || !beta || !o) return EFLA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(beta, 4))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if (varlen && BH > 0 && !aligned(layout->cu_seqlens, 4)) return EFLA_ERR_INVALID_ARG;
+    if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+        return EFLA_ERR_INVALID_ARG;
+    const void* cu = varlen ? (const void*)layout->cu_seqlens : nullptr;
+    // o overlaps nothing; the final state overlaps no input; initial and final state are identical or disjoint
+    if (overlap(o, nob, q, nq) || overlap(o, nob, k, nk) || overlap(o, nob, v, nv) || overlap(o, nob, beta, nbe) ||
+        overlap(o, nob, initial_state, ns) || overlap(o, nob, final_state, ns) || overlap(o, nob, cu, ncu))
+        return EFLA_ERR_INVALID_ARG;
+    if (overlap(final_state, ns, q, nq) || overlap(final_state, ns, k, nk) || overlap(final_state, ns, v, nv) ||
+        overlap(final_state, ns, beta, nbe) || overlap(final_state, ns, cu, ncu))
+        return EFLA_ERR_INVALID_ARG;
+    if ((const void*)initial_state != (const void*)final_state && overlap(initial_state, ns, final_state, ns))
+        return EFLA_ERR_INVALID_ARG;
+    const bool runs = BH > 0 && (L > 0 || final_state);
+    if (runs && lp.sp.total > 0) {
+        const size_t need = lp.sp.total;
+        if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+        if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nk) || overlap(workspace, need, v, nv) ||
+            overlap(workspace, need, beta, nbe) || overlap(workspace, need, o, nob) ||
+            overlap(workspace, need, initial_state, ns) || overlap(workspace, need, final_state, ns) ||
+            overlap(workspace, need, cu, ncu))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if (!runs) return EFLA_OK;
+    st = device_present();
+    if (st != EFLA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     char* ws = static_cast<char*>(workspace);
-    const bool bf = dtype == EFLA_BF16;
-    auto chain = [&](const efla::SplitArgs& a, bool with_ut) {
-        return bf ? efla::launch_split_fwd_bf16(a, with_ut, s) : efla::launch_split_fwd_f32(a, with_ut, s);
-    };
-    efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, ws, (int)BH, L, d_k, d_v, chunk, p.dvs, gate};
-    if (p.nseg == 1) {
-        const hipError_t e = chain(a, true);
-        return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_scan launch");
+    hipError_t e = hipSuccess;
+    if (varlen) {
+        int* cu_tok = reinterpret_cast<int*>(ws);
+        int* cu_chunks = cu_tok + (B + 1);
+        int* chunk_seq = cu_chunks + (B + 1);
+        ly.cu_seqlens = cu_tok;
+        ly.cu_chunks = cu_chunks;
+        ly.chunk_seq = chunk_seq;
+        e = efla::launch_varlen_prep(layout->cu_seqlens, cu_tok, cu_chunks, chunk_seq, B, L, chunk,
+                                     (L + chunk - 1) / chunk + B, s);
     }
-    float* states = reinterpret_cast<float*>(ws + p.off_states);
-    float* s_in = reinterpret_cast<float*>(ws + p.off_sin);
-    // UT transform of every chunk; pass 1: every segment from a zero state, with the transition columns
-    hipError_t e = bf ? efla::launch_ut_bf16(k, beta, ws, (int)BH, L, d_k, chunk, gate, s)
-                      : efla::launch_ut_f32(k, beta, ws, (int)BH, L, d_k, chunk, gate, s);
-    efla::SplitArgs a1 = a;
-    a1.o = nullptr;
-    a1.s0 = nullptr;
-    a1.sf = states;
-    a1.nseg = p.nseg;
-    a1.seg_chunks = p.seg_chunks;
-    a1.aug = 1;
-    a1.sf_all = 1;
-    if (e == hipSuccess) e = chain(a1, false);
-    // the segments' initial states
-    if (e == hipSuccess) e = efla::launch_seg_scan(states, initial_state, s_in, (int)BH, p.nseg, d_k, d_v, s);
-    // pass 2: every segment from its initial state, writing the outputs and the last segment's final state
-    efla::SplitArgs a2 = a;
-    a2.s0 = s_in;
-    a2.nseg = p.nseg;
-    a2.seg_chunks = p.seg_chunks;
-    if (e == hipSuccess) e = chain(a2, false);
-    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_scan launch");
+    efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, ws + lp.off_ut, (int)BH, L, d_k, d_v, chunk,
+                      lp.sp.dvs, gate};
+    a.layout = &ly;
+    if (e == hipSuccess) e = run_fwd(dtype == EFLA_BF16, a, lp.sp, ws, s);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_layout launch");
 }
 
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype, void* o,

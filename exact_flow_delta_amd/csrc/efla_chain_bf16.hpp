@@ -83,7 +83,8 @@ __device__ __forceinline__ int sw_v(int t) {
 template <int DK, int C, int DVS, bool OUT>
 __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
-    bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg) {
+    bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg,
+    TokLayout ly) {
     typedef ChainBf16Shape<DK, C, DVS> SH;
     typedef Mma<bf16> M;
     typedef M::quad quad;
@@ -122,12 +123,14 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     const bool trans = slab >= sg.nslab_v;         // transition slab: zero values, identity start, no outputs
     const bool producer = w == NW;                 // the extra wave: it only fetches
     const int colw = slab_col + 16 * (producer ? 0 : w);
-    const int64_t tok0 = (int64_t)bh * L;
-    const int NC = (L + C - 1) / C;
+    const SeqView sv = seq_view(ly, bh, L, C);      // this head's tokens: offsets, row strides, length
+    const int len = sv.len;
+    const int NC = (len + C - 1) / C;
+    const int64_t qs = ly.q_t, ks = ly.k_t, vs = ly.v_t, os = ly.o_t;
     const int seg = blockIdx.y, nseg = gridDim.y;
     const int c0 = seg * sg.seg_chunks;            // this workgroup's chunks [c0, c1)
     const int c1 = NC < c0 + sg.seg_chunks ? NC : c0 + sg.seg_chunks;
-    const bf16* twh = tw + (int64_t)bh * NC * (NQ * QE);
+    const bf16* twh = tw + (int64_t)sv.chunk0 * (NQ * QE);
 
     // ---- per-lane LDS byte offsets, fixed for the whole sequence ---------------------------------
     // fragment reads: row 16 rb + r, logical chunk 4 kp + g  ->  + 16 * ((4 kp + g) ^ sw(row))
@@ -147,11 +150,11 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     constexpr int NISSUE = NLOAD - (OUT ? 0 : SH::NLQ);       // the ones issued (no Q tile without outputs)
     auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
         const int t = c * C;
-        const int n = (L - t < C) ? (L - t) : C;   // <= 0 past the end: an empty range, zeros
-        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (tok0 + t) * DK, n > 0 ? n * DK * 2 : 0);
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, n > 0 ? n * DK * 2 : 0);
+        const int n = (len - t < C) ? (len - t) : C;   // <= 0 past the end: an empty range, zeros
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + sv.q0 + t * qs, n > 0 ? ((n - 1) * qs + DK) * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + sv.k0 + t * ks, n > 0 ? ((n - 1) * ks + DK) * 2 : 0);
         const __amdgpu_buffer_rsrc_t rv =
-            buffer_rsrc(v + (tok0 + t) * DV + slab_col, n > 0 && !trans ? ((n - 1) * DV + DVS) * 2 : 0);
+            buffer_rsrc(v + sv.v0 + t * vs + slab_col, n > 0 && !trans ? ((n - 1) * vs + DVS) * 2 : 0);
         const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(twh + (int64_t)c * (NQ * QE), SH::TBYTES);
         static_for<NLOAD>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
                 // rows >= C (slack of a last partial load) and rows >= n are out of range and land as zeros
                 const int tr = p / RB;
                 const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
-                const int ld = tile == 2 ? DV : DK;
+                const int ld = (int)(tile == 2 ? vs : tile == 1 ? ks : qs);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 0 ? rq : tile == 1 ? rk : rv, dst, 16,
                                                          (tr * ld + 8 * lc) * 2, 0, 0, 0);
             }
@@ -248,8 +251,8 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     // empty range before the first chunk)
     auto store_pending = [&](int rb) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t ors =
-            buffer_rsrc(o + (tok0 + pend_t0) * DV + colw, pend_n > 0 ? ((pend_n - 1) * DV + 16) * 2 : 0);
-        buffer_store<quad>(ors, ((16 * rb + r) * DV + 4 * g) * 2, M::cvt(Ot[rb]));
+            buffer_rsrc(o + sv.o0 + pend_t0 * os + colw, pend_n > 0 ? ((pend_n - 1) * os + 16) * 2 : 0);
+        buffer_store<quad>(ors, ((16 * rb + r) * (int)os + 4 * g) * 2, M::cvt(Ot[rb]));
     };
 
     // one chunk of the compute waves: the previous chunk's outputs are stored a row block at a time while
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
             }
         });
         pend_t0 = c * C;
-        pend_n = !write_o ? 0 : (L - pend_t0 < C) ? (L - pend_t0) : C;
+        pend_n = !write_o ? 0 : (len - pend_t0 < C) ? (len - pend_t0) : C;
         wait_vm(INB{});   // LDS reads done; only this chunk's stores may still be in flight
         __builtin_amdgcn_s_barrier();
     };
@@ -410,6 +413,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
 template <int DK, int C, int DVS>
 hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
     const ChainSeg sg = chain_seg(a, DK, C, DVS);
+    const TokLayout ly = a.layout ? *a.layout : contiguous_layout(1, a.L, DK, a.d_v);
     const int nslab = (a.d_v + (a.aug ? DK : 0)) / DVS;
     const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
     const dim3 g3((unsigned)grid, (unsigned)(a.nseg > 0 ? a.nseg : 1));
@@ -417,12 +421,12 @@ hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, false>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
-                           sg);
+                           sg, ly);
     else
         hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, true>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
-                           sg);
+                           sg, ly);
     return hipGetLastError();
 }
 

@@ -43,12 +43,28 @@ struct TileRegs {
     static constexpr int N = (C * VPR + NT - 1) / NT;
     V16 x[N];
 
+    // Rows >= n read as zeros: the range ends at row n - 1, and with a row stride ld >= W every later row
+    // starts past it.
     __device__ __forceinline__ void load(const E* __restrict__ base, int ld, int n, int tid) {
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, n > 0 ? ((n - 1) * ld + W) * (int)sizeof(E) : 0);
+        if constexpr (NT % VPR == 0) {
+            // pass `it` covers rows it * RPI + tid / VPR: one (wave-uniform) range per pass, so that a
+            // single per-lane offset serves every pass whatever the row stride
+            constexpr int RPI = NT / VPR;
+            const int lane_off = ((tid / VPR) * ld + (tid % VPR) * VEC) * (int)sizeof(E);
 #pragma unroll
-        for (int it = 0; it < N; ++it) {
-            const int idx = it * NT + tid;   // idx >= C * VPR lands on a row >= C >= n: out of range
-            x[it] = buffer_load<V16>(rs, ((idx / VPR) * ld + (idx % VPR) * VEC) * (int)sizeof(E));
+            for (int it = 0; it < N; ++it) {
+                const int nr = n - it * RPI;
+                const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base + (int64_t)it * RPI * ld,
+                                                              nr > 0 ? ((nr - 1) * ld + W) * (int)sizeof(E) : 0);
+                x[it] = buffer_load<V16>(rs, lane_off);
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, n > 0 ? ((n - 1) * ld + W) * (int)sizeof(E) : 0);
+#pragma unroll
+            for (int it = 0; it < N; ++it) {
+                const int idx = it * NT + tid;   // idx >= C * VPR lands on a row >= C >= n: out of range
+                x[it] = buffer_load<V16>(rs, ((idx / VPR) * ld + (idx % VPR) * VEC) * (int)sizeof(E));
+            }
         }
     }
     __device__ __forceinline__ void store(E* s, int lds_ld, int tid) const {
@@ -177,9 +193,10 @@ __device__ __forceinline__ void ut_rows_balanced(const E* sK, const float* sLam,
     M::lds_store_quad(sTat + (b0 + r) * LD_CE + b0 + 4 * g, M::cvt(mine * ar));
 }
 
-template <typename E, int DK, int C>
+template <typename E, int DK, int C, bool VL>
 __global__ __launch_bounds__(C / 16 * 64) void ut_kernel(const E* __restrict__ k, const float* __restrict__ beta,
-                                                         E* __restrict__ tw, int L, int NC, int total, int gate) {
+                                                         E* __restrict__ tw, int L, int NC, int BH, int gate,
+                                                         TokLayout ly) {
     typedef UtLayout<sizeof(E), DK, C> LY;
     typedef Mma<E> M;
     typedef typename M::quad quad;
@@ -210,16 +227,19 @@ __global__ __launch_bounds__(C / 16 * 64) void ut_kernel(const E* __restrict__ k
     // that token's step; rows past the end of the sequence read as zero keys with zero step
     KT kt;
     float bt[KT::N];
+    const int total = ut_chunks<VL>(ly, BH, NC);
     auto load = [&](int u) {
-        const int bh = u / NC;
-        const int t0 = (u - bh * NC) * C;
-        const int n = (L - t0 < C) ? (L - t0) : C;
-        const int64_t tok = (int64_t)bh * L + t0;
-        kt.load(k + tok * DK, DK, n, tid);
-        const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(beta + tok, n * 4);
+        int bh, c;
+        chunk_of<VL>(ly, u, NC, bh, c);
+        const SeqView sv = seq_view_t<VL>(ly, bh, L, C);
+        const int t0 = c * C;
+        const int n = (sv.len - t0 < C) ? (sv.len - t0) : C;
+        const int ks = (int)ly.k_t, bs = (int)ly.be_t;
+        kt.load(k + sv.k0 + (int64_t)t0 * ks, ks, n, tid);
+        const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(beta + sv.be0 + (int64_t)t0 * bs, n > 0 ? ((n - 1) * bs + 1) * 4 : 0);
 #pragma unroll
         for (int it = 0; it < KT::N; ++it)
-            bt[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, ((it * NT + tid) / KT::VPR) * 4, 0, 0));
+            bt[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(brs, ((it * NT + tid) / KT::VPR) * bs * 4, 0, 0));
     };
     int u = blockIdx.x;
     if (u < total) load(u);
@@ -302,7 +322,7 @@ constexpr int chain_layout_bytes(int dk, int c, int dvs) {
 template <typename E, int DK, int C, int DVS>
 __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ tw,
-    E* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg) {
+    E* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg, TokLayout ly) {
     typedef ChainLayout<sizeof(E), DK, C, DVS> LY;
     typedef Mma<E> M;
     typedef typename M::quad quad;
@@ -335,13 +355,15 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
     const int slab_col = slab * DVS;              // column of the state (value columns first, then transition)
     const bool trans = slab >= sg.nslab_v;        // transition slab: zero values, identity start, no outputs
     const int colw = slab_col + 16 * w;
-    const int64_t tok0 = (int64_t)bh * L;
-    const int NC = (L + C - 1) / C;
+    const SeqView sv = seq_view(ly, bh, L, C);     // this head's tokens: offsets, row strides, length
+    const int len = sv.len;
+    const int NC = (len + C - 1) / C;
+    const int64_t qs = ly.q_t, ks = ly.k_t, vs = ly.v_t, os = ly.o_t;
     const int seg = blockIdx.y, nseg = gridDim.y;
     const int c0 = seg * sg.seg_chunks;           // this workgroup's chunks [c0, c1)
     const int c1 = NC < c0 + sg.seg_chunks ? NC : c0 + sg.seg_chunks;
     const bool write_o = o != nullptr && !trans;
-    const E* twh = tw + (int64_t)bh * NC * (NQ * QE) + lane * 4;
+    const E* twh = tw + (int64_t)sv.chunk0 * (NQ * QE) + lane * 4;
 
     auto sQ = [&](int b) { return reinterpret_cast<E*>(smem + b * LY::BUF + LY::OFF_Q); };
     auto sK = [&](int b) { return reinterpret_cast<E*>(smem + b * LY::BUF + LY::OFF_K); };
@@ -351,10 +373,10 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
     TileRegs<E, C, DVS, NT> rv;
     auto load_stage = [&](int c) {
         const int t = c * C;
-        const int n = (L - t < C) ? (L - t) : C;
-        rq.load(q + (tok0 + t) * DK, DK, n, tid);
-        rk.load(k + (tok0 + t) * DK, DK, n, tid);
-        rv.load(v + (tok0 + t) * DV + slab_col, DV, trans ? 0 : n, tid);
+        const int n = (len - t < C) ? (len - t) : C;
+        rq.load(q + sv.q0 + t * qs, (int)qs, n, tid);
+        rk.load(k + sv.k0 + t * ks, (int)ks, n, tid);
+        rv.load(v + sv.v0 + t * vs + slab_col, (int)vs, trans ? 0 : n, tid);
     };
     auto store_stage = [&](int b) {
         rq.store(sQ(b), LD_DK, tid);
@@ -391,7 +413,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
 
     for (int c = c0; c < c1; ++c) {
         const int t0 = c * C;
-        const int n = (L - t0 < C) ? (L - t0) : C;
+        const int n = (len - t0 < C) ? (len - t0) : C;
         const int b = DB ? ((c - c0) & 1) : 0;
         if constexpr (DB) {
             // Straight-line on purpose (no branch for the last chunks): past the end of the sequence the
@@ -479,7 +501,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
         // O^T = (Q S)^T + Delta^T lower_incl(Q K^T)^T; four consecutive outputs of one token per lane, stored
         // through a buffer resource that ends at the chunk's last valid row
         const __amdgpu_buffer_rsrc_t ors =
-            buffer_rsrc(o + (tok0 + t0) * DV + colw, write_o ? ((n - 1) * DV + 16) * (int)sizeof(E) : 0);
+            buffer_rsrc(o + sv.o0 + t0 * os + colw, write_o ? ((n - 1) * (int)os + 16) * (int)sizeof(E) : 0);
         static_for<NB>([&](auto rbc) {
             constexpr int rb = decltype(rbc)::value;
             constexpr int p0 = rb * (rb + 1) / 2;
@@ -488,7 +510,7 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
                 M::mma2(Ot[rb], Dq[kb], Dq[kb + 1], Pq[p0 + kb], Pq[p0 + kb + 1]);
             });
             if constexpr ((rb + 1) & 1) M::mma1(Ot[rb], Dq[rb], Pq[p0 + rb]);
-            buffer_store<quad>(ors, ((16 * rb + r) * DV + 4 * g) * (int)sizeof(E), M::cvt(Ot[rb]));
+            buffer_store<quad>(ors, ((16 * rb + r) * (int)os + 4 * g) * (int)sizeof(E), M::cvt(Ot[rb]));
         });
         // S += K^T Delta (K^T blocks fetched down the columns of K)
 #pragma unroll
@@ -517,11 +539,13 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
 // ------------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------------
-template <typename E, int DK, int C>
-hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L, int gate, hipStream_t stream) {
+template <typename E, int DK, int C, bool VL>
+hipError_t launch_ut_vl(const void* k, const float* beta, void* tw, int BH, int L, int gate, const TokLayout& ly,
+                        hipStream_t stream) {
     static_assert(UtLayout<sizeof(E), DK, C>::BYTES <= kMaxLdsBytes, "UT kernel LDS too large");
     const int NC = (L + C - 1) / C;
-    const int64_t total = (int64_t)BH * NC;
+    // chunks of the workspace (with packed sequences an upper bound; the kernel reads the exact count)
+    const int64_t total = VL ? (int64_t)ly.H * (NC + ly.nseq) : (int64_t)BH * NC;
     if (total == 0) return hipSuccess;
     if constexpr (std::is_same<E, bf16>::value && DK >= 32) {
         // one wave per (batch*head, chunk) at a time; as many waves as the device holds at once
@@ -530,13 +554,13 @@ hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ut_wave_kernel<DK, C>),
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ut_wave_kernel<DK, C, VL>),
                                                               WPB * 64, 0);
         if (e != hipSuccess) return e;
         const int64_t resident = (int64_t)(cus < 1 ? 1 : cus) * (per_cu < 1 ? 1 : per_cu);
         const int64_t need = (total + WPB - 1) / WPB;
-        hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3((unsigned)(need < resident ? need : resident)), dim3(WPB * 64), 0,
-                           stream, static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, (int)total, gate);
+        hipLaunchKernelGGL((ut_wave_kernel<DK, C, VL>), dim3((unsigned)(need < resident ? need : resident)), dim3(WPB * 64), 0,
+                           stream, static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly);
         return hipGetLastError();
     }
     // as many workgroups as the device holds at once, each walking several pairs
@@ -544,14 +568,22 @@ hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ut_kernel<E, DK, C>),
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ut_kernel<E, DK, C, VL>),
                                                           C / 16 * 64, 0);
     if (e != hipSuccess) return e;
     const int64_t resident = (int64_t)(cus < 1 ? 1 : cus) * (per_cu < 1 ? 1 : per_cu);
     const int64_t grid = total < resident ? total : resident;
-    hipLaunchKernelGGL((ut_kernel<E, DK, C>), dim3((unsigned)grid), dim3(C / 16 * 64), 0, stream,
-                       static_cast<const E*>(k), beta, static_cast<E*>(tw), L, NC, (int)total, gate);
+    hipLaunchKernelGGL((ut_kernel<E, DK, C, VL>), dim3((unsigned)grid), dim3(C / 16 * 64), 0, stream,
+                       static_cast<const E*>(k), beta, static_cast<E*>(tw), L, NC, BH, gate, ly);
     return hipGetLastError();
+}
+
+template <typename E, int DK, int C>
+hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L, int gate, const TokLayout* lyp,
+                       hipStream_t stream) {
+    const TokLayout ly = lyp ? *lyp : contiguous_layout(1, L, DK, DK);   // contiguous: every (batch, head) is a "batch"
+    return ly.cu_seqlens ? launch_ut_vl<E, DK, C, true>(k, beta, tw, BH, L, gate, ly, stream)
+                         : launch_ut_vl<E, DK, C, false>(k, beta, tw, BH, L, gate, ly, stream);
 }
 
 template <typename E, int DK, int C, int DVS>
@@ -562,12 +594,13 @@ hipError_t launch_chain_t(const SplitArgs& a, hipStream_t stream) {
         return hipErrorInvalidConfiguration;
     } else {
         const ChainSeg sg = chain_seg(a, DK, C, DVS);
+        const TokLayout ly = a.layout ? *a.layout : contiguous_layout(1, a.L, DK, a.d_v);
         const int nslab = (a.d_v + (a.aug ? DK : 0)) / DVS;
         const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
         hipLaunchKernelGGL((chain_kernel<E, DK, C, DVS>), dim3((unsigned)grid, (unsigned)(a.nseg > 0 ? a.nseg : 1)),
                            dim3(DVS / 16 * 64), 0, stream, static_cast<const E*>(a.q), static_cast<const E*>(a.k),
                            static_cast<const E*>(a.v), static_cast<const E*>(a.tw), static_cast<E*>(a.o), a.s0, a.sf,
-                           a.BH, a.L, a.d_v, nslab, sg);
+                           a.BH, a.L, a.d_v, nslab, sg, ly);
         return hipGetLastError();
     }
 }
@@ -575,7 +608,7 @@ hipError_t launch_chain_t(const SplitArgs& a, hipStream_t stream) {
 template <typename E, int DK, int C>
 hipError_t launch_split_c(const SplitArgs& a, bool with_ut, hipStream_t s) {
     if (with_ut && a.L > 0) {
-        const hipError_t e = launch_ut_t<E, DK, C>(a.k, a.beta, a.tw, a.BH, a.L, a.gate, s);
+        const hipError_t e = launch_ut_t<E, DK, C>(a.k, a.beta, a.tw, a.BH, a.L, a.gate, a.layout, s);
         if (e != hipSuccess) return e;
     }
     switch (a.dvs) {
@@ -611,9 +644,9 @@ hipError_t launch_split_e(const SplitArgs& a, bool with_ut, hipStream_t s) {
 template <typename E, int DK>
 hipError_t launch_ut_dk(const void* k, const float* beta, void* tw, int BH, int L, int chunk, int gate, hipStream_t s) {
     switch (chunk) {
-        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, gate, s);
-        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, gate, s);
-        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, gate, s);
+        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, gate, nullptr, s);
+        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, gate, nullptr, s);
+        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, gate, nullptr, s);
     }
     return hipErrorInvalidValue;
 }

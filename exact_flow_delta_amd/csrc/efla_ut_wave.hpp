@@ -24,6 +24,7 @@
 #pragma once
 
 #include "efla_common.hpp"
+#include "efla_launch.hpp"
 #include "efla_ut.hpp"
 
 namespace efla {
@@ -41,10 +42,10 @@ struct UtWaveShape {
     static constexpr int WPB = 4;                     // waves per workgroup (the launch bounds assume 4)
 };
 
-template <int DK, int C>
+template <int DK, int C, bool VL>
 __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
-    const bf16* __restrict__ k, const float* __restrict__ beta, bf16* __restrict__ tw, int L, int NC, int total,
-    int gate) {
+    const bf16* __restrict__ k, const float* __restrict__ beta, bf16* __restrict__ tw, int L, int NC, int BH,
+    int gate, TokLayout ly) {
     typedef UtWaveShape<DK, C> SH;
     typedef Mma<bf16> M;
     typedef M::quad quad;
@@ -61,6 +62,7 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
     const int r = lane & 15;
     const int g = lane >> 4;
     const int stride = gridDim.x * SH::WPB;
+    const int total = ut_chunks<VL>(ly, BH, NC);
     int u = blockIdx.x * SH::WPB + w;
     if (u >= total) return;   // whole wave
     float* sAt = reinterpret_cast<float*>(smem + w * SH::BYTES + SH::OFF_AT);
@@ -77,19 +79,25 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
     auto load = [&](int uu) __attribute__((always_inline)) {
         const bool any = uu < total;
         if (!any) uu = 0;
-        const int bh = uu / NC;
-        const int t0 = (uu - bh * NC) * C;
-        const int n = !any ? 0 : (L - t0 < C) ? (L - t0) : C;   // valid rows; the rest read as zero keys and steps
-        const int64_t tok = (int64_t)bh * L + t0;
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + tok * DK, n * DK * 2);
+        int bh, c;
+        chunk_of<VL>(ly, uu, NC, bh, c);
+        const SeqView sv = seq_view_t<VL>(ly, bh, L, C);
+        const int t0 = c * C;
+        const int n = !any ? 0 : (sv.len - t0 < C) ? (sv.len - t0) : C;   // valid rows; the rest read as zeros
+        const int kt = (int)ly.k_t, bt = (int)ly.be_t;
+        // one range per row block (wave-uniform), so that the only per-lane offset is that of row r
+        const int lane_off = (r * kt + 8 * g) * 2;
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
+            const int nr = n - 16 * rb;   // valid rows of this block
+            const __amdgpu_buffer_rsrc_t rk =
+                buffer_rsrc(k + sv.k0 + (int64_t)(t0 + 16 * rb) * kt, nr > 0 ? ((nr - 1) * kt + DK) * 2 : 0);
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp)
-                kf[rb][kp] = __builtin_bit_cast(bx8, buffer_load<u32x4>(rk, ((16 * rb + r) * DK + 32 * kp + 8 * g) * 2));
+                kf[rb][kp] = __builtin_bit_cast(bx8, buffer_load<u32x4>(rk, lane_off + 64 * kp));
         }
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(beta + tok, n * 4);
-        beta_mine = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0));
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(beta + sv.be0 + (int64_t)t0 * bt, n > 0 ? ((n - 1) * bt + 1) * 4 : 0);
+        beta_mine = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * bt * 4, 0, 0));
     };
     load(u);
     for (; u < total; u += stride) {

@@ -6,7 +6,7 @@ seeded by ``SeedSequence([config_id, tensor_id, step, salt])``, stored as float3
 bfloat16 workloads -- rounded to bfloat16 with round-to-nearest-even before either side sees
 it, so that both sides read exactly the same values.
 
-Tensor ids: 0=q, 1=k, 2=v, 3=beta, 4=key scale / mask, 5=value noise, 6=initial state.
+Tensor ids: 0=q, 1=k, 2=v, 3=beta, 4=key scale / mask, 5=value noise, 6=initial state, 7=packed lengths.
 
 The five workloads (sizes, distributions) follow the targets this library is measured on:
   1 "tiny"          B1 H1 L256 d16 fp32, q,k,v ~ N(0,1), beta = sigmoid(N(0,1)), S0 = 0, chunk 16
@@ -30,7 +30,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-T_Q, T_K, T_V, T_BETA, T_SCALE, T_NOISE, T_S0 = range(7)
+T_Q, T_K, T_V, T_BETA, T_SCALE, T_NOISE, T_S0, T_LEN = range(8)
 
 
 @dataclass(frozen=True)
@@ -137,6 +137,30 @@ def make_fwd_inputs(w: Workload, salt: int = 0) -> dict:
     return dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype),
                 beta=beta.astype(np.float32),
                 initial_state=None if s0 is None else s0.astype(np.float32))
+
+
+def packed_lengths(cfg_id: int, n: int, mean: float, salt: int = 0) -> list:
+    """n sequence lengths of a packed batch: round(exp(N(log(mean) - 1/2, 1))), a log-normal mix of mean
+    about `mean` with many short and a few long sequences (zero lengths included when mean is small)."""
+    z = _rng(cfg_id, T_LEN, 0, salt).standard_normal(n)
+    return [int(x) for x in np.rint(np.exp(np.log(mean) - 0.5 + z))]
+
+
+def make_packed_inputs(w: Workload, lengths, salt: int = 0) -> dict:
+    """Packed sequences of workload w's distributions: q, k, v [1,H,T,d], beta [1,H,T] for T = sum(lengths)
+    tokens drawn as one sequence of w, cu_seqlens [N+1] int32, and per-sequence initial states
+    [N,H,d_k,d_v] = 0.1 N(0,1) (or None when w has none)."""
+    lengths = [int(n) for n in lengths]
+    T = int(sum(lengths))
+    x = make_fwd_inputs(replace(w, B=1, L=T), salt)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    s0 = None
+    if x["initial_state"] is not None:
+        s0 = (0.1 * _rng(w.cfg_id, T_S0, 1, salt).standard_normal((len(lengths), w.H, w.d_k, w.d_v))).astype(np.float32)
+    x["initial_state"] = s0
+    x["cu_seqlens"] = cu
+    return x
 
 
 def make_decode_state(w: Workload, salt: int = 0) -> np.ndarray:

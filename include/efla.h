@@ -19,6 +19,7 @@
  *     take a caller-owned workspace and say how large it must be.
  *   - Layouts are contiguous row-major.  q, k: [B,H,L,d_k]; v, o: [B,H,L,d_v]; beta: [B,H,L];
  *     state: [B,H,d_k,d_v] (S as the update writes it: row i is key dimension i).
+ *     efla_chunk_fwd_layout also takes strided views and packed sequences (efla_layout).
  *   - q, k, v, o use the storage type `dtype` (fp32 or bf16).  beta, alpha and the state are fp32.
  *     Arithmetic is fp32 (bf16 operands are multiplied on bf16 matrix cores with fp32 accumulation).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work and returns;
@@ -243,6 +244,55 @@ efla_status efla_chunk_fwd_scan(const void* q, const void* k, const void* v, con
  * segment, state slab width and workspace bytes.  Errors as efla_chunk_fwd_scan would return for the sizes. */
 efla_status efla_chunk_scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int segments,
                                  int* nseg, int* seg_chunks, int* slab_width, size_t* workspace_bytes);
+
+/*
+ * Token layouts of efla_chunk_fwd_layout.  The pages place the method as a drop-in replacement inside
+ * existing chunked delta-rule pipelines ("Error-Free Linear Attention guida completa" (mauroscia.it),
+ * section "Chunkwise parallelism"), so the forward reads the tensors as a model layer holds them instead of
+ * requiring transposed copies.
+ *
+ * Every stride counts elements (not bytes).  Element (b, h, t, i) of q is q[b*q[0] + h*q[1] + t*q[2] + i]
+ * (feature index i contiguous); likewise k, v and o; beta(b, h, t) = beta[b*beta[0] + h*beta[1] + t*beta[2]].
+ * [B,H,L,d] contiguous is {H*L*d, L*d, d}; [B,L,H,d] is {L*H*d, d, H*d}.
+ *
+ * cu_seqlens (device memory, B + 1 int32, or NULL): packed sequences.  Then B counts sequences, L is the
+ * packed token count, sequence b is tokens [cu_seqlens[b], cu_seqlens[b+1]) of every head, the batch strides
+ * are ignored, and every sequence starts from its own initial state and ends in its own final state
+ * ([B,H,d_k,d_v]).  The offsets are read sanitised: each clamped to [0, L], then replaced by the largest of
+ * itself and the entries before it (so an out-of-order or out-of-range entry gives shorter or empty
+ * sequences, never overlapping ones nor an access outside [0, L)).  An empty sequence passes its initial
+ * state through.
+ */
+typedef struct efla_layout {
+    int64_t q[3], k[3], v[3], o[3]; /* batch, head, token strides */
+    int64_t beta[3];                /* batch, head, token strides */
+    const int32_t* cu_seqlens;      /* device, B + 1 entries, or NULL */
+} efla_layout;
+
+/*
+ * efla_chunk_fwd_layout -- efla_chunk_fwd_split_gate / efla_chunk_fwd_scan over tensors in the layout
+ * described by `layout` (NULL: contiguous [B,H,L,d]).  Same operator, gate, states, aliasing rules and
+ * errors, plus:
+ *   strides    all >= 0; those of q, k, v, o multiples of 16 bytes / element size (8 for bf16, 4 for fp32);
+ *              token strides at least the row (d_k for q and k, d_v for v) and 1 for beta, and below
+ *              2^31 / (64 * element size); the rows of o must not overlap one another (sorted by stride,
+ *              each stride at least the extent of the dimensions inside it); else EFLA_ERR_INVALID_ARG.
+ *              Overlap checks between arguments use each tensor's address extent.
+ *   segments   as efla_chunk_fwd_scan (0 = the library's choice); with cu_seqlens only 0 or 1 (one segment).
+ *   workspace  device memory of at least efla_chunk_layout_plan(...)'s workspace_bytes, 256-byte aligned,
+ *              overlapping no other argument.  With cu_seqlens it holds the sanitised token offsets and the
+ *              sequences' chunk offsets (made on `stream` by this call), then the UT output of
+ *              sum_b ceil(len_b / chunk) chunks per head.
+ */
+efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, const float* beta,
+                                  efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                  int B, int H, int L, int d_k, int d_v, int chunk, int segments, int gate,
+                                  const efla_layout* layout, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Segments used and workspace bytes of efla_chunk_fwd_layout for these sizes (host only); varlen != 0 when
+ * cu_seqlens will be given.  Errors as efla_chunk_fwd_layout would return for the sizes. */
+efla_status efla_chunk_layout_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int varlen,
+                                   int segments, int* nseg, size_t* workspace_bytes);
 
 /* Like efla_chunk_fwd_plan, for the state-pass launch of efla_chunk_fwd_split / efla_chunk_state_pass. */
 efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,

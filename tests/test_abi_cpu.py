@@ -298,3 +298,87 @@ def test_scan_argument_errors(lib):
 def test_scan_reaches_the_device_check(lib):
     assert _scan_call(lib) == NO_DEVICE
     assert _scan_call(lib, seg=0, s0=P(6)) == NO_DEVICE      # in-place state passing
+
+
+def test_layout_plan(lib):
+    # fixed-length sequences: the scan plan (split workspace and one segment when heads are many)
+    assert efla.layout_plan(8, 16, 4096, 128, 128, 64, torch.bfloat16) == (1, 41943040)
+    assert efla.layout_plan(1, 16, 65536, 128, 128, 64, torch.bfloat16) == (8, 109051904)
+    assert efla.layout_plan(1, 16, 65536, 128, 128, 64, torch.bfloat16, segments=1) == (1, 16 * 1024 * 10 * 512)
+    # packed sequences: 256-byte-rounded chunk offsets, then H * (ceil(T / C) + N) chunks of UT output
+    ns, nb = efla.layout_plan(5, 3, 1000, 64, 64, 32, torch.float32, varlen=True)
+    assert ns == 1
+    assert nb == 256 + 3 * (32 + 5) * 3 * 256 * 4   # 2 x 6 offsets fit in 256 bytes
+    n, b = ctypes.c_int(), ctypes.c_size_t()
+    assert lib.efla_chunk_layout_plan(5, 3, 1000, 64, 64, 32, F32, 1, 2, ctypes.byref(n), ctypes.byref(b)) == UNSUPPORTED
+    assert lib.efla_chunk_layout_plan(5, 3, 1000, 64, 64, 32, F32, 1, -1, ctypes.byref(n), ctypes.byref(b)) == INVALID
+    assert lib.efla_chunk_layout_plan(5, 3, 1000, 96, 64, 32, F32, 0, 0, ctypes.byref(n), ctypes.byref(b)) == UNSUPPORTED
+
+
+def _bthd(B, H, L, dk, dv):
+    """efla_layout of [B,L,H,d] tensors (beta [B,L,H])."""
+    lay = efla.Layout()
+    lay.q[:] = [L * H * dk, dk, H * dk]
+    lay.k[:] = [L * H * dk, dk, H * dk]
+    lay.v[:] = [L * H * dv, dv, H * dv]
+    lay.o[:] = [L * H * dv, dv, H * dv]
+    lay.beta[:] = [L * H, 1, H]
+    return lay
+
+
+def _layout_call(lib, lay, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=BF16, o=P(5), s0=None, sf=P(6), B=2, H=4, L=1000, dk=64, dv=64,
+             C=64, seg=0, gate=0, ws=P(7), wsb=1 << 30)
+    a.update(kw)
+    return lib.efla_chunk_fwd_layout(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["o"], a["s0"], a["sf"], a["B"],
+                                     a["H"], a["L"], a["dk"], a["dv"], a["C"], a["seg"], a["gate"],
+                                     None if lay is None else ctypes.byref(lay), a["ws"], a["wsb"], None)
+
+
+def test_layout_argument_errors(lib):
+    lay = _bthd(2, 4, 1000, 64, 64)
+    assert _layout_call(lib, lay, ws=None) == WORKSPACE
+    assert _layout_call(lib, lay, gate=-1) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.q[2] = 4 * 64 + 4            # rows not 16-byte aligned in bf16
+    assert _layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.k[1] = -64
+    assert _layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.k[2] = 0                     # every token of k on one row: rows past a sequence's end would not read 0
+    assert _layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.beta[2] = 0
+    assert _layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.o[2] = 32                    # rows of o overlap one another
+    assert _layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.o[:] = [1000 * 4 * 64, 64, 64 * 2]   # heads and tokens interleave onto the same rows
+    assert _layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.v[2] = 1 << 28               # token stride beyond the 32-bit in-chunk offsets
+    assert _layout_call(lib, bad) == INVALID
+    # o inside q's extent (q spans 2 * 1000 * 4 * 64 bf16 elements)
+    assert _layout_call(lib, lay, o=ctypes.c_void_p(0x7F0100000000 + 4096)) == INVALID
+    # packed sequences: more than one segment is not built; cu_seqlens inside o
+    cu = _bthd(1, 4, 1000, 64, 64)
+    cu.cu_seqlens = 0x7F0800000000
+    assert _layout_call(lib, cu, seg=2) == UNSUPPORTED
+    cu.cu_seqlens = 0x7F0500000000 + 64
+    assert _layout_call(lib, cu) == INVALID
+    # nothing to do
+    assert _layout_call(lib, lay, B=0, ws=None, wsb=0) == OK
+    assert _layout_call(lib, lay, L=0, sf=None, q=None, k=None, v=None, beta=None, o=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_layout_reaches_the_device_check(lib):
+    assert _layout_call(lib, _bthd(2, 4, 1000, 64, 64)) == NO_DEVICE
+    assert _layout_call(lib, None) == NO_DEVICE
+    cu = _bthd(1, 4, 1000, 64, 64)
+    cu.cu_seqlens = 0x7F0800000000
+    assert _layout_call(lib, cu, B=7) == NO_DEVICE
+    # an empty packed batch still writes the final states (from the initial ones)
+    assert _layout_call(lib, cu, B=7, L=0, q=None, k=None, v=None, beta=None, o=None) == NO_DEVICE
