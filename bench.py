@@ -74,13 +74,15 @@ def decode_algorithmic(NH, dk, dv, esize=2):
 # hash to what was measured)
 TRAFFIC_KERNELS = {
     "chain_bf16_kernel<128,64,64>": {
-        "symbol": ["chain_bf16_kernelILi128ELi64ELi64E", "chain_bf16_kernel<128, 64, 64>"],
+        "symbol": ["chain_bf16_kernelILi128ELi64ELi64ELb1E", "chain_bf16_kernel<128, 64, 64, true>"],
         "sources": ["exact_flow_delta_amd/csrc/efla_chain_bf16.hpp", "exact_flow_delta_amd/csrc/efla_chunk_split.hpp",
-                    "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
+                    "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_launch.hpp",
+                    "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
     "ut_wave_kernel<128,64>": {
-        "symbol": ["ut_wave_kernelILi128ELi64E", "ut_wave_kernel<128, 64>"],
+        "symbol": ["ut_wave_kernelILi128ELi64ELb0E", "ut_wave_kernel<128, 64, false>"],
         "sources": ["exact_flow_delta_amd/csrc/efla_ut_wave.hpp", "exact_flow_delta_amd/csrc/efla_chunk_split.hpp",
-                    "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
+                    "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_launch.hpp",
+                    "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
     "recurrent_step_kernel<bf16,128,128>": {
         "symbol": ["recurrent_step_kernelIDF16bLi128ELi128E", "recurrent_step_kernel<__bf16, 128, 128>"],
         "sources": ["exact_flow_delta_amd/csrc/efla_recurrent.hip", "exact_flow_delta_amd/csrc/efla_common.hpp"]},

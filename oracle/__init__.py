@@ -56,6 +56,8 @@ class Oracle:
         lib.efla_oracle_ut.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.efla_oracle_ut.restype = ctypes.c_int
+        lib.efla_oracle_bwd.argtypes = [_dp] * 12 + [ctypes.c_int] * 7
+        lib.efla_oracle_bwd.restype = ctypes.c_int
         self.lib = lib
 
     def alpha(self, k, beta, gate=0):
@@ -88,6 +90,29 @@ class Oracle:
         used = self.lib.efla_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
                                         B, H, L, d_k, d_v, int(gate), int(n_threads))
         return o, sf, used
+
+    def bwd(self, q, k, v, beta, initial_state, d_o, d_final=None, n_threads=0, gate=0):
+        """Gradients of sum(o * d_o) + sum(S_L * d_final) with respect to q, k, v, beta and the initial state
+        (the adjoint of the token recurrence, see efla_oracle_bwd).
+
+        Returns (dq, dk, dv, dbeta, d_initial) as float64 arrays of the inputs' shapes ([B,H,d_k,d_v] for
+        d_initial, also when initial_state is None)."""
+        q, k, v, beta, d_o = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(d_o)
+        B, H, L, d_k = k.shape
+        d_v = v.shape[-1]
+        assert q.shape == k.shape and v.shape[:3] == (B, H, L) and beta.shape == (B, H, L)
+        assert d_o.shape == v.shape
+        s0 = None if initial_state is None else _f64(initial_state)
+        dsf = None if d_final is None else _f64(d_final)
+        for x in (s0, dsf):
+            assert x is None or x.shape == (B, H, d_k, d_v)
+        dq, dk = np.empty_like(q), np.empty_like(k)
+        dv, db = np.empty_like(v), np.empty_like(beta)
+        ds0 = np.empty((B, H, d_k, d_v), dtype=np.float64)
+        self.lib.efla_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(d_o), _ptr(dsf),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(ds0), B, H, L, d_k, d_v, int(gate),
+                                 int(n_threads))
+        return dq, dk, dv, db, ds0
 
     def ut(self, k, beta, chunk, n_threads=0, gate=0):
         """Intra-chunk transform T diag(alpha), T = (I + strict_lower(diag(alpha) K K^T))^{-1}, per chunk.
@@ -141,6 +166,10 @@ def fwd(q, k, v, beta, initial_state=None, n_threads=0, want_o=True, want_state=
 
 def step(q, k, v, beta, state, n_threads=0, gate=0):
     return default().step(q, k, v, beta, state, n_threads, gate)
+
+
+def bwd(q, k, v, beta, initial_state, d_o, d_final=None, n_threads=0, gate=0):
+    return default().bwd(q, k, v, beta, initial_state, d_o, d_final, n_threads, gate)
 
 
 def ut(k, beta, chunk, n_threads=0, gate=0):

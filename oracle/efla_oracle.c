@@ -266,3 +266,170 @@ int efla_oracle_ut(const double *k, const double *beta, double *tout, int B, int
     (void)nt;
     return used;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Gradients (reverse mode) of the token recurrence.  The pages train every model they report, but print
+ * no backward pass ("Exact Flow Linear Attention" (gist.science), Risultati Sperimentali item 4: training
+ * throughput matches DeltaNet; "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), the language
+ * modelling results at 340M and 1.3B parameters), so this is the adjoint of the forward above, derived term
+ * by term from the update as written:
+ *   S_t = S_{t-1} - alpha k a^T + alpha k v^T,  a = S_{t-1}^T k,   o_t = S_t^T q_t,
+ *   alpha = f(beta, lambda),  lambda = k^T k.
+ * Going backwards over the tokens with G = dLoss/dS_t (the gradient of the final state, or 0, at the end):
+ *   readout:  dq_t = S_t do_t;                      G += q_t do_t^T
+ *   update:   w = G^T k;  e = v - a
+ *             dv_t = alpha w;   da = -alpha w;   dalpha = w . e
+ *             dk_t = alpha G e + S_{t-1} da + 2 k dlambda,   dlambda = dalpha df/dlambda
+ *             dbeta_t = dalpha df/dbeta;   G <- G + k da^T   (the gradient of S_{t-1})
+ * and the gradient of the initial state is the G left after token 0.
+ * ------------------------------------------------------------------------------------------------ */
+
+/* d alpha / d beta and d alpha / d lambda of the gate.
+ * gate 0: alpha = (1 - e^{-x}) / lambda, x = beta lambda:  d/dbeta = e^{-x};
+ *         d/dlambda = beta^2 g(x),  g(x) = (x e^{-x} - (1 - e^{-x})) / x^2 = sum_{m>=2} (-1)^{m-1} (m-1)/m! x^{m-2}
+ *         (the series below x = 1/2, where the closed form cancels; g(0) = -1/2).
+ * gate p: the derivatives of sum_{n=1}^{p} (-1)^{n-1} beta^n lambda^{n-1} / n!, term by term. */
+static void oracle_alpha_grad(double beta, double lambda, int gate, double *da_dbeta, double *da_dlambda)
+{
+    if (gate > 0) {
+        double db = 0.0, dl = 0.0, nfact = 1.0;   /* n! */
+        for (int n = 1; n <= gate; ++n) {
+            nfact *= n;
+            const double sgn = (n & 1) ? 1.0 : -1.0;   /* (-1)^{n-1} */
+            db += sgn * n * pow(beta * lambda, n - 1) / nfact;
+            if (n >= 2)
+                dl += sgn * (n - 1) * pow(beta, n) * pow(lambda, n - 2) / nfact;
+        }
+        *da_dbeta = db;
+        *da_dlambda = dl;
+        return;
+    }
+    const double x = beta * lambda;
+    *da_dbeta = exp(-x);
+    double g;
+    if (x < 0.5) {
+        g = 0.0;
+        double xp = 1.0, factorial = 2.0;   /* x^{m-2}, m! */
+        for (int m = 2; m < 40; ++m) {
+            if (m > 2) {
+                xp *= x;
+                factorial *= m;
+            }
+            const double sign = (m % 2 == 1) ? 1.0 : -1.0;   /* (-1)^{m-1} */
+            g += sign * (m - 1) * xp / factorial;
+        }
+    } else {
+        g = (x * exp(-x) + expm1(-x)) / (x * x);
+    }
+    *da_dlambda = beta * beta * g;
+}
+
+/* Gradients of sum(o * d_o) + sum(S_L * d_final) with respect to q, k, v, beta and the initial state,
+ * for the recurrence of efla_oracle_fwd (same layouts; d_o [B,H,L,d_v]; d_final and d_initial
+ * [B,H,d_k,d_v]; initial_state, d_final may be NULL = 0; d_initial may be NULL = not written).
+ * Every state S_0 .. S_L of a (b, h) is kept (L + 1 blocks of d_k x d_v).  Returns the threads used. */
+int efla_oracle_bwd(const double *q, const double *k, const double *v, const double *beta,
+                    const double *initial_state, const double *d_o, const double *d_final,
+                    double *dq, double *dk, double *dv, double *dbeta, double *d_initial,
+                    int B, int H, int L, int d_k, int d_v, int gate, int n_threads)
+{
+    const int64_t BH = (int64_t)B * H;
+    const int nt = oracle_threads(n_threads);
+    int used = 1;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        const size_t ssz = (size_t)d_k * d_v;
+        double *Sall = (double *)malloc(sizeof(double) * ssz * (size_t)(L + 1));
+        double *G = (double *)malloc(sizeof(double) * ssz);
+        double *kS = (double *)malloc(sizeof(double) * (size_t)d_v);
+        double *w = (double *)malloc(sizeof(double) * (size_t)d_v);
+        double *e = (double *)malloc(sizeof(double) * (size_t)d_v);
+        double *da = (double *)malloc(sizeof(double) * (size_t)d_v);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t bh = 0; bh < BH; ++bh) {
+            /* forward, keeping every state */
+            if (initial_state)
+                memcpy(Sall, initial_state + bh * ssz, sizeof(double) * ssz);
+            else
+                memset(Sall, 0, sizeof(double) * ssz);
+            for (int t = 0; t < L; ++t) {
+                const int64_t tok = bh * L + t;
+                memcpy(Sall + (size_t)(t + 1) * ssz, Sall + (size_t)t * ssz, sizeof(double) * ssz);
+                oracle_token(Sall + (size_t)(t + 1) * ssz, q + tok * d_k, k + tok * d_k, v + tok * d_v, beta[tok],
+                             NULL, kS, d_k, d_v, gate);
+            }
+            /* backward */
+            if (d_final)
+                memcpy(G, d_final + bh * ssz, sizeof(double) * ssz);
+            else
+                memset(G, 0, sizeof(double) * ssz);
+            for (int t = L - 1; t >= 0; --t) {
+                const int64_t tok = bh * L + t;
+                const double *St = Sall + (size_t)(t + 1) * ssz;
+                const double *Sp = Sall + (size_t)t * ssz;
+                const double *qt = q + tok * d_k, *kt = k + tok * d_k, *vt = v + tok * d_v, *dot = d_o + tok * d_v;
+                /* readout o_t = S_t^T q_t */
+                for (int i = 0; i < d_k; ++i) {
+                    double s = 0.0;
+                    for (int j = 0; j < d_v; ++j)
+                        s += St[(size_t)i * d_v + j] * dot[j];
+                    dq[tok * d_k + i] = s;
+                }
+                for (int i = 0; i < d_k; ++i)
+                    for (int j = 0; j < d_v; ++j)
+                        G[(size_t)i * d_v + j] += qt[i] * dot[j];
+                /* update S_t = S_{t-1} - alpha k a^T + alpha k v^T */
+                double lambda = 0.0;
+                for (int i = 0; i < d_k; ++i)
+                    lambda += kt[i] * kt[i];
+                const double alpha = oracle_alpha_one(kt, beta[tok], d_k, gate);
+                for (int j = 0; j < d_v; ++j) {
+                    double a = 0.0, s = 0.0;
+                    for (int i = 0; i < d_k; ++i) {
+                        a += kt[i] * Sp[(size_t)i * d_v + j];
+                        s += G[(size_t)i * d_v + j] * kt[i];
+                    }
+                    e[j] = vt[j] - a;
+                    w[j] = s;
+                }
+                double dalpha = 0.0;
+                for (int j = 0; j < d_v; ++j) {
+                    dalpha += w[j] * e[j];
+                    dv[tok * d_v + j] = alpha * w[j];
+                    da[j] = -alpha * w[j];
+                }
+                double da_db, da_dl;
+                oracle_alpha_grad(beta[tok], lambda, gate, &da_db, &da_dl);
+                const double dlambda = dalpha * da_dl;
+                dbeta[tok] = dalpha * da_db;
+                for (int i = 0; i < d_k; ++i) {
+                    double s = 0.0;
+                    for (int j = 0; j < d_v; ++j)
+                        s += alpha * G[(size_t)i * d_v + j] * e[j] + Sp[(size_t)i * d_v + j] * da[j];
+                    dk[tok * d_k + i] = s + 2.0 * kt[i] * dlambda;
+                }
+                for (int i = 0; i < d_k; ++i)
+                    for (int j = 0; j < d_v; ++j)
+                        G[(size_t)i * d_v + j] += kt[i] * da[j];
+            }
+            if (d_initial)
+                memcpy(d_initial + bh * ssz, G, sizeof(double) * ssz);
+        }
+        free(Sall);
+        free(G);
+        free(kS);
+        free(w);
+        free(e);
+        free(da);
+    }
+    (void)nt;
+    return used;
+}

@@ -19,7 +19,11 @@ Sources of the pins:
   * the integrator family the exact flow closes ("Error-Free Linear Attention guida completa"
     (mauroscia.it), section on RK-infinity; howistudyai.com building blocks "Delta Rule" and
     "Runge-Kutta Methods"): a gate of order p must be one step of a textbook p-th order Runge-Kutta
-    method applied to the ODE itself, order 1 the delta rule, and high orders the exact flow.
+    method applied to the ODE itself, order 1 the delta rule, and high orders the exact flow;
+  * the gradients (the pages train their models but print no backward pass): central finite differences
+    of the pinned forward, a one-token closed form with the gate's derivatives d alpha / d beta = e^{-x},
+    d alpha / d lambda = -(alpha - beta e^{-x}) / lambda, linearity in the incoming gradients, and
+    chaining through the state gradient of a split sequence.
 """
 import json
 import os
@@ -470,11 +474,99 @@ def check_gate_chunk_identity(orc):
     np.testing.assert_allclose(S, Sf[0, 0], rtol=0, atol=1e-11)
 
 
+def _bwd_problem(rng, L=7, d_k=3, d_v=2, H=2):
+    """Tiny inputs with a zero key, small and large beta lambda, and a random initial state."""
+    k = np.stack([_mixed_keys(rng, L, d_k, 0.05, 3.0) for _ in range(H)])[None]
+    k[0, 0, 2] = 0.0
+    q = rng.standard_normal((1, H, L, d_k))
+    v = rng.standard_normal((1, H, L, d_v))
+    beta = rng.uniform(0.2, 0.9, (1, H, L))
+    s0 = 0.5 * rng.standard_normal((1, H, d_k, d_v))
+    do = rng.standard_normal((1, H, L, d_v))
+    dsf = rng.standard_normal((1, H, d_k, d_v))
+    return q, k, v, beta, s0, do, dsf
+
+
+def check_bwd_finite_differences(orc):
+    """Every gradient against central differences of the forward's loss sum(o * do) + sum(S_L * dS_L)."""
+    rng = np.random.default_rng(41)
+    for gate in (0, 3):
+        q, k, v, beta, s0, do, dsf = _bwd_problem(rng)
+        x = dict(q=q, k=k, v=v, beta=beta, s0=s0)
+
+        def loss(xx):
+            o, S, _ = orc.fwd(xx["q"], xx["k"], xx["v"], xx["beta"], xx["s0"], n_threads=1, gate=gate)
+            return float(np.sum(o * do) + np.sum(S * dsf))
+
+        g = dict(zip(("q", "k", "v", "beta", "s0"), orc.bwd(q, k, v, beta, s0, do, dsf, gate=gate)))
+        for name, arr in x.items():
+            fd = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                h = 1e-6 * max(1.0, abs(arr[idx]))
+                xp = {n: a.copy() for n, a in x.items()}
+                xm = {n: a.copy() for n, a in x.items()}
+                xp[name][idx] += h
+                xm[name][idx] -= h
+                fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+            scale = max(1.0, np.abs(fd).max())
+            assert np.abs(g[name] - fd).max() <= 2e-7 * scale, (gate, name, np.abs(g[name] - fd).max())
+
+
+def check_bwd_one_token(orc):
+    """One token from S_0 = 0: o = alpha (k.q) v, so every gradient has a closed form."""
+    rng = np.random.default_rng(42)
+    for kscale in (0.1, 1.0, 3.0):
+        d_k, d_v = 4, 3
+        k = kscale * rng.standard_normal(d_k)
+        q, v, do = rng.standard_normal(d_k), rng.standard_normal(d_v), rng.standard_normal(d_v)
+        beta = 0.7
+        lam = k @ k
+        ex = np.exp(-beta * lam)
+        a = (1 - ex) / lam
+        da_db, da_dl = ex, -(a - beta * ex) / lam
+        kq, vdo = k @ q, v @ do
+        dq, dk, dv, db, ds0 = orc.bwd(q.reshape(1, 1, 1, d_k), k.reshape(1, 1, 1, d_k), v.reshape(1, 1, 1, d_v),
+                                      np.array([[[beta]]]), None, do.reshape(1, 1, 1, d_v))
+        np.testing.assert_allclose(dq[0, 0, 0], a * vdo * k, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dv[0, 0, 0], a * kq * do, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(db[0, 0, 0], kq * vdo * da_db, rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(dk[0, 0, 0], a * vdo * q + kq * vdo * 2 * k * da_dl, rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(ds0[0, 0], np.outer(q - a * kq * k, do), rtol=1e-12, atol=1e-13)
+
+
+def check_bwd_linearity(orc):
+    """The gradients are linear in the incoming gradients (do, dS_L)."""
+    rng = np.random.default_rng(43)
+    q, k, v, beta, s0, do1, ds1 = _bwd_problem(rng)
+    do2, ds2 = rng.standard_normal(do1.shape), rng.standard_normal(ds1.shape)
+    g1 = orc.bwd(q, k, v, beta, s0, do1, ds1)
+    g2 = orc.bwd(q, k, v, beta, s0, do2, ds2)
+    g3 = orc.bwd(q, k, v, beta, s0, 2 * do1 - 3 * do2, 2 * ds1 - 3 * ds2)
+    for a1, a2, a3 in zip(g1, g2, g3):
+        np.testing.assert_allclose(a3, 2 * a1 - 3 * a2, rtol=1e-10, atol=1e-11)
+
+
+def check_bwd_state_chaining(orc):
+    """Gradients over [0, L) equal those of the second half (from the first half's final state) followed by
+    the first half with the second half's initial-state gradient as its final-state gradient."""
+    rng = np.random.default_rng(44)
+    q, k, v, beta, s0, do, dsf = _bwd_problem(rng, L=10)
+    full = orc.bwd(q, k, v, beta, s0, do, dsf)
+    m = 4
+    _, Sm, _ = orc.fwd(q[:, :, :m], k[:, :, :m], v[:, :, :m], beta[:, :, :m], s0)
+    second = orc.bwd(q[:, :, m:], k[:, :, m:], v[:, :, m:], beta[:, :, m:], Sm, do[:, :, m:], dsf)
+    first = orc.bwd(q[:, :, :m], k[:, :, :m], v[:, :, :m], beta[:, :, :m], s0, do[:, :, :m], second[4])
+    for i in range(4):
+        np.testing.assert_allclose(full[i], np.concatenate([first[i], second[i]], axis=2), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(full[4], first[4], rtol=1e-11, atol=1e-12)
+
+
 PINS = [check_worked_example, check_expm_erase, check_van_loan, check_rk4_sequence, check_alpha_extremes,
         check_euler_limit, check_directional_decay, check_stiff_overwrite, check_contractive,
         check_linearity, check_chunk_identity, check_state_chaining, check_zero_initial_state,
         check_ut_chunk_identity, check_ut_orthogonal_keys, check_gate_rk_tableaus, check_gate_limits,
-        check_gate_chunk_identity]
+        check_gate_chunk_identity, check_bwd_one_token, check_bwd_state_chaining, check_bwd_linearity,
+        check_bwd_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -549,6 +641,18 @@ MUTANTS = {
     "rk_factorial": ("factorial *= n;", "factorial *= (n > 1 ? n - 1 : 1);"),
     "rk_lambda_power": ("pow(lambda, n - 1)", "pow(lambda, n)"),
     "gate_ignored": ("    if (gate > 0)\n        return oracle_alpha_rk(beta, lambda, gate);\n", ""),
+    "bwd_da_sign": ("da[j] = -alpha * w[j];", "da[j] = alpha * w[j];"),
+    "bwd_state_grad_dropped": ("G[(size_t)i * d_v + j] += kt[i] * da[j];", ";"),
+    "bwd_lambda_factor": ("dk[tok * d_k + i] = s + 2.0 * kt[i] * dlambda;", "dk[tok * d_k + i] = s + kt[i] * dlambda;"),
+    "bwd_readout_previous_state": ("s += St[(size_t)i * d_v + j] * dot[j];", "s += Sp[(size_t)i * d_v + j] * dot[j];"),
+    "bwd_dalpha_without_erase": ("dalpha += w[j] * e[j];", "dalpha += w[j] * vt[j];"),
+    "bwd_dbeta_without_decay": ("*da_dbeta = exp(-x);", "*da_dbeta = 1.0;"),
+    "bwd_series_sign": ("const double sign = (m % 2 == 1) ? 1.0 : -1.0;", "const double sign = (m % 2 == 0) ? 1.0 : -1.0;"),
+    "bwd_closed_form_sign": ("g = (x * exp(-x) + expm1(-x)) / (x * x);", "g = (x * exp(-x) - expm1(-x)) / (x * x);"),
+    "bwd_rk_lambda_power": ("pow(beta, n) * pow(lambda, n - 2)", "pow(beta, n) * pow(lambda, n - 1)"),
+    "bwd_direct_dk_dropped": ("s += alpha * G[(size_t)i * d_v + j] * e[j] + Sp[(size_t)i * d_v + j] * da[j];",
+                              "s += Sp[(size_t)i * d_v + j] * da[j];"),
+    "bwd_readout_state_grad_dropped": ("G[(size_t)i * d_v + j] += qt[i] * dot[j];", ";"),
 }
 
 
@@ -566,12 +670,13 @@ def test_pins_catch_mutants(name):
         lib = oracle.build(force=True, src=mpath, out=os.path.join(tmp, "libmutant.so"))
         orc = oracle.Oracle(lib)
         failed = []
-        for pin in PINS:
+        for pin in PINS:   # the first pin that fails is enough
             try:
                 with np.errstate(all="ignore"):
                     pin(orc)
             except AssertionError:
                 failed.append(pin.__name__)
+                break
         assert failed, "no pin detects mutant " + name
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
