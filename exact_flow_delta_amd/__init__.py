@@ -11,6 +11,8 @@ library is missing, every call raises.
     t    = ut_transform(k, beta, chunk_size=64)          # T diag(alpha) per chunk (operand layout)
 
     o, S = chunk_fwd_layout(q, k, v, beta, cu_seqlens=None)   # strided [B,H,L,d] views, packed sequences
+    dq, dk, dv, dbeta, dS0 = chunk_bwd(q, k, v, beta, d_o, initial_state=None, d_final=None)
+    o, S = efla_attention(q, k, v, beta, initial_state=None)   # differentiable (torch.autograd)
 
 chunk_fwd runs the two-launch form by default (UT transform of all chunks into a workspace, then the
 state pass); method="fused" runs the single-kernel form, which needs no workspace; method="scan" cuts long
@@ -34,7 +36,8 @@ import os
 
 import torch
 
-__all__ = ["EflaError", "alpha", "chunk_fwd", "chunk_fwd_layout", "layout_plan", "recurrent_step", "chunk_plan",
+__all__ = ["EflaError", "alpha", "chunk_fwd", "chunk_fwd_layout", "layout_plan", "chunk_bwd", "chunk_bwd_workspace_size",
+           "efla_attention", "recurrent_step", "chunk_plan",
            "chunk_workspace_size", "ut_transform", "state_pass", "scan_plan", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +110,9 @@ def load_library():
                                           _i32, _i32, _i32, ctypes.POINTER(Layout), _vp, _sz, _vp]
     lib.efla_chunk_layout_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
+    lib.efla_chunk_bwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                   _i32, _i32, _i32, _i32, _vp, _sz, _vp]
+    lib.efla_chunk_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
     lib.efla_chunk_state_pass.argtypes = [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
@@ -362,6 +368,78 @@ def chunk_fwd_layout(q, k, v, beta, cu_seqlens=None, initial_state=None, output_
                                      workspace.numel() * workspace.element_size(), _stream(v.device)),
            "efla_chunk_fwd_layout")
     return out, final_state
+
+
+def chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace chunk_bwd needs (host only)."""
+    lib = load_library()
+    n = _sz()
+    _check(lib.efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, _dtype_of(dtype), ctypes.byref(n)),
+           "efla_chunk_bwd_workspace_size")
+    return n.value
+
+
+def chunk_bwd(q, k, v, beta, d_o, initial_state=None, d_final=None, chunk_size=64, gate=GATE_EXACT,
+              want_initial_grad=True, workspace=None):
+    """Gradients of the chunked forward (efla_chunk_bwd): given d_o [B,H,L,d_v] (dLoss/do) and d_final
+    [B,H,d_k,d_v] (dLoss/dS_L, None = 0), returns (dq, dk, dv in the input dtype, dbeta fp32, d_initial fp32
+    [B,H,d_k,d_v] or None)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("d_o", d_o)):
+        _dev_tensor(t, name)
+    if not (q.dtype == k.dtype == v.dtype == d_o.dtype):
+        raise TypeError("q, k, v, d_o must share a dtype")
+    B, H, L, d_k = k.shape
+    d_v = v.shape[-1]
+    if tuple(q.shape) != (B, H, L, d_k) or tuple(v.shape[:3]) != (B, H, L) or d_o.shape != v.shape:
+        raise ValueError("q, k, v, d_o shapes disagree")
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, L):
+        raise ValueError("beta must be float32 [B,H,L]")
+    for name, x in (("initial_state", initial_state), ("d_final", d_final)):
+        if x is not None:
+            _dev_tensor(x, name)
+            if x.dtype != torch.float32 or tuple(x.shape) != (B, H, d_k, d_v):
+                raise ValueError("%s must be float32 [B,H,d_k,d_v]" % name)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbeta = torch.empty_like(beta)
+    d_init = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=v.device) if want_initial_grad else None
+    need = chunk_bwd_workspace_size(B, H, L, d_k, d_v, int(chunk_size), v.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+    _dev_tensor(workspace, "workspace")
+    _check(lib.efla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(initial_state), _ptr(d_o),
+                              _ptr(d_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(d_init), B, H, L, d_k, d_v,
+                              int(chunk_size), int(gate), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(v.device)), "efla_chunk_bwd")
+    return dq, dk, dv, dbeta, d_init
+
+
+class _EflaFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, beta, initial_state, chunk_size, gate):
+        q, k, v, beta = (x.contiguous() for x in (q, k, v, beta))
+        s0 = None if initial_state is None else initial_state.contiguous()
+        o, sf = chunk_fwd(q, k, v, beta, initial_state=s0, chunk_size=chunk_size, method="split", gate=gate)
+        ctx.save_for_backward(q, k, v, beta, s0 if s0 is not None else torch.empty(0, device=v.device))
+        ctx.has_s0 = s0 is not None
+        ctx.chunk_size, ctx.gate = chunk_size, gate
+        return o, sf
+
+    @staticmethod
+    def backward(ctx, d_o, d_final):
+        q, k, v, beta, s0 = ctx.saved_tensors
+        s0 = s0 if ctx.has_s0 else None
+        d_o = torch.zeros_like(v) if d_o is None else d_o.contiguous().to(v.dtype)
+        d_final = None if d_final is None else d_final.contiguous().float()
+        dq, dk, dv, dbeta, ds0 = chunk_bwd(q, k, v, beta, d_o, initial_state=s0, d_final=d_final,
+                                           chunk_size=ctx.chunk_size, gate=ctx.gate, want_initial_grad=ctx.has_s0)
+        return dq, dk, dv, dbeta, ds0, None, None
+
+
+def efla_attention(q, k, v, beta, initial_state=None, chunk_size=64, gate=GATE_EXACT):
+    """The chunked forward as a differentiable torch op: returns (o, final state); gradients flow to q, k, v,
+    beta and initial_state through chunk_bwd."""
+    return _EflaFunction.apply(q, k, v, beta, initial_state, int(chunk_size), int(gate))
 
 
 def scan_plan(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, segments=0):

@@ -20,7 +20,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libefla.so")
 
 SOURCES = ["efla_api.hip", "efla_alpha.hip", "efla_recurrent.hip", "efla_chunk_f32.hip", "efla_chunk_bf16.hip",
-           "efla_split_f32.hip", "efla_split_bf16.hip", "efla_seg_scan.hip", "efla_varlen.hip"]
+           "efla_split_f32.hip", "efla_split_bf16.hip", "efla_seg_scan.hip", "efla_varlen.hip",
+           "efla_bwd_f32.hip", "efla_bwd_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

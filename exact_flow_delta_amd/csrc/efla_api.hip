@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "efla.h"
+#include "efla_bwd.hpp"
 #include "efla_chunk_fwd.hpp"
 #include "efla_chunk_split.hpp"
 #include "efla_launch.hpp"
@@ -207,7 +208,7 @@ int64_t chunk_grid(int BH, int d_v, int dvs) { return (int64_t)((BH + 7) / 8) * 
 
 extern "C" {
 
-int efla_version(void) { return 10300; }
+int efla_version(void) { return 10400; }
 
 const char* efla_status_string(efla_status s) {
     switch (s) {
@@ -596,6 +597,93 @@ efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, c
     a.layout = &ly;
     if (e == hipSuccess) e = run_fwd(dtype == EFLA_BF16, a, lp.sp, ws, s);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_layout launch");
+}
+
+namespace {
+
+// Workspace of efla_chunk_bwd: the UT output (Ta), then the state entering and the gradient of the state
+// leaving every chunk (fp32, d_k x d_v each), each part 256-byte aligned.
+struct BwdPlan {
+    size_t off_s, off_ds, total;
+};
+
+efla_status bwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, BwdPlan* p) {
+    if (!valid_dtype(dt) || B < 0 || H < 0 || L < 0) return EFLA_ERR_INVALID_ARG;
+    if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    const int64_t NC = (L + chunk - 1) / chunk;
+    if (BH > INT32_MAX || BH * NC > INT32_MAX || BH * (d_v / 16) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    const size_t states = round_up_256((size_t)BH * NC * d_k * d_v * 4);
+    p->off_s = round_up_256(ut_bytes(BH, L, chunk, dt));
+    p->off_ds = p->off_s + states;
+    p->total = p->off_ds + states;
+    return EFLA_OK;
+}
+
+}  // namespace
+
+efla_status efla_chunk_bwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                          size_t* bytes) {
+    BwdPlan p;
+    const efla_status st = bwd_plan(B, H, L, d_k, d_v, chunk, dtype, &p);
+    if (st != EFLA_OK) return st;
+    if (!bytes) return EFLA_ERR_INVALID_ARG;
+    *bytes = p.total;
+    return EFLA_OK;
+}
+
+efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                           const float* initial_state, const void* d_o, const float* d_final, void* dq, void* dk,
+                           void* dv, float* dbeta, float* d_initial, int B, int H, int L, int d_k, int d_v,
+                           int chunk, int gate, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
+    BwdPlan p;
+    efla_status st = bwd_plan(B, H, L, d_k, d_v, chunk, dtype, &p);
+    if (st != EFLA_OK) return st;
+    const int64_t BH = (int64_t)B * H;
+    const size_t es = esize(dtype);
+    const size_t nq = (size_t)BH * L * d_k * es, nv = (size_t)BH * L * d_v * es, nb = (size_t)BH * L * 4;
+    const size_t ns = (size_t)BH * d_k * d_v * 4;
+    if (L > 0 && BH > 0) {
+        if (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta) return EFLA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) || !aligned(dq, 16) ||
+            !aligned(dk, 16) || !aligned(dv, 16) || !aligned(beta, 4) || !aligned(dbeta, 4))
+            return EFLA_ERR_INVALID_ARG;
+    }
+    if ((initial_state && !aligned(initial_state, 16)) || (d_final && !aligned(d_final, 16)) ||
+        (d_initial && !aligned(d_initial, 16)))
+        return EFLA_ERR_INVALID_ARG;
+    // outputs overlap nothing (inputs, one another, the workspace)
+    const void* in[7] = {q, k, v, beta, initial_state, d_o, d_final};
+    const size_t in_n[7] = {nq, nq, nv, nb, ns, nv, ns};
+    const void* out[5] = {dq, dk, dv, dbeta, d_initial};
+    const size_t out_n[5] = {nq, nq, nv, nb, ns};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlap(out[i], out_n[i], in[j], in_n[j])) return EFLA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(out[i], out_n[i], out[j], out_n[j])) return EFLA_ERR_INVALID_ARG;
+    }
+    if (BH == 0) return EFLA_OK;
+    if (L == 0 && !d_initial) return EFLA_OK;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total) return EFLA_ERR_WORKSPACE;
+    for (int j = 0; j < 7; ++j)
+        if (overlap(workspace, p.total, in[j], in_n[j])) return EFLA_ERR_INVALID_ARG;
+    for (int j = 0; j < 5; ++j)
+        if (overlap(workspace, p.total, out[j], out_n[j])) return EFLA_ERR_INVALID_ARG;
+    st = device_present();
+    if (st != EFLA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = static_cast<char*>(workspace);
+    const bool bf = dtype == EFLA_BF16;
+    hipError_t e = hipSuccess;
+    if (L > 0)
+        e = bf ? efla::launch_ut_bf16(k, beta, ws, (int)BH, L, d_k, chunk, gate, s)
+               : efla::launch_ut_f32(k, beta, ws, (int)BH, L, d_k, chunk, gate, s);
+    efla::BwdArgs a{q, k, v, beta, initial_state, d_o, d_final, dq, dk, dv, dbeta, d_initial, (int)BH, L, d_k, d_v,
+                    chunk, gate, ws, reinterpret_cast<float*>(ws + p.off_s), reinterpret_cast<float*>(ws + p.off_ds)};
+    if (e == hipSuccess) e = bf ? efla::launch_bwd_bf16(a, s) : efla::launch_bwd_f32(a, s);
+    return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_bwd launch");
 }
 
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype, void* o,

@@ -88,6 +88,47 @@ __device__ __forceinline__ float gate_alpha(float beta, float lambda, int gate) 
     return beta * s;
 }
 
+// Derivatives of the gate for the backward pass: *da_db = d alpha / d beta, *da_dl = d alpha / d lambda.
+// Writing alpha = beta phi(y), y = beta lambda:  d/dbeta = phi(y) + y phi'(y),  d/dlambda = beta^2 phi'(y).
+//   gate 0: phi(y) = (1 - e^{-y}) / y, so d/dbeta = e^{-y} and phi'(y) = (y e^{-y} - (1 - e^{-y})) / y^2,
+//           taken from its series sum_{n>=0} (-1)^{n+1} (n+1)/(n+2)! y^n below y = 1/2 (the closed form
+//           cancels there), phi'(0) = -1/2.
+//   gate p: phi(y) = sum_{n=0}^{p-1} (-y)^n / (n+1)!, differentiated term by term.
+__device__ __forceinline__ void gate_alpha_grad(float beta, float lambda, int gate, float* da_db, float* da_dl) {
+    const float y = beta * lambda;
+    float dphi;
+    if (gate == 0) {
+        *da_db = expf(-y);
+        if (y < 0.5f) {
+            // Horner over n = 10 .. 0 of c_n y^n, c_n = (-1)^{n+1} (n+1) / (n+2)!
+            float f = 1.0f;   // 1/(n+2)!, built for n = 10 first
+            for (int m = 3; m <= 12; ++m) f /= (float)m;   // 1/12! * 2
+            f *= 0.5f;
+            float acc = 0.0f;
+            for (int n = 10; n >= 0; --n) {
+                const float c = ((n & 1) ? 1.0f : -1.0f) * (float)(n + 1) * f;
+                acc = acc * y + c;
+                f *= (float)(n + 2);   // 1/(n+1)!
+            }
+            dphi = acc;
+        } else {
+            dphi = (y * expf(-y) + expm1f(-y)) / (y * y);
+        }
+    } else {
+        float phi = 0.0f, d = 0.0f, yn = 1.0f, fact = 1.0f;   // y^n, (n+1)!
+        for (int n = 0; n < gate; ++n) {
+            fact *= (float)(n + 1);
+            const float sgn = (n & 1) ? -1.0f : 1.0f;
+            phi += sgn * yn / fact;
+            if (n + 1 < gate) d += -sgn * (float)(n + 1) * yn / (fact * (float)(n + 2));   // term n+1
+            yn *= y;
+        }
+        dphi = d;
+        *da_db = phi + y * dphi;
+    }
+    *da_dl = beta * beta * dphi;
+}
+
 // ------------------------------------------------------------------------------------------------
 // element conversion
 // ------------------------------------------------------------------------------------------------

@@ -6,7 +6,8 @@ seeded by ``SeedSequence([config_id, tensor_id, step, salt])``, stored as float3
 bfloat16 workloads -- rounded to bfloat16 with round-to-nearest-even before either side sees
 it, so that both sides read exactly the same values.
 
-Tensor ids: 0=q, 1=k, 2=v, 3=beta, 4=key scale / mask, 5=value noise, 6=initial state, 7=packed lengths.
+Tensor ids: 0=q, 1=k, 2=v, 3=beta, 4=key scale / mask, 5=value noise, 6=initial state, 7=packed lengths,
+8=output gradient, 9=final-state gradient.
 
 The five workloads (sizes, distributions) follow the targets this library is measured on:
   1 "tiny"          B1 H1 L256 d16 fp32, q,k,v ~ N(0,1), beta = sigmoid(N(0,1)), S0 = 0, chunk 16
@@ -30,7 +31,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-T_Q, T_K, T_V, T_BETA, T_SCALE, T_NOISE, T_S0, T_LEN = range(8)
+T_Q, T_K, T_V, T_BETA, T_SCALE, T_NOISE, T_S0, T_LEN, T_DO, T_DSF = range(10)
 
 
 @dataclass(frozen=True)
@@ -161,6 +162,14 @@ def make_packed_inputs(w: Workload, lengths, salt: int = 0) -> dict:
     x["initial_state"] = s0
     x["cu_seqlens"] = cu
     return x
+
+
+def make_grads(w: Workload, salt: int = 0) -> dict:
+    """Incoming gradients of a backward pass: d_o [B,H,L,d_v] ~ N(0,1) in w's storage type and d_final
+    [B,H,d_k,d_v] ~ 0.1 N(0,1) fp32."""
+    d_o = _rng(w.cfg_id, T_DO, 0, salt).standard_normal((w.B, w.H, w.L, w.d_v))
+    dsf = 0.1 * _rng(w.cfg_id, T_DSF, 0, salt).standard_normal((w.B, w.H, w.d_k, w.d_v))
+    return dict(d_o=_store(d_o, w.dtype), d_final=dsf.astype(np.float32))
 
 
 def make_decode_state(w: Workload, salt: int = 0) -> np.ndarray:

@@ -294,6 +294,36 @@ efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, c
 efla_status efla_chunk_layout_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int varlen,
                                    int segments, int* nseg, size_t* workspace_bytes);
 
+/*
+ * efla_chunk_bwd -- gradients of the chunked forward (efla_chunk_fwd_split_gate with the same q, k, v, beta,
+ * initial_state, chunk and gate): given d_o = dLoss/do and d_final = dLoss/dS_L, writes dLoss/dq, /dk, /dv,
+ * /dbeta and /dinitial_state.  The pages train every model they report but print no backward pass ("Exact
+ * Flow Linear Attention" (gist.science), Risultati Sperimentali item 4; "Error-Free Linear Attention is a
+ * Free Lunch" (howistudyai.com), the language-modelling results), so this is the adjoint of the chunked form
+ * of Step 4, with d alpha / d beta and d alpha / d lambda of the gate in use (gate as in "Gates" above).
+ *   q, k, v, beta, initial_state   the forward's inputs (initial_state NULL = zeros), read only
+ *   d_o            [B,H,L,d_v] dtype, read only (required when L > 0)
+ *   d_final        [B,H,d_k,d_v] fp32 or NULL (= zeros), read only
+ *   dq, dk         [B,H,L,d_k] dtype, written;  dv [B,H,L,d_v] dtype, written;  dbeta [B,H,L] fp32, written
+ *   d_initial      [B,H,d_k,d_v] fp32, written, or NULL (not written)
+ *   workspace      device memory of at least efla_chunk_bwd_workspace_size(...) bytes, 256-byte aligned:
+ *                  the chunks' T diag(alpha), and the state entering and the state gradient leaving every
+ *                  chunk in fp32 (2 B H ceil(L/chunk) d_k d_v floats: 1.07 GB for B8 H16 L4096 d128)
+ * Outputs must not overlap one another, any input or the workspace (EFLA_ERR_INVALID_ARG).  Launches, all on
+ * `stream`: the UT transform, the state pass again (keeping every chunk's entering state), the state
+ * gradient backwards over the chunks (dv, d_initial), and one launch over all (head, chunk) pairs (dq, dk,
+ * dbeta).  Arithmetic is fp32; bf16 inputs are widened.  Sizes as efla_chunk_fwd.
+ */
+efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                           const float* initial_state, const void* d_o, const float* d_final,
+                           void* dq, void* dk, void* dv, float* dbeta, float* d_initial,
+                           int B, int H, int L, int d_k, int d_v, int chunk, int gate,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes efla_chunk_bwd needs for these sizes (host only). */
+efla_status efla_chunk_bwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                          size_t* bytes);
+
 /* Like efla_chunk_fwd_plan, for the state-pass launch of efla_chunk_fwd_split / efla_chunk_state_pass. */
 efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
                                       int dv_slab, int* workgroups, int* slab_width, int* lds_bytes);

@@ -382,3 +382,49 @@ def test_layout_reaches_the_device_check(lib):
     assert _layout_call(lib, cu, B=7) == NO_DEVICE
     # an empty packed batch still writes the final states (from the initial ones)
     assert _layout_call(lib, cu, B=7, L=0, q=None, k=None, v=None, beta=None, o=None) == NO_DEVICE
+
+
+def test_bwd_workspace_size(lib):
+    # UT output, then two fp32 blocks of B H ceil(L/C) d_k d_v (each 256-byte rounded)
+    nb = efla.chunk_bwd_workspace_size(8, 16, 4096, 128, 128, 64, torch.bfloat16)
+    assert nb == 41943040 + 2 * 128 * 64 * 128 * 128 * 4
+    nb = efla.chunk_bwd_workspace_size(1, 3, 100, 32, 16, 32, torch.float32)
+    ut = 3 * 4 * 3 * 256 * 4
+    st = -(-(3 * 4 * 32 * 16 * 4) // 256) * 256
+    assert nb == ut + 2 * st
+    n = ctypes.c_size_t()
+    assert lib.efla_chunk_bwd_workspace_size(1, 1, 8, 96, 64, 64, BF16, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.efla_chunk_bwd_workspace_size(1, 1, 8, 64, 64, 48, BF16, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.efla_chunk_bwd_workspace_size(-1, 1, 8, 64, 64, 64, BF16, ctypes.byref(n)) == INVALID
+
+
+def _bwd_call(lib, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=BF16, s0=None, do=P(5), dsf=None, dq=P(6), dk=P(7), dv=P(8),
+             db=P(9), ds0=P(10), B=1, H=2, L=1000, dk_=64, dv_=64, C=64, gate=0, ws=P(11), wsb=1 << 30)
+    a.update(kw)
+    return lib.efla_chunk_bwd(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["s0"], a["do"], a["dsf"], a["dq"], a["dk"],
+                              a["dv"], a["db"], a["ds0"], a["B"], a["H"], a["L"], a["dk_"], a["dv_"], a["C"], a["gate"],
+                              a["ws"], a["wsb"], None)
+
+
+def test_bwd_argument_errors(lib):
+    need = efla.chunk_bwd_workspace_size(1, 2, 1000, 64, 64, 64, torch.bfloat16)
+    assert _bwd_call(lib, ws=None) == WORKSPACE
+    assert _bwd_call(lib, wsb=need - 1) == WORKSPACE
+    assert _bwd_call(lib, ws=ctypes.c_void_p(0x7F0B00000000 + 128)) == WORKSPACE
+    assert _bwd_call(lib, gate=17) == INVALID
+    assert _bwd_call(lib, dk_=96) == UNSUPPORTED
+    assert _bwd_call(lib, do=None) == INVALID
+    assert _bwd_call(lib, dq=None) == INVALID
+    assert _bwd_call(lib, dq=ctypes.c_void_p(0x7F0100000000 + 64)) == INVALID    # dq inside q
+    assert _bwd_call(lib, dv=ctypes.c_void_p(0x7F0600000000 + 64)) == INVALID    # dv inside dq
+    assert _bwd_call(lib, ws=ctypes.c_void_p(0x7F0300000000)) == INVALID         # workspace on v
+    assert _bwd_call(lib, B=0, ws=None, wsb=0) == OK
+    assert _bwd_call(lib, L=0, ds0=None, q=None, k=None, v=None, beta=None, do=None, dq=None, dk=None, dv=None,
+                     db=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_bwd_reaches_the_device_check(lib):
+    assert _bwd_call(lib) == NO_DEVICE
+    assert _bwd_call(lib, s0=P(12), dsf=P(13), gate=3) == NO_DEVICE
