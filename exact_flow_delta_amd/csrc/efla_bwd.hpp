@@ -20,8 +20,8 @@
 //                      leaving every chunk (fp32), dV and the initial state's gradient;
 //   bwd_chunk_kernel   one workgroup per (head, chunk): T by forward substitution in fp32, then dQ, dK, dbeta.
 // The first two are sequential over chunks and independent over (head, slab of state columns); the third is
-// parallel over all chunks.  All arithmetic is fp32 on the vector units through LDS tiles (a 16 x 16 thread
-// grid of register micro-tiles); inputs of either storage type are widened on load.
+// parallel over all chunks.  All products are fp32 matrix-core instructions (16x16x4) on fp32 LDS tiles, each
+// wave owning whole 16x16 output tiles; inputs of either storage type are widened on load.
 #pragma once
 
 #include "efla_common.hpp"
@@ -31,34 +31,58 @@ namespace efla {
 
 namespace bwd {
 
-constexpr int NT = 256;   // threads per workgroup: tx = tid & 15 (columns), ty = tid >> 4 (rows)
+constexpr int NT = 256;   // threads per workgroup: four waves
 
-// acc[mi][nj] += sum_{k < K} A(ty + 16 mi, k) B(k, tx + 16 nj), A(i, k) = A[i * ars + k * acs],
-// B(k, j) = B[k * brs + j * bcs] (LDS, fp32)
-template <int MI, int NJ>
-__device__ __forceinline__ void mm(float (&acc)[MI][NJ], const float* A, int ars, int acs, const float* B, int brs,
-                                   int bcs, int K, int ty, int tx) {
-    // unrolled so that the LDS reads of several steps are in flight together (one wave per SIMD here)
-#pragma unroll 8
-    for (int k = 0; k < K; ++k) {
-        float a[MI], b[NJ];
+// An M x N fp32 product distributed over the four waves by 16x16 tiles: tile tt = w + 4 s (s < TPW) of the
+// row-major tile grid belongs to wave w, whose lane (r, g) (r = lane & 15, g = lane >> 4) holds its elements
+// (16 ti + 4 g + i, 16 tj + r), i = 0..3 -- the matrix cores' accumulator layout.
+template <int M, int N>
+struct Acc {
+    static constexpr int TN = N / 16, NTT = (M / 16) * (N / 16), TPW = (NTT + 3) / 4;
+    f32x4 t[TPW];
+    __device__ __forceinline__ void zero() {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) a[mi] = A[(ty + 16 * mi) * ars + k * acs];
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) b[nj] = B[k * brs + (tx + 16 * nj) * bcs];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = fmaf(a[mi], b[nj], acc[mi][nj]);
+        for (int s = 0; s < TPW; ++s) t[s] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-}
+    // f(row, col, element) for every element this lane holds
+    template <class F>
+    __device__ __forceinline__ void each(int w, int lane, F f) {
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            const int tt = w + 4 * s;
+            if (NTT % 4 == 0 || tt < NTT) {
+                const int ti = tt / TN, tj = tt - ti * TN;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = t[s][i];
+                    f(16 * ti + 4 * (lane >> 4) + i, 16 * tj + (lane & 15), x);
+                    t[s][i] = x;
+                }
+            }
+        }
+    }
+};
 
-template <int MI, int NJ>
-__device__ __forceinline__ void zero(float (&acc)[MI][NJ]) {
+// acc += A B over k < K (a multiple of 4), A(i, k) = A[i * ars + k * acs], B(k, j) = B[k * brs + j * bcs] in LDS:
+// per 16x16x4 step lane (r, g) supplies A(16 ti + r, k + g) and B(k + g, 16 tj + r)
+template <int M, int N>
+__device__ __forceinline__ void mm(Acc<M, N>& acc, const float* A, int ars, int acs, const float* B, int brs, int bcs,
+                                   int K, int w, int lane) {
+    const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = 0.0f;
+    for (int s = 0; s < Acc<M, N>::TPW; ++s) {
+        const int tt = w + 4 * s;
+        if (Acc<M, N>::NTT % 4 == 0 || tt < Acc<M, N>::NTT) {
+            const int ti = tt / Acc<M, N>::TN, tj = tt - ti * Acc<M, N>::TN;
+            const float* pa = A + (16 * ti + r) * ars + g * acs;
+            const float* pb = B + g * brs + (16 * tj + r) * bcs;
+            f32x4 c = acc.t[s];
+#pragma unroll 8
+            for (int k = 0; k < K; k += 4)
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * acs], pb[k * brs], c, 0, 0, 0);
+            acc.t[s] = c;
+        }
+    }
 }
 
 // ROWS x COLS of a row-major global matrix (row stride ld elements, 16-byte aligned rows) held in registers
@@ -145,20 +169,17 @@ __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict
                                                              const E* __restrict__ tw, const float* __restrict__ s0,
                                                              float* __restrict__ s_all, int L, int DV, int nslab) {
     using namespace bwd;
-    constexpr int LDK = DK + 1, LDV = DVS + 1, LDC = C + 1;
+    constexpr int LDK = DK + 2, LDV = DVS + 2, LDC = C + 2;
     constexpr int NQE = (C / 16) * (C / 16 + 1) / 2 * 256;
     __shared__ float sK[C * LDK], sV[C * LDV], sR[C * LDV], sT[C * LDC], sS[DK * LDV];
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int bh = blockIdx.x / nslab, slab = blockIdx.x - bh * nslab;
     const int col0 = slab * DVS;
     const int NC = (L + C - 1) / C;
     const int64_t tok0 = (int64_t)bh * L;
-    float S[DK / 16][DVS / 16];
-#pragma unroll
-    for (int mi = 0; mi < DK / 16; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < DVS / 16; ++nj)
-            S[mi][nj] = s0 ? s0[((int64_t)bh * DK + ty + 16 * mi) * DV + col0 + tx + 16 * nj] : 0.0f;
+    Acc<DK, DVS> S;
+    S.zero();
+    if (s0) S.each(w, lane, [&](int i, int j, float& x) { x = s0[((int64_t)bh * DK + i) * DV + col0 + j]; });
     Tile<E, C, DK> tk;
     Tile<E, C, DVS> tv;
     TaTile<E, C> tt;
@@ -172,42 +193,30 @@ __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict
     if (NC > 0) load(0);
     for (int c = 0; c < NC; ++c) {
         float* out = s_all + ((int64_t)bh * NC + c) * DK * DV;
-#pragma unroll
-        for (int mi = 0; mi < DK / 16; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < DVS / 16; ++nj) {
-                out[(ty + 16 * mi) * DV + col0 + tx + 16 * nj] = S[mi][nj];
-                sS[(ty + 16 * mi) * LDV + tx + 16 * nj] = S[mi][nj];
-            }
+        S.each(w, lane, [&](int i, int j, float& x) {
+            out[i * DV + col0 + j] = x;
+            sS[i * LDV + j] = x;
+        });
         tk.store(sK, LDK, tid);
         tv.store(sV, LDV, tid);
         tt.store(sT, LDC, tid);
         __syncthreads();
         if (c + 1 < NC) load(c + 1);
         {   // R = V - K S
-            float a[C / 16][DVS / 16];
-            zero(a);
-            mm(a, sK, LDK, 1, sS, LDV, 1, DK, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < C / 16; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < DVS / 16; ++nj) {
-                    const int i = ty + 16 * mi, j = tx + 16 * nj;
-                    sR[i * LDV + j] = sV[i * LDV + j] - a[mi][nj];
-                }
+            Acc<C, DVS> a;
+            a.zero();
+            mm(a, sK, LDK, 1, sS, LDV, 1, DK, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) { sR[i * LDV + j] = sV[i * LDV + j] - x; });
         }
         __syncthreads();
         {   // Delta = Ta R  (into sV)
-            float a[C / 16][DVS / 16];
-            zero(a);
-            mm(a, sT, LDC, 1, sR, LDV, 1, C, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < C / 16; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < DVS / 16; ++nj) sV[(ty + 16 * mi) * LDV + tx + 16 * nj] = a[mi][nj];
+            Acc<C, DVS> a;
+            a.zero();
+            mm(a, sT, LDC, 1, sR, LDV, 1, C, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) { sV[i * LDV + j] = x; });
         }
         __syncthreads();
-        mm(S, sK, 1, LDK, sV, LDV, 1, C, ty, tx);   // S += K^T Delta
+        mm(S, sK, 1, LDK, sV, LDV, 1, C, w, lane);   // S += K^T Delta
         __syncthreads();
     }
 }
@@ -223,21 +232,19 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
                                                             float* __restrict__ ds_all, E* __restrict__ dv,
                                                             float* __restrict__ d_initial, int L, int DV, int nslab) {
     using namespace bwd;
-    constexpr int LDK = DK + 1, LDV = DVS + 1, LDC = C + 1;
+    constexpr int LDK = DK + 2, LDV = DVS + 2, LDC = C + 2;
     constexpr int NQE = (C / 16) * (C / 16 + 1) / 2 * 256;
     __shared__ float sQ[C * LDK], sK[C * LDK], sO[C * LDV], sD[C * LDV], sR[C * LDV], sT[C * LDC], sP[C * LDC],
         sS[DK * LDV];
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int bh = blockIdx.x / nslab, slab = blockIdx.x - bh * nslab;
     const int col0 = slab * DVS;
     const int NC = (L + C - 1) / C;
     const int64_t tok0 = (int64_t)bh * L;
-    float dS[DK / 16][DVS / 16];
-#pragma unroll
-    for (int mi = 0; mi < DK / 16; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < DVS / 16; ++nj)
-            dS[mi][nj] = d_final ? d_final[((int64_t)bh * DK + ty + 16 * mi) * DV + col0 + tx + 16 * nj] : 0.0f;
+    Acc<DK, DVS> dS;
+    dS.zero();
+    if (d_final)
+        dS.each(w, lane, [&](int i, int j, float& x) { x = d_final[((int64_t)bh * DK + i) * DV + col0 + j]; });
     Tile<E, C, DK> tq, tk;
     Tile<E, C, DVS> to;
     TaTile<E, C> tt;
@@ -253,13 +260,10 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
     for (int c = NC - 1; c >= 0; --c) {
         const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
         float* out = ds_all + ((int64_t)bh * NC + c) * DK * DV;
-#pragma unroll
-        for (int mi = 0; mi < DK / 16; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < DVS / 16; ++nj) {
-                out[(ty + 16 * mi) * DV + col0 + tx + 16 * nj] = dS[mi][nj];
-                sS[(ty + 16 * mi) * LDV + tx + 16 * nj] = dS[mi][nj];
-            }
+        dS.each(w, lane, [&](int i, int j, float& x) {
+            out[i * DV + col0 + j] = x;
+            sS[i * LDV + j] = x;
+        });
         tq.store(sQ, LDK, tid);
         tk.store(sK, LDK, tid);
         to.store(sO, LDV, tid);
@@ -267,63 +271,36 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
         __syncthreads();
         if (c > 0) load(c - 1);
         {   // P = lower_incl(Q K^T)
-            float a[C / 16][C / 16];
-            zero(a);
-            mm(a, sQ, LDK, 1, sK, 1, LDK, DK, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < C / 16; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < C / 16; ++nj) {
-                    const int i = ty + 16 * mi, j = tx + 16 * nj;
-                    sP[i * LDC + j] = j <= i ? a[mi][nj] : 0.0f;
-                }
+            Acc<C, C> a;
+            a.zero();
+            mm(a, sQ, LDK, 1, sK, 1, LDK, DK, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = j <= i ? x : 0.0f; });
         }
         __syncthreads();
         {   // dDelta = P^T dO + K dS'
-            float a[C / 16][DVS / 16];
-            zero(a);
-            mm(a, sP, 1, LDC, sO, LDV, 1, C, ty, tx);
-            mm(a, sK, LDK, 1, sS, LDV, 1, DK, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < C / 16; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < DVS / 16; ++nj) sD[(ty + 16 * mi) * LDV + tx + 16 * nj] = a[mi][nj];
+            Acc<C, DVS> a;
+            a.zero();
+            mm(a, sP, 1, LDC, sO, LDV, 1, C, w, lane);
+            mm(a, sK, LDK, 1, sS, LDV, 1, DK, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) { sD[i * LDV + j] = x; });
         }
         __syncthreads();
-        {   // dR = Ta^T dDelta = dV
-            float a[C / 16][DVS / 16];
-            zero(a);
-            mm(a, sT, 1, LDC, sD, LDV, 1, C, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < C / 16; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < DVS / 16; ++nj) {
-                    const int i = ty + 16 * mi, j = tx + 16 * nj;
-                    sR[i * LDV + j] = a[mi][nj];
-                    if (i < n) dv[(tok0 + t0 + i) * DV + col0 + j] = from_f32<E>(a[mi][nj]);
-                }
+        {   // dR = Ta^T dDelta = dV; -dR kept for the state gradient
+            Acc<C, DVS> a;
+            a.zero();
+            mm(a, sT, 1, LDC, sD, LDV, 1, C, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) {
+                sR[i * LDV + j] = -x;
+                if (i < n) dv[(tok0 + t0 + i) * DV + col0 + j] = from_f32<E>(x);
+            });
         }
         __syncthreads();
-        {   // dS = dS' + Q^T dO - K^T dR
-            float a[DK / 16][DVS / 16], b[DK / 16][DVS / 16];
-            zero(a);
-            zero(b);
-            mm(a, sQ, 1, LDK, sO, LDV, 1, C, ty, tx);
-            mm(b, sK, 1, LDK, sR, LDV, 1, C, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < DK / 16; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < DVS / 16; ++nj) dS[mi][nj] += a[mi][nj] - b[mi][nj];
-        }
+        mm(dS, sQ, 1, LDK, sO, LDV, 1, C, w, lane);   // dS += Q^T dO
+        mm(dS, sK, 1, LDK, sR, LDV, 1, C, w, lane);   //    - K^T dR
         __syncthreads();
     }
-    if (d_initial) {
-#pragma unroll
-        for (int mi = 0; mi < DK / 16; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < DVS / 16; ++nj)
-                d_initial[((int64_t)bh * DK + ty + 16 * mi) * DV + col0 + tx + 16 * nj] = dS[mi][nj];
-    }
+    if (d_initial)
+        dS.each(w, lane, [&](int i, int j, float& x) { d_initial[((int64_t)bh * DK + i) * DV + col0 + j] = x; });
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -332,8 +309,8 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
 // ------------------------------------------------------------------------------------------------
 template <typename E, int DK, int C>
 struct BwdChunkLds {
-    static constexpr int LDK = DK + 1, LDC = C + 1, LDV = 17;
-    static constexpr int BYTES = 4 * (2 * C * LDK + 3 * C * LDC + 2 * DK * LDV + 6 * C * LDV + 4 * C);
+    static constexpr int LDK = DK + 2, LDC = C + 2, LDV = 17;
+    static constexpr int BYTES = 4 * (2 * C * LDK + 3 * C * LDC + 2 * DK * LDV + 5 * C * LDV + 4 * C);
 };
 
 template <typename E, int DK, int C>
@@ -344,27 +321,25 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
     using namespace bwd;
     typedef BwdChunkLds<E, DK, C> LY;
     constexpr int LDK = LY::LDK, LDC = LY::LDC, LDV = LY::LDV;
-    constexpr int MC = C / 16, MK = DK / 16;
     extern __shared__ float smem[];
     float* sQ = smem;
     float* sK = sQ + C * LDK;
     float* sL = sK + C * LDK;    // K K^T (full)
     float* sP = sL + C * LDC;    // lower_incl(Q K^T); later M o (dO Delta^T)
-    float* sT = sP + C * LDC;    // T; later dL
+    float* sT = sP + C * LDC;    // T; later G Delta^T, then dL
     float* sS = sT + C * LDC;    // S[:, slab]
     float* sG2 = sS + DK * LDV;  // dS'[:, slab]
-    float* sV = sG2 + DK * LDV;  // V slab; then D R
+    float* sV = sG2 + DK * LDV;  // V slab; then D R; then -dR
     float* sO = sV + C * LDV;    // dO slab
     float* sDl = sO + C * LDV;   // Delta slab
     float* sDd = sDl + C * LDV;  // dDelta slab
     float* sGs = sDd + C * LDV;  // G slab
-    float* sDr = sGs + C * LDV;  // dR slab
-    float* sAl = sDr + C * LDV;  // alpha
+    float* sAl = sGs + C * LDV;  // alpha
     float* sDb = sAl + C;        // dalpha/dbeta
     float* sDlam = sDb + C;      // dalpha/dlambda
     float* sDa = sDlam + C;      // dalpha, then dlambda
 
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int NC = (L + C - 1) / C;
     const int bh = blockIdx.x / NC, c = blockIdx.x - bh * NC;
     const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
@@ -389,6 +364,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         to.load(d_o + tok * DV + col0, DV, n, tid);
     };
     load_slab(0);
+    if (tid < C) sDa[tid] = 0.0f;
     __syncthreads();
     if (tid < C) {   // gates of the chunk's tokens (rows past the end: zero keys, zero step)
         float lam = 0.0f;
@@ -401,19 +377,13 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         sDlam[tid] = dl;
     }
     {   // L = K K^T, P = lower_incl(Q K^T)
-        float a[MC][MC], b[MC][MC];
-        zero(a);
-        zero(b);
-        mm(a, sK, LDK, 1, sK, 1, LDK, DK, ty, tx);
-        mm(b, sQ, LDK, 1, sK, 1, LDK, DK, ty, tx);
-#pragma unroll
-        for (int mi = 0; mi < MC; ++mi)
-#pragma unroll
-            for (int nj = 0; nj < MC; ++nj) {
-                const int i = ty + 16 * mi, j = tx + 16 * nj;
-                sL[i * LDC + j] = a[mi][nj];
-                sP[i * LDC + j] = j <= i ? b[mi][nj] : 0.0f;
-            }
+        Acc<C, C> a, b;
+        a.zero();
+        b.zero();
+        mm(a, sK, LDK, 1, sK, 1, LDK, DK, w, lane);
+        mm(b, sQ, LDK, 1, sK, 1, LDK, DK, w, lane);
+        a.each(w, lane, [&](int i, int j, float& x) { sL[i * LDC + j] = x; });
+        b.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = j <= i ? x : 0.0f; });
     }
     __syncthreads();
     // T = (I + D strict_lower(L))^{-1} by forward substitution, one column per lane of wave 0 in registers:
@@ -436,15 +406,12 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
     }
     __syncthreads();
 
-    float aQ[MC][MK], aK[MC][MK], W1[MC][MC], W2[MC][MC];
-    zero(aQ);
-    zero(aK);
-    zero(W1);
-    zero(W2);
-    float dap[MC];   // this thread's share of rowsum(G o R): rows ty + 16 mi, columns tx of every slab
-#pragma unroll
-    for (int mi = 0; mi < MC; ++mi) dap[mi] = 0.0f;
-
+    Acc<C, DK> aQ, aK;
+    Acc<C, C> W1, W2;
+    aQ.zero();
+    aK.zero();
+    W1.zero();
+    W2.zero();
     for (int col0 = 0; col0 < DV; col0 += 16) {
         ts.store(sS, LDV, tid);
         tds.store(sG2, LDV, tid);
@@ -452,115 +419,89 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         to.store(sO, LDV, tid);
         __syncthreads();
         if (col0 + 16 < DV) load_slab(col0 + 16);
-        float r[MC];
-        {   // R = V - K S; keep R, write D R over V
-            float a[MC][1];
-            zero(a);
-            mm(a, sK, LDK, 1, sS, LDV, 1, DK, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < MC; ++mi) r[mi] = sV[(ty + 16 * mi) * LDV + tx] - a[mi][0];
-        }
+        Acc<C, 16> R;   // R = V - K S, kept for dalpha; D R over V
+        R.zero();
+        mm(R, sK, LDK, 1, sS, LDV, 1, DK, w, lane);
+        R.each(w, lane, [&](int i, int j, float& x) { x = sV[i * LDV + j] - x; });
         __syncthreads();
-#pragma unroll
-        for (int mi = 0; mi < MC; ++mi) sV[(ty + 16 * mi) * LDV + tx] = sAl[ty + 16 * mi] * r[mi];
+        R.each(w, lane, [&](int i, int j, float& x) { sV[i * LDV + j] = sAl[i] * x; });
         __syncthreads();
         {   // Delta = T (D R); dDelta = P^T dO + K dS'
-            float a[MC][1], b[MC][1];
-            zero(a);
-            zero(b);
-            mm(a, sT, LDC, 1, sV, LDV, 1, C, ty, tx);
-            mm(b, sP, 1, LDC, sO, LDV, 1, C, ty, tx);
-            mm(b, sK, LDK, 1, sG2, LDV, 1, DK, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < MC; ++mi) {
-                sDl[(ty + 16 * mi) * LDV + tx] = a[mi][0];
-                sDd[(ty + 16 * mi) * LDV + tx] = b[mi][0];
-            }
+            Acc<C, 16> a, b;
+            a.zero();
+            b.zero();
+            mm(a, sT, LDC, 1, sV, LDV, 1, C, w, lane);
+            mm(b, sP, 1, LDC, sO, LDV, 1, C, w, lane);
+            mm(b, sK, LDK, 1, sG2, LDV, 1, DK, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) { sDl[i * LDV + j] = x; });
+            b.each(w, lane, [&](int i, int j, float& x) { sDd[i * LDV + j] = x; });
         }
         __syncthreads();
-        {   // G = T^T dDelta; dR = D G
-            float a[MC][1];
-            zero(a);
-            mm(a, sT, 1, LDC, sDd, LDV, 1, C, ty, tx);
+        {   // G = T^T dDelta; -dR = -D G over V; dalpha += rowsum(G o R)
+            Acc<C, 16> a;
+            a.zero();
+            mm(a, sT, 1, LDC, sDd, LDV, 1, C, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) {
+                sGs[i * LDV + j] = x;
+                sV[i * LDV + j] = -sAl[i] * x;
+            });
+            // rows of this lane's elements: the same (tile, i) for a and R, summed over the 16 columns (lanes r)
 #pragma unroll
-            for (int mi = 0; mi < MC; ++mi) {
-                const int i = ty + 16 * mi;
-                sGs[i * LDV + tx] = a[mi][0];
-                sDr[i * LDV + tx] = sAl[i] * a[mi][0];
-                dap[mi] = fmaf(a[mi][0], r[mi], dap[mi]);
+            for (int s = 0; s < Acc<C, 16>::TPW; ++s) {
+                const int tt = w + 4 * s;
+                if (Acc<C, 16>::NTT % 4 == 0 || tt < Acc<C, 16>::NTT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float p = a.t[s][i] * R.t[s][i];
+                        p += __shfl_xor(p, 1, 16);
+                        p += __shfl_xor(p, 2, 16);
+                        p += __shfl_xor(p, 4, 16);
+                        p += __shfl_xor(p, 8, 16);
+                        if ((lane & 15) == 0) sDa[16 * tt + 4 * (lane >> 4) + i] += p;
+                    }
+                }
             }
         }
         __syncthreads();
         // dQ += dO S^T; dK += Delta dS'^T - dR S^T; W1 += dO Delta^T; W2 += G Delta^T
-        mm(aQ, sO, LDV, 1, sS, 1, LDV, 16, ty, tx);
-        mm(aK, sDl, LDV, 1, sG2, 1, LDV, 16, ty, tx);
-        {
-            float b[MC][MK];
-            zero(b);
-            mm(b, sDr, LDV, 1, sS, 1, LDV, 16, ty, tx);
-#pragma unroll
-            for (int mi = 0; mi < MC; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < MK; ++nj) aK[mi][nj] -= b[mi][nj];
-        }
-        mm(W1, sO, LDV, 1, sDl, 1, LDV, 16, ty, tx);
-        mm(W2, sGs, LDV, 1, sDl, 1, LDV, 16, ty, tx);
+        mm(aQ, sO, LDV, 1, sS, 1, LDV, 16, w, lane);
+        mm(aK, sDl, LDV, 1, sG2, 1, LDV, 16, w, lane);
+        mm(aK, sV, LDV, 1, sS, 1, LDV, 16, w, lane);
+        mm(W1, sO, LDV, 1, sDl, 1, LDV, 16, w, lane);
+        mm(W2, sGs, LDV, 1, sDl, 1, LDV, 16, w, lane);
         __syncthreads();
     }
 
-    // dalpha = rowsum(G o R) - rowsum(strict_lower(L) o W2): reduce over the 16 column threads of a row
-    float dal[MC];
-#pragma unroll
-    for (int mi = 0; mi < MC; ++mi) {
-        const int i = ty + 16 * mi;
-        float s = dap[mi];
-#pragma unroll
-        for (int nj = 0; nj < MC; ++nj) {
-            const int j = tx + 16 * nj;
-            if (j < i) s -= sL[i * LDC + j] * W2[mi][nj];
-        }
-        s += __shfl_xor(s, 1, 16);
-        s += __shfl_xor(s, 2, 16);
-        s += __shfl_xor(s, 4, 16);
-        s += __shfl_xor(s, 8, 16);
-        dal[mi] = s;
+    // M o W1 into sP, W2 into sT
+    W1.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = j <= i ? x : 0.0f; });
+    W2.each(w, lane, [&](int i, int j, float& x) { sT[i * LDC + j] = x; });
+    __syncthreads();
+    // dalpha = rowsum(G o R) - rowsum(strict_lower(L) o W2); dbeta; dlambda
+    if (tid < C) {
+        const int i = tid;
+        float s = sDa[i];
+        for (int j = 0; j < i; ++j) s -= sL[i * LDC + j] * sT[i * LDC + j];
+        if (i < n) dbeta[tok + i] = s * sDb[i];
+        sDa[i] = s * sDlam[i];
     }
-    // M o W1 into sP, dL = -strict_lower(D W2) into sT
-#pragma unroll
-    for (int mi = 0; mi < MC; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < MC; ++nj) {
-            const int i = ty + 16 * mi, j = tx + 16 * nj;
-            sP[i * LDC + j] = j <= i ? W1[mi][nj] : 0.0f;
-            sT[i * LDC + j] = j < i ? -sAl[i] * W2[mi][nj] : 0.0f;
-        }
-    if (tx == 0) {
-#pragma unroll
-        for (int mi = 0; mi < MC; ++mi) {
-            const int i = ty + 16 * mi;
-            const float db = dal[mi] * sDb[i];
-            sDa[i] = dal[mi] * sDlam[i];   // dlambda
-            if (i < n) dbeta[tok + i] = db;
-        }
+    __syncthreads();
+    // dL = -strict_lower(D W2) in place
+    for (int idx = tid; idx < C * C; idx += NT) {
+        const int i = idx / C, j = idx - i * C;
+        sT[i * LDC + j] = j < i ? -sAl[i] * sT[i * LDC + j] : 0.0f;
     }
     __syncthreads();
     // dQ += (M o W1) K;  dK += (M o W1)^T Q + dL K + dL^T K + 2 dlambda o K
-    mm(aQ, sP, LDC, 1, sK, LDK, 1, C, ty, tx);
-    mm(aK, sP, 1, LDC, sQ, LDK, 1, C, ty, tx);
-    mm(aK, sT, LDC, 1, sK, LDK, 1, C, ty, tx);
-    mm(aK, sT, 1, LDC, sK, LDK, 1, C, ty, tx);
-#pragma unroll
-    for (int mi = 0; mi < MC; ++mi) {
-        const int i = ty + 16 * mi;
-        if (i >= n) continue;
-        const float dl2 = 2.0f * sDa[i];
-#pragma unroll
-        for (int nj = 0; nj < MK; ++nj) {
-            const int e = tx + 16 * nj;
-            dq[(tok + i) * DK + e] = from_f32<E>(aQ[mi][nj]);
-            dk[(tok + i) * DK + e] = from_f32<E>(fmaf(dl2, sK[i * LDK + e], aK[mi][nj]));
-        }
-    }
+    mm(aQ, sP, LDC, 1, sK, LDK, 1, C, w, lane);
+    mm(aK, sP, 1, LDC, sQ, LDK, 1, C, w, lane);
+    mm(aK, sT, LDC, 1, sK, LDK, 1, C, w, lane);
+    mm(aK, sT, 1, LDC, sK, LDK, 1, C, w, lane);
+    aQ.each(w, lane, [&](int i, int e, float& x) {
+        if (i < n) dq[(tok + i) * DK + e] = from_f32<E>(x);
+    });
+    aK.each(w, lane, [&](int i, int e, float& x) {
+        if (i < n) dk[(tok + i) * DK + e] = from_f32<E>(fmaf(2.0f * sDa[i], sK[i * LDK + e], x));
+    });
 }
 
 // ------------------------------------------------------------------------------------------------
