@@ -10,11 +10,12 @@ the roofline line is the state-pass kernel's, the dominant one.
 The batched decode workload (256 sequences x 32 heads, d 128, 512 MiB fp32 state, 64 dependent
 one-token steps, one launch per step) is timed in the same run and reported under "decode".
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--only fwd|decode|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long] [--no-bwd]
+                    [--only fwd|decode|copy|long|bwd]
     python bench.py --record-traffic DIR
 
---only runs one leg for profiling: the forward alone, the decode alone, or a plain 512 MiB
-device-to-device copy (the reference for scaling the HBM byte counters).
+--only runs one leg for profiling: the forward alone, the decode alone, a plain 512 MiB device-to-device
+copy (the reference for scaling the HBM byte counters), the long-context forward, or the LM-layer backward.
 --record-traffic (host only) reads the rocprofv3 counter CSVs of six runs under DIR -- fetch_fwd,
 write_fwd, fetch_dec, write_dec, fetch_copy, write_copy, one FETCH_SIZE or WRITE_SIZE run each (the
 commands are in profiles/hbm_counter_calibration_copy512MiB.md) -- and writes profiles/hbm_traffic.json.
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "EFLA chunked-fwd tokens/s at B8 H16 L4096 d128; % MFMA peak; decode HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector), published
 
 
 def chain_algorithmic(B, H, L, dk, dv, esize=2):
@@ -236,6 +238,59 @@ def run_forward(efla, W, torch, steps, warmup):
                        launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds, ut_waves=w.B * w.H * nc))
 
 
+def bwd_algorithmic(B, H, L, dk, dv, C):
+    """Flops of one backward pass (efla_chunk_bwd), dense-counted per chunk of C tokens from the products the
+    method needs once each: the state recomputation (K S, Ta R, K^T Delta), the state gradient (P = Q K^T,
+    P^T dO, K dS', Ta^T dDelta, Q^T dO, K^T dR) and the per-chunk gradients (R, L = K K^T, T (D R), G = T^T
+    dDelta, dO S^T, Delta dS'^T, dR S^T, dO Delta^T, G Delta^T, and the four C x C by C x d_k products of dQ
+    and dK), 2 flops per multiply-add; the UT transform is counted as in the forward."""
+    cdv, ccv, cck = C * dk * dv, C * C * dv, C * C * dk
+    per_chunk = 2 * ((2 * cdv + ccv) + (cck + 2 * ccv + 3 * cdv) + (5 * cdv + 5 * ccv + 6 * cck))
+    nc = -(-L // C)
+    ut = C * C * dk + C ** 3 // 3
+    return B * H * nc * (per_chunk + 2 * ut)
+
+
+def run_backward(efla, W, torch, steps=5, warmup=2):
+    """The LM-layer backward (B8 H16 L4096 d128 bf16): one efla_chunk_bwd call per step."""
+    w = W.workload(3)
+    x = W.make_fwd_inputs(w)
+    g = W.make_grads(w)
+
+    def dev(a):
+        return torch.from_numpy(W.bf16_bits(a)).view(torch.bfloat16).cuda()
+
+    q, k, v, d_o = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(g["d_o"])
+    beta = torch.from_numpy(x["beta"]).cuda()
+    dsf = torch.from_numpy(g["d_final"]).cuda()
+    del x, g
+    need = efla.chunk_bwd_workspace_size(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        return efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=w.chunk, workspace=ws)
+    for _ in range(warmup):
+        out = fn()
+    torch.cuda.synchronize()
+    time.sleep(0.5)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        out = fn()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    assert all(torch.isfinite(t.float()).all().item() for t in out), "non-finite gradients"
+    flops = bwd_algorithmic(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "lm_layer_bwd B8 H16 L4096 d128 bf16 chunk 64 (dq, dk, dv, dbeta, dS0)", "steps": steps,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+            "workspace_bytes": need,
+            "roofline": {"bound": "mfma", "dtype": "f32", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_PEAK_TFLOPS, 4), "flops_per_call": flops,
+                         "scope": "whole call (UT transform + 3 launches)"}}
+
+
 def run_long_context(efla, W, torch, steps=8, warmup=2):
     """The long-context forward (16 heads x 65,536 tokens): the split forward, whose state pass runs 1,024
     chunks back to back per (head, slab), against the segment-parallel one."""
@@ -324,7 +379,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context forward")
-    ap.add_argument("--only", choices=["fwd", "decode", "copy", "long"], default=None,
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
+    ap.add_argument("--only", choices=["fwd", "decode", "copy", "long", "bwd"], default=None,
                     help="run one leg only (for profiling); prints a short JSON line")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter CSVs under DIR (host only)")
@@ -361,6 +417,10 @@ def main():
         return
     if args.only == "long":
         print(json.dumps({"leg": "long", **run_long_context(efla, W, torch)}), flush=True)
+        return
+    if args.only == "bwd":
+        print(json.dumps({"leg": "bwd", **run_backward(efla, W, torch, steps=args.steps, warmup=args.warmup)}),
+              flush=True)
         return
     if args.only == "decode":
         dw, step_ms = run_decode(efla, W, torch)
@@ -425,6 +485,8 @@ def main():
         }
     if not args.no_long:
         result["long_context"] = run_long_context(efla, W, torch)
+    if not args.no_bwd:
+        result["backward"] = run_backward(efla, W, torch)
     if not args.no_cpu:
         threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
         result["cpu_baseline"] = cpu_baseline(W, threads)
