@@ -7,6 +7,7 @@
 
 #include "efla.h"
 #include "efla_bwd.hpp"
+#include "efla_chain_bf16.hpp"
 #include "efla_chunk_fwd.hpp"
 #include "efla_chunk_split.hpp"
 #include "efla_launch.hpp"
@@ -53,9 +54,12 @@ int split_lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) {
     return (b <= efla::kMaxLdsBytes && u <= efla::kMaxLdsBytes) ? b : -1;
 }
 
+// LDS of the one-launch forward: bf16 with d_k >= 32 and 64-token chunks runs the state pass with its own UT
+// wave, everything else the fused chunk kernel
 int lds_bytes(efla_dtype dt, int d_k, int chunk, int dvs) {
-    const int b = dt == EFLA_BF16 ? efla::chunk_layout_bytes<2>(d_k, chunk, dvs)
-                                  : efla::chunk_layout_bytes<4>(d_k, chunk, dvs);
+    const int b = dt == EFLA_BF16 && d_k >= 32 && chunk == 64 ? efla::chain_ut_bf16_bytes(d_k, dvs)
+                  : dt == EFLA_BF16                           ? efla::chunk_layout_bytes<2>(d_k, chunk, dvs)
+                                                              : efla::chunk_layout_bytes<4>(d_k, chunk, dvs);
     return b <= efla::kMaxLdsBytes ? b : -1;
 }
 

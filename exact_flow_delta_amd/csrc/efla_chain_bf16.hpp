@@ -28,6 +28,13 @@
 // so that the buffers rotate as distinct arrays, which also lets the compiler see that loads into one
 // never alias reads of another.  A chunk's outputs are stored a row block at a time while the following
 // chunk is computed.
+//
+// UTW (in-workgroup UT transform, 64-token chunks): one more wave forms each chunk's Ta itself, one chunk
+// ahead of the compute waves, from the key tile and the betas already staged in LDS, and writes it where
+// the producer would otherwise have put the UT launch's output; the keys cross HBM once and no workspace
+// is written or read.  Only the diagonal 32 x 32 blocks of Ta are formed (the half-chunk steps read no
+// other).  The producer then fetches each chunk's keys and betas first and waits for them one step
+// earlier, so that they are in LDS by the step in which the UT wave transforms that chunk.
 #pragma once
 
 #include "efla_chunk_split.hpp"
@@ -37,8 +44,18 @@ namespace efla {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef bf16x8 __attribute__((address_space(3))) lds_bf16x8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) bf16 lds_b16;
+typedef f32x4 __attribute__((address_space(3))) lds_f32x4;
+typedef bf16x4 __attribute__((address_space(3))) lds_b16x4;
 
-template <int DK, int C, int DVS>
+// LDS of one in-workgroup UT wave (ut_half_lds below): two transposed fp32 diagonal blocks of A, then T_bb^T
+// (bf16); Ta^T (three bf16 quads) reuses the space of the A blocks
+constexpr int kUtHalfAtb = 16 * 20 + 4;                       // floats per transposed diagonal block of A
+constexpr int kUtHalfOffTt = 2 * kUtHalfAtb * 4;
+constexpr int kUtHalfBytes = kUtHalfOffTt + 2 * 512;
+
+template <int DK, int C, int DVS, bool UTW = false>
 struct ChainBf16Shape {
     static constexpr int RBQ = DK * 2;                       // bytes per Q / K row
     static constexpr int RBV = DVS * 2;                      // bytes per V-slab row
@@ -52,9 +69,11 @@ struct ChainBf16Shape {
     static constexpr int OFF_K = NLQ * 1024;
     static constexpr int OFF_V = 2 * NLQ * 1024;
     static constexpr int OFF_T = (2 * NLQ + NLV) * 1024;
-    static constexpr int BUF = (2 * NLQ + NLV + NLT) * 1024;   // one buffer (each tile rounded up to 1 KiB)
-    static constexpr int NBUF = 3 * BUF <= kMaxLdsBytes ? 3 : 2;   // prefetch distance NBUF - 1 chunks
-    static constexpr int BYTES = NBUF * BUF;
+    static constexpr int OFF_B = (2 * NLQ + NLV + NLT) * 1024;   // betas of the chunk (UTW only)
+    static constexpr int BUF = OFF_B + (UTW ? 1024 : 0);        // one buffer (each tile rounded up to 1 KiB)
+    static constexpr int UTS = UTW ? 2 * kUtHalfBytes : 0;          // the two UT waves' private LDS
+    static constexpr int NBUF = 3 * BUF + UTS <= kMaxLdsBytes ? 3 : 2;   // prefetch distance NBUF - 1 chunks
+    static constexpr int BYTES = NBUF * BUF + UTS;
 };
 
 // shape of one tile for the load routine: row bytes, wave loads, whether it is a V tile
@@ -78,14 +97,156 @@ __device__ __forceinline__ int sw_v(int t) {
     else return 0;
 }
 
+// The UT transform of one 32-token half of a 64-token chunk, from the chunk's key tile (the state pass's
+// swizzled layout) and betas in LDS.  The diagonal 32 x 32 blocks of the chunk's Ta = T diag(alpha),
+// T = (I + strict_lower(diag(alpha) K K^T))^{-1}, are the halves' own Ta (the diagonal blocks of the inverse of a
+// block lower triangular matrix are the inverses of its diagonal blocks), and they are all the half-chunk steps
+// of the state pass read; half h is blocks 2h and 2h + 1.  Its three quads go to `ta` in the order the state pass
+// reads: quad qi = rb (rb + 1) / 2 + kb at byte 512 qi, lane (r, g) holding Ta[16 rb + r][16 kb + 4 g .. +3].
+// One wave, the steps of ut_wave_kernel: lambda and the gate from the key fragments, the three lower Gram blocks
+// on the matrix cores, both 16 x 16 diagonal solves at once in fp32 (lane groups 2 and 3 repeat 0 and 1 and
+// store nothing), T_10 = -T_11 A_10 T_00, a transposing export.  `scr` is the wave's private kUtHalfBytes.
+// Rows past the end of the sequence hold zero keys and betas: their alpha is 0, their rows of T those of I.
+template <int DK>
+__device__ __forceinline__ void ut_half_lds(const lds_u8* cK, const lds_u8* cB, lds_u8* scr, lds_u8* ta, int gate,
+                                            int lane, int h) {
+    constexpr int NKP = DK / 32;
+    constexpr int RBQ = DK * 2;
+    constexpr int LDAT = 20;
+    typedef Mma<bf16> M;
+    typedef M::quad quad;
+    typedef bf16x8 bx8;
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int gb = g & 1;   // the block this lane group solves
+    const int swr = sw_qk<DK>(r);
+    lds_f32* const sAt = (lds_f32*)scr;
+    lds_b16* const sTt = (lds_b16*)(scr + kUtHalfOffTt);
+    lds_b16* const sTat = (lds_b16*)scr;
+    // column quad of a row-major 16 x 16 bf16 block: lane (r, g) <- X[4g .. 4g+3][r] (as Mma::lds_quad_t)
+    const int tr = M::tr_offset(lane, 16);
+    auto quad_t = [&](const lds_b16* X) __attribute__((always_inline)) {
+        return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_b16*>(X) + tr)));
+    };
+
+    // keys: lane (r, g) holds row 32 h + 16 j + r, d_k 32 kp + 8 g .. +7 (one 16-byte read per fragment)
+    bx8 kf[2][NKP];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp)
+            kf[j][kp] = bx8(*reinterpret_cast<const lds_bf16x8*>(cK + (32 * h + 16 * j + r) * RBQ + 16 * ((4 * kp + g) ^ swr)));
+    }
+    const float beta_mine = reinterpret_cast<const lds_f32*>(cB)[32 * h + (lane & 31)];   // token 32 h + 16 gb + r
+
+    // lambda of rows 32 h + 16 j + r (fp32 sum of exact bf16 squares, the four lanes of a row combined)
+    float lam[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) sq += sum_sq(kf[j][kp]);
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        lam[j] = sq;
+    }
+    const float alpha_mine = gate_alpha(beta_mine, gb ? lam[1] : lam[0], gate);
+    float ar[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ar[j] = __shfl(alpha_mine, 16 * j + r, 64);
+
+    // Gram blocks (j, l), l <= j: acc lane (r, g), element i = (K K^T)[32 h + 16 j + r][32 h + 16 l + 4 g + i]
+    quad A10;
+    static_for<2>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        static_for<j + 1>([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[l][kp], kf[j][kp], acc, 0, 0, 0);
+            if constexpr (l < j) {
+                A10 = M::cvt(acc * ar[1]);
+            } else {
+                // strict lower part, transposed: At[m][i] = A[16 j + i][16 j + m]
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sAt[j * kUtHalfAtb + (4 * g + i) * LDAT + r] = (4 * g + i < r) ? ar[j] * acc[i] : 0.0f;
+            }
+        });
+    });
+    __asm__ volatile("" ::: "memory");   // this wave's LDS operations complete in order
+
+    // diagonal solves, both blocks at once: lane (r, g) carries column r of T_{gb gb}
+    const lds_f32* at = sAt + gb * kUtHalfAtb;
+    float sv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+    f32x4 ring[4][4];   // rows of At read three steps ahead of their use
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+#pragma unroll
+        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) ring[m][i4] = *reinterpret_cast<const lds_f32x4*>(at + m * LDAT + 4 * i4);
+    }
+#pragma unroll
+    for (int m = 0; m < 15; ++m) {
+        if (m + 3 < 15) {
+#pragma unroll
+            for (int i4 = (m + 4) / 4; i4 < 4; ++i4)
+                ring[(m + 3) & 3][i4] = *reinterpret_cast<const lds_f32x4*>(at + (m + 3) * LDAT + 4 * i4);
+        }
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
+    }
+    if (g < 2) {
+        // row r of T_gg^T and of Ta_gg^T (column r scaled by the gate of token 32 h + 16 g + r)
+        bx8 t0v, t1v, a0v, a1v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            t0v[i] = (bf16)sv[i];
+            t1v[i] = (bf16)sv[8 + i];
+            a0v[i] = (bf16)(sv[i] * alpha_mine);
+            a1v[i] = (bf16)(sv[8 + i] * alpha_mine);
+        }
+        lds_b16* tt = sTt + g * 256 + r * 16;
+        *reinterpret_cast<lds_bf16x8*>(tt) = t0v;
+        *reinterpret_cast<lds_bf16x8*>(tt + 8) = t1v;
+        lds_b16* tq = sTat + (2 * g) * 256 + r * 16;   // local quads: 0 = (0, 0), 1 = (1, 0), 2 = (1, 1)
+        *reinterpret_cast<lds_bf16x8*>(tq) = a0v;
+        *reinterpret_cast<lds_bf16x8*>(tq + 8) = a1v;
+    }
+    __asm__ volatile("" ::: "memory");
+
+    // T_10 = -T_11 (A_10 T_00)
+    {
+        const quad T00 = *reinterpret_cast<const lds_b16x4*>(sTt + r * 16 + 4 * g);   // T_00[4g + e][r]
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        M::mma1(y, A10, T00);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        M::mma1(z, quad_t(sTt + 256), M::cvt_neg(y));   // T_11 as the A operand
+        // z lane (r, g), element e = T_10[4g + e][r]: row r of Ta_10^T after the column gate of token 32 h + r
+        *reinterpret_cast<lds_b16x4*>(sTat + 256 + r * 16 + 4 * g) = M::cvt(z * ar[0]);
+    }
+    __asm__ volatile("" ::: "memory");
+
+    // export: lane (r, g) of block (rb, kb) takes Ta[16 rb + r][16 kb + 4 g + e] = Ta^T[4 g + e][r]
+    // blocks (2h, 2h), (2h+1, 2h), (2h+1, 2h+1) are quads 0, 1, 2 (h = 0) or 5, 8, 9 (h = 1)
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+        const int qi = l == 0 ? 5 * h : l + 7 * h;
+        *reinterpret_cast<lds_b16x4*>(ta + 512 * qi + 8 * lane) = quad_t(sTat + l * 256);
+    }
+    __asm__ volatile("" ::: "memory");   // the next chunk's A blocks overwrite Ta^T
+}
+
 // OUT = false: no outputs (the first pass of the segment-parallel forward needs only the final states), so no
 // Q tile, no Q S, no Q K^T and no O -- 38 matrix instructions per chunk and wave instead of 100.
-template <int DK, int C, int DVS, bool OUT>
-__global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
+// UTW: the in-workgroup UT transform (tw unused; beta and gate read); 64-token chunks with outputs, one segment.
+template <int DK, int C, int DVS, bool OUT, bool UTW = false>
+__global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
     bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg,
-    TokLayout ly) {
-    typedef ChainBf16Shape<DK, C, DVS> SH;
+    TokLayout ly, const float* __restrict__ beta, int gate) {
+    typedef ChainBf16Shape<DK, C, DVS, UTW> SH;
     typedef Mma<bf16> M;
     typedef M::quad quad;
     constexpr int NW = DVS / 16;
@@ -99,11 +260,13 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     constexpr int NBS = NB / NSUB;              // row blocks per sub-chunk
     static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
     static_assert(SH::BYTES <= kMaxLdsBytes, "state pass LDS too large");
+    static_assert(!UTW || (C == 64 && OUT && SH::NBUF == 3), "in-workgroup UT: 64-token chunks, outputs, 3 buffers");
 
     constexpr int PD = SH::NBUF - 1;   // chunks fetched ahead
     __shared__ __attribute__((aligned(1024))) unsigned char buf0_[SH::BUF];
     __shared__ __attribute__((aligned(1024))) unsigned char buf1_[SH::BUF];
     __shared__ __attribute__((aligned(1024))) unsigned char buf2_[PD == 2 ? SH::BUF : 1024];
+    __shared__ __attribute__((aligned(16))) unsigned char uts_[UTW ? SH::UTS : 16];   // the UT wave's scratch
     // LDS is addressed only through LDS-space pointers (no generic pointer ever points into it)
     lds_u8* const buf0 = (lds_u8*)buf0_;
     lds_u8* const buf1 = (lds_u8*)buf1_;
@@ -147,8 +310,15 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     // ---- loads (producer wave only): wave load j of a tile covers its bytes [1024 j, 1024 j + 1024); lane L
     //      writes 16 bytes at 1024 j + 16 L, i.e. physical chunk p of row t, holding logical chunk p ^ sw(t)
     constexpr int NLOAD = 2 * SH::NLQ + SH::NLV + SH::NLT;   // loads of a chunk's tiles
-    constexpr int NISSUE = NLOAD - (OUT ? 0 : SH::NLQ);       // the ones issued (no Q tile without outputs)
-    auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
+    // the ones issued: no Q tile without outputs, and no load of Ta quads 6 and 7 with half-chunk steps
+    constexpr int NISSUE = NLOAD - (OUT ? 0 : SH::NLQ) - (NSUB == 2 ? 1 : 0);
+    // with UTW: the keys and betas of a chunk (issued first), then its queries and values; no Ta load
+    constexpr int NKB = SH::NLQ + 1;
+    constexpr int NQV = SH::NLQ + SH::NLV;
+    static_assert(NSUB != 2 || SH::NLT == 5, "Ta of a 64-token chunk is five 1 KiB loads");
+    // part 0: every tile of the chunk (Q, K, V, Ta); part 1 (UTW): K and the betas; part 2 (UTW): Q and V
+    auto issue_part = [&](int c, lds_u8* buf, auto part_c) __attribute__((always_inline)) {
+        constexpr int PART = decltype(part_c)::value;
         const int t = c * C;
         const int n = (len - t < C) ? (len - t) : C;   // <= 0 past the end: an empty range, zeros
         const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + sv.q0 + t * qs, n > 0 ? ((n - 1) * qs + DK) * 2 : 0);
@@ -167,6 +337,12 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
             const int p = 1024 * j + 16 * lane;
             if constexpr (tile == 0 && !OUT) {
                 return;
+            } else if constexpr ((PART == 1 && tile != 1) || (PART == 2 && tile != 0 && tile != 2)) {
+                return;
+            } else if constexpr (tile == 3 && NSUB == 2 && j == 3) {
+                // bytes [3072, 4096) of Ta are quads 6 and 7, blocks (3, 0) and (3, 1) of the off-diagonal
+                // 32 x 32 block, which the half-chunk steps never read
+                return;
             } else if constexpr (tile == 3) {
                 // Ta blocks: contiguous in the workspace, copied as they are
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
@@ -179,6 +355,15 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
                                                          (tr * ld + 8 * lc) * 2, 0, 0, 0);
             }
         });
+        if constexpr (PART == 1) {
+            // beta of token t + lane -> 4 bytes at OFF_B + 4 lane (zero past the end)
+            const int64_t bt = ly.be_t;
+            const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(beta + sv.be0 + t * bt, n > 0 ? (int)(((n - 1) * bt + 1) * 4) : 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(buf + SH::OFF_B), 4, (int)(lane * bt * 4), 0, 0, 0);
+        }
+    };
+    auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
+        issue_part(c, buf, std::integral_constant<int, 0>{});
     };
     // wait until at most N vector-memory operations of this wave are in flight and all its LDS operations
     // are done (N is an immediate of the wait instruction; operations retire in issue order)
@@ -191,7 +376,52 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
     typedef std::integral_constant<int, NISSUE> ILOAD;
     typedef std::integral_constant<int, NB> INB;
 
-    if (producer) {
+    if constexpr (UTW) {
+        typedef std::integral_constant<int, 1> I1;
+        typedef std::integral_constant<int, 2> I2;
+        typedef std::integral_constant<int, NQV> IQV;
+        auto bufsel = [&](int i) __attribute__((always_inline)) { return i == 0 ? buf0 : i == 1 ? buf1 : buf2; };
+        if (producer) {
+            // Step c (c = c0 - 1: the prologue's) issues chunk c + 2, keys and betas first, and ends once chunk
+            // c + 1 has landed whole and the keys and betas of chunk c + 2 too: in step c + 1 the compute waves
+            // use chunk c + 1 and the UT wave transforms chunk c + 2.  Chunk c lives in buffer (c - c0) mod 3.
+            if (c1 > c0) {
+                issue_part(c0, buf0, I1{});
+                issue_part(c0, buf0, I2{});
+                wait_vm(IQV{});   // keys and betas of chunk c0
+                __builtin_amdgcn_s_barrier();
+                for (int c = c0 - 1; c < c1; ++c) {
+                    if (c + 2 < c1) {
+                        lds_u8* nb = bufsel((c + 2 - c0) % 3);
+                        issue_part(c + 2, nb, I1{});
+                        issue_part(c + 2, nb, I2{});
+                        wait_vm(IQV{});
+                    } else {
+                        wait_vm(I0{});
+                    }
+                    __builtin_amdgcn_s_barrier();
+                }
+            }
+            return;
+        }
+        if (w > NW) {
+            // the UT waves, one per 32-token half: in step c, Ta of chunk c + 1 into that chunk's buffer
+            const int half = w - NW - 1;
+            lds_u8* const scr = (lds_u8*)uts_ + half * kUtHalfBytes;
+            if (c1 > c0) {
+                __builtin_amdgcn_s_barrier();   // keys and betas of chunk c0 are in
+                for (int c = c0 - 1; c < c1; ++c) {
+                    if (c + 1 < c1) {
+                        lds_u8* nb = bufsel((c + 1 - c0) % 3);
+                        ut_half_lds<DK>(nb + SH::OFF_K, nb + SH::OFF_B, scr, nb + SH::OFF_T, gate, lane, half);
+                    }
+                    wait_vm(I0{});   // its LDS writes are done before the barrier
+                    __builtin_amdgcn_s_barrier();
+                }
+            }
+            return;
+        }
+    } else if (producer) {
         // Chunk c's tiles go out at the step of chunk c - PD (the prologue fetches the first PD).  At the end
         // of the step of chunk c those of chunk c + 1 must have landed; with PD = 2 the ones issued during
         // the step (chunk c + 2) may still be in flight.  One barrier per step, as the compute waves.
@@ -381,7 +611,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void chain_bf16_kernel(
         __builtin_amdgcn_s_barrier();
     };
 
-    if (c1 > c0) __builtin_amdgcn_s_barrier();   // the producer's prologue
+    if (c1 > c0) {
+        __builtin_amdgcn_s_barrier();   // the producer's prologue
+        if constexpr (UTW) __builtin_amdgcn_s_barrier();   // and the UT wave's transform of chunk c0
+    }
     if constexpr (PD == 2) {
         for (int c = c0; c < c1; c += 3) {
             step(c, buf0);
@@ -421,13 +654,62 @@ hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, false>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
-                           sg, ly);
+                           sg, ly, nullptr, 0);
     else
         hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, true>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
-                           sg, ly);
+                           sg, ly, nullptr, 0);
     return hipGetLastError();
+}
+
+// LDS bytes of the one-launch forward with the in-workgroup UT transform (mirror of ChainBf16Shape<.., true>)
+constexpr int chain_ut_bf16_bytes(int dk, int dvs) {
+    const int buf = (2 * ((64 * dk * 2 + 1023) / 1024) + (64 * dvs * 2 + 1023) / 1024 + (10 * 512 + 1023) / 1024 + 1) * 1024;
+    return 3 * buf + 2 * kUtHalfBytes;
+}
+
+// The whole chunked forward in one launch (bf16, d_k >= 32, 64-token chunks, contiguous [B,H,L,d]): the state
+// pass with its own UT wave per workgroup.
+template <int DK, int DVS>
+hipError_t launch_chain_ut_bf16_t(const ChunkArgs& a, hipStream_t stream) {
+    typedef ChainBf16Shape<DK, 64, DVS, true> SH;
+    static_assert(SH::BYTES == chain_ut_bf16_bytes(DK, DVS), "host mirror of the LDS size");
+    SplitArgs sa{};
+    sa.BH = a.BH;
+    sa.L = a.L;
+    sa.d_k = DK;
+    sa.d_v = a.d_v;
+    sa.chunk = 64;
+    sa.dvs = DVS;
+    const ChainSeg sg = chain_seg(sa, DK, 64, DVS);
+    const TokLayout ly = contiguous_layout(1, a.L, DK, a.d_v);
+    const int nslab = a.d_v / DVS;
+    const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
+    hipLaunchKernelGGL((chain_bf16_kernel<DK, 64, DVS, true, true>), dim3((unsigned)grid), dim3(DVS / 16 * 64 + 192),
+                       0, stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                       static_cast<const bf16*>(a.v), nullptr, static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v,
+                       nslab, sg, ly, a.beta, a.gate);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_chain_ut_bf16_dvs(const ChunkArgs& a, hipStream_t stream) {
+    switch (a.dvs) {
+        case 16: return launch_chain_ut_bf16_t<DK, 16>(a, stream);
+        case 32: return launch_chain_ut_bf16_t<DK, 32>(a, stream);
+        case 64: return launch_chain_ut_bf16_t<DK, 64>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+inline hipError_t launch_chain_ut_bf16(const ChunkArgs& a, hipStream_t stream) {
+    switch (a.d_k) {
+        case 32: return launch_chain_ut_bf16_dvs<32>(a, stream);
+        case 64: return launch_chain_ut_bf16_dvs<64>(a, stream);
+        case 128: return launch_chain_ut_bf16_dvs<128>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace efla

@@ -539,9 +539,11 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
 // ------------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------------
+// diag32: only the diagonal 32 x 32 blocks of every 64-token chunk's Ta are needed (the bf16 state pass
+// reads no other); the wave kernel then skips the rest (other kernels form the whole transform regardless)
 template <typename E, int DK, int C, bool VL>
 hipError_t launch_ut_vl(const void* k, const float* beta, void* tw, int BH, int L, int gate, const TokLayout& ly,
-                        hipStream_t stream) {
+                        bool diag32, hipStream_t stream) {
     static_assert(UtLayout<sizeof(E), DK, C>::BYTES <= kMaxLdsBytes, "UT kernel LDS too large");
     const int NC = (L + C - 1) / C;
     // chunks of the workspace (with packed sequences an upper bound; the kernel reads the exact count)
@@ -550,17 +552,24 @@ hipError_t launch_ut_vl(const void* k, const float* beta, void* tw, int BH, int 
     if constexpr (std::is_same<E, bf16>::value && DK >= 32) {
         // one wave per (batch*head, chunk) at a time; as many waves as the device holds at once
         constexpr int WPB = UtWaveShape<DK, C>::WPB;
+        constexpr bool CAN_DG = C == 64;
+        const bool dg = CAN_DG && diag32;
+        const void* kfn = dg ? reinterpret_cast<const void*>(&ut_wave_kernel<DK, C, VL, CAN_DG>)
+                             : reinterpret_cast<const void*>(&ut_wave_kernel<DK, C, VL, false>);
         int dev = 0, cus = 0, per_cu = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&ut_wave_kernel<DK, C, VL>),
-                                                              WPB * 64, 0);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, WPB * 64, 0);
         if (e != hipSuccess) return e;
         const int64_t resident = (int64_t)(cus < 1 ? 1 : cus) * (per_cu < 1 ? 1 : per_cu);
         const int64_t need = (total + WPB - 1) / WPB;
-        hipLaunchKernelGGL((ut_wave_kernel<DK, C, VL>), dim3((unsigned)(need < resident ? need : resident)), dim3(WPB * 64), 0,
-                           stream, static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly);
+        const dim3 grid((unsigned)(need < resident ? need : resident));
+        if (dg)
+            hipLaunchKernelGGL((ut_wave_kernel<DK, C, VL, CAN_DG>), grid, dim3(WPB * 64), 0, stream,
+                               static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly);
+        else
+            hipLaunchKernelGGL((ut_wave_kernel<DK, C, VL, false>), grid, dim3(WPB * 64), 0, stream,
+                               static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly);
         return hipGetLastError();
     }
     // as many workgroups as the device holds at once, each walking several pairs
@@ -580,10 +589,10 @@ hipError_t launch_ut_vl(const void* k, const float* beta, void* tw, int BH, int 
 
 template <typename E, int DK, int C>
 hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L, int gate, const TokLayout* lyp,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool diag32 = false) {
     const TokLayout ly = lyp ? *lyp : contiguous_layout(1, L, DK, DK);   // contiguous: every (batch, head) is a "batch"
-    return ly.cu_seqlens ? launch_ut_vl<E, DK, C, true>(k, beta, tw, BH, L, gate, ly, stream)
-                         : launch_ut_vl<E, DK, C, false>(k, beta, tw, BH, L, gate, ly, stream);
+    return ly.cu_seqlens ? launch_ut_vl<E, DK, C, true>(k, beta, tw, BH, L, gate, ly, diag32, stream)
+                         : launch_ut_vl<E, DK, C, false>(k, beta, tw, BH, L, gate, ly, diag32, stream);
 }
 
 template <typename E, int DK, int C, int DVS>
@@ -608,7 +617,10 @@ hipError_t launch_chain_t(const SplitArgs& a, hipStream_t stream) {
 template <typename E, int DK, int C>
 hipError_t launch_split_c(const SplitArgs& a, bool with_ut, hipStream_t s) {
     if (with_ut && a.L > 0) {
-        const hipError_t e = launch_ut_t<E, DK, C>(a.k, a.beta, a.tw, a.BH, a.L, a.gate, a.layout, s);
+        // the bf16 state pass (d_k >= 32) steps 64-token chunks in 32-token halves and reads only the
+        // diagonal 32 x 32 blocks of Ta
+        constexpr bool diag32 = std::is_same<E, bf16>::value && DK >= 32 && C == 64;
+        const hipError_t e = launch_ut_t<E, DK, C>(a.k, a.beta, a.tw, a.BH, a.L, a.gate, a.layout, s, diag32);
         if (e != hipSuccess) return e;
     }
     switch (a.dvs) {

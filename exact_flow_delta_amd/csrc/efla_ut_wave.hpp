@@ -18,6 +18,13 @@
 // T (bf16, transposed, read back as either operand), and Ta^T for the export (in the space of the
 // A blocks, which are dead by then).
 //
+// DG (diagonal 32-blocks only, C = 64): a state pass that steps a 64-token chunk as two 32-token halves
+// reads only the two diagonal 32 x 32 blocks of Ta -- each is the Ta of its half on its own, because the
+// diagonal blocks of the inverse of a block lower triangular matrix are the inverses of its diagonal blocks.
+// With DG the Gram blocks, the block substitution and the export skip the off-diagonal 32 x 32 block (quads
+// (2,0), (2,1), (3,0), (3,1)), which is left unwritten; the six quads written are bit-identical to the full
+// transform's.
+//
 // The grid is persistent: each wave walks chunks u, u + W, u + 2W, ... (W waves in the grid) and loads
 // the next chunk's keys into the operand registers once the current chunk's Gram blocks and diagonal
 // solves are done, so that the load runs under the off-diagonal blocks and the export.  Several waves per SIMD hide the rest.
@@ -42,7 +49,11 @@ struct UtWaveShape {
     static constexpr int WPB = 4;                     // waves per workgroup (the launch bounds assume 4)
 };
 
-template <int DK, int C, bool VL>
+// block (hi, lo) of a chunk's Ta is formed: all of them, or with DG those inside a diagonal 32 x 32 block
+template <bool DG>
+__host__ __device__ constexpr bool ut_block_used(int hi, int lo) { return !DG || (hi >> 1) == (lo >> 1); }
+
+template <int DK, int C, bool VL, bool DG>
 __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
     const bf16* __restrict__ k, const float* __restrict__ beta, bf16* __restrict__ tw, int L, int NC, int BH,
     int gate, TokLayout ly) {
@@ -55,6 +66,7 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
     static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
     static_assert(C == 16 || C == 32 || C == 64, "chunk of 16, 32 or 64");
     static_assert(SH::WPB * 64 == 256, "launch bounds");
+    static_assert(!DG || C == 64, "diagonal 32-blocks only for 64-token chunks");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SH::WPB * SH::BYTES];
     const int lane = threadIdx.x & 63;
@@ -129,6 +141,7 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
             constexpr int hi = decltype(hc)::value;
             static_for<hi + 1>([&](auto lc) {
                 constexpr int lo = decltype(lc)::value;
+                if constexpr (!ut_block_used<DG>(hi, lo)) return;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kp = 0; kp < NKP; ++kp) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[lo][kp], kf[hi][kp], acc, 0, 0, 0);
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
             Tq[J] = M::lds_quad(sTt + J * 256 + r * 16 + 4 * g);   // T_JJ[4g + e][r] = T_JJ^T[r][4g + e]
             static_for<NB>([&](auto ic) {
                 constexpr int I = decltype(ic)::value;
-                if constexpr (I > J) {
+                if constexpr (I > J && ut_block_used<DG>(I, J)) {
                     f32x4 y = {0.f, 0.f, 0.f, 0.f};
                     static_for<(I - J) / 2>([&](auto pc) {
                         constexpr int m = J + 2 * decltype(pc)::value;
@@ -217,8 +230,15 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
 
         // ---- export: lane (r, g) of block qi takes Ta[16 rb + r][16 kb + 4 g + e] = Ta^T[4 g + e][r] -----------
         bf16* dst = tw + (int64_t)u * (SH::NQ * 256) + lane * 4;
-#pragma unroll
-        for (int qi = 0; qi < SH::NQ; ++qi) *reinterpret_cast<quad*>(dst + qi * 256) = M::lds_quad_t(sTat + qi * 256, 16, tr);
+        static_for<NB>([&](auto rc) {
+            constexpr int rb = decltype(rc)::value;
+            static_for<rb + 1>([&](auto kc) {
+                constexpr int kb = decltype(kc)::value;
+                constexpr int qi = rb * (rb + 1) / 2 + kb;
+                if constexpr (ut_block_used<DG>(rb, kb))
+                    *reinterpret_cast<quad*>(dst + qi * 256) = M::lds_quad_t(sTat + qi * 256, 16, tr);
+            });
+        });
         __asm__ volatile("" ::: "memory");   // the next chunk's A blocks overwrite Ta^T
     }
 }

@@ -86,17 +86,33 @@ def test_ut_transform_zero_keys_and_zero_beta():
     assert np.all(got[0, 1, 0, :, 9] == 0)
 
 
-def test_split_workspace_holds_ut_output():
-    """The two-launch forward leaves exactly the stand-alone UT output in its workspace."""
-    w = W.workload(3, B=2, H=3, L=200)
+# quads (row block, column block) of a 64-token chunk's Ta inside its two diagonal 32 x 32 blocks:
+# (0,0) (1,0) (1,1) (2,2) (3,2) (3,3) at qi = rb (rb + 1) / 2 + kb
+DIAG32_QUADS = [0, 1, 2, 5, 8, 9]
+
+
+@pytest.mark.parametrize("dtype,d_k,chunk,diag_only", [("bf16", 128, 64, True), ("bf16", 64, 32, False),
+                                                       ("bf16", 16, 64, False), ("f32", 64, 64, False)])
+def test_split_workspace_holds_ut_output(dtype, d_k, chunk, diag_only):
+    """The two-launch forward leaves the stand-alone UT output in its workspace, bit for bit.  With bf16
+    inputs, d_k >= 32 and 64-token chunks the state pass steps each chunk as two 32-token halves and reads
+    only the diagonal 32 x 32 blocks of Ta, so the forward forms only those (the other quads are unwritten)."""
+    w = W.workload(3, B=2, H=3, L=200, d_k=d_k, d_v=d_k)
     x = W.make_fwd_inputs(w)
-    d = fwd_inputs_dev(x, "bf16")
-    nbytes = efla.chunk_workspace_size(2, 3, 200, 64, torch.bfloat16)
+    d = fwd_inputs_dev(x, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    nbytes = efla.chunk_workspace_size(2, 3, 200, chunk, tdt)
     ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
-    efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], workspace=ws)
-    t = efla.ut_transform(d["k"], d["beta"], chunk_size=64)
+    efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], workspace=ws, chunk_size=chunk, method="split")
+    t = efla.ut_transform(d["k"], d["beta"], chunk_size=chunk)
     torch.cuda.synchronize()
-    assert torch.equal(ws.view(torch.bfloat16), t.flatten())
+    got = ws.view(tdt)[: t.numel()].view(t.shape)
+    if diag_only:
+        assert torch.equal(got[:, :, :, DIAG32_QUADS], t[:, :, :, DIAG32_QUADS])
+        off = [qi for qi in range(t.shape[3]) if qi not in DIAG32_QUADS]
+        assert torch.all(got[:, :, :, off] == 0)   # left as the zeros the test filled in
+    else:
+        assert torch.equal(got, t)
 
 
 def test_split_equals_fused_closely():
