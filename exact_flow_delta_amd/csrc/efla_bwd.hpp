@@ -33,12 +33,13 @@ namespace bwd {
 
 constexpr int NT = 256;   // threads per workgroup: four waves
 
-// An M x N fp32 product distributed over the four waves by 16x16 tiles: tile tt = w + 4 s (s < TPW) of the
-// row-major tile grid belongs to wave w, whose lane (r, g) (r = lane & 15, g = lane >> 4) holds its elements
-// (16 ti + 4 g + i, 16 tj + r), i = 0..3 -- the matrix cores' accumulator layout.
-template <int M, int N>
+// An M x N fp32 product distributed over the NWV waves of the workgroup by 16x16 tiles: tile tt = w + NWV s
+// (s < TPW) of the row-major tile grid belongs to wave w, whose lane (r, g) (r = lane & 15, g = lane >> 4) holds
+// its elements (16 ti + 4 g + i, 16 tj + r), i = 0..3 -- the matrix cores' accumulator layout.
+template <int M, int N, int NWV = 4>
 struct Acc {
-    static constexpr int TN = N / 16, NTT = (M / 16) * (N / 16), TPW = (NTT + 3) / 4;
+    static constexpr int TN = N / 16, NTT = (M / 16) * (N / 16), TPW = (NTT + NWV - 1) / NWV;
+    static constexpr bool ALL = NTT % NWV == 0;   // every wave owns TPW tiles
     f32x4 t[TPW];
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -49,8 +50,8 @@ struct Acc {
     __device__ __forceinline__ void each(int w, int lane, F f) {
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
-            const int tt = w + 4 * s;
-            if (NTT % 4 == 0 || tt < NTT) {
+            const int tt = w + NWV * s;
+            if (ALL || tt < NTT) {
                 const int ti = tt / TN, tj = tt - ti * TN;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -64,23 +65,43 @@ struct Acc {
 };
 
 // acc += A B over k < K (a multiple of 4), A(i, k) = A[i * ars + k * acs], B(k, j) = B[k * brs + j * bcs] in LDS:
-// per 16x16x4 step lane (r, g) supplies A(16 ti + r, k + g) and B(k + g, 16 tj + r)
-template <int M, int N>
-__device__ __forceinline__ void mm(Acc<M, N>& acc, const float* A, int ars, int acs, const float* B, int brs, int bcs,
-                                   int K, int w, int lane) {
+// per 16x16x4 step lane (r, g) supplies A(16 ti + r, k + g) and B(k + g, 16 tj + r).  The reduction steps run in
+// the outer loop and the wave's tiles in the inner one, so that consecutive matrix instructions are independent;
+// a wave with a single tile splits its reduction into two chains (even and odd steps), summed at the end.
+template <int M, int N, int NWV>
+__device__ __forceinline__ void mm(Acc<M, N, NWV>& acc, const float* A, int ars, int acs, const float* B, int brs,
+                                   int bcs, int K, int w, int lane) {
+    typedef Acc<M, N, NWV> AC;
+    constexpr int TPW = AC::TPW;
     const int r = lane & 15, g = lane >> 4;
+    const float* pa[TPW];
+    const float* pb[TPW];
 #pragma unroll
-    for (int s = 0; s < Acc<M, N>::TPW; ++s) {
-        const int tt = w + 4 * s;
-        if (Acc<M, N>::NTT % 4 == 0 || tt < Acc<M, N>::NTT) {
-            const int ti = tt / Acc<M, N>::TN, tj = tt - ti * Acc<M, N>::TN;
-            const float* pa = A + (16 * ti + r) * ars + g * acs;
-            const float* pb = B + g * brs + (16 * tj + r) * bcs;
-            f32x4 c = acc.t[s];
-#pragma unroll 8
-            for (int k = 0; k < K; k += 4)
-                c = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * acs], pb[k * brs], c, 0, 0, 0);
-            acc.t[s] = c;
+    for (int s = 0; s < TPW; ++s) {
+        const int tt = w + NWV * s;
+        const int ti = tt / AC::TN, tj = tt - ti * AC::TN;
+        pa[s] = A + (16 * ti + r) * ars + g * acs;
+        pb[s] = B + g * brs + (16 * tj + r) * bcs;
+    }
+    if constexpr (TPW == 1) {
+        if (AC::ALL || w < AC::NTT) {
+            f32x4 c0 = acc.t[0], c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int k = 0; k < K; k += 8) {
+                c0 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[0][k * acs], pb[0][k * brs], c0, 0, 0, 0);
+                if (k + 4 < K) c1 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[0][(k + 4) * acs], pb[0][(k + 4) * brs], c1, 0, 0, 0);
+            }
+            acc.t[0] = c0 + c1;
+        }
+    } else {
+        const bool last = AC::ALL || w + NWV * (TPW - 1) < AC::NTT;   // this wave owns a tile in slot TPW - 1
+#pragma unroll 2
+        for (int k = 0; k < K; k += 4) {
+#pragma unroll
+            for (int s = 0; s < TPW; ++s) {
+                if (s < TPW - 1 || last)
+                    acc.t[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s][k * acs], pb[s][k * brs], acc.t[s], 0, 0, 0);
+            }
         }
     }
 }
@@ -89,19 +110,19 @@ __device__ __forceinline__ void mm(Acc<M, N>& acc, const float* A, int ars, int 
 // between a load (16 bytes per thread and request, all requests issued before any is used; rows >= n read as
 // zeros) and a store into LDS (row stride sld) widened to fp32.  Loading the next tile before computing on
 // the current one keeps its latency off the critical path.
-template <typename E, int ROWS, int COLS>
+template <typename E, int ROWS, int COLS, int NTH = NT>
 struct Tile {
     typedef typename Vec16<E>::type V;
     static constexpr int VEC = Vec16<E>::N;
     static constexpr int VPR = COLS / VEC;
     static constexpr int TOT = ROWS * VPR;
-    static constexpr int N = (TOT + NT - 1) / NT;
+    static constexpr int N = (TOT + NTH - 1) / NTH;
     static_assert(COLS % VEC == 0, "whole 16-byte vectors per row");
     V x[N];
     __device__ __forceinline__ void load(const E* g, int64_t ld, int n, int tid) {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
-            const int idx = it * NT + tid, r = idx / VPR, c = (idx - r * VPR) * VEC;
+            const int idx = it * NTH + tid, r = idx / VPR, c = (idx - r * VPR) * VEC;
             x[it] = (idx < TOT && r < n) ? *reinterpret_cast<const V*>(g + (int64_t)r * ld + c)
                                          : __builtin_bit_cast(V, u32x4{0u, 0u, 0u, 0u});
         }
@@ -109,8 +130,8 @@ struct Tile {
     __device__ __forceinline__ void store(float* s, int sld, int tid) const {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
-            const int idx = it * NT + tid, r = idx / VPR, c = (idx - r * VPR) * VEC;
-            if (TOT % NT == 0 || idx < TOT) {
+            const int idx = it * NTH + tid, r = idx / VPR, c = (idx - r * VPR) * VEC;
+            if (TOT % NTH == 0 || idx < TOT) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) s[r * sld + c + e] = to_f32<E>(x[it][e]);
             }
@@ -121,25 +142,25 @@ struct Tile {
 // The lower 16x16 blocks of one chunk's Ta from the UT workspace's operand order: block qi = rb (rb + 1) / 2 + kb
 // (kb <= rb) holds at [lane = 16 g + r][j] the entry (16 rb + r, 16 kb + 4 g + j).  The blocks above the
 // diagonal are never written here: zero_upper clears them once.
-template <typename E, int C>
+template <typename E, int C, int NTH = NT>
 struct TaTile {
     static constexpr int NQ = (C / 16) * (C / 16 + 1) / 2;
     static constexpr int TOT = NQ * 64;   // 4-element groups
-    static constexpr int N = (TOT + NT - 1) / NT;
+    static constexpr int N = (TOT + NTH - 1) / NTH;
     typedef E V4 __attribute__((ext_vector_type(4)));
     V4 x[N];
     __device__ __forceinline__ void load(const E* blk, int tid) {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
-            const int idx = it * NT + tid;
-            if (TOT % NT == 0 || idx < TOT) x[it] = *reinterpret_cast<const V4*>(blk + 4 * idx);
+            const int idx = it * NTH + tid;
+            if (TOT % NTH == 0 || idx < TOT) x[it] = *reinterpret_cast<const V4*>(blk + 4 * idx);
         }
     }
     __device__ __forceinline__ void store(float* s, int sld, int tid) const {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
-            const int idx = it * NT + tid;
-            if (TOT % NT == 0 || idx < TOT) {
+            const int idx = it * NTH + tid;
+            if (TOT % NTH == 0 || idx < TOT) {
                 const int qi = idx >> 6, lane = idx & 63;
                 int rb = 0;
                 while ((rb + 1) * (rb + 2) / 2 <= qi) ++rb;
@@ -151,7 +172,7 @@ struct TaTile {
         }
     }
     static __device__ __forceinline__ void zero_upper(float* s, int sld, int tid) {
-        for (int idx = tid; idx < C * C; idx += NT) {
+        for (int idx = tid; idx < C * C; idx += NTH) {
             const int row = idx / C, col = idx - row * C;
             if ((col >> 4) > (row >> 4)) s[row * sld + col] = 0.0f;
         }
@@ -171,7 +192,9 @@ __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict
     using namespace bwd;
     constexpr int LDK = DK + 2, LDV = DVS + 2, LDC = C + 2;
     constexpr int NQE = (C / 16) * (C / 16 + 1) / 2 * 256;
-    __shared__ float sK[C * LDK], sV[C * LDV], sR[C * LDV], sT[C * LDC], sS[DK * LDV];
+    // V, then R = V - K S in place, then Delta (76 KB for d_k = 128, 64-token chunks and 32 columns: two
+    // workgroups per compute unit)
+    __shared__ float sK[C * LDK], sV[C * LDV], sT[C * LDC], sS[DK * LDV];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int bh = blockIdx.x / nslab, slab = blockIdx.x - bh * nslab;
     const int col0 = slab * DVS;
@@ -202,17 +225,18 @@ __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict
         tt.store(sT, LDC, tid);
         __syncthreads();
         if (c + 1 < NC) load(c + 1);
-        {   // R = V - K S
+        {   // R = V - K S (each element read and written by the lane that holds it)
             Acc<C, DVS> a;
             a.zero();
             mm(a, sK, LDK, 1, sS, LDV, 1, DK, w, lane);
-            a.each(w, lane, [&](int i, int j, float& x) { sR[i * LDV + j] = sV[i * LDV + j] - x; });
+            a.each(w, lane, [&](int i, int j, float& x) { sV[i * LDV + j] -= x; });
         }
         __syncthreads();
-        {   // Delta = Ta R  (into sV)
+        {   // Delta = Ta R, over R once every wave has read it
             Acc<C, DVS> a;
             a.zero();
-            mm(a, sT, LDC, 1, sR, LDV, 1, C, w, lane);
+            mm(a, sT, LDC, 1, sV, LDV, 1, C, w, lane);
+            __syncthreads();
             a.each(w, lane, [&](int i, int j, float& x) { sV[i * LDV + j] = x; });
         }
         __syncthreads();
@@ -221,17 +245,21 @@ __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict
     }
 }
 
+constexpr int kChainThreads = 512;   // threads of the state-gradient kernel (eight waves)
+
 // ------------------------------------------------------------------------------------------------
 // The state gradient, backwards over the chunks, for one (head, slab of DVS columns): ds_all[bh][c] =
 // the gradient of the state leaving chunk c; dV of the slab; d_initial = the gradient of S_0.
 // ------------------------------------------------------------------------------------------------
 template <typename E, int DK, int C, int DVS>
-__global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                             const E* __restrict__ tw, const E* __restrict__ d_o,
                                                             const float* __restrict__ d_final,
                                                             float* __restrict__ ds_all, E* __restrict__ dv,
                                                             float* __restrict__ d_initial, int L, int DV, int nslab) {
     using namespace bwd;
+    constexpr int NWV = kChainThreads / 64;   // two waves per SIMD
+    constexpr int NTH = kChainThreads;
     constexpr int LDK = DK + 2, LDV = DVS + 2, LDC = C + 2;
     constexpr int NQE = (C / 16) * (C / 16 + 1) / 2 * 256;
     __shared__ float sQ[C * LDK], sK[C * LDK], sO[C * LDV], sD[C * LDV], sR[C * LDV], sT[C * LDC], sP[C * LDC],
@@ -241,13 +269,13 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
     const int col0 = slab * DVS;
     const int NC = (L + C - 1) / C;
     const int64_t tok0 = (int64_t)bh * L;
-    Acc<DK, DVS> dS;
+    Acc<DK, DVS, NWV> dS;
     dS.zero();
     if (d_final)
         dS.each(w, lane, [&](int i, int j, float& x) { x = d_final[((int64_t)bh * DK + i) * DV + col0 + j]; });
-    Tile<E, C, DK> tq, tk;
-    Tile<E, C, DVS> to;
-    TaTile<E, C> tt;
+    Tile<E, C, DK, NTH> tq, tk;
+    Tile<E, C, DVS, NTH> to;
+    TaTile<E, C, NTH> tt;
     auto load = [&](int c) {
         const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
         tq.load(q + (tok0 + t0) * DK, DK, n, tid);
@@ -255,7 +283,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
         to.load(d_o + (tok0 + t0) * DV + col0, DV, n, tid);
         tt.load(tw + ((int64_t)bh * NC + c) * NQE, tid);
     };
-    TaTile<E, C>::zero_upper(sT, LDC, tid);
+    TaTile<E, C, NTH>::zero_upper(sT, LDC, tid);
     if (NC > 0) load(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
         const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
@@ -271,14 +299,14 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
         __syncthreads();
         if (c > 0) load(c - 1);
         {   // P = lower_incl(Q K^T)
-            Acc<C, C> a;
+            Acc<C, C, NWV> a;
             a.zero();
             mm(a, sQ, LDK, 1, sK, 1, LDK, DK, w, lane);
             a.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = j <= i ? x : 0.0f; });
         }
         __syncthreads();
         {   // dDelta = P^T dO + K dS'
-            Acc<C, DVS> a;
+            Acc<C, DVS, NWV> a;
             a.zero();
             mm(a, sP, 1, LDC, sO, LDV, 1, C, w, lane);
             mm(a, sK, LDK, 1, sS, LDV, 1, DK, w, lane);
@@ -286,7 +314,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
         }
         __syncthreads();
         {   // dR = Ta^T dDelta = dV; -dR kept for the state gradient
-            Acc<C, DVS> a;
+            Acc<C, DVS, NWV> a;
             a.zero();
             mm(a, sT, 1, LDC, sD, LDV, 1, C, w, lane);
             a.each(w, lane, [&](int i, int j, float& x) {
@@ -307,6 +335,8 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chain_kernel(const E* __restrict_
 // dQ, dK and dbeta of one chunk (one workgroup per (head, chunk)), from the chunk's entering state
 // (s_all) and the gradient of its leaving state (ds_all); the d_v columns are taken 16 at a time.
 // ------------------------------------------------------------------------------------------------
+constexpr int kChunkThreads = 512;   // threads of the per-chunk gradient kernel (eight waves)
+
 template <typename E, int DK, int C>
 struct BwdChunkLds {
     static constexpr int LDK = DK + 2, LDC = C + 2, LDV = 17;
@@ -314,11 +344,13 @@ struct BwdChunkLds {
 };
 
 template <typename E, int DK, int C>
-__global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
+__global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ beta,
     const E* __restrict__ d_o, const float* __restrict__ s_all, const float* __restrict__ ds_all, E* __restrict__ dq,
     E* __restrict__ dk, float* __restrict__ dbeta, int L, int DV, int gate) {
     using namespace bwd;
+    constexpr int NWV = kChunkThreads / 64;   // two waves per SIMD: one's LDS reads and barriers overlap the other's products
+    constexpr int NTH = kChunkThreads;
     typedef BwdChunkLds<E, DK, C> LY;
     constexpr int LDK = LY::LDK, LDC = LY::LDC, LDV = LY::LDV;
     extern __shared__ float smem[];
@@ -348,15 +380,15 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
     const float* dSg = ds_all + ((int64_t)bh * NC + c) * DK * DV;
 
     {
-        Tile<E, C, DK> tq, tk;
+        Tile<E, C, DK, NTH> tq, tk;
         tq.load(q + tok * DK, DK, n, tid);
         tk.load(k + tok * DK, DK, n, tid);
         tq.store(sQ, LDK, tid);
         tk.store(sK, LDK, tid);
     }
     // the d_v slabs' tiles, loaded one slab ahead
-    Tile<float, DK, 16> ts, tds;
-    Tile<E, C, 16> tv, to;
+    Tile<float, DK, 16, NTH> ts, tds;
+    Tile<E, C, 16, NTH> tv, to;
     auto load_slab = [&](int col0) {
         ts.load(Sg + col0, DV, DK, tid);
         tds.load(dSg + col0, DV, DK, tid);
@@ -377,7 +409,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         sDlam[tid] = dl;
     }
     {   // L = K K^T, P = lower_incl(Q K^T)
-        Acc<C, C> a, b;
+        Acc<C, C, NWV> a, b;
         a.zero();
         b.zero();
         mm(a, sK, LDK, 1, sK, 1, LDK, DK, w, lane);
@@ -393,10 +425,10 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         float t[C];
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            float s = 0.0f;
+            float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four partial sums: a quarter of the dependent chain
 #pragma unroll
-            for (int m = 0; m < i; ++m) s = fmaf(sL[i * LDC + m], t[m], s);
-            t[i] = (i == j ? 1.0f : 0.0f) - sAl[i] * s;
+            for (int m = 0; m < i; ++m) s4[m & 3] = fmaf(sL[i * LDC + m], t[m], s4[m & 3]);
+            t[i] = (i == j ? 1.0f : 0.0f) - sAl[i] * ((s4[0] + s4[1]) + (s4[2] + s4[3]));
             if (i < j) t[i] = 0.0f;
         }
         if (j < C) {
@@ -406,8 +438,8 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
     }
     __syncthreads();
 
-    Acc<C, DK> aQ, aK;
-    Acc<C, C> W1, W2;
+    Acc<C, DK, NWV> aQ, aK;
+    Acc<C, C, NWV> W1, W2;
     aQ.zero();
     aK.zero();
     W1.zero();
@@ -419,7 +451,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         to.store(sO, LDV, tid);
         __syncthreads();
         if (col0 + 16 < DV) load_slab(col0 + 16);
-        Acc<C, 16> R;   // R = V - K S, kept for dalpha; D R over V
+        Acc<C, 16, NWV> R;   // R = V - K S, kept for dalpha; D R over V
         R.zero();
         mm(R, sK, LDK, 1, sS, LDV, 1, DK, w, lane);
         R.each(w, lane, [&](int i, int j, float& x) { x = sV[i * LDV + j] - x; });
@@ -427,7 +459,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         R.each(w, lane, [&](int i, int j, float& x) { sV[i * LDV + j] = sAl[i] * x; });
         __syncthreads();
         {   // Delta = T (D R); dDelta = P^T dO + K dS'
-            Acc<C, 16> a, b;
+            Acc<C, 16, NWV> a, b;
             a.zero();
             b.zero();
             mm(a, sT, LDC, 1, sV, LDV, 1, C, w, lane);
@@ -438,7 +470,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
         }
         __syncthreads();
         {   // G = T^T dDelta; -dR = -D G over V; dalpha += rowsum(G o R)
-            Acc<C, 16> a;
+            Acc<C, 16, NWV> a;
             a.zero();
             mm(a, sT, 1, LDC, sDd, LDV, 1, C, w, lane);
             a.each(w, lane, [&](int i, int j, float& x) {
@@ -447,9 +479,9 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
             });
             // rows of this lane's elements: the same (tile, i) for a and R, summed over the 16 columns (lanes r)
 #pragma unroll
-            for (int s = 0; s < Acc<C, 16>::TPW; ++s) {
-                const int tt = w + 4 * s;
-                if (Acc<C, 16>::NTT % 4 == 0 || tt < Acc<C, 16>::NTT) {
+            for (int s = 0; s < Acc<C, 16, NWV>::TPW; ++s) {
+                const int tt = w + NWV * s;
+                if (Acc<C, 16, NWV>::ALL || tt < Acc<C, 16, NWV>::NTT) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float p = a.t[s][i] * R.t[s][i];
@@ -486,7 +518,7 @@ __global__ __launch_bounds__(bwd::NT) void bwd_chunk_kernel(
     }
     __syncthreads();
     // dL = -strict_lower(D W2) in place
-    for (int idx = tid; idx < C * C; idx += NT) {
+    for (int idx = tid; idx < C * C; idx += NTH) {
         const int i = idx / C, j = idx - i * C;
         sT[i * LDC + j] = j < i ? -sAl[i] * sT[i * LDC + j] : 0.0f;
     }
@@ -545,11 +577,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     }
     if (a.d_v >= 32) {
         const int nslab = a.d_v / 32;
-        hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(bwd::NT), 0, s, q, k,
+        hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(kChainThreads), 0, s, q, k,
                            tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab);
     } else {
         const int nslab = a.d_v / 16;
-        hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 16>), dim3((unsigned)(a.BH * nslab)), dim3(bwd::NT), 0, s, q, k,
+        hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 16>), dim3((unsigned)(a.BH * nslab)), dim3(kChainThreads), 0, s, q, k,
                            tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab);
     }
     hipError_t e = hipGetLastError();
@@ -559,7 +591,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_kernel<E, DK, C>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, C>), dim3((unsigned)((int64_t)a.BH * NC)), dim3(bwd::NT), LDS, s, q, k,
+    hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, C>), dim3((unsigned)((int64_t)a.BH * NC)), dim3(kChunkThreads), LDS, s, q, k,
                        v, a.beta, d_o, a.s_all, a.ds_all, static_cast<E*>(a.dq), static_cast<E*>(a.dk), a.dbeta, a.L,
                        a.d_v, a.gate);
     return hipGetLastError();
