@@ -170,6 +170,21 @@ def test_chunk_fwd_ragged_lengths(L, method):
 
 
 @pytest.mark.parametrize("method", METHODS)
+@pytest.mark.parametrize("d_k,d_v", [(128, 128), (32, 64), (64, 16)])
+@pytest.mark.parametrize("L", [1, 31, 32, 33, 63, 64, 65, 129, 200])
+def test_chunk_fwd_ragged_lengths_bf16(L, d_k, d_v, method):
+    """bf16 inputs with 64-token chunks at short and ragged lengths (with "fused" this is the one-launch kernel
+    whose UT waves transform each 32-token half of a chunk: halves that are partly or wholly past the end), with
+    an initial state."""
+    w = W.workload(3, B=1, H=3, L=L, d_k=d_k, d_v=d_v)
+    x = W.make_fwd_inputs(w, salt=L + d_k)
+    x["initial_state"] = (0.1 * np.random.default_rng(L).standard_normal((1, 3, d_k, d_v))).astype(np.float32)
+    o, S = _run_fwd(x, "bf16", 64, method=method)
+    eo, eS = errs(o, S, *_oracle_fwd(x))
+    assert eo < TOL["bf16"] and eS < TOL["bf16"], (eo, eS)
+
+
+@pytest.mark.parametrize("method", METHODS)
 def test_chunk_fwd_empty_sequence_copies_state(method):
     rng = np.random.default_rng(5)
     s0 = torch.from_numpy(rng.standard_normal((2, 3, 64, 32)).astype(np.float32)).cuda()
