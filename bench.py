@@ -5,13 +5,14 @@ One step = one chunked forward of the LM-layer workload (B8 H16 L4096 d_k = d_v 
 fp32 beta and state, chunk 64, zero initial state, final state returned), as the library's default
 two-launch form: the UT transform of all 8192 (head, chunk) pairs (exact gate included) into a workspace,
 then the inter-chunk state pass.  The two launches are also timed one by one (HIP events on the stream
-they run on, through the stand-alone UT and state-pass entry points, which launch the same kernels), and
-the roofline line is the state-pass kernel's, the dominant one.  The step's UT launch forms only the diagonal
+they run on, through the stand-alone UT and state-pass entry points: the same state-pass kernel, and the UT
+kernel in its all-blocks form), and the roofline line is the state-pass kernel's, the dominant one.  The step's UT launch forms only the diagonal
 32 x 32 blocks of each chunk's T diag(alpha) (all the state pass reads); the one-launch forward
 (efla_chunk_fwd: the state pass with its own UT waves, no workspace) is timed too and reported under
 "one_launch".
 The batched decode workload (256 sequences x 32 heads, d 128, 512 MiB fp32 state, 64 dependent
-one-token steps, one launch per step) is timed in the same run and reported under "decode".
+one-token steps, one launch per step) is timed in the same run and reported under "decode"; the two small fp32
+parity workloads (tiny single-head, stiff mixed-norm) are timed under "small_fp32".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long] [--no-bwd]
                     [--only fwd|decode|copy|long|bwd]
@@ -346,6 +347,41 @@ def run_long_context(efla, W, torch, steps=8, warmup=2):
             "scan_speedup": round(res["split"] / res["scan"], 3)}
 
 
+def run_small(efla, W, torch, steps=20, warmup=3):
+    """The two fp32 parity workloads, timed: the tiny single-head recurrence (B1 H1 L256 d16, chunk 16) and the
+    stiff mixed-norm one (B4 H8 L2048 d64, chunk 64, initial state); one efla_chunk_fwd_split call per step,
+    median over `steps` HIP-event intervals.  Both are far too small to fill the GPU: launch latency and the
+    length of the chunk chain set their times."""
+    out = {}
+    for cfg, name in ((1, "tiny B1 H1 L256 d16 f32 chunk 16"), (2, "stiff B4 H8 L2048 d64 f32 chunk 64")):
+        w = W.workload(cfg)
+        x = W.make_fwd_inputs(w)
+        q, k, v = (torch.from_numpy(x[n]).cuda() for n in ("q", "k", "v"))
+        beta = torch.from_numpy(x["beta"]).cuda()
+        s0 = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).cuda()
+        o = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.float32, device="cuda")
+        S = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+        ws = torch.empty((efla.chunk_workspace_size(w.B, w.H, w.L, w.chunk, torch.float32),), dtype=torch.uint8,
+                         device="cuda")
+
+        def fn():
+            efla.chunk_fwd(q, k, v, beta, initial_state=s0, chunk_size=w.chunk, out=o, final_state=S, workspace=ws,
+                           method="split")
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        med = statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        out["cfg%d" % cfg] = {"workload": name, "median_ms_per_step": round(med, 5),
+                              "tokens_per_s": round(w.B * w.L / (med * 1e-3), 1)}
+    return out
+
+
 def run_decode(efla, W, torch, warmup=3):
     w = W.workload(5)
     S = torch.from_numpy(W.make_decode_state(w)).cuda()
@@ -512,6 +548,7 @@ def main():
         }
     if not args.no_long:
         result["long_context"] = run_long_context(efla, W, torch)
+    result["small_fp32"] = run_small(efla, W, torch)
     if not args.no_bwd:
         result["backward"] = run_backward(efla, W, torch)
     if not args.no_cpu:
