@@ -109,6 +109,7 @@ efla_status efla_alpha_gate(const void* k, efla_dtype k_dtype, const float* beta
  *   chunk         16, 32 or 64 tokens per chunk
  * The state is carried in fp32 for the whole sequence.  L == 0 copies initial_state (or zeros) to
  * final_state.  q, k, v, beta and o may be NULL only when L == 0.
+ * One launch and no workspace: each workgroup forms the chunks' T diag(alpha) itself.
  */
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
                            efla_dtype dtype, void* o, const float* initial_state, float* final_state,
@@ -188,7 +189,10 @@ efla_status efla_ut_transform_gate(const void* k, const float* beta, efla_dtype 
  * aliasing rules and errors as efla_chunk_fwd_slab, plus:
  *   workspace        device memory of at least efla_chunk_workspace_size(B, H, L, chunk, dtype) bytes,
  *                    16-byte aligned, overlapping no other argument (else EFLA_ERR_WORKSPACE /
- *                    EFLA_ERR_INVALID_ARG); its contents on return are the UT output described above.
+ *                    EFLA_ERR_INVALID_ARG); its contents on return are the UT output described above,
+ *                    except that with bf16 inputs, d_k >= 32 and chunk 64 only the blocks (rb, kb) with
+ *                    rb / 2 == kb / 2 (the two diagonal 32 x 32 blocks of each chunk, all the state pass reads
+ *                    there) are written; the other four blocks of each chunk are left as they were.
  * The UT launch spreads over all (batch*head, chunk) pairs, so the serial state pass carries only the
  * state-dependent products.  Calls that share a workspace must be ordered on one stream.
  */
