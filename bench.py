@@ -80,7 +80,7 @@ def decode_algorithmic(NH, dk, dv, esize=2):
 # hash to what was measured)
 TRAFFIC_KERNELS = {
     "chain_bf16_kernel<128,64,64>": {
-        "symbol": ["chain_bf16_kernelILi128ELi64ELi64ELb1ELb0E", "chain_bf16_kernel<128, 64, 64, true, false>"],
+        "symbol": ["chain_bf16_kernelILi128ELi64ELi64ELb1ELi0E", "chain_bf16_kernel<128, 64, 64, true, 0>"],
         "sources": ["exact_flow_delta_amd/csrc/efla_chain_bf16.hpp", "exact_flow_delta_amd/csrc/efla_chunk_split.hpp",
                     "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_launch.hpp",
                     "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
@@ -90,7 +90,7 @@ TRAFFIC_KERNELS = {
                     "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_launch.hpp",
                     "exact_flow_delta_amd/csrc/efla_split_bf16.hip"]},
     "chain_bf16_kernel<128,64,64,utw>": {
-        "symbol": ["chain_bf16_kernelILi128ELi64ELi64ELb1ELb1E", "chain_bf16_kernel<128, 64, 64, true, true>"],
+        "symbol": ["chain_bf16_kernelILi128ELi64ELi64ELb1ELi2E", "chain_bf16_kernel<128, 64, 64, true, 2>"],
         "sources": ["exact_flow_delta_amd/csrc/efla_chain_bf16.hpp", "exact_flow_delta_amd/csrc/efla_chunk_split.hpp",
                     "exact_flow_delta_amd/csrc/efla_common.hpp", "exact_flow_delta_amd/csrc/efla_launch.hpp",
                     "exact_flow_delta_amd/csrc/efla_ut_wave.hpp", "exact_flow_delta_amd/csrc/efla_chunk_bf16.hip"]},
@@ -518,8 +518,8 @@ def main():
                "achieved_gbs_est": round(ut_bytes / (max(ms - info["chain_ms"], 1e-6) * 1e-3) / 1e9, 1),
                "workspace_written_bytes": info["workspace_bytes"] * 6 // 10,
                "traffic": measured_traffic(ut_kernel)},
-        "one_launch": {"kernel": fused_kernel, "entry": "efla_chunk_fwd (UT waves inside the state pass, no "
-                       "workspace)", "ms_per_step": round(info["fused_ms"], 5),
+        "one_launch": {"kernel": fused_kernel, "entry": "efla_chunk_fwd (four UT waves inside the state pass, "
+                       "no workspace)", "ms_per_step": round(info["fused_ms"], 5),
                        "tokens_per_s": round(w.B * w.L / (info["fused_ms"] * 1e-3), 1),
                        "achieved_gbs": round(nbytes / (info["fused_ms"] * 1e-3) / 1e9, 1),
                        "frac": round(nbytes / (info["fused_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -29,12 +29,16 @@
 // never alias reads of another.  A chunk's outputs are stored a row block at a time while the following
 // chunk is computed.
 //
-// UTW (in-workgroup UT transform, 64-token chunks): one more wave forms each chunk's Ta itself, one chunk
-// ahead of the compute waves, from the key tile and the betas already staged in LDS, and writes it where
-// the producer would otherwise have put the UT launch's output; the keys cross HBM once and no workspace
-// is written or read.  Only the diagonal 32 x 32 blocks of Ta are formed (the half-chunk steps read no
-// other).  The producer then fetches each chunk's keys and betas first and waits for them one step
-// earlier, so that they are in LDS by the step in which the UT wave transforms that chunk.
+// UTW (in-workgroup UT transform, 64-token chunks): more waves form each chunk's Ta in the workgroup itself,
+// ahead of the compute waves, from the key tile and the betas already staged in LDS, and write it where the
+// compute waves would otherwise read the UT launch's output; the keys cross HBM once and no workspace is
+// written or read.  Only the diagonal 32 x 32 blocks of Ta are formed (the half-chunk steps read no other).
+//   UTW = 1: two UT waves (one per 32-token half) transform chunk c + 1 during step c, over the three
+//            whole-chunk buffers; the producer fetches a chunk's keys and betas first and waits for them one
+//            step earlier than for its queries and values.
+//   UTW = 2: four UT waves, in pairs on alternate chunks, each half-chunk transform cut into two parts run in
+//            steps c - 2 and c - 1 for chunk c; the first UT wave also issues the loads; LDS rings of their own
+//            (keys and betas four chunks deep, queries and V slab two deep, Ta two deep).
 #pragma once
 
 #include "efla_chunk_split.hpp"
@@ -49,13 +53,14 @@ typedef __attribute__((address_space(3))) bf16 lds_b16;
 typedef f32x4 __attribute__((address_space(3))) lds_f32x4;
 typedef bf16x4 __attribute__((address_space(3))) lds_b16x4;
 
-// LDS of one in-workgroup UT wave (ut_half_lds below): two transposed fp32 diagonal blocks of A, then T_bb^T
-// (bf16); Ta^T (three bf16 quads) reuses the space of the A blocks
+// LDS of one in-workgroup UT wave (ut_half_lds and its two-part form below): two transposed fp32 diagonal blocks
+// of A, then T_bb^T (bf16); Ta^T (three bf16 quads) reuses the space of the A blocks
 constexpr int kUtHalfAtb = 16 * 20 + 4;                       // floats per transposed diagonal block of A
 constexpr int kUtHalfOffTt = 2 * kUtHalfAtb * 4;
 constexpr int kUtHalfBytes = kUtHalfOffTt + 2 * 512;
 
-template <int DK, int C, int DVS, bool UTW = false>
+// UTW: 0 none, 1 two in-workgroup UT waves over three buffers, 2 four UT waves over separate rings (below)
+template <int DK, int C, int DVS, int UTW = 0>
 struct ChainBf16Shape {
     static constexpr int RBQ = DK * 2;                       // bytes per Q / K row
     static constexpr int RBV = DVS * 2;                      // bytes per V-slab row
@@ -70,10 +75,16 @@ struct ChainBf16Shape {
     static constexpr int OFF_V = 2 * NLQ * 1024;
     static constexpr int OFF_T = (2 * NLQ + NLV) * 1024;
     static constexpr int OFF_B = (2 * NLQ + NLV + NLT) * 1024;   // betas of the chunk (UTW only)
-    static constexpr int BUF = OFF_B + (UTW ? 1024 : 0);        // one buffer (each tile rounded up to 1 KiB)
-    static constexpr int UTS = UTW ? 2 * kUtHalfBytes : 0;          // the two UT waves' private LDS
+    static constexpr int BUF = OFF_B + (UTW == 1 ? 1024 : 0);   // one buffer (each tile rounded up to 1 KiB)
+    static constexpr int UTS = UTW == 1 ? 2 * kUtHalfBytes : 0;     // the two UT waves' private LDS
     static constexpr int NBUF = 3 * BUF + UTS <= kMaxLdsBytes ? 3 : 2;   // prefetch distance NBUF - 1 chunks
-    static constexpr int BYTES = NBUF * BUF + UTS;
+    // UTW == 2: rings of their own -- keys and betas four deep, queries and values two deep, Ta two deep -- and
+    // four UT waves' private LDS
+    static constexpr int KBS = NLQ * 1024 + 1024;            // K tile, then the betas
+    static constexpr int QVS = (NLQ + NLV) * 1024;           // Q tile, then the V slab
+    static constexpr int TS = NLT * 1024;
+    static constexpr int RING2 = 4 * KBS + 2 * QVS + 2 * TS + 4 * kUtHalfBytes;
+    static constexpr int BYTES = UTW == 2 ? RING2 : NBUF * BUF + UTS;
 };
 
 // shape of one tile for the load routine: row bytes, wave loads, whether it is a V tile
@@ -238,11 +249,156 @@ __device__ __forceinline__ void ut_half_lds(const lds_u8* cK, const lds_u8* cB, 
     __asm__ volatile("" ::: "memory");   // the next chunk's A blocks overwrite Ta^T
 }
 
+// The same half-chunk transform as ut_half_lds, cut into two parts run in consecutive chunk steps by one wave
+// (the four-UT-wave workgroup: two pairs of waves take alternate chunks, so each has two steps per chunk).  Part 1:
+// keys, lambda, gates, the Gram blocks and the first MS steps of both substitutions; part 2: the remaining steps,
+// the diagonal blocks, T_10 and the export.  What part 2 needs stays in the wave's registers (UtCarry) and in its
+// private LDS (the transposed diagonal blocks of A, then Ta^T and T_bb^T).
+struct UtCarry {
+    float sv[16];        // column r of the lane group's diagonal block of T, after the steps done so far
+    bf16x4 A10;          // A_10 as a bf16 A operand
+    float ar0, ar1;      // gates of rows 16 j + r
+    float alpha_mine;    // gate of token 32 h + 16 (g & 1) + r
+};
+constexpr int kUtSplit = 6;   // substitution steps in part 1
+
+// steps m = M0 .. M1 - 1 of the right-looking substitution on the transposed diagonal block `at` (rows of At read
+// three steps ahead)
+template <int M0, int M1>
+__device__ __forceinline__ void ut_solve_steps(const lds_f32* at, float* sv) {
+    constexpr int LDAT = 20;
+    f32x4 ring[4][4];
+#pragma unroll
+    for (int m = M0; m < M0 + 3 && m < M1; ++m) {
+#pragma unroll
+        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) ring[m & 3][i4] = *reinterpret_cast<const lds_f32x4*>(at + m * LDAT + 4 * i4);
+    }
+#pragma unroll
+    for (int m = M0; m < M1; ++m) {
+        if (m + 3 < M1) {
+#pragma unroll
+            for (int i4 = (m + 4) / 4; i4 < 4; ++i4)
+                ring[(m + 3) & 3][i4] = *reinterpret_cast<const lds_f32x4*>(at + (m + 3) * LDAT + 4 * i4);
+        }
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
+    }
+}
+
+template <int DK>
+__device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB, lds_u8* scr, int gate, int lane,
+                                              int h, UtCarry& u) {
+    constexpr int NKP = DK / 32;
+    constexpr int RBQ = DK * 2;
+    constexpr int LDAT = 20;
+    typedef Mma<bf16> M;
+    typedef bf16x8 bx8;
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int gb = g & 1;
+    const int swr = sw_qk<DK>(r);
+    lds_f32* const sAt = (lds_f32*)scr;
+    bx8 kf[2][NKP];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp)
+            kf[j][kp] = bx8(*reinterpret_cast<const lds_bf16x8*>(cK + (32 * h + 16 * j + r) * RBQ + 16 * ((4 * kp + g) ^ swr)));
+    }
+    const float beta_mine = reinterpret_cast<const lds_f32*>(cB)[32 * h + (lane & 31)];
+    float lam[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float sq = 0.0f;
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) sq += sum_sq(kf[j][kp]);
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        lam[j] = sq;
+    }
+    u.alpha_mine = gate_alpha(beta_mine, gb ? lam[1] : lam[0], gate);
+    u.ar0 = __shfl(u.alpha_mine, r, 64);
+    u.ar1 = __shfl(u.alpha_mine, 16 + r, 64);
+    static_for<2>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const float arj = j ? u.ar1 : u.ar0;
+        static_for<j + 1>([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[l][kp], kf[j][kp], acc, 0, 0, 0);
+            if constexpr (l < j) {
+                u.A10 = M::cvt(acc * u.ar1);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sAt[j * kUtHalfAtb + (4 * g + i) * LDAT + r] = (4 * g + i < r) ? arj * acc[i] : 0.0f;
+            }
+        });
+    });
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u.sv[i] = (i == r) ? 1.0f : 0.0f;
+    ut_solve_steps<0, kUtSplit>(sAt + gb * kUtHalfAtb, u.sv);
+}
+
+__device__ __forceinline__ void ut_half_part2(lds_u8* scr, lds_u8* ta, int lane, int h, UtCarry& u) {
+    typedef Mma<bf16> M;
+    typedef M::quad quad;
+    typedef bf16x8 bx8;
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int gb = g & 1;
+    const lds_f32* sAt = (const lds_f32*)scr;
+    lds_b16* const sTt = (lds_b16*)(scr + kUtHalfOffTt);
+    lds_b16* const sTat = (lds_b16*)scr;
+    const int tr = M::tr_offset(lane, 16);
+    auto quad_t = [&](const lds_b16* X) __attribute__((always_inline)) {
+        return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_b16*>(X) + tr)));
+    };
+    ut_solve_steps<kUtSplit, 15>(sAt + gb * kUtHalfAtb, u.sv);
+    __asm__ volatile("" ::: "memory");   // the rows of A are read before Ta^T overwrites them
+    if (g < 2) {
+        bx8 t0v, t1v, a0v, a1v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            t0v[i] = (bf16)u.sv[i];
+            t1v[i] = (bf16)u.sv[8 + i];
+            a0v[i] = (bf16)(u.sv[i] * u.alpha_mine);
+            a1v[i] = (bf16)(u.sv[8 + i] * u.alpha_mine);
+        }
+        lds_b16* tt = sTt + g * 256 + r * 16;
+        *reinterpret_cast<lds_bf16x8*>(tt) = t0v;
+        *reinterpret_cast<lds_bf16x8*>(tt + 8) = t1v;
+        lds_b16* tq = sTat + (2 * g) * 256 + r * 16;
+        *reinterpret_cast<lds_bf16x8*>(tq) = a0v;
+        *reinterpret_cast<lds_bf16x8*>(tq + 8) = a1v;
+    }
+    __asm__ volatile("" ::: "memory");
+    {
+        const quad T00 = *reinterpret_cast<const lds_b16x4*>(sTt + r * 16 + 4 * g);
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        M::mma1(y, u.A10, T00);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        M::mma1(z, quad_t(sTt + 256), M::cvt_neg(y));
+        *reinterpret_cast<lds_b16x4*>(sTat + 256 + r * 16 + 4 * g) = M::cvt(z * u.ar0);
+    }
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+        const int qi = l == 0 ? 5 * h : l + 7 * h;
+        *reinterpret_cast<lds_b16x4*>(ta + 512 * qi + 8 * lane) = quad_t(sTat + l * 256);
+    }
+    __asm__ volatile("" ::: "memory");
+}
+
 // OUT = false: no outputs (the first pass of the segment-parallel forward needs only the final states), so no
 // Q tile, no Q S, no Q K^T and no O -- 38 matrix instructions per chunk and wave instead of 100.
 // UTW: the in-workgroup UT transform (tw unused; beta and gate read); 64-token chunks with outputs, one segment.
-template <int DK, int C, int DVS, bool OUT, bool UTW = false>
-__global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf16_kernel(
+// 1: two UT waves and the load producer over three chunk buffers; 2: four UT waves, the first of which also issues
+// the loads, over separate rings (keys and betas four chunks deep, so that a UT wave has two steps per chunk).
+template <int DK, int C, int DVS, bool OUT, int UTW = 0>
+__global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 64)) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
     bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg,
     TokLayout ly, const float* __restrict__ beta, int gate) {
@@ -260,17 +416,24 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
     constexpr int NBS = NB / NSUB;              // row blocks per sub-chunk
     static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
     static_assert(SH::BYTES <= kMaxLdsBytes, "state pass LDS too large");
-    static_assert(!UTW || (C == 64 && OUT && SH::NBUF == 3), "in-workgroup UT: 64-token chunks, outputs, 3 buffers");
+    static_assert(UTW == 0 || (C == 64 && OUT), "in-workgroup UT: 64-token chunks with outputs");
+    static_assert(UTW != 1 || SH::NBUF == 3, "two UT waves: three buffers");
 
     constexpr int PD = SH::NBUF - 1;   // chunks fetched ahead
-    __shared__ __attribute__((aligned(1024))) unsigned char buf0_[SH::BUF];
-    __shared__ __attribute__((aligned(1024))) unsigned char buf1_[SH::BUF];
-    __shared__ __attribute__((aligned(1024))) unsigned char buf2_[PD == 2 ? SH::BUF : 1024];
-    __shared__ __attribute__((aligned(16))) unsigned char uts_[UTW ? SH::UTS : 16];   // the UT wave's scratch
+    __shared__ __attribute__((aligned(1024))) unsigned char buf0_[UTW == 2 ? 16 : SH::BUF];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf1_[UTW == 2 ? 16 : SH::BUF];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf2_[UTW != 2 && PD == 2 ? SH::BUF : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring_[UTW == 2 ? SH::RING2 - 4 * kUtHalfBytes : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char uts_[UTW == 1 ? SH::UTS : UTW == 2 ? 4 * kUtHalfBytes : 16];
     // LDS is addressed only through LDS-space pointers (no generic pointer ever points into it)
     lds_u8* const buf0 = (lds_u8*)buf0_;
     lds_u8* const buf1 = (lds_u8*)buf1_;
     lds_u8* const buf2 = (lds_u8*)buf2_;
+    lds_u8* const ring = (lds_u8*)ring_;
+    // UTW == 2: chunk x's keys and betas, queries and V slab, and Ta
+    auto kbslot = [&](int x) __attribute__((always_inline)) { return ring + (x & 3) * SH::KBS; };
+    auto qvslot = [&](int x) __attribute__((always_inline)) { return ring + 4 * SH::KBS + (x & 1) * SH::QVS; };
+    auto tslot = [&](int x) __attribute__((always_inline)) { return ring + 4 * SH::KBS + 2 * SH::QVS + (x & 1) * SH::TS; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -317,7 +480,8 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
     constexpr int NQV = SH::NLQ + SH::NLV;
     static_assert(NSUB != 2 || SH::NLT == 5, "Ta of a 64-token chunk is five 1 KiB loads");
     // part 0: every tile of the chunk (Q, K, V, Ta); part 1 (UTW): K and the betas; part 2 (UTW): Q and V
-    auto issue_part = [&](int c, lds_u8* buf, auto part_c) __attribute__((always_inline)) {
+    auto issue_to = [&](int c, lds_u8* dQ, lds_u8* dK, lds_u8* dV, lds_u8* dT, lds_u8* dB, auto part_c)
+                        __attribute__((always_inline)) {
         constexpr int PART = decltype(part_c)::value;
         const int t = c * C;
         const int n = (len - t < C) ? (len - t) : C;   // <= 0 past the end: an empty range, zeros
@@ -332,8 +496,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
             constexpr int j = tile == 0 ? kk : tile == 1 ? kk - SH::NLQ : tile == 2 ? kk - 2 * SH::NLQ
                                                                                   : kk - 2 * SH::NLQ - SH::NLV;
             constexpr int RB = tile < 2 ? SH::RBQ : SH::RBV;
-            constexpr int OFF = tile == 0 ? SH::OFF_Q : tile == 1 ? SH::OFF_K : tile == 2 ? SH::OFF_V : SH::OFF_T;
-            lds_void* dst = (lds_void*)(buf + OFF + 1024 * j);
+            lds_void* dst = (lds_void*)((tile == 0 ? dQ : tile == 1 ? dK : tile == 2 ? dV : dT) + 1024 * j);
             const int p = 1024 * j + 16 * lane;
             if constexpr (tile == 0 && !OUT) {
                 return;
@@ -359,8 +522,11 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
             // beta of token t + lane -> 4 bytes at OFF_B + 4 lane (zero past the end)
             const int64_t bt = ly.be_t;
             const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(beta + sv.be0 + t * bt, n > 0 ? (int)(((n - 1) * bt + 1) * 4) : 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(buf + SH::OFF_B), 4, (int)(lane * bt * 4), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)dB, 4, (int)(lane * bt * 4), 0, 0, 0);
         }
+    };
+    auto issue_part = [&](int c, lds_u8* buf, auto part_c) __attribute__((always_inline)) {
+        issue_to(c, buf + SH::OFF_Q, buf + SH::OFF_K, buf + SH::OFF_V, buf + SH::OFF_T, buf + SH::OFF_B, part_c);
     };
     auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
         issue_part(c, buf, std::integral_constant<int, 0>{});
@@ -376,7 +542,57 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
     typedef std::integral_constant<int, NISSUE> ILOAD;
     typedef std::integral_constant<int, NB> INB;
 
-    if constexpr (UTW) {
+    if constexpr (UTW == 2) {
+        if (w >= NW) {
+            // UT wave u: pair u >> 1 takes the chunks of that parity, u & 1 is its half.  In step c (c0 - 2 <= c < c1)
+            // pair c & 1 runs part 1 of chunk c + 2 and the other pair part 2 of chunk c + 1 (which writes its Ta).
+            // Wave 0 also issues the loads: before the first barrier the keys and betas of chunks c0 .. c0 + 2 and
+            // the queries and values of c0; in step c >= c0 the keys and betas of c + 3 and the queries and values
+            // of c + 1, all landed by the end of the step.
+            typedef std::integral_constant<int, 1> I1;
+            typedef std::integral_constant<int, 2> I2;
+            const int u = w - NW;
+            const int pair = u >> 1, half = u & 1;
+            const bool prod = u == 0;
+            lds_u8* const scr = (lds_u8*)uts_ + u * kUtHalfBytes;
+            auto issue_kb = [&](int x) __attribute__((always_inline)) {
+                lds_u8* d = kbslot(x);
+                issue_to(x, d, d, d, d, d + SH::NLQ * 1024, I1{});
+            };
+            auto issue_qv = [&](int x) __attribute__((always_inline)) {
+                lds_u8* d = qvslot(x);
+                issue_to(x, d, d, d + SH::NLQ * 1024, d, d, I2{});
+            };
+            UtCarry uc;
+            if (c1 > c0) {
+                if (prod) {
+                    issue_kb(c0);
+                    if (c0 + 1 < c1) issue_kb(c0 + 1);
+                    if (c0 + 2 < c1) issue_kb(c0 + 2);
+                    issue_qv(c0);
+                    wait_vm(I0{});
+                }
+                __builtin_amdgcn_s_barrier();
+                for (int c = c0 - 2; c < c1; ++c) {
+                    if (prod && c >= c0) {
+                        if (c + 3 < c1) issue_kb(c + 3);
+                        if (c + 1 < c1) issue_qv(c + 1);
+                    }
+                    if ((c & 1) == pair) {
+                        if (c + 2 < c1) {
+                            lds_u8* kb = kbslot(c + 2);
+                            ut_half_part1<DK>(kb, kb + SH::NLQ * 1024, scr, gate, lane, half, uc);
+                        }
+                    } else if (c + 1 >= c0 && c + 1 < c1) {
+                        ut_half_part2(scr, tslot(c + 1), lane, half, uc);
+                    }
+                    wait_vm(I0{});   // this step's loads have landed and this wave's LDS writes are done
+                    __builtin_amdgcn_s_barrier();
+                }
+            }
+            return;
+        }
+    } else if constexpr (UTW == 1) {
         typedef std::integral_constant<int, 1> I1;
         typedef std::integral_constant<int, 2> I2;
         typedef std::integral_constant<int, NQV> IQV;
@@ -487,10 +703,8 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
 
     // one chunk of the compute waves: the previous chunk's outputs are stored a row block at a time while
     // this one is computed
-    auto step = [&](int c, const lds_u8* cur) __attribute__((always_inline)) {
-        const lds_u8* cQ = cur + SH::OFF_Q;
-        const lds_u8* cK = cur + SH::OFF_K;
-        const lds_u8* cV = cur + SH::OFF_V;
+    auto step = [&](int c, const lds_u8* cQ, const lds_u8* cK, const lds_u8* cV, const lds_u8* cT)
+                    __attribute__((always_inline)) {
         typedef bf16x8 bx8;
         auto frag = [&](const lds_u8* tile, int rb, int kp) __attribute__((always_inline)) {   // row 16 rb + r, d_k 32 kp + 8 g .. +7
             return bx8(*reinterpret_cast<const lds_bf16x8*>(tile + (16 * rb + r) * SH::RBQ + 16 * ((4 * kp + g) ^ swr)));
@@ -562,7 +776,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
             // Delta = Ta R over the sub-chunk; Ta block (rb, kb) of the chunk is quad qi = rb (rb + 1) / 2 + kb,
             // lane (r, g)'s at byte 512 qi + 8 lane
             auto ta = [&](int rb, int kb) __attribute__((always_inline)) {
-                return *reinterpret_cast<const lds_quad*>(cur + SH::OFF_T + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+                return *reinterpret_cast<const lds_quad*>(cT + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
             };
             quad Dq[NBS];
             static_for<NBS>([&](auto jc) {
@@ -611,20 +825,36 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64 + (UTW ? 128 : 0)) void chain_bf
         __builtin_amdgcn_s_barrier();
     };
 
-    if (c1 > c0) {
-        __builtin_amdgcn_s_barrier();   // the producer's prologue
-        if constexpr (UTW) __builtin_amdgcn_s_barrier();   // and the UT wave's transform of chunk c0
-    }
-    if constexpr (PD == 2) {
-        for (int c = c0; c < c1; c += 3) {
-            step(c, buf0);
-            if (c + 1 < c1) step(c + 1, buf1);
-            if (c + 2 < c1) step(c + 2, buf2);
+    auto stepb = [&](int c, const lds_u8* b) __attribute__((always_inline)) {
+        step(c, b + SH::OFF_Q, b + SH::OFF_K, b + SH::OFF_V, b + SH::OFF_T);
+    };
+    if constexpr (UTW == 2) {
+        if (c1 > c0) {
+            // the loads' prologue, then the two steps in which the UT waves start chunks c0 and c0 + 1
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+        }
+        for (int c = c0; c < c1; ++c) {
+            const lds_u8* qv = qvslot(c);
+            step(c, qv, kbslot(c), qv + SH::NLQ * 1024, tslot(c));
         }
     } else {
-        for (int c = c0; c < c1; c += 2) {
-            step(c, buf0);
-            if (c + 1 < c1) step(c + 1, buf1);
+        if (c1 > c0) {
+            __builtin_amdgcn_s_barrier();   // the producer's prologue
+            if constexpr (UTW == 1) __builtin_amdgcn_s_barrier();   // and the UT waves' transform of chunk c0
+        }
+        if constexpr (PD == 2) {
+            for (int c = c0; c < c1; c += 3) {
+                stepb(c, buf0);
+                if (c + 1 < c1) stepb(c + 1, buf1);
+                if (c + 2 < c1) stepb(c + 2, buf2);
+            }
+        } else {
+            for (int c = c0; c < c1; c += 2) {
+                stepb(c, buf0);
+                if (c + 1 < c1) stepb(c + 1, buf1);
+            }
         }
     }
     if constexpr (OUT) {
@@ -663,17 +893,22 @@ hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// LDS bytes of the one-launch forward with the in-workgroup UT transform (mirror of ChainBf16Shape<.., true>)
+// The in-workgroup UT mode of the one-launch forward (1 or 2, see chain_bf16_kernel)
+constexpr int kOneLaunchUtMode = 2;
+
+// LDS bytes of the one-launch forward (mirror of ChainBf16Shape<.., kOneLaunchUtMode>)
 constexpr int chain_ut_bf16_bytes(int dk, int dvs) {
-    const int buf = (2 * ((64 * dk * 2 + 1023) / 1024) + (64 * dvs * 2 + 1023) / 1024 + (10 * 512 + 1023) / 1024 + 1) * 1024;
-    return 3 * buf + 2 * kUtHalfBytes;
+    const int nlq = (64 * dk * 2 + 1023) / 1024, nlv = (64 * dvs * 2 + 1023) / 1024, nlt = (10 * 512 + 1023) / 1024;
+    if (kOneLaunchUtMode == 2) return 4 * (nlq + 1) * 1024 + 2 * (nlq + nlv) * 1024 + 2 * nlt * 1024 + 4 * kUtHalfBytes;
+    return 3 * (2 * nlq + nlv + nlt + 1) * 1024 + 2 * kUtHalfBytes;
 }
 
 // The whole chunked forward in one launch (bf16, d_k >= 32, 64-token chunks, contiguous [B,H,L,d]): the state
-// pass with its own UT wave per workgroup.
+// pass with its own UT waves in every workgroup.
 template <int DK, int DVS>
 hipError_t launch_chain_ut_bf16_t(const ChunkArgs& a, hipStream_t stream) {
-    typedef ChainBf16Shape<DK, 64, DVS, true> SH;
+    constexpr int MODE = kOneLaunchUtMode;
+    typedef ChainBf16Shape<DK, 64, DVS, MODE> SH;
     static_assert(SH::BYTES == chain_ut_bf16_bytes(DK, DVS), "host mirror of the LDS size");
     SplitArgs sa{};
     sa.BH = a.BH;
@@ -686,7 +921,8 @@ hipError_t launch_chain_ut_bf16_t(const ChunkArgs& a, hipStream_t stream) {
     const TokLayout ly = contiguous_layout(1, a.L, DK, a.d_v);
     const int nslab = a.d_v / DVS;
     const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
-    hipLaunchKernelGGL((chain_bf16_kernel<DK, 64, DVS, true, true>), dim3((unsigned)grid), dim3(DVS / 16 * 64 + 192),
+    const int threads = DVS / 16 * 64 + (MODE == 2 ? 256 : 192);
+    hipLaunchKernelGGL((chain_bf16_kernel<DK, 64, DVS, true, MODE>), dim3((unsigned)grid), dim3(threads),
                        0, stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                        static_cast<const bf16*>(a.v), nullptr, static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v,
                        nslab, sg, ly, a.beta, a.gate);
