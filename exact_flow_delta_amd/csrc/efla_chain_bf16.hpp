@@ -835,9 +835,16 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_s_barrier();
         }
-        for (int c = c0; c < c1; ++c) {
-            const lds_u8* qv = qvslot(c);
-            step(c, qv, kbslot(c), qv + SH::NLQ * 1024, tslot(c));
+        // one segment (c0 = 0): unrolled over the key ring's four slots, so that every slot is a constant offset
+        auto stepr = [&](int c, int i) __attribute__((always_inline)) {
+            const lds_u8* qv = qvslot(i);
+            step(c, qv, kbslot(i), qv + SH::NLQ * 1024, tslot(i));
+        };
+        for (int c = 0; c < c1; c += 4) {
+            stepr(c, 0);
+            if (c + 1 < c1) stepr(c + 1, 1);
+            if (c + 2 < c1) stepr(c + 2, 2);
+            if (c + 3 < c1) stepr(c + 3, 3);
         }
     } else {
         if (c1 > c0) {
