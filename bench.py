@@ -2,14 +2,15 @@
 """Benchmark of the EFLA hot path on one MI355X.
 
 One step = one chunked forward of the LM-layer workload (B8 H16 L4096 d_k = d_v = 128, bf16 q/k/v/o,
-fp32 beta and state, chunk 64, zero initial state, final state returned), as the library's default
-two-launch form: the UT transform of all 8192 (head, chunk) pairs (exact gate included) into a workspace,
-then the inter-chunk state pass.  The two launches are also timed one by one (HIP events on the stream
-they run on, through the stand-alone UT and state-pass entry points: the same state-pass kernel, and the UT
-kernel in its all-blocks form), and the roofline line is the state-pass kernel's, the dominant one.  The step's UT launch forms only the diagonal
-32 x 32 blocks of each chunk's T diag(alpha) (all the state pass reads); the one-launch forward
-(efla_chunk_fwd: the state pass with its own UT waves, no workspace) is timed too and reported under
-"one_launch".
+fp32 beta and state, chunk 64, zero initial state, final state returned), as the library's default form for
+these sizes: the one-launch forward (efla_chunk_fwd), whose workgroups run the inter-chunk state pass and, on
+waves of their own, the UT transform of their head's chunks (exact gate included), with no workspace.  The
+roofline line is that kernel's: the forward's algorithmic bytes over its average launch duration (HIP events on
+the stream it runs on).  The two-launch form (efla_chunk_fwd_split: the UT transform of all 8192 (head, chunk)
+pairs into a workspace, then the state pass) is timed on the same inputs under "split", with its two launches
+also timed one by one through the stand-alone UT and state-pass entry points (the same state-pass kernel; the
+UT kernel in its all-blocks form, while the step's UT launch forms only the diagonal 32 x 32 blocks of each
+chunk's T diag(alpha), all the state pass reads).
 The batched decode workload (256 sequences x 32 heads, d 128, 512 MiB fp32 state, 64 dependent
 one-token steps, one launch per step) is timed in the same run and reported under "decode"; the two small fp32
 parity workloads (tiny single-head, stiff mixed-norm) are timed under "small_fp32".
@@ -193,7 +194,11 @@ def run_forward(efla, W, torch, steps, warmup):
         time.sleep(0.5)
 
     def one_call(gate=efla.GATE_EXACT):
-        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, gate=gate, method="split")
+        # the library's default form for these sizes: the one-launch forward (efla_chunk_fwd)
+        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, gate=gate)
+
+    def split_call():
+        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, method="split")
 
     def timed(fn):
         settle()
@@ -205,18 +210,35 @@ def run_forward(efla, W, torch, steps, warmup):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
+    def spin():
+        # a spin kernel queued first keeps the GPU busy while the host queues the whole loop, so that no event
+        # interval below holds host time between two launches
+        settle()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(steps * 400e-6 * 2.0e9))   # ~400 us of clock ticks per step queued
+
     for _ in range(warmup):
         one_call()
-    ms = timed(one_call)   # the headline: the whole forward, one efla_chunk_fwd_split call per step
+    ms = timed(one_call)   # the headline: the whole forward, one efla_chunk_fwd call (one kernel) per step
     assert torch.isfinite(S).all().item(), "non-finite final state"
 
-    # The same two launches through their own entry points (efla_ut_transform, then efla_chunk_state_pass: bit-
-    # identical results), with HIP events between them on torch's current stream -- the stream the library
-    # launches on -- for each kernel's average duration.  A spin kernel queued first keeps the GPU busy while
-    # the host queues the whole loop, so that no event interval holds host time between two launches.
-    settle()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(steps * 400e-6 * 2.0e9))   # ~400 us of clock ticks per step queued
+    # the same kernel between HIP events on torch's current stream -- the stream the library launches on --
+    # for its average launch duration
+    spin()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        one_call()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    fused_launch_ms = statistics.mean(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+
+    # the two-launch form (efla_chunk_fwd_split), then its two launches through their own entry points
+    # (efla_ut_transform, then efla_chunk_state_pass: bit-identical results) between events
+    for _ in range(warmup):
+        split_call()
+    split_ms = timed(split_call)
+    spin()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     for i in range(steps):
         ev[3 * i].record()
@@ -228,7 +250,7 @@ def run_forward(efla, W, torch, steps, warmup):
     ut_ms = statistics.mean(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps))
     chain_ms = statistics.mean(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))
 
-    # the delta rule's coefficient alpha = beta (gate 1) on the same kernels: steps of the two gates alternate, so
+    # the delta rule's coefficient alpha = beta (gate 1) on the same kernel: steps of the two gates alternate, so
     # that both see the same clock, and each gate's median step is kept
     settle()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
@@ -242,16 +264,10 @@ def run_forward(efla, W, torch, steps, warmup):
     alt_exact_ms = statistics.median(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
     deltanet_ms = statistics.median(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(steps))
 
-    # the one-launch forward (efla_chunk_fwd: the state pass with its own UT waves, no workspace)
-    def one_launch():
-        efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, method="fused")
-    for _ in range(warmup):
-        one_launch()
-    fused_ms = timed(one_launch)
-    wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
-    return w, ms, dict(ut_ms=ut_ms, chain_ms=chain_ms, workspace_bytes=nbytes, deltanet_ms=deltanet_ms,
-                       alt_exact_ms=alt_exact_ms, fused_ms=fused_ms,
-                       launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds, ut_waves=w.B * w.H * nc))
+    wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16, method="fused")
+    return w, ms, dict(fused_launch_ms=fused_launch_ms, split_ms=split_ms, ut_ms=ut_ms, chain_ms=chain_ms,
+                       workspace_bytes=nbytes, deltanet_ms=deltanet_ms, alt_exact_ms=alt_exact_ms,
+                       launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds))
 
 
 def bwd_algorithmic(B, H, L, dk, dv, C):
@@ -486,7 +502,9 @@ def main():
     nbytes, flops = fwd_algorithmic(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk)
     chain_bytes = chain_algorithmic(w.B, w.H, w.L, w.d_k, w.d_v)
     ut_bytes = ut_algorithmic(w.B, w.H, w.L, w.d_k)
+    fused_gbs = nbytes / (info["fused_launch_ms"] * 1e-3) / 1e9
     chain_gbs = chain_bytes / (info["chain_ms"] * 1e-3) / 1e9
+    split_ms = info["split_ms"]
     tflops = flops / (ms * 1e-3) / 1e12
     chain_kernel = "chain_bf16_kernel<128,64,64>"
     ut_kernel = "ut_wave_kernel<128,64,diag32>"
@@ -505,27 +523,29 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "lm_layer_fwd", "B": w.B, "H": w.H, "L": w.L, "d_k": w.d_k, "d_v": w.d_v,
-                   "chunk": w.chunk, "io": "bf16", "state": "fp32", "method": "split", **info["launch"]},
-        "roofline": {"bound": "hbm", "achieved": round(chain_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(chain_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(chain_kernel),
-                     "kernel": chain_kernel, "bytes_per_launch": chain_bytes,
-                     "avg_launch_ms": round(info["chain_ms"], 5)},
-        # the step's UT launch forms only the diagonal 32 x 32 blocks of each chunk's T diag(alpha); the stand-alone
-        # efla_ut_transform entry (timed between events, same kernel, all blocks) is an upper bound on it, and
-        # the step minus the state pass estimates it
-        "ut": {"kernel": ut_kernel, "entry_avg_launch_ms": round(info["ut_ms"], 5),
-               "in_step_est_ms": round(ms - info["chain_ms"], 5), "bytes_per_launch": ut_bytes,
-               "achieved_gbs_est": round(ut_bytes / (max(ms - info["chain_ms"], 1e-6) * 1e-3) / 1e9, 1),
-               "workspace_written_bytes": info["workspace_bytes"] * 6 // 10,
-               "traffic": measured_traffic(ut_kernel)},
-        "one_launch": {"kernel": fused_kernel, "entry": "efla_chunk_fwd (four UT waves inside the state pass, "
-                       "no workspace)", "ms_per_step": round(info["fused_ms"], 5),
-                       "tokens_per_s": round(w.B * w.L / (info["fused_ms"] * 1e-3), 1),
-                       "achieved_gbs": round(nbytes / (info["fused_ms"] * 1e-3) / 1e9, 1),
-                       "frac": round(nbytes / (info["fused_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                       "traffic": measured_traffic(fused_kernel)},
-        "step": {"algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                 "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                   "chunk": w.chunk, "io": "bf16", "state": "fp32", "method": "fused (one launch)", **info["launch"]},
+        # the step is one kernel: its algorithmic bytes (every input read and the outputs written once) over its
+        # average launch duration
+        "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(fused_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(fused_kernel),
+                     "kernel": fused_kernel, "bytes_per_launch": nbytes,
+                     "avg_launch_ms": round(info["fused_launch_ms"], 5)},
+        # the two-launch form (efla_chunk_fwd_split) on the same inputs: the state pass's roofline, and the UT
+        # launch, which forms only the diagonal 32 x 32 blocks of each chunk's T diag(alpha) (the stand-alone
+        # efla_ut_transform entry, timed between events, is the same kernel on all blocks: an upper bound; the
+        # split step minus the state pass estimates it)
+        "split": {"entry": "efla_chunk_fwd_split (UT launch, then the state pass)", "ms_per_step": round(split_ms, 5),
+                  "tokens_per_s": round(w.B * w.L / (split_ms * 1e-3), 1),
+                  "workspace_written_bytes": info["workspace_bytes"] * 6 // 10,
+                  "state_pass": {"kernel": chain_kernel, "bytes_per_launch": chain_bytes,
+                                 "avg_launch_ms": round(info["chain_ms"], 5), "achieved_gbs": round(chain_gbs, 1),
+                                 "frac": round(chain_gbs / HBM_PEAK_GBS, 4),
+                                 "traffic": measured_traffic(chain_kernel)},
+                  "ut": {"kernel": ut_kernel, "entry_avg_launch_ms": round(info["ut_ms"], 5),
+                         "in_step_est_ms": round(split_ms - info["chain_ms"], 5), "bytes_per_launch": ut_bytes,
+                         "achieved_gbs_est": round(ut_bytes / (max(split_ms - info["chain_ms"], 1e-6) * 1e-3) / 1e9,
+                                                   1),
+                         "traffic": measured_traffic(ut_kernel)}},
         "deltanet_gate": {"median_ms_per_step": round(info["deltanet_ms"], 5),
                           "exact_median_ms_per_step": round(info["alt_exact_ms"], 5),
                           "exact_over_deltanet": round(info["alt_exact_ms"] / info["deltanet_ms"], 4)},

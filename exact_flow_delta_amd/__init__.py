@@ -14,9 +14,11 @@ library is missing, every call raises.
     dq, dk, dv, dbeta, dS0 = chunk_bwd(q, k, v, beta, d_o, initial_state=None, d_final=None)
     o, S = efla_attention(q, k, v, beta, initial_state=None)   # differentiable (torch.autograd)
 
-chunk_fwd runs the two-launch form by default (UT transform of all chunks into a workspace, then the
-state pass); method="fused" runs the single-kernel form, which needs no workspace; method="scan" cuts long
-sequences into segments processed at the same time (for few heads), see efla_chunk_fwd_scan.
+chunk_fwd picks its form by default: for bf16, d_k >= 32 and 64-token chunks the single kernel
+(method="fused": the chunks' UT transform runs in the same workgroups as the state pass, no workspace),
+otherwise the two-launch form (method="split": UT transform of all chunks into a workspace, then the state
+pass); method="scan" cuts long sequences into segments processed at the same time (for few heads), see
+efla_chunk_fwd_scan.
 
 Every call that forms alpha takes ``gate``: GATE_EXACT (0, the default) for the exact coefficient, or
 p in 1 .. GATE_MAX_ORDER for the coefficient of a p-th order Runge-Kutta step of the same dynamics
@@ -227,8 +229,9 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
     tensor of at least chunk_workspace_size(...) bytes, allocated here when not given), "fused" (one
     kernel, no workspace), "scan" (segment-parallel: ``segments`` segments per sequence, 0 = the library's
     choice; workspace of scan_plan(...)[3] bytes) or "auto" (the default: "scan" when the library would
-    cut the sequences into more than one segment -- few heads, long sequences -- else "split"; the scan
-    workspace is then the split one).
+    cut the sequences into more than one segment -- few heads, long sequences; else "fused" for bf16 inputs
+    with d_k >= 32 and 64-token chunks, whose single kernel transforms the chunks in the workgroup and reads
+    every input once; else "split").
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
@@ -255,7 +258,12 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
         if final_state.dtype != torch.float32 or tuple(final_state.shape) != (B, H, d_k, d_v):
             raise ValueError("final_state must be float32 [B,H,d_k,d_v]")
     if method == "auto":
-        method = "scan" if scan_plan(B, H, L, d_k, d_v, int(chunk_size), v.dtype)[0] > 1 else "split"
+        if scan_plan(B, H, L, d_k, d_v, int(chunk_size), v.dtype)[0] > 1:
+            method = "scan"
+        elif v.dtype == torch.bfloat16 and d_k >= 32 and int(chunk_size) == 64:
+            method = "fused"     # the one-launch kernel with in-workgroup UT waves: fewer HBM bytes than split
+        else:
+            method = "split"
     if method == "fused":
         _check(lib.efla_chunk_fwd_slab_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
                                             _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v,
@@ -419,7 +427,7 @@ class _EflaFunction(torch.autograd.Function):
     def forward(ctx, q, k, v, beta, initial_state, chunk_size, gate):
         q, k, v, beta = (x.contiguous() for x in (q, k, v, beta))
         s0 = None if initial_state is None else initial_state.contiguous()
-        o, sf = chunk_fwd(q, k, v, beta, initial_state=s0, chunk_size=chunk_size, method="split", gate=gate)
+        o, sf = chunk_fwd(q, k, v, beta, initial_state=s0, chunk_size=chunk_size, gate=gate)
         ctx.save_for_backward(q, k, v, beta, s0 if s0 is not None else torch.empty(0, device=v.device))
         ctx.has_s0 = s0 is not None
         ctx.chunk_size, ctx.gate = chunk_size, gate

@@ -133,7 +133,7 @@ def test_state_pass_after_ut_transform_equals_split():
     x = W.make_fwd_inputs(w)
     d = fwd_inputs_dev(x, "bf16")
     s0 = torch.from_numpy((0.1 * np.random.default_rng(4).standard_normal((2, 3, 128, 128))).astype(np.float32)).cuda()
-    o1, S1 = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=s0)
+    o1, S1 = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=s0, method="split")
     t = efla.ut_transform(d["k"], d["beta"])
     o2, S2 = efla.state_pass(d["q"], d["k"], d["v"], t, initial_state=s0)
     torch.cuda.synchronize()
