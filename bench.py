@@ -186,13 +186,10 @@ def run_forward(efla, W, torch, steps, warmup):
     nc, nb = (w.L + w.chunk - 1) // w.chunk, (w.chunk // 16) * (w.chunk // 16 + 1) // 2
     t = ws.view(torch.bfloat16).view(w.B, w.H, nc, nb, 64, 4)
 
-    # The MI355X lowers its clock a few milliseconds into sustained load (in a kernel trace the state pass
-    # goes from ~118 us per launch to ~180 us and back), so each timed loop below starts after the same
-    # short idle period; the loops themselves run back to back.
-    def settle():
-        torch.cuda.synchronize()
-        time.sleep(0.5)
-
+    # After an idle period the first ~150 forwards run up to 20 % slower than the steady state that sustained
+    # back-to-back calls reach (a few tens of milliseconds in).  Every loop below therefore queues its own warm-up
+    # calls immediately before its timed calls, with no synchronisation between them: the GPU is still busy with
+    # the warm-up when the first event is recorded, so no interval holds host time or an idle gap.
     def one_call(gate=efla.GATE_EXACT):
         # the library's default form for these sizes: the one-launch forward (efla_chunk_fwd)
         efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, gate=gate)
@@ -201,7 +198,8 @@ def run_forward(efla, W, torch, steps, warmup):
         efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, method="split")
 
     def timed(fn):
-        settle()
+        for _ in range(warmup):
+            fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
@@ -210,63 +208,47 @@ def run_forward(efla, W, torch, steps, warmup):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    def spin():
-        # a spin kernel queued first keeps the GPU busy while the host queues the whole loop, so that no event
-        # interval below holds host time between two launches
-        settle()
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(int(steps * 400e-6 * 2.0e9))   # ~400 us of clock ticks per step queued
+    def per_launch(fns):
+        """Mean time of each of `fns` over `steps` rounds of calling them in turn, events between the calls."""
+        for _ in range(warmup):
+            for fn in fns:
+                fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) * steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            for j, fn in enumerate(fns):
+                fn()
+                ev[len(fns) * i + j + 1].record()
+        torch.cuda.synchronize()
+        return [[ev[len(fns) * i + j].elapsed_time(ev[len(fns) * i + j + 1]) for i in range(steps)]
+                for j in range(len(fns))]
 
-    for _ in range(warmup):
-        one_call()
+    torch.cuda.synchronize()
     ms = timed(one_call)   # the headline: the whole forward, one efla_chunk_fwd call (one kernel) per step
     assert torch.isfinite(S).all().item(), "non-finite final state"
-
-    # the same kernel between HIP events on torch's current stream -- the stream the library launches on --
-    # for its average launch duration
-    spin()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record()
-    for i in range(steps):
-        one_call()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    fused_launch_ms = statistics.mean(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    # the same kernel between HIP events on torch's current stream -- the stream the library launches on -- for
+    # its average launch duration
+    fused_launch_ms = statistics.mean(per_launch([one_call])[0])
 
     # the two-launch form (efla_chunk_fwd_split), then its two launches through their own entry points
     # (efla_ut_transform, then efla_chunk_state_pass: bit-identical results) between events
-    for _ in range(warmup):
-        split_call()
     split_ms = timed(split_call)
-    spin()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
-    for i in range(steps):
-        ev[3 * i].record()
-        efla.ut_transform(k, beta, chunk_size=w.chunk, out=t)
-        ev[3 * i + 1].record()
-        efla.state_pass(q, k, v, t, chunk_size=w.chunk, out=o, final_state=S)
-        ev[3 * i + 2].record()
-    torch.cuda.synchronize()
-    ut_ms = statistics.mean(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps))
-    chain_ms = statistics.mean(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))
+    ut_t, chain_t = per_launch([lambda: efla.ut_transform(k, beta, chunk_size=w.chunk, out=t),
+                                lambda: efla.state_pass(q, k, v, t, chunk_size=w.chunk, out=o, final_state=S)])
+    ut_ms, chain_ms = statistics.mean(ut_t), statistics.mean(chain_t)
 
     # the delta rule's coefficient alpha = beta (gate 1) on the same kernel: steps of the two gates alternate, so
-    # that both see the same clock, and each gate's median step is kept
-    settle()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
-    ev[0].record()
-    for i in range(steps):
-        one_call(efla.GATE_EXACT)
-        ev[2 * i + 1].record()
-        one_call(efla.GATE_DELTANET)
-        ev[2 * i + 2].record()
-    torch.cuda.synchronize()
-    alt_exact_ms = statistics.median(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
-    deltanet_ms = statistics.median(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(steps))
+    # that both see the same clock, and each gate's median step is kept; the same for the one-launch and split
+    # forms
+    ex_t, dn_t = per_launch([lambda: one_call(efla.GATE_EXACT), lambda: one_call(efla.GATE_DELTANET)])
+    alt_exact_ms, deltanet_ms = statistics.median(ex_t), statistics.median(dn_t)
+    f_t, s_t = per_launch([one_call, split_call])
+    alt_fused_ms, alt_split_ms = statistics.median(f_t), statistics.median(s_t)
 
     wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16, method="fused")
     return w, ms, dict(fused_launch_ms=fused_launch_ms, split_ms=split_ms, ut_ms=ut_ms, chain_ms=chain_ms,
                        workspace_bytes=nbytes, deltanet_ms=deltanet_ms, alt_exact_ms=alt_exact_ms,
+                       alt_fused_ms=alt_fused_ms, alt_split_ms=alt_split_ms,
                        launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds))
 
 
@@ -283,7 +265,7 @@ def bwd_algorithmic(B, H, L, dk, dv, C):
     return B * H * nc * (per_chunk + 2 * ut)
 
 
-def run_backward(efla, W, torch, steps=5, warmup=2):
+def run_backward(efla, W, torch, steps=5, warmup=5):
     """The LM-layer backward (B8 H16 L4096 d128 bf16): one efla_chunk_bwd call per step."""
     w = W.workload(3)
     x = W.make_fwd_inputs(w)
@@ -301,10 +283,8 @@ def run_backward(efla, W, torch, steps=5, warmup=2):
 
     def fn():
         return efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=w.chunk, workspace=ws)
-    for _ in range(warmup):
+    for _ in range(warmup):     # queued right before the timed calls (no idle gap: see run_forward)
         out = fn()
-    torch.cuda.synchronize()
-    time.sleep(0.5)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
@@ -323,7 +303,7 @@ def run_backward(efla, W, torch, steps=5, warmup=2):
                          "scope": "whole call (UT transform + 3 launches)"}}
 
 
-def run_long_context(efla, W, torch, steps=8, warmup=2):
+def run_long_context(efla, W, torch, steps=20, warmup=30):
     """The long-context forward (16 heads x 65,536 tokens): the split forward, whose state pass runs 1,024
     chunks back to back per (head, slab), against the segment-parallel one."""
     w = W.workload(4)
@@ -344,10 +324,8 @@ def run_long_context(efla, W, torch, steps=8, warmup=2):
     for method in ("split", "scan"):
         def fn():
             efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, method=method)
-        for _ in range(warmup):
+        for _ in range(warmup):     # queued right before the timed calls (no idle gap: see run_forward)
             fn()
-        torch.cuda.synchronize()
-        time.sleep(0.5)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
@@ -363,7 +341,7 @@ def run_long_context(efla, W, torch, steps=8, warmup=2):
             "scan_speedup": round(res["split"] / res["scan"], 3)}
 
 
-def run_small(efla, W, torch, steps=20, warmup=3):
+def run_small(efla, W, torch, steps=50, warmup=100):
     """The two fp32 parity workloads, timed: the tiny single-head recurrence (B1 H1 L256 d16, chunk 16) and the
     stiff mixed-norm one (B4 H8 L2048 d64, chunk 64, initial state); one efla_chunk_fwd_split call per step,
     median over `steps` HIP-event intervals.  Both are far too small to fill the GPU: launch latency and the
@@ -398,7 +376,7 @@ def run_small(efla, W, torch, steps=20, warmup=3):
     return out
 
 
-def run_decode(efla, W, torch, warmup=3):
+def run_decode(efla, W, torch, warmup=100):
     w = W.workload(5)
     S = torch.from_numpy(W.make_decode_state(w)).cuda()
     toks = []
@@ -408,11 +386,10 @@ def run_decode(efla, W, torch, warmup=3):
                     + (torch.from_numpy(t["beta"]).cuda(),))
     o = torch.empty((w.NH, w.d_v), dtype=torch.bfloat16, device="cuda")
     scratch = S.clone()
-    for i in range(warmup):
-        efla.recurrent_step(*toks[i], scratch, out=o)
-    del scratch
     torch.cuda.synchronize()
-    time.sleep(0.5)   # start from the same clock state as the forward's timed loops
+    # warm-up steps on a copy of the state, queued right before the timed steps (no idle gap: see run_forward)
+    for i in range(warmup):
+        efla.recurrent_step(*toks[i % w.steps], scratch, out=o)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.steps + 1)]
     ev[0].record()
     for s in range(w.steps):
@@ -441,8 +418,8 @@ def cpu_baseline(W, max_threads):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context forward")
@@ -536,6 +513,9 @@ def main():
         # split step minus the state pass estimates it)
         "split": {"entry": "efla_chunk_fwd_split (UT launch, then the state pass)", "ms_per_step": round(split_ms, 5),
                   "tokens_per_s": round(w.B * w.L / (split_ms * 1e-3), 1),
+                  # steps of the two forms alternating, median of each
+                  "alternating_median_ms": {"one_launch": round(info["alt_fused_ms"], 5),
+                                            "split": round(info["alt_split_ms"], 5)},
                   "workspace_written_bytes": info["workspace_bytes"] * 6 // 10,
                   "state_pass": {"kernel": chain_kernel, "bytes_per_launch": chain_bytes,
                                  "avg_launch_ms": round(info["chain_ms"], 5), "achieved_gbs": round(chain_gbs, 1),
