@@ -147,9 +147,13 @@ efla_status scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dty
     if (efla::chunk_grid((int)BH, d_v + d_k, dvs) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
     int64_t G = segments;
     if (G == 0) {
+        // Segments pay for a second state pass; they win only when one segment's grid leaves most of the
+        // 256 compute units idle.  Measured (d 128, bf16): 16 heads x 65,536 tokens best at 8 segments, 32 x 16,384
+        // and 32 x 32,768 at 4; 64 heads x 8,192 tokens is faster unsegmented (2 segments: 20 % slower).
         const int64_t per_seg = BH * (d_v / dvs);   // second-pass workgroups of one segment
         G = 1;
-        while (per_seg * 2 * G <= 256 && NC >= 32 * G) G *= 2;
+        if (per_seg <= 64)
+            while (per_seg * 2 * G <= 256 && NC >= 32 * G) G *= 2;
     }
     if (G > NC) G = NC > 0 ? NC : 1;
     if (G > 65535) return EFLA_ERR_INVALID_ARG;

@@ -245,7 +245,10 @@ efla_status efla_chunk_fwd_scan(const void* q, const void* k, const void* v, con
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Launch shape and workspace of efla_chunk_fwd_scan for these sizes (host only): segments used, chunks per
- * segment, state slab width and workspace bytes.  Errors as efla_chunk_fwd_scan would return for the sizes. */
+ * segment, state slab width and workspace bytes.  Errors as efla_chunk_fwd_scan would return for the sizes.
+ * With segments = 0 the library cuts sequences only when one segment's state pass would run at most 64
+ * workgroups (a quarter of the compute units), then doubles the count while the second pass stays within 256
+ * workgroups and every segment keeps at least 32 chunks; otherwise one segment. */
 efla_status efla_chunk_scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int segments,
                                  int* nseg, int* seg_chunks, int* slab_width, size_t* workspace_bytes);
 
