@@ -260,7 +260,7 @@ struct UtCarry {
     float ar0, ar1;      // gates of rows 16 j + r
     float alpha_mine;    // gate of token 32 h + 16 (g & 1) + r
 };
-constexpr int kUtSplit = 6;   // substitution steps in part 1
+constexpr int kUtSplit = 2;   // substitution steps in part 1 (part 1 holds the Gram products: 2 balances the two)
 
 // steps m = M0 .. M1 - 1 of the right-looking substitution on the transposed diagonal block `at` (rows of At read
 // three steps ahead)
