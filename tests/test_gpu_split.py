@@ -138,3 +138,24 @@ def test_state_pass_after_ut_transform_equals_split():
     o2, S2 = efla.state_pass(d["q"], d["k"], d["v"], t, initial_state=s0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("dtype,d_k,chunk,L,expect", [
+    ("bf16", 128, 64, 300, "fused"),    # the one-launch kernel's shapes
+    ("bf16", 32, 64, 130, "fused"),
+    ("bf16", 128, 32, 300, "split"),    # other chunk sizes: two launches
+    ("bf16", 16, 64, 130, "split"),
+    ("f32", 64, 64, 300, "split"),
+])
+def test_default_method_dispatch(dtype, d_k, chunk, L, expect):
+    """chunk_fwd with no method picks the one-launch forward for bf16, d_k >= 32 and 64-token chunks and the
+    two-launch one otherwise (many heads: no segments); the outputs are bit-identical to that method's."""
+    w = W.workload(3, B=2, H=8, L=L, d_k=d_k, d_v=64, chunk=chunk, dtype=dtype)
+    x = W.make_fwd_inputs(w)
+    d = fwd_inputs_dev(x, dtype)
+    assert efla.scan_plan(w.B, w.H, w.L, d_k, 64, chunk, d["v"].dtype)[0] == 1
+    o0, S0 = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=d["initial_state"], chunk_size=chunk)
+    o1, S1 = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=d["initial_state"], chunk_size=chunk,
+                            method=expect)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(S0, S1)
