@@ -251,7 +251,8 @@ __device__ __forceinline__ void ut_half_lds(const lds_u8* cK, const lds_u8* cB, 
 
 // The same half-chunk transform as ut_half_lds, cut into two parts run in consecutive chunk steps by one wave
 // (the four-UT-wave workgroup: two pairs of waves take alternate chunks, so each has two steps per chunk).  Part 1:
-// keys, lambda, gates, the Gram blocks and the first MS steps of both substitutions; part 2: the remaining steps,
+// keys, the Gram blocks (whose diagonals give lambda), gates and the first kUtSplit steps of both substitutions;
+// part 2: the remaining steps,
 // the diagonal blocks, T_10 and the export.  What part 2 needs stays in the wave's registers (UtCarry) and in its
 // private LDS (the transposed diagonal blocks of A, then Ta^T and T_bb^T).
 struct UtCarry {
@@ -306,36 +307,29 @@ __device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB
             kf[j][kp] = bx8(*reinterpret_cast<const lds_bf16x8*>(cK + (32 * h + 16 * j + r) * RBQ + 16 * ((4 * kp + g) ^ swr)));
     }
     const float beta_mine = reinterpret_cast<const lds_f32*>(cB)[32 * h + (lane & 31)];
-    float lam[2];
+    // the three Gram blocks of the half-chunk, (0, 0), (1, 1) and (1, 0): lane (r, g) holds entries (4 g + i, r)
+    f32x4 gr[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        float sq = 0.0f;
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp) sq += sum_sq(kf[j][kp]);
-        sq += __shfl_xor(sq, 16, 64);
-        sq += __shfl_xor(sq, 32, 64);
-        lam[j] = sq;
+    for (int kp = 0; kp < NKP; ++kp) {
+        gr[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kp], kf[0][kp], gr[0], 0, 0, 0);
+        gr[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kp], kf[1][kp], gr[1], 0, 0, 0);
+        gr[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kp], kf[1][kp], gr[2], 0, 0, 0);
     }
-    u.alpha_mine = gate_alpha(beta_mine, gb ? lam[1] : lam[0], gate);
+    // lambda of row 16 j + r is the diagonal entry (r, r) of block (j, j), held by lane (r, r / 4) as element r % 4
+    const int dsrc = r + 16 * (r >> 2);
+    const float lam0 = __shfl(gr[0][r & 3], dsrc, 64);
+    const float lam1 = __shfl(gr[1][r & 3], dsrc, 64);
+    u.alpha_mine = gate_alpha(beta_mine, gb ? lam1 : lam0, gate);
     u.ar0 = __shfl(u.alpha_mine, r, 64);
     u.ar1 = __shfl(u.alpha_mine, 16 + r, 64);
-    static_for<2>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
+    u.A10 = M::cvt(gr[2] * u.ar1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
         const float arj = j ? u.ar1 : u.ar0;
-        static_for<j + 1>([&](auto lc) {
-            constexpr int l = decltype(lc)::value;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[l][kp], kf[j][kp], acc, 0, 0, 0);
-            if constexpr (l < j) {
-                u.A10 = M::cvt(acc * u.ar1);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sAt[j * kUtHalfAtb + (4 * g + i) * LDAT + r] = (4 * g + i < r) ? arj * acc[i] : 0.0f;
-            }
-        });
-    });
+        for (int i = 0; i < 4; ++i)
+            sAt[j * kUtHalfAtb + (4 * g + i) * LDAT + r] = (4 * g + i < r) ? arj * gr[j][i] : 0.0f;
+    }
     __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 16; ++i) u.sv[i] = (i == r) ? 1.0f : 0.0f;
