@@ -185,11 +185,12 @@ def test_chunk_fwd_ragged_lengths_bf16(L, d_k, d_v, method):
 
 
 @pytest.mark.parametrize("method", METHODS)
-def test_chunk_fwd_empty_sequence_copies_state(method):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])   # bf16, d_k 64, chunk 64: the one-launch kernel
+def test_chunk_fwd_empty_sequence_copies_state(method, dtype):
     rng = np.random.default_rng(5)
     s0 = torch.from_numpy(rng.standard_normal((2, 3, 64, 32)).astype(np.float32)).cuda()
-    e = torch.empty((2, 3, 0, 64), device="cuda")
-    ev = torch.empty((2, 3, 0, 32), device="cuda")
+    e = torch.empty((2, 3, 0, 64), device="cuda", dtype=dtype)
+    ev = torch.empty((2, 3, 0, 32), device="cuda", dtype=dtype)
     b = torch.empty((2, 3, 0), device="cuda")
     o, S = efla.chunk_fwd(e, e, ev, b, initial_state=s0, method=method)
     torch.cuda.synchronize()
