@@ -260,6 +260,12 @@ def test_scan_plan(lib):
     assert efla.scan_plan(1, 16, 65536, 128, 128, 64, torch.bfloat16) == (8, 128, 64, 109051904)
     # many heads: one segment, i.e. the split forward and its workspace
     assert efla.scan_plan(8, 16, 4096, 128, 128, 64, torch.bfloat16) == (1, 64, 64, 41943040)
+    # segments only while one segment's grid fills at most a quarter of the chip (64 workgroups): 32 heads x 2
+    # slabs -> 4 segments; 64 heads x 2 slabs (128 workgroups) -> none, however long the sequences
+    assert efla.scan_plan(2, 16, 16384, 128, 128, 64, torch.bfloat16)[:2] == (4, 64)
+    assert efla.scan_plan(1, 32, 32768, 128, 128, 64, torch.bfloat16)[:2] == (4, 128)
+    assert efla.scan_plan(4, 16, 8192, 128, 128, 64, torch.bfloat16)[:2] == (1, 128)
+    assert efla.scan_plan(4, 16, 65536, 128, 128, 64, torch.bfloat16)[0] == 1
     # explicit counts: no empty segment; at most one per chunk; d_k = 16 narrows the slab
     assert efla.scan_plan(1, 1, 256, 16, 16, 16, torch.float32, 5)[:3] == (4, 4, 16)
     assert efla.scan_plan(1, 1, 100, 64, 64, 64, torch.float32, 9)[:2] == (2, 1)
