@@ -540,9 +540,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
         if (w >= NW) {
             // UT wave u: pair u >> 1 takes the chunks of that parity, u & 1 is its half.  In step c (c0 - 2 <= c < c1)
             // pair c & 1 runs part 1 of chunk c + 2 and the other pair part 2 of chunk c + 1 (which writes its Ta).
-            // Wave 0 also issues the loads: before the first barrier the keys and betas of chunks c0 .. c0 + 2 and
-            // the queries and values of c0; in step c >= c0 the keys and betas of c + 3 and the queries and values
-            // of c + 1, all landed by the end of the step.
+            // The UT waves also issue the loads: wave 0 before the first barrier the keys and betas of chunks
+            // c0 .. c0 + 2 and the queries and values of c0; in step c >= c0 the first wave of the pair running part
+            // 1 (the lighter part) the keys and betas of c + 3 and the queries and values of c + 1, all landed by the
+            // end of the step.
             typedef std::integral_constant<int, 1> I1;
             typedef std::integral_constant<int, 2> I2;
             const int u = w - NW;
@@ -568,7 +569,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
                 }
                 __builtin_amdgcn_s_barrier();
                 for (int c = c0 - 2; c < c1; ++c) {
-                    if (prod && c >= c0) {
+                    if (u == 2 * (c & 1) && c >= c0) {
                         if (c + 3 < c1) issue_kb(c + 3);
                         if (c + 1 < c1) issue_qv(c + 1);
                     }
