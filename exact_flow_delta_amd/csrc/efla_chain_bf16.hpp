@@ -261,7 +261,8 @@ struct UtCarry {
     float ar0, ar1;      // gates of rows 16 j + r
     float alpha_mine;    // gate of token 32 h + 16 (g & 1) + r
 };
-constexpr int kUtSplit = 2;   // substitution steps in part 1 (part 1 holds the Gram products: 2 balances the two)
+constexpr int kUtSplit = 1;   // substitution steps in part 1 (part 1 holds the Gram products and, in the wave that
+                              // issues a step's loads, their issue: 1 balances the two)
 
 // steps m = M0 .. M1 - 1 of the right-looking substitution on the transposed diagonal block `at` (rows of At read
 // three steps ahead)
