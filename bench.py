@@ -76,6 +76,26 @@ def decode_algorithmic(NH, dk, dv, esize=2):
     return NH * (2 * dk * dv * 4 + (2 * dk + 2 * dv) * esize + 4)
 
 
+PREWARM_S = 0.5   # wall-clock seconds of back-to-back calls before every timed loop
+
+
+def prewarm(torch, fn, seconds=PREWARM_S, batch=20):
+    """Back-to-back calls of fn for at least `seconds` of wall-clock time, so that the timed loop after it runs in
+    the GPU's sustained state instead of the slower one after an idle period.  Synchronises after each batch
+    except the last, so the GPU is still busy with it when the caller queues its next work.  Returns (seconds,
+    calls)."""
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        for _ in range(batch):
+            fn()
+        calls += batch
+        if time.perf_counter() - t0 >= seconds:
+            break
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0, calls
+
+
 # kernels whose HBM traffic bench.py reports: the names the profiler may list them under (mangled or
 # demangled) and the sources they are built from (the recorded traffic is used only while these still
 # hash to what was measured)
@@ -157,6 +177,56 @@ def record_traffic(run_dir):
                       for k, v in out.items() if k not in ("note",)}))
 
 
+def record_mfma(run_dir):
+    """profiles/mfma_counters.json from one rocprofv3 --pmc run (host only): per dispatch of every kernel in
+    TRAFFIC_KERNELS that the run holds, the matrix instructions executed (SQ_INSTS_MFMA), the bf16 matrix work in
+    units of 512 flops (SQ_INSTS_VALU_MFMA_MOPS_BF16), the matrix-core busy cycles summed over all SIMDs
+    (SQ_VALU_MFMA_BUSY_CYCLES) and the GPU's active cycles (GRBM_GUI_ACTIVE)."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter CSV under %s" % run_dir)
+    rows = []
+    with open(files[0]) as f:
+        rows = list(csv.DictReader(f))
+    counters = ("SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+    out = {"note": "Matrix-core counters per launch from one rocprofv3 --pmc run (mean over the kernel's dispatches); "
+                   "executed flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / "
+                   "(GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs); valid only while the kernel sources hash to "
+                   "'sources_sha256_16'. Written by bench.py --record-mfma."}
+    for name, info in TRAFFIC_KERNELS.items():
+        per = {}
+        for row in rows:
+            if any(x in row["Kernel_Name"] for x in info["symbol"]) and row["Counter_Name"] in counters:
+                d = per.setdefault(row["Dispatch_Id"], {})
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        if not per:
+            continue
+        mean = {c: statistics.mean(d.get(c, 0.0) for d in per.values()) for c in counters}
+        out[name] = {"sources": info["sources"], "sources_sha256_16": _sources_hash(info["sources"]),
+                     "dispatches": len(per), **mean,
+                     "executed_flops": mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+                     "busy_frac": mean["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, mean["GRBM_GUI_ACTIVE"] * 256 * 4)}
+    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: v.get("executed_flops") for k, v in out.items() if isinstance(v, dict)}))
+
+
+def measured_mfma(kernel):
+    """The committed matrix-core counters of `kernel` (profiles/mfma_counters.json), or None when absent or when
+    the kernel's sources no longer hash to what was measured."""
+    path = os.path.join(ROOT, "profiles", "mfma_counters.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f)[kernel]
+        return entry if _sources_hash(entry["sources"]) == entry["sources_sha256_16"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary (profiles/hbm_traffic.json),
     or None when the kernel's sources no longer hash to what was measured."""
@@ -167,6 +237,23 @@ def measured_traffic(kernel):
         return entry["traffic_bytes"] if _sources_hash(entry["sources"]) == entry["sources_sha256_16"] else None
     except (OSError, KeyError, ValueError):
         return None
+
+
+def mfma_block(flops, tflops, launch_ms, kernel):
+    """The matrix-core figures of the headline kernel: the algorithmic flops of a step against the dense bf16 peak,
+    and -- from the committed rocprofv3 counters, while they match the kernel's sources -- the flops the matrix
+    cores executed per launch over the average launch time measured here, and their busy-cycle fraction."""
+    m = {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops}
+    c = measured_mfma(kernel)
+    if c is None:
+        m.update(executed_flops_per_launch=None, executed_frac=None, busy_frac=None)
+    else:
+        ex = c["executed_flops"] / (launch_ms * 1e-3) / 1e12
+        m.update(executed_flops_per_launch=c["executed_flops"], executed_tflops=round(ex, 2),
+                 executed_frac=round(ex / BF16_PEAK_TFLOPS, 4), busy_frac=round(c["busy_frac"], 4),
+                 counters="profiles/mfma_counters.json")
+    return m
 
 
 def run_forward(efla, W, torch, steps, warmup):
@@ -181,15 +268,16 @@ def run_forward(efla, W, torch, steps, warmup):
     o = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.bfloat16, device="cuda")
     S = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
     del x
-    nbytes = efla.chunk_workspace_size(w.B, w.H, w.L, w.chunk, torch.bfloat16)
+    nbytes = efla.split_workspace_size(w.B, w.H, w.L, w.chunk, torch.bfloat16)
     ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
     nc, nb = (w.L + w.chunk - 1) // w.chunk, (w.chunk // 16) * (w.chunk // 16 + 1) // 2
     t = ws.view(torch.bfloat16).view(w.B, w.H, nc, nb, 64, 4)
 
     # After an idle period the first ~150 forwards run up to 20 % slower than the steady state that sustained
-    # back-to-back calls reach (a few tens of milliseconds in).  Every loop below therefore queues its own warm-up
-    # calls immediately before its timed calls, with no synchronisation between them: the GPU is still busy with
-    # the warm-up when the first event is recorded, so no interval holds host time or an idle gap.
+    # back-to-back calls reach (a few tens of milliseconds in).  Every loop below is therefore preceded by a
+    # pre-warm of back-to-back calls for a fixed wall-clock time (PREWARM_S, whatever --warmup says), and then
+    # queues its own --warmup calls immediately before its timed calls, with no synchronisation between them:
+    # the GPU is still busy when the first event is recorded, so no interval holds host time or an idle gap.
     def one_call(gate=efla.GATE_EXACT):
         # the library's default form for these sizes: the one-launch forward (efla_chunk_fwd)
         efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, gate=gate)
@@ -197,7 +285,9 @@ def run_forward(efla, W, torch, steps, warmup):
     def split_call():
         efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, method="split")
 
-    def timed(fn):
+    def timed(fn, do_prewarm=True):
+        if do_prewarm:
+            prewarm(torch, fn)
         for _ in range(warmup):
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -210,6 +300,7 @@ def run_forward(efla, W, torch, steps, warmup):
 
     def per_launch(fns):
         """Mean time of each of `fns` over `steps` rounds of calling them in turn, events between the calls."""
+        prewarm(torch, lambda: [fn() for fn in fns])
         for _ in range(warmup):
             for fn in fns:
                 fn()
@@ -224,7 +315,8 @@ def run_forward(efla, W, torch, steps, warmup):
                 for j in range(len(fns))]
 
     torch.cuda.synchronize()
-    ms = timed(one_call)   # the headline: the whole forward, one efla_chunk_fwd call (one kernel) per step
+    head_prewarm = prewarm(torch, one_call)   # the headline's pre-warm, reported with the line
+    ms = timed(one_call, do_prewarm=False)   # the headline: the whole forward, one efla_chunk_fwd call (one kernel) per step
     assert torch.isfinite(S).all().item(), "non-finite final state"
     # the same kernel between HIP events on torch's current stream -- the stream the library launches on -- for
     # its average launch duration
@@ -246,7 +338,7 @@ def run_forward(efla, W, torch, steps, warmup):
     alt_fused_ms, alt_split_ms = statistics.median(f_t), statistics.median(s_t)
 
     wg, slab, lds = efla.chunk_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16, method="fused")
-    return w, ms, dict(fused_launch_ms=fused_launch_ms, split_ms=split_ms, ut_ms=ut_ms, chain_ms=chain_ms,
+    return w, ms, dict(prewarm=head_prewarm, fused_launch_ms=fused_launch_ms, split_ms=split_ms, ut_ms=ut_ms, chain_ms=chain_ms,
                        workspace_bytes=nbytes, deltanet_ms=deltanet_ms, alt_exact_ms=alt_exact_ms,
                        alt_fused_ms=alt_fused_ms, alt_split_ms=alt_split_ms,
                        launch=dict(workgroups=wg, slab_width=slab, lds_bytes=lds))
@@ -283,6 +375,7 @@ def run_backward(efla, W, torch, steps=5, warmup=5):
 
     def fn():
         return efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=w.chunk, workspace=ws)
+    prewarm(torch, fn, batch=2)
     for _ in range(warmup):     # queued right before the timed calls (no idle gap: see run_forward)
         out = fn()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -318,12 +411,13 @@ def run_long_context(efla, W, torch, steps=20, warmup=30):
     o = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.bfloat16, device="cuda")
     S = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
     nseg, seg_chunks, _, need = efla.scan_plan(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.bfloat16)
-    ws = torch.empty((max(need, efla.chunk_workspace_size(w.B, w.H, w.L, w.chunk, torch.bfloat16)),),
+    ws = torch.empty((max(need, efla.split_workspace_size(w.B, w.H, w.L, w.chunk, torch.bfloat16)),),
                      dtype=torch.uint8, device="cuda")
     res = {}
     for method in ("split", "scan"):
         def fn():
             efla.chunk_fwd(q, k, v, beta, chunk_size=w.chunk, out=o, final_state=S, workspace=ws, method=method)
+        prewarm(torch, fn)
         for _ in range(warmup):     # queued right before the timed calls (no idle gap: see run_forward)
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -343,9 +437,9 @@ def run_long_context(efla, W, torch, steps=20, warmup=30):
 
 def run_small(efla, W, torch, steps=50, warmup=100):
     """The two fp32 parity workloads, timed: the tiny single-head recurrence (B1 H1 L256 d16, chunk 16) and the
-    stiff mixed-norm one (B4 H8 L2048 d64, chunk 64, initial state); one efla_chunk_fwd_split call per step,
-    median over `steps` HIP-event intervals.  Both are far too small to fill the GPU: launch latency and the
-    length of the chunk chain set their times."""
+    stiff mixed-norm one (B4 H8 L2048 d64, chunk 64, initial state); one efla_chunk_fwd call per step (the form
+    the library picks for the sizes, named in the result), median over `steps` HIP-event intervals.  Both are far
+    too small to fill the GPU: launch latency and the length of the chunk chain set their times."""
     out = {}
     for cfg, name in ((1, "tiny B1 H1 L256 d16 f32 chunk 16"), (2, "stiff B4 H8 L2048 d64 f32 chunk 64")):
         w = W.workload(cfg)
@@ -355,12 +449,12 @@ def run_small(efla, W, torch, steps=50, warmup=100):
         s0 = None if x["initial_state"] is None else torch.from_numpy(x["initial_state"]).cuda()
         o = torch.empty((w.B, w.H, w.L, w.d_v), dtype=torch.float32, device="cuda")
         S = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
-        ws = torch.empty((efla.chunk_workspace_size(w.B, w.H, w.L, w.chunk, torch.float32),), dtype=torch.uint8,
-                         device="cuda")
+        form, nseg, need = efla.fwd_form(w.B, w.H, w.L, w.d_k, w.d_v, w.chunk, torch.float32)
+        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device="cuda")
 
         def fn():
-            efla.chunk_fwd(q, k, v, beta, initial_state=s0, chunk_size=w.chunk, out=o, final_state=S, workspace=ws,
-                           method="split")
+            efla.chunk_fwd(q, k, v, beta, initial_state=s0, chunk_size=w.chunk, out=o, final_state=S, workspace=ws)
+        prewarm(torch, fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -371,7 +465,7 @@ def run_small(efla, W, torch, steps=50, warmup=100):
             ev[i + 1].record()
         torch.cuda.synchronize()
         med = statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-        out["cfg%d" % cfg] = {"workload": name, "median_ms_per_step": round(med, 5),
+        out["cfg%d" % cfg] = {"workload": name, "form": form, "segments": nseg, "median_ms_per_step": round(med, 5),
                               "tokens_per_s": round(w.B * w.L / (med * 1e-3), 1)}
     return out
 
@@ -388,6 +482,8 @@ def run_decode(efla, W, torch, warmup=100):
     scratch = S.clone()
     torch.cuda.synchronize()
     # warm-up steps on a copy of the state, queued right before the timed steps (no idle gap: see run_forward)
+    it = iter(range(1 << 30))
+    prewarm(torch, lambda: efla.recurrent_step(*toks[next(it) % w.steps], scratch, out=o))
     for i in range(warmup):
         efla.recurrent_step(*toks[i % w.steps], scratch, out=o)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.steps + 1)]
@@ -401,18 +497,66 @@ def run_decode(efla, W, torch, warmup=100):
     return w, step_ms
 
 
-def cpu_baseline(W, max_threads):
-    """The fp64 oracle on the full LM-layer forward (all heads, full length) on the host cores."""
+def host_cpu():
+    """(CPU model name, CPUs in this process's affinity mask, threads the oracle may use).  The thread count is the
+    affinity mask's, lowered to OMP_NUM_THREADS when the environment sets it (the host's share of its cores)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    mask = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "").strip()
+    threads = min(mask, int(env)) if env.isdigit() and int(env) > 0 else mask
+    return model, mask, threads
+
+
+def cpu_baseline(W):
+    """The fp64 oracle, as it stands, on the host cores: the full LM-layer forward (all heads, full length) --
+    the headline's rate --, the decode workload (all 8,192 states, its first 8 steps), and the two small fp32
+    workloads on one thread."""
     import oracle
 
+    model, mask, threads = host_cpu()
     w = W.workload(3)
     x = W.make_fwd_inputs(w)
     t0 = time.perf_counter()
-    _, _, used = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], None, n_threads=max_threads, want_o=True,
+    _, _, used = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], None, n_threads=threads, want_o=True,
                             want_state=True)
     dt = time.perf_counter() - t0
-    return dict(value=w.B * w.L / dt, unit="tokens/s", cores=int(used), kind="oracle",
-                sample="full LM-layer forward B8 H16 L4096 d128 (all 128 heads), fp64 token-by-token, %.1f s" % dt)
+    del x
+    res = dict(value=w.B * w.L / dt, unit="tokens/s", cores=int(used), kind="oracle",
+               sample="full LM-layer forward B8 H16 L4096 d128 (all 128 heads), fp64 token-by-token, %.1f s on %d "
+                      "threads" % (dt, used),
+               cpu_model=model, affinity_cpus=mask, omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
+    # the decode workload: its first 8 dependent steps of all 256 x 32 states (each step streams the 1 GiB fp64
+    # state, so the whole 64 would take tens of seconds)
+    dw = W.workload(5)
+    S = W.make_decode_state(dw).astype("float64")
+    nsteps = 8
+    toks = [W.make_decode_token(dw, i) for i in range(nsteps)]
+    t0 = time.perf_counter()
+    for t in toks:
+        _, S, dused = oracle.step(t["q"], t["k"], t["v"], t["beta"], S, n_threads=threads)
+    ddt = time.perf_counter() - t0
+    res["decode"] = {"tokens_per_s": round(dw.B * nsteps / ddt, 1), "seconds": round(ddt, 3), "threads": int(dused),
+                     "sample": "decode 256 seq x 32 heads d128, steps 0-7 of 64, fp64"}
+    # the small fp32 workloads on one thread (their whole size)
+    single = {}
+    for cfg in (1, 2):
+        sw = W.workload(cfg)
+        sx = W.make_fwd_inputs(sw)
+        t0 = time.perf_counter()
+        _, _, u1 = oracle.fwd(sx["q"], sx["k"], sx["v"], sx["beta"], sx["initial_state"], n_threads=1)
+        sdt = time.perf_counter() - t0
+        single["cfg%d" % cfg] = {"tokens_per_s": round(sw.B * sw.L / sdt, 1), "seconds": round(sdt, 4),
+                                 "threads": int(u1)}
+    res["single_thread"] = single
+    return res
 
 
 def main():
@@ -428,9 +572,14 @@ def main():
                     help="run one leg only (for profiling); prints a short JSON line")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter CSVs under DIR (host only)")
+    ap.add_argument("--record-mfma", metavar="DIR", default=None,
+                    help="write profiles/mfma_counters.json from one rocprofv3 matrix-counter run under DIR (host only)")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(args.record_traffic)
+        return
+    if args.record_mfma:
+        record_mfma(args.record_mfma)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -529,8 +678,8 @@ def main():
         "deltanet_gate": {"median_ms_per_step": round(info["deltanet_ms"], 5),
                           "exact_median_ms_per_step": round(info["alt_exact_ms"], 5),
                           "exact_over_deltanet": round(info["alt_exact_ms"] / info["deltanet_ms"], 4)},
-        "mfma": {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
-                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops},
+        "mfma": mfma_block(flops, tflops, info["fused_launch_ms"], fused_kernel),
+        "prewarm": {"seconds": round(info["prewarm"][0], 3), "calls": info["prewarm"][1]},
     }
     if not args.no_decode:
         dw, step_ms = run_decode(efla, W, torch)
@@ -552,8 +701,7 @@ def main():
     if not args.no_bwd:
         result["backward"] = run_backward(efla, W, torch)
     if not args.no_cpu:
-        threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
-        result["cpu_baseline"] = cpu_baseline(W, threads)
+        result["cpu_baseline"] = cpu_baseline(W)
     print(json.dumps(result), flush=True)
 
 

@@ -14,11 +14,11 @@ library is missing, every call raises.
     dq, dk, dv, dbeta, dS0 = chunk_bwd(q, k, v, beta, d_o, initial_state=None, d_final=None)
     o, S = efla_attention(q, k, v, beta, initial_state=None)   # differentiable (torch.autograd)
 
-chunk_fwd picks its form by default: for bf16, d_k >= 32 and 64-token chunks the single kernel
-(method="fused": the chunks' UT transform runs in the same workgroups as the state pass, no workspace),
-otherwise the two-launch form (method="split": UT transform of all chunks into a workspace, then the state
-pass); method="scan" cuts long sequences into segments processed at the same time (for few heads), see
-efla_chunk_fwd_scan.
+chunk_fwd calls efla_chunk_fwd by default, where the library picks the form for the sizes (fwd_form): the
+segment-parallel one for few heads and long sequences (method="scan"), else for bf16, d_k >= 32 and 64-token
+chunks the single kernel (method="fused": the chunks' UT transform runs in the same workgroups as the state
+pass, no workspace), else the two-launch form (method="split": UT transform of all chunks into a workspace,
+then the state pass).
 
 Every call that forms alpha takes ``gate``: GATE_EXACT (0, the default) for the exact coefficient, or
 p in 1 .. GATE_MAX_ORDER for the coefficient of a p-th order Runge-Kutta step of the same dynamics
@@ -40,13 +40,15 @@ import torch
 
 __all__ = ["EflaError", "alpha", "chunk_fwd", "chunk_fwd_layout", "layout_plan", "chunk_bwd", "chunk_bwd_workspace_size",
            "efla_attention", "recurrent_step", "chunk_plan",
-           "chunk_workspace_size", "ut_transform", "state_pass", "scan_plan", "library_path", "load_library"]
+           "split_workspace_size", "fwd_workspace_size", "fwd_form", "ut_transform", "state_pass", "scan_plan", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libefla.so")
 _lib = None
 
-EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_NO_DEVICE, EFLA_ERR_HIP, EFLA_ERR_WORKSPACE = range(6)
+EFLA_OK, EFLA_ERR_INVALID_ARG, EFLA_ERR_UNSUPPORTED, EFLA_ERR_WORKSPACE, EFLA_ERR_NO_DEVICE, EFLA_ERR_HIP = range(6)
+FWD_ONE_LAUNCH, FWD_SPLIT, FWD_SCAN = 0, 1, 2
+FORM_NAMES = {FWD_ONE_LAUNCH: "fused", FWD_SPLIT: "split", FWD_SCAN: "scan"}
 EFLA_F32, EFLA_BF16 = 0, 1
 GATE_EXACT, GATE_DELTANET, GATE_MAX_ORDER = 0, 1, 16
 
@@ -86,14 +88,21 @@ def load_library():
         raise RuntimeError("libefla.so is not built (%s); run `python -m exact_flow_delta_amd.build`" % _LIB_PATH)
     lib = ctypes.CDLL(_LIB_PATH)
     lib.efla_alpha.argtypes = [_vp, _i32, _vp, _vp, _i64, _i32, _vp]
-    lib.efla_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    lib.efla_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _vp, _sz, _vp]
+    lib.efla_chunk_fwd_gate.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _vp, _sz, _vp]
+    lib.efla_chunk_fwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    lib.efla_chunk_fwd_workspace_size.restype = _sz
+    lib.efla_chunk_fwd_form.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32),
+                                        ctypes.POINTER(_i32), ctypes.POINTER(_sz)]
     lib.efla_chunk_fwd_slab.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.efla_recurrent_step.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp]
     lib.efla_chunk_fwd_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                         ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
     lib.efla_chunk_fwd_split_plan.argtypes = lib.efla_chunk_fwd_plan.argtypes
-    lib.efla_chunk_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+    lib.efla_chunk_split_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
     lib.efla_ut_transform.argtypes = [_vp, _vp, _i32, _vp, _sz, _i32, _i32, _i32, _i32, _i32, _vp]
     lib.efla_chunk_fwd_split.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]
@@ -117,8 +126,8 @@ def load_library():
     lib.efla_chunk_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
     lib.efla_chunk_state_pass.argtypes = [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
-    for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
-               "efla_chunk_fwd_split_plan", "efla_chunk_workspace_size", "efla_ut_transform", "efla_chunk_fwd_split",
+    for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_gate", "efla_chunk_fwd_form", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
+               "efla_chunk_fwd_split_plan", "efla_chunk_split_workspace_size", "efla_ut_transform", "efla_chunk_fwd_split",
                "efla_chunk_state_pass"):
         getattr(lib, fn).restype = _i32
     lib.efla_status_string.argtypes = [_i32]
@@ -188,13 +197,28 @@ def _dtype_of(dtype) -> int:
     return EFLA_BF16 if dtype == torch.bfloat16 else EFLA_F32
 
 
-def chunk_workspace_size(B, H, L, chunk=64, dtype=torch.bfloat16) -> int:
+def split_workspace_size(B, H, L, chunk=64, dtype=torch.bfloat16) -> int:
     """Bytes of workspace the two-launch chunked forward needs (= size of the UT transform output)."""
     lib = load_library()
     n = _sz()
-    _check(lib.efla_chunk_workspace_size(B, H, L, chunk, _dtype_of(dtype), ctypes.byref(n)),
-           "efla_chunk_workspace_size")
+    _check(lib.efla_chunk_split_workspace_size(B, H, L, chunk, _dtype_of(dtype), ctypes.byref(n)),
+           "efla_chunk_split_workspace_size")
     return n.value
+
+
+def fwd_workspace_size(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace efla_chunk_fwd needs for these sizes (0 for the one-launch form)."""
+    return int(load_library().efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, _dtype_of(dtype)))
+
+
+def fwd_form(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16):
+    """(form name, segments, workspace bytes) efla_chunk_fwd picks for these sizes: "fused" (the one-launch
+    kernel), "split" or "scan"."""
+    lib = load_library()
+    f, ns, nb = _i32(), _i32(), _sz()
+    _check(lib.efla_chunk_fwd_form(B, H, L, d_k, d_v, chunk, _dtype_of(dtype), ctypes.byref(f), ctypes.byref(ns),
+                                   ctypes.byref(nb)), "efla_chunk_fwd_form")
+    return FORM_NAMES[f.value], ns.value, nb.value
 
 
 def ut_transform(k, beta, chunk_size=64, out=None, gate=GATE_EXACT):
@@ -225,13 +249,12 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
 
     Returns (o [B,H,L,d_v] in the input dtype, final state [B,H,d_k,d_v] fp32 or None).
     ``final_state`` may be passed (and may be ``initial_state`` itself) to receive the state in place.
-    ``method`` is "split" (UT transform launch + state-pass launch, through ``workspace``: a device
-    tensor of at least chunk_workspace_size(...) bytes, allocated here when not given), "fused" (one
-    kernel, no workspace), "scan" (segment-parallel: ``segments`` segments per sequence, 0 = the library's
-    choice; workspace of scan_plan(...)[3] bytes) or "auto" (the default: "scan" when the library would
-    cut the sequences into more than one segment -- few heads, long sequences; else "fused" for bf16 inputs
-    with d_k >= 32 and 64-token chunks, whose single kernel transforms the chunks in the workgroup and reads
-    every input once; else "split").
+    ``method`` is "auto" (the default: efla_chunk_fwd, where the library picks the form for the sizes, see
+    fwd_form; ``workspace``: a device tensor of at least fwd_workspace_size(...) bytes, allocated here when
+    not given), "split" (UT transform launch + state-pass launch, efla_chunk_fwd_split; workspace of
+    split_workspace_size(...) bytes), "fused" (one kernel, no workspace: efla_chunk_fwd_slab) or "scan"
+    (segment-parallel: ``segments`` segments per sequence, 0 = the library's choice; workspace of
+    scan_plan(...)[3] bytes).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
@@ -258,19 +281,24 @@ def chunk_fwd(q, k, v, beta, initial_state=None, output_final_state=True, chunk_
         if final_state.dtype != torch.float32 or tuple(final_state.shape) != (B, H, d_k, d_v):
             raise ValueError("final_state must be float32 [B,H,d_k,d_v]")
     if method == "auto":
-        if scan_plan(B, H, L, d_k, d_v, int(chunk_size), v.dtype)[0] > 1:
-            method = "scan"
-        elif v.dtype == torch.bfloat16 and d_k >= 32 and int(chunk_size) == 64:
-            method = "fused"     # the one-launch kernel with in-workgroup UT waves: fewer HBM bytes than split
-        else:
-            method = "split"
+        need = fwd_workspace_size(B, H, L, d_k, d_v, int(chunk_size), v.dtype)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+        if workspace is not None:
+            _dev_tensor(workspace, "workspace")
+        _check(lib.efla_chunk_fwd_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
+                                       _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v, int(chunk_size),
+                                       int(gate), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                       _stream(v.device)), "efla_chunk_fwd")
+        return out, final_state
     if method == "fused":
         _check(lib.efla_chunk_fwd_slab_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(out),
                                             _ptr(initial_state), _ptr(final_state), B, H, L, d_k, d_v,
                                             int(chunk_size), int(dv_slab), int(gate), _stream(v.device)),
-               "efla_chunk_fwd")
+               "efla_chunk_fwd_slab")
     elif method == "split":
-        need = chunk_workspace_size(B, H, L, int(chunk_size), v.dtype)
+        need = split_workspace_size(B, H, L, int(chunk_size), v.dtype)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
         _dev_tensor(workspace, "workspace")

@@ -216,16 +216,16 @@ int64_t chunk_grid(int BH, int d_v, int dvs) { return (int64_t)((BH + 7) / 8) * 
 
 extern "C" {
 
-int efla_version(void) { return 10400; }
+int efla_version(void) { return 20000; }
 
 const char* efla_status_string(efla_status s) {
     switch (s) {
         case EFLA_OK: return "EFLA_OK";
         case EFLA_ERR_INVALID_ARG: return "EFLA_ERR_INVALID_ARG: invalid argument";
         case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED: size or type combination not built";
+        case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case EFLA_ERR_NO_DEVICE: return "EFLA_ERR_NO_DEVICE: no HIP device";
         case EFLA_ERR_HIP: return "EFLA_ERR_HIP: HIP runtime error";
-        case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     }
     return "EFLA: unknown status";
 }
@@ -293,7 +293,7 @@ efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, con
 }
 
 
-efla_status efla_chunk_workspace_size(int B, int H, int L, int chunk, efla_dtype dtype, size_t* bytes) {
+efla_status efla_chunk_split_workspace_size(int B, int H, int L, int chunk, efla_dtype dtype, size_t* bytes) {
     if (!valid_dtype(dtype) || B < 0 || H < 0 || L < 0 || !bytes) return EFLA_ERR_INVALID_ARG;
     if (!valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
     *bytes = ut_bytes((int64_t)B * H, L, chunk, dtype);
@@ -694,11 +694,81 @@ efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const fl
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_bwd launch");
 }
 
+namespace {
+
+// The form efla_chunk_fwd takes for these sizes: the segment-parallel one when the automatic segment count is
+// above one (few heads, long sequences), else the one-launch kernel for bf16 with d_k >= 32 and 64-token chunks,
+// else the split form; and the workspace that form needs.
+struct FwdForm {
+    int form;
+    ScanPlan scan;
+    size_t workspace;
+};
+
+efla_status fwd_form(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, FwdForm* f) {
+    efla_status st = scan_plan(B, H, L, d_k, d_v, chunk, dt, 0, &f->scan);
+    if (st != EFLA_OK) return st;
+    int dvs = 0;
+    if (f->scan.nseg > 1) {
+        f->form = EFLA_FWD_SCAN;
+        f->workspace = f->scan.total;
+    } else if (dt == EFLA_BF16 && d_k >= 32 && chunk == 64) {
+        st = check_chunk_sizes(false, B, H, L, d_k, d_v, chunk, dt, 0, &dvs);
+        if (st != EFLA_OK) return st;
+        f->form = EFLA_FWD_ONE_LAUNCH;
+        f->workspace = 0;
+    } else {
+        st = check_chunk_sizes(true, B, H, L, d_k, d_v, chunk, dt, 0, &dvs);
+        if (st != EFLA_OK) return st;
+        f->form = EFLA_FWD_SPLIT;
+        f->workspace = ut_bytes((int64_t)B * H, L, chunk, dt);
+    }
+    return EFLA_OK;
+}
+
+}  // namespace
+
+size_t efla_chunk_fwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype) {
+    FwdForm f;
+    return fwd_form(B, H, L, d_k, d_v, chunk, dtype, &f) == EFLA_OK ? f.workspace : 0;
+}
+
+efla_status efla_chunk_fwd_form(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int* form,
+                                int* segments, size_t* workspace_bytes) {
+    FwdForm f;
+    const efla_status st = fwd_form(B, H, L, d_k, d_v, chunk, dtype, &f);
+    if (st != EFLA_OK) return st;
+    if (form) *form = f.form;
+    if (segments) *segments = f.form == EFLA_FWD_SCAN ? f.scan.nseg : 1;
+    if (workspace_bytes) *workspace_bytes = f.workspace;
+    return EFLA_OK;
+}
+
+efla_status efla_chunk_fwd_gate(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                void* o, const float* initial_state, float* final_state, int B, int H, int L, int d_k,
+                                int d_v, int chunk, int gate, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
+    FwdForm f;
+    const efla_status st = fwd_form(B, H, L, d_k, d_v, chunk, dtype, &f);
+    if (st != EFLA_OK) return st;
+    if (f.form == EFLA_FWD_ONE_LAUNCH)
+        return efla_chunk_fwd_slab_gate(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v,
+                                        chunk, 0, gate, stream);
+    // the workspace is checked against the stricter 256-byte alignment of the scan form for every form
+    if (f.workspace > 0 && (int64_t)B * H > 0 && (L > 0 || final_state) && workspace && !aligned(workspace, 256))
+        return EFLA_ERR_WORKSPACE;
+    if (f.form == EFLA_FWD_SCAN)
+        return efla_chunk_fwd_scan(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, 0,
+                                   gate, workspace, workspace_bytes, stream);
+    return split_entry(true, q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, 0, gate,
+                       workspace, workspace_bytes, stream);
+}
+
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype, void* o,
                            const float* initial_state, float* final_state, int B, int H, int L, int d_k, int d_v,
-                           int chunk, void* stream) {
-    return efla_chunk_fwd_slab(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, 0,
-                               stream);
+                           int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    return efla_chunk_fwd_gate(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk,
+                               EFLA_GATE_EXACT, workspace, workspace_bytes, stream);
 }
 
 efla_status efla_recurrent_step_gate(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,

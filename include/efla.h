@@ -45,9 +45,9 @@ typedef enum {
     EFLA_OK = 0,
     EFLA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, overlapping buffers, bad enum */
     EFLA_ERR_UNSUPPORTED = 2,   /* d_k, d_v, chunk or dtype combination this build does not provide    */
-    EFLA_ERR_NO_DEVICE = 3,     /* no HIP device is visible to the process                             */
-    EFLA_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed                          */
-    EFLA_ERR_WORKSPACE = 5      /* workspace / output buffer missing, misaligned or smaller than needed */
+    EFLA_ERR_WORKSPACE = 3,     /* workspace / output buffer missing, misaligned or smaller than needed */
+    EFLA_ERR_NO_DEVICE = 4,     /* no HIP device is visible to the process                             */
+    EFLA_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed                          */
 } efla_status;
 
 typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
@@ -93,7 +93,8 @@ efla_status efla_alpha_gate(const void* k, efla_dtype k_dtype, const float* beta
  * efla_chunk_fwd -- the whole sequence forward: every o_t and (optionally) the final state.
  * Chunkwise-parallel form ("Exact Flow Linear Attention", Metodologia item 3: the update keeps the
  * rank-1 delta-rule structure, so the WY/UT chunk scheme applies; "Error-Free Linear Attention is a
- * Free Lunch", Step 4: within-chunk transforms in parallel, chunks joined by passing the state).
+ * Free Lunch", Step 4 and the pipeline summary: within-chunk transforms in parallel, chunks joined by
+ * passing the state, "for each token (or for each chunk in parallel)").
  * Per chunk of C tokens with state S entering it:
  *   A = strict_lower(diag(alpha) K K^T),  T = (I + A)^{-1},  R = V - K S,  Delta = T diag(alpha) R,
  *   O = Q S + lower_incl(Q K^T) Delta,    S <- S + K^T Delta
@@ -107,20 +108,59 @@ efla_status efla_alpha_gate(const void* k, efla_dtype k_dtype, const float* beta
  *   final_state   [B,H,d_k,d_v] fp32 or NULL (= not written).  May be the same pointer as
  *                 initial_state (in-place state passing); any other overlap is rejected.
  *   chunk         16, 32 or 64 tokens per chunk
+ *   workspace     device memory of at least efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype)
+ *                 bytes, 256-byte aligned, overlapping no other argument; may be NULL when that size is 0.
+ *                 Smaller, NULL or misaligned when needed: EFLA_ERR_WORKSPACE.  Its contents on return are
+ *                 unspecified; calls that share a workspace must be ordered on one stream.
+ * The library picks the form for the sizes (efla_chunk_fwd_form reports it; every form gives the same result
+ * up to rounding, and the same form always gives bit-identical results):
+ *   EFLA_FWD_SCAN        few (batch, head) pairs and long sequences (one segment's state pass would occupy at
+ *                        most a quarter of the compute units): the segment-parallel form of efla_chunk_fwd_scan
+ *                        with the library's segment count;
+ *   EFLA_FWD_ONE_LAUNCH  otherwise, bf16 with d_k >= 32 and 64-token chunks: one kernel whose workgroups form
+ *                        the chunks' T diag(alpha) themselves (efla_chunk_fwd_slab); no workspace;
+ *   EFLA_FWD_SPLIT       otherwise: the UT transform of every chunk into the workspace, then the state pass
+ *                        (efla_chunk_fwd_split).
  * The state is carried in fp32 for the whole sequence.  L == 0 copies initial_state (or zeros) to
  * final_state.  q, k, v, beta and o may be NULL only when L == 0.
- * One launch and no workspace: each workgroup forms the chunks' T diag(alpha) itself.
  */
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
                            efla_dtype dtype, void* o, const float* initial_state, float* final_state,
-                           int B, int H, int L, int d_k, int d_v, int chunk, void* stream);
+                           int B, int H, int L, int d_k, int d_v, int chunk,
+                           void* workspace, size_t workspace_bytes, void* stream);
+/* efla_chunk_fwd with a gate (see "Gates" above); efla_chunk_fwd is gate EFLA_GATE_EXACT. */
+efla_status efla_chunk_fwd_gate(const void* q, const void* k, const void* v, const float* beta,
+                                efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                int B, int H, int L, int d_k, int d_v, int chunk, int gate,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * efla_chunk_fwd_slab -- efla_chunk_fwd with an explicit split of the d_v columns of the state
- * across workgroups: each workgroup owns `dv_slab` columns (16, 32 or 64, dividing d_v; 0 = the
- * library's choice).  Columns of S evolve independently, so every valid split gives the same
- * result up to rounding; this exists to test and tune that split.  Same arguments and errors as
- * efla_chunk_fwd otherwise.
+ * efla_chunk_fwd_workspace_size -- bytes of workspace efla_chunk_fwd needs for these sizes (host only, no
+ * device needed): 0 for the one-launch form; the UT output for the split form; the UT output and the
+ * segments' states for the scan form.  Sizes efla_chunk_fwd would reject give 0 (the call itself then
+ * returns the error).
+ */
+size_t efla_chunk_fwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype);
+
+/* The forms efla_chunk_fwd chooses between (see there). */
+typedef enum { EFLA_FWD_ONE_LAUNCH = 0, EFLA_FWD_SPLIT = 1, EFLA_FWD_SCAN = 2 } efla_fwd_form;
+
+/*
+ * efla_chunk_fwd_form -- the form efla_chunk_fwd takes for these sizes, its segment count (1 unless
+ * EFLA_FWD_SCAN) and its workspace bytes (host only).  Any output pointer may be NULL.  Returns the error
+ * efla_chunk_fwd would return for the sizes alone, else EFLA_OK.
+ */
+efla_status efla_chunk_fwd_form(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                int* form, int* segments, size_t* workspace_bytes);
+
+/*
+ * efla_chunk_fwd_slab -- the forward in one launch and without workspace, with an explicit split of the d_v
+ * columns of the state across workgroups: each workgroup owns `dv_slab` columns (16, 32 or 64, dividing d_v;
+ * 0 = the library's choice).  For bf16, d_k >= 32 and 64-token chunks the kernel is the one of efla_chunk_fwd's
+ * one-launch form (each workgroup runs the state pass and, on waves of its own, the chunks' UT transform);
+ * otherwise a fused kernel that repeats every chunk's UT transform in each of its head's workgroups.  Columns of
+ * S evolve independently, so every valid split gives the same result up to rounding.  Same arguments and errors
+ * as efla_chunk_fwd otherwise (there is no workspace).
  */
 efla_status efla_chunk_fwd_slab(const void* q, const void* k, const void* v, const float* beta,
                                 efla_dtype dtype, void* o, const float* initial_state, float* final_state,
@@ -153,12 +193,12 @@ efla_status efla_recurrent_step_gate(const void* q, const void* k, const void* v
                                      int64_t NH, int d_k, int d_v, int gate, void* stream);
 
 /*
- * efla_chunk_workspace_size -- bytes of the workspace efla_chunk_fwd_split needs, which is also the
+ * efla_chunk_split_workspace_size -- bytes of the workspace efla_chunk_fwd_split needs, which is also the
  * size of the efla_ut_transform output: ceil(L / chunk) * (chunk/16)(chunk/16 + 1)/2 * 256 elements of
  * the storage type per (batch, head).  Host only.  Fills *bytes and returns EFLA_OK, or INVALID_ARG
  * (negative size, bad dtype, NULL bytes) / UNSUPPORTED (chunk).
  */
-efla_status efla_chunk_workspace_size(int B, int H, int L, int chunk, efla_dtype dtype, size_t* bytes);
+efla_status efla_chunk_split_workspace_size(int B, int H, int L, int chunk, efla_dtype dtype, size_t* bytes);
 
 /*
  * efla_ut_transform -- the intra-chunk UT transform alone: for every chunk of C = chunk tokens of every
@@ -169,7 +209,7 @@ efla_status efla_chunk_workspace_size(int B, int H, int L, int chunk, efla_dtype
  * keeps the delta-rule rank-1 form, so the WY/UT representation applies).  A short last chunk is padded
  * with zero keys and zero beta, so its missing rows and columns of T diag(alpha) are zero.
  *   k      [B,H,L,d_k] dtype, read only;  beta [B,H,L] fp32, read only
- *   t_out  written, t_out_bytes >= efla_chunk_workspace_size(...) (else EFLA_ERR_WORKSPACE), 16-byte
+ *   t_out  written, t_out_bytes >= efla_chunk_split_workspace_size(...) (else EFLA_ERR_WORKSPACE), 16-byte
  *          aligned, no overlap with k or beta.  Layout, in the storage type, per (bh, chunk c): the
  *          (C/16)(C/16+1)/2 lower 16x16 blocks (rb, kb), kb <= rb, in the order rb (rb+1)/2 + kb, each as
  *          256 elements [lane][j] with lane = 16 g + r holding (T diag(alpha))[16 rb + r][16 kb + 4 g + j]
@@ -187,7 +227,7 @@ efla_status efla_ut_transform_gate(const void* k, const float* beta, efla_dtype 
  * efla_chunk_fwd_split -- efla_chunk_fwd as two launches on `stream`: efla_ut_transform of every chunk into
  * `workspace`, then the inter-chunk state pass, which reads T diag(alpha) from it.  Same operator, arguments,
  * aliasing rules and errors as efla_chunk_fwd_slab, plus:
- *   workspace        device memory of at least efla_chunk_workspace_size(B, H, L, chunk, dtype) bytes,
+ *   workspace        device memory of at least efla_chunk_split_workspace_size(B, H, L, chunk, dtype) bytes,
  *                    16-byte aligned, overlapping no other argument (else EFLA_ERR_WORKSPACE /
  *                    EFLA_ERR_INVALID_ARG); its contents on return are the UT output described above,
  *                    except that with bf16 inputs, d_k >= 32 and chunk 64 only the blocks (rb, kb) with
@@ -215,7 +255,7 @@ efla_status efla_chunk_fwd_split_gate(const void* q, const void* k, const void* 
  * ("Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 4: chunks joined by passing the
  * state; Step 3: o_t = S_t^T q_t after each token's update).  efla_chunk_fwd_split is efla_ut_transform
  * followed by this call, and gives bit-identical results.
- *   t_in  read only, t_in_bytes >= efla_chunk_workspace_size(...) (else EFLA_ERR_WORKSPACE), 16-byte
+ *   t_in  read only, t_in_bytes >= efla_chunk_split_workspace_size(...) (else EFLA_ERR_WORKSPACE), 16-byte
  *         aligned, overlapping no output.  Other arguments as efla_chunk_fwd_slab (there is no beta).
  */
 efla_status efla_chunk_state_pass(const void* q, const void* k, const void* v, const void* t_in, size_t t_in_bytes,

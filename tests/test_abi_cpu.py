@@ -14,7 +14,7 @@ import exact_flow_delta_amd as efla
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "efla.h")
 
-OK, INVALID, UNSUPPORTED, NO_DEVICE, HIP, WORKSPACE = range(6)
+OK, INVALID, UNSUPPORTED, WORKSPACE, NO_DEVICE, HIP = range(6)
 F32, BF16 = 0, 1
 
 pytestmark = pytest.mark.skipif(not os.path.exists(efla.library_path()), reason="libefla.so not built")
@@ -22,7 +22,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(efla.library_path()), reason=
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:efla_status|const char\*|int)\s+(efla_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:efla_status|const char\*|int|size_t)\s+(efla_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -44,6 +44,18 @@ def test_exports_match_header(lib):
     assert {"efla_alpha", "efla_chunk_fwd", "efla_recurrent_step"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "missing export " + n
+
+
+def test_status_values_match_header(lib):
+    # the numeric values are part of the ABI: read them from the header and from the library's strings
+    text = open(HEADER).read()
+    vals = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"(EFLA_(?:OK|ERR_\w+))\s*=\s*(\d+)", text))
+    assert vals == {"EFLA_OK": 0, "EFLA_ERR_INVALID_ARG": 1, "EFLA_ERR_UNSUPPORTED": 2, "EFLA_ERR_WORKSPACE": 3,
+                    "EFLA_ERR_NO_DEVICE": 4, "EFLA_ERR_HIP": 5}
+    for name, v in vals.items():
+        assert lib.efla_status_string(v).decode().startswith(name)
+    assert (efla.EFLA_OK, efla.EFLA_ERR_INVALID_ARG, efla.EFLA_ERR_UNSUPPORTED, efla.EFLA_ERR_WORKSPACE,
+            efla.EFLA_ERR_NO_DEVICE, efla.EFLA_ERR_HIP) == (0, 1, 2, 3, 4, 5)
 
 
 def test_status_strings_and_version(lib):
@@ -157,14 +169,14 @@ def test_binding_refuses_cpu_tensors():
 
 def test_workspace_size(lib):
     # per (batch, head) and chunk: (C/16)(C/16+1)/2 blocks of 256 elements
-    assert efla.chunk_workspace_size(2, 3, 100, 64, torch.bfloat16) == 6 * 2 * 10 * 256 * 2
-    assert efla.chunk_workspace_size(2, 3, 100, 16, torch.float32) == 6 * 7 * 1 * 256 * 4
-    assert efla.chunk_workspace_size(8, 16, 4096, 64, torch.bfloat16) == 128 * 64 * 10 * 512
-    assert efla.chunk_workspace_size(1, 1, 0, 32, torch.bfloat16) == 0
+    assert efla.split_workspace_size(2, 3, 100, 64, torch.bfloat16) == 6 * 2 * 10 * 256 * 2
+    assert efla.split_workspace_size(2, 3, 100, 16, torch.float32) == 6 * 7 * 1 * 256 * 4
+    assert efla.split_workspace_size(8, 16, 4096, 64, torch.bfloat16) == 128 * 64 * 10 * 512
+    assert efla.split_workspace_size(1, 1, 0, 32, torch.bfloat16) == 0
     n = ctypes.c_size_t()
-    assert lib.efla_chunk_workspace_size(1, 1, 8, 48, BF16, ctypes.byref(n)) == UNSUPPORTED
-    assert lib.efla_chunk_workspace_size(1, -1, 8, 64, BF16, ctypes.byref(n)) == INVALID
-    assert lib.efla_chunk_workspace_size(1, 1, 8, 64, BF16, None) == INVALID
+    assert lib.efla_chunk_split_workspace_size(1, 1, 8, 48, BF16, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.efla_chunk_split_workspace_size(1, -1, 8, 64, BF16, ctypes.byref(n)) == INVALID
+    assert lib.efla_chunk_split_workspace_size(1, 1, 8, 64, BF16, None) == INVALID
 
 
 def _split(lib, **kw):
@@ -434,3 +446,77 @@ def test_bwd_argument_errors(lib):
 def test_bwd_reaches_the_device_check(lib):
     assert _bwd_call(lib) == NO_DEVICE
     assert _bwd_call(lib, s0=P(12), dsf=P(13), gate=3) == NO_DEVICE
+
+
+def _form(lib, B, H, L, dk, dv, C, dt):
+    f, ns, nb = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_size_t(7)
+    st = lib.efla_chunk_fwd_form(B, H, L, dk, dv, C, dt, ctypes.byref(f), ctypes.byref(ns), ctypes.byref(nb))
+    return st, f.value, ns.value, nb.value
+
+
+def test_fwd_form_policy(lib):
+    # the LM-layer shape: the one-launch kernel, no workspace
+    assert _form(lib, 8, 16, 4096, 128, 128, 64, BF16) == (OK, efla.FWD_ONE_LAUNCH, 1, 0)
+    assert lib.efla_chunk_fwd_workspace_size(8, 16, 4096, 128, 128, 64, BF16) == 0
+    # 16 heads x 65,536 tokens: the segment-parallel form, with the scan plan's segments and workspace
+    st, form, ns, nb = _form(lib, 1, 16, 65536, 128, 128, 64, BF16)
+    assert (st, form) == (OK, efla.FWD_SCAN) and ns > 1
+    n, b = ctypes.c_int(), ctypes.c_size_t()
+    assert lib.efla_chunk_scan_plan(1, 16, 65536, 128, 128, 64, BF16, 0, ctypes.byref(n), None, None,
+                                    ctypes.byref(b)) == OK
+    assert (ns, nb) == (n.value, b.value)
+    assert lib.efla_chunk_fwd_workspace_size(1, 16, 65536, 128, 128, 64, BF16) == b.value
+    # fp32, and bf16 with chunks below 64 or d_k = 16: the split form, whose workspace is the UT output
+    for args in [(1, 1, 256, 16, 16, 16, F32), (2, 3, 100, 64, 64, 32, BF16), (2, 3, 100, 16, 64, 64, BF16),
+                 (8, 16, 300, 64, 64, 64, F32)]:
+        B, H, L, dk, dv, C, dt = args
+        st, form, ns, nb = _form(lib, *args)
+        assert (st, form, ns) == (OK, efla.FWD_SPLIT, 1), args
+        m = ctypes.c_size_t()
+        assert lib.efla_chunk_split_workspace_size(B, H, L, C, dt, ctypes.byref(m)) == OK
+        assert nb == m.value == lib.efla_chunk_fwd_workspace_size(*args), args
+    # invalid sizes: the call's error, and a size of 0
+    assert _form(lib, 1, 1, 8, 48, 64, 64, BF16)[0] == UNSUPPORTED
+    assert _form(lib, 1, 1, 8, 64, 64, 8, BF16)[0] == UNSUPPORTED
+    assert _form(lib, -1, 1, 8, 64, 64, 64, BF16)[0] == INVALID
+    assert _form(lib, 1, 1, 8, 64, 64, 64, 9)[0] == INVALID
+    assert lib.efla_chunk_fwd_workspace_size(1, 1, 8, 48, 64, 64, BF16) == 0
+    assert lib.efla_chunk_fwd_form(8, 16, 4096, 128, 128, 64, BF16, None, None, None) == OK
+    # the binding reports the same
+    assert efla.fwd_form(8, 16, 4096, 128, 128, 64, torch.bfloat16) == ("fused", 1, 0)
+    assert efla.fwd_form(1, 16, 65536, 128, 128, 64, torch.bfloat16)[0] == "scan"
+    assert efla.fwd_workspace_size(4, 8, 2048, 64, 64, 64, torch.float32) == \
+        efla.fwd_form(4, 8, 2048, 64, 64, 64, torch.float32)[2]
+
+
+def _fwd(lib, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=BF16, o=P(5), s0=None, sf=P(6), B=2, H=3, L=100, dk=64, dv=64,
+             C=32, ws=P(7), wsb=6 * 4 * 3 * 256 * 2, gate=0)
+    a.update(kw)
+    return lib.efla_chunk_fwd_gate(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["o"], a["s0"], a["sf"], a["B"],
+                                   a["H"], a["L"], a["dk"], a["dv"], a["C"], a["gate"], a["ws"], a["wsb"], None)
+
+
+def test_chunk_fwd_workspace_errors(lib):
+    need = lib.efla_chunk_fwd_workspace_size(2, 3, 100, 64, 64, 32, BF16)
+    assert need == 6 * 4 * 3 * 256 * 2            # split form: 4 chunks of 32 tokens, 3 blocks each
+    assert _fwd(lib, ws=None) == WORKSPACE
+    assert _fwd(lib, wsb=need - 1) == WORKSPACE
+    assert _fwd(lib, ws=ctypes.c_void_p(0x7F0700000000 + 16)) == WORKSPACE     # not 256-byte aligned
+    assert _fwd(lib, ws=P(6)) == INVALID                                      # is the final state
+    assert _fwd(lib, gate=17) == INVALID
+    assert _fwd(lib, dk=96) == UNSUPPORTED
+    assert _fwd(lib, B=0, ws=None, wsb=0) == OK
+    # the one-launch form takes no workspace: NULL is fine
+    assert _fwd(lib, C=64, ws=None, wsb=0, dk=128, dv=128, B=0) == OK
+    # the plain entry is the exact gate
+    assert lib.efla_chunk_fwd(P(1), P(2), P(3), P(4), BF16, P(5), None, P(6), 2, 3, 100, 64, 64, 32, None, 0,
+                              None) == WORKSPACE
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_chunk_fwd_reaches_device_check(lib):
+    assert _fwd(lib) == NO_DEVICE
+    assert _fwd(lib, C=64, dk=128, dv=128, ws=None, wsb=0) == NO_DEVICE                      # one launch
+    need = lib.efla_chunk_fwd_workspace_size(1, 16, 65536, 128, 128, 64, BF16)
+    assert _fwd(lib, B=1, H=16, L=65536, dk=128, dv=128, C=64, ws=P(8), wsb=need) == NO_DEVICE  # scan

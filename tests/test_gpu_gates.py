@@ -60,16 +60,23 @@ def test_chunk_fwd_gates(dtype, gate, method):
     assert eo < TOL[dtype] and eS < TOL[dtype], (dtype, gate, method, eo, eS)
 
 
+@pytest.mark.parametrize("method", ["auto", "split", "fused"])
+@pytest.mark.parametrize("gate", GATES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_chunk_fwd_gate_headline_shape(dtype):
-    """d_k = d_v = 128, chunk 64: the per-wave UT kernel (bf16) and the swizzled state pass take the gate."""
+def test_chunk_fwd_gate_headline_shape(dtype, gate, method):
+    """d_k = d_v = 128, chunk 64, a ragged length: for bf16 the one-launch kernel ("auto" and "fused"), whose UT
+    waves form every gate's alpha, and the diagonal-block UT launch of the split form; for fp32 the split form."""
     w, x = _inputs(dtype, B=1, H=3, L=200, d_k=128, d_v=128, chunk=64)
-    ro, rS, _ = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["initial_state"], gate=2)
+    if dtype == "bf16" and method != "split":
+        assert efla.fwd_form(w.B, w.H, w.L, 128, 128, 64, torch.bfloat16)[0] == "fused"
+    ro, rS, _ = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["initial_state"], gate=gate)
     a = fwd_inputs_dev(x, dtype)
-    o, S = efla.chunk_fwd(a["q"], a["k"], a["v"], a["beta"], initial_state=a["initial_state"], chunk_size=64, gate=2)
+    sf = torch.full((w.B, w.H, 128, 128), float("nan"), device="cuda")
+    o, S = efla.chunk_fwd(a["q"], a["k"], a["v"], a["beta"], initial_state=a["initial_state"], chunk_size=64,
+                          gate=gate, method=method, final_state=sf)
     torch.cuda.synchronize()
     eo, eS = errs(o, S, ro, rS)
-    assert eo < TOL[dtype] and eS < TOL[dtype], (dtype, eo, eS)
+    assert eo < TOL[dtype] and eS < TOL[dtype], (dtype, gate, method, eo, eS)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

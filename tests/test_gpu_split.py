@@ -101,7 +101,7 @@ def test_split_workspace_holds_ut_output(dtype, d_k, chunk, diag_only):
     x = W.make_fwd_inputs(w)
     d = fwd_inputs_dev(x, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    nbytes = efla.chunk_workspace_size(2, 3, 200, chunk, tdt)
+    nbytes = efla.split_workspace_size(2, 3, 200, chunk, tdt)
     ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
     efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], workspace=ws, chunk_size=chunk, method="split")
     t = efla.ut_transform(d["k"], d["beta"], chunk_size=chunk)
@@ -148,12 +148,14 @@ def test_state_pass_after_ut_transform_equals_split():
     ("f32", 64, 64, 300, "split"),
 ])
 def test_default_method_dispatch(dtype, d_k, chunk, L, expect):
-    """chunk_fwd with no method picks the one-launch forward for bf16, d_k >= 32 and 64-token chunks and the
-    two-launch one otherwise (many heads: no segments); the outputs are bit-identical to that method's."""
+    """efla_chunk_fwd (chunk_fwd with no method) picks the one-launch forward for bf16, d_k >= 32 and 64-token
+    chunks and the two-launch one otherwise (many heads: no segments); the outputs are bit-identical to that
+    method's."""
     w = W.workload(3, B=2, H=8, L=L, d_k=d_k, d_v=64, chunk=chunk, dtype=dtype)
     x = W.make_fwd_inputs(w)
     d = fwd_inputs_dev(x, dtype)
     assert efla.scan_plan(w.B, w.H, w.L, d_k, 64, chunk, d["v"].dtype)[0] == 1
+    assert efla.fwd_form(w.B, w.H, w.L, d_k, 64, chunk, d["v"].dtype)[0] == expect
     o0, S0 = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=d["initial_state"], chunk_size=chunk)
     o1, S1 = efla.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], initial_state=d["initial_state"], chunk_size=chunk,
                             method=expect)
