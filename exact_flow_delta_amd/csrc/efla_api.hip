@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "efla.h"
 #include "efla_bwd.hpp"
 #include "efla_chain_bf16.hpp"
@@ -769,6 +772,79 @@ efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            int chunk, void* workspace, size_t workspace_bytes, void* stream) {
     return efla_chunk_fwd_gate(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk,
                                EFLA_GATE_EXACT, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free forward's scratch ------------------------------------------------------------------
+// A file-scope device array that every GPU running the library holds (from the module's load to the process's
+// end).  In host code its name is only a stand-in for the symbol: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, once per device, and only that address is ever handed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[EFLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on the first call for that device), or an error.
+efla_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        snprintf(g_last_error, sizeof(g_last_error), "no HIP device visible (%s)", hipGetErrorName(e));
+        return EFLA_ERR_NO_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        snprintf(g_last_error, sizeof(g_last_error), "device %d beyond the %d this library tracks", dev, kMaxDevices);
+        return EFLA_ERR_UNSUPPORTED;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return fail_hip(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                       "efla_chunk_fwd_noalloc: hipGetSymbolAddress(scratch)");
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return EFLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+efla_status efla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                   void* o, const float* initial_state, float* final_state, int B, int H, int L,
+                                   int d_k, int d_v, int chunk, int gate, void* stream) {
+    if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
+    FwdForm f;
+    efla_status st = fwd_form(B, H, L, d_k, d_v, chunk, dtype, &f);
+    if (st != EFLA_OK) return st;
+    if (f.workspace > EFLA_NOALLOC_SCRATCH_BYTES) {
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "efla_chunk_fwd_noalloc: these sizes need %zu bytes of scratch, above the library's %zu", f.workspace,
+                 (size_t)EFLA_NOALLOC_SCRATCH_BYTES);
+        return EFLA_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    if (f.workspace > 0) {
+        // argument checks that need no device first, so that bad arguments report as such on any machine
+        const int64_t BH = (int64_t)B * H;
+        st = check_fwd_buffers(q, k, v, beta, dtype, o, initial_state, final_state, BH, L, d_k, d_v);
+        if (st != EFLA_OK) return st;
+        if (BH == 0 || (L == 0 && !final_state)) return EFLA_OK;
+        st = scratch_address(&ws);
+        if (st != EFLA_OK) return st;
+    }
+    return efla_chunk_fwd_gate(q, k, v, beta, dtype, o, initial_state, final_state, B, H, L, d_k, d_v, chunk, gate, ws,
+                               ws ? (size_t)EFLA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 efla_status efla_recurrent_step_gate(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,

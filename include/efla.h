@@ -14,9 +14,10 @@
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers (memory from hipMalloc / a PyTorch CUDA tensor) unless stated.
- *     The library never allocates, frees or keeps device memory, and keeps no state between calls
- *     apart from a thread-local copy of the last HIP error text.  Calls that need scratch memory
- *     take a caller-owned workspace and say how large it must be.
+ *     The library never allocates or frees device memory, and keeps no state between calls apart from
+ *     a thread-local copy of the last HIP error text and, per device, the address of the fixed scratch
+ *     array of efla_chunk_fwd_noalloc.  Calls that need scratch memory take a caller-owned workspace
+ *     and say how large it must be (efla_chunk_fwd_noalloc uses the library's array instead).
  *   - Layouts are contiguous row-major.  q, k: [B,H,L,d_k]; v, o: [B,H,L,d_v]; beta: [B,H,L];
  *     state: [B,H,d_k,d_v] (S as the update writes it: row i is key dimension i).
  *     efla_chunk_fwd_layout also takes strided views and packed sequences (efla_layout).
@@ -152,6 +153,26 @@ typedef enum { EFLA_FWD_ONE_LAUNCH = 0, EFLA_FWD_SPLIT = 1, EFLA_FWD_SCAN = 2 } 
  */
 efla_status efla_chunk_fwd_form(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
                                 int* form, int* segments, size_t* workspace_bytes);
+
+/*
+ * efla_chunk_fwd_noalloc -- efla_chunk_fwd_gate for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same forms, kernels and results
+ * (bit-identical to efla_chunk_fwd_gate with a workspace of its own), with the workspace taken from a scratch
+ * array of EFLA_NOALLOC_SCRATCH_BYTES that the library holds in device memory on every GPU it runs on, from its
+ * code's load until the process ends.  The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library routine.  The caller still passes every input and output.
+ *   Sizes whose efla_chunk_fwd_workspace_size exceeds EFLA_NOALLOC_SCRATCH_BYTES: EFLA_ERR_WORKSPACE, nothing
+ *   enqueued.  The forms that need no workspace (the one-launch form) never touch the scratch.
+ *   Every call on one GPU uses that GPU's one scratch array, which keeps what the last call left there: calls
+ *   that may run at the same time on one GPU (other streams, other threads) race and give wrong results; order
+ *   them on one stream.  Nothing in the scratch needs to start at any value (each call writes what it reads).
+ *   The device is the calling thread's current HIP device; its scratch address is looked up once per device.
+ * Other arguments and errors as efla_chunk_fwd_gate.
+ */
+#define EFLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+efla_status efla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* beta,
+                                   efla_dtype dtype, void* o, const float* initial_state, float* final_state,
+                                   int B, int H, int L, int d_k, int d_v, int chunk, int gate, void* stream);
 
 /*
  * efla_chunk_fwd_slab -- the forward in one launch and without workspace, with an explicit split of the d_v

@@ -520,3 +520,34 @@ def test_chunk_fwd_reaches_device_check(lib):
     assert _fwd(lib, C=64, dk=128, dv=128, ws=None, wsb=0) == NO_DEVICE                      # one launch
     need = lib.efla_chunk_fwd_workspace_size(1, 16, 65536, 128, 128, 64, BF16)
     assert _fwd(lib, B=1, H=16, L=65536, dk=128, dv=128, C=64, ws=P(8), wsb=need) == NO_DEVICE  # scan
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=F32, o=P(5), s0=None, sf=P(6), B=2, H=3, L=100, dk=64, dv=64,
+             C=32, gate=0)
+    a.update(kw)
+    return lib.efla_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["o"], a["s0"], a["sf"], a["B"],
+                                      a["H"], a["L"], a["dk"], a["dv"], a["C"], a["gate"], None)
+
+
+def test_noalloc_limit_and_argument_errors(lib):
+    limit = 128 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define EFLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)128 << 20\)", text)
+    # fp32, 16 x 16 heads of 8192 tokens, d 128: the split form's UT output alone is 335 MB
+    need = lib.efla_chunk_fwd_workspace_size(16, 16, 8192, 128, 128, 64, F32)
+    assert need > limit
+    assert _noalloc(lib, B=16, H=16, L=8192, dk=128, dv=128, C=64) == WORKSPACE
+    assert b"above the library" in lib.efla_last_error()
+    assert _noalloc(lib, gate=-1) == INVALID
+    assert _noalloc(lib, dk=96) == UNSUPPORTED
+    assert _noalloc(lib, q=None) == INVALID
+    assert _noalloc(lib, o=P(1)) == INVALID                 # o overlaps q
+    assert _noalloc(lib, B=0) == OK                         # empty: nothing to do, no device touched
+    assert _noalloc(lib, L=0, sf=None, q=None, k=None, v=None, beta=None, o=None) == OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_noalloc_reaches_device_check(lib):
+    assert _noalloc(lib) == NO_DEVICE                                           # split form: needs the scratch
+    assert _noalloc(lib, dt=BF16, C=64, dk=128, dv=128) == NO_DEVICE             # one launch: no scratch
