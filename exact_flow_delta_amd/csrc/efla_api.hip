@@ -229,6 +229,7 @@ const char* efla_status_string(efla_status s) {
         case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case EFLA_ERR_NO_DEVICE: return "EFLA_ERR_NO_DEVICE: no HIP device";
         case EFLA_ERR_HIP: return "EFLA_ERR_HIP: HIP runtime error";
+        default: break;
     }
     return "EFLA: unknown status";
 }

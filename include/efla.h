@@ -48,10 +48,17 @@ typedef enum {
     EFLA_ERR_UNSUPPORTED = 2,   /* d_k, d_v, chunk or dtype combination this build does not provide    */
     EFLA_ERR_WORKSPACE = 3,     /* workspace / output buffer missing, misaligned or smaller than needed */
     EFLA_ERR_NO_DEVICE = 4,     /* no HIP device is visible to the process                             */
-    EFLA_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed                          */
-} efla_status;
+    EFLA_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed                          */
+    EFLA_STATUS_RANGE_MIN_ = -0x7FFFFFFF - 1,   /* never returned: with these two bounds every 32-bit int */
+    EFLA_STATUS_RANGE_MAX_ = 0x7FFFFFFF         /* is a value of the type, so a C caller's bad value is   */
+} efla_status;                                  /* defined and reaches the argument checks               */
 
-typedef enum { EFLA_F32 = 0, EFLA_BF16 = 1 } efla_dtype;
+typedef enum {
+    EFLA_F32 = 0,
+    EFLA_BF16 = 1,
+    EFLA_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,    /* never valid: every 32-bit int is a value of the type */
+    EFLA_DTYPE_RANGE_MAX_ = 0x7FFFFFFF          /* (an invalid one is rejected as EFLA_ERR_INVALID_ARG)  */
+} efla_dtype;
 
 /*
  * Gates.  The calls below use the exact coefficient alpha_t.  Their *_gate variants take an `int gate`
@@ -144,7 +151,13 @@ efla_status efla_chunk_fwd_gate(const void* q, const void* k, const void* v, con
 size_t efla_chunk_fwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype);
 
 /* The forms efla_chunk_fwd chooses between (see there). */
-typedef enum { EFLA_FWD_ONE_LAUNCH = 0, EFLA_FWD_SPLIT = 1, EFLA_FWD_SCAN = 2 } efla_fwd_form;
+typedef enum {
+    EFLA_FWD_ONE_LAUNCH = 0,
+    EFLA_FWD_SPLIT = 1,
+    EFLA_FWD_SCAN = 2,
+    EFLA_FWD_FORM_RANGE_MIN_ = -0x7FFFFFFF - 1,   /* never reported (32-bit range, as efla_dtype) */
+    EFLA_FWD_FORM_RANGE_MAX_ = 0x7FFFFFFF
+} efla_fwd_form;
 
 /*
  * efla_chunk_fwd_form -- the form efla_chunk_fwd takes for these sizes, its segment count (1 unless

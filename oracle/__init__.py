@@ -28,12 +28,13 @@ _LIB_PATH = os.path.join(_HERE, "liboracle_efla.so")
 _dp = ctypes.POINTER(ctypes.c_double)
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
-    """Compile an oracle C source with gcc (-O2, OpenMP, no fast-math) into a shared library."""
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH, extra_flags=()) -> str:
+    """Compile an oracle C source with gcc (-O2, OpenMP, no fast-math) into a shared library.  ``extra_flags``
+    are added to the command (the sanitizer test builds an instrumented copy elsewhere with them)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-               "-ffp-contract=off", src, "-o", tmp, "-lm"]
+               "-ffp-contract=off", *extra_flags, src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
