@@ -614,9 +614,12 @@ efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, c
 namespace {
 
 // Workspace of efla_chunk_bwd: the UT output (Ta), then the state entering and the gradient of the state
-// leaving every chunk (fp32, d_k x d_v each), each part 256-byte aligned.
+// leaving every chunk (fp32, d_k x d_v each), then -- where the per-chunk gradients run on bf16 matrix cores (bf16,
+// d_k >= 32, chunk 32 or 64, d_v a multiple of 32) -- T^T of every chunk (bf16, chunk x chunk); each part 256-byte
+// aligned.
 struct BwdPlan {
-    size_t off_s, off_ds, total;
+    size_t off_s, off_ds, off_tt, total;
+    bool tt;
 };
 
 efla_status bwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, BwdPlan* p) {
@@ -628,7 +631,9 @@ efla_status bwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtyp
     const size_t states = round_up_256((size_t)BH * NC * d_k * d_v * 4);
     p->off_s = round_up_256(ut_bytes(BH, L, chunk, dt));
     p->off_ds = p->off_s + states;
-    p->total = p->off_ds + states;
+    p->off_tt = p->off_ds + states;
+    p->tt = dt == EFLA_BF16 && d_k >= 32 && chunk >= 32 && d_v % 32 == 0;
+    p->total = p->off_tt + (p->tt ? round_up_256((size_t)BH * NC * chunk * chunk * 2) : 0);
     return EFLA_OK;
 }
 
@@ -689,11 +694,13 @@ efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const fl
     char* ws = static_cast<char*>(workspace);
     const bool bf = dtype == EFLA_BF16;
     hipError_t e = hipSuccess;
+    void* tt = p.tt ? (void*)(ws + p.off_tt) : nullptr;
     if (L > 0)
-        e = bf ? efla::launch_ut_bf16(k, beta, ws, (int)BH, L, d_k, chunk, gate, s)
+        e = bf ? efla::launch_ut_bf16(k, beta, ws, (int)BH, L, d_k, chunk, gate, s, tt)
                : efla::launch_ut_f32(k, beta, ws, (int)BH, L, d_k, chunk, gate, s);
     efla::BwdArgs a{q, k, v, beta, initial_state, d_o, d_final, dq, dk, dv, dbeta, d_initial, (int)BH, L, d_k, d_v,
-                    chunk, gate, ws, reinterpret_cast<float*>(ws + p.off_s), reinterpret_cast<float*>(ws + p.off_ds)};
+                    chunk, gate, ws, reinterpret_cast<float*>(ws + p.off_s), reinterpret_cast<float*>(ws + p.off_ds),
+                    tt};
     if (e == hipSuccess) e = bf ? efla::launch_bwd_bf16(a, s) : efla::launch_bwd_f32(a, s);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_bwd launch");
 }

@@ -552,6 +552,14 @@ struct BwdArgs {
     void* tw;        // UT output (Ta), already written
     float* s_all;    // BH x NC x d_k x d_v
     float* ds_all;   // BH x NC x d_k x d_v
+    void* tt;        // T^T of every chunk (BH x NC x chunk x chunk, storage type), or null
+};
+
+// The per-chunk gradient kernel on bf16 matrix cores (efla_bwd_mx.hpp) takes the shapes it supports by
+// specialising this for bf16; launch() returns false where it does not apply.
+template <typename E, int DK, int C>
+struct BwdChunkFast {
+    static bool launch(const BwdArgs&, hipStream_t, hipError_t*) { return false; }
 };
 
 template <typename E, int DK, int C>
@@ -586,6 +594,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.L == 0) return e;
+    if (BwdChunkFast<E, DK, C>::launch(a, s, &e)) return e;
     constexpr int LDS = BwdChunkLds<E, DK, C>::BYTES;
     static_assert(LDS <= kMaxLdsBytes, "backward chunk kernel LDS too large");
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_kernel<E, DK, C>),

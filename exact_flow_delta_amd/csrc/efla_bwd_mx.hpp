@@ -1,0 +1,382 @@
+// efla_bwd_mx.hpp -- the per-chunk gradient kernel of the backward pass on bf16 matrix cores (bf16 inputs,
+// d_k >= 32, chunks of 32 or 64 tokens, d_v a multiple of 32).
+//
+// Same chunk gradients as bwd_chunk_kernel (efla_bwd.hpp, where they are derived: the adjoint of the chunked form
+// of "Error-Free Linear Attention is a Free Lunch" (howistudyai.com), Step 4), in the same phases, with every
+// product a 16x16x32 bf16 matrix instruction accumulating in fp32 over bf16 tiles in LDS:
+//   * Tiles are row-major bf16 with rows padded by 8 elements (16 bytes), so that the 16 rows of a fragment start
+//     on different banks.
+//   * An operand whose reduction index runs along its rows' contiguous elements is read 8 elements per lane with
+//     one 16-byte read (lane (r, g): reduction indices 8 g .. 8 g + 7).  When either operand of a product has its
+//     reduction index along columns instead, both take the other convention -- lane (r, g) carries reduction
+//     indices 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 -- read with two 8-byte reads, or two transposing reads
+//     (ds_read_tr16_b64) on the strided side.  The matrix instruction sums over whatever indices each slot holds,
+//     as long as both operands agree.
+//   * The d_v columns are taken 32 at a time (one reduction step of the products over d_v), the state and state
+//     gradient slabs widened from the fp32 workspace to bf16 on the way into LDS.
+// T = (I + D strict_lower(L))^{-1} comes from the UT launch (its T^T export, bf16), and L = K K^T is formed only where
+// dalpha needs it, on the tiles of W2 the wave holds, so no fp32 C x C matrix passes through LDS.
+#pragma once
+
+#include "efla_bwd.hpp"
+
+namespace efla {
+
+namespace bwdx {
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// 8 consecutive bf16 at a 16-byte aligned LDS address
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+// 4 consecutive bf16 at an 8-byte aligned LDS address
+__device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+// transposing read of a row-major bf16 block X (leading dimension baked into tr_off = Mma<bf16>::tr_offset):
+// lane (r, g) receives X[4 g .. 4 g + 3][r]
+__device__ __forceinline__ bf16x4 ldt(const bf16* X, int tr_off) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(X + tr_off)));
+}
+
+// acc += A B over a reduction of K (a multiple of 32) on the wave's tiles of an M x N product (tile assignment of
+// bwd::Acc).  A(i, k) is A[i * lda + k] when AK (reduction index contiguous), else A[k * lda + i]; B(k, j) is
+// B[j * ldb + k] when BK, else B[k * ldb + j].  Reduction steps in the outer loop, the wave's tiles inside, so that
+// consecutive matrix instructions are independent.
+template <int M, int N, int NWV, bool AK, bool BK, int K>
+__device__ __forceinline__ void mmx(bwd::Acc<M, N, NWV>& acc, const bf16* A, int lda, const bf16* B, int ldb, int w,
+                                    int lane) {
+    typedef bwd::Acc<M, N, NWV> AC;
+    constexpr int TPW = AC::TPW;
+    static_assert(K % 32 == 0, "reduction in steps of 32");
+    const int r = lane & 15, g = lane >> 4;
+    const int tra = Mma<bf16>::tr_offset(lane, lda), trb = Mma<bf16>::tr_offset(lane, ldb);
+    const bool last = AC::ALL || w + NWV * (TPW - 1) < AC::NTT;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            if (s == TPW - 1 && !last) continue;
+            const int tt = w + NWV * s;
+            const int ti = tt / AC::TN, tj = tt - ti * AC::TN;
+            if constexpr (AK && BK) {
+                const bf16x8 a = ld8(A + (16 * ti + r) * lda + k0 + 8 * g);
+                const bf16x8 b = ld8(B + (16 * tj + r) * ldb + k0 + 8 * g);
+                acc.t[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc.t[s], 0, 0, 0);
+            } else {
+                bf16x4 a0, a1, b0, b1;
+                if constexpr (AK) {
+                    const bf16* pa = A + (16 * ti + r) * lda + k0 + 4 * g;
+                    a0 = ld4(pa);
+                    a1 = ld4(pa + 16);
+                } else {
+                    a0 = ldt(A + k0 * lda + 16 * ti, tra);
+                    a1 = ldt(A + (k0 + 16) * lda + 16 * ti, tra);
+                }
+                if constexpr (BK) {
+                    const bf16* pb = B + (16 * tj + r) * ldb + k0 + 4 * g;
+                    b0 = ld4(pb);
+                    b1 = ld4(pb + 16);
+                } else {
+                    b0 = ldt(B + k0 * ldb + 16 * tj, trb);
+                    b1 = ldt(B + (k0 + 16) * ldb + 16 * tj, trb);
+                }
+                Mma<bf16>::mma2(acc.t[s], a0, a1, b0, b1);
+            }
+        }
+    }
+}
+
+// ROWS x COLS of a row-major global matrix (row stride ld elements, 16-byte aligned rows) in registers between a
+// load (16 bytes per thread and request; rows >= n read as zeros) and a store into a bf16 LDS tile (row stride sld,
+// a multiple of 8).
+template <typename E, int ROWS, int COLS, int NTH>
+struct TileB {
+    typedef typename Vec16<E>::type V;
+    static constexpr int VEC = Vec16<E>::N;
+    static constexpr int VPR = COLS / VEC;
+    static constexpr int TOT = ROWS * VPR;
+    static constexpr int N = (TOT + NTH - 1) / NTH;
+    static_assert(COLS % VEC == 0, "whole 16-byte vectors per row");
+    V x[N];
+    __device__ __forceinline__ void load(const E* g, int64_t ld, int n, int tid) {
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int idx = it * NTH + tid, r = idx / VPR, c = (idx - r * VPR) * VEC;
+            x[it] = (idx < TOT && r < n) ? *reinterpret_cast<const V*>(g + (int64_t)r * ld + c)
+                                         : __builtin_bit_cast(V, u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+    __device__ __forceinline__ void store(bf16* s, int sld, int tid) const {
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int idx = it * NTH + tid, r = idx / VPR, c = (idx - r * VPR) * VEC;
+            if (TOT % NTH == 0 || idx < TOT) {
+                if constexpr (VEC == 8) {
+                    *reinterpret_cast<bf16x8*>(s + r * sld + c) = x[it];
+                } else {
+                    bf16x4 h;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[e] = (bf16)x[it][e];
+                    *reinterpret_cast<bf16x4*>(s + r * sld + c) = h;
+                }
+            }
+        }
+    }
+};
+
+// LDS of the kernel (byte offsets): bf16 tiles Q, K (C x DK), P and T^T (C x C), the d_v slab tiles S, dS' (DK x NV)
+// and V, dO, Delta, dDelta, G (C x NV); four fp32 C-vectors.
+template <int DK, int C>
+struct BwdXLds {
+    static constexpr int NV = 32;
+    static constexpr int LDK = DK + 8, LDC = C + 8, LDV = NV + 8;
+    static constexpr int Q = 0;
+    static constexpr int K = Q + C * LDK * 2;
+    static constexpr int P = K + C * LDK * 2;
+    static constexpr int T = P + C * LDC * 2;
+    static constexpr int S = T + C * LDC * 2;
+    static constexpr int G2 = S + DK * LDV * 2;
+    static constexpr int V = G2 + DK * LDV * 2;
+    static constexpr int O = V + C * LDV * 2;
+    static constexpr int DL = O + C * LDV * 2;
+    static constexpr int DD = DL + C * LDV * 2;
+    static constexpr int GS = DD + C * LDV * 2;
+    static constexpr int AL = GS + C * LDV * 2;
+    static constexpr int BYTES = AL + 4 * C * 4;
+};
+
+}  // namespace bwdx
+
+constexpr int kChunkXThreads = 512;   // eight waves
+
+template <int DK, int C>
+__global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ beta,
+    const bf16* __restrict__ d_o, const float* __restrict__ s_all, const float* __restrict__ ds_all,
+    const bf16* __restrict__ tt, bf16* __restrict__ dq, bf16* __restrict__ dk, float* __restrict__ dbeta, int L, int DV,
+    int gate) {
+    using namespace bwd;
+    using namespace bwdx;
+    constexpr int NWV = kChunkXThreads / 64;
+    constexpr int NTH = kChunkXThreads;
+    typedef BwdXLds<DK, C> LY;
+    constexpr int NV = LY::NV, LDK = LY::LDK, LDC = LY::LDC, LDV = LY::LDV;
+    static_assert(DK % 32 == 0 && C % 32 == 0, "d_k and chunk multiples of 32");
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_x[];
+    bf16* sQ = reinterpret_cast<bf16*>(smem_x + LY::Q);
+    bf16* sK = reinterpret_cast<bf16*>(smem_x + LY::K);
+    bf16* sP = reinterpret_cast<bf16*>(smem_x + LY::P);    // lower_incl(Q K^T); later M o W1
+    bf16* sT = reinterpret_cast<bf16*>(smem_x + LY::T);    // T^T; later dL
+    bf16* sS = reinterpret_cast<bf16*>(smem_x + LY::S);    // S[:, slab]
+    bf16* sG2 = reinterpret_cast<bf16*>(smem_x + LY::G2);  // dS'[:, slab]
+    bf16* sV = reinterpret_cast<bf16*>(smem_x + LY::V);    // V slab; then D R; then -dR
+    bf16* sO = reinterpret_cast<bf16*>(smem_x + LY::O);    // dO slab
+    bf16* sDl = reinterpret_cast<bf16*>(smem_x + LY::DL);  // Delta slab
+    bf16* sDd = reinterpret_cast<bf16*>(smem_x + LY::DD);  // dDelta slab
+    bf16* sGs = reinterpret_cast<bf16*>(smem_x + LY::GS);  // G slab
+    float* sAl = reinterpret_cast<float*>(smem_x + LY::AL);
+    float* sDb = sAl + C;
+    float* sDlam = sDb + C;
+    float* sDa = sDlam + C;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int NC = (L + C - 1) / C;
+    const int bh = blockIdx.x / NC, c = blockIdx.x - bh * NC;
+    const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
+    const int64_t tok = (int64_t)bh * L + t0;
+    const float* Sg = s_all + ((int64_t)bh * NC + c) * DK * DV;
+    const float* dSg = ds_all + ((int64_t)bh * NC + c) * DK * DV;
+
+    {
+        TileB<bf16, C, DK, NTH> tq, tk;
+        TileB<bf16, C, C, NTH> ttl;
+        tq.load(q + tok * DK, DK, n, tid);
+        tk.load(k + tok * DK, DK, n, tid);
+        ttl.load(tt + ((int64_t)bh * NC + c) * C * C, C, C, tid);
+        tq.store(sQ, LDK, tid);
+        tk.store(sK, LDK, tid);
+        ttl.store(sT, LDC, tid);
+    }
+    // the d_v slabs' tiles, loaded one slab ahead
+    TileB<float, DK, NV, NTH> ts, tds;
+    TileB<bf16, C, NV, NTH> tv, to;
+    auto load_slab = [&](int col0) {
+        ts.load(Sg + col0, DV, DK, tid);
+        tds.load(dSg + col0, DV, DK, tid);
+        tv.load(v + tok * DV + col0, DV, n, tid);
+        to.load(d_o + tok * DV + col0, DV, n, tid);
+    };
+    load_slab(0);
+    if (tid < C) sDa[tid] = 0.0f;
+    __syncthreads();
+    if (tid < C) {   // gates of the chunk's tokens (rows past the end: zero keys, zero step)
+        float lam = 0.0f;
+        for (int e = 0; e < DK; ++e) {
+            const float x = (float)sK[tid * LDK + e];
+            lam = fmaf(x, x, lam);
+        }
+        const float b = tid < n ? beta[tok + tid] : 0.0f;
+        sAl[tid] = gate_alpha(b, lam, gate);
+        float db, dl;
+        gate_alpha_grad(b, lam, gate, &db, &dl);
+        sDb[tid] = db;
+        sDlam[tid] = dl;
+    }
+    {   // P = lower_incl(Q K^T)
+        Acc<C, C, NWV> b;
+        b.zero();
+        mmx<C, C, NWV, true, true, DK>(b, sQ, LDK, sK, LDK, w, lane);
+        b.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = (bf16)(j <= i ? x : 0.0f); });
+    }
+    __syncthreads();
+
+    Acc<C, DK, NWV> aQ, aK;
+    Acc<C, C, NWV> W1, W2;
+    aQ.zero();
+    aK.zero();
+    W1.zero();
+    W2.zero();
+    for (int col0 = 0; col0 < DV; col0 += NV) {
+        ts.store(sS, LDV, tid);
+        tds.store(sG2, LDV, tid);
+        tv.store(sV, LDV, tid);
+        to.store(sO, LDV, tid);
+        __syncthreads();
+        if (col0 + NV < DV) load_slab(col0 + NV);
+        Acc<C, NV, NWV> R;   // R = V - K S, kept for dalpha; D R over V
+        R.zero();
+        mmx<C, NV, NWV, true, false, DK>(R, sK, LDK, sS, LDV, w, lane);
+        R.each(w, lane, [&](int i, int j, float& x) { x = (float)sV[i * LDV + j] - x; });
+        __syncthreads();
+        R.each(w, lane, [&](int i, int j, float& x) { sV[i * LDV + j] = (bf16)(sAl[i] * x); });
+        __syncthreads();
+        {   // Delta = T (D R); dDelta = P^T dO + K dS'
+            Acc<C, NV, NWV> a, b;
+            a.zero();
+            b.zero();
+            mmx<C, NV, NWV, false, false, C>(a, sT, LDC, sV, LDV, w, lane);
+            mmx<C, NV, NWV, false, false, C>(b, sP, LDC, sO, LDV, w, lane);
+            mmx<C, NV, NWV, true, false, DK>(b, sK, LDK, sG2, LDV, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) { sDl[i * LDV + j] = (bf16)x; });
+            b.each(w, lane, [&](int i, int j, float& x) { sDd[i * LDV + j] = (bf16)x; });
+        }
+        __syncthreads();
+        {   // G = T^T dDelta; -dR = -D G over V; dalpha += rowsum(G o R)
+            Acc<C, NV, NWV> a;
+            a.zero();
+            mmx<C, NV, NWV, true, false, C>(a, sT, LDC, sDd, LDV, w, lane);
+            a.each(w, lane, [&](int i, int j, float& x) {
+                sGs[i * LDV + j] = (bf16)x;
+                sV[i * LDV + j] = (bf16)(-sAl[i] * x);
+            });
+            // rows of this lane's elements: the same (tile, i) for a and R, summed over the tile's 16 columns
+            typedef Acc<C, NV, NWV> AN;
+#pragma unroll
+            for (int s = 0; s < AN::TPW; ++s) {
+                const int tt = w + NWV * s;
+                if (AN::ALL || tt < AN::NTT) {
+                    const int ti = tt / AN::TN;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float p = a.t[s][i] * R.t[s][i];
+                        p += __shfl_xor(p, 1, 16);
+                        p += __shfl_xor(p, 2, 16);
+                        p += __shfl_xor(p, 4, 16);
+                        p += __shfl_xor(p, 8, 16);
+                        if ((lane & 15) == 0) atomicAdd(&sDa[16 * ti + 4 * (lane >> 4) + i], p);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // dQ += dO S^T; dK += Delta dS'^T - dR S^T; W1 += dO Delta^T; W2 += G Delta^T (reduction over the slab)
+        mmx<C, DK, NWV, true, true, NV>(aQ, sO, LDV, sS, LDV, w, lane);
+        mmx<C, DK, NWV, true, true, NV>(aK, sDl, LDV, sG2, LDV, w, lane);
+        mmx<C, DK, NWV, true, true, NV>(aK, sV, LDV, sS, LDV, w, lane);
+        mmx<C, C, NWV, true, true, NV>(W1, sO, LDV, sDl, LDV, w, lane);
+        mmx<C, C, NWV, true, true, NV>(W2, sGs, LDV, sDl, LDV, w, lane);
+        __syncthreads();
+    }
+
+    // M o W1 into sP; dL = -strict_lower(D W2) into sT (T is no longer needed); dalpha -= rowsum(strict_lower(L) o W2)
+    // with L = K K^T formed on the wave's tiles of W2
+    W1.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = (bf16)(j <= i ? x : 0.0f); });
+    W2.each(w, lane, [&](int i, int j, float& x) { sT[i * LDC + j] = (bf16)(j < i ? -sAl[i] * x : 0.0f); });
+    {
+        typedef Acc<C, C, NWV> AC;
+        AC Lt;
+        Lt.zero();
+        mmx<C, C, NWV, true, true, DK>(Lt, sK, LDK, sK, LDK, w, lane);
+#pragma unroll
+        for (int s = 0; s < AC::TPW; ++s) {
+            const int tt2 = w + NWV * s;
+            if (AC::ALL || tt2 < AC::NTT) {
+                const int ti = tt2 / AC::TN, tj = tt2 - ti * AC::TN;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * ti + 4 * (lane >> 4) + i, col = 16 * tj + (lane & 15);
+                    float p = col < row ? Lt.t[s][i] * W2.t[s][i] : 0.0f;
+                    p += __shfl_xor(p, 1, 16);
+                    p += __shfl_xor(p, 2, 16);
+                    p += __shfl_xor(p, 4, 16);
+                    p += __shfl_xor(p, 8, 16);
+                    if ((lane & 15) == 0) atomicAdd(&sDa[row], -p);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // dbeta; dlambda
+    if (tid < C) {
+        const int i = tid;
+        const float s = sDa[i];
+        if (i < n) dbeta[tok + i] = s * sDb[i];
+        sDa[i] = s * sDlam[i];
+    }
+    __syncthreads();
+    // dQ += (M o W1) K;  dK += (M o W1)^T Q + dL K + dL^T K + 2 dlambda o K
+    mmx<C, DK, NWV, true, false, C>(aQ, sP, LDC, sK, LDK, w, lane);
+    mmx<C, DK, NWV, false, false, C>(aK, sP, LDC, sQ, LDK, w, lane);
+    mmx<C, DK, NWV, true, false, C>(aK, sT, LDC, sK, LDK, w, lane);
+    mmx<C, DK, NWV, false, false, C>(aK, sT, LDC, sK, LDK, w, lane);
+    aQ.each(w, lane, [&](int i, int e, float& x) {
+        if (i < n) dq[(tok + i) * DK + e] = (bf16)x;
+    });
+    aK.each(w, lane, [&](int i, int e, float& x) {
+        if (i < n) dk[(tok + i) * DK + e] = (bf16)fmaf(2.0f * sDa[i], (float)sK[i * LDK + e], x);
+    });
+}
+
+// Launches the matrix-core chunk kernel when it applies (bf16, d_k >= 32, chunk 32 or 64, d_v a multiple of 32, and
+// the UT launch wrote T^T); returns false otherwise, leaving the launch to bwd_chunk_kernel.
+template <int DK, int C>
+bool launch_bwd_chunk_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
+    if constexpr (DK < 32 || C < 32) {
+        (void)a;
+        (void)s;
+        (void)err;
+        return false;
+    } else {
+        if (a.d_v % 32 != 0 || a.tt == nullptr) return false;
+        constexpr int LDS = bwdx::BwdXLds<DK, C>::BYTES;
+        static_assert(LDS <= kMaxLdsBytes, "matrix-core chunk kernel LDS too large");
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_mx_kernel<DK, C>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e == hipSuccess) {
+            const int NC = (a.L + C - 1) / C;
+            hipLaunchKernelGGL((bwd_chunk_mx_kernel<DK, C>), dim3((unsigned)((int64_t)a.BH * NC)), dim3(kChunkXThreads),
+                               LDS, s, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                               static_cast<const bf16*>(a.v), a.beta, static_cast<const bf16*>(a.d_o), a.s_all,
+                               a.ds_all, static_cast<const bf16*>(a.tt), static_cast<bf16*>(a.dq),
+                               static_cast<bf16*>(a.dk), a.dbeta, a.L, a.d_v, a.gate);
+            e = hipGetLastError();
+        }
+        *err = e;
+        return true;
+    }
+}
+
+template <int DK, int C>
+struct BwdChunkFast<bf16, DK, C> {
+    static bool launch(const BwdArgs& a, hipStream_t s, hipError_t* e) { return launch_bwd_chunk_mx<DK, C>(a, s, e); }
+};
+
+}  // namespace efla

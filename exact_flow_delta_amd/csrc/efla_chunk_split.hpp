@@ -541,9 +541,10 @@ __global__ __launch_bounds__(DVS / 16 * 64) void chain_kernel(
 // ------------------------------------------------------------------------------------------------
 // diag32: only the diagonal 32 x 32 blocks of every 64-token chunk's Ta are needed (the bf16 state pass
 // reads no other); the wave kernel then skips the rest (other kernels form the whole transform regardless)
+// tt (bf16 with d_k >= 32 only, not with diag32): also T^T of every chunk, row-major C x C (the backward pass)
 template <typename E, int DK, int C, bool VL>
 hipError_t launch_ut_vl(const void* k, const float* beta, void* tw, int BH, int L, int gate, const TokLayout& ly,
-                        bool diag32, hipStream_t stream) {
+                        bool diag32, hipStream_t stream, void* tt = nullptr) {
     static_assert(UtLayout<sizeof(E), DK, C>::BYTES <= kMaxLdsBytes, "UT kernel LDS too large");
     const int NC = (L + C - 1) / C;
     // chunks of the workspace (with packed sequences an upper bound; the kernel reads the exact count)
@@ -566,10 +567,11 @@ hipError_t launch_ut_vl(const void* k, const float* beta, void* tw, int BH, int 
         const dim3 grid((unsigned)(need < resident ? need : resident));
         if (dg)
             hipLaunchKernelGGL((ut_wave_kernel<DK, C, VL, CAN_DG>), grid, dim3(WPB * 64), 0, stream,
-                               static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly);
+                               static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly, nullptr);
         else
             hipLaunchKernelGGL((ut_wave_kernel<DK, C, VL, false>), grid, dim3(WPB * 64), 0, stream,
-                               static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly);
+                               static_cast<const bf16*>(k), beta, static_cast<bf16*>(tw), L, NC, BH, gate, ly,
+                               static_cast<bf16*>(tt));
         return hipGetLastError();
     }
     // as many workgroups as the device holds at once, each walking several pairs
@@ -589,10 +591,10 @@ hipError_t launch_ut_vl(const void* k, const float* beta, void* tw, int BH, int 
 
 template <typename E, int DK, int C>
 hipError_t launch_ut_t(const void* k, const float* beta, void* tw, int BH, int L, int gate, const TokLayout* lyp,
-                       hipStream_t stream, bool diag32 = false) {
+                       hipStream_t stream, bool diag32 = false, void* tt = nullptr) {
     const TokLayout ly = lyp ? *lyp : contiguous_layout(1, L, DK, DK);   // contiguous: every (batch, head) is a "batch"
-    return ly.cu_seqlens ? launch_ut_vl<E, DK, C, true>(k, beta, tw, BH, L, gate, ly, diag32, stream)
-                         : launch_ut_vl<E, DK, C, false>(k, beta, tw, BH, L, gate, ly, diag32, stream);
+    return ly.cu_seqlens ? launch_ut_vl<E, DK, C, true>(k, beta, tw, BH, L, gate, ly, diag32, stream, tt)
+                         : launch_ut_vl<E, DK, C, false>(k, beta, tw, BH, L, gate, ly, diag32, stream, tt);
 }
 
 template <typename E, int DK, int C, int DVS>
@@ -654,23 +656,24 @@ hipError_t launch_split_e(const SplitArgs& a, bool with_ut, hipStream_t s) {
 }
 
 template <typename E, int DK>
-hipError_t launch_ut_dk(const void* k, const float* beta, void* tw, int BH, int L, int chunk, int gate, hipStream_t s) {
+hipError_t launch_ut_dk(const void* k, const float* beta, void* tw, int BH, int L, int chunk, int gate, hipStream_t s,
+                        void* tt) {
     switch (chunk) {
-        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, gate, nullptr, s);
-        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, gate, nullptr, s);
-        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, gate, nullptr, s);
+        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, gate, nullptr, s, false, tt);
+        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, gate, nullptr, s, false, tt);
+        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, gate, nullptr, s, false, tt);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename E>
 hipError_t launch_ut_e(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
-                       hipStream_t s) {
+                       hipStream_t s, void* tt = nullptr) {
     switch (d_k) {
-        case 16: return launch_ut_dk<E, 16>(k, beta, tw, BH, L, chunk, gate, s);
-        case 32: return launch_ut_dk<E, 32>(k, beta, tw, BH, L, chunk, gate, s);
-        case 64: return launch_ut_dk<E, 64>(k, beta, tw, BH, L, chunk, gate, s);
-        case 128: return launch_ut_dk<E, 128>(k, beta, tw, BH, L, chunk, gate, s);
+        case 16: return launch_ut_dk<E, 16>(k, beta, tw, BH, L, chunk, gate, s, tt);
+        case 32: return launch_ut_dk<E, 32>(k, beta, tw, BH, L, chunk, gate, s, tt);
+        case 64: return launch_ut_dk<E, 64>(k, beta, tw, BH, L, chunk, gate, s, tt);
+        case 128: return launch_ut_dk<E, 128>(k, beta, tw, BH, L, chunk, gate, s, tt);
     }
     return hipErrorInvalidValue;
 }

@@ -194,7 +194,8 @@ hipError_t launch_seg_scan(const float* seg_states, const float* s0, float* s_in
 
 hipError_t launch_ut_f32(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
                          hipStream_t stream);
+// tt (optional; d_k >= 32): also T^T of every chunk as a row-major chunk x chunk bf16 matrix, for the backward pass
 hipError_t launch_ut_bf16(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
-                          hipStream_t stream);
+                          hipStream_t stream, void* tt = nullptr);
 
 }  // namespace efla

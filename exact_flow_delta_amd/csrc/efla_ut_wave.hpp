@@ -53,10 +53,12 @@ struct UtWaveShape {
 template <bool DG>
 __host__ __device__ constexpr bool ut_block_used(int hi, int lo) { return !DG || (hi >> 1) == (lo >> 1); }
 
+// tt (optional, not with DG): T^T of every chunk as a row-major C x C bf16 matrix (tt[u][j][i] = T[i][j], zeros below
+// the diagonal), for the backward pass.
 template <int DK, int C, bool VL, bool DG>
 __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
     const bf16* __restrict__ k, const float* __restrict__ beta, bf16* __restrict__ tw, int L, int NC, int BH,
-    int gate, TokLayout ly) {
+    int gate, TokLayout ly, bf16* __restrict__ tt_out) {
     typedef UtWaveShape<DK, C> SH;
     typedef Mma<bf16> M;
     typedef M::quad quad;
@@ -195,6 +197,11 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
             bf16* tt = sTt + g * 256 + r * 16;
             *reinterpret_cast<bx8*>(tt) = t0v;
             *reinterpret_cast<bx8*>(tt + 8) = t1v;
+            if (tt_out) {   // row r of T_gg^T is row 16 g + r of T^T, columns 16 g .. 16 g + 15
+                bf16* o = tt_out + (int64_t)u * (C * C) + (16 * g + r) * C + 16 * g;
+                *reinterpret_cast<bx8*>(o) = t0v;
+                *reinterpret_cast<bx8*>(o + 8) = t1v;
+            }
             // diagonal block qi = g (g + 3) / 2
             bf16* ta = sTat + (g * (g + 3) / 2) * 256 + r * 16;
             *reinterpret_cast<bx8*>(ta) = a0v;
@@ -223,6 +230,11 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
                     // z lane (r, g), element e = T_IJ[4g + e][r]: row r of Ta_IJ^T after the column gate of token 16 J + r
                     Tq[I] = M::cvt(z);
                     M::lds_store_quad(sTat + (I * (I + 1) / 2 + J) * 256 + r * 16 + 4 * g, M::cvt(z * ar[J]));
+                    if (tt_out) {   // T_IJ[4g + e][r] = T^T[16 J + r][16 I + 4 g + e]; zeros at T^T block (I, J)
+                        bf16* o = tt_out + (int64_t)u * (C * C);
+                        *reinterpret_cast<quad*>(o + (16 * J + r) * C + 16 * I + 4 * g) = Tq[I];
+                        *reinterpret_cast<quad*>(o + (16 * I + r) * C + 16 * J + 4 * g) = M::zero();
+                    }
                 }
             });
         });

@@ -403,9 +403,10 @@ def test_layout_reaches_the_device_check(lib):
 
 
 def test_bwd_workspace_size(lib):
-    # UT output, then two fp32 blocks of B H ceil(L/C) d_k d_v (each 256-byte rounded)
+    # UT output, then two fp32 blocks of B H ceil(L/C) d_k d_v (each 256-byte rounded), then (bf16 with d_k >= 32,
+    # chunk >= 32, d_v a multiple of 32: the matrix-core per-chunk kernel) T^T of every chunk in bf16
     nb = efla.chunk_bwd_workspace_size(8, 16, 4096, 128, 128, 64, torch.bfloat16)
-    assert nb == 41943040 + 2 * 128 * 64 * 128 * 128 * 4
+    assert nb == 41943040 + 2 * 128 * 64 * 128 * 128 * 4 + 128 * 64 * 64 * 64 * 2
     nb = efla.chunk_bwd_workspace_size(1, 3, 100, 32, 16, 32, torch.float32)
     ut = 3 * 4 * 3 * 256 * 4
     st = -(-(3 * 4 * 32 * 16 * 4) // 256) * 256
