@@ -561,6 +561,11 @@ template <typename E, int DK, int C>
 struct BwdChunkFast {
     static bool launch(const BwdArgs&, hipStream_t, hipError_t*) { return false; }
 };
+// Likewise the state-gradient pass on bf16 matrix cores (efla_bwd_chain_mx.hpp).
+template <typename E, int DK, int C>
+struct BwdChainFast {
+    static bool launch(const BwdArgs&, hipStream_t, hipError_t*) { return false; }
+};
 
 template <typename E, int DK, int C>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
@@ -583,7 +588,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.d_v >= 32) {
+    hipError_t ec = hipSuccess;
+    if (BwdChainFast<E, DK, C>::launch(a, s, &ec)) {
+        if (ec != hipSuccess) return ec;
+    } else if (a.d_v >= 32) {
         const int nslab = a.d_v / 32;
         hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(kChainThreads), 0, s, q, k,
                            tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab);
