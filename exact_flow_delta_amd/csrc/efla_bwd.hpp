@@ -561,7 +561,11 @@ template <typename E, int DK, int C>
 struct BwdChunkFast {
     static bool launch(const BwdArgs&, hipStream_t, hipError_t*) { return false; }
 };
-// Likewise the state-gradient pass on bf16 matrix cores (efla_bwd_chain_mx.hpp).
+// Likewise the state recompute and the state-gradient pass on bf16 matrix cores (efla_bwd_chain_mx.hpp).
+template <typename E, int DK, int C>
+struct BwdStatesFast {
+    static bool launch(const BwdArgs&, hipStream_t, hipError_t*) { return false; }
+};
 template <typename E, int DK, int C>
 struct BwdChainFast {
     static bool launch(const BwdArgs&, hipStream_t, hipError_t*) { return false; }
@@ -576,7 +580,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     const E* d_o = static_cast<const E*>(a.d_o);
     const E* tw = static_cast<const E*>(a.tw);
     if (a.L > 0) {
-        if (a.d_v >= 32) {
+        hipError_t es = hipSuccess;
+        if (BwdStatesFast<E, DK, C>::launch(a, s, &es)) {
+            if (es != hipSuccess) return es;
+        } else if (a.d_v >= 32) {
             const int nslab = a.d_v / 32;
             hipLaunchKernelGGL((bwd_states_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(bwd::NT), 0, s, k,
                                v, tw, a.s0, a.s_all, a.L, a.d_v, nslab);

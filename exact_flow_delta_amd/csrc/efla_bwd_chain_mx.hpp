@@ -305,6 +305,194 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     }
 }
 
+// The state entering every chunk, s_all[bh][c] (fp32, d_k x d_v), for the per-chunk gradients: the forward state
+// pass again without outputs (per 32-token half: R = V - K S, Delta = Ta R, S <- S + K^T Delta), organised as
+// bwd_chain_mx_kernel but in chunk order, with only K, the V slab and Ta loaded.
+template <int DK, int DVS>
+__global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw, const float* __restrict__ s0,
+    float* __restrict__ s_all, int BH, int L, int DV, int nslab) {
+    constexpr int C = 64;
+    typedef ChainBf16Shape<DK, C, DVS, 0> SH;
+    typedef Mma<bf16> M;
+    typedef M::quad quad;
+    typedef bf16x8 bx8;
+    constexpr int NW = DVS / 16;
+    constexpr int NKD = DK / 16;
+    constexpr int NKP = DK / 32;
+    constexpr int NQ = TaShape<C>::NQ;
+    constexpr int QE = TaShape<C>::QE;
+    constexpr int NCV = DVS / 8;
+    static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
+    static_assert(SH::NLT == 5, "Ta of a 64-token chunk is five 1 KiB loads");
+    // one buffer: K tile, V slab, Ta (no Q tile)
+    constexpr int OK_ = 0, OV_ = SH::NLQ * 1024, OT_ = (SH::NLQ + SH::NLV) * 1024;
+    constexpr int BUFB = (SH::NLQ + SH::NLV + SH::NLT) * 1024;
+    __shared__ __attribute__((aligned(1024))) unsigned char buf0_[BUFB];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf1_[BUFB];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf2_[BUFB];
+    lds_u8* const buf0 = (lds_u8*)buf0_;
+    lds_u8* const buf1 = (lds_u8*)buf1_;
+    lds_u8* const buf2 = (lds_u8*)buf2_;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int bid = blockIdx.x;
+    const int slab = (bid >> 3) % nslab;
+    const int bh = ((bid >> 3) / nslab) * 8 + (bid & 7);
+    if (bh >= BH) return;
+    const int slab_col = slab * DVS;
+    const bool producer = w == NW;
+    const int colw = slab_col + 16 * (producer ? 0 : w);
+    const int NC = (L + C - 1) / C;
+    const int64_t tok0 = (int64_t)bh * L;
+    const bf16* twh = tw + (int64_t)bh * NC * (NQ * QE);
+
+    constexpr int NLOAD = SH::NLQ + SH::NLV + SH::NLT - 1;   // Ta quads 6 and 7 are not read
+    auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
+        const int t = c * C;
+        const int n = (L - t < C) ? (L - t) : C;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, n * DK * 2);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + (tok0 + t) * DV + slab_col, ((n - 1) * DV + DVS) * 2);
+        const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(twh + (int64_t)c * (NQ * QE), SH::TBYTES);
+        static_for<SH::NLQ + SH::NLV + SH::NLT>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            constexpr int tile = kk < SH::NLQ ? 1 : kk < SH::NLQ + SH::NLV ? 2 : 3;
+            constexpr int j = tile == 1 ? kk : tile == 2 ? kk - SH::NLQ : kk - SH::NLQ - SH::NLV;
+            constexpr int RB = tile == 1 ? SH::RBQ : SH::RBV;
+            constexpr int off = tile == 1 ? OK_ : tile == 2 ? OV_ : OT_;
+            lds_void* dst = (lds_void*)(buf + off + 1024 * j);
+            const int p = 1024 * j + 16 * lane;
+            if constexpr (tile == 3 && j == 3) {
+                return;
+            } else if constexpr (tile == 3) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
+            } else {
+                const int tr = p / RB;
+                const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
+                const int ld = tile == 2 ? DV : DK;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 1 ? rk : rv, dst, 16, (tr * ld + 8 * lc) * 2, 0, 0, 0);
+            }
+        });
+    };
+    auto wait_vm = [&](auto n_c) __attribute__((always_inline)) {
+        constexpr int N = decltype(n_c)::value;
+        static_assert(N >= 0 && N < 64, "vector-memory count field");
+        __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    };
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, NLOAD> ILOAD;
+
+    if (producer) {
+        if (NC > 0) {
+            issue_chunk(0, buf0);
+            if (NC > 1) {
+                issue_chunk(1, buf1);
+                wait_vm(ILOAD{});
+            } else {
+                wait_vm(I0{});
+            }
+            __builtin_amdgcn_s_barrier();
+        }
+        auto pstep = [&](int c, lds_u8* nxt) __attribute__((always_inline)) {
+            if (c + 2 < NC) {
+                issue_chunk(c + 2, nxt);
+                wait_vm(ILOAD{});
+            } else {
+                wait_vm(I0{});
+            }
+            __builtin_amdgcn_s_barrier();
+        };
+        for (int c = 0; c < NC; c += 3) {
+            pstep(c, buf2);
+            if (c + 1 < NC) pstep(c + 1, buf0);
+            if (c + 2 < NC) pstep(c + 2, buf1);
+        }
+        return;
+    }
+
+    auto srow = [&](int rt, int i) __attribute__((always_inline)) { return 32 * (rt >> 1) + 8 * g + 4 * (rt & 1) + i; };
+    f32x4 S[NKD];
+#pragma unroll
+    for (int rt = 0; rt < NKD; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[((int64_t)bh * DK + srow(rt, i)) * DV + colw + r] : 0.0f;
+    }
+    const int swr = sw_qk<DK>(r);
+    const int te = 4 * g + ((lane >> 2) & 3);
+    const int tc = lane & 3;
+    const int swt = sw_qk<DK>(te);
+    const int v_off = te * SH::RBV + 16 * (((2 * w + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
+    const int s_lane = (8 * g * DV + colw + r) * 4;
+
+    auto step = [&](int c, const lds_u8* cK, const lds_u8* cV, const lds_u8* cT) __attribute__((always_inline)) {
+        typedef quad __attribute__((address_space(3))) lds_quad;
+        {   // the state entering chunk c
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(s_all + ((int64_t)bh * NC + c) * DK * DV, DK * DV * 4);
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = S[rt][i];   // to a scalar before the bit cast (see bwd_chain_mx_kernel)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), rs, s_lane,
+                                                          (32 * (rt >> 1) + 4 * (rt & 1) + i) * DV * 4, 0);
+                }
+            }
+        }
+        auto frag = [&](int rb, int kp) __attribute__((always_inline)) {
+            return bx8(*reinterpret_cast<const lds_bf16x8*>(cK + (16 * rb + r) * SH::RBQ + 16 * ((4 * kp + g) ^ swr)));
+        };
+        auto pair = [&](quad a, quad b) __attribute__((always_inline)) -> bx8 { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); };
+        auto kt = [&](int rt, int kb) __attribute__((always_inline)) {
+            const int off = te * SH::RBQ + 16 * ((4 * (rt >> 1) + tc) ^ swt) + 8 * (rt & 1);
+            return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (lds_s16x4*)(const_cast<lds_u8*>(cK) + 16 * kb * SH::RBQ + off)));
+        };
+        auto ta = [&](int rb, int kb) __attribute__((always_inline)) {
+            return *reinterpret_cast<const lds_quad*>(cT + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+        };
+        static_for<2>([&](auto hc) {
+            constexpr int b0 = 2 * decltype(hc)::value;
+            bx8 Sq[NKP];
+#pragma unroll
+            for (int kp = 0; kp < NKP; ++kp) Sq[kp] = pair(M::cvt(S[2 * kp]), M::cvt(S[2 * kp + 1]));
+            quad Rq[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4 xk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kp = 0; kp < NKP; ++kp) xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag(b0 + j, kp), Sq[kp], xk, 0, 0, 0);
+                const quad vq = __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                             (lds_s16x4*)(const_cast<lds_u8*>(cV) + 16 * (b0 + j) * SH::RBV + v_off)));
+                f32x4 rr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rr[e] = (float)vq[e] - xk[e];
+                Rq[j] = M::cvt(rr);
+            }
+            // Delta = Ta R over the half (its diagonal 32 x 32 block of Ta)
+            f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+            M::mma1(d0, ta(b0, b0), Rq[0]);
+            M::mma2(d1, ta(b0 + 1, b0), ta(b0 + 1, b0 + 1), Rq[0], Rq[1]);
+            const quad D0 = M::cvt(d0), D1 = M::cvt(d1);
+            // S += K^T Delta
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) M::mma2(S[rt], kt(rt, b0), kt(rt, b0 + 1), D0, D1);
+        });
+        wait_vm(I0{});
+        __builtin_amdgcn_s_barrier();
+    };
+    auto stepb = [&](int c, const lds_u8* b) __attribute__((always_inline)) { step(c, b + OK_, b + OV_, b + OT_); };
+    if (NC > 0) __builtin_amdgcn_s_barrier();
+    for (int c = 0; c < NC; c += 3) {
+        stepb(c, buf0);
+        if (c + 1 < NC) stepb(c + 1, buf1);
+        if (c + 2 < NC) stepb(c + 2, buf2);
+    }
+}
+
 // Launches the matrix-core state-gradient pass when it applies (bf16, d_k >= 32, 64-token chunks); returns false
 // otherwise, leaving the launch to bwd_chain_kernel.
 template <int DK, int C>
@@ -343,6 +531,46 @@ bool launch_bwd_chain_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
         return true;
     }
 }
+
+// Launches the matrix-core state recompute when it applies (bf16, d_k >= 32, 64-token chunks).
+template <int DK, int C>
+bool launch_bwd_states_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
+    if constexpr (DK < 32 || C != 64) {
+        (void)a;
+        (void)s;
+        (void)err;
+        return false;
+    } else {
+        int dvs = a.d_v < 64 ? a.d_v : 64;
+        while (dvs > 16 && (int64_t)a.BH * (a.d_v / dvs) < 256) dvs /= 2;
+        const int nslab = a.d_v / dvs;
+        const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
+        const bf16* k = static_cast<const bf16*>(a.k);
+        const bf16* v = static_cast<const bf16*>(a.v);
+        const bf16* tw = static_cast<const bf16*>(a.tw);
+        switch (dvs) {
+            case 16:
+                hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 16>), dim3((unsigned)grid), dim3(16 / 16 * 64 + 64), 0, s,
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab);
+                break;
+            case 32:
+                hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 32>), dim3((unsigned)grid), dim3(32 / 16 * 64 + 64), 0, s,
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab);
+                break;
+            default:
+                hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 64>), dim3((unsigned)grid), dim3(64 / 16 * 64 + 64), 0, s,
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab);
+                break;
+        }
+        *err = hipGetLastError();
+        return true;
+    }
+}
+
+template <int DK, int C>
+struct BwdStatesFast<bf16, DK, C> {
+    static bool launch(const BwdArgs& a, hipStream_t s, hipError_t* e) { return launch_bwd_states_mx<DK, C>(a, s, e); }
+};
 
 template <int DK, int C>
 struct BwdChainFast<bf16, DK, C> {
