@@ -604,6 +604,16 @@ efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, c
         e = efla::launch_varlen_prep(layout->cu_seqlens, cu_tok, cu_chunks, chunk_seq, B, L, chunk,
                                      (L + chunk - 1) / chunk + B, s);
     }
+    if (dtype == EFLA_BF16 && d_k >= 32 && chunk == 64 && lp.sp.nseg == 1) {
+        // the one-launch kernel (efla_chunk_fwd's form for these sizes) reads the views and packed sequences itself;
+        // of the workspace it uses only the sanitised offsets
+        int dvs = 0;
+        st = check_chunk_sizes(false, B, H, L, d_k, d_v, chunk, dtype, 0, &dvs);
+        if (st != EFLA_OK) return st;
+        efla::ChunkArgs a1{q, k, v, beta, o, initial_state, final_state, (int)BH, L, d_k, d_v, chunk, dvs, gate, &ly};
+        if (e == hipSuccess) e = efla::launch_chunk_fwd_bf16(a1, s);
+        return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_fwd_layout launch");
+    }
     efla::SplitArgs a{q, k, v, beta, o, initial_state, final_state, ws + lp.off_ut, (int)BH, L, d_k, d_v, chunk,
                       lp.sp.dvs, gate};
     a.layout = &ly;

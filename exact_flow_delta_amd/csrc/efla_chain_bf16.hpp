@@ -906,8 +906,8 @@ constexpr int chain_ut_bf16_bytes(int dk, int dvs) {
     return 3 * (2 * nlq + nlv + nlt + 1) * 1024 + 2 * kUtHalfBytes;
 }
 
-// The whole chunked forward in one launch (bf16, d_k >= 32, 64-token chunks, contiguous [B,H,L,d]): the state
-// pass with its own UT waves in every workgroup.
+// The whole chunked forward in one launch (bf16, d_k >= 32, 64-token chunks; contiguous [B,H,L,d], or the strided
+// views and packed sequences of a.layout): the state pass with its own UT waves in every workgroup.
 template <int DK, int DVS>
 hipError_t launch_chain_ut_bf16_t(const ChunkArgs& a, hipStream_t stream) {
     constexpr int MODE = kOneLaunchUtMode;
@@ -921,7 +921,7 @@ hipError_t launch_chain_ut_bf16_t(const ChunkArgs& a, hipStream_t stream) {
     sa.chunk = 64;
     sa.dvs = DVS;
     const ChainSeg sg = chain_seg(sa, DK, 64, DVS);
-    const TokLayout ly = contiguous_layout(1, a.L, DK, a.d_v);
+    const TokLayout ly = a.layout ? *a.layout : contiguous_layout(1, a.L, DK, a.d_v);
     const int nslab = a.d_v / DVS;
     const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
     const int threads = DVS / 16 * 64 + (MODE == 2 ? 256 : 192);

@@ -17,6 +17,8 @@ hipError_t launch_alpha(const void* k, efla_dtype dt, const float* beta, float* 
 hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, const float* beta, efla_dtype dt,
                                  float* state, void* o, int64_t NH, int d_k, int d_v, int gate, hipStream_t stream);
 
+struct TokLayout;
+
 // Chunked forward.  One workgroup per (batch*head, d_v slab of `dvs` columns); every workgroup
 // walks the chunks of its sequence in order, carrying its slab of the state.
 struct ChunkArgs {
@@ -29,6 +31,7 @@ struct ChunkArgs {
     float* sf;         // may be null
     int BH, L, d_k, d_v, chunk, dvs;
     int gate;          // 0: exact coefficient; p: p-th order Runge-Kutta (gate_alpha)
+    const TokLayout* layout = nullptr;   // null: contiguous [B,H,L,d] (the one-launch kernel takes any other)
 };
 
 // LDS bytes of the chunk kernel for these sizes, or -1 when no kernel is built for them.

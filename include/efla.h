@@ -351,9 +351,10 @@ typedef struct efla_layout {
 } efla_layout;
 
 /*
- * efla_chunk_fwd_layout -- efla_chunk_fwd_split_gate / efla_chunk_fwd_scan over tensors in the layout
- * described by `layout` (NULL: contiguous [B,H,L,d]).  Same operator, gate, states, aliasing rules and
- * errors, plus:
+ * efla_chunk_fwd_layout -- the forward over tensors in the layout described by `layout` (NULL: contiguous
+ * [B,H,L,d]), in the form efla_chunk_fwd_gate would take: the one-launch kernel for bf16 with d_k >= 32 and
+ * 64-token chunks when one segment is used (then bit-identical to that kernel on contiguous copies), else
+ * efla_chunk_fwd_split_gate or efla_chunk_fwd_scan.  Same operator, gate, states, aliasing rules and errors, plus:
  *   strides    all >= 0; those of q, k, v, o multiples of 16 bytes / element size (8 for bf16, 4 for fp32);
  *              token strides at least the row (d_k for q and k, d_v for v) and 1 for beta, and below
  *              2^31 / (64 * element size); the rows of o must not overlap one another (sorted by stride,

@@ -3,12 +3,14 @@ with the fp64 oracle.
 
 The layouts change only where the kernels read and write, so the results must match the token recurrence to
 the same bar as the contiguous forward: max |x - ref| / max |ref| per tensor below 1e-5 (fp32 inputs) or 2e-2
-(bf16 inputs); with a contiguous layout they must equal the split forward's bit for bit.  Packed sequences are
+(bf16 inputs); with a contiguous layout they must equal efla_chunk_fwd's form for the sizes bit for bit.  Packed sequences are
 checked one sequence at a time against the oracle run on that sequence alone from its own initial state.
 Cases: [B,L,H,d] views, slices of a fused projection (token stride 3 H d, beta with a token stride),
 segment-parallel runs over strided views, packed batches with empty, one-token, chunk-edge and long
 sequences, a long mixed-length batch, offsets that need clamping, and each state-pass kernel (the swizzled
-bf16 one for d_k >= 32, the generic one for fp32)."""
+bf16 one for d_k >= 32, the generic one for fp32); bf16 with d_k >= 32 and 64-token chunks runs the one-launch
+kernel (the UT transform inside the state pass's workgroups), whose strided and packed results must equal its
+contiguous ones bit for bit."""
 import os
 import sys
 
@@ -93,15 +95,49 @@ def test_strided_segments(dtype, d_k, chunk):
     _check(x, dtype, o, S)
 
 
-def test_contiguous_layout_equals_split():
+@pytest.mark.parametrize("chunk,method", [(64, "fused"), (32, "split")])
+def test_contiguous_layout_equals_default(chunk, method):
+    """With a contiguous layout the layout entry is efla_chunk_fwd's form for the sizes, bit for bit: the one-launch
+    kernel for bf16 with 64-token chunks, the split form otherwise."""
     w = W.workload(3, B=2, H=4, L=700)
     x = W.make_fwd_inputs(w)
     d = {n: dev(x[n], "bf16") for n in ("q", "k", "v")}
     beta = torch.from_numpy(x["beta"]).cuda()
-    o1, S1 = efla.chunk_fwd(d["q"], d["k"], d["v"], beta, method="split")
-    o2, S2 = efla.chunk_fwd_layout(d["q"], d["k"], d["v"], beta)
+    o1, S1 = efla.chunk_fwd(d["q"], d["k"], d["v"], beta, method=method, chunk_size=chunk)
+    o2, S2 = efla.chunk_fwd_layout(d["q"], d["k"], d["v"], beta, chunk_size=chunk)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("gate", [0, 3])
+def test_one_launch_bthd_equals_contiguous(gate):
+    """[B,L,H,d] views through the one-launch kernel (bf16, d_k 128, 64-token chunks, a ragged length, an initial
+    state): the same arithmetic as on contiguous copies, so the same bits; and the oracle's result."""
+    w = W.workload(6 if gate else 3, B=2, H=3, L=333, d_k=128, d_v=128, chunk=64, dtype="bf16")
+    x = W.make_fwd_inputs(w)
+    if x["initial_state"] is None:
+        x["initial_state"] = (0.1 * np.random.default_rng(5).standard_normal((2, 3, 128, 128))).astype(np.float32)
+    q, k, v = _bthd(x["q"], "bf16"), _bthd(x["k"], "bf16"), _bthd(x["v"], "bf16")
+    beta = _beta_bth(x["beta"])
+    out = torch.full_like(v, float("nan"))
+    sf = torch.full((2, 3, 128, 128), float("nan"), device="cuda")
+    o1, S1 = efla.chunk_fwd_layout(q, k, v, beta, initial_state=_s0(x), chunk_size=64, gate=gate, out=out,
+                                   final_state=sf)
+    o2, S2 = efla.chunk_fwd(q.contiguous(), k.contiguous(), v.contiguous(), beta.contiguous(), initial_state=_s0(x),
+                            chunk_size=64, gate=gate, method="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(o1.contiguous(), o2) and torch.equal(S1, S2)
+    _check(x, "bf16", o1, S1, gate=gate)
+
+
+def test_one_launch_packed_gate_no_initial_state():
+    # packed sequences through the one-launch kernel with a Runge-Kutta gate and no initial state
+    lengths = [130, 0, 64, 1, 250, 63]
+    w = W.workload(6, H=2, d_k=128, d_v=128, chunk=64, dtype="bf16")
+    x = W.make_packed_inputs(w, lengths)
+    x["initial_state"] = None
+    o, S = _packed(x, "bf16", 64, gate=3)
+    _check_packed(x, "bf16", o, S, x["cu_seqlens"], gate=3)
 
 
 def _packed(x, dtype, chunk, gate=0, bthd=False, cu_override=None, out_nan=True):
@@ -180,12 +216,13 @@ def test_packed_gate_and_no_initial_state():
     _check_packed(x, "bf16", o, S, x["cu_seqlens"], gate=2)
 
 
+@pytest.mark.parametrize("dtype,chunk", [("f32", 32), ("bf16", 64)])
 @pytest.mark.parametrize("cu", [[-5, 120, 90, 400], [0, 200, 0, 200], [50, 10, 70, 70]])
-def test_packed_offsets_are_sanitised(cu):
+def test_packed_offsets_are_sanitised(cu, dtype, chunk):
     # offsets out of order and out of range: [-5,120,90,400] -> [0,120,120,200]; [0,200,0,200] -> one full
-    # sequence and two empty ones; [50,10,70,70] -> [50,50,70,70]
-    w = W.workload(2, H=2, d_k=64, d_v=64, chunk=32, dtype="f32")
+    # sequence and two empty ones; [50,10,70,70] -> [50,50,70,70] (bf16 with 64-token chunks: the one-launch kernel)
+    w = W.workload(2, H=2, d_k=64, d_v=64, chunk=chunk, dtype=dtype)
     x = W.make_packed_inputs(w, [100, 40, 60])
     cu = np.array(cu, dtype=np.int32)
-    o, S = _packed(x, "f32", 32, cu_override=cu, out_nan=False)
-    _check_packed(x, "f32", o, S, cu)
+    o, S = _packed(x, dtype, chunk, cu_override=cu, out_nan=False)
+    _check_packed(x, dtype, o, S, cu)
