@@ -124,6 +124,10 @@ def load_library():
     lib.efla_chunk_bwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                    _i32, _i32, _i32, _i32, _vp, _sz, _vp]
     lib.efla_chunk_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+    lib.efla_chunk_bwd_layout.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(Layout), _vp, _sz, _vp]
+    lib.efla_chunk_bwd_layout_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                         ctypes.POINTER(_sz)]
     lib.efla_chunk_state_pass.argtypes = [_vp, _vp, _vp, _vp, _sz, _i32, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     for fn in ("efla_alpha", "efla_chunk_fwd", "efla_chunk_fwd_gate", "efla_chunk_fwd_form", "efla_chunk_fwd_slab", "efla_recurrent_step", "efla_chunk_fwd_plan",
@@ -447,6 +451,75 @@ def chunk_bwd(q, k, v, beta, d_o, initial_state=None, d_final=None, chunk_size=6
                               _ptr(d_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(d_init), B, H, L, d_k, d_v,
                               int(chunk_size), int(gate), _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(v.device)), "efla_chunk_bwd")
+    return dq, dk, dv, dbeta, d_init
+
+
+def chunk_bwd_layout_workspace_size(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, varlen=False) -> int:
+    """Bytes of workspace chunk_bwd_layout needs (host only); varlen: packed sequences."""
+    lib = load_library()
+    n = _sz()
+    _check(lib.efla_chunk_bwd_layout_workspace_size(B, H, L, d_k, d_v, chunk, _dtype_of(dtype), int(bool(varlen)),
+                                                    ctypes.byref(n)), "efla_chunk_bwd_layout_workspace_size")
+    return n.value
+
+
+def chunk_bwd_layout(q, k, v, beta, d_o, cu_seqlens=None, initial_state=None, d_final=None, chunk_size=64,
+                     gate=GATE_EXACT, want_initial_grad=True, grads=None, workspace=None):
+    """Gradients of chunk_fwd_layout's operator over strided views or packed sequences (efla_chunk_bwd_layout).
+
+    q, k, v, beta, d_o and cu_seqlens as chunk_fwd_layout's q, k, v, beta, o and cu_seqlens (any strides, the
+    feature dimension contiguous).  The gradients are written with the strides of their inputs: ``grads`` =
+    (dq, dk, dv, dbeta) views of exactly those strides (e.g. slices of a fused gradient buffer when q, k, v are
+    slices of a fused projection), or None to allocate them.  Returns (dq, dk, dv, dbeta, d_initial or None);
+    states are [N,H,d_k,d_v] for N packed sequences.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
+        _dev_view(t, name, 4)
+    _dev_view(beta, "beta", 3)
+    if not (q.dtype == k.dtype == v.dtype == d_o.dtype):
+        raise TypeError("q, k, v, d_o must share a dtype")
+    B, H, L, d_k = k.shape
+    d_v = v.shape[-1]
+    if tuple(q.shape) != (B, H, L, d_k) or tuple(v.shape[:3]) != (B, H, L) or d_o.shape != v.shape:
+        raise ValueError("q, k, v, d_o shapes disagree")
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, L):
+        raise ValueError("beta must be float32 [B,H,L]")
+    N = B
+    if cu_seqlens is not None:
+        _dev_tensor(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+        if B != 1:
+            raise ValueError("packed sequences are given as [1,H,T,d] views")
+        N = cu_seqlens.numel() - 1
+    for name, x in (("initial_state", initial_state), ("d_final", d_final)):
+        if x is not None:
+            _dev_tensor(x, name)
+            if x.dtype != torch.float32 or tuple(x.shape) != (N, H, d_k, d_v):
+                raise ValueError("%s must be float32 [%d,H,d_k,d_v]" % (name, N))
+    if grads is None:
+        grads = tuple(torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device) for t in (q, k, v, beta))
+    dq, dk, dv, dbeta = grads
+    for g, t, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (dbeta, beta, "dbeta")):
+        if not isinstance(g, torch.Tensor) or g.device != t.device or g.dtype != t.dtype or g.shape != t.shape or \
+                g.stride() != t.stride():
+            raise ValueError("%s must be a %s tensor of %s's shape and strides" % (name, t.dtype, name[1:]))
+    d_init = torch.empty((N, H, d_k, d_v), dtype=torch.float32, device=v.device) if want_initial_grad else None
+    lay = Layout()
+    for f, t in (("q", q), ("k", k), ("v", v), ("o", d_o)):
+        getattr(lay, f)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    lay.beta[:] = [beta.stride(0), beta.stride(1), beta.stride(2)]
+    lay.cu_seqlens = _ptr(cu_seqlens)
+    need = chunk_bwd_layout_workspace_size(N, H, L, d_k, d_v, int(chunk_size), v.dtype, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=v.device)
+    _dev_tensor(workspace, "workspace")
+    _check(lib.efla_chunk_bwd_layout(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _dtype_code(v), _ptr(initial_state),
+                                     _ptr(d_o), _ptr(d_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(d_init),
+                                     N, H, L, d_k, d_v, int(chunk_size), int(gate), ctypes.byref(lay),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(v.device)), "efla_chunk_bwd_layout")
     return dq, dk, dv, dbeta, d_init
 
 

@@ -489,8 +489,9 @@ int64_t span(const int64_t st[3], int64_t n0, int64_t n1, int64_t n2, int64_t in
 }
 
 // No two rows share an element: the dimensions of more than one row, sorted by stride, each step over at
-// least the extent of the ones inside it.
+// least the extent of the ones inside it.  An empty tensor has no rows.
 bool rows_disjoint(const int64_t st[3], const int64_t n[3], int64_t inner) {
+    if (n[0] <= 0 || n[1] <= 0 || n[2] <= 0) return true;
     int idx[3] = {0, 1, 2};
     for (int i = 0; i < 3; ++i)
         for (int j = i + 1; j < 3; ++j)
@@ -503,6 +504,88 @@ bool rows_disjoint(const int64_t st[3], const int64_t n[3], int64_t inner) {
         ext += (n[d] - 1) * st[d];
     }
     return true;
+}
+
+// The kernels' token layout for the caller's (NULL: contiguous [B,H,L,d]), with the stride checks every entry point
+// over layouts makes (see efla_chunk_fwd_layout).
+efla_status make_layout(const efla_layout* layout, efla_dtype dt, int B, int H, int L, int d_k, int d_v,
+                        efla::TokLayout* out) {
+    const bool varlen = layout && layout->cu_seqlens;
+    const int64_t es = (int64_t)esize(dt);
+    efla::TokLayout ly = efla::contiguous_layout(H, L, d_k, d_v);
+    if (layout) {
+        const int64_t* src[5] = {layout->q, layout->k, layout->v, layout->o, layout->beta};
+        int64_t* dst[5] = {&ly.q_b, &ly.k_b, &ly.v_b, &ly.o_b, &ly.be_b};
+        for (int i = 0; i < 5; ++i) {
+            for (int j = 0; j < 3; ++j) {
+                const int64_t x = (varlen && j == 0) ? 0 : src[i][j];   // packed: no batch stride
+                if (x < 0) return EFLA_ERR_INVALID_ARG;
+                if (i < 4 && x % (16 / es) != 0) return EFLA_ERR_INVALID_ARG;   // 16-byte rows
+                dst[i][j] = x;
+            }
+        }
+        // rows of a chunk past the end of a sequence read as zeros only when no token's row overlaps the next
+        if (ly.q_t < d_k || ly.k_t < d_k || ly.v_t < d_v || ly.be_t < 1) return EFLA_ERR_INVALID_ARG;
+        // in-chunk offsets are 32-bit byte offsets
+        const int64_t lim = (int64_t)INT32_MAX / 64;
+        if (ly.q_t * es >= lim || ly.k_t * es >= lim || ly.v_t * es >= lim || ly.o_t * es >= lim || ly.be_t * 4 >= lim)
+            return EFLA_ERR_INVALID_ARG;
+        ly.cu_seqlens = layout->cu_seqlens;
+    }
+    ly.H = H;
+    ly.nseq = B;
+    *out = ly;
+    return EFLA_OK;
+}
+
+// Two strided tensors of the same element size es, strides st and sizes n (rows of `inner` contiguous elements) at
+// bases a and b share no element although their address extents overlap -- slices of one fused buffer.  Sufficient
+// test: with the dimensions of more than one index sorted by stride, those adjacent to the block so far (stride
+// equal to it) merged into it, every remaining stride is a multiple of the smallest remaining one, s, so every block
+// of either tensor starts at the same residue modulo s as its base; blocks of `block` elements starting at residues
+// 0 and r = |b - a| mod s then miss one another when block <= r <= s - block.
+bool rows_interleave(const void* a, const void* b, int64_t es, const int64_t st[3], const int64_t n[3],
+                     int64_t inner) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    const uint64_t dbytes = pa > pb ? pa - pb : pb - pa;
+    if (es <= 0 || dbytes % (uint64_t)es != 0) return false;
+    const int64_t delta = (int64_t)(dbytes / (uint64_t)es);
+    int idx[3], m = 0;
+    for (int d = 0; d < 3; ++d)
+        if (n[d] > 1) idx[m++] = d;
+    for (int i = 0; i < m; ++i)
+        for (int j = i + 1; j < m; ++j)
+            if (st[idx[j]] < st[idx[i]]) { const int t = idx[i]; idx[i] = idx[j]; idx[j] = t; }
+    int64_t block = inner;
+    int i = 0;
+    while (i < m && st[idx[i]] == block) block *= n[idx[i++]];
+    if (i == m) return false;   // one contiguous block: the extents decide
+    const int64_t sm = st[idx[i]];
+    if (sm < 2 * block) return false;
+    for (int j = i + 1; j < m; ++j)
+        if (st[idx[j]] % sm != 0) return false;
+    const int64_t r = delta % sm;
+    return r >= block && r <= sm - block;
+}
+
+// A tensor argument for the overlap checks: its address extent and, when strided (st set), its element size,
+// strides, sizes and row length.
+struct Ext {
+    const void* p;
+    size_t bytes;
+    int64_t es;
+    const int64_t* st;
+    const int64_t* n;
+    int64_t inner;
+};
+
+// No element shared: disjoint extents, or rows that interleave (same element size, strides, sizes and rows)
+bool disjoint(const Ext& a, const Ext& b) {
+    if (!overlap(a.p, a.bytes, b.p, b.bytes)) return true;
+    if (!a.st || !b.st || a.es != b.es || a.inner != b.inner) return false;
+    for (int d = 0; d < 3; ++d)
+        if (a.st[d] != b.st[d] || a.n[d] != b.n[d]) return false;
+    return rows_interleave(a.p, b.p, a.es, a.st, a.n, a.inner);
 }
 
 }  // namespace
@@ -528,28 +611,9 @@ efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, c
     if (st != EFLA_OK) return st;
     const int64_t BH = (int64_t)B * H;
     const int64_t es = (int64_t)esize(dtype);
-    efla::TokLayout ly = efla::contiguous_layout(H, L, d_k, d_v);
-    if (layout) {
-        const int64_t* src[5] = {layout->q, layout->k, layout->v, layout->o, layout->beta};
-        int64_t* dst[5] = {&ly.q_b, &ly.k_b, &ly.v_b, &ly.o_b, &ly.be_b};
-        for (int i = 0; i < 5; ++i) {
-            for (int j = 0; j < 3; ++j) {
-                const int64_t x = (varlen && j == 0) ? 0 : src[i][j];   // packed: no batch stride
-                if (x < 0) return EFLA_ERR_INVALID_ARG;
-                if (i < 4 && x % (16 / es) != 0) return EFLA_ERR_INVALID_ARG;   // 16-byte rows
-                dst[i][j] = x;
-            }
-        }
-        // rows of a chunk past the end of a sequence read as zeros only when no token's row overlaps the next
-        if (ly.q_t < d_k || ly.k_t < d_k || ly.v_t < d_v || ly.be_t < 1) return EFLA_ERR_INVALID_ARG;
-        // in-chunk offsets are 32-bit byte offsets
-        const int64_t lim = (int64_t)INT32_MAX / 64;
-        if (ly.q_t * es >= lim || ly.k_t * es >= lim || ly.v_t * es >= lim || ly.o_t * es >= lim || ly.be_t * 4 >= lim)
-            return EFLA_ERR_INVALID_ARG;
-        ly.cu_seqlens = layout->cu_seqlens;
-    }
-    ly.H = H;
-    ly.nseq = B;
+    efla::TokLayout ly;
+    st = make_layout(layout, dtype, B, H, L, d_k, d_v, &ly);
+    if (st != EFLA_OK) return st;
     const int64_t nb = varlen ? 1 : B;   // batch extent of the token tensors
     const int64_t so[3] = {ly.o_b, ly.o_h, ly.o_t}, no[3] = {nb, H, L};
     if (!rows_disjoint(so, no, d_v)) return EFLA_ERR_INVALID_ARG;
@@ -623,96 +687,148 @@ efla_status efla_chunk_fwd_layout(const void* q, const void* k, const void* v, c
 
 namespace {
 
-// Workspace of efla_chunk_bwd: the UT output (Ta), then the state entering and the gradient of the state
-// leaving every chunk (fp32, d_k x d_v each), then -- where the per-chunk gradients run on bf16 matrix cores (bf16,
-// d_k >= 32, chunk 32 or 64, d_v a multiple of 32) -- T^T of every chunk (bf16, chunk x chunk); each part 256-byte
-// aligned.
+// Workspace of efla_chunk_bwd_layout: with packed sequences first the sanitised token offsets, the chunk offsets
+// (B + 1 int32 each) and the chunk -> sequence table (ceil(L / C) + B int32); then the UT output (Ta), the state
+// entering and the gradient of the state leaving every chunk (fp32, d_k x d_v each), then -- where the per-chunk
+// gradients run on bf16 matrix cores (bf16, d_k >= 32, chunk 32 or 64, d_v a multiple of 32) -- T^T of every chunk
+// (bf16, chunk x chunk); each part 256-byte aligned.  Chunks: B H ceil(L / C), or with packed sequences
+// H (ceil(L / C) + B), which bounds H sum_b ceil(len_b / C) for disjoint sequences.
 struct BwdPlan {
-    size_t off_s, off_ds, off_tt, total;
+    size_t off_ut, off_s, off_ds, off_tt, total;
     bool tt;
 };
 
-efla_status bwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, BwdPlan* p) {
+efla_status bwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, bool varlen, BwdPlan* p) {
     if (!valid_dtype(dt) || B < 0 || H < 0 || L < 0) return EFLA_ERR_INVALID_ARG;
     if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     const int64_t NC = (L + chunk - 1) / chunk;
-    if (BH > INT32_MAX || BH * NC > INT32_MAX || BH * (d_v / 16) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
-    const size_t states = round_up_256((size_t)BH * NC * d_k * d_v * 4);
-    p->off_s = round_up_256(ut_bytes(BH, L, chunk, dt));
+    const int64_t NU = varlen ? (int64_t)H * (NC + B) : BH * NC;
+    if (BH > INT32_MAX || NU > INT32_MAX || BH * (d_v / 16) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
+    if (varlen && (int64_t)B + 1 > INT32_MAX / 8) return EFLA_ERR_INVALID_ARG;
+    const size_t states = round_up_256((size_t)NU * d_k * d_v * 4);
+    p->off_ut = varlen ? round_up_256((size_t)(B + 1) * 8 + (size_t)(NC + B) * 4) : 0;
+    p->off_s = p->off_ut + round_up_256((size_t)NU * (size_t)efla::ut_block_elems(chunk) * esize(dt));
     p->off_ds = p->off_s + states;
     p->off_tt = p->off_ds + states;
     p->tt = dt == EFLA_BF16 && d_k >= 32 && chunk >= 32 && d_v % 32 == 0;
-    p->total = p->off_tt + (p->tt ? round_up_256((size_t)BH * NC * chunk * chunk * 2) : 0);
+    p->total = p->off_tt + (p->tt ? round_up_256((size_t)NU * chunk * chunk * 2) : 0);
     return EFLA_OK;
 }
 
 }  // namespace
 
-efla_status efla_chunk_bwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
-                                          size_t* bytes) {
+efla_status efla_chunk_bwd_layout_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                                 int varlen, size_t* bytes) {
     BwdPlan p;
-    const efla_status st = bwd_plan(B, H, L, d_k, d_v, chunk, dtype, &p);
+    const efla_status st = bwd_plan(B, H, L, d_k, d_v, chunk, dtype, varlen != 0, &p);
     if (st != EFLA_OK) return st;
     if (!bytes) return EFLA_ERR_INVALID_ARG;
     *bytes = p.total;
     return EFLA_OK;
 }
 
-efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
-                           const float* initial_state, const void* d_o, const float* d_final, void* dq, void* dk,
-                           void* dv, float* dbeta, float* d_initial, int B, int H, int L, int d_k, int d_v,
-                           int chunk, int gate, void* workspace, size_t workspace_bytes, void* stream) {
+efla_status efla_chunk_bwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                          size_t* bytes) {
+    return efla_chunk_bwd_layout_workspace_size(B, H, L, d_k, d_v, chunk, dtype, 0, bytes);
+}
+
+efla_status efla_chunk_bwd_layout(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                  const float* initial_state, const void* d_o, const float* d_final, void* dq,
+                                  void* dk, void* dv, float* dbeta, float* d_initial, int B, int H, int L, int d_k,
+                                  int d_v, int chunk, int gate, const efla_layout* layout, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
     if (!valid_gate(gate)) return EFLA_ERR_INVALID_ARG;
+    const bool varlen = layout && layout->cu_seqlens;
     BwdPlan p;
-    efla_status st = bwd_plan(B, H, L, d_k, d_v, chunk, dtype, &p);
+    efla_status st = bwd_plan(B, H, L, d_k, d_v, chunk, dtype, varlen, &p);
+    if (st != EFLA_OK) return st;
+    efla::TokLayout ly;
+    st = make_layout(layout, dtype, B, H, L, d_k, d_v, &ly);
     if (st != EFLA_OK) return st;
     const int64_t BH = (int64_t)B * H;
-    const size_t es = esize(dtype);
-    const size_t nq = (size_t)BH * L * d_k * es, nv = (size_t)BH * L * d_v * es, nb = (size_t)BH * L * 4;
+    const int64_t es = (int64_t)esize(dtype);
+    const int64_t nb = varlen ? 1 : B;   // batch extent of the token tensors
+    const int64_t sq[3] = {ly.q_b, ly.q_h, ly.q_t}, sk[3] = {ly.k_b, ly.k_h, ly.k_t}, sv[3] = {ly.v_b, ly.v_h, ly.v_t};
+    const int64_t so[3] = {ly.o_b, ly.o_h, ly.o_t}, sb[3] = {ly.be_b, ly.be_h, ly.be_t}, n3[3] = {nb, H, L};
+    // the gradients take their inputs' strides: no two of their rows (elements for dbeta) may share memory
+    if (!rows_disjoint(sq, n3, d_k) || !rows_disjoint(sk, n3, d_k) || !rows_disjoint(sv, n3, d_v) ||
+        !rows_disjoint(sb, n3, 1))
+        return EFLA_ERR_INVALID_ARG;
+    const size_t nq = (size_t)(span(sq, nb, H, L, d_k) * es), nk = (size_t)(span(sk, nb, H, L, d_k) * es);
+    const size_t nv = (size_t)(span(sv, nb, H, L, d_v) * es), no = (size_t)(span(so, nb, H, L, d_v) * es);
+    const size_t nbe = (size_t)(span(sb, nb, H, L, 1) * 4);
     const size_t ns = (size_t)BH * d_k * d_v * 4;
+    const size_t ncu = varlen ? (size_t)(B + 1) * 4 : 0;
     if (L > 0 && BH > 0) {
         if (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta) return EFLA_ERR_INVALID_ARG;
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) || !aligned(dq, 16) ||
             !aligned(dk, 16) || !aligned(dv, 16) || !aligned(beta, 4) || !aligned(dbeta, 4))
             return EFLA_ERR_INVALID_ARG;
     }
+    if (varlen && BH > 0 && !aligned(layout->cu_seqlens, 4)) return EFLA_ERR_INVALID_ARG;
     if ((initial_state && !aligned(initial_state, 16)) || (d_final && !aligned(d_final, 16)) ||
         (d_initial && !aligned(d_initial, 16)))
         return EFLA_ERR_INVALID_ARG;
-    // outputs overlap nothing (inputs, one another, the workspace)
-    const void* in[7] = {q, k, v, beta, initial_state, d_o, d_final};
-    const size_t in_n[7] = {nq, nq, nv, nb, ns, nv, ns};
-    const void* out[5] = {dq, dk, dv, dbeta, d_initial};
-    const size_t out_n[5] = {nq, nq, nv, nb, ns};
+    // outputs overlap nothing (inputs, one another, the workspace): disjoint address extents, or rows of equal
+    // strides that interleave (slices of one fused buffer)
+    const void* cu = varlen ? (const void*)layout->cu_seqlens : nullptr;
+    const int64_t ek = (int64_t)es;
+    const Ext in[8] = {{q, nq, ek, sq, n3, d_k},   {k, nk, ek, sk, n3, d_k},       {v, nv, ek, sv, n3, d_v},
+                       {beta, nbe, 4, sb, n3, 1},   {initial_state, ns, 4, nullptr, nullptr, 0},
+                       {d_o, no, ek, so, n3, d_v}, {d_final, ns, 4, nullptr, nullptr, 0},
+                       {cu, ncu, 4, nullptr, nullptr, 0}};
+    const Ext out[5] = {{dq, nq, ek, sq, n3, d_k}, {dk, nk, ek, sk, n3, d_k}, {dv, nv, ek, sv, n3, d_v},
+                        {dbeta, nbe, 4, sb, n3, 1}, {d_initial, ns, 4, nullptr, nullptr, 0}};
     for (int i = 0; i < 5; ++i) {
-        for (int j = 0; j < 7; ++j)
-            if (overlap(out[i], out_n[i], in[j], in_n[j])) return EFLA_ERR_INVALID_ARG;
+        for (int j = 0; j < 8; ++j)
+            if (!disjoint(out[i], in[j])) return EFLA_ERR_INVALID_ARG;
         for (int j = i + 1; j < 5; ++j)
-            if (overlap(out[i], out_n[i], out[j], out_n[j])) return EFLA_ERR_INVALID_ARG;
+            if (!disjoint(out[i], out[j])) return EFLA_ERR_INVALID_ARG;
     }
     if (BH == 0) return EFLA_OK;
     if (L == 0 && !d_initial) return EFLA_OK;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total) return EFLA_ERR_WORKSPACE;
-    for (int j = 0; j < 7; ++j)
-        if (overlap(workspace, p.total, in[j], in_n[j])) return EFLA_ERR_INVALID_ARG;
+    for (int j = 0; j < 8; ++j)
+        if (overlap(workspace, p.total, in[j].p, in[j].bytes)) return EFLA_ERR_INVALID_ARG;
     for (int j = 0; j < 5; ++j)
-        if (overlap(workspace, p.total, out[j], out_n[j])) return EFLA_ERR_INVALID_ARG;
+        if (overlap(workspace, p.total, out[j].p, out[j].bytes)) return EFLA_ERR_INVALID_ARG;
     st = device_present();
     if (st != EFLA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     char* ws = static_cast<char*>(workspace);
     const bool bf = dtype == EFLA_BF16;
     hipError_t e = hipSuccess;
+    if (varlen) {
+        int* cu_tok = reinterpret_cast<int*>(ws);
+        int* cu_chunks = cu_tok + (B + 1);
+        int* chunk_seq = cu_chunks + (B + 1);
+        ly.cu_seqlens = cu_tok;
+        ly.cu_chunks = cu_chunks;
+        ly.chunk_seq = chunk_seq;
+        e = efla::launch_varlen_prep(layout->cu_seqlens, cu_tok, cu_chunks, chunk_seq, B, L, chunk,
+                                     (L + chunk - 1) / chunk + B, s);
+    }
+    void* tw = ws + p.off_ut;
     void* tt = p.tt ? (void*)(ws + p.off_tt) : nullptr;
-    if (L > 0)
-        e = bf ? efla::launch_ut_bf16(k, beta, ws, (int)BH, L, d_k, chunk, gate, s, tt)
-               : efla::launch_ut_f32(k, beta, ws, (int)BH, L, d_k, chunk, gate, s);
+    // contiguous tensors: every (batch, head) is one sequence of L tokens
+    const efla::TokLayout* lyp = layout ? &ly : nullptr;
+    if (L > 0 && e == hipSuccess)
+        e = bf ? efla::launch_ut_bf16(k, beta, tw, (int)BH, L, d_k, chunk, gate, s, tt, lyp)
+               : efla::launch_ut_f32(k, beta, tw, (int)BH, L, d_k, chunk, gate, s, lyp);
     efla::BwdArgs a{q, k, v, beta, initial_state, d_o, d_final, dq, dk, dv, dbeta, d_initial, (int)BH, L, d_k, d_v,
-                    chunk, gate, ws, reinterpret_cast<float*>(ws + p.off_s), reinterpret_cast<float*>(ws + p.off_ds),
-                    tt};
+                    chunk, gate, tw, reinterpret_cast<float*>(ws + p.off_s), reinterpret_cast<float*>(ws + p.off_ds),
+                    tt, lyp};
     if (e == hipSuccess) e = bf ? efla::launch_bwd_bf16(a, s) : efla::launch_bwd_f32(a, s);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_bwd launch");
+}
+
+efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                           const float* initial_state, const void* d_o, const float* d_final, void* dq, void* dk,
+                           void* dv, float* dbeta, float* d_initial, int B, int H, int L, int d_k, int d_v,
+                           int chunk, int gate, void* workspace, size_t workspace_bytes, void* stream) {
+    return efla_chunk_bwd_layout(q, k, v, beta, dtype, initial_state, d_o, d_final, dq, dk, dv, dbeta, d_initial, B,
+                                 H, L, d_k, d_v, chunk, gate, nullptr, workspace, workspace_bytes, stream);
 }
 
 namespace {

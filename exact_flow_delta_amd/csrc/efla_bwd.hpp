@@ -181,6 +181,21 @@ struct TaTile {
 
 }  // namespace bwd
 
+// The (batch*head, chunk) of workgroup u of a launch over every chunk of the UT workspace, and that sequence's
+// tokens; false for a workgroup past the last chunk (with packed sequences the grid is an upper bound).
+__device__ inline bool chunk_at(const TokLayout& ly, int u, int L, int C, int& bh, int& c, SeqView& sv) {
+    const int NC = (L + C - 1) / C;
+    if (ly.cu_seqlens) {
+        if (u >= ly.H * ly.cu_chunks[ly.nseq]) return false;
+        chunk_of<true>(ly, u, NC, bh, c);
+        sv = seq_view_t<true>(ly, bh, L, C);
+    } else {
+        chunk_of<false>(ly, u, NC, bh, c);
+        sv = seq_view_t<false>(ly, bh, L, C);
+    }
+    return true;
+}
+
 // ------------------------------------------------------------------------------------------------
 // The state entering every chunk: s_all[bh][c][i][j] (fp32, d_k x d_v), from S_0 = s0 (or 0) and
 // S <- S + K^T Ta (V - K S).  One workgroup per (head, slab of DVS state columns).
@@ -188,7 +203,8 @@ struct TaTile {
 template <typename E, int DK, int C, int DVS>
 __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict__ k, const E* __restrict__ v,
                                                              const E* __restrict__ tw, const float* __restrict__ s0,
-                                                             float* __restrict__ s_all, int L, int DV, int nslab) {
+                                                             float* __restrict__ s_all, int L, int DV, int nslab,
+                                                             TokLayout ly) {
     using namespace bwd;
     constexpr int LDK = DK + 2, LDV = DVS + 2, LDC = C + 2;
     constexpr int NQE = (C / 16) * (C / 16 + 1) / 2 * 256;
@@ -198,8 +214,8 @@ __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int bh = blockIdx.x / nslab, slab = blockIdx.x - bh * nslab;
     const int col0 = slab * DVS;
-    const int NC = (L + C - 1) / C;
-    const int64_t tok0 = (int64_t)bh * L;
+    const SeqView sv = seq_view(ly, bh, L, C);   // this sequence's tokens and first chunk
+    const int NC = (sv.len + C - 1) / C;
     Acc<DK, DVS> S;
     S.zero();
     if (s0) S.each(w, lane, [&](int i, int j, float& x) { x = s0[((int64_t)bh * DK + i) * DV + col0 + j]; });
@@ -207,15 +223,15 @@ __global__ __launch_bounds__(bwd::NT) void bwd_states_kernel(const E* __restrict
     Tile<E, C, DVS> tv;
     TaTile<E, C> tt;
     auto load = [&](int c) {
-        const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
-        tk.load(k + (tok0 + t0) * DK, DK, n, tid);
-        tv.load(v + (tok0 + t0) * DV + col0, DV, n, tid);
-        tt.load(tw + ((int64_t)bh * NC + c) * NQE, tid);
+        const int t0 = c * C, n = sv.len - t0 < C ? sv.len - t0 : C;
+        tk.load(k + sv.k0 + t0 * ly.k_t, ly.k_t, n, tid);
+        tv.load(v + sv.v0 + t0 * ly.v_t + col0, ly.v_t, n, tid);
+        tt.load(tw + ((int64_t)sv.chunk0 + c) * NQE, tid);
     };
     TaTile<E, C>::zero_upper(sT, LDC, tid);
     if (NC > 0) load(0);
     for (int c = 0; c < NC; ++c) {
-        float* out = s_all + ((int64_t)bh * NC + c) * DK * DV;
+        float* out = s_all + ((int64_t)sv.chunk0 + c) * DK * DV;
         S.each(w, lane, [&](int i, int j, float& x) {
             out[i * DV + col0 + j] = x;
             sS[i * LDV + j] = x;
@@ -256,7 +272,8 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(const E* __res
                                                             const E* __restrict__ tw, const E* __restrict__ d_o,
                                                             const float* __restrict__ d_final,
                                                             float* __restrict__ ds_all, E* __restrict__ dv,
-                                                            float* __restrict__ d_initial, int L, int DV, int nslab) {
+                                                            float* __restrict__ d_initial, int L, int DV, int nslab,
+                                                            TokLayout ly) {
     using namespace bwd;
     constexpr int NWV = kChainThreads / 64;   // two waves per SIMD
     constexpr int NTH = kChainThreads;
@@ -267,8 +284,8 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(const E* __res
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int bh = blockIdx.x / nslab, slab = blockIdx.x - bh * nslab;
     const int col0 = slab * DVS;
-    const int NC = (L + C - 1) / C;
-    const int64_t tok0 = (int64_t)bh * L;
+    const SeqView sv = seq_view(ly, bh, L, C);
+    const int NC = (sv.len + C - 1) / C;
     Acc<DK, DVS, NWV> dS;
     dS.zero();
     if (d_final)
@@ -277,17 +294,17 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(const E* __res
     Tile<E, C, DVS, NTH> to;
     TaTile<E, C, NTH> tt;
     auto load = [&](int c) {
-        const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
-        tq.load(q + (tok0 + t0) * DK, DK, n, tid);
-        tk.load(k + (tok0 + t0) * DK, DK, n, tid);
-        to.load(d_o + (tok0 + t0) * DV + col0, DV, n, tid);
-        tt.load(tw + ((int64_t)bh * NC + c) * NQE, tid);
+        const int t0 = c * C, n = sv.len - t0 < C ? sv.len - t0 : C;
+        tq.load(q + sv.q0 + t0 * ly.q_t, ly.q_t, n, tid);
+        tk.load(k + sv.k0 + t0 * ly.k_t, ly.k_t, n, tid);
+        to.load(d_o + sv.o0 + t0 * ly.o_t + col0, ly.o_t, n, tid);
+        tt.load(tw + ((int64_t)sv.chunk0 + c) * NQE, tid);
     };
     TaTile<E, C, NTH>::zero_upper(sT, LDC, tid);
     if (NC > 0) load(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
-        const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
-        float* out = ds_all + ((int64_t)bh * NC + c) * DK * DV;
+        const int t0 = c * C, n = sv.len - t0 < C ? sv.len - t0 : C;
+        float* out = ds_all + ((int64_t)sv.chunk0 + c) * DK * DV;
         dS.each(w, lane, [&](int i, int j, float& x) {
             out[i * DV + col0 + j] = x;
             sS[i * LDV + j] = x;
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(const E* __res
             mm(a, sT, 1, LDC, sD, LDV, 1, C, w, lane);
             a.each(w, lane, [&](int i, int j, float& x) {
                 sR[i * LDV + j] = -x;
-                if (i < n) dv[(tok0 + t0 + i) * DV + col0 + j] = from_f32<E>(x);
+                if (i < n) dv[sv.v0 + (int64_t)(t0 + i) * ly.v_t + col0 + j] = from_f32<E>(x);
             });
         }
         __syncthreads();
@@ -347,7 +364,7 @@ template <typename E, int DK, int C>
 __global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ beta,
     const E* __restrict__ d_o, const float* __restrict__ s_all, const float* __restrict__ ds_all, E* __restrict__ dq,
-    E* __restrict__ dk, float* __restrict__ dbeta, int L, int DV, int gate) {
+    E* __restrict__ dk, float* __restrict__ dbeta, int L, int DV, int gate, TokLayout ly) {
     using namespace bwd;
     constexpr int NWV = kChunkThreads / 64;   // two waves per SIMD: one's LDS reads and barriers overlap the other's products
     constexpr int NTH = kChunkThreads;
@@ -372,17 +389,21 @@ __global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
     float* sDa = sDlam + C;      // dalpha, then dlambda
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int NC = (L + C - 1) / C;
-    const int bh = blockIdx.x / NC, c = blockIdx.x - bh * NC;
-    const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
-    const int64_t tok = (int64_t)bh * L + t0;
-    const float* Sg = s_all + ((int64_t)bh * NC + c) * DK * DV;
-    const float* dSg = ds_all + ((int64_t)bh * NC + c) * DK * DV;
+    int bh, c;
+    SeqView sv;
+    if (!chunk_at(ly, blockIdx.x, L, C, bh, c, sv)) return;
+    const int t0 = c * C, n = sv.len - t0 < C ? sv.len - t0 : C;
+    const int64_t q0 = sv.q0 + (int64_t)t0 * ly.q_t, k0 = sv.k0 + (int64_t)t0 * ly.k_t;   // the chunk's first rows
+    const int64_t v0 = sv.v0 + (int64_t)t0 * ly.v_t, o0 = sv.o0 + (int64_t)t0 * ly.o_t;
+    const int64_t be0 = sv.be0 + (int64_t)t0 * ly.be_t;
+    const float* Sg = s_all + (int64_t)blockIdx.x * DK * DV;   // workgroup u works on chunk u of the workspace
+    const float* dSg = ds_all + (int64_t)blockIdx.x * DK * DV;
+    (void)bh;
 
     {
         Tile<E, C, DK, NTH> tq, tk;
-        tq.load(q + tok * DK, DK, n, tid);
-        tk.load(k + tok * DK, DK, n, tid);
+        tq.load(q + q0, ly.q_t, n, tid);
+        tk.load(k + k0, ly.k_t, n, tid);
         tq.store(sQ, LDK, tid);
         tk.store(sK, LDK, tid);
     }
@@ -392,8 +413,8 @@ __global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
     auto load_slab = [&](int col0) {
         ts.load(Sg + col0, DV, DK, tid);
         tds.load(dSg + col0, DV, DK, tid);
-        tv.load(v + tok * DV + col0, DV, n, tid);
-        to.load(d_o + tok * DV + col0, DV, n, tid);
+        tv.load(v + v0 + col0, ly.v_t, n, tid);
+        to.load(d_o + o0 + col0, ly.o_t, n, tid);
     };
     load_slab(0);
     if (tid < C) sDa[tid] = 0.0f;
@@ -401,7 +422,7 @@ __global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
     if (tid < C) {   // gates of the chunk's tokens (rows past the end: zero keys, zero step)
         float lam = 0.0f;
         for (int e = 0; e < DK; ++e) lam = fmaf(sK[tid * LDK + e], sK[tid * LDK + e], lam);
-        const float b = tid < n ? beta[tok + tid] : 0.0f;
+        const float b = tid < n ? beta[be0 + (int64_t)tid * ly.be_t] : 0.0f;
         sAl[tid] = gate_alpha(b, lam, gate);
         float db, dl;
         gate_alpha_grad(b, lam, gate, &db, &dl);
@@ -513,7 +534,7 @@ __global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
         const int i = tid;
         float s = sDa[i];
         for (int j = 0; j < i; ++j) s -= sL[i * LDC + j] * sT[i * LDC + j];
-        if (i < n) dbeta[tok + i] = s * sDb[i];
+        if (i < n) dbeta[be0 + (int64_t)i * ly.be_t] = s * sDb[i];
         sDa[i] = s * sDlam[i];
     }
     __syncthreads();
@@ -529,10 +550,10 @@ __global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
     mm(aK, sT, LDC, 1, sK, LDK, 1, C, w, lane);
     mm(aK, sT, 1, LDC, sK, LDK, 1, C, w, lane);
     aQ.each(w, lane, [&](int i, int e, float& x) {
-        if (i < n) dq[(tok + i) * DK + e] = from_f32<E>(x);
+        if (i < n) dq[q0 + (int64_t)i * ly.q_t + e] = from_f32<E>(x);
     });
     aK.each(w, lane, [&](int i, int e, float& x) {
-        if (i < n) dk[(tok + i) * DK + e] = from_f32<E>(fmaf(2.0f * sDa[i], sK[i * LDK + e], x));
+        if (i < n) dk[k0 + (int64_t)i * ly.k_t + e] = from_f32<E>(fmaf(2.0f * sDa[i], sK[i * LDK + e], x));
     });
 }
 
@@ -553,7 +574,21 @@ struct BwdArgs {
     float* s_all;    // BH x NC x d_k x d_v
     float* ds_all;   // BH x NC x d_k x d_v
     void* tt;        // T^T of every chunk (BH x NC x chunk x chunk, storage type), or null
+    // null: contiguous [B,H,L,d] tensors; else the strides of q, k, v, d_o (in o's place) and beta -- the
+    // gradients dq, dk, dv, dbeta take those of their input -- and packed sequences (then the UT workspace,
+    // s_all, ds_all and tt hold the chunks of the sequences in the layout's order)
+    const TokLayout* layout = nullptr;
 };
+
+// contiguous [B,H,L,d] tensors: every (batch, head) a sequence of L tokens
+inline TokLayout bwd_layout(const BwdArgs& a) {
+    return a.layout ? *a.layout : contiguous_layout(1, a.L, a.d_k, a.d_v);
+}
+// workgroups of a launch over every chunk of the workspace (packed sequences: an upper bound)
+inline int64_t bwd_chunk_grid(const BwdArgs& a, int C) {
+    const int64_t NC = (a.L + C - 1) / C;
+    return a.layout && a.layout->cu_seqlens ? (int64_t)a.layout->H * (NC + a.layout->nseq) : (int64_t)a.BH * NC;
+}
 
 // The per-chunk gradient kernel on bf16 matrix cores (efla_bwd_mx.hpp) takes the shapes it supports by
 // specialising this for bf16; launch() returns false where it does not apply.
@@ -573,12 +608,12 @@ struct BwdChainFast {
 
 template <typename E, int DK, int C>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-    const int NC = (a.L + C - 1) / C;
     const E* q = static_cast<const E*>(a.q);
     const E* k = static_cast<const E*>(a.k);
     const E* v = static_cast<const E*>(a.v);
     const E* d_o = static_cast<const E*>(a.d_o);
     const E* tw = static_cast<const E*>(a.tw);
+    const TokLayout ly = bwd_layout(a);
     if (a.L > 0) {
         hipError_t es = hipSuccess;
         if (BwdStatesFast<E, DK, C>::launch(a, s, &es)) {
@@ -586,11 +621,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
         } else if (a.d_v >= 32) {
             const int nslab = a.d_v / 32;
             hipLaunchKernelGGL((bwd_states_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(bwd::NT), 0, s, k,
-                               v, tw, a.s0, a.s_all, a.L, a.d_v, nslab);
+                               v, tw, a.s0, a.s_all, a.L, a.d_v, nslab, ly);
         } else {
             const int nslab = a.d_v / 16;
             hipLaunchKernelGGL((bwd_states_kernel<E, DK, C, 16>), dim3((unsigned)(a.BH * nslab)), dim3(bwd::NT), 0, s, k,
-                               v, tw, a.s0, a.s_all, a.L, a.d_v, nslab);
+                               v, tw, a.s0, a.s_all, a.L, a.d_v, nslab, ly);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -601,11 +636,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     } else if (a.d_v >= 32) {
         const int nslab = a.d_v / 32;
         hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(kChainThreads), 0, s, q, k,
-                           tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab);
+                           tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab, ly);
     } else {
         const int nslab = a.d_v / 16;
         hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 16>), dim3((unsigned)(a.BH * nslab)), dim3(kChainThreads), 0, s, q, k,
-                           tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab);
+                           tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab, ly);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.L == 0) return e;
@@ -615,9 +650,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_kernel<E, DK, C>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, C>), dim3((unsigned)((int64_t)a.BH * NC)), dim3(kChunkThreads), LDS, s, q, k,
-                       v, a.beta, d_o, a.s_all, a.ds_all, static_cast<E*>(a.dq), static_cast<E*>(a.dk), a.dbeta, a.L,
-                       a.d_v, a.gate);
+    hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, C>), dim3((unsigned)bwd_chunk_grid(a, C)), dim3(kChunkThreads), LDS, s, q,
+                       k, v, a.beta, d_o, a.s_all, a.ds_all, static_cast<E*>(a.dq), static_cast<E*>(a.dk), a.dbeta,
+                       a.L, a.d_v, a.gate, ly);
     return hipGetLastError();
 }
 

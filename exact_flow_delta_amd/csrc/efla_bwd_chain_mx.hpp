@@ -29,7 +29,7 @@ template <int DK, int DVS>
 __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ tw, const bf16* __restrict__ d_o,
     const float* __restrict__ d_final, float* __restrict__ ds_all, bf16* __restrict__ dv, float* __restrict__ d_initial,
-    int BH, int L, int DV, int nslab) {
+    int BH, int L, int DV, int nslab, TokLayout ly) {
     constexpr int C = 64;
     typedef ChainBf16Shape<DK, C, DVS, 0> SH;
     typedef Mma<bf16> M;
@@ -63,9 +63,11 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     const int slab_col = slab * DVS;
     const bool producer = w == NW;
     const int colw = slab_col + 16 * (producer ? 0 : w);
-    const int NC = (L + C - 1) / C;
-    const int64_t tok0 = (int64_t)bh * L;
-    const bf16* twh = tw + (int64_t)bh * NC * (NQ * QE);
+    const SeqView sv = seq_view(ly, bh, L, C);   // this sequence's tokens and first chunk
+    const int len = sv.len;
+    const int NC = (len + C - 1) / C;
+    const int64_t qs = ly.q_t, ks = ly.k_t, vs = ly.v_t, os = ly.o_t;   // token strides (elements)
+    const bf16* twh = tw + (int64_t)sv.chunk0 * (NQ * QE);
 
     // ---- loads (producer wave): chunk c's Q, K, dO slab and Ta blocks into one buffer, as the forward state pass
     //      lays them out (wave load j of a tile covers its bytes [1024 j, 1024 j + 1024); lane L writes 16 bytes at
@@ -74,10 +76,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     constexpr int NLOAD = 2 * SH::NLQ + SH::NLV + SH::NLT - 1;   // Ta quads 6 and 7 are not read
     auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
         const int t = c * C;
-        const int n = (L - t < C) ? (L - t) : C;
-        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (tok0 + t) * DK, ((n - 1) * DK + DK) * 2);
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, ((n - 1) * DK + DK) * 2);
-        const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(d_o + (tok0 + t) * DV + slab_col, ((n - 1) * DV + DVS) * 2);
+        const int n = (len - t < C) ? (len - t) : C;
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + sv.q0 + t * qs, (int)((n - 1) * qs + DK) * 2);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + sv.k0 + t * ks, (int)((n - 1) * ks + DK) * 2);
+        const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(d_o + sv.o0 + t * os + slab_col, (int)((n - 1) * os + DVS) * 2);
         const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(twh + (int64_t)c * (NQ * QE), SH::TBYTES);
         static_for<2 * SH::NLQ + SH::NLV + SH::NLT>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
             } else {
                 const int tr = p / RB;
                 const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
-                const int ld = tile == 2 ? DV : DK;
+                const int ld = (int)(tile == 2 ? os : tile == 1 ? ks : qs);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 0 ? rq : tile == 1 ? rk : ro, dst, 16,
                                                          (tr * ld + 8 * lc) * 2, 0, 0, 0);
             }
@@ -158,19 +160,19 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     const int ta_off = 8 * (16 * (lane & 3) + 4 * g + ((lane >> 2) & 3));
     // byte offsets of this lane's state-gradient and dV elements (row 8 g or 4 g, column colw + r)
     const int ds_lane = (8 * g * DV + colw + r) * 4;
-    const int dv_lane = (4 * g * DV + colw + r) * 2;
+    const int dv_lane = (int)(4 * g * vs + colw + r) * 2;
 
     auto step = [&](int c, const lds_u8* cQ, const lds_u8* cK, const lds_u8* cO, const lds_u8* cT)
                     __attribute__((always_inline)) {
         typedef quad __attribute__((address_space(3))) lds_quad;
         (void)sizeof(lds_quad);
         const int t0 = c * C;
-        const int n = (L - t0 < C) ? (L - t0) : C;
+        const int n = (len - t0 < C) ? (len - t0) : C;
         // the gradient of the state leaving chunk c, for the per-chunk gradients: element i of tile rt is row
         // 32 kp + 8 g + 4 h + i, i.e. the lane's offset plus a wave-uniform one (buffer stores with a scalar offset,
         // so that no per-element address stays live across the chunk loop; every row is inside the chunk's state)
         {
-            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ds_all + ((int64_t)bh * NC + c) * DK * DV, DK * DV * 4);
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ds_all + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 4);
 #pragma unroll
             for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
@@ -266,14 +268,14 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
             // dV = dR: rows 16 (b0 + j) + 4 g + e of the chunk; those past its end fall outside the buffer range (the
             // row is in the per-lane offset, which the range check covers) and are dropped
             {
-                const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(dv + (tok0 + t0) * DV, n * DV * 2);
+                const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(dv + sv.v0 + t0 * vs, (int)((n - 1) * vs + DV) * 2);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const bf16 x0 = (bf16)dR0[e], x1 = (bf16)dR1[e];
                     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x0), rv,
-                                                          dv_lane + (16 * b0 + e) * DV * 2, 0, 0);
+                                                          dv_lane + (16 * b0 + e) * (int)vs * 2, 0, 0);
                     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x1), rv,
-                                                          dv_lane + (16 * b0 + 16 + e) * DV * 2, 0, 0);
+                                                          dv_lane + (16 * b0 + 16 + e) * (int)vs * 2, 0, 0);
                 }
             }
             // dS += Q^T dO - K^T dR over the half; the tiles' chains interleaved
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
 template <int DK, int DVS>
 __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw, const float* __restrict__ s0,
-    float* __restrict__ s_all, int BH, int L, int DV, int nslab) {
+    float* __restrict__ s_all, int BH, int L, int DV, int nslab, TokLayout ly) {
     constexpr int C = 64;
     typedef ChainBf16Shape<DK, C, DVS, 0> SH;
     typedef Mma<bf16> M;
@@ -347,16 +349,18 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
     const int slab_col = slab * DVS;
     const bool producer = w == NW;
     const int colw = slab_col + 16 * (producer ? 0 : w);
-    const int NC = (L + C - 1) / C;
-    const int64_t tok0 = (int64_t)bh * L;
-    const bf16* twh = tw + (int64_t)bh * NC * (NQ * QE);
+    const SeqView sv = seq_view(ly, bh, L, C);   // this sequence's tokens and first chunk
+    const int len = sv.len;
+    const int NC = (len + C - 1) / C;
+    const int64_t ks = ly.k_t, vs = ly.v_t;   // token strides (elements)
+    const bf16* twh = tw + (int64_t)sv.chunk0 * (NQ * QE);
 
     constexpr int NLOAD = SH::NLQ + SH::NLV + SH::NLT - 1;   // Ta quads 6 and 7 are not read
     auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
         const int t = c * C;
-        const int n = (L - t < C) ? (L - t) : C;
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + (tok0 + t) * DK, n * DK * 2);
-        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + (tok0 + t) * DV + slab_col, ((n - 1) * DV + DVS) * 2);
+        const int n = (len - t < C) ? (len - t) : C;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + sv.k0 + t * ks, (int)((n - 1) * ks + DK) * 2);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + sv.v0 + t * vs + slab_col, (int)((n - 1) * vs + DVS) * 2);
         const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(twh + (int64_t)c * (NQ * QE), SH::TBYTES);
         static_for<SH::NLQ + SH::NLV + SH::NLT>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
             } else {
                 const int tr = p / RB;
                 const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
-                const int ld = tile == 2 ? DV : DK;
+                const int ld = (int)(tile == 2 ? vs : ks);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 1 ? rk : rv, dst, 16, (tr * ld + 8 * lc) * 2, 0, 0, 0);
             }
         });
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
     auto step = [&](int c, const lds_u8* cK, const lds_u8* cV, const lds_u8* cT) __attribute__((always_inline)) {
         typedef quad __attribute__((address_space(3))) lds_quad;
         {   // the state entering chunk c
-            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(s_all + ((int64_t)bh * NC + c) * DK * DV, DK * DV * 4);
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(s_all + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 4);
 #pragma unroll
             for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
@@ -513,18 +517,19 @@ bool launch_bwd_chain_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
         const bf16* tw = static_cast<const bf16*>(a.tw);
         const bf16* d_o = static_cast<const bf16*>(a.d_o);
         bf16* dv = static_cast<bf16*>(a.dv);
+        const TokLayout ly = bwd_layout(a);
         switch (dvs) {
             case 16:
                 hipLaunchKernelGGL((bwd_chain_mx_kernel<DK, 16>), dim3((unsigned)grid), dim3(16 / 16 * 64 + 64), 0, s, q,
-                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab);
+                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly);
                 break;
             case 32:
                 hipLaunchKernelGGL((bwd_chain_mx_kernel<DK, 32>), dim3((unsigned)grid), dim3(32 / 16 * 64 + 64), 0, s, q,
-                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab);
+                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly);
                 break;
             default:
                 hipLaunchKernelGGL((bwd_chain_mx_kernel<DK, 64>), dim3((unsigned)grid), dim3(64 / 16 * 64 + 64), 0, s, q,
-                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab);
+                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly);
                 break;
         }
         *err = hipGetLastError();
@@ -548,18 +553,19 @@ bool launch_bwd_states_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
         const bf16* k = static_cast<const bf16*>(a.k);
         const bf16* v = static_cast<const bf16*>(a.v);
         const bf16* tw = static_cast<const bf16*>(a.tw);
+        const TokLayout ly = bwd_layout(a);
         switch (dvs) {
             case 16:
                 hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 16>), dim3((unsigned)grid), dim3(16 / 16 * 64 + 64), 0, s,
-                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab);
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly);
                 break;
             case 32:
                 hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 32>), dim3((unsigned)grid), dim3(32 / 16 * 64 + 64), 0, s,
-                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab);
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly);
                 break;
             default:
                 hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 64>), dim3((unsigned)grid), dim3(64 / 16 * 64 + 64), 0, s,
-                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab);
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly);
                 break;
         }
         *err = hipGetLastError();

@@ -123,7 +123,8 @@ struct TileB {
 };
 
 // LDS of the kernel (byte offsets): bf16 tiles Q, K (C x DK), P and T^T (C x C), the d_v slab tiles S, dS' (DK x NV)
-// and V, dO, Delta, dDelta, G (C x NV); four fp32 C-vectors.
+// and V, dO, Delta, dDelta, G (C x NV); four fp32 C-vectors; the fp32 row sums behind dalpha, one C-vector per
+// 16-column tile column of G o R (NV / 16) and of strict_lower(L) o W2 (C / 16), each element written by one lane.
 template <int DK, int C>
 struct BwdXLds {
     static constexpr int NV = 32;
@@ -140,7 +141,8 @@ struct BwdXLds {
     static constexpr int DD = DL + C * LDV * 2;
     static constexpr int GS = DD + C * LDV * 2;
     static constexpr int AL = GS + C * LDV * 2;
-    static constexpr int BYTES = AL + 4 * C * 4;
+    static constexpr int RS = AL + 4 * C * 4;
+    static constexpr int BYTES = RS + (NV / 16 + C / 16) * C * 4;
 };
 
 }  // namespace bwdx
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ beta,
     const bf16* __restrict__ d_o, const float* __restrict__ s_all, const float* __restrict__ ds_all,
     const bf16* __restrict__ tt, bf16* __restrict__ dq, bf16* __restrict__ dk, float* __restrict__ dbeta, int L, int DV,
-    int gate) {
+    int gate, TokLayout ly) {
     using namespace bwd;
     using namespace bwdx;
     constexpr int NWV = kChunkXThreads / 64;
@@ -176,21 +178,28 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     float* sDb = sAl + C;
     float* sDlam = sDb + C;
     float* sDa = sDlam + C;
+    float* sGR = reinterpret_cast<float*>(smem_x + LY::RS);   // [NV / 16][C]: rowsum(G o R) by tile column
+    float* sLW = sGR + (NV / 16) * C;                         // [C / 16][C]: rowsum(strict_lower(L) o W2) likewise
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int NC = (L + C - 1) / C;
-    const int bh = blockIdx.x / NC, c = blockIdx.x - bh * NC;
-    const int t0 = c * C, n = L - t0 < C ? L - t0 : C;
-    const int64_t tok = (int64_t)bh * L + t0;
-    const float* Sg = s_all + ((int64_t)bh * NC + c) * DK * DV;
-    const float* dSg = ds_all + ((int64_t)bh * NC + c) * DK * DV;
+    int bh, c;
+    SeqView sv;
+    if (!chunk_at(ly, blockIdx.x, L, C, bh, c, sv)) return;
+    (void)bh;
+    const int t0 = c * C, n = sv.len - t0 < C ? sv.len - t0 : C;
+    const int64_t q0 = sv.q0 + (int64_t)t0 * ly.q_t, k0 = sv.k0 + (int64_t)t0 * ly.k_t;   // the chunk's first rows
+    const int64_t v0 = sv.v0 + (int64_t)t0 * ly.v_t, o0 = sv.o0 + (int64_t)t0 * ly.o_t;
+    const int64_t be0 = sv.be0 + (int64_t)t0 * ly.be_t;
+    const int64_t u = blockIdx.x;   // workgroup u works on chunk u of the workspace
+    const float* Sg = s_all + u * DK * DV;
+    const float* dSg = ds_all + u * DK * DV;
 
     {
         TileB<bf16, C, DK, NTH> tq, tk;
         TileB<bf16, C, C, NTH> ttl;
-        tq.load(q + tok * DK, DK, n, tid);
-        tk.load(k + tok * DK, DK, n, tid);
-        ttl.load(tt + ((int64_t)bh * NC + c) * C * C, C, C, tid);
+        tq.load(q + q0, ly.q_t, n, tid);
+        tk.load(k + k0, ly.k_t, n, tid);
+        ttl.load(tt + u * C * C, C, C, tid);
         tq.store(sQ, LDK, tid);
         tk.store(sK, LDK, tid);
         ttl.store(sT, LDC, tid);
@@ -201,11 +210,11 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     auto load_slab = [&](int col0) {
         ts.load(Sg + col0, DV, DK, tid);
         tds.load(dSg + col0, DV, DK, tid);
-        tv.load(v + tok * DV + col0, DV, n, tid);
-        to.load(d_o + tok * DV + col0, DV, n, tid);
+        tv.load(v + v0 + col0, ly.v_t, n, tid);
+        to.load(d_o + o0 + col0, ly.o_t, n, tid);
     };
     load_slab(0);
-    if (tid < C) sDa[tid] = 0.0f;
+    if (tid < (NV / 16) * C) sGR[tid] = 0.0f;
     __syncthreads();
     if (tid < C) {   // gates of the chunk's tokens (rows past the end: zero keys, zero step)
         float lam = 0.0f;
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
             const float x = (float)sK[tid * LDK + e];
             lam = fmaf(x, x, lam);
         }
-        const float b = tid < n ? beta[tok + tid] : 0.0f;
+        const float b = tid < n ? beta[be0 + (int64_t)tid * ly.be_t] : 0.0f;
         sAl[tid] = gate_alpha(b, lam, gate);
         float db, dl;
         gate_alpha_grad(b, lam, gate, &db, &dl);
@@ -267,13 +276,15 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
                 sGs[i * LDV + j] = (bf16)x;
                 sV[i * LDV + j] = (bf16)(-sAl[i] * x);
             });
-            // rows of this lane's elements: the same (tile, i) for a and R, summed over the tile's 16 columns
+            // rows of this lane's elements: the same (tile, i) for a and R, summed over the tile's 16 columns into
+            // the tile column's row sums (a tile belongs to the same wave in every slab: one writer per element, and
+            // a fixed order of the sums, so the gradients do not depend on the waves' timing)
             typedef Acc<C, NV, NWV> AN;
 #pragma unroll
             for (int s = 0; s < AN::TPW; ++s) {
                 const int tt = w + NWV * s;
                 if (AN::ALL || tt < AN::NTT) {
-                    const int ti = tt / AN::TN;
+                    const int ti = tt / AN::TN, tj = tt - ti * AN::TN;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float p = a.t[s][i] * R.t[s][i];
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
                         p += __shfl_xor(p, 2, 16);
                         p += __shfl_xor(p, 4, 16);
                         p += __shfl_xor(p, 8, 16);
-                        if ((lane & 15) == 0) atomicAdd(&sDa[16 * ti + 4 * (lane >> 4) + i], p);
+                        if ((lane & 15) == 0) sGR[tj * C + 16 * ti + 4 * (lane >> 4) + i] += p;
                     }
                 }
             }
@@ -296,8 +307,8 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
         __syncthreads();
     }
 
-    // M o W1 into sP; dL = -strict_lower(D W2) into sT (T is no longer needed); dalpha -= rowsum(strict_lower(L) o W2)
-    // with L = K K^T formed on the wave's tiles of W2
+    // M o W1 into sP; dL = -strict_lower(D W2) into sT (T is no longer needed); the row sums of strict_lower(L) o W2
+    // by tile column, with L = K K^T formed on the wave's tiles of W2
     W1.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = (bf16)(j <= i ? x : 0.0f); });
     W2.each(w, lane, [&](int i, int j, float& x) { sT[i * LDC + j] = (bf16)(j < i ? -sAl[i] * x : 0.0f); });
     {
@@ -318,17 +329,22 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
                     p += __shfl_xor(p, 2, 16);
                     p += __shfl_xor(p, 4, 16);
                     p += __shfl_xor(p, 8, 16);
-                    if ((lane & 15) == 0) atomicAdd(&sDa[row], -p);
+                    if ((lane & 15) == 0) sLW[tj * C + row] = p;
                 }
             }
         }
     }
     __syncthreads();
-    // dbeta; dlambda
+    // dalpha = rowsum(G o R) - rowsum(strict_lower(L) o W2), tile columns summed in order; dbeta; dlambda
     if (tid < C) {
         const int i = tid;
-        const float s = sDa[i];
-        if (i < n) dbeta[tok + i] = s * sDb[i];
+        float gr = 0.0f, lw = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NV / 16; ++j) gr += sGR[j * C + i];
+#pragma unroll
+        for (int j = 0; j < C / 16; ++j) lw += sLW[j * C + i];
+        const float s = gr - lw;
+        if (i < n) dbeta[be0 + (int64_t)i * ly.be_t] = s * sDb[i];
         sDa[i] = s * sDlam[i];
     }
     __syncthreads();
@@ -338,10 +354,10 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     mmx<C, DK, NWV, true, false, C>(aK, sT, LDC, sK, LDK, w, lane);
     mmx<C, DK, NWV, false, false, C>(aK, sT, LDC, sK, LDK, w, lane);
     aQ.each(w, lane, [&](int i, int e, float& x) {
-        if (i < n) dq[(tok + i) * DK + e] = (bf16)x;
+        if (i < n) dq[q0 + (int64_t)i * ly.q_t + e] = (bf16)x;
     });
     aK.each(w, lane, [&](int i, int e, float& x) {
-        if (i < n) dk[(tok + i) * DK + e] = (bf16)fmaf(2.0f * sDa[i], (float)sK[i * LDK + e], x);
+        if (i < n) dk[k0 + (int64_t)i * ly.k_t + e] = (bf16)fmaf(2.0f * sDa[i], (float)sK[i * LDK + e], x);
     });
 }
 
@@ -361,12 +377,11 @@ bool launch_bwd_chunk_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_mx_kernel<DK, C>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
         if (e == hipSuccess) {
-            const int NC = (a.L + C - 1) / C;
-            hipLaunchKernelGGL((bwd_chunk_mx_kernel<DK, C>), dim3((unsigned)((int64_t)a.BH * NC)), dim3(kChunkXThreads),
+            hipLaunchKernelGGL((bwd_chunk_mx_kernel<DK, C>), dim3((unsigned)bwd_chunk_grid(a, C)), dim3(kChunkXThreads),
                                LDS, s, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                                static_cast<const bf16*>(a.v), a.beta, static_cast<const bf16*>(a.d_o), a.s_all,
                                a.ds_all, static_cast<const bf16*>(a.tt), static_cast<bf16*>(a.dq),
-                               static_cast<bf16*>(a.dk), a.dbeta, a.L, a.d_v, a.gate);
+                               static_cast<bf16*>(a.dk), a.dbeta, a.L, a.d_v, a.gate, bwd_layout(a));
             e = hipGetLastError();
         }
         *err = e;

@@ -657,23 +657,23 @@ hipError_t launch_split_e(const SplitArgs& a, bool with_ut, hipStream_t s) {
 
 template <typename E, int DK>
 hipError_t launch_ut_dk(const void* k, const float* beta, void* tw, int BH, int L, int chunk, int gate, hipStream_t s,
-                        void* tt) {
+                        void* tt, const TokLayout* ly) {
     switch (chunk) {
-        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, gate, nullptr, s, false, tt);
-        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, gate, nullptr, s, false, tt);
-        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, gate, nullptr, s, false, tt);
+        case 16: return launch_ut_t<E, DK, 16>(k, beta, tw, BH, L, gate, ly, s, false, tt);
+        case 32: return launch_ut_t<E, DK, 32>(k, beta, tw, BH, L, gate, ly, s, false, tt);
+        case 64: return launch_ut_t<E, DK, 64>(k, beta, tw, BH, L, gate, ly, s, false, tt);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename E>
 hipError_t launch_ut_e(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
-                       hipStream_t s, void* tt = nullptr) {
+                       hipStream_t s, void* tt = nullptr, const TokLayout* ly = nullptr) {
     switch (d_k) {
-        case 16: return launch_ut_dk<E, 16>(k, beta, tw, BH, L, chunk, gate, s, tt);
-        case 32: return launch_ut_dk<E, 32>(k, beta, tw, BH, L, chunk, gate, s, tt);
-        case 64: return launch_ut_dk<E, 64>(k, beta, tw, BH, L, chunk, gate, s, tt);
-        case 128: return launch_ut_dk<E, 128>(k, beta, tw, BH, L, chunk, gate, s, tt);
+        case 16: return launch_ut_dk<E, 16>(k, beta, tw, BH, L, chunk, gate, s, tt, ly);
+        case 32: return launch_ut_dk<E, 32>(k, beta, tw, BH, L, chunk, gate, s, tt, ly);
+        case 64: return launch_ut_dk<E, 64>(k, beta, tw, BH, L, chunk, gate, s, tt, ly);
+        case 128: return launch_ut_dk<E, 128>(k, beta, tw, BH, L, chunk, gate, s, tt, ly);
     }
     return hipErrorInvalidValue;
 }

@@ -195,10 +195,11 @@ hipError_t launch_split_fwd_bf16(const SplitArgs& a, bool with_ut, hipStream_t s
 hipError_t launch_seg_scan(const float* seg_states, const float* s0, float* s_in, int BH, int nseg, int d_k, int d_v,
                            hipStream_t stream);
 
+// layout: null for contiguous [B,H,L,d_k] keys and [B,H,L] betas, else the tensors' strides (and packed sequences)
 hipError_t launch_ut_f32(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
-                         hipStream_t stream);
+                         hipStream_t stream, const TokLayout* layout = nullptr);
 // tt (optional; d_k >= 32): also T^T of every chunk as a row-major chunk x chunk bf16 matrix, for the backward pass
 hipError_t launch_ut_bf16(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
-                          hipStream_t stream, void* tt = nullptr);
+                          hipStream_t stream, void* tt = nullptr, const TokLayout* layout = nullptr);
 
 }  // namespace efla

@@ -7,7 +7,7 @@ hipError_t launch_split_fwd_bf16(const SplitArgs& a, bool with_ut, hipStream_t s
     return launch_split_e<bf16>(a, with_ut, stream);
 }
 hipError_t launch_ut_bf16(const void* k, const float* beta, void* tw, int BH, int L, int d_k, int chunk, int gate,
-                          hipStream_t stream, void* tt) {
-    return launch_ut_e<bf16>(k, beta, tw, BH, L, d_k, chunk, gate, stream, tt);
+                          hipStream_t stream, void* tt, const TokLayout* layout) {
+    return launch_ut_e<bf16>(k, beta, tw, BH, L, d_k, chunk, gate, stream, tt, layout);
 }
 }  // namespace efla

@@ -406,6 +406,43 @@ efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const fl
 efla_status efla_chunk_bwd_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
                                           size_t* bytes);
 
+/*
+ * efla_chunk_bwd_layout -- efla_chunk_bwd over tensors in the layout described by `layout` (NULL: contiguous
+ * [B,H,L,d], exactly efla_chunk_bwd): the gradients of efla_chunk_fwd_layout's operator, for model layers that
+ * hold q, k, v as [B,L,H,d] views, slices of a fused projection or packed sequences ("Error-Free Linear
+ * Attention guida completa" (mauroscia.it), section "Chunkwise parallelism": the method drops into existing
+ * chunked pipelines, whose training runs the backward over the same tensors).
+ *   layout     as efla_chunk_fwd_layout's (same stride rules), with o's strides describing d_o.  dq, dk, dv and
+ *              dbeta are written with the strides of q, k, v and beta (e.g. slices of one fused gradient buffer
+ *              when q, k, v are slices of a fused projection); no two of their rows (elements, for dbeta) may
+ *              share memory, else EFLA_ERR_INVALID_ARG.
+ *   cu_seqlens packed sequences (layout->cu_seqlens, read sanitised as in efla_chunk_fwd_layout): B counts
+ *              sequences, every sequence starts from its own initial state, and initial_state, d_final and
+ *              d_initial hold one [d_k,d_v] state per (sequence, head).  Gradients of tokens outside every
+ *              sequence are not written.
+ *   workspace  at least efla_chunk_bwd_layout_workspace_size(...) bytes, 256-byte aligned, overlapping no other
+ *              argument; with cu_seqlens it begins with the sanitised offsets, made on `stream` by this call.
+ * Arithmetic, launches and errors as efla_chunk_bwd; a layout changes only where the kernels read and write, so
+ * the results equal efla_chunk_bwd's on contiguous copies of the tensors bit for bit, and for packed sequences
+ * those of separate calls, one per sequence (no kernel of the backward accumulates with atomics: the same inputs
+ * give the same bits).  Overlap checks use each tensor's address extent, except that two tensors of the same
+ * element size, sizes and strides may share an extent when their rows provably miss one another, as slices of
+ * one fused buffer do: with the dimensions sorted by stride and those contiguous with the row merged into a block
+ * of m elements, every other stride a multiple of the smallest, s, and the bases' distance d (elements) with
+ * m <= d mod s <= s - m.
+ */
+efla_status efla_chunk_bwd_layout(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
+                                  const float* initial_state, const void* d_o, const float* d_final,
+                                  void* dq, void* dk, void* dv, float* dbeta, float* d_initial,
+                                  int B, int H, int L, int d_k, int d_v, int chunk, int gate,
+                                  const efla_layout* layout, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes efla_chunk_bwd_layout needs for these sizes (host only); varlen != 0 when cu_seqlens will be
+ * given (then the bound H (ceil(L / chunk) + B) on the sequences' chunks sizes it).  Errors as
+ * efla_chunk_bwd_layout would return for the sizes. */
+efla_status efla_chunk_bwd_layout_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                                 int varlen, size_t* bytes);
+
 /* Like efla_chunk_fwd_plan, for the state-pass launch of efla_chunk_fwd_split / efla_chunk_state_pass. */
 efla_status efla_chunk_fwd_split_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype,
                                       int dv_slab, int* workgroups, int* slab_width, int* lds_bytes);

@@ -449,6 +449,103 @@ def test_bwd_reaches_the_device_check(lib):
     assert _bwd_call(lib, s0=P(12), dsf=P(13), gate=3) == NO_DEVICE
 
 
+def test_bwd_layout_workspace_size(lib):
+    # without packed sequences the same bytes as efla_chunk_bwd's; with them the offsets ((B + 1) x 2 int32, then
+    # ceil(L/C) + B int32, 256-byte rounded) first and H (ceil(L/C) + B) chunks in every later part
+    for args in ((8, 16, 4096, 128, 128, 64, torch.bfloat16), (1, 3, 100, 32, 16, 32, torch.float32)):
+        assert efla.chunk_bwd_layout_workspace_size(*args) == efla.chunk_bwd_workspace_size(*args)
+    B, H, L, dk, dv, C = 5, 4, 1000, 128, 64, 64
+    nu = H * (-(-L // C) + B)
+    r = lambda n: -(-n // 256) * 256  # noqa: E731
+    want = r((B + 1) * 8 + (-(-L // C) + B) * 4) + r(nu * 10 * 256 * 2) + 2 * r(nu * dk * dv * 4) + r(nu * C * C * 2)
+    assert efla.chunk_bwd_layout_workspace_size(B, H, L, dk, dv, C, torch.bfloat16, varlen=True) == want
+    n = ctypes.c_size_t()
+    assert lib.efla_chunk_bwd_layout_workspace_size(1, 1, 8, 96, 64, 64, BF16, 1, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.efla_chunk_bwd_layout_workspace_size(1, -1, 8, 64, 64, 64, BF16, 1, ctypes.byref(n)) == INVALID
+    assert lib.efla_chunk_bwd_layout_workspace_size(1, 1, 8, 64, 64, 64, BF16, 1, None) == INVALID
+
+
+def _bwd_layout_call(lib, lay, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), beta=P(4), dt=BF16, s0=None, do=P(5), dsf=None, dq=P(6), dk=P(7), dv=P(8),
+             db=P(9), ds0=P(10), B=2, H=4, L=1000, dk_=64, dv_=64, C=64, gate=0, ws=P(11), wsb=1 << 30)
+    a.update(kw)
+    return lib.efla_chunk_bwd_layout(a["q"], a["k"], a["v"], a["beta"], a["dt"], a["s0"], a["do"], a["dsf"], a["dq"],
+                                     a["dk"], a["dv"], a["db"], a["ds0"], a["B"], a["H"], a["L"], a["dk_"], a["dv_"],
+                                     a["C"], a["gate"], None if lay is None else ctypes.byref(lay), a["ws"], a["wsb"],
+                                     None)
+
+
+def _fused(B, H, L, d):
+    """efla_layout of q, k, v as slices of a [B,L,3,H,d] buffer, beta a slice of [B,L,H,2], d_o [B,L,H,d]."""
+    lay = _bthd(B, H, L, d, d)
+    for f in ("q", "k", "v"):
+        getattr(lay, f)[:] = [L * 3 * H * d, d, 3 * H * d]
+    lay.beta[:] = [L * H * 2, 2, 2 * H]
+    return lay, 0x7F2000000000
+
+
+def _fused_grads(base, step, shift=0):
+    """dq, dk, dv at base + {0, 1, 2} * step (+ shift for dk) bytes; dbeta element 1 of each pair in its buffer."""
+    return dict(dq=ctypes.c_void_p(base), dk=ctypes.c_void_p(base + step + shift), dv=ctypes.c_void_p(base + 2 * step),
+                db=ctypes.c_void_p(0x7F3000000000 + 4))
+
+
+def test_bwd_layout_argument_errors(lib):
+    lay = _bthd(2, 4, 1000, 64, 64)
+    need = efla.chunk_bwd_layout_workspace_size(2, 4, 1000, 64, 64, 64, torch.bfloat16)
+    assert _bwd_layout_call(lib, lay, ws=None) == WORKSPACE
+    assert _bwd_layout_call(lib, lay, wsb=need - 1) == WORKSPACE
+    assert _bwd_layout_call(lib, lay, gate=17) == INVALID
+    assert _bwd_layout_call(lib, lay, dk_=96) == UNSUPPORTED
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.q[2] = 4 * 64 + 4            # rows not 16-byte aligned in bf16
+    assert _bwd_layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.v[2] = 32                    # rows of v, hence of dv, overlap one another
+    assert _bwd_layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.k[:] = [1000 * 4 * 64, 64, 64 * 2]   # heads and tokens of k (and dk) interleave onto the same rows
+    assert _bwd_layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.beta[:] = [1000 * 4, 1, 1]           # dbeta elements shared between heads and tokens
+    assert _bwd_layout_call(lib, bad) == INVALID
+    bad = _bthd(2, 4, 1000, 64, 64)
+    bad.o[2] = 1 << 28               # d_o's token stride beyond the 32-bit in-chunk offsets
+    assert _bwd_layout_call(lib, bad) == INVALID
+    # d_o's rows may overlap (it is only read); a [B,L,H,d] q's extent is 2 * 1000 * 4 * 64 bf16 elements
+    ok = _bthd(2, 4, 1000, 64, 64)
+    ok.o[2] = 0
+    assert _bwd_layout_call(lib, ok, ws=None) == WORKSPACE
+    assert _bwd_layout_call(lib, lay, dq=ctypes.c_void_p(0x7F0100000000 + 4096)) == INVALID   # dq inside q
+    assert _bwd_layout_call(lib, lay, dv=ctypes.c_void_p(0x7F0500000000 + 4096)) == INVALID   # dv inside d_o
+    cu = _bthd(1, 4, 1000, 64, 64)
+    cu.cu_seqlens = 0x7F0600000000 + 64                                                    # offsets inside dq
+    assert _bwd_layout_call(lib, cu, B=3) == INVALID
+    # gradients as slices of one fused [B,L,3,H,d] buffer (H d elements apart) interleave; dk shifted by one row
+    # (d elements) overlaps dq's heads
+    fz, base = _fused(2, 4, 1000, 64)
+    assert _bwd_layout_call(lib, fz, **_fused_grads(base, 4 * 64 * 2), ws=None) == WORKSPACE
+    assert _bwd_layout_call(lib, fz, **_fused_grads(base, 4 * 64 * 2, shift=64 * 2)) == INVALID
+    assert _bwd_layout_call(lib, fz, **_fused_grads(base, 4 * 64 * 2, shift=3)) == INVALID   # not element-aligned
+    assert _bwd_layout_call(lib, lay, B=0, ws=None, wsb=0) == OK
+    assert _bwd_layout_call(lib, lay, L=0, ds0=None, q=None, k=None, v=None, beta=None, do=None, dq=None, dk=None,
+                            dv=None, db=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_bwd_layout_reaches_the_device_check(lib):
+    assert _bwd_layout_call(lib, _bthd(2, 4, 1000, 64, 64)) == NO_DEVICE
+    assert _bwd_layout_call(lib, None) == NO_DEVICE
+    cu = _bthd(1, 4, 1000, 64, 64)
+    cu.cu_seqlens = 0x7F0C00000000
+    assert _bwd_layout_call(lib, cu, B=7, s0=P(12), dsf=P(13), gate=3) == NO_DEVICE
+    fz, base = _fused(2, 4, 1000, 64)
+    assert _bwd_layout_call(lib, fz, **_fused_grads(base, 4 * 64 * 2)) == NO_DEVICE
+    # an empty packed batch still writes d_initial (from d_final)
+    assert _bwd_layout_call(lib, cu, B=7, L=0, q=None, k=None, v=None, beta=None, do=None, dq=None, dk=None, dv=None,
+                            db=None) == NO_DEVICE
+
+
 def _form(lib, B, H, L, dk, dv, C, dt):
     f, ns, nb = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_size_t(7)
     st = lib.efla_chunk_fwd_form(B, H, L, dk, dv, C, dt, ctypes.byref(f), ctypes.byref(ns), ctypes.byref(nb))

@@ -6,7 +6,8 @@ separately by max |x - ref| / max |ref| over the tensor, at the forward's bar: b
 2e-2 for bf16 inputs (the bf16 path also reads the forward's bf16 T diag(alpha) workspace).
 Cases: every d_k path and chunk size, ragged last chunks, with and without the initial state and the
 final-state gradient, stiff keys, the Runge-Kutta gates, and the full LM-layer shape checked on sampled heads
-(heads are independent).  Also the autograd wrapper against direct calls."""
+(heads are independent) and for determinism: a second call gives the same bits (no kernel accumulates with
+atomics, so the sums' order never depends on timing).  Also the autograd wrapper against direct calls."""
 import os
 import sys
 
@@ -81,7 +82,11 @@ def test_bwd_lm_layer_sampled_heads():
     beta = torch.from_numpy(x["beta"]).cuda()
     dsf = torch.from_numpy(g["d_final"]).cuda()
     dq, dk, dv, db, ds0 = efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=64)
+    again = efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=64)
     torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dbeta", "d_initial"), (dq, dk, dv, db, ds0), again):
+        assert torch.equal(a, b), name
+    del again
     for b, h in ((0, 0), (5, 11)):
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = oracle.bwd(x["q"][sl], x["k"][sl], x["v"][sl], x["beta"][sl], None, g["d_o"][sl], g["d_final"][sl])
