@@ -135,6 +135,7 @@ size_t round_up_256(size_t n) { return (n + 255) / 256 * 256; }
 // [S_g(0) | M_g] (fp32, d_k x (d_v + d_k)), then the segments' initial states (fp32, d_k x d_v).
 struct ScanPlan {
     int dvs, nseg, seg_chunks;
+    int dvs1;   // slab width of the first pass (transition columns included)
     size_t off_states, off_sin, total;
 };
 
@@ -163,6 +164,11 @@ efla_status scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dty
     const int64_t sc = NC > 0 ? (NC + G - 1) / G : 1;
     G = NC > 0 ? (NC + sc - 1) / sc : 1;   // no empty segment
     p->dvs = dvs;
+    // the first pass carries d_v + d_k columns without outputs: at d_k = d_v = 128 (bf16, 64-token chunks) one slab
+    // of 128 columns per workgroup (eight compute waves sharing each chunk's K and Ta tiles) while that still gives
+    // every compute unit a workgroup
+    p->dvs1 = dvs;
+    if (dt == EFLA_BF16 && d_k == 128 && d_v == 128 && chunk == 64 && BH * G * 2 >= 256) p->dvs1 = 128;
     p->nseg = (int)G;
     p->seg_chunks = (int)sc;
     const size_t ut = round_up_256(ut_bytes(BH, L, chunk, dt));
@@ -193,6 +199,7 @@ hipError_t run_fwd(bool bf, const efla::SplitArgs& a, const ScanPlan& p, char* w
     a1.seg_chunks = p.seg_chunks;
     a1.aug = 1;
     a1.sf_all = 1;
+    a1.dvs = p.dvs1;
     hipError_t e = chain(a1, true);
     if (e == hipSuccess) e = efla::launch_seg_scan(states, a.s0, s_in, a.BH, p.nseg, a.d_k, a.d_v, s);
     efla::SplitArgs a2 = a;
@@ -462,7 +469,7 @@ efla_status layout_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_d
         if (L < 0) return EFLA_ERR_INVALID_ARG;
         const int64_t n_ut = (int64_t)H * ((L + chunk - 1) / chunk + B);
         if (n_ut > INT32_MAX || (int64_t)B + 1 > INT32_MAX / 8) return EFLA_ERR_INVALID_ARG;
-        lp->sp.dvs = dvs;
+        lp->sp.dvs = lp->sp.dvs1 = dvs;
         lp->sp.nseg = 1;
         lp->sp.seg_chunks = 0;
         lp->off_ut = round_up_256((size_t)(B + 1) * 8 + (size_t)((L + chunk - 1) / chunk + B) * 4);

@@ -104,7 +104,8 @@ __device__ __forceinline__ int sw_qk(int t) {
 }
 template <int DVS>
 __device__ __forceinline__ int sw_v(int t) {
-    if constexpr (DVS == 64) return 2 * ((t >> 1) & 1);
+    if constexpr (DVS == 128) return 2 * (t & 7);   // 256-byte rows: 8 rows' chunk pairs on distinct banks
+    else if constexpr (DVS == 64) return 2 * ((t >> 1) & 1);
     else return 0;
 }
 
@@ -878,6 +879,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
 
 template <int DK, int C, int DVS>
 hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
+    if constexpr (DVS == 128) {
+        // the 128-column slab (eight compute waves) is built for the pass without outputs only
+        if (a.o != nullptr) return hipErrorInvalidValue;
+    }
     const ChainSeg sg = chain_seg(a, DK, C, DVS);
     const TokLayout ly = a.layout ? *a.layout : contiguous_layout(1, a.L, DK, a.d_v);
     const int nslab = (a.d_v + (a.aug ? DK : 0)) / DVS;
@@ -888,7 +893,7 @@ hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
                            sg, ly, nullptr, 0);
-    else
+    else if constexpr (DVS != 128)
         hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, true>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,

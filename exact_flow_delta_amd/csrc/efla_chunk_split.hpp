@@ -629,6 +629,10 @@ hipError_t launch_split_c(const SplitArgs& a, bool with_ut, hipStream_t s) {
         case 16: return launch_chain_t<E, DK, C, 16>(a, s);
         case 32: return launch_chain_t<E, DK, C, 32>(a, s);
         case 64: return launch_chain_t<E, DK, C, 64>(a, s);
+        case 128:
+            // the first pass of the segment-parallel forward at d_k 128 (bf16, 64-token chunks, no outputs)
+            if constexpr (std::is_same<E, bf16>::value && DK == 128 && C == 64) return launch_chain_t<E, DK, C, 128>(a, s);
+            break;
     }
     return hipErrorInvalidValue;
 }

@@ -5,7 +5,7 @@ S_out = M S_in + S_out(0)), so its outputs and final state must match the token 
 tolerance as the other forms: max |x - ref| / max |ref| per tensor below 1e-5 (fp32 inputs) or 2e-2 (bf16
 inputs).  Cases cover segment counts that leave a short last segment, a ragged last chunk, initial states,
 in-place state passing, every d_k path (the swizzled bf16 state pass for d_k >= 32, the generic one for fp32
-and d_k = 16) and a Runge-Kutta gate.  The full-size long-context workload runs in test_gpu_parity.py."""
+and d_k = 16), the 128-column first pass of d_k = d_v = 128, and a Runge-Kutta gate.  The full-size long-context workload runs in test_gpu_parity.py."""
 import os
 import sys
 
@@ -79,6 +79,16 @@ def test_scan_lm_heads_with_gate():
     o, S, nseg = _scan(x, "bf16", 64, 6, gate=3)
     assert nseg == 6
     _check(x, "bf16", o, S, gate=3)
+
+
+def test_scan_wide_first_pass():
+    # 16 heads x 8 segments of 3 chunks (the last chunk ragged): at d_k = d_v = 128 the first pass then takes
+    # 128-column slabs (eight compute waves sharing each chunk's K and Ta), the second 64-column ones
+    w = W.workload(4, H=16, L=24 * 64 - 27)
+    x = W.make_fwd_inputs(w)
+    o, S, nseg = _scan(x, "bf16", 64, 8)
+    assert nseg == 8
+    _check(x, "bf16", o, S)
 
 
 def test_scan_automatic_segments_long_heads():
