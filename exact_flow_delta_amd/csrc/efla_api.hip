@@ -696,13 +696,15 @@ namespace {
 
 // Workspace of efla_chunk_bwd_layout: with packed sequences first the sanitised token offsets, the chunk offsets
 // (B + 1 int32 each) and the chunk -> sequence table (ceil(L / C) + B int32); then the UT output (Ta), the state
-// entering and the gradient of the state leaving every chunk (fp32, d_k x d_v each), then -- where the per-chunk
+// entering and the gradient of the state leaving every chunk (d_k x d_v each), then -- where the per-chunk
 // gradients run on bf16 matrix cores (bf16, d_k >= 32, chunk 32 or 64, d_v a multiple of 32) -- T^T of every chunk
-// (bf16, chunk x chunk); each part 256-byte aligned.  Chunks: B H ceil(L / C), or with packed sequences
-// H (ceil(L / C) + B), which bounds H sum_b ceil(len_b / C) for disjoint sequences.
+// (bf16, chunk x chunk); each part 256-byte aligned.  The per-chunk states are bf16 where all three passes run on
+// the matrix cores (those sizes with 64-token chunks: the per-chunk kernel takes them as bf16 operands), else
+// fp32.  Chunks: B H ceil(L / C), or with packed sequences H (ceil(L / C) + B), which bounds H sum_b
+// ceil(len_b / C) for disjoint sequences.
 struct BwdPlan {
     size_t off_ut, off_s, off_ds, off_tt, total;
-    bool tt;
+    bool tt, sbf;
 };
 
 efla_status bwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dt, bool varlen, BwdPlan* p) {
@@ -713,12 +715,13 @@ efla_status bwd_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtyp
     const int64_t NU = varlen ? (int64_t)H * (NC + B) : BH * NC;
     if (BH > INT32_MAX || NU > INT32_MAX || BH * (d_v / 16) > INT32_MAX) return EFLA_ERR_INVALID_ARG;
     if (varlen && (int64_t)B + 1 > INT32_MAX / 8) return EFLA_ERR_INVALID_ARG;
-    const size_t states = round_up_256((size_t)NU * d_k * d_v * 4);
+    p->tt = dt == EFLA_BF16 && d_k >= 32 && chunk >= 32 && d_v % 32 == 0;
+    p->sbf = p->tt && chunk == 64;
+    const size_t states = round_up_256((size_t)NU * d_k * d_v * (p->sbf ? 2 : 4));
     p->off_ut = varlen ? round_up_256((size_t)(B + 1) * 8 + (size_t)(NC + B) * 4) : 0;
     p->off_s = p->off_ut + round_up_256((size_t)NU * (size_t)efla::ut_block_elems(chunk) * esize(dt));
     p->off_ds = p->off_s + states;
     p->off_tt = p->off_ds + states;
-    p->tt = dt == EFLA_BF16 && d_k >= 32 && chunk >= 32 && d_v % 32 == 0;
     p->total = p->off_tt + (p->tt ? round_up_256((size_t)NU * chunk * chunk * 2) : 0);
     return EFLA_OK;
 }
@@ -824,8 +827,7 @@ efla_status efla_chunk_bwd_layout(const void* q, const void* k, const void* v, c
         e = bf ? efla::launch_ut_bf16(k, beta, tw, (int)BH, L, d_k, chunk, gate, s, tt, lyp)
                : efla::launch_ut_f32(k, beta, tw, (int)BH, L, d_k, chunk, gate, s, lyp);
     efla::BwdArgs a{q, k, v, beta, initial_state, d_o, d_final, dq, dk, dv, dbeta, d_initial, (int)BH, L, d_k, d_v,
-                    chunk, gate, tw, reinterpret_cast<float*>(ws + p.off_s), reinterpret_cast<float*>(ws + p.off_ds),
-                    tt, lyp};
+                    chunk, gate, tw, ws + p.off_s, ws + p.off_ds, tt, lyp, p.sbf};
     if (e == hipSuccess) e = bf ? efla::launch_bwd_bf16(a, s) : efla::launch_bwd_f32(a, s);
     return e == hipSuccess ? EFLA_OK : fail_hip(e, "efla_chunk_bwd launch");
 }

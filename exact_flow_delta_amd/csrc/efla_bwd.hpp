@@ -571,13 +571,17 @@ struct BwdArgs {
     float* d_initial;
     int BH, L, d_k, d_v, chunk, gate;
     void* tw;        // UT output (Ta), already written
-    float* s_all;    // BH x NC x d_k x d_v
-    float* ds_all;   // BH x NC x d_k x d_v
+    void* s_all;     // BH x NC x d_k x d_v: fp32, or bf16 when sbf
+    void* ds_all;    // BH x NC x d_k x d_v: fp32, or bf16 when sbf
     void* tt;        // T^T of every chunk (BH x NC x chunk x chunk, storage type), or null
     // null: contiguous [B,H,L,d] tensors; else the strides of q, k, v, d_o (in o's place) and beta -- the
     // gradients dq, dk, dv, dbeta take those of their input -- and packed sequences (then the UT workspace,
     // s_all, ds_all and tt hold the chunks of the sequences in the layout's order)
     const TokLayout* layout = nullptr;
+    // the per-chunk states in bf16: only where all three kernels after the UT launch run on bf16 matrix cores
+    // (bf16, d_k >= 32, 64-token chunks, d_v a multiple of 32), whose per-chunk kernel rounds them to bf16 operands
+    // anyway -- the same values, half the workspace and its traffic
+    bool sbf = false;
 };
 
 // contiguous [B,H,L,d] tensors: every (batch, head) a sequence of L tokens
@@ -614,6 +618,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     const E* d_o = static_cast<const E*>(a.d_o);
     const E* tw = static_cast<const E*>(a.tw);
     const TokLayout ly = bwd_layout(a);
+    // bf16 states are planned only where the matrix-core kernels run all three passes; check the pairing
+    const bool fast_states = std::is_same<E, bf16>::value && DK >= 32 && C == 64;
+    const bool fast_chunk = std::is_same<E, bf16>::value && DK >= 32 && C >= 32 && a.d_v % 32 == 0 && a.tt;
+    if (a.sbf && !(fast_states && fast_chunk)) return hipErrorInvalidValue;
     if (a.L > 0) {
         hipError_t es = hipSuccess;
         if (BwdStatesFast<E, DK, C>::launch(a, s, &es)) {
@@ -621,11 +629,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
         } else if (a.d_v >= 32) {
             const int nslab = a.d_v / 32;
             hipLaunchKernelGGL((bwd_states_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(bwd::NT), 0, s, k,
-                               v, tw, a.s0, a.s_all, a.L, a.d_v, nslab, ly);
+                               v, tw, a.s0, static_cast<float*>(a.s_all), a.L, a.d_v, nslab, ly);
         } else {
             const int nslab = a.d_v / 16;
             hipLaunchKernelGGL((bwd_states_kernel<E, DK, C, 16>), dim3((unsigned)(a.BH * nslab)), dim3(bwd::NT), 0, s, k,
-                               v, tw, a.s0, a.s_all, a.L, a.d_v, nslab, ly);
+                               v, tw, a.s0, static_cast<float*>(a.s_all), a.L, a.d_v, nslab, ly);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -636,11 +644,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     } else if (a.d_v >= 32) {
         const int nslab = a.d_v / 32;
         hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 32>), dim3((unsigned)(a.BH * nslab)), dim3(kChainThreads), 0, s, q, k,
-                           tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab, ly);
+                           tw, d_o, a.d_final, static_cast<float*>(a.ds_all), static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab,
+                           ly);
     } else {
         const int nslab = a.d_v / 16;
         hipLaunchKernelGGL((bwd_chain_kernel<E, DK, C, 16>), dim3((unsigned)(a.BH * nslab)), dim3(kChainThreads), 0, s, q, k,
-                           tw, d_o, a.d_final, a.ds_all, static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab, ly);
+                           tw, d_o, a.d_final, static_cast<float*>(a.ds_all), static_cast<E*>(a.dv), a.d_initial, a.L, a.d_v, nslab,
+                           ly);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.L == 0) return e;
@@ -651,7 +661,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, C>), dim3((unsigned)bwd_chunk_grid(a, C)), dim3(kChunkThreads), LDS, s, q,
-                       k, v, a.beta, d_o, a.s_all, a.ds_all, static_cast<E*>(a.dq), static_cast<E*>(a.dk), a.dbeta,
+                       k, v, a.beta, d_o, static_cast<const float*>(a.s_all), static_cast<const float*>(a.ds_all),
+                       static_cast<E*>(a.dq), static_cast<E*>(a.dk), a.dbeta,
                        a.L, a.d_v, a.gate, ly);
     return hipGetLastError();
 }

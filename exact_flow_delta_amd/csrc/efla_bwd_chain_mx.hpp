@@ -28,8 +28,8 @@ namespace efla {
 template <int DK, int DVS>
 __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ tw, const bf16* __restrict__ d_o,
-    const float* __restrict__ d_final, float* __restrict__ ds_all, bf16* __restrict__ dv, float* __restrict__ d_initial,
-    int BH, int L, int DV, int nslab, TokLayout ly) {
+    const float* __restrict__ d_final, void* __restrict__ ds_all, bf16* __restrict__ dv, float* __restrict__ d_initial,
+    int BH, int L, int DV, int nslab, TokLayout ly, int sbf) {
     constexpr int C = 64;
     typedef ChainBf16Shape<DK, C, DVS, 0> SH;
     typedef Mma<bf16> M;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     // Ta^T from the stored operand layout: lane 4 e + c of group g reads stored lane 16 c + 4 g + e of the block
     const int ta_off = 8 * (16 * (lane & 3) + 4 * g + ((lane >> 2) & 3));
     // byte offsets of this lane's state-gradient and dV elements (row 8 g or 4 g, column colw + r)
-    const int ds_lane = (8 * g * DV + colw + r) * 4;
+    const int ds_lane = (8 * g * DV + colw + r) * (sbf ? 2 : 4);
     const int dv_lane = (int)(4 * g * vs + colw + r) * 2;
 
     auto step = [&](int c, const lds_u8* cQ, const lds_u8* cK, const lds_u8* cO, const lds_u8* cT)
@@ -171,8 +171,21 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
         // the gradient of the state leaving chunk c, for the per-chunk gradients: element i of tile rt is row
         // 32 kp + 8 g + 4 h + i, i.e. the lane's offset plus a wave-uniform one (buffer stores with a scalar offset,
         // so that no per-element address stays live across the chunk loop; every row is inside the chunk's state)
-        {
-            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ds_all + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 4);
+        if (sbf) {   // rounded to bf16 as the per-chunk kernel rounds its operands
+            const __amdgpu_buffer_rsrc_t rs =
+                buffer_rsrc(static_cast<bf16*>(ds_all) + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 2);
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16 x = (bf16)dS[rt][i];
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), rs, ds_lane,
+                                                          (32 * (rt >> 1) + 4 * (rt & 1) + i) * DV * 2, 0);
+                }
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t rs =
+                buffer_rsrc(static_cast<float*>(ds_all) + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 4);
 #pragma unroll
             for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
@@ -307,13 +320,13 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     }
 }
 
-// The state entering every chunk, s_all[bh][c] (fp32, d_k x d_v), for the per-chunk gradients: the forward state
+// The state entering every chunk, s_all[bh][c] (d_k x d_v; bf16 when sbf, else fp32), for the per-chunk gradients: the forward state
 // pass again without outputs (per 32-token half: R = V - K S, Delta = Ta R, S <- S + K^T Delta), organised as
 // bwd_chain_mx_kernel but in chunk order, with only K, the V slab and Ta loaded.
 template <int DK, int DVS>
 __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw, const float* __restrict__ s0,
-    float* __restrict__ s_all, int BH, int L, int DV, int nslab, TokLayout ly) {
+    void* __restrict__ s_all, int BH, int L, int DV, int nslab, TokLayout ly, int sbf) {
     constexpr int C = 64;
     typedef ChainBf16Shape<DK, C, DVS, 0> SH;
     typedef Mma<bf16> M;
@@ -430,12 +443,25 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
     const int tc = lane & 3;
     const int swt = sw_qk<DK>(te);
     const int v_off = te * SH::RBV + 16 * (((2 * w + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
-    const int s_lane = (8 * g * DV + colw + r) * 4;
+    const int s_lane = (8 * g * DV + colw + r) * (sbf ? 2 : 4);
 
     auto step = [&](int c, const lds_u8* cK, const lds_u8* cV, const lds_u8* cT) __attribute__((always_inline)) {
         typedef quad __attribute__((address_space(3))) lds_quad;
-        {   // the state entering chunk c
-            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(s_all + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 4);
+        if (sbf) {   // the state entering chunk c, rounded to bf16 as the per-chunk kernel rounds its operands
+            const __amdgpu_buffer_rsrc_t rs =
+                buffer_rsrc(static_cast<bf16*>(s_all) + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 2);
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16 x = (bf16)S[rt][i];
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), rs, s_lane,
+                                                          (32 * (rt >> 1) + 4 * (rt & 1) + i) * DV * 2, 0);
+                }
+            }
+        } else {   // the state entering chunk c
+            const __amdgpu_buffer_rsrc_t rs =
+                buffer_rsrc(static_cast<float*>(s_all) + ((int64_t)sv.chunk0 + c) * DK * DV, DK * DV * 4);
 #pragma unroll
             for (int rt = 0; rt < NKD; ++rt) {
 #pragma unroll
@@ -521,15 +547,18 @@ bool launch_bwd_chain_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
         switch (dvs) {
             case 16:
                 hipLaunchKernelGGL((bwd_chain_mx_kernel<DK, 16>), dim3((unsigned)grid), dim3(16 / 16 * 64 + 64), 0, s, q,
-                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly);
+                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly,
+                                   (int)a.sbf);
                 break;
             case 32:
                 hipLaunchKernelGGL((bwd_chain_mx_kernel<DK, 32>), dim3((unsigned)grid), dim3(32 / 16 * 64 + 64), 0, s, q,
-                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly);
+                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly,
+                                   (int)a.sbf);
                 break;
             default:
                 hipLaunchKernelGGL((bwd_chain_mx_kernel<DK, 64>), dim3((unsigned)grid), dim3(64 / 16 * 64 + 64), 0, s, q,
-                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly);
+                                   k, tw, d_o, a.d_final, a.ds_all, dv, a.d_initial, a.BH, a.L, a.d_v, nslab, ly,
+                                   (int)a.sbf);
                 break;
         }
         *err = hipGetLastError();
@@ -557,15 +586,18 @@ bool launch_bwd_states_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
         switch (dvs) {
             case 16:
                 hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 16>), dim3((unsigned)grid), dim3(16 / 16 * 64 + 64), 0, s,
-                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly);
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly,
+                                   (int)a.sbf);
                 break;
             case 32:
                 hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 32>), dim3((unsigned)grid), dim3(32 / 16 * 64 + 64), 0, s,
-                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly);
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly,
+                                   (int)a.sbf);
                 break;
             default:
                 hipLaunchKernelGGL((bwd_states_mx_kernel<DK, 64>), dim3((unsigned)grid), dim3(64 / 16 * 64 + 64), 0, s,
-                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly);
+                                   k, v, tw, a.s0, a.s_all, a.BH, a.L, a.d_v, nslab, ly,
+                                   (int)a.sbf);
                 break;
         }
         *err = hipGetLastError();

@@ -152,7 +152,7 @@ constexpr int kChunkXThreads = 512;   // eight waves
 template <int DK, int C>
 __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ beta,
-    const bf16* __restrict__ d_o, const float* __restrict__ s_all, const float* __restrict__ ds_all,
+    const bf16* __restrict__ d_o, const void* __restrict__ s_all, const void* __restrict__ ds_all,
     const bf16* __restrict__ tt, bf16* __restrict__ dq, bf16* __restrict__ dk, float* __restrict__ dbeta, int L, int DV,
     int gate, TokLayout ly) {
     using namespace bwd;
@@ -191,8 +191,11 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     const int64_t v0 = sv.v0 + (int64_t)t0 * ly.v_t, o0 = sv.o0 + (int64_t)t0 * ly.o_t;
     const int64_t be0 = sv.be0 + (int64_t)t0 * ly.be_t;
     const int64_t u = blockIdx.x;   // workgroup u works on chunk u of the workspace
-    const float* Sg = s_all + u * DK * DV;
-    const float* dSg = ds_all + u * DK * DV;
+    // the chunk's entering state and leaving state gradient: bf16 with 64-token chunks (the state passes on
+    // matrix cores store them rounded as this kernel would), else fp32
+    typedef typename std::conditional<C == 64, bf16, float>::type SE;
+    const SE* Sg = static_cast<const SE*>(s_all) + u * DK * DV;
+    const SE* dSg = static_cast<const SE*>(ds_all) + u * DK * DV;
 
     {
         TileB<bf16, C, DK, NTH> tq, tk;
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
         ttl.store(sT, LDC, tid);
     }
     // the d_v slabs' tiles, loaded one slab ahead
-    TileB<float, DK, NV, NTH> ts, tds;
+    TileB<SE, DK, NV, NTH> ts, tds;
     TileB<bf16, C, NV, NTH> tv, to;
     auto load_slab = [&](int col0) {
         ts.load(Sg + col0, DV, DK, tid);
@@ -372,6 +375,10 @@ bool launch_bwd_chunk_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
         return false;
     } else {
         if (a.d_v % 32 != 0 || a.tt == nullptr) return false;
+        if ((C == 64) != a.sbf) {   // the kernel reads bf16 states exactly with 64-token chunks
+            *err = hipErrorInvalidValue;
+            return true;
+        }
         constexpr int LDS = bwdx::BwdXLds<DK, C>::BYTES;
         static_assert(LDS <= kMaxLdsBytes, "matrix-core chunk kernel LDS too large");
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_mx_kernel<DK, C>),

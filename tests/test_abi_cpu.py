@@ -403,10 +403,15 @@ def test_layout_reaches_the_device_check(lib):
 
 
 def test_bwd_workspace_size(lib):
-    # UT output, then two fp32 blocks of B H ceil(L/C) d_k d_v (each 256-byte rounded), then (bf16 with d_k >= 32,
-    # chunk >= 32, d_v a multiple of 32: the matrix-core per-chunk kernel) T^T of every chunk in bf16
+    # UT output, then two blocks of B H ceil(L/C) d_k d_v states (each 256-byte rounded), then (bf16 with d_k >= 32,
+    # chunk >= 32, d_v a multiple of 32: the matrix-core per-chunk kernel) T^T of every chunk in bf16; the states
+    # are bf16 when all three passes run on the matrix cores (those sizes with 64-token chunks), else fp32
     nb = efla.chunk_bwd_workspace_size(8, 16, 4096, 128, 128, 64, torch.bfloat16)
-    assert nb == 41943040 + 2 * 128 * 64 * 128 * 128 * 4 + 128 * 64 * 64 * 64 * 2
+    assert nb == 41943040 + 2 * 128 * 64 * 128 * 128 * 2 + 128 * 64 * 64 * 64 * 2
+    nb = efla.chunk_bwd_workspace_size(8, 16, 4096, 128, 128, 32, torch.bfloat16)
+    assert nb == 128 * 128 * 3 * 256 * 2 + 2 * 128 * 128 * 128 * 128 * 4 + 128 * 128 * 32 * 32 * 2
+    nb = efla.chunk_bwd_workspace_size(1, 2, 64, 128, 16, 64, torch.bfloat16)   # d_v 16: generic per-chunk kernel
+    assert nb == 2 * 10 * 256 * 2 + 2 * 256 * (-(-(2 * 128 * 16 * 4) // 256))
     nb = efla.chunk_bwd_workspace_size(1, 3, 100, 32, 16, 32, torch.float32)
     ut = 3 * 4 * 3 * 256 * 4
     st = -(-(3 * 4 * 32 * 16 * 4) // 256) * 256
@@ -457,7 +462,7 @@ def test_bwd_layout_workspace_size(lib):
     B, H, L, dk, dv, C = 5, 4, 1000, 128, 64, 64
     nu = H * (-(-L // C) + B)
     r = lambda n: -(-n // 256) * 256  # noqa: E731
-    want = r((B + 1) * 8 + (-(-L // C) + B) * 4) + r(nu * 10 * 256 * 2) + 2 * r(nu * dk * dv * 4) + r(nu * C * C * 2)
+    want = r((B + 1) * 8 + (-(-L // C) + B) * 4) + r(nu * 10 * 256 * 2) + 2 * r(nu * dk * dv * 2) + r(nu * C * C * 2)
     assert efla.chunk_bwd_layout_workspace_size(B, H, L, dk, dv, C, torch.bfloat16, varlen=True) == want
     n = ctypes.c_size_t()
     assert lib.efla_chunk_bwd_layout_workspace_size(1, 1, 8, 96, 64, 64, BF16, 1, ctypes.byref(n)) == UNSUPPORTED
