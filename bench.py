@@ -193,9 +193,11 @@ def record_mfma(run_dir):
         rows = list(csv.DictReader(f))
     counters = ("SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
     out = {"note": "Matrix-core counters per launch from one rocprofv3 --pmc run (mean over the kernel's dispatches); "
-                   "executed flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / "
-                   "(GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs); valid only while the kernel sources hash to "
-                   "'sources_sha256_16'. Written by bench.py --record-mfma."}
+                   "executed flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; SQ_VALU_MFMA_BUSY_CYCLES is summed over the "
+                   "1,024 SIMDs, and bench.py divides it by 1,024 x the average launch time it measures x 2.4 GHz "
+                   "(GRBM_GUI_ACTIVE is inflated by the counter run's serialised dispatches and is kept for reference "
+                   "only); valid only while the kernel sources hash to 'sources_sha256_16'. Written by "
+                   "bench.py --record-mfma."}
     for name, info in TRAFFIC_KERNELS.items():
         per = {}
         for row in rows:
@@ -207,8 +209,7 @@ def record_mfma(run_dir):
         mean = {c: statistics.mean(d.get(c, 0.0) for d in per.values()) for c in counters}
         out[name] = {"sources": info["sources"], "sources_sha256_16": _sources_hash(info["sources"]),
                      "dispatches": len(per), **mean,
-                     "executed_flops": mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
-                     "busy_frac": mean["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, mean["GRBM_GUI_ACTIVE"] * 256 * 4)}
+                     "executed_flops": mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0}
     path = os.path.join(ROOT, "profiles", "mfma_counters.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -242,7 +243,8 @@ def measured_traffic(kernel):
 def mfma_block(flops, tflops, launch_ms, kernel):
     """The matrix-core figures of the headline kernel: the algorithmic flops of a step against the dense bf16 peak,
     and -- from the committed rocprofv3 counters, while they match the kernel's sources -- the flops the matrix
-    cores executed per launch over the average launch time measured here, and their busy-cycle fraction."""
+    cores executed per launch over the average launch time measured here, and the matrix cores' busy cycles (summed
+    over the 1,024 SIMDs) over that time at the 2.4 GHz peak clock."""
     m = {"algorithmic_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
          "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops}
     c = measured_mfma(kernel)
@@ -250,8 +252,9 @@ def mfma_block(flops, tflops, launch_ms, kernel):
         m.update(executed_flops_per_launch=None, executed_frac=None, busy_frac=None)
     else:
         ex = c["executed_flops"] / (launch_ms * 1e-3) / 1e12
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * launch_ms * 1e-3 * 2.4e9)
         m.update(executed_flops_per_launch=c["executed_flops"], executed_tflops=round(ex, 2),
-                 executed_frac=round(ex / BF16_PEAK_TFLOPS, 4), busy_frac=round(c["busy_frac"], 4),
+                 executed_frac=round(ex / BF16_PEAK_TFLOPS, 4), busy_frac=round(busy, 4),
                  counters="profiles/mfma_counters.json")
     return m
 
