@@ -321,8 +321,8 @@ efla_status efla_chunk_fwd_scan(const void* q, const void* k, const void* v, con
 /* Launch shape and workspace of efla_chunk_fwd_scan for these sizes (host only): segments used, chunks per
  * segment, state slab width and workspace bytes.  Errors as efla_chunk_fwd_scan would return for the sizes.
  * With segments = 0 the library cuts sequences only when one segment's state pass would run at most 64
- * workgroups (a quarter of the compute units), then doubles the count while the second pass stays within 256
- * workgroups and every segment keeps at least 32 chunks; otherwise one segment. */
+ * workgroups (a quarter of the compute units): the count G starts at 1 and doubles while 2G segments' second
+ * pass stays within 256 workgroups and the sequence holds at least 32 G chunks; otherwise one segment. */
 efla_status efla_chunk_scan_plan(int B, int H, int L, int d_k, int d_v, int chunk, efla_dtype dtype, int segments,
                                  int* nseg, int* seg_chunks, int* slab_width, size_t* workspace_bytes);
 
@@ -389,12 +389,18 @@ efla_status efla_chunk_layout_plan(int B, int H, int L, int d_k, int d_v, int ch
  *   dq, dk         [B,H,L,d_k] dtype, written;  dv [B,H,L,d_v] dtype, written;  dbeta [B,H,L] fp32, written
  *   d_initial      [B,H,d_k,d_v] fp32, written, or NULL (not written)
  *   workspace      device memory of at least efla_chunk_bwd_workspace_size(...) bytes, 256-byte aligned:
- *                  the chunks' T diag(alpha), and the state entering and the state gradient leaving every
- *                  chunk in fp32 (2 B H ceil(L/chunk) d_k d_v floats: 1.07 GB for B8 H16 L4096 d128)
+ *                  the chunks' T diag(alpha), the state entering and the state gradient leaving every chunk
+ *                  (2 B H ceil(L/chunk) d_k d_v elements: bf16 where all three passes below run on bf16 matrix
+ *                  cores -- bf16, d_k >= 32, 64-token chunks, d_v a multiple of 32 -- else fp32; 0.54 GB of the
+ *                  0.65 GB for B8 H16 L4096 d128), and for bf16 with d_k >= 32, chunks of 32 or 64 and d_v a
+ *                  multiple of 32 each chunk's T^T (bf16)
  * Outputs must not overlap one another, any input or the workspace (EFLA_ERR_INVALID_ARG).  Launches, all on
  * `stream`: the UT transform, the state pass again (keeping every chunk's entering state), the state
  * gradient backwards over the chunks (dv, d_initial), and one launch over all (head, chunk) pairs (dq, dk,
- * dbeta).  Arithmetic is fp32; bf16 inputs are widened.  Sizes as efla_chunk_fwd.
+ * dbeta).  Arithmetic: bf16 inputs with d_k >= 32 take every product on bf16 matrix cores with fp32
+ * accumulation (operands, the per-chunk states included, rounded to bf16) where the sizes above allow, fp32
+ * matrix cores otherwise; fp32 inputs are fp32 throughout.  No kernel accumulates with atomics: the same
+ * inputs give the same bits.  Sizes as efla_chunk_fwd.
  */
 efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const float* beta, efla_dtype dtype,
                            const float* initial_state, const void* d_o, const float* d_final,
