@@ -523,32 +523,58 @@ def chunk_bwd_layout(q, k, v, beta, d_o, cu_seqlens=None, initial_state=None, d_
     return dq, dk, dv, dbeta, d_init
 
 
+def _dense(t: torch.Tensor, feature_contiguous: bool) -> torch.Tensor:
+    """t itself when its elements tile a block of memory without gaps or overlaps (a contiguous tensor, or a
+    permutation of one such as the [B,H,L,d] view of a [B,L,H,d] tensor) and, for q, k, v, d_o, its feature
+    dimension is contiguous; else a contiguous copy.  Gradients are then allocated with the same strides."""
+    dims = sorted((d for d in range(t.dim()) if t.shape[d] > 1), key=lambda d: t.stride(d))
+    expect = 1
+    dense = True
+    for d in dims:
+        if t.stride(d) != expect:
+            dense = False
+            break
+        expect *= t.shape[d]
+    if feature_contiguous and t.shape[-1] > 1 and t.stride(-1) != 1:
+        dense = False
+    return t if dense else t.contiguous()
+
+
 class _EflaFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, beta, initial_state, chunk_size, gate):
-        q, k, v, beta = (x.contiguous() for x in (q, k, v, beta))
+    def forward(ctx, q, k, v, beta, initial_state, cu_seqlens, chunk_size, gate):
+        q, k, v = (_dense(x, True) for x in (q, k, v))
+        beta = _dense(beta, False)
         s0 = None if initial_state is None else initial_state.contiguous()
-        o, sf = chunk_fwd(q, k, v, beta, initial_state=s0, chunk_size=chunk_size, gate=gate)
-        ctx.save_for_backward(q, k, v, beta, s0 if s0 is not None else torch.empty(0, device=v.device))
-        ctx.has_s0 = s0 is not None
+        o, sf = chunk_fwd_layout(q, k, v, beta, cu_seqlens=cu_seqlens, initial_state=s0, chunk_size=chunk_size,
+                                 gate=gate)
+        empty = torch.empty(0, device=v.device)
+        ctx.save_for_backward(q, k, v, beta, s0 if s0 is not None else empty,
+                              cu_seqlens if cu_seqlens is not None else empty)
+        ctx.has_s0, ctx.has_cu = s0 is not None, cu_seqlens is not None
         ctx.chunk_size, ctx.gate = chunk_size, gate
         return o, sf
 
     @staticmethod
     def backward(ctx, d_o, d_final):
-        q, k, v, beta, s0 = ctx.saved_tensors
+        q, k, v, beta, s0, cu = ctx.saved_tensors
         s0 = s0 if ctx.has_s0 else None
-        d_o = torch.zeros_like(v) if d_o is None else d_o.contiguous().to(v.dtype)
+        cu = cu if ctx.has_cu else None
+        d_o = torch.zeros_like(v) if d_o is None else _dense(d_o.to(v.dtype), True)
         d_final = None if d_final is None else d_final.contiguous().float()
-        dq, dk, dv, dbeta, ds0 = chunk_bwd(q, k, v, beta, d_o, initial_state=s0, d_final=d_final,
-                                           chunk_size=ctx.chunk_size, gate=ctx.gate, want_initial_grad=ctx.has_s0)
-        return dq, dk, dv, dbeta, ds0, None, None
+        dq, dk, dv, dbeta, ds0 = chunk_bwd_layout(q, k, v, beta, d_o, cu_seqlens=cu, initial_state=s0,
+                                                  d_final=d_final, chunk_size=ctx.chunk_size, gate=ctx.gate,
+                                                  want_initial_grad=ctx.has_s0)
+        return dq, dk, dv, dbeta, ds0, None, None, None
 
 
-def efla_attention(q, k, v, beta, initial_state=None, chunk_size=64, gate=GATE_EXACT):
+def efla_attention(q, k, v, beta, initial_state=None, chunk_size=64, gate=GATE_EXACT, cu_seqlens=None):
     """The chunked forward as a differentiable torch op: returns (o, final state); gradients flow to q, k, v,
-    beta and initial_state through chunk_bwd."""
-    return _EflaFunction.apply(q, k, v, beta, initial_state, int(chunk_size), int(gate))
+    beta and initial_state through the backward pass.  q, k, v [B,H,L,d] and beta [B,H,L] may be views of
+    another layout (e.g. ``x.transpose(1, 2)`` of [B,L,H,d] projections): dense views are used as they are, with
+    o and the gradients laid out like them, other views are copied first.  ``cu_seqlens`` (int32 GPU tensor of
+    N + 1 offsets) takes [1,H,T,d] packed sequences with per-sequence states [N,H,d_k,d_v], as chunk_fwd_layout."""
+    return _EflaFunction.apply(q, k, v, beta, initial_state, cu_seqlens, int(chunk_size), int(gate))
 
 
 def scan_plan(B, H, L, d_k, d_v, chunk=64, dtype=torch.bfloat16, segments=0):

@@ -7,9 +7,12 @@ separately by max |x - ref| / max |ref| over the tensor, at the forward's bar: b
 Cases: every d_k path and chunk size, ragged last chunks, with and without the initial state and the
 final-state gradient, stiff keys, the Runge-Kutta gates, and the full LM-layer shape checked on sampled heads
 (heads are independent) and for determinism: a second call gives the same bits (no kernel accumulates with
-atomics, so the sums' order never depends on timing).  Also the autograd wrapper against direct calls."""
+atomics, so the sums' order never depends on timing).  Also the autograd wrapper against direct calls, over
+[B,L,H,d] views (bit-identical to contiguous tensors) and over packed sequences (bit-identical to one call per
+sequence)."""
 import os
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -109,3 +112,71 @@ def test_autograd_wrapper_matches_direct_calls():
     torch.cuda.synchronize()
     for a, b in ((q.grad, dq), (k.grad, dk), (v.grad, dv), (beta.grad, db), (s0.grad, ds0)):
         assert torch.equal(a, b)
+
+
+def test_autograd_wrapper_over_bthd_views():
+    # q, k, v as [B,H,L,d] views of [B,L,H,d] leaves (a model layer's projections), beta of [B,L,H]: no copies, o
+    # laid out like v, and every output and gradient bit-identical to the same op on contiguous tensors
+    w = W.workload(3, B=2, H=4, L=300)
+    x = W.make_fwd_inputs(w)
+    g = W.make_grads(w)
+
+    def leaves(bthd):
+        ts = []
+        for a in (x["q"], x["k"], x["v"]):
+            t = dev(np.ascontiguousarray(a.transpose(0, 2, 1, 3)) if bthd else a, "bf16")
+            ts.append(t.requires_grad_())
+        b = x["beta"].transpose(0, 2, 1) if bthd else x["beta"]
+        ts.append(torch.from_numpy(np.ascontiguousarray(b)).cuda().requires_grad_())
+        return ts
+
+    d_o, dsf = dev(g["d_o"], "bf16"), torch.from_numpy(g["d_final"]).cuda()
+    lv = leaves(True)
+    views = [t.transpose(1, 2) for t in lv]
+    o, sf = efla.efla_attention(*views)
+    assert o.stride() == views[2].stride()
+    ((o.float() * d_o.float()).sum() + (sf * dsf).sum()).backward()
+    lc = leaves(False)
+    o2, sf2 = efla.efla_attention(*lc)
+    ((o2.float() * d_o.float()).sum() + (sf2 * dsf).sum()).backward()
+    torch.cuda.synchronize()
+    assert torch.equal(o.contiguous(), o2) and torch.equal(sf, sf2)
+    for a, b in zip(lv, lc):
+        assert torch.equal(a.grad.transpose(1, 2).contiguous(), b.grad)
+
+
+def test_autograd_wrapper_packed_sequences():
+    # three packed sequences (one empty) with their own initial states: outputs, final states and gradients equal
+    # those of one call per sequence
+    lengths = [130, 0, 77]
+    w = W.workload(2, H=2, d_k=64, d_v=64, chunk=64, dtype="bf16")
+    x = W.make_packed_inputs(w, lengths)
+    cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+    T = sum(lengths)
+    d_o = dev(W.make_grads(replace(w, B=1, L=T))["d_o"], "bf16")
+
+    def inputs(sl):
+        ts = [dev(np.ascontiguousarray(x[n][:, :, sl]), "bf16").requires_grad_() for n in ("q", "k", "v")]
+        ts.append(torch.from_numpy(np.ascontiguousarray(x["beta"][:, :, sl])).cuda().requires_grad_())
+        return ts
+
+    full = inputs(slice(0, T))
+    s0 = torch.from_numpy(x["initial_state"]).cuda().requires_grad_()
+    o, sf = efla.efla_attention(*full, initial_state=s0, cu_seqlens=cu)
+    ((o.float() * d_o.float()).sum() + sf.sum()).backward()
+    torch.cuda.synchronize()
+    for n in range(len(lengths)):
+        t0, t1 = int(x["cu_seqlens"][n]), int(x["cu_seqlens"][n + 1])
+        part = inputs(slice(t0, t1))
+        s0n = torch.from_numpy(np.ascontiguousarray(x["initial_state"][n:n + 1])).cuda().requires_grad_()
+        if t1 > t0:
+            on, sfn = efla.efla_attention(*part, initial_state=s0n)
+            ((on.float() * d_o[:, :, t0:t1].float()).sum() + sfn.sum()).backward()
+            torch.cuda.synchronize()
+            assert torch.equal(o[:, :, t0:t1], on) and torch.equal(sf[n:n + 1], sfn)
+            for a, b in zip(full, part):
+                assert torch.equal(a.grad[:, :, t0:t1], b.grad)
+            assert torch.equal(s0.grad[n:n + 1], s0n.grad)
+        else:   # an empty sequence passes its state through: S_L = S_0, so dS_0 = dS_L = 1
+            assert torch.equal(sf[n:n + 1], s0[n:n + 1].detach())
+            assert torch.equal(s0.grad[n:n + 1], torch.ones_like(s0n))
