@@ -5,8 +5,8 @@ forward (tests/test_oracle_pins.py).  Each gradient -- dq, dk, dv, dbeta and the
 separately by max |x - ref| / max |ref| over the tensor, at the forward's bar: below 1e-5 for fp32 inputs and
 2e-2 for bf16 inputs (the bf16 path also reads the forward's bf16 T diag(alpha) workspace).
 Cases: every d_k path and chunk size, ragged last chunks, with and without the initial state and the
-final-state gradient, stiff keys, the Runge-Kutta gates, and the full LM-layer shape checked on sampled heads
-(heads are independent) and for determinism: a second call gives the same bits (no kernel accumulates with
+final-state gradient, stiff keys, the Runge-Kutta gates, and the full LM-layer shape checked on every head and
+for determinism: a second call gives the same bits (no kernel accumulates with
 atomics, so the sums' order never depends on timing).  Also the autograd wrapper against direct calls, over
 [B,L,H,d] views (bit-identical to contiguous tensors) and over packed sequences (bit-identical to one call per
 sequence)."""
@@ -76,25 +76,23 @@ def test_bwd_gates(gate):
     _check(got, ref, "f32")
 
 
-def test_bwd_lm_layer_sampled_heads():
-    # the full LM-layer shape; the oracle checks two of the 128 heads (each head is an independent problem)
+def test_bwd_lm_layer_full_size_all_heads():
+    # the full LM-layer shape (B8 H16 L4096 d128 bf16, the matrix-core kernels), every head against the oracle, and a
+    # second call for determinism
     w = W.workload(3)
     x = W.make_fwd_inputs(w)
     g = W.make_grads(w)
     q, k, v, d_o = (dev(a, "bf16") for a in (x["q"], x["k"], x["v"], g["d_o"]))
     beta = torch.from_numpy(x["beta"]).cuda()
     dsf = torch.from_numpy(g["d_final"]).cuda()
-    dq, dk, dv, db, ds0 = efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=64)
+    got = efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=64)
     again = efla.chunk_bwd(q, k, v, beta, d_o, d_final=dsf, chunk_size=64)
     torch.cuda.synchronize()
-    for name, a, b in zip(("dq", "dk", "dv", "dbeta", "d_initial"), (dq, dk, dv, db, ds0), again):
+    for name, a, b in zip(("dq", "dk", "dv", "dbeta", "d_initial"), got, again):
         assert torch.equal(a, b), name
-    del again
-    for b, h in ((0, 0), (5, 11)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle.bwd(x["q"][sl], x["k"][sl], x["v"][sl], x["beta"][sl], None, g["d_o"][sl], g["d_final"][sl])
-        got = tuple(t[sl] for t in (dq, dk, dv, db, ds0))
-        _check(got, ref, "bf16")
+    del again, q, k, v, d_o
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["beta"], None, g["d_o"], g["d_final"])
+    _check(got, ref, "bf16")
 
 
 def test_autograd_wrapper_matches_direct_calls():
