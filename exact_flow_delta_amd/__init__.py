@@ -12,7 +12,8 @@ library is missing, every call raises.
 
     o, S = chunk_fwd_layout(q, k, v, beta, cu_seqlens=None)   # strided [B,H,L,d] views, packed sequences
     dq, dk, dv, dbeta, dS0 = chunk_bwd(q, k, v, beta, d_o, initial_state=None, d_final=None)
-    o, S = efla_attention(q, k, v, beta, initial_state=None)   # differentiable (torch.autograd)
+    dq, dk, dv, dbeta, dS0 = chunk_bwd_layout(q, k, v, beta, d_o, cu_seqlens=None)   # gradients in the inputs' strides
+    o, S = efla_attention(q, k, v, beta, initial_state=None, cu_seqlens=None)   # differentiable (torch.autograd)
 
 chunk_fwd calls efla_chunk_fwd by default, where the library picks the form for the sizes (fwd_form): the
 segment-parallel one for few heads and long sequences (method="scan"), else for bf16, d_k >= 32 and 64-token
@@ -39,7 +40,7 @@ import os
 import torch
 
 __all__ = ["EflaError", "alpha", "chunk_fwd", "chunk_fwd_layout", "layout_plan", "chunk_bwd", "chunk_bwd_workspace_size",
-           "efla_attention", "recurrent_step", "chunk_plan",
+           "chunk_bwd_layout", "chunk_bwd_layout_workspace_size", "efla_attention", "recurrent_step", "chunk_plan",
            "split_workspace_size", "fwd_workspace_size", "fwd_form", "ut_transform", "state_pass", "scan_plan", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))

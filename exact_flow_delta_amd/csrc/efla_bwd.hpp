@@ -20,8 +20,12 @@
 //                      leaving every chunk (fp32), dV and the initial state's gradient;
 //   bwd_chunk_kernel   one workgroup per (head, chunk): T by forward substitution in fp32, then dQ, dK, dbeta.
 // The first two are sequential over chunks and independent over (head, slab of state columns); the third is
-// parallel over all chunks.  All products are fp32 matrix-core instructions (16x16x4) on fp32 LDS tiles, each
-// wave owning whole 16x16 output tiles; inputs of either storage type are widened on load.
+// parallel over all chunks.  These generic kernels take every product as an fp32 matrix-core instruction
+// (16x16x4) on fp32 LDS tiles, each wave owning whole 16x16 output tiles, inputs of either storage type widened on
+// load; they serve fp32 inputs and the bf16 sizes the matrix-core kernels below do not take.  bf16 inputs with
+// d_k >= 32 run the three on bf16 matrix cores where the sizes allow (launch_bwd_t tries them first):
+// efla_bwd_chain_mx.hpp (state recompute and state gradient, 64-token chunks) and efla_bwd_mx.hpp (per-chunk
+// gradients, chunks of 32 or 64, d_v a multiple of 32, T^T from the UT launch).
 #pragma once
 
 #include "efla_common.hpp"

@@ -12,8 +12,9 @@
 //     indices 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 -- read with two 8-byte reads, or two transposing reads
 //     (ds_read_tr16_b64) on the strided side.  The matrix instruction sums over whatever indices each slot holds,
 //     as long as both operands agree.
-//   * The d_v columns are taken 32 at a time (one reduction step of the products over d_v), the state and state
-//     gradient slabs widened from the fp32 workspace to bf16 on the way into LDS.
+//   * The d_v columns are taken 32 at a time (one reduction step of the products over d_v); the state and state
+//     gradient slabs are read as bf16 from the workspace with 64-token chunks (the matrix-core state passes store
+//     them rounded to bf16) and rounded to bf16 on the way into LDS from the fp32 workspace otherwise.
 // T = (I + D strict_lower(L))^{-1} comes from the UT launch (its T^T export, bf16), and L = K K^T is formed only where
 // dalpha needs it, on the tiles of W2 the wave holds, so no fp32 C x C matrix passes through LDS.
 #pragma once
