@@ -471,8 +471,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
     constexpr int NLOAD = 2 * SH::NLQ + SH::NLV + SH::NLT;   // loads of a chunk's tiles
     // the ones issued: no Q tile without outputs, and no load of Ta quads 6 and 7 with half-chunk steps
     constexpr int NISSUE = NLOAD - (OUT ? 0 : SH::NLQ) - (NSUB == 2 ? 1 : 0);
-    // with UTW: the keys and betas of a chunk (issued first), then its queries and values; no Ta load
-    constexpr int NKB = SH::NLQ + 1;
+    // with UTW: the keys and betas of a chunk (issued first), then its queries and values (NQV loads); no Ta load
     constexpr int NQV = SH::NLQ + SH::NLV;
     static_assert(NSUB != 2 || SH::NLT == 5, "Ta of a 64-token chunk is five 1 KiB loads");
     // part 0: every tile of the chunk (Q, K, V, Ta); part 1 (UTW): K and the betas; part 2 (UTW): Q and V
