@@ -20,7 +20,8 @@
  *     and say how large it must be (efla_chunk_fwd_noalloc uses the library's array instead).
  *   - Layouts are contiguous row-major.  q, k: [B,H,L,d_k]; v, o: [B,H,L,d_v]; beta: [B,H,L];
  *     state: [B,H,d_k,d_v] (S as the update writes it: row i is key dimension i).
- *     efla_chunk_fwd_layout also takes strided views and packed sequences (efla_layout).
+ *     efla_chunk_fwd_layout and efla_chunk_bwd_layout also take strided views and packed sequences
+ *     (efla_layout).
  *   - q, k, v, o use the storage type `dtype` (fp32 or bf16).  beta, alpha and the state are fp32.
  *     Arithmetic is fp32 (bf16 operands are multiplied on bf16 matrix cores with fp32 accumulation).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work and returns;
@@ -319,7 +320,9 @@ efla_status efla_chunk_fwd_scan(const void* q, const void* k, const void* v, con
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Launch shape and workspace of efla_chunk_fwd_scan for these sizes (host only): segments used, chunks per
- * segment, state slab width and workspace bytes.  Errors as efla_chunk_fwd_scan would return for the sizes.
+ * segment, state slab width (of the pass that writes the outputs; the first pass, which carries d_v + d_k
+ * columns, takes slabs of 128 at d_k = d_v = 128 with bf16 and 64-token chunks when that still gives every
+ * compute unit a workgroup) and workspace bytes.  Errors as efla_chunk_fwd_scan would return for the sizes.
  * With segments = 0 the library cuts sequences only when one segment's state pass would run at most 64
  * workgroups (a quarter of the compute units): the count G starts at 1 and doubles while 2G segments' second
  * pass stays within 256 workgroups and the sequence holds at least 32 G chunks; otherwise one segment. */
