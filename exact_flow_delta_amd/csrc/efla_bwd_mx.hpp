@@ -221,11 +221,9 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     if (tid < (NV / 16) * C) sGR[tid] = 0.0f;
     __syncthreads();
     if (tid < C) {   // gates of the chunk's tokens (rows past the end: zero keys, zero step)
-        float lam = 0.0f;
-        for (int e = 0; e < DK; ++e) {
-            const float x = (float)sK[tid * LDK + e];
-            lam = fmaf(x, x, lam);
-        }
+        float lam = 0.0f;   // exact bf16 squares summed in fp32, 16 bytes of the key row per read
+#pragma unroll
+        for (int e = 0; e < DK; e += 8) lam += sum_sq(ld8(sK + tid * LDK + e));
         const float b = tid < n ? beta[be0 + (int64_t)tid * ly.be_t] : 0.0f;
         sAl[tid] = gate_alpha(b, lam, gate);
         float db, dl;
@@ -257,9 +255,11 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
         Acc<C, NV, NWV> R;   // R = V - K S, kept for dalpha; D R over V
         R.zero();
         mmx<C, NV, NWV, true, false, DK>(R, sK, LDK, sS, LDV, w, lane);
-        R.each(w, lane, [&](int i, int j, float& x) { x = (float)sV[i * LDV + j] - x; });
-        __syncthreads();
-        R.each(w, lane, [&](int i, int j, float& x) { sV[i * LDV + j] = (bf16)(sAl[i] * x); });
+        // each element of sV is read and then overwritten by the one lane that holds it in R: no barrier between
+        R.each(w, lane, [&](int i, int j, float& x) {
+            x = (float)sV[i * LDV + j] - x;
+            sV[i * LDV + j] = (bf16)(sAl[i] * x);
+        });
         __syncthreads();
         {   // Delta = T (D R); dDelta = P^T dO + K dS'
             Acc<C, NV, NWV> a, b;
@@ -357,12 +357,21 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     mmx<C, DK, NWV, false, false, C>(aK, sP, LDC, sQ, LDK, w, lane);
     mmx<C, DK, NWV, true, false, C>(aK, sT, LDC, sK, LDK, w, lane);
     mmx<C, DK, NWV, false, false, C>(aK, sT, LDC, sK, LDK, w, lane);
-    aQ.each(w, lane, [&](int i, int e, float& x) {
-        if (i < n) dq[q0 + (int64_t)i * ly.q_t + e] = (bf16)x;
-    });
-    aK.each(w, lane, [&](int i, int e, float& x) {
-        if (i < n) dk[k0 + (int64_t)i * ly.k_t + e] = (bf16)fmaf(2.0f * sDa[i], (float)sK[i * LDK + e], x);
-    });
+    // dQ and dK staged as bf16 tiles in the slab tiles' space (no product reads it any more), then written as
+    // 16-byte pieces of the chunk's rows
+    static_assert(2 * C * LDK * 2 <= LY::AL - LY::S, "dQ and dK tiles fit where the slab tiles were");
+    bf16* sDQ = reinterpret_cast<bf16*>(smem_x + LY::S);
+    bf16* sDK = sDQ + C * LDK;
+    aQ.each(w, lane, [&](int i, int e, float& x) { sDQ[i * LDK + e] = (bf16)x; });
+    aK.each(w, lane, [&](int i, int e, float& x) { sDK[i * LDK + e] = (bf16)fmaf(2.0f * sDa[i], (float)sK[i * LDK + e], x); });
+    __syncthreads();
+    for (int idx = tid; idx < C * (DK / 8); idx += NTH) {
+        const int r = idx / (DK / 8), c8 = (idx - r * (DK / 8)) * 8;
+        if (r < n) {
+            *reinterpret_cast<bf16x8*>(dq + q0 + (int64_t)r * ly.q_t + c8) = ld8(sDQ + r * LDK + c8);
+            *reinterpret_cast<bf16x8*>(dk + k0 + (int64_t)r * ly.k_t + c8) = ld8(sDK + r * LDK + c8);
+        }
+    }
 }
 
 // Launches the matrix-core chunk kernel when it applies (bf16, d_k >= 32, chunk 32 or 64, d_v a multiple of 32, and
