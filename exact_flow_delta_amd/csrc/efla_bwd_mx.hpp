@@ -126,9 +126,9 @@ struct TileB {
 // LDS of the kernel (byte offsets): bf16 tiles Q, K (C x DK), P and T^T (C x C), the d_v slab tiles S, dS' (DK x NV)
 // and V, dO, Delta, dDelta, G (C x NV); four fp32 C-vectors; the fp32 row sums behind dalpha, one C-vector per
 // 16-column tile column of G o R (NV / 16) and of strict_lower(L) o W2 (C / 16), each element written by one lane.
-template <int DK, int C>
+template <int DK, int C, int NV_>
 struct BwdXLds {
-    static constexpr int NV = 32;
+    static constexpr int NV = NV_;   // d_v columns per slab (32 or 64)
     static constexpr int LDK = DK + 8, LDC = C + 8, LDV = NV + 8;
     static constexpr int Q = 0;
     static constexpr int K = Q + C * LDK * 2;
@@ -150,7 +150,7 @@ struct BwdXLds {
 
 constexpr int kChunkXThreads = 512;   // eight waves
 
-template <int DK, int C>
+template <int DK, int C, int NVS>
 __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ beta,
     const bf16* __restrict__ d_o, const void* __restrict__ s_all, const void* __restrict__ ds_all,
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     using namespace bwdx;
     constexpr int NWV = kChunkXThreads / 64;
     constexpr int NTH = kChunkXThreads;
-    typedef BwdXLds<DK, C> LY;
+    typedef BwdXLds<DK, C, NVS> LY;
     constexpr int NV = LY::NV, LDK = LY::LDK, LDC = LY::LDC, LDV = LY::LDV;
     static_assert(DK % 32 == 0 && C % 32 == 0, "d_k and chunk multiples of 32");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_x[];
@@ -374,8 +374,24 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     }
 }
 
+template <int DK, int C, int NV>
+hipError_t launch_bwd_chunk_mx_nv(const BwdArgs& a, hipStream_t s) {
+    constexpr int LDS = bwdx::BwdXLds<DK, C, NV>::BYTES;
+    static_assert(LDS <= kMaxLdsBytes, "matrix-core chunk kernel LDS too large");
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_mx_kernel<DK, C, NV>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_chunk_mx_kernel<DK, C, NV>), dim3((unsigned)bwd_chunk_grid(a, C)), dim3(kChunkXThreads), LDS,
+                       s, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                       a.beta, static_cast<const bf16*>(a.d_o), a.s_all, a.ds_all, static_cast<const bf16*>(a.tt),
+                       static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk), a.dbeta, a.L, a.d_v, a.gate, bwd_layout(a));
+    return hipGetLastError();
+}
+
 // Launches the matrix-core chunk kernel when it applies (bf16, d_k >= 32, chunk 32 or 64, d_v a multiple of 32, and
-// the UT launch wrote T^T); returns false otherwise, leaving the launch to bwd_chunk_kernel.
+// the UT launch wrote T^T); returns false otherwise, leaving the launch to bwd_chunk_kernel.  The d_v columns are
+// taken 64 at a time where d_v allows (the products over a slab then reuse each operand fragment for two tiles of
+// a wave, and a chunk has half as many slab phases), else 32.
 template <int DK, int C>
 bool launch_bwd_chunk_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
     if constexpr (DK < 32 || C < 32) {
@@ -389,19 +405,7 @@ bool launch_bwd_chunk_mx(const BwdArgs& a, hipStream_t s, hipError_t* err) {
             *err = hipErrorInvalidValue;
             return true;
         }
-        constexpr int LDS = bwdx::BwdXLds<DK, C>::BYTES;
-        static_assert(LDS <= kMaxLdsBytes, "matrix-core chunk kernel LDS too large");
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_chunk_mx_kernel<DK, C>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL((bwd_chunk_mx_kernel<DK, C>), dim3((unsigned)bwd_chunk_grid(a, C)), dim3(kChunkXThreads),
-                               LDS, s, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                               static_cast<const bf16*>(a.v), a.beta, static_cast<const bf16*>(a.d_o), a.s_all,
-                               a.ds_all, static_cast<const bf16*>(a.tt), static_cast<bf16*>(a.dq),
-                               static_cast<bf16*>(a.dk), a.dbeta, a.L, a.d_v, a.gate, bwd_layout(a));
-            e = hipGetLastError();
-        }
-        *err = e;
+        *err = a.d_v % 64 == 0 ? launch_bwd_chunk_mx_nv<DK, C, 64>(a, s) : launch_bwd_chunk_mx_nv<DK, C, 32>(a, s);
         return true;
     }
 }

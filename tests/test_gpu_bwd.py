@@ -55,7 +55,7 @@ def _check(got, ref, dtype):
 @pytest.mark.parametrize("cfg,dtype,d_k,d_v,chunk,L", [
     (1, "f32", 16, 16, 16, 77), (2, "f32", 64, 64, 64, 300), (2, "f32", 32, 64, 32, 130), (6, "f32", 64, 16, 16, 99),
     (2, "f32", 128, 32, 64, 200), (3, "bf16", 128, 128, 64, 300), (2, "bf16", 64, 64, 32, 257),
-    (6, "bf16", 32, 128, 16, 150)])
+    (6, "bf16", 32, 128, 16, 150), (3, "bf16", 128, 32, 64, 203), (2, "bf16", 32, 32, 32, 161)])
 def test_bwd_shapes(cfg, dtype, d_k, d_v, chunk, L):
     w = W.workload(cfg, B=1, H=2, L=L, d_k=d_k, d_v=d_v, chunk=chunk, dtype=dtype)
     got, ref = _run(w)
