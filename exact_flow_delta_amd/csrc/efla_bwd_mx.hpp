@@ -124,7 +124,7 @@ struct TileB {
 };
 
 // LDS of the kernel (byte offsets): bf16 tiles Q, K (C x DK), P and T^T (C x C), the d_v slab tiles S, dS' (DK x NV)
-// and V, dO, Delta, dDelta, G (C x NV); four fp32 C-vectors; the fp32 row sums behind dalpha, one C-vector per
+// and V (then D R), dO, Delta, dDelta, G, -dR (C x NV); four fp32 C-vectors; the fp32 row sums behind dalpha, one C-vector per
 // 16-column tile column of G o R (NV / 16) and of strict_lower(L) o W2 (C / 16), each element written by one lane.
 template <int DK, int C, int NV_>
 struct BwdXLds {
@@ -141,7 +141,8 @@ struct BwdXLds {
     static constexpr int DL = O + C * LDV * 2;
     static constexpr int DD = DL + C * LDV * 2;
     static constexpr int GS = DD + C * LDV * 2;
-    static constexpr int AL = GS + C * LDV * 2;
+    static constexpr int DRN = GS + C * LDV * 2;
+    static constexpr int AL = DRN + C * LDV * 2;
     static constexpr int RS = AL + 4 * C * 4;
     static constexpr int BYTES = RS + (NV / 16 + C / 16) * C * 4;
 };
@@ -170,11 +171,12 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     bf16* sT = reinterpret_cast<bf16*>(smem_x + LY::T);    // T^T; later dL
     bf16* sS = reinterpret_cast<bf16*>(smem_x + LY::S);    // S[:, slab]
     bf16* sG2 = reinterpret_cast<bf16*>(smem_x + LY::G2);  // dS'[:, slab]
-    bf16* sV = reinterpret_cast<bf16*>(smem_x + LY::V);    // V slab; then D R; then -dR
+    bf16* sV = reinterpret_cast<bf16*>(smem_x + LY::V);    // V slab; then D R
     bf16* sO = reinterpret_cast<bf16*>(smem_x + LY::O);    // dO slab
     bf16* sDl = reinterpret_cast<bf16*>(smem_x + LY::DL);  // Delta slab
     bf16* sDd = reinterpret_cast<bf16*>(smem_x + LY::DD);  // dDelta slab
     bf16* sGs = reinterpret_cast<bf16*>(smem_x + LY::GS);  // G slab
+    bf16* sDr = reinterpret_cast<bf16*>(smem_x + LY::DRN); // -dR slab
     float* sAl = reinterpret_cast<float*>(smem_x + LY::AL);
     float* sDb = sAl + C;
     float* sDlam = sDb + C;
@@ -252,35 +254,33 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
         to.store(sO, LDV, tid);
         __syncthreads();
         if (col0 + NV < DV) load_slab(col0 + NV);
-        Acc<C, NV, NWV> R;   // R = V - K S, kept for dalpha; D R over V
+        // phase A: R = V - K S (kept for dalpha; D R over V) and dDelta = K dS' + P^T dO -- the two share the key
+        // fragments and need nothing from each other
+        Acc<C, NV, NWV> R, dD;
         R.zero();
+        dD.zero();
         mmx<C, NV, NWV, true, false, DK>(R, sK, LDK, sS, LDV, w, lane);
+        mmx<C, NV, NWV, true, false, DK>(dD, sK, LDK, sG2, LDV, w, lane);
+        mmx<C, NV, NWV, false, false, C>(dD, sP, LDC, sO, LDV, w, lane);
         // each element of sV is read and then overwritten by the one lane that holds it in R: no barrier between
         R.each(w, lane, [&](int i, int j, float& x) {
             x = (float)sV[i * LDV + j] - x;
             sV[i * LDV + j] = (bf16)(sAl[i] * x);
         });
+        dD.each(w, lane, [&](int i, int j, float& x) { sDd[i * LDV + j] = (bf16)x; });
         __syncthreads();
-        {   // Delta = T (D R); dDelta = P^T dO + K dS'
-            Acc<C, NV, NWV> a, b;
+        {   // phase B: Delta = T (D R); G = T^T dDelta; -dR = -D G; dalpha += rowsum(G o R)
+            Acc<C, NV, NWV> a, gg;
             a.zero();
-            b.zero();
+            gg.zero();
             mmx<C, NV, NWV, false, false, C>(a, sT, LDC, sV, LDV, w, lane);
-            mmx<C, NV, NWV, false, false, C>(b, sP, LDC, sO, LDV, w, lane);
-            mmx<C, NV, NWV, true, false, DK>(b, sK, LDK, sG2, LDV, w, lane);
+            mmx<C, NV, NWV, true, false, C>(gg, sT, LDC, sDd, LDV, w, lane);
             a.each(w, lane, [&](int i, int j, float& x) { sDl[i * LDV + j] = (bf16)x; });
-            b.each(w, lane, [&](int i, int j, float& x) { sDd[i * LDV + j] = (bf16)x; });
-        }
-        __syncthreads();
-        {   // G = T^T dDelta; -dR = -D G over V; dalpha += rowsum(G o R)
-            Acc<C, NV, NWV> a;
-            a.zero();
-            mmx<C, NV, NWV, true, false, C>(a, sT, LDC, sDd, LDV, w, lane);
-            a.each(w, lane, [&](int i, int j, float& x) {
+            gg.each(w, lane, [&](int i, int j, float& x) {
                 sGs[i * LDV + j] = (bf16)x;
-                sV[i * LDV + j] = (bf16)(-sAl[i] * x);
+                sDr[i * LDV + j] = (bf16)(-sAl[i] * x);
             });
-            // rows of this lane's elements: the same (tile, i) for a and R, summed over the tile's 16 columns into
+            // rows of this lane's elements: the same (tile, i) for gg and R, summed over the tile's 16 columns into
             // the tile column's row sums (a tile belongs to the same wave in every slab: one writer per element, and
             // a fixed order of the sums, so the gradients do not depend on the waves' timing)
             typedef Acc<C, NV, NWV> AN;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
                     const int ti = tt / AN::TN, tj = tt - ti * AN::TN;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float p = a.t[s][i] * R.t[s][i];
+                        float p = gg.t[s][i] * R.t[s][i];
                         p += __shfl_xor(p, 1, 16);
                         p += __shfl_xor(p, 2, 16);
                         p += __shfl_xor(p, 4, 16);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
         // dQ += dO S^T; dK += Delta dS'^T - dR S^T; W1 += dO Delta^T; W2 += G Delta^T (reduction over the slab)
         mmx<C, DK, NWV, true, true, NV>(aQ, sO, LDV, sS, LDV, w, lane);
         mmx<C, DK, NWV, true, true, NV>(aK, sDl, LDV, sG2, LDV, w, lane);
-        mmx<C, DK, NWV, true, true, NV>(aK, sV, LDV, sS, LDV, w, lane);
+        mmx<C, DK, NWV, true, true, NV>(aK, sDr, LDV, sS, LDV, w, lane);
         mmx<C, C, NWV, true, true, NV>(W1, sO, LDV, sDl, LDV, w, lane);
         mmx<C, C, NWV, true, true, NV>(W2, sGs, LDV, sDl, LDV, w, lane);
         __syncthreads();
