@@ -129,7 +129,7 @@ struct TileB {
 template <int DK, int C, int NV_>
 struct BwdXLds {
     static constexpr int NV = NV_;   // d_v columns per slab (32 or 64)
-    static constexpr int LDK = DK + 8, LDC = C + 8, LDV = NV + 8;
+    static constexpr int LDK = DK + 8, LDC = C + 8, LDV = NV + 16;   // row padding (elements) measured best
     static constexpr int Q = 0;
     static constexpr int K = Q + C * LDK * 2;
     static constexpr int P = K + C * LDK * 2;
