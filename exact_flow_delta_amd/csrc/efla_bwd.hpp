@@ -510,10 +510,7 @@ __global__ __launch_bounds__(kChunkThreads) void bwd_chunk_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float p = a.t[s][i] * R.t[s][i];
-                        p += __shfl_xor(p, 1, 16);
-                        p += __shfl_xor(p, 2, 16);
-                        p += __shfl_xor(p, 4, 16);
-                        p += __shfl_xor(p, 8, 16);
+                        p = group_sum<16>(p);   // the tile row's 16 columns, by DPP moves
                         if ((lane & 15) == 0) sDa[16 * tt + 4 * (lane >> 4) + i] += p;
                     }
                 }

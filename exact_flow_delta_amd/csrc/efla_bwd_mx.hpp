@@ -292,10 +292,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float p = gg.t[s][i] * R.t[s][i];
-                        p += __shfl_xor(p, 1, 16);
-                        p += __shfl_xor(p, 2, 16);
-                        p += __shfl_xor(p, 4, 16);
-                        p += __shfl_xor(p, 8, 16);
+                        p = group_sum<16>(p);   // the tile row's 16 columns, by DPP moves
                         if ((lane & 15) == 0) sGR[tj * C + 16 * ti + 4 * (lane >> 4) + i] += p;
                     }
                 }
@@ -329,10 +326,7 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * ti + 4 * (lane >> 4) + i, col = 16 * tj + (lane & 15);
                     float p = col < row ? Lt.t[s][i] * W2.t[s][i] : 0.0f;
-                    p += __shfl_xor(p, 1, 16);
-                    p += __shfl_xor(p, 2, 16);
-                    p += __shfl_xor(p, 4, 16);
-                    p += __shfl_xor(p, 8, 16);
+                    p = group_sum<16>(p);   // the tile row's 16 columns, by DPP moves
                     if ((lane & 15) == 0) sLW[tj * C + row] = p;
                 }
             }
