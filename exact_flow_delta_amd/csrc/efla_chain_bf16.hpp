@@ -158,14 +158,11 @@ __device__ __forceinline__ void ut_half_lds(const lds_u8* cK, const lds_u8* cB, 
         float sq = 0.0f;
 #pragma unroll
         for (int kp = 0; kp < NKP; ++kp) sq += sum_sq(kf[j][kp]);
-        sq += __shfl_xor(sq, 16, 64);
-        sq += __shfl_xor(sq, 32, 64);
-        lam[j] = sq;
+        lam[j] = cross_row_sum(sq);
     }
     const float alpha_mine = gate_alpha(beta_mine, gb ? lam[1] : lam[0], gate);
-    float ar[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) ar[j] = __shfl(alpha_mine, 16 * j + r, 64);
+    float ar[2];   // gate of row 16 j + r: rows 0 and 2 of the wave hold the tokens of block 0, rows 1 and 3 block 1
+    row_swap16(alpha_mine, ar[0], ar[1]);
 
     // Gram blocks (j, l), l <= j: acc lane (r, g), element i = (K K^T)[32 h + 16 j + r][32 h + 16 l + 4 g + i]
     quad A10;
@@ -317,13 +314,18 @@ __device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB
         gr[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kp], kf[1][kp], gr[1], 0, 0, 0);
         gr[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kp], kf[1][kp], gr[2], 0, 0, 0);
     }
-    // lambda of row 16 j + r is the diagonal entry (r, r) of block (j, j), held by lane (r, r / 4) as element r % 4
-    const int dsrc = r + 16 * (r >> 2);
-    const float lam0 = __shfl(gr[0][r & 3], dsrc, 64);
-    const float lam1 = __shfl(gr[1][r & 3], dsrc, 64);
+    // lambda of row 16 j + r is the diagonal entry (r, r) of block (j, j), held by lane (r, r / 4) as element r % 4:
+    // row r / 4 of the wave, taken to its whole column by two row swaps
+    auto diag = [&](const f32x4& blk) __attribute__((always_inline)) {
+        float e, o, lo, hi;
+        row_swap16(blk[r & 3], e, o);
+        row_swap32((r >> 2) & 1 ? o : e, lo, hi);
+        return (r >> 3) & 1 ? hi : lo;
+    };
+    const float lam0 = diag(gr[0]);
+    const float lam1 = diag(gr[1]);
     u.alpha_mine = gate_alpha(beta_mine, gb ? lam1 : lam0, gate);
-    u.ar0 = __shfl(u.alpha_mine, r, 64);
-    u.ar1 = __shfl(u.alpha_mine, 16 + r, 64);
+    row_swap16(u.alpha_mine, u.ar0, u.ar1);   // rows 0 and 2 hold block 0's tokens, rows 1 and 3 block 1's
     u.A10 = M::cvt(gr[2] * u.ar1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

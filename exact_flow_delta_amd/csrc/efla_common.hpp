@@ -242,18 +242,59 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// gfx950 row swaps between the 16-lane rows of a wave (v_permlane16_swap / v_permlane32_swap, vector ALU, no
+// LDS), both operands x.  row_swap16: `even` holds, in rows 0..3, rows 0, 0, 2, 2 of x and `odd` rows 1, 1, 3, 3.
+// row_swap32: `lo` holds rows 0, 1, 0, 1 and `hi` rows 2, 3, 2, 3.  Every lane of the wave must be active.
+// The two results leave the builtin's vector by value (__uint_as_float): a bit cast of a subscripted element of a
+// vector lvalue reads element 0 in this compiler.
+__device__ __forceinline__ void row_swap16(float x, float& even, float& odd) {
+    const unsigned u = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    even = __uint_as_float(p[0]);
+    odd = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void row_swap32(float x, float& lo, float& hi) {
+    const unsigned u = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(p[0]);
+    hi = __uint_as_float(p[1]);
+}
+// Sum of the four lanes r, 16 + r, 32 + r, 48 + r, on each of them: (x0 + x1) + (x2 + x3), as a butterfly
+// over lane distances 16 and 32 pairs them.
+__device__ __forceinline__ float cross_row_sum(float x) {
+    float a, b;
+    row_swap16(x, a, b);
+    row_swap32(a + b, a, b);
+    return a + b;
+}
+// out[i] = x of lane 16 i + r, on every lane of column r.
+__device__ __forceinline__ void rows_bcast4(float x, float out[4]) {
+    float e, o;
+    row_swap16(x, e, o);
+    row_swap32(e, out[0], out[2]);
+    row_swap32(o, out[1], out[3]);
+}
+
 // Sum over aligned groups of WIDTH consecutive lanes (WIDTH a power of two <= 64); every lane of a
 // group receives the group's sum.  Within a 16-lane row the partners come from DPP moves: swap
 // neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror each half row, mirror the
-// row; wider groups add cross-row swizzles.
+// row; wider groups add the row swaps.
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float x) {
     if constexpr (WIDTH >= 2) x += dpp_mov<0xB1>(x);
     if constexpr (WIDTH >= 4) x += dpp_mov<0x4E>(x);
     if constexpr (WIDTH >= 8) x += dpp_mov<0x141>(x);
     if constexpr (WIDTH >= 16) x += dpp_mov<0x140>(x);
-    if constexpr (WIDTH >= 32) x += __shfl_xor(x, 16, 64);
-    if constexpr (WIDTH >= 64) x += __shfl_xor(x, 32, 64);
+    if constexpr (WIDTH >= 32) {
+        float e, o;
+        row_swap16(x, e, o);
+        x = e + o;
+    }
+    if constexpr (WIDTH >= 64) {
+        float lo, hi;
+        row_swap32(x, lo, hi);
+        x = lo + hi;
+    }
     return x;
 }
 

@@ -123,9 +123,7 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
             float s = 0.0f;
 #pragma unroll
             for (int kp = 0; kp < NKP; ++kp) s += sum_sq(kf[rb][kp]);
-            s += __shfl_xor(s, 16, 64);
-            s += __shfl_xor(s, 32, 64);
-            lam[rb] = s;
+            lam[rb] = cross_row_sum(s);
         }
         // gate of token 16 g + r on lane (r, g) (lanes past the chunk compute an unused value), then the gate
         // of row 16 rb + r on every lane of row r
@@ -133,9 +131,8 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
 #pragma unroll
         for (int rb = 1; rb < NB; ++rb) lam_mine = g == rb ? lam[rb] : lam_mine;
         const float alpha_mine = gate_alpha(beta_mine, lam_mine, gate);
-        float ar[NB];
-#pragma unroll
-        for (int rb = 0; rb < NB; ++rb) ar[rb] = __shfl(alpha_mine, 16 * rb + r, 64);
+        float ar[4];
+        rows_bcast4(alpha_mine, ar);
 
         // ---- Gram blocks: acc lane (r, g), element i = (K K^T)[16 hi + r][16 lo + 4 g + i] --------------------
         quad Aq[SH::NQ];   // off-diagonal blocks of A (row order, qi = hi (hi + 1) / 2 + lo), bf16 A operands
