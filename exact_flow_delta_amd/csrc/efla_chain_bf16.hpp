@@ -729,6 +729,16 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
             quad Rq[NBS];
             bx8 kq[NBS][NKP];
             quad Pq[NBS * (NBS + 1) / 2];   // block (j, lo) of the sub-chunk at j (j + 1) / 2 + lo
+            // Delta = Ta R over the sub-chunk; Ta block (rb, kb) of the chunk is quad qi = rb (rb + 1) / 2 + kb,
+            // lane (r, g)'s at byte 512 qi + 8 lane
+            auto ta = [&](int rb, int kb) __attribute__((always_inline)) {
+                return *reinterpret_cast<const lds_quad*>(cT + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+            };
+            // R = V - K S: lane (r, g), element e of row block rb: row 16 rb + 4g + e, column 16 w + r of the slab
+            auto vblk = [&](int rb) __attribute__((always_inline)) {
+                return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                    (lds_s16x4*)(const_cast<lds_u8*>(cV) + 16 * rb * SH::RBV + v_off)));
+            };
             static_for<NBS>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 constexpr int rb = b0 + j;
@@ -746,9 +756,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
                     if constexpr (OUT) Ot[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Sq[kp], qq[kp], Ot[rb], 0, 0, 0);   // (Q S)^T
                     xk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[j][kp], Sq[kp], xk, 0, 0, 0);       // K S
                 }
-                // R = V - K S: lane (r, g), element e: row 16 rb + 4g + e, column 16 w + r of the slab
-                const s16x4 vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_u8*>(cV) + 16 * rb * SH::RBV + v_off));
-                const quad vq = __builtin_bit_cast(quad, vr);
+                const quad vq = vblk(rb);
                 f32x4 rr;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) rr[e] = (float)vq[e] - xk[e];
@@ -771,10 +779,21 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
 #pragma unroll
                 for (int lo = 0; lo <= j; ++lo) Pq[j * (j + 1) / 2 + lo] = M::cvt(pacc[lo]);
             });
-            // Delta = Ta R over the sub-chunk; Ta block (rb, kb) of the chunk is quad qi = rb (rb + 1) / 2 + kb,
-            // lane (r, g)'s at byte 512 qi + 8 lane
-            auto ta = [&](int rb, int kb) __attribute__((always_inline)) {
-                return *reinterpret_cast<const lds_quad*>(cT + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+            // the transposed key blocks of the state update depend on nothing computed in the sub-chunk: with the
+            // UT waves in the workgroup, read them all here, ahead of the Delta products, and keep the scheduler
+            // from sinking them to their uses (measured faster there, slower in the state pass on its own)
+            constexpr bool kKtEarly = UTW == 2;
+            quad kte[NBS][NKD];
+            if constexpr (kKtEarly) {
+#pragma unroll
+                for (int rt = 0; rt < NKD; ++rt)
+#pragma unroll
+                    for (int i = 0; i < NBS; ++i) kte[i][rt] = kt(rt, b0 + i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            auto ktb = [&](int rt, int kb) __attribute__((always_inline)) {
+                if constexpr (kKtEarly) return kte[kb - b0][rt];
+                else return kt(rt, kb);
             };
             quad Dq[NBS];
             static_for<NBS>([&](auto jc) {
@@ -806,15 +825,15 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
                 quad k0[NKD], k1[NKD];
 #pragma unroll
                 for (int rt = 0; rt < NKD; ++rt) {
-                    k0[rt] = kt(rt, b0 + i);
-                    k1[rt] = kt(rt, b0 + i + 1);
+                    k0[rt] = ktb(rt, b0 + i);
+                    k1[rt] = ktb(rt, b0 + i + 1);
                 }
 #pragma unroll
                 for (int rt = 0; rt < NKD; ++rt) M::mma2(S[rt], k0[rt], k1[rt], Dq[i], Dq[i + 1]);
             }
             if constexpr (NBS & 1) {
 #pragma unroll
-                for (int rt = 0; rt < NKD; ++rt) M::mma1(S[rt], kt(rt, b0 + NBS - 1), Dq[NBS - 1]);
+                for (int rt = 0; rt < NKD; ++rt) M::mma1(S[rt], ktb(rt, b0 + NBS - 1), Dq[NBS - 1]);
             }
         });
         pend_t0 = c * C;
