@@ -259,8 +259,8 @@ struct UtCarry {
     float ar0, ar1;      // gates of rows 16 j + r
     float alpha_mine;    // gate of token 32 h + 16 (g & 1) + r
 };
-constexpr int kUtSplit = 1;   // substitution steps in part 1 (part 1 holds the Gram products and, in the wave that
-                              // issues a step's loads, their issue: 1 balances the two)
+constexpr int kUtSplit = 1;   // substitution steps in part 1 (part 1 also holds the Gram products and the issue of
+                              // a step's loads; measured against 0, 2, 3 and 5)
 
 // steps m = M0 .. M1 - 1 of the right-looking substitution on the transposed diagonal block `at` (rows of At read
 // three steps ahead)
@@ -393,8 +393,8 @@ __device__ __forceinline__ void ut_half_part2(lds_u8* scr, lds_u8* ta, int lane,
 // OUT = false: no outputs (the first pass of the segment-parallel forward needs only the final states), so no
 // Q tile, no Q S, no Q K^T and no O -- 38 matrix instructions per chunk and wave instead of 100.
 // UTW: the in-workgroup UT transform (tw unused; beta and gate read); 64-token chunks with outputs, one segment.
-// 1: two UT waves and the load producer over three chunk buffers; 2: four UT waves, the first of which also issues
-// the loads, over separate rings (keys and betas four chunks deep, so that a UT wave has two steps per chunk).
+// 1: two UT waves and the load producer over three chunk buffers; 2: four UT waves, which also issue the loads,
+// over separate rings (keys and betas four chunks deep, so that a UT wave has two steps per chunk).
 template <int DK, int C, int DVS, bool OUT, int UTW = 0>
 __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 64)) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
@@ -544,9 +544,9 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
             // UT wave u: pair u >> 1 takes the chunks of that parity, u & 1 is its half.  In step c (c0 - 2 <= c < c1)
             // pair c & 1 runs part 1 of chunk c + 2 and the other pair part 2 of chunk c + 1 (which writes its Ta).
             // The UT waves also issue the loads: wave 0 before the first barrier the keys and betas of chunks
-            // c0 .. c0 + 2 and the queries and values of c0; in step c >= c0 the first wave of the pair running part
-            // 1 (the lighter part) the keys and betas of c + 3 and the queries and values of c + 1, all landed by the
-            // end of the step.
+            // c0 .. c0 + 2 and the queries and values of c0; in step c >= c0 the pair running part 1 (the lighter
+            // part), its first wave the keys and betas of c + 3 and its second the queries and values of c + 1, each
+            // landed by the end of the step.
             typedef std::integral_constant<int, 1> I1;
             typedef std::integral_constant<int, 2> I2;
             const int u = w - NW;
@@ -572,10 +572,8 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
                 }
                 __builtin_amdgcn_s_barrier();
                 for (int c = c0 - 2; c < c1; ++c) {
-                    if (u == 2 * (c & 1) && c >= c0) {
-                        if (c + 3 < c1) issue_kb(c + 3);
-                        if (c + 1 < c1) issue_qv(c + 1);
-                    }
+                    if (u == 2 * (c & 1) && c >= c0 && c + 3 < c1) issue_kb(c + 3);
+                    if (u == 2 * (c & 1) + 1 && c >= c0 && c + 1 < c1) issue_qv(c + 1);
                     if ((c & 1) == pair) {
                         if (c + 2 < c1) {
                             lds_u8* kb = kbslot(c + 2);
