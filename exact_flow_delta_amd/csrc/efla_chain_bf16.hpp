@@ -285,6 +285,23 @@ __device__ __forceinline__ void ut_solve_steps(const lds_f32* at, float* sv) {
     }
 }
 
+// steps m = M0 .. M1 - 1 of the same substitution with every row of `at` it needs read first (all in flight at once)
+template <int M0, int M1>
+__device__ __forceinline__ void ut_solve_steps_all(const lds_f32* at, float* sv) {
+    constexpr int LDAT = 20;
+    f32x4 rows[16][4];
+#pragma unroll
+    for (int m = M0; m < M1; ++m) {
+#pragma unroll
+        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) rows[m][i4] = *reinterpret_cast<const lds_f32x4*>(at + m * LDAT + 4 * i4);
+    }
+#pragma unroll
+    for (int m = M0; m < M1; ++m) {
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) sv[i] -= rows[m][i / 4][i % 4] * sv[m];
+    }
+}
+
 template <int DK>
 __device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB, lds_u8* scr, int gate, int lane,
                                               int h, UtCarry& u) {
@@ -340,6 +357,9 @@ __device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB
     ut_solve_steps<0, kUtSplit>(sAt + gb * kUtHalfAtb, u.sv);
 }
 
+// ALL_ROWS: the substitution reads every row it needs first (measured faster with d_k = 128; it raises the
+// register count of the smaller shapes' kernels)
+template <bool ALL_ROWS>
 __device__ __forceinline__ void ut_half_part2(lds_u8* scr, lds_u8* ta, int lane, int h, UtCarry& u) {
     typedef Mma<bf16> M;
     typedef M::quad quad;
@@ -354,7 +374,10 @@ __device__ __forceinline__ void ut_half_part2(lds_u8* scr, lds_u8* ta, int lane,
     auto quad_t = [&](const lds_b16* X) __attribute__((always_inline)) {
         return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_b16*>(X) + tr)));
     };
-    ut_solve_steps<kUtSplit, 15>(sAt + gb * kUtHalfAtb, u.sv);
+    if constexpr (ALL_ROWS)
+        ut_solve_steps_all<kUtSplit, 15>(sAt + gb * kUtHalfAtb, u.sv);
+    else
+        ut_solve_steps<kUtSplit, 15>(sAt + gb * kUtHalfAtb, u.sv);
     __asm__ volatile("" ::: "memory");   // the rows of A are read before Ta^T overwrites them
     if (g < 2) {
         bx8 t0v, t1v, a0v, a1v;
@@ -580,7 +603,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
                             ut_half_part1<DK>(kb, kb + SH::NLQ * 1024, scr, gate, lane, half, uc);
                         }
                     } else if (c + 1 >= c0 && c + 1 < c1) {
-                        ut_half_part2(scr, tslot(c + 1), lane, half, uc);
+                        ut_half_part2<DK == 128>(scr, tslot(c + 1), lane, half, uc);
                     }
                     wait_vm(I0{});   // this step's loads have landed and this wave's LDS writes are done
                     __builtin_amdgcn_s_barrier();
