@@ -85,6 +85,27 @@ __device__ __forceinline__ void mmx(bwd::Acc<M, N, NWV>& acc, const bf16* A, int
     }
 }
 
+// The wave's tiles of C^T for an M x N product C formed with its operands exchanged (an Acc<N, M>): lane (r, g) of
+// tile (ti, tj) holds C[16 tj + r][16 ti + 4 g .. + 3], four consecutive columns of one row of C, so that the
+// row-major LDS tiles take them with one 8-byte access.  f(row, col0, x) for each of the wave's tiles.
+template <int MT, int NT, int NWV, class F>
+__device__ __forceinline__ void rows4(bwd::Acc<MT, NT, NWV>& at, int w, int lane, F f) {
+    typedef bwd::Acc<MT, NT, NWV> AC;
+#pragma unroll
+    for (int s = 0; s < AC::TPW; ++s) {
+        const int tt = w + NWV * s;
+        if (AC::ALL || tt < AC::NTT) {
+            const int ti = tt / AC::TN, tj = tt - ti * AC::TN;
+            f(16 * tj + (lane & 15), 16 * ti + 4 * (lane >> 4), at.t[s]);
+        }
+    }
+}
+__device__ __forceinline__ void st4(bf16* p, const f32x4& x) { *reinterpret_cast<bf16x4*>(p) = Mma<bf16>::cvt(x); }
+__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+    const bf16x4 h = ld4(p);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
 // ROWS x COLS of a row-major global matrix (row stride ld elements, 16-byte aligned rows) in registers between a
 // load (16 bytes per thread and request; rows >= n read as zeros) and a store into a bf16 LDS tile (row stride sld,
 // a multiple of 8).
@@ -233,15 +254,22 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
         sDb[tid] = db;
         sDlam[tid] = dl;
     }
+    // Every product below is formed with its operands exchanged (C^T = B^T A^T), so that each lane's accumulator
+    // elements are four consecutive columns of one row of C (rows4).
     {   // P = lower_incl(Q K^T)
         Acc<C, C, NWV> b;
         b.zero();
-        mmx<C, C, NWV, true, true, DK>(b, sQ, LDK, sK, LDK, w, lane);
-        b.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = (bf16)(j <= i ? x : 0.0f); });
+        mmx<C, C, NWV, true, true, DK>(b, sK, LDK, sQ, LDK, w, lane);
+        rows4(b, w, lane, [&](int i, int j0, f32x4& x) {
+            f32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = j0 + e <= i ? x[e] : 0.0f;
+            st4(sP + i * LDC + j0, y);
+        });
     }
     __syncthreads();
 
-    Acc<C, DK, NWV> aQ, aK;
+    Acc<DK, C, NWV> aQ, aK;   // dQ^T, dK^T
     Acc<C, C, NWV> W1, W2;
     aQ.zero();
     aK.zero();
@@ -256,65 +284,74 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
         if (col0 + NV < DV) load_slab(col0 + NV);
         // phase A: R = V - K S (kept for dalpha; D R over V) and dDelta = K dS' + P^T dO -- the two share the key
         // fragments and need nothing from each other
-        Acc<C, NV, NWV> R, dD;
+        Acc<NV, C, NWV> R, dD;   // R^T, dDelta^T
         R.zero();
         dD.zero();
-        mmx<C, NV, NWV, true, false, DK>(R, sK, LDK, sS, LDV, w, lane);
-        mmx<C, NV, NWV, true, false, DK>(dD, sK, LDK, sG2, LDV, w, lane);
-        mmx<C, NV, NWV, false, false, C>(dD, sP, LDC, sO, LDV, w, lane);
+        mmx<NV, C, NWV, false, true, DK>(R, sS, LDV, sK, LDK, w, lane);
+        mmx<NV, C, NWV, false, true, DK>(dD, sG2, LDV, sK, LDK, w, lane);
+        mmx<NV, C, NWV, false, false, C>(dD, sO, LDV, sP, LDC, w, lane);
         // each element of sV is read and then overwritten by the one lane that holds it in R: no barrier between
-        R.each(w, lane, [&](int i, int j, float& x) {
-            x = (float)sV[i * LDV + j] - x;
-            sV[i * LDV + j] = (bf16)(sAl[i] * x);
+        rows4(R, w, lane, [&](int i, int j0, f32x4& x) {
+            x = ld4f(sV + i * LDV + j0) - x;
+            st4(sV + i * LDV + j0, sAl[i] * x);
         });
-        dD.each(w, lane, [&](int i, int j, float& x) { sDd[i * LDV + j] = (bf16)x; });
+        rows4(dD, w, lane, [&](int i, int j0, f32x4& x) { st4(sDd + i * LDV + j0, x); });
         __syncthreads();
         {   // phase B: Delta = T (D R); G = T^T dDelta; -dR = -D G; dalpha += rowsum(G o R)
-            Acc<C, NV, NWV> a, gg;
+            Acc<NV, C, NWV> a, gg;   // Delta^T, G^T
             a.zero();
             gg.zero();
-            mmx<C, NV, NWV, false, false, C>(a, sT, LDC, sV, LDV, w, lane);
-            mmx<C, NV, NWV, true, false, C>(gg, sT, LDC, sDd, LDV, w, lane);
-            a.each(w, lane, [&](int i, int j, float& x) { sDl[i * LDV + j] = (bf16)x; });
-            gg.each(w, lane, [&](int i, int j, float& x) {
-                sGs[i * LDV + j] = (bf16)x;
-                sDr[i * LDV + j] = (bf16)(-sAl[i] * x);
+            mmx<NV, C, NWV, false, false, C>(a, sV, LDV, sT, LDC, w, lane);
+            mmx<NV, C, NWV, false, true, C>(gg, sDd, LDV, sT, LDC, w, lane);
+            rows4(a, w, lane, [&](int i, int j0, f32x4& x) { st4(sDl + i * LDV + j0, x); });
+            rows4(gg, w, lane, [&](int i, int j0, f32x4& x) {
+                st4(sGs + i * LDV + j0, x);
+                st4(sDr + i * LDV + j0, -sAl[i] * x);
             });
-            // rows of this lane's elements: the same (tile, i) for gg and R, summed over the tile's 16 columns into
-            // the tile column's row sums (a tile belongs to the same wave in every slab: one writer per element, and
-            // a fixed order of the sums, so the gradients do not depend on the waves' timing)
-            typedef Acc<C, NV, NWV> AN;
+            // rows of this lane's elements: the same (tile, row) for gg and R, summed over the tile's 16 columns (the
+            // lane's four, then across the four lane rows) into the tile column's row sums (a tile belongs to the
+            // same wave in every slab: one writer per element, and a fixed order of the sums, so the gradients do not
+            // depend on the waves' timing)
+            typedef Acc<NV, C, NWV> AN;
 #pragma unroll
             for (int s = 0; s < AN::TPW; ++s) {
                 const int tt = w + NWV * s;
                 if (AN::ALL || tt < AN::NTT) {
                     const int ti = tt / AN::TN, tj = tt - ti * AN::TN;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float p = gg.t[s][i] * R.t[s][i];
-                        p = group_sum<16>(p);   // the tile row's 16 columns, by DPP moves
-                        if ((lane & 15) == 0) sGR[tj * C + 16 * ti + 4 * (lane >> 4) + i] += p;
-                    }
+                    float p = (gg.t[s][0] * R.t[s][0] + gg.t[s][1] * R.t[s][1]) +
+                              (gg.t[s][2] * R.t[s][2] + gg.t[s][3] * R.t[s][3]);
+                    p = cross_row_sum(p);
+                    if ((lane >> 4) == 0) sGR[ti * C + 16 * tj + (lane & 15)] += p;
                 }
             }
         }
         __syncthreads();
         // dQ += dO S^T; dK += Delta dS'^T - dR S^T; W1 += dO Delta^T; W2 += G Delta^T (reduction over the slab)
-        mmx<C, DK, NWV, true, true, NV>(aQ, sO, LDV, sS, LDV, w, lane);
-        mmx<C, DK, NWV, true, true, NV>(aK, sDl, LDV, sG2, LDV, w, lane);
-        mmx<C, DK, NWV, true, true, NV>(aK, sDr, LDV, sS, LDV, w, lane);
-        mmx<C, C, NWV, true, true, NV>(W1, sO, LDV, sDl, LDV, w, lane);
-        mmx<C, C, NWV, true, true, NV>(W2, sGs, LDV, sDl, LDV, w, lane);
+        mmx<DK, C, NWV, true, true, NV>(aQ, sS, LDV, sO, LDV, w, lane);
+        mmx<DK, C, NWV, true, true, NV>(aK, sG2, LDV, sDl, LDV, w, lane);
+        mmx<DK, C, NWV, true, true, NV>(aK, sS, LDV, sDr, LDV, w, lane);
+        mmx<C, C, NWV, true, true, NV>(W1, sDl, LDV, sO, LDV, w, lane);
+        mmx<C, C, NWV, true, true, NV>(W2, sDl, LDV, sGs, LDV, w, lane);
         __syncthreads();
     }
 
     // M o W1 into sP; dL = -strict_lower(D W2) into sT (T is no longer needed); the row sums of strict_lower(L) o W2
     // by tile column, with L = K K^T formed on the wave's tiles of W2
-    W1.each(w, lane, [&](int i, int j, float& x) { sP[i * LDC + j] = (bf16)(j <= i ? x : 0.0f); });
-    W2.each(w, lane, [&](int i, int j, float& x) { sT[i * LDC + j] = (bf16)(j < i ? -sAl[i] * x : 0.0f); });
+    rows4(W1, w, lane, [&](int i, int j0, f32x4& x) {
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = j0 + e <= i ? x[e] : 0.0f;
+        st4(sP + i * LDC + j0, y);
+    });
+    rows4(W2, w, lane, [&](int i, int j0, f32x4& x) {
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = j0 + e < i ? -sAl[i] * x[e] : 0.0f;
+        st4(sT + i * LDC + j0, y);
+    });
     {
         typedef Acc<C, C, NWV> AC;
-        AC Lt;
+        AC Lt;   // L = K K^T is symmetric: its tiles line up with those of W2^T element by element
         Lt.zero();
         mmx<C, C, NWV, true, true, DK>(Lt, sK, LDK, sK, LDK, w, lane);
 #pragma unroll
@@ -322,13 +359,13 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
             const int tt2 = w + NWV * s;
             if (AC::ALL || tt2 < AC::NTT) {
                 const int ti = tt2 / AC::TN, tj = tt2 - ti * AC::TN;
+                const int row = 16 * tj + (lane & 15), col0 = 16 * ti + 4 * (lane >> 4);
+                float q[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * ti + 4 * (lane >> 4) + i, col = 16 * tj + (lane & 15);
-                    float p = col < row ? Lt.t[s][i] * W2.t[s][i] : 0.0f;
-                    p = group_sum<16>(p);   // the tile row's 16 columns, by DPP moves
-                    if ((lane & 15) == 0) sLW[tj * C + row] = p;
-                }
+                for (int e = 0; e < 4; ++e) q[e] = col0 + e < row ? Lt.t[s][e] * W2.t[s][e] : 0.0f;
+                float p = (q[0] + q[1]) + (q[2] + q[3]);
+                p = cross_row_sum(p);
+                if ((lane >> 4) == 0) sLW[ti * C + row] = p;
             }
         }
     }
@@ -347,17 +384,23 @@ __global__ __launch_bounds__(kChunkXThreads) void bwd_chunk_mx_kernel(
     }
     __syncthreads();
     // dQ += (M o W1) K;  dK += (M o W1)^T Q + dL K + dL^T K + 2 dlambda o K
-    mmx<C, DK, NWV, true, false, C>(aQ, sP, LDC, sK, LDK, w, lane);
-    mmx<C, DK, NWV, false, false, C>(aK, sP, LDC, sQ, LDK, w, lane);
-    mmx<C, DK, NWV, true, false, C>(aK, sT, LDC, sK, LDK, w, lane);
-    mmx<C, DK, NWV, false, false, C>(aK, sT, LDC, sK, LDK, w, lane);
+    mmx<DK, C, NWV, false, true, C>(aQ, sK, LDK, sP, LDC, w, lane);
+    mmx<DK, C, NWV, false, false, C>(aK, sQ, LDK, sP, LDC, w, lane);
+    mmx<DK, C, NWV, false, true, C>(aK, sK, LDK, sT, LDC, w, lane);
+    mmx<DK, C, NWV, false, false, C>(aK, sK, LDK, sT, LDC, w, lane);
     // dQ and dK staged as bf16 tiles in the slab tiles' space (no product reads it any more), then written as
     // 16-byte pieces of the chunk's rows
     static_assert(2 * C * LDK * 2 <= LY::AL - LY::S, "dQ and dK tiles fit where the slab tiles were");
     bf16* sDQ = reinterpret_cast<bf16*>(smem_x + LY::S);
     bf16* sDK = sDQ + C * LDK;
-    aQ.each(w, lane, [&](int i, int e, float& x) { sDQ[i * LDK + e] = (bf16)x; });
-    aK.each(w, lane, [&](int i, int e, float& x) { sDK[i * LDK + e] = (bf16)fmaf(2.0f * sDa[i], (float)sK[i * LDK + e], x); });
+    rows4(aQ, w, lane, [&](int i, int e0, f32x4& x) { st4(sDQ + i * LDK + e0, x); });
+    rows4(aK, w, lane, [&](int i, int e0, f32x4& x) {
+        const f32x4 kr = ld4f(sK + i * LDK + e0);
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(2.0f * sDa[i], kr[e], x[e]);
+        st4(sDK + i * LDK + e0, y);
+    });
     __syncthreads();
     for (int idx = tid; idx < C * (DK / 8); idx += NTH) {
         const int r = idx / (DK / 8), c8 = (idx - r * (DK / 8)) * 8;
