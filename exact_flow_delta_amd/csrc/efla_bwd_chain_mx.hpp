@@ -96,7 +96,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
             } else {
                 const int tr = p / RB;
-                const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
+                const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk_tr<DK>(tr));
                 const int ld = (int)(tile == 2 ? os : tile == 1 ? ks : qs);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 0 ? rq : tile == 1 ? rk : ro, dst, 16,
                                                          (tr * ld + 8 * lc) * 2, 0, 0, 0);
@@ -151,10 +151,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_chain_mx_kernel(
     }
 
     // per-lane LDS offsets, as in the forward state pass
-    const int swr = sw_qk<DK>(r);
+    const int swr = sw_qk_tr<DK>(r);
     const int te = 4 * g + ((lane >> 2) & 3);
     const int tc = lane & 3;
-    const int swt = sw_qk<DK>(te);
+    const int swt = sw_qk_tr<DK>(te);
     const int o_off = te * SH::RBV + 16 * (((2 * w + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
     // Ta^T from the stored operand layout: lane 4 e + c of group g reads stored lane 16 c + 4 g + e of the block
     const int ta_off = 8 * (16 * (lane & 3) + 4 * g + ((lane >> 2) & 3));
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, dst, 16, p, 0, 0, 0);
             } else {
                 const int tr = p / RB;
-                const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk<DK>(tr));
+                const int lc = ((p % RB) / 16) ^ (tile == 2 ? sw_v<DVS>(tr) : sw_qk_tr<DK>(tr));
                 const int ld = (int)(tile == 2 ? vs : ks);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(tile == 1 ? rk : rv, dst, 16, (tr * ld + 8 * lc) * 2, 0, 0, 0);
             }
@@ -438,10 +438,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + 64) void bwd_states_mx_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[rt][i] = s0 ? s0[((int64_t)bh * DK + srow(rt, i)) * DV + colw + r] : 0.0f;
     }
-    const int swr = sw_qk<DK>(r);
+    const int swr = sw_qk_tr<DK>(r);
     const int te = 4 * g + ((lane >> 2) & 3);
     const int tc = lane & 3;
-    const int swt = sw_qk<DK>(te);
+    const int swt = sw_qk_tr<DK>(te);
     const int v_off = te * SH::RBV + 16 * (((2 * w + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
     const int s_lane = (8 * g * DV + colw + r) * (sbf ? 2 : 4);
 

@@ -18,8 +18,8 @@
 //    S[32 kp + 8 g + 4 h + i][column r].  The K^T operand of the state update is read with the
 //    transposing LDS read, addressed with the same permutation.
 //  * XOR-swizzled, unpadded tiles.  Row t of a tile keeps its 16-byte chunk c at position c ^ sw(t),
-//    with sw chosen per row width so that the 16 rows of a fragment read and the 4x4 row/column
-//    pattern of a transposing read land on distinct banks.
+//    with sw chosen per row width by measurement (sw_qk below) so that fragment reads and the transposing reads
+//    of the state update lose as few cycles as possible to bank conflicts.
 //
 // One workgroup per (batch*head, slab of DVS state columns): DVS/16 compute waves (16 state columns each)
 // and one producer wave that only issues the tile loads and waits for them, so the compute waves never
@@ -95,12 +95,22 @@ struct TileTag {
     static constexpr int ISV = ISV_;
 };
 
-// chunk swizzles (16-byte chunks within a row)
+// chunk swizzles (16-byte chunks within a row).  256-byte rows (d_k = 128): row t's chunk c sits at c ^ sw(t), sw a
+// linear map of the row's low four bits (bits 1, 2, 4, 8 -> masks 3, 10, 5, 4), chosen by timing all 20,160
+// invertible maps on gfx950: conflict-free 16-byte fragment reads (16 rows, four chunks each) and the fewest
+// conflict cycles of the transposing reads of four rows by four chunks.
 template <int DK>
 __device__ __forceinline__ int sw_qk(int t) {
-    if constexpr (DK == 128) return 4 * (t & 3) + ((t >> 2) & 3);
+    if constexpr (DK == 128) return ((t & 1) ? 3 : 0) ^ ((t & 2) ? 10 : 0) ^ ((t & 4) ? 5 : 0) ^ ((t & 8) ? 4 : 0);
     else if constexpr (DK == 64) return 4 * ((t >> 1) & 1) + ((t >> 2) & 3);
     else return (t >> 2) & 3;
+}
+// The earlier 256-byte-row swizzle (4 (t & 3) + (t >> 2 & 3)): fewer cycles where transposing reads dominate (the
+// backward's state passes measured faster with it)
+template <int DK>
+__device__ __forceinline__ int sw_qk_tr(int t) {
+    if constexpr (DK == 128) return 4 * (t & 3) + ((t >> 2) & 3);
+    else return sw_qk<DK>(t);
 }
 template <int DVS>
 __device__ __forceinline__ int sw_v(int t) {
