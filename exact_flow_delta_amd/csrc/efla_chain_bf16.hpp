@@ -37,8 +37,9 @@
 //            whole-chunk buffers; the producer fetches a chunk's keys and betas first and waits for them one
 //            step earlier than for its queries and values.
 //   UTW = 2: four UT waves, in pairs on alternate chunks, each half-chunk transform cut into two parts run in
-//            steps c - 2 and c - 1 for chunk c; the first UT wave also issues the loads; LDS rings of their own
-//            (keys and betas four chunks deep, queries and V slab two deep, Ta two deep).
+//            steps c - 2 and c - 1 for chunk c; the waves running part 1 also issue the loads; LDS rings of
+//            their own (keys and betas four chunks deep, queries and V slab two deep), and Ta read by the compute
+//            waves from the UT waves' private LDS, where part 2 leaves it.
 #pragma once
 
 #include "efla_chunk_split.hpp"
@@ -78,12 +79,11 @@ struct ChainBf16Shape {
     static constexpr int BUF = OFF_B + (UTW == 1 ? 1024 : 0);   // one buffer (each tile rounded up to 1 KiB)
     static constexpr int UTS = UTW == 1 ? 2 * kUtHalfBytes : 0;     // the two UT waves' private LDS
     static constexpr int NBUF = 3 * BUF + UTS <= kMaxLdsBytes ? 3 : 2;   // prefetch distance NBUF - 1 chunks
-    // UTW == 2: rings of their own -- keys and betas four deep, queries and values two deep, Ta two deep -- and
-    // four UT waves' private LDS
+    // UTW == 2: rings of their own -- keys and betas four deep, queries and values two deep -- and four UT
+    // waves' private LDS (which also holds the Ta blocks the compute waves read)
     static constexpr int KBS = NLQ * 1024 + 1024;            // K tile, then the betas
     static constexpr int QVS = (NLQ + NLV) * 1024;           // Q tile, then the V slab
-    static constexpr int TS = NLT * 1024;
-    static constexpr int RING2 = 4 * KBS + 2 * QVS + 2 * TS + 4 * kUtHalfBytes;
+    static constexpr int RING2 = 4 * KBS + 2 * QVS + 4 * kUtHalfBytes;
     static constexpr int BYTES = UTW == 2 ? RING2 : NBUF * BUF + UTS;
 };
 
@@ -258,73 +258,31 @@ __device__ __forceinline__ void ut_half_lds(const lds_u8* cK, const lds_u8* cB, 
 }
 
 // The same half-chunk transform as ut_half_lds, cut into two parts run in consecutive chunk steps by one wave
-// (the four-UT-wave workgroup: two pairs of waves take alternate chunks, so each has two steps per chunk).  Part 1:
-// keys, the Gram blocks (whose diagonals give lambda), gates and the first kUtSplit steps of both substitutions;
-// part 2: the remaining steps,
-// the diagonal blocks, T_10 and the export.  What part 2 needs stays in the wave's registers (UtCarry) and in its
-// private LDS (the transposed diagonal blocks of A, then Ta^T and T_bb^T).
+// (the four-UT-wave workgroup: two pairs of waves take alternate chunks, so each has two steps per chunk).
+// Part 1 (registers only, no LDS writes): the keys, the Gram blocks (whose diagonals give lambda), the gates,
+// A_10 and the two diagonal blocks of A.  Part 2: the diagonal blocks of A into the wave's private LDS, both
+// 16 x 16 substitutions by row broadcast, T_bb^T and Ta^T, then T_10.  Ta^T stays in the private LDS for the
+// compute waves of the next step, which read it transposed; part 1 of the wave's next chunk, run in that step,
+// writes no LDS, and its part 2 comes a step later.  The split point was measured: every substitution step moved
+// into part 1, or the gates moved into part 2, made the step slower.
 struct UtCarry {
-    float sv[16];        // column r of the lane group's diagonal block of T, after the steps done so far
     bf16x4 A10;          // A_10 as a bf16 A operand
     float ar0, ar1;      // gates of rows 16 j + r
     float alpha_mine;    // gate of token 32 h + 16 (g & 1) + r
+    f32x4 at0, at1;      // lane (r, g): A_jj[r][4 g + i] of the two diagonal blocks, zero on and above the diagonal
 };
-constexpr int kUtSplit = 1;   // substitution steps in part 1 (part 1 also holds the Gram products and the issue of
-                              // a step's loads; measured against 0, 2, 3 and 5)
-
-// steps m = M0 .. M1 - 1 of the right-looking substitution on the transposed diagonal block `at` (rows of At read
-// three steps ahead)
-template <int M0, int M1>
-__device__ __forceinline__ void ut_solve_steps(const lds_f32* at, float* sv) {
-    constexpr int LDAT = 20;
-    f32x4 ring[4][4];
-#pragma unroll
-    for (int m = M0; m < M0 + 3 && m < M1; ++m) {
-#pragma unroll
-        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) ring[m & 3][i4] = *reinterpret_cast<const lds_f32x4*>(at + m * LDAT + 4 * i4);
-    }
-#pragma unroll
-    for (int m = M0; m < M1; ++m) {
-        if (m + 3 < M1) {
-#pragma unroll
-            for (int i4 = (m + 4) / 4; i4 < 4; ++i4)
-                ring[(m + 3) & 3][i4] = *reinterpret_cast<const lds_f32x4*>(at + (m + 3) * LDAT + 4 * i4);
-        }
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
-    }
-}
-
-// steps m = M0 .. M1 - 1 of the same substitution with every row of `at` it needs read first (all in flight at once)
-template <int M0, int M1>
-__device__ __forceinline__ void ut_solve_steps_all(const lds_f32* at, float* sv) {
-    constexpr int LDAT = 20;
-    f32x4 rows[16][4];
-#pragma unroll
-    for (int m = M0; m < M1; ++m) {
-#pragma unroll
-        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) rows[m][i4] = *reinterpret_cast<const lds_f32x4*>(at + m * LDAT + 4 * i4);
-    }
-#pragma unroll
-    for (int m = M0; m < M1; ++m) {
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) sv[i] -= rows[m][i / 4][i % 4] * sv[m];
-    }
-}
 
 template <int DK>
-__device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB, lds_u8* scr, int gate, int lane,
-                                              int h, UtCarry& u) {
+__device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB, int gate, int lane, int h,
+                                              UtCarry& u) {
     constexpr int NKP = DK / 32;
     constexpr int RBQ = DK * 2;
-    constexpr int LDAT = 20;
     typedef Mma<bf16> M;
     typedef bf16x8 bx8;
     const int r = lane & 15;
     const int g = lane >> 4;
     const int gb = g & 1;
     const int swr = sw_qk<DK>(r);
-    lds_f32* const sAt = (lds_f32*)scr;
     bx8 kf[2][NKP];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -355,70 +313,76 @@ __device__ __forceinline__ void ut_half_part1(const lds_u8* cK, const lds_u8* cB
     row_swap16(u.alpha_mine, u.ar0, u.ar1);   // rows 0 and 2 hold block 0's tokens, rows 1 and 3 block 1's
     u.A10 = M::cvt(gr[2] * u.ar1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const float arj = j ? u.ar1 : u.ar0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sAt[j * kUtHalfAtb + (4 * g + i) * LDAT + r] = (4 * g + i < r) ? arj * gr[j][i] : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        u.at0[i] = (4 * g + i < r) ? u.ar0 * gr[0][i] : 0.0f;
+        u.at1[i] = (4 * g + i < r) ? u.ar1 * gr[1][i] : 0.0f;
     }
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < 16; ++i) u.sv[i] = (i == r) ? 1.0f : 0.0f;
-    ut_solve_steps<0, kUtSplit>(sAt + gb * kUtHalfAtb, u.sv);
 }
 
-// ALL_ROWS: the substitution reads every row it needs first (measured faster with d_k = 128; it raises the
-// register count of the smaller shapes' kernels)
-template <bool ALL_ROWS>
-__device__ __forceinline__ void ut_half_part2(lds_u8* scr, lds_u8* ta, int lane, int h, UtCarry& u) {
+// part 2; `scr` is the wave's private kUtHalfBytes, which ends holding Ta^T: quads (0, 0), (1, 0), (1, 1) of the
+// half-chunk at bytes 0, 512 and 1024, each a row-major 16 x 16 bf16 block (row c = column c of Ta)
+__device__ __forceinline__ void ut_half_part2(lds_u8* scr, int lane, const UtCarry& u) {
+    constexpr int LDAT = 20;
     typedef Mma<bf16> M;
     typedef M::quad quad;
     typedef bf16x8 bx8;
     const int r = lane & 15;
     const int g = lane >> 4;
     const int gb = g & 1;
-    const lds_f32* sAt = (const lds_f32*)scr;
+    lds_f32* const sAt = (lds_f32*)scr;
     lds_b16* const sTt = (lds_b16*)(scr + kUtHalfOffTt);
     lds_b16* const sTat = (lds_b16*)scr;
     const int tr = M::tr_offset(lane, 16);
-    auto quad_t = [&](const lds_b16* X) __attribute__((always_inline)) {
-        return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_b16*>(X) + tr)));
-    };
-    if constexpr (ALL_ROWS)
-        ut_solve_steps_all<kUtSplit, 15>(sAt + gb * kUtHalfAtb, u.sv);
-    else
-        ut_solve_steps<kUtSplit, 15>(sAt + gb * kUtHalfAtb, u.sv);
-    __asm__ volatile("" ::: "memory");   // the rows of A are read before Ta^T overwrites them
+    // transposed diagonal blocks of A (At[m][i] = A[i][m]); lane r then reads row r of its block, column r of A
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sAt[(4 * g + i) * LDAT + r] = u.at0[i];
+        sAt[kUtHalfAtb + (4 * g + i) * LDAT + r] = u.at1[i];
+    }
+    __asm__ volatile("" ::: "memory");   // this wave's LDS operations complete in order
+    float sv[16];   // column r of the lane group's diagonal block of T
+    {
+        float acol[16];
+        const lds_f32* at = sAt + gb * kUtHalfAtb + r * LDAT;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 a = *reinterpret_cast<const lds_f32x4*>(at + 4 * i4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acol[4 * i4 + e] = a[e];
+        }
+        __asm__ volatile("" ::: "memory");   // the block of A is read before Ta^T overwrites it
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+        tri_solve_row_bcast<0, 15>(acol, sv);   // rows 2 and 3 repeat rows 0 and 1
+    }
     if (g < 2) {
+        // row r of T_gg^T and of Ta_gg^T (column r scaled by the gate of token 32 h + 16 g + r)
         bx8 t0v, t1v, a0v, a1v;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            t0v[i] = (bf16)u.sv[i];
-            t1v[i] = (bf16)u.sv[8 + i];
-            a0v[i] = (bf16)(u.sv[i] * u.alpha_mine);
-            a1v[i] = (bf16)(u.sv[8 + i] * u.alpha_mine);
+            t0v[i] = (bf16)sv[i];
+            t1v[i] = (bf16)sv[8 + i];
+            a0v[i] = (bf16)(sv[i] * u.alpha_mine);
+            a1v[i] = (bf16)(sv[8 + i] * u.alpha_mine);
         }
         lds_b16* tt = sTt + g * 256 + r * 16;
         *reinterpret_cast<lds_bf16x8*>(tt) = t0v;
         *reinterpret_cast<lds_bf16x8*>(tt + 8) = t1v;
-        lds_b16* tq = sTat + (2 * g) * 256 + r * 16;
+        lds_b16* tq = sTat + (2 * g) * 256 + r * 16;   // local quads: 0 = (0, 0), 1 = (1, 0), 2 = (1, 1)
         *reinterpret_cast<lds_bf16x8*>(tq) = a0v;
         *reinterpret_cast<lds_bf16x8*>(tq + 8) = a1v;
     }
     __asm__ volatile("" ::: "memory");
+    // T_10 = -T_11 (A_10 T_00)
     {
-        const quad T00 = *reinterpret_cast<const lds_b16x4*>(sTt + r * 16 + 4 * g);
+        const quad T00 = *reinterpret_cast<const lds_b16x4*>(sTt + r * 16 + 4 * g);   // T_00[4g + e][r]
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
         M::mma1(y, u.A10, T00);
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        M::mma1(z, quad_t(sTt + 256), M::cvt_neg(y));
+        const quad T11 = __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sTt + 256 + tr)));
+        M::mma1(z, T11, M::cvt_neg(y));   // T_11 as the A operand
+        // z lane (r, g), element e = T_10[4g + e][r]: row r of Ta_10^T after the column gate of token 32 h + r
         *reinterpret_cast<lds_b16x4*>(sTat + 256 + r * 16 + 4 * g) = M::cvt(z * u.ar0);
-    }
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int l = 0; l < 3; ++l) {
-        const int qi = l == 0 ? 5 * h : l + 7 * h;
-        *reinterpret_cast<lds_b16x4*>(ta + 512 * qi + 8 * lane) = quad_t(sTat + l * 256);
     }
     __asm__ volatile("" ::: "memory");
 }
@@ -461,10 +425,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
     lds_u8* const buf1 = (lds_u8*)buf1_;
     lds_u8* const buf2 = (lds_u8*)buf2_;
     lds_u8* const ring = (lds_u8*)ring_;
-    // UTW == 2: chunk x's keys and betas, queries and V slab, and Ta
+    // UTW == 2: chunk x's keys and betas, queries and V slab, and the private LDS of the UT pair that forms its Ta
     auto kbslot = [&](int x) __attribute__((always_inline)) { return ring + (x & 3) * SH::KBS; };
     auto qvslot = [&](int x) __attribute__((always_inline)) { return ring + 4 * SH::KBS + (x & 1) * SH::QVS; };
-    auto tslot = [&](int x) __attribute__((always_inline)) { return ring + 4 * SH::KBS + 2 * SH::QVS + (x & 1) * SH::TS; };
+    auto tpair = [&](int x) __attribute__((always_inline)) { return (const lds_u8*)uts_ + 2 * (x & 1) * kUtHalfBytes; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -500,6 +464,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
     const int swt = sw_qk<DK>(te);
     // transposing V reads: row 16 rb + 4 g + e, columns 16 w + 4 c .. +3: logical chunk 2 w + (c >> 1), byte 8 (c & 1)
     const int v_off = te * SH::RBV + 16 * (((2 * w + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
+    const int ta_tr = 2 * M::tr_offset(lane, 16);   // transposing reads of a row-major 16 x 16 bf16 block (bytes)
 
     // ---- loads (producer wave only): wave load j of a tile covers its bytes [1024 j, 1024 j + 1024); lane L
     //      writes 16 bytes at 1024 j + 16 L, i.e. physical chunk p of row t, holding logical chunk p ^ sw(t)
@@ -577,9 +542,9 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
             // UT wave u: pair u >> 1 takes the chunks of that parity, u & 1 is its half.  In step c (c0 - 2 <= c < c1)
             // pair c & 1 runs part 1 of chunk c + 2 and the other pair part 2 of chunk c + 1 (which writes its Ta).
             // The UT waves also issue the loads: wave 0 before the first barrier the keys and betas of chunks
-            // c0 .. c0 + 2 and the queries and values of c0; in step c >= c0 the pair running part 1 (the lighter
-            // part), its first wave the keys and betas of c + 3 and its second the queries and values of c + 1, each
-            // landed by the end of the step.
+            // c0 .. c0 + 2 and the queries and values of c0; in step c >= c0 the pair running part 1, its first wave
+            // the keys and betas of c + 3 and its second the queries and values of c + 1, each landed by the end of
+            // the step (issued by the part-2 pair instead, they measured slower).
             typedef std::integral_constant<int, 1> I1;
             typedef std::integral_constant<int, 2> I2;
             const int u = w - NW;
@@ -610,10 +575,10 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
                     if ((c & 1) == pair) {
                         if (c + 2 < c1) {
                             lds_u8* kb = kbslot(c + 2);
-                            ut_half_part1<DK>(kb, kb + SH::NLQ * 1024, scr, gate, lane, half, uc);
+                            ut_half_part1<DK>(kb, kb + SH::NLQ * 1024, gate, lane, half, uc);
                         }
                     } else if (c + 1 >= c0 && c + 1 < c1) {
-                        ut_half_part2<DK == 128>(scr, tslot(c + 1), lane, half, uc);
+                        ut_half_part2(scr, lane, uc);
                     }
                     wait_vm(I0{});   // this step's loads have landed and this wave's LDS writes are done
                     __builtin_amdgcn_s_barrier();
@@ -763,7 +728,15 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
             // Delta = Ta R over the sub-chunk; Ta block (rb, kb) of the chunk is quad qi = rb (rb + 1) / 2 + kb,
             // lane (r, g)'s at byte 512 qi + 8 lane
             auto ta = [&](int rb, int kb) __attribute__((always_inline)) {
-                return *reinterpret_cast<const lds_quad*>(cT + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+                if constexpr (UTW == 2) {
+                    // from the private LDS of the half's UT wave: its Ta^T quads (0, 0), (1, 0), (1, 1), read
+                    // transposed
+                    const int hh = rb / NBS, lr = rb - hh * NBS, lk = kb - hh * NBS;
+                    return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(const_cast<lds_u8*>(cT) + hh * kUtHalfBytes + 512 * (lr * (lr + 1) / 2 + lk) + ta_tr)));
+                } else {
+                    return *reinterpret_cast<const lds_quad*>(cT + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+                }
             };
             // R = V - K S: lane (r, g), element e of row block rb: row 16 rb + 4g + e, column 16 w + r of the slab
             auto vblk = [&](int rb) __attribute__((always_inline)) {
@@ -886,7 +859,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
         // one segment (c0 = 0): unrolled over the key ring's four slots, so that every slot is a constant offset
         auto stepr = [&](int c, int i) __attribute__((always_inline)) {
             const lds_u8* qv = qvslot(i);
-            step(c, qv, kbslot(i), qv + SH::NLQ * 1024, tslot(i));
+            step(c, qv, kbslot(i), qv + SH::NLQ * 1024, tpair(i));
         };
         for (int c = 0; c < c1; c += 4) {
             stepr(c, 0);
@@ -958,7 +931,7 @@ constexpr int kOneLaunchUtMode = 2;
 // LDS bytes of the one-launch forward (mirror of ChainBf16Shape<.., kOneLaunchUtMode>)
 constexpr int chain_ut_bf16_bytes(int dk, int dvs) {
     const int nlq = (64 * dk * 2 + 1023) / 1024, nlv = (64 * dvs * 2 + 1023) / 1024, nlt = (10 * 512 + 1023) / 1024;
-    if (kOneLaunchUtMode == 2) return 4 * (nlq + 1) * 1024 + 2 * (nlq + nlv) * 1024 + 2 * nlt * 1024 + 4 * kUtHalfBytes;
+    if (kOneLaunchUtMode == 2) return 4 * (nlq + 1) * 1024 + 2 * (nlq + nlv) * 1024 + 4 * kUtHalfBytes;
     return 3 * (2 * nlq + nlv + nlt + 1) * 1024 + 2 * kUtHalfBytes;
 }
 

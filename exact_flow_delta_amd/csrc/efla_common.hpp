@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace efla {
 
 typedef __bf16 bf16;
@@ -273,6 +275,52 @@ __device__ __forceinline__ void rows_bcast4(float x, float out[4]) {
     row_swap16(x, e, o);
     row_swap32(e, out[0], out[2]);
     row_swap32(o, out[1], out[3]);
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_impl<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl<0, N>(f);
+}
+
+// x -= (a of lane M of this lane's 16-lane row) * y: v_fmac_f32 with the row_newbcast:M data-parallel modifier
+// and a negated broadcast operand (the compiler folds row broadcasts into adds but not into multiply-adds).  A DPP
+// instruction may not read a VGPR that a vector instruction wrote in the two instructions before it; NOP leads with
+// those two wait states.  Vector ALU only.
+template <int M, bool NOP>
+__device__ __forceinline__ void fmac_row_bcast_neg(float& x, float a, float y) {
+    static_assert(M >= 0 && M < 16, "lane of a 16-lane row");
+    if constexpr (NOP)
+        asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "+v"(x) : "v"(a), "v"(y), "i"(M));
+    else
+        asm volatile("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "+v"(x) : "v"(a), "v"(y), "i"(M));
+}
+
+// Steps m = M0 .. M1 - 1 of the right-looking forward substitution for one column of (I + A)^-1, A strictly lower
+// 16 x 16: step m subtracts A[i][m] x[m] from x[i] for every i > m.  Each 16-lane row of the wave solves its own
+// block; lane m of the row holds column m of that block (acol[i] = A[i][m], zero for i <= m) and lane r column r of
+// the inverse in x (x = e_r before step 0).  Step m takes A[i][m] from lane m by row broadcast, so no lane reads the
+// block from memory.  The first multiply-add of a step leads with the wait states (it reads x[m], written by the
+// step before), and so does every one of the first step, whose x registers the compiler may have just set.
+template <int M0, int M1>
+__device__ __forceinline__ void tri_solve_row_bcast(const float* acol, float* x) {
+    static_assert(M0 >= 0 && M0 <= M1 && M1 <= 15, "substitution steps of a 16 x 16 block");
+    static_for<M1 - M0>([&](auto mc) {
+        constexpr int m = M0 + decltype(mc)::value;
+        static_for<15 - m>([&](auto jc) {
+            constexpr int i = m + 1 + decltype(jc)::value;
+            fmac_row_bcast_neg<m, i == m + 1 || m == M0>(x[i], acol[i], x[m]);
+        });
+    });
 }
 
 // Sum over aligned groups of WIDTH consecutive lanes (WIDTH a power of two <= 64); every lane of a

@@ -23,18 +23,6 @@
 
 namespace efla {
 
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for_impl(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for_impl<I + 1, N>(f);
-    }
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl<0, N>(f);
-}
-
 constexpr int kLdAt = 16 + 4;   // row stride of sAt (fp32)
 
 // Per wave: for every block row hi with hi % NW == w, alpha of its 16 tokens, the Gram block row
