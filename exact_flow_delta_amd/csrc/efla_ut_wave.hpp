@@ -161,23 +161,19 @@ __global__ __launch_bounds__(256, 3) void ut_wave_kernel(
         const int blk = g < NB ? g : 0;   // lanes of groups past the last block repeat block 0 and store nothing
         const float* at = sAt + blk * SH::ATB;
         float sv[16];
+        {
+            // lane r reads row r of its block of At (column r of A); the substitution takes column m from lane m
+            // of the row by row broadcast
+            float acol[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
-        f32x4 ring[4][4];   // rows of At read three steps ahead of their use
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(at + r * SH::LDAT + 4 * i4);
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-#pragma unroll
-            for (int i4 = (m + 1) / 4; i4 < 4; ++i4) ring[m][i4] = *reinterpret_cast<const f32x4*>(at + m * SH::LDAT + 4 * i4);
-        }
-#pragma unroll
-        for (int m = 0; m < 15; ++m) {
-            if (m + 3 < 15) {
-#pragma unroll
-                for (int i4 = (m + 4) / 4; i4 < 4; ++i4)
-                    ring[(m + 3) & 3][i4] = *reinterpret_cast<const f32x4*>(at + (m + 3) * SH::LDAT + 4 * i4);
+                for (int e = 0; e < 4; ++e) acol[4 * i4 + e] = a[e];
             }
 #pragma unroll
-            for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
+            for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
+            tri_solve_row_bcast<0, 15>(acol, sv);
         }
         // the keys are consumed: fetch the next chunk's (after the solves, which hold the most registers)
         load(u + stride);
