@@ -30,12 +30,9 @@
 // chunk is computed.
 //
 // UTW (in-workgroup UT transform, 64-token chunks): more waves form each chunk's Ta in the workgroup itself,
-// ahead of the compute waves, from the key tile and the betas already staged in LDS, and write it where the
-// compute waves would otherwise read the UT launch's output; the keys cross HBM once and no workspace is
-// written or read.  Only the diagonal 32 x 32 blocks of Ta are formed (the half-chunk steps read no other).
-//   UTW = 1: two UT waves (one per 32-token half) transform chunk c + 1 during step c, over the three
-//            whole-chunk buffers; the producer fetches a chunk's keys and betas first and waits for them one
-//            step earlier than for its queries and values.
+// ahead of the compute waves, from the key tile and the betas already staged in LDS; the keys cross HBM once and
+// no workspace is written or read.  Only the diagonal 32 x 32 blocks of Ta are formed (the half-chunk steps read
+// no other).
 //   UTW = 2: four UT waves, in pairs on alternate chunks, each half-chunk transform cut into two parts run in
 //            steps c - 2 and c - 1 for chunk c; the waves running part 1 also issue the loads; LDS rings of
 //            their own (keys and betas four chunks deep, queries and V slab two deep), and Ta read by the compute
@@ -54,13 +51,13 @@ typedef __attribute__((address_space(3))) bf16 lds_b16;
 typedef f32x4 __attribute__((address_space(3))) lds_f32x4;
 typedef bf16x4 __attribute__((address_space(3))) lds_b16x4;
 
-// LDS of one in-workgroup UT wave (ut_half_lds and its two-part form below): two transposed fp32 diagonal blocks
-// of A, then T_bb^T (bf16); Ta^T (three bf16 quads) reuses the space of the A blocks
+// LDS of one in-workgroup UT wave: two transposed fp32 diagonal blocks of A, then T_bb^T (bf16); Ta^T (three
+// bf16 quads) reuses the space of the A blocks
 constexpr int kUtHalfAtb = 16 * 20 + 4;                       // floats per transposed diagonal block of A
 constexpr int kUtHalfOffTt = 2 * kUtHalfAtb * 4;
 constexpr int kUtHalfBytes = kUtHalfOffTt + 2 * 512;
 
-// UTW: 0 none, 1 two in-workgroup UT waves over three buffers, 2 four UT waves over separate rings (below)
+// UTW: 0 none (the UT launch's Ta is read), 2 four in-workgroup UT waves over separate rings (below)
 template <int DK, int C, int DVS, int UTW = 0>
 struct ChainBf16Shape {
     static constexpr int RBQ = DK * 2;                       // bytes per Q / K row
@@ -75,16 +72,14 @@ struct ChainBf16Shape {
     static constexpr int OFF_K = NLQ * 1024;
     static constexpr int OFF_V = 2 * NLQ * 1024;
     static constexpr int OFF_T = (2 * NLQ + NLV) * 1024;
-    static constexpr int OFF_B = (2 * NLQ + NLV + NLT) * 1024;   // betas of the chunk (UTW only)
-    static constexpr int BUF = OFF_B + (UTW == 1 ? 1024 : 0);   // one buffer (each tile rounded up to 1 KiB)
-    static constexpr int UTS = UTW == 1 ? 2 * kUtHalfBytes : 0;     // the two UT waves' private LDS
-    static constexpr int NBUF = 3 * BUF + UTS <= kMaxLdsBytes ? 3 : 2;   // prefetch distance NBUF - 1 chunks
+    static constexpr int BUF = (2 * NLQ + NLV + NLT) * 1024;   // one buffer (each tile rounded up to 1 KiB)
+    static constexpr int NBUF = 3 * BUF <= kMaxLdsBytes ? 3 : 2;   // prefetch distance NBUF - 1 chunks
     // UTW == 2: rings of their own -- keys and betas four deep, queries and values two deep -- and four UT
     // waves' private LDS (which also holds the Ta blocks the compute waves read)
     static constexpr int KBS = NLQ * 1024 + 1024;            // K tile, then the betas
     static constexpr int QVS = (NLQ + NLV) * 1024;           // Q tile, then the V slab
     static constexpr int RING2 = 4 * KBS + 2 * QVS + 4 * kUtHalfBytes;
-    static constexpr int BYTES = UTW == 2 ? RING2 : NBUF * BUF + UTS;
+    static constexpr int BYTES = UTW == 2 ? RING2 : NBUF * BUF;
 };
 
 // shape of one tile for the load routine: row bytes, wave loads, whether it is a V tile
@@ -123,142 +118,9 @@ __device__ __forceinline__ int sw_v(int t) {
 // swizzled layout) and betas in LDS.  The diagonal 32 x 32 blocks of the chunk's Ta = T diag(alpha),
 // T = (I + strict_lower(diag(alpha) K K^T))^{-1}, are the halves' own Ta (the diagonal blocks of the inverse of a
 // block lower triangular matrix are the inverses of its diagonal blocks), and they are all the half-chunk steps
-// of the state pass read; half h is blocks 2h and 2h + 1.  Its three quads go to `ta` in the order the state pass
-// reads: quad qi = rb (rb + 1) / 2 + kb at byte 512 qi, lane (r, g) holding Ta[16 rb + r][16 kb + 4 g .. +3].
-// One wave, the steps of ut_wave_kernel: lambda and the gate from the key fragments, the three lower Gram blocks
-// on the matrix cores, both 16 x 16 diagonal solves at once in fp32 (lane groups 2 and 3 repeat 0 and 1 and
-// store nothing), T_10 = -T_11 A_10 T_00, a transposing export.  `scr` is the wave's private kUtHalfBytes.
-// Rows past the end of the sequence hold zero keys and betas: their alpha is 0, their rows of T those of I.
-template <int DK>
-__device__ __forceinline__ void ut_half_lds(const lds_u8* cK, const lds_u8* cB, lds_u8* scr, lds_u8* ta, int gate,
-                                            int lane, int h) {
-    constexpr int NKP = DK / 32;
-    constexpr int RBQ = DK * 2;
-    constexpr int LDAT = 20;
-    typedef Mma<bf16> M;
-    typedef M::quad quad;
-    typedef bf16x8 bx8;
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const int gb = g & 1;   // the block this lane group solves
-    const int swr = sw_qk<DK>(r);
-    lds_f32* const sAt = (lds_f32*)scr;
-    lds_b16* const sTt = (lds_b16*)(scr + kUtHalfOffTt);
-    lds_b16* const sTat = (lds_b16*)scr;
-    // column quad of a row-major 16 x 16 bf16 block: lane (r, g) <- X[4g .. 4g+3][r] (as Mma::lds_quad_t)
-    const int tr = M::tr_offset(lane, 16);
-    auto quad_t = [&](const lds_b16* X) __attribute__((always_inline)) {
-        return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<lds_b16*>(X) + tr)));
-    };
-
-    // keys: lane (r, g) holds row 32 h + 16 j + r, d_k 32 kp + 8 g .. +7 (one 16-byte read per fragment)
-    bx8 kf[2][NKP];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp)
-            kf[j][kp] = bx8(*reinterpret_cast<const lds_bf16x8*>(cK + (32 * h + 16 * j + r) * RBQ + 16 * ((4 * kp + g) ^ swr)));
-    }
-    const float beta_mine = reinterpret_cast<const lds_f32*>(cB)[32 * h + (lane & 31)];   // token 32 h + 16 gb + r
-
-    // lambda of rows 32 h + 16 j + r (fp32 sum of exact bf16 squares, the four lanes of a row combined)
-    float lam[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        float sq = 0.0f;
-#pragma unroll
-        for (int kp = 0; kp < NKP; ++kp) sq += sum_sq(kf[j][kp]);
-        lam[j] = cross_row_sum(sq);
-    }
-    const float alpha_mine = gate_alpha(beta_mine, gb ? lam[1] : lam[0], gate);
-    float ar[2];   // gate of row 16 j + r: rows 0 and 2 of the wave hold the tokens of block 0, rows 1 and 3 block 1
-    row_swap16(alpha_mine, ar[0], ar[1]);
-
-    // Gram blocks (j, l), l <= j: acc lane (r, g), element i = (K K^T)[32 h + 16 j + r][32 h + 16 l + 4 g + i]
-    quad A10;
-    static_for<2>([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        static_for<j + 1>([&](auto lc) {
-            constexpr int l = decltype(lc)::value;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kp = 0; kp < NKP; ++kp) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[l][kp], kf[j][kp], acc, 0, 0, 0);
-            if constexpr (l < j) {
-                A10 = M::cvt(acc * ar[1]);
-            } else {
-                // strict lower part, transposed: At[m][i] = A[16 j + i][16 j + m]
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sAt[j * kUtHalfAtb + (4 * g + i) * LDAT + r] = (4 * g + i < r) ? ar[j] * acc[i] : 0.0f;
-            }
-        });
-    });
-    __asm__ volatile("" ::: "memory");   // this wave's LDS operations complete in order
-
-    // diagonal solves, both blocks at once: lane (r, g) carries column r of T_{gb gb}
-    const lds_f32* at = sAt + gb * kUtHalfAtb;
-    float sv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = (i == r) ? 1.0f : 0.0f;
-    f32x4 ring[4][4];   // rows of At read three steps ahead of their use
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-#pragma unroll
-        for (int i4 = (m + 1) / 4; i4 < 4; ++i4) ring[m][i4] = *reinterpret_cast<const lds_f32x4*>(at + m * LDAT + 4 * i4);
-    }
-#pragma unroll
-    for (int m = 0; m < 15; ++m) {
-        if (m + 3 < 15) {
-#pragma unroll
-            for (int i4 = (m + 4) / 4; i4 < 4; ++i4)
-                ring[(m + 3) & 3][i4] = *reinterpret_cast<const lds_f32x4*>(at + (m + 3) * LDAT + 4 * i4);
-        }
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) sv[i] -= ring[m & 3][i / 4][i % 4] * sv[m];
-    }
-    if (g < 2) {
-        // row r of T_gg^T and of Ta_gg^T (column r scaled by the gate of token 32 h + 16 g + r)
-        bx8 t0v, t1v, a0v, a1v;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            t0v[i] = (bf16)sv[i];
-            t1v[i] = (bf16)sv[8 + i];
-            a0v[i] = (bf16)(sv[i] * alpha_mine);
-            a1v[i] = (bf16)(sv[8 + i] * alpha_mine);
-        }
-        lds_b16* tt = sTt + g * 256 + r * 16;
-        *reinterpret_cast<lds_bf16x8*>(tt) = t0v;
-        *reinterpret_cast<lds_bf16x8*>(tt + 8) = t1v;
-        lds_b16* tq = sTat + (2 * g) * 256 + r * 16;   // local quads: 0 = (0, 0), 1 = (1, 0), 2 = (1, 1)
-        *reinterpret_cast<lds_bf16x8*>(tq) = a0v;
-        *reinterpret_cast<lds_bf16x8*>(tq + 8) = a1v;
-    }
-    __asm__ volatile("" ::: "memory");
-
-    // T_10 = -T_11 (A_10 T_00)
-    {
-        const quad T00 = *reinterpret_cast<const lds_b16x4*>(sTt + r * 16 + 4 * g);   // T_00[4g + e][r]
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        M::mma1(y, A10, T00);
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        M::mma1(z, quad_t(sTt + 256), M::cvt_neg(y));   // T_11 as the A operand
-        // z lane (r, g), element e = T_10[4g + e][r]: row r of Ta_10^T after the column gate of token 32 h + r
-        *reinterpret_cast<lds_b16x4*>(sTat + 256 + r * 16 + 4 * g) = M::cvt(z * ar[0]);
-    }
-    __asm__ volatile("" ::: "memory");
-
-    // export: lane (r, g) of block (rb, kb) takes Ta[16 rb + r][16 kb + 4 g + e] = Ta^T[4 g + e][r]
-    // blocks (2h, 2h), (2h+1, 2h), (2h+1, 2h+1) are quads 0, 1, 2 (h = 0) or 5, 8, 9 (h = 1)
-#pragma unroll
-    for (int l = 0; l < 3; ++l) {
-        const int qi = l == 0 ? 5 * h : l + 7 * h;
-        *reinterpret_cast<lds_b16x4*>(ta + 512 * qi + 8 * lane) = quad_t(sTat + l * 256);
-    }
-    __asm__ volatile("" ::: "memory");   // the next chunk's A blocks overwrite Ta^T
-}
-
-// The same half-chunk transform as ut_half_lds, cut into two parts run in consecutive chunk steps by one wave
-// (the four-UT-wave workgroup: two pairs of waves take alternate chunks, so each has two steps per chunk).
+// of the state pass read; half h is blocks 2h and 2h + 1.  Rows past the end of the sequence hold zero keys and
+// betas: their alpha is 0, their rows of T those of I.  One wave runs it in two parts in consecutive chunk steps
+// (two pairs of UT waves take alternate chunks, so each has two steps per chunk).
 // Part 1 (registers only, no LDS writes): the keys, the Gram blocks (whose diagonals give lambda), the gates,
 // A_10 and the two diagonal blocks of A.  Part 2: the diagonal blocks of A into the wave's private LDS, both
 // 16 x 16 substitutions by row broadcast, T_bb^T and Ta^T, then T_10.  Ta^T stays in the private LDS for the
@@ -389,11 +251,11 @@ __device__ __forceinline__ void ut_half_part2(lds_u8* scr, int lane, const UtCar
 
 // OUT = false: no outputs (the first pass of the segment-parallel forward needs only the final states), so no
 // Q tile, no Q S, no Q K^T and no O -- 38 matrix instructions per chunk and wave instead of 100.
-// UTW: the in-workgroup UT transform (tw unused; beta and gate read); 64-token chunks with outputs, one segment.
-// 1: two UT waves and the load producer over three chunk buffers; 2: four UT waves, which also issue the loads,
-// over separate rings (keys and betas four chunks deep, so that a UT wave has two steps per chunk).
+// UTW = 2: the in-workgroup UT transform (tw unused; beta and gate read); 64-token chunks with outputs, one
+// segment; four UT waves, which also issue the loads, over separate rings (keys and betas four chunks deep, so that
+// a UT wave has two steps per chunk).
 template <int DK, int C, int DVS, bool OUT, int UTW = 0>
-__global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 64)) void chain_bf16_kernel(
+__global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : 64)) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
     bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg,
     TokLayout ly, const float* __restrict__ beta, int gate) {
@@ -412,14 +274,14 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
     static_assert(DK == 32 || DK == 64 || DK == 128, "d_k of 32, 64 or 128");
     static_assert(SH::BYTES <= kMaxLdsBytes, "state pass LDS too large");
     static_assert(UTW == 0 || (C == 64 && OUT), "in-workgroup UT: 64-token chunks with outputs");
-    static_assert(UTW != 1 || SH::NBUF == 3, "two UT waves: three buffers");
+    static_assert(UTW == 0 || UTW == 2, "no in-workgroup UT, or four UT waves");
 
     constexpr int PD = SH::NBUF - 1;   // chunks fetched ahead
     __shared__ __attribute__((aligned(1024))) unsigned char buf0_[UTW == 2 ? 16 : SH::BUF];
     __shared__ __attribute__((aligned(1024))) unsigned char buf1_[UTW == 2 ? 16 : SH::BUF];
     __shared__ __attribute__((aligned(1024))) unsigned char buf2_[UTW != 2 && PD == 2 ? SH::BUF : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char ring_[UTW == 2 ? SH::RING2 - 4 * kUtHalfBytes : 16];
-    __shared__ __attribute__((aligned(16))) unsigned char uts_[UTW == 1 ? SH::UTS : UTW == 2 ? 4 * kUtHalfBytes : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char uts_[UTW == 2 ? 4 * kUtHalfBytes : 16];
     // LDS is addressed only through LDS-space pointers (no generic pointer ever points into it)
     lds_u8* const buf0 = (lds_u8*)buf0_;
     lds_u8* const buf1 = (lds_u8*)buf1_;
@@ -514,17 +376,14 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
             }
         });
         if constexpr (PART == 1) {
-            // beta of token t + lane -> 4 bytes at OFF_B + 4 lane (zero past the end)
+            // beta of token t + lane -> 4 bytes at dB + 4 lane (zero past the end)
             const int64_t bt = ly.be_t;
             const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(beta + sv.be0 + t * bt, n > 0 ? (int)(((n - 1) * bt + 1) * 4) : 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)dB, 4, (int)(lane * bt * 4), 0, 0, 0);
         }
     };
-    auto issue_part = [&](int c, lds_u8* buf, auto part_c) __attribute__((always_inline)) {
-        issue_to(c, buf + SH::OFF_Q, buf + SH::OFF_K, buf + SH::OFF_V, buf + SH::OFF_T, buf + SH::OFF_B, part_c);
-    };
     auto issue_chunk = [&](int c, lds_u8* buf) __attribute__((always_inline)) {
-        issue_part(c, buf, std::integral_constant<int, 0>{});
+        issue_to(c, buf + SH::OFF_Q, buf + SH::OFF_K, buf + SH::OFF_V, buf + SH::OFF_T, buf, std::integral_constant<int, 0>{});
     };
     // wait until at most N vector-memory operations of this wave are in flight and all its LDS operations
     // are done (N is an immediate of the wait instruction; operations retire in issue order)
@@ -581,51 +440,6 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
                         ut_half_part2(scr, lane, uc);
                     }
                     wait_vm(I0{});   // this step's loads have landed and this wave's LDS writes are done
-                    __builtin_amdgcn_s_barrier();
-                }
-            }
-            return;
-        }
-    } else if constexpr (UTW == 1) {
-        typedef std::integral_constant<int, 1> I1;
-        typedef std::integral_constant<int, 2> I2;
-        typedef std::integral_constant<int, NQV> IQV;
-        auto bufsel = [&](int i) __attribute__((always_inline)) { return i == 0 ? buf0 : i == 1 ? buf1 : buf2; };
-        if (producer) {
-            // Step c (c = c0 - 1: the prologue's) issues chunk c + 2, keys and betas first, and ends once chunk
-            // c + 1 has landed whole and the keys and betas of chunk c + 2 too: in step c + 1 the compute waves
-            // use chunk c + 1 and the UT wave transforms chunk c + 2.  Chunk c lives in buffer (c - c0) mod 3.
-            if (c1 > c0) {
-                issue_part(c0, buf0, I1{});
-                issue_part(c0, buf0, I2{});
-                wait_vm(IQV{});   // keys and betas of chunk c0
-                __builtin_amdgcn_s_barrier();
-                for (int c = c0 - 1; c < c1; ++c) {
-                    if (c + 2 < c1) {
-                        lds_u8* nb = bufsel((c + 2 - c0) % 3);
-                        issue_part(c + 2, nb, I1{});
-                        issue_part(c + 2, nb, I2{});
-                        wait_vm(IQV{});
-                    } else {
-                        wait_vm(I0{});
-                    }
-                    __builtin_amdgcn_s_barrier();
-                }
-            }
-            return;
-        }
-        if (w > NW) {
-            // the UT waves, one per 32-token half: in step c, Ta of chunk c + 1 into that chunk's buffer
-            const int half = w - NW - 1;
-            lds_u8* const scr = (lds_u8*)uts_ + half * kUtHalfBytes;
-            if (c1 > c0) {
-                __builtin_amdgcn_s_barrier();   // keys and betas of chunk c0 are in
-                for (int c = c0 - 1; c < c1; ++c) {
-                    if (c + 1 < c1) {
-                        lds_u8* nb = bufsel((c + 1 - c0) % 3);
-                        ut_half_lds<DK>(nb + SH::OFF_K, nb + SH::OFF_B, scr, nb + SH::OFF_T, gate, lane, half);
-                    }
-                    wait_vm(I0{});   // its LDS writes are done before the barrier
                     __builtin_amdgcn_s_barrier();
                 }
             }
@@ -870,7 +684,6 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : UTW == 1 ? 192 : 
     } else {
         if (c1 > c0) {
             __builtin_amdgcn_s_barrier();   // the producer's prologue
-            if constexpr (UTW == 1) __builtin_amdgcn_s_barrier();   // and the UT waves' transform of chunk c0
         }
         if constexpr (PD == 2) {
             for (int c = c0; c < c1; c += 3) {
@@ -925,22 +738,17 @@ hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// The in-workgroup UT mode of the one-launch forward (1 or 2, see chain_bf16_kernel)
-constexpr int kOneLaunchUtMode = 2;
-
-// LDS bytes of the one-launch forward (mirror of ChainBf16Shape<.., kOneLaunchUtMode>)
+// LDS bytes of the one-launch forward (mirror of ChainBf16Shape<.., 2>)
 constexpr int chain_ut_bf16_bytes(int dk, int dvs) {
-    const int nlq = (64 * dk * 2 + 1023) / 1024, nlv = (64 * dvs * 2 + 1023) / 1024, nlt = (10 * 512 + 1023) / 1024;
-    if (kOneLaunchUtMode == 2) return 4 * (nlq + 1) * 1024 + 2 * (nlq + nlv) * 1024 + 4 * kUtHalfBytes;
-    return 3 * (2 * nlq + nlv + nlt + 1) * 1024 + 2 * kUtHalfBytes;
+    const int nlq = (64 * dk * 2 + 1023) / 1024, nlv = (64 * dvs * 2 + 1023) / 1024;
+    return 4 * (nlq + 1) * 1024 + 2 * (nlq + nlv) * 1024 + 4 * kUtHalfBytes;
 }
 
 // The whole chunked forward in one launch (bf16, d_k >= 32, 64-token chunks; contiguous [B,H,L,d], or the strided
 // views and packed sequences of a.layout): the state pass with its own UT waves in every workgroup.
 template <int DK, int DVS>
 hipError_t launch_chain_ut_bf16_t(const ChunkArgs& a, hipStream_t stream) {
-    constexpr int MODE = kOneLaunchUtMode;
-    typedef ChainBf16Shape<DK, 64, DVS, MODE> SH;
+    typedef ChainBf16Shape<DK, 64, DVS, 2> SH;
     static_assert(SH::BYTES == chain_ut_bf16_bytes(DK, DVS), "host mirror of the LDS size");
     SplitArgs sa{};
     sa.BH = a.BH;
@@ -953,8 +761,8 @@ hipError_t launch_chain_ut_bf16_t(const ChunkArgs& a, hipStream_t stream) {
     const TokLayout ly = a.layout ? *a.layout : contiguous_layout(1, a.L, DK, a.d_v);
     const int nslab = a.d_v / DVS;
     const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
-    const int threads = DVS / 16 * 64 + (MODE == 2 ? 256 : 192);
-    hipLaunchKernelGGL((chain_bf16_kernel<DK, 64, DVS, true, MODE>), dim3((unsigned)grid), dim3(threads),
+    const int threads = DVS / 16 * 64 + 256;
+    hipLaunchKernelGGL((chain_bf16_kernel<DK, 64, DVS, true, 2>), dim3((unsigned)grid), dim3(threads),
                        0, stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                        static_cast<const bf16*>(a.v), nullptr, static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v,
                        nslab, sg, ly, a.beta, a.gate);
