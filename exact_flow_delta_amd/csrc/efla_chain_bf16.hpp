@@ -21,8 +21,8 @@
 //    with sw chosen per row width by measurement (sw_qk below) so that fragment reads and the transposing reads
 //    of the state update lose as few cycles as possible to bank conflicts.
 //
-// One workgroup per (batch*head, slab of DVS state columns): DVS/16 compute waves (16 state columns each)
-// and one producer wave that only issues the tile loads and waits for them, so the compute waves never
+// One workgroup per (batch*head, slab of DVS state columns): DVS/16 compute waves (16 state columns each; on the
+// 128-column slab without outputs, four of 32 columns) and one producer wave that only issues the tile loads and waits for them, so the compute waves never
 // stall on the address unit.  All waves meet at one barrier per chunk.  Tiles are fetched two chunks
 // ahead into three LDS buffers when they fit (else one chunk ahead into two); the chunk loops are unrolled
 // so that the buffers rotate as distinct arrays, which also lets the compiler see that loads into one
@@ -254,15 +254,25 @@ __device__ __forceinline__ void ut_half_part2(lds_u8* scr, int lane, const UtCar
 // UTW = 2: the in-workgroup UT transform (tw unused; beta and gate read); 64-token chunks with outputs, one
 // segment; four UT waves, which also issue the loads, over separate rings (keys and betas four chunks deep, so that
 // a UT wave has two steps per chunk).
+// State columns per compute wave: 32 on the 128-column slab without outputs (the first pass of the segment-parallel
+// forward at d_k = 128: four compute waves, each key fragment read feeding the products of two column tiles, which
+// halves the LDS reads that bound that pass), else 16.
+template <int DVS, bool OUT, int UTW>
+constexpr int chain_cols_per_wave() { return (!OUT && UTW == 0 && DVS == 128) ? 32 : 16; }
+template <int DVS, bool OUT, int UTW>
+constexpr int chain_threads() { return DVS / chain_cols_per_wave<DVS, OUT, UTW>() * 64 + (UTW == 2 ? 256 : 64); }
+
 template <int DK, int C, int DVS, bool OUT, int UTW = 0>
-__global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : 64)) void chain_bf16_kernel(
+__global__ __launch_bounds__((chain_threads<DVS, OUT, UTW>())) void chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ tw,
     bf16* __restrict__ o, const float* s0, float* sf, int BH, int L, int DV, int nslab, ChainSeg sg,
     TokLayout ly, const float* __restrict__ beta, int gate) {
     typedef ChainBf16Shape<DK, C, DVS, UTW> SH;
     typedef Mma<bf16> M;
     typedef M::quad quad;
-    constexpr int NW = DVS / 16;
+    constexpr int CPW = chain_cols_per_wave<DVS, OUT, UTW>();
+    constexpr int NW = DVS / CPW;   // compute waves
+    static_assert(CPW == 16 || (DK == 128 && C == 64), "32-column waves: d_k = 128, 64-token chunks");
     constexpr int NB = C / 16;
     constexpr int NKD = DK / 16;   // state tiles (16 d_k rows each)
     constexpr int NKP = DK / 32;   // 32-wide d_k slices
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : 64)) void chain_b
     const int slab_col = slab * DVS;               // column of the state (value columns first, then transition)
     const bool trans = slab >= sg.nslab_v;         // transition slab: zero values, identity start, no outputs
     const bool producer = w == NW;                 // the extra wave: it only fetches
-    const int colw = slab_col + 16 * (producer ? 0 : w);
+    const int colw = slab_col + CPW * (producer ? 0 : w);
     const SeqView sv = seq_view(ly, bh, L, C);      // this head's tokens: offsets, row strides, length
     const int len = sv.len;
     const int NC = (len + C - 1) / C;
@@ -485,6 +495,133 @@ __global__ __launch_bounds__(DVS / 16 * 64 + (UTW == 2 ? 256 : 64)) void chain_b
 
     // ---- the state: S[32 kp + 8 g + 4 h + i][colw + r] in tile rt = 2 kp + h, element i ------------------
     auto srow = [&](int rt, int i) __attribute__((always_inline)) { return 32 * (rt >> 1) + 8 * g + 4 * (rt & 1) + i; };
+
+    if constexpr (CPW == 32) {
+        // Two 16-column state tiles per wave (columns colw .. +15 and colw + 16 .. +31), no outputs: per 32-token
+        // sub-chunk R = V - K S, Delta = Ta R, S += K^T Delta for both tiles, every key fragment, transposed key block
+        // and Ta block read once for the two.
+        typedef bf16x8 bx8;
+        typedef quad __attribute__((address_space(3))) lds_quad;
+        f32x4 S2[2][NKD];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int col = colw + 16 * ct;
+#pragma unroll
+            for (int rt = 0; rt < NKD; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = srow(rt, i);
+                    S2[ct][rt][i] = trans ? (row == col - DV + r ? 1.0f : 0.0f)
+                                          : s0 ? s0[(((int64_t)bh * nseg + seg) * DK + row) * DV + col + r] : 0.0f;
+                }
+            }
+        }
+        // transposing V reads of tile ct: row 16 rb + 4 g + e, columns 32 w + 16 ct + 4 c .. +3 of the slab
+        int v_off2[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+            v_off2[ct] = te * SH::RBV + 16 * (((2 * (2 * w + ct) + (tc >> 1)) % NCV) ^ sw_v<DVS>(te)) + 8 * (tc & 1);
+        auto pair = [&](quad a, quad b) __attribute__((always_inline)) -> bx8 { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); };
+        auto step32 = [&](const lds_u8* cK, const lds_u8* cV, const lds_u8* cT) __attribute__((always_inline)) {
+            auto frag = [&](int rb, int kp) __attribute__((always_inline)) {   // row 16 rb + r, d_k 32 kp + 8 g .. +7
+                return bx8(*reinterpret_cast<const lds_bf16x8*>(cK + (16 * rb + r) * SH::RBQ + 16 * ((4 * kp + g) ^ swr)));
+            };
+            auto kt = [&](int rt, int kb) __attribute__((always_inline)) {
+                const int off = te * SH::RBQ + 16 * ((4 * (rt >> 1) + tc) ^ swt) + 8 * (rt & 1);
+                return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                    (lds_s16x4*)(const_cast<lds_u8*>(cK) + 16 * kb * SH::RBQ + off)));
+            };
+            auto ta = [&](int rb, int kb) __attribute__((always_inline)) {
+                return *reinterpret_cast<const lds_quad*>(cT + 512 * (rb * (rb + 1) / 2 + kb) + 8 * lane);
+            };
+            auto vblk = [&](int rb, int ct) __attribute__((always_inline)) {
+                return __builtin_bit_cast(quad, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                    (lds_s16x4*)(const_cast<lds_u8*>(cV) + 16 * rb * SH::RBV + v_off2[ct])));
+            };
+            static_for<NSUB>([&](auto hc) {
+                constexpr int b0 = decltype(hc)::value * NBS;
+                bx8 Sq[2][NKP];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int kp = 0; kp < NKP; ++kp) Sq[ct][kp] = pair(M::cvt(S2[ct][2 * kp]), M::cvt(S2[ct][2 * kp + 1]));
+                quad Rq[2][NBS];
+                static_for<NBS>([&](auto jc) {
+                    constexpr int rb = b0 + decltype(jc)::value;
+                    bx8 kq[NKP];
+#pragma unroll
+                    for (int kp = 0; kp < NKP; ++kp) kq[kp] = frag(rb, kp);
+                    f32x4 xk[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                    for (int kp = 0; kp < NKP; ++kp)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct)
+                            xk[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[kp], Sq[ct][kp], xk[ct], 0, 0, 0);   // K S
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const quad vq = vblk(rb, ct);
+                        f32x4 rr;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) rr[e] = (float)vq[e] - xk[ct][e];
+                        Rq[ct][decltype(jc)::value] = M::cvt(rr);
+                    }
+                });
+                quad Dq[2][NBS];
+                static_for<NBS>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    constexpr int rb = b0 + j;
+                    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                    static_for<(j + 1) / 2>([&](auto pc) {
+                        constexpr int i = 2 * decltype(pc)::value;
+                        const quad a0 = ta(rb, b0 + i), a1 = ta(rb, b0 + i + 1);
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct) M::mma2(acc[ct], a0, a1, Rq[ct][i], Rq[ct][i + 1]);
+                    });
+                    if constexpr ((j + 1) & 1) {
+                        const quad a = ta(rb, rb);
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct) M::mma1(acc[ct], a, Rq[ct][j]);
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) Dq[ct][j] = M::cvt(acc[ct]);
+                });
+                static_assert(NBS == 2, "two row blocks per sub-chunk");
+                quad k0[NKD], k1[NKD];
+#pragma unroll
+                for (int rt = 0; rt < NKD; ++rt) {
+                    k0[rt] = kt(rt, b0);
+                    k1[rt] = kt(rt, b0 + 1);
+                }
+#pragma unroll
+                for (int rt = 0; rt < NKD; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) M::mma2(S2[ct][rt], k0[rt], k1[rt], Dq[ct][0], Dq[ct][1]);
+            });
+            wait_vm(I0{});   // LDS reads done
+            __builtin_amdgcn_s_barrier();
+        };
+        auto stepb32 = [&](const lds_u8* b) __attribute__((always_inline)) {
+            step32(b + SH::OFF_K, b + SH::OFF_V, b + SH::OFF_T);
+        };
+        static_assert(PD == 2, "three buffers");
+        if (c1 > c0) __builtin_amdgcn_s_barrier();   // the producer's prologue
+        for (int c = c0; c < c1; c += 3) {
+            stepb32(buf0);
+            if (c + 1 < c1) stepb32(buf1);
+            if (c + 2 < c1) stepb32(buf2);
+        }
+        if (sf && (sg.sf_all || seg == nseg - 1)) {
+            const int64_t base = sg.sf_all ? (int64_t)bh * nseg + seg : bh;
+            const int ld = sg.sf_all ? sg.ld_sf : DV;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int rt = 0; rt < NKD; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sf[(base * DK + srow(rt, i)) * ld + colw + 16 * ct + r] = S2[ct][rt][i];
+        }
+        return;
+    }
     f32x4 S[NKD];
 #pragma unroll
     for (int rt = 0; rt < NKD; ++rt) {
@@ -726,12 +863,12 @@ hipError_t launch_chain_bf16(const SplitArgs& a, hipStream_t stream) {
     const int64_t grid = (int64_t)((a.BH + 7) / 8) * 8 * nslab;
     const dim3 g3((unsigned)grid, (unsigned)(a.nseg > 0 ? a.nseg : 1));
     if (a.o == nullptr)
-        hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, false>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
+        hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, false>), g3, dim3(chain_threads<DVS, false, 0>()), 0, stream,
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
                            sg, ly, nullptr, 0);
     else if constexpr (DVS != 128)
-        hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, true>), g3, dim3(DVS / 16 * 64 + 64), 0, stream,
+        hipLaunchKernelGGL((chain_bf16_kernel<DK, C, DVS, true>), g3, dim3(chain_threads<DVS, true, 0>()), 0, stream,
                            static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                            static_cast<const bf16*>(a.tw), static_cast<bf16*>(a.o), a.s0, a.sf, a.BH, a.L, a.d_v, nslab,
                            sg, ly, nullptr, 0);
